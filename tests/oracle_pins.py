@@ -1,0 +1,340 @@
+"""Pins of the fp64 oracle against what the MTLA pages and the mathematics fix.
+
+Each ``pin_*`` function takes the oracle module ``o`` and raises
+AssertionError when the oracle disagrees with the pinned fact.  They are run
+against the real oracle (tests/test_oracle_pins.py) and against deliberately
+broken copies of it (tests/test_oracle_mutations.py), which shows that a
+plausible mistake anywhere in the oracle fails at least one pin.
+
+None of these checks re-types an oracle formula: each compares the oracle with
+an independent construction (enumeration, closed form, library routine, page
+value, or a second schedule of the same computation).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_values.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _rand_case(seed, N, s, H, d_h, d_c, d_r, w_scale=None):
+    g = np.random.default_rng(seed)
+    c = g.standard_normal((N, d_c))
+    k_r = g.standard_normal((N, d_r))
+    q_c = g.standard_normal((N, H, d_h))
+    q_r = g.standard_normal((N, H, d_r))
+    ws = 1.0 / math.sqrt(d_c) if w_scale is None else w_scale
+    w_hyp = g.standard_normal(d_c) * ws
+    w_uk = g.standard_normal((H, d_h, d_c)) * ws
+    w_uv = g.standard_normal((H, d_h, d_c)) * ws
+    return c, k_r, q_c, q_r, w_hyp, w_uk, w_uv
+
+
+# ---------------------------------------------------------------------------
+# Integer structure
+# ---------------------------------------------------------------------------
+
+def pin_slot_index(o):
+    """Slot of each token by enumerating blocks of s tokens (no division)."""
+    for s in range(1, 9):
+        tokens_to_slot = []
+        for b in range(1, 40):
+            tokens_to_slot += [b] * s
+        for t in range(1, len(tokens_to_slot) + 1):
+            assert o.slot_of(t, s) == tokens_to_slot[t - 1], (t, s)
+
+
+def pin_block_starts(o):
+    """Tokens that open a slot are 1, s+1, 2s+1, ... (a range, not a modulus)."""
+    for s in range(1, 9):
+        starts = set(range(1, 200, s))
+        for t in range(1, 200):
+            assert o.opens_slot(t, s) == (t in starts), (t, s)
+
+
+def pin_slot_count(o):
+    """ceil(N/s) slots = number of distinct slots the tokens 1..N occupy."""
+    for s in range(1, 9):
+        for N in range(0, 60):
+            distinct = len({o.slot_of(t, s) for t in range(1, N + 1)})
+            assert o.num_slots(N, s) == distinct, (N, s)
+
+
+def pin_mask_special_cases(o):
+    """s=1: the ordinary causal mask (np.tril).  s>=N: only the diagonal."""
+    for N in range(1, 24):
+        assert np.array_equal(o.stride_mask(N, 1), np.tril(np.ones((N, N), dtype=bool)))
+        for s in (N, N + 1, N + 5):
+            assert np.array_equal(o.stride_mask(N, s), np.eye(N, dtype=bool))
+
+
+def pin_mask_structure(o):
+    """Causal, diagonal always visible, and query i sees ceil(i/s) keys."""
+    for s in range(1, 7):
+        N = 5 * s + 3
+        M = o.stride_mask(N, s)
+        assert not np.triu(M, 1).any()
+        assert M.diagonal().all()
+        for i in range(1, N + 1):
+            # its own partial slot plus the completed slots before it
+            assert M[i - 1].sum() == len(range(1, i + 1, s)), (i, s)
+
+
+def pin_mask_matches_incremental_cache(o):
+    """The partial merges the mask exposes to query i are exactly the slots the
+    incremental decoder holds after token i (the pages' consistency claim at
+    the level of the attended rows)."""
+    g = np.random.default_rng(7)
+    for s in range(1, 6):
+        N = 4 * s + 3
+        x = g.standard_normal((N, 5))
+        w = g.uniform(0.1, 0.9, N)
+        P = o.partial_merges(x, w, s)
+        M = o.stride_mask(N, s)
+        for i in range(1, N + 1):
+            cache = o.merge_incremental(x[:i], w[:i], s)
+            seen = P[M[i - 1]]
+            assert seen.shape == cache.shape, (i, s)
+            np.testing.assert_allclose(seen, cache, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Page values
+# ---------------------------------------------------------------------------
+
+def pin_cache_ratio(o):
+    g = golden()
+    d = g["cache_ratio_default_s2"]["dims"]
+    for N in (8, 64, 4096):
+        r = o.cache_ratio_vs_mqa(N, d["s"], d["d_h"], d["d_c"], d["d_r"])
+        assert r == Fraction(g["cache_ratio_default_s2"]["value"]), r
+    f = g["cache_ratio_formula"]
+    for d_h in (16, 64, 128):
+        for s in range(1, 7):
+            N = 12 * s
+            r = o.cache_ratio_vs_mqa(N, s, d_h, 4 * d_h, d_h // 2)
+            assert r == Fraction(f["numerator"], f["denominator_per_s"] * s), (d_h, s, r)
+    # s does not divide N: the stored slot count rounds up, so the ratio is larger
+    assert o.cache_ratio_vs_mqa(4096, 3, 64, 256, 32) > Fraction(9, 12)
+
+
+def pin_row_bytes(o):
+    g = golden()
+    e = g["latent_row_bytes_bf16"]
+    row = o.cache_row_bytes(e["d_c"], e["d_r"], e["bytes_per_element"])
+    assert row == e["value"]
+    assert row * g["latent_bytes_78_layers"]["layers"] == g["latent_bytes_78_layers"]["value"]
+    assert row * 78 * g["latent_bytes_1M_positions"]["positions"] == g["latent_bytes_1M_positions"]["value"]
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+
+def pin_gate_zero_weights(o):
+    """W_hyp = 0: every gate is sigmoid(0) = 1/2 exactly, whatever c and pe are."""
+    g = np.random.default_rng(3)
+    c = g.standard_normal((9, 16))
+    pe = o.sinusoidal_pe(9, 16)
+    w = o.gate(c, pe, np.zeros(16))
+    assert np.all(w == 0.5)
+    # a positive logit gives a gate above 1/2, a negative one below
+    wp = o.gate(np.ones((1, 16)) - pe[:1], pe[:1], np.ones(16))
+    assert wp[0] > 0.5 and abs(wp[0] - 1.0 / (1.0 + math.exp(-16.0))) < 1e-15
+
+
+def pin_merge_half_sum(o):
+    """With w = 1/2 the slot is half the block sum; integers keep it exact."""
+    g = np.random.default_rng(5)
+    for s in range(1, 6):
+        N = 3 * s + 2
+        x = g.integers(-8, 9, size=(N, 4)).astype(float)
+        cache = o.merge_incremental(x, np.full(N, 0.5), s)
+        for b in range(cache.shape[0]):
+            blk = x[b * s: min(N, (b + 1) * s)]
+            assert np.array_equal(cache[b], 0.5 * blk.sum(axis=0)), (s, b)
+
+
+def pin_block_start_overwrites(o):
+    """A token that opens a block writes a new slot: whatever the slot row held
+    before (a reused cache) does not leak into the merged value."""
+    g = np.random.default_rng(6)
+    for s in range(1, 5):
+        N = 4 * s + 1
+        x = g.standard_normal((N, 3))
+        w = g.uniform(0.1, 0.9, N)
+        fresh = o.merge_incremental(x, w, s)
+        stale = g.standard_normal(fresh.shape) * 100.0
+        reused = o.merge_incremental(x, w, s, cache=stale)
+        np.testing.assert_allclose(reused, fresh, rtol=0, atol=1e-12)
+        # continuing from a block start on a cache with garbage beyond it
+        t0 = s + 1
+        head = o.merge_incremental(x[: t0 - 1], w[: t0 - 1], s)
+        junk = np.vstack([head, g.standard_normal((fresh.shape[0] - head.shape[0], 3))])
+        cont = o.merge_incremental(x[t0 - 1:], w[t0 - 1:], s, cache=junk, t0=t0)
+        np.testing.assert_allclose(cont, fresh, rtol=0, atol=1e-12)
+
+
+def pin_uniform_attention_keyset(o):
+    """q = 0, W_hyp = 0, basis-vector latents, W_UV = I: output i is
+    1/(2 |K(i)|) on tokens 1..i and 0 after, with |K(i)| = 1 + floor((i-1)/s).
+
+    Each token k <= i lies in exactly one attended key (a completed block, or
+    the own partial block), so the uniform mean puts equal mass on all of them.
+    """
+    for s in range(1, 5):
+        N = 3 * s + 2
+        d = N
+        c = np.eye(N)
+        k_r = np.zeros((N, 2))
+        q_c = np.zeros((N, 1, d))
+        q_r = np.zeros((N, 1, 2))
+        eye = np.eye(d)[None]
+        for sched in (o.incremental, o.parallel):
+            out = sched(c, k_r, q_c, q_r, np.zeros(d), eye, eye, s, 0.5, pe=np.zeros((N, d)))
+            for i in range(1, N + 1):
+                nk = 1 + (i - 1) // s
+                want = np.where(np.arange(1, d + 1) <= i, 1.0 / (2 * nk), 0.0)
+                np.testing.assert_allclose(out[i - 1, 0], want, rtol=0, atol=1e-14,
+                                           err_msg=f"{sched.__name__} s={s} i={i}")
+
+
+# ---------------------------------------------------------------------------
+# Identities and library reductions
+# ---------------------------------------------------------------------------
+
+def pin_absorption(o):
+    """Absorbed decode (W_UK into the query, W_UV after the sum) equals the
+    explicit per-head key/value form."""
+    g = np.random.default_rng(11)
+    for (H, d_h, d_c, d_r, n) in ((2, 4, 12, 2, 5), (3, 8, 6, 4, 9), (1, 5, 5, 0, 3)):
+        S = g.standard_normal((n, d_c + d_r))
+        q_c = g.standard_normal((H, d_h))
+        q_r = g.standard_normal((H, d_r))
+        w_uk = g.standard_normal((H, d_h, d_c))
+        w_uv = g.standard_normal((H, d_h, d_c))
+        a = o.decode_absorbed(q_c, q_r, S, w_uk, w_uv, d_c, 0.3)
+        e = o.decode_explicit(q_c, q_r, S, w_uk, w_uv, d_c, 0.3)
+        np.testing.assert_allclose(a, e, rtol=1e-12, atol=1e-12)
+
+
+def pin_decode_single_slot(o):
+    """One slot: softmax of a single score is 1, so o_h = W_UV[h] c_1 exactly."""
+    g = np.random.default_rng(12)
+    S = g.standard_normal((1, 10))
+    w_uv = g.standard_normal((2, 3, 8))
+    out = o.decode_absorbed(g.standard_normal((2, 3)), g.standard_normal((2, 2)), S,
+                            g.standard_normal((2, 3, 8)), w_uv, 8, 0.7)
+    np.testing.assert_allclose(out, np.einsum("hek,k->he", w_uv, S[0, :8]), rtol=1e-13)
+
+
+def pin_s1_equals_causal_sdpa(o):
+    """s = 1 and W_hyp = 0 (w = 1/2) reduce MTLA to causal attention with keys
+    [W_UK c_j / 2 ; k^R_j / 2] and values W_UV c_j / 2.  Compared with torch's
+    scaled_dot_product_attention in fp64 on the CPU (an independent routine)."""
+    import torch
+    H, d_h, d_c, d_r, N = 2, 6, 10, 4, 11
+    c, k_r, q_c, q_r, _, w_uk, w_uv = _rand_case(21, N, 1, H, d_h, d_c, d_r)
+    scale = 1.0 / math.sqrt(d_h + d_r)
+    outs = [sched(c, k_r, q_c, q_r, np.zeros(d_c), w_uk, w_uv, 1, scale, pe=np.zeros((N, d_c)))
+            for sched in (o.parallel, o.incremental)]
+    tq = torch.tensor(np.concatenate([q_c, q_r], axis=2)).permute(1, 0, 2)         # H N d
+    K = np.stack([0.5 * c @ w_uk[h].T for h in range(H)])                         # H N d_h
+    V = np.stack([0.5 * c @ w_uv[h].T for h in range(H)])
+    Kr = np.broadcast_to(0.5 * k_r, (H, N, d_r))
+    tk = torch.tensor(np.concatenate([K, Kr], axis=2))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, torch.tensor(V), is_causal=True, scale=scale).permute(1, 0, 2).numpy()
+    for out in outs:
+        np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_parallel_equals_incremental(o, cases=None):
+    """The stride-masked parallel pass equals token-by-token decoding (the pages'
+    central claim), in fp64, for the given (seed, N, s, H, d_h, d_c, d_r)."""
+    cases = cases or [(1, 13, 2, 2, 4, 8, 2), (2, 17, 3, 1, 3, 5, 4), (3, 9, 4, 2, 2, 6, 2),
+                      (4, 10, 1, 1, 4, 4, 2), (5, 7, 9, 2, 3, 7, 2)]
+    for (seed, N, s, H, d_h, d_c, d_r) in cases:
+        c, k_r, q_c, q_r, w_hyp, w_uk, w_uv = _rand_case(seed, N, s, H, d_h, d_c, d_r)
+        scale = 1.0 / math.sqrt(d_h + d_r)
+        inc = o.incremental(c, k_r, q_c, q_r, w_hyp, w_uk, w_uv, s, scale)
+        par = o.parallel(c, k_r, q_c, q_r, w_hyp, w_uk, w_uv, s, scale)
+        assert o.max_rel_err(par, inc) <= 1e-12, (seed, N, s, o.max_rel_err(par, inc))
+
+
+def pin_prefill_query_rows(o):
+    """prefill_query(i) reproduces row i of the dense parallel pass."""
+    N, s, H, d_h, d_c, d_r = 11, 3, 2, 4, 6, 2
+    c, k_r, q_c, q_r, w_hyp, w_uk, w_uv = _rand_case(31, N, s, H, d_h, d_c, d_r)
+    scale = 0.4
+    par, P = o.parallel(c, k_r, q_c, q_r, w_hyp, w_uk, w_uv, s, scale, return_partials=True)
+    for i in range(1, N + 1):
+        row = o.prefill_query(P, i, q_c[i - 1], q_r[i - 1], w_uk, w_uv, s, d_c, scale)
+        np.testing.assert_allclose(row, par[i - 1], rtol=1e-12, atol=1e-13)
+
+
+def pin_rope(o):
+    """RoPE: identity at position 0, norm preserving, and scores depend only on
+    the relative position (q rotated at p, k at p') ."""
+    g = np.random.default_rng(41)
+    q, k = g.standard_normal(8), g.standard_normal(8)
+    np.testing.assert_allclose(o.rope(q, 0), q, rtol=0, atol=0)
+    for p in (1, 7, 300):
+        assert abs(np.linalg.norm(o.rope(q, p)) - np.linalg.norm(q)) < 1e-12
+    a = o.rope(q, 10) @ o.rope(k, 4)
+    b = o.rope(q, 106) @ o.rope(k, 100)
+    assert abs(a - b) < 1e-12
+    # the pair (2k, 2k+1) rotates as a complex multiplication by e^{i*angle}
+    z = complex(q[0], q[1]) * np.exp(1j * 5.0)
+    r = o.rope(q, 5)
+    assert abs(r[0] - z.real) < 1e-12 and abs(r[1] - z.imag) < 1e-12
+
+
+def pin_pe(o):
+    """pe: position 0 is (sin 0, cos 0) = (0, 1) per pair; pairs lie on the unit
+    circle; the first pair advances by one radian per position."""
+    pe = o.sinusoidal_pe(50, 12)
+    np.testing.assert_array_equal(pe[0], np.tile([0.0, 1.0], 6))
+    np.testing.assert_allclose(pe[:, 0::2] ** 2 + pe[:, 1::2] ** 2, 1.0, rtol=1e-14)
+    ang = np.arctan2(pe[:, 0], pe[:, 1])
+    np.testing.assert_allclose(np.unwrap(ang), np.arange(50.0), atol=1e-12)
+
+
+def pin_layer_schedules(o):
+    """The full layer gives the same y with either attention schedule, and its
+    output projection is linear in the attention output."""
+    g = np.random.default_rng(51)
+    N, dm, H, d_h, d_c, d_r, s = 7, 12, 2, 4, 8, 2, 2
+    p = {"w_dkv": g.standard_normal((d_c, dm)) / math.sqrt(dm),
+         "w_q": g.standard_normal((H * (d_h + d_r), dm)) / math.sqrt(dm),
+         "w_r": g.standard_normal((d_r, dm)) / math.sqrt(dm),
+         "w_o": g.standard_normal((dm, H * d_h)) / math.sqrt(H * d_h),
+         "w_hyp": g.standard_normal(d_c) / math.sqrt(d_c),
+         "w_uk": g.standard_normal((H, d_h, d_c)) / math.sqrt(d_c),
+         "w_uv": g.standard_normal((H, d_h, d_c)) / math.sqrt(d_c)}
+    h = g.standard_normal((N, dm))
+    y1 = o.layer(h, p, H, d_h, d_r, s, 0.4, "incremental")
+    y2 = o.layer(h, p, H, d_h, d_r, s, 0.4, "parallel")
+    assert o.max_rel_err(y1, y2) < 1e-12
+    p0 = dict(p, w_o=np.zeros_like(p["w_o"]))
+    assert np.all(o.layer(h, p0, H, d_h, d_r, s, 0.4) == 0)
+
+
+ALL_PINS = [
+    pin_slot_index, pin_block_starts, pin_slot_count, pin_mask_special_cases,
+    pin_mask_structure, pin_mask_matches_incremental_cache, pin_cache_ratio,
+    pin_row_bytes, pin_gate_zero_weights, pin_merge_half_sum, pin_block_start_overwrites,
+    pin_uniform_attention_keyset, pin_absorption, pin_decode_single_slot,
+    pin_s1_equals_causal_sdpa, pin_parallel_equals_incremental,
+    pin_prefill_query_rows, pin_rope, pin_pe, pin_layer_schedules,
+]

@@ -1,0 +1,126 @@
+"""CPU: plant plausible mistakes in the oracle and show the pins catch each one.
+
+Every mutation replaces one oracle function with a subtly wrong variant (an
+off-by-one key set, a missing block reset, a dropped rope term, a transposed
+operand, a wrong scale, ...).  The pin suite must fail for every mutation; if a
+mutation survived, the pins would not be strong enough to trust the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import mtla as O
+from tests import oracle_pins as pins
+
+
+def _visible_keys_block_starts(i, s):
+    # completed slots read at the first token of each block instead of the last
+    return [s * (b - 1) + 1 for b in range(1, O.slot_of(i, s))] + [i]
+
+
+def _visible_keys_off_by_one(i, s):
+    return [s * b for b in range(1, O.slot_of(i, s) - 1)] + [i]
+
+
+def _visible_keys_no_diag(i, s):
+    ks = [s * b for b in range(1, O.slot_of(i, s))]
+    return ks if ks else [i]
+
+
+def _opens_slot_wrong(t, s):
+    return t % s == 0
+
+
+def _slot_of_floor(t, s):
+    return t // s + 1
+
+
+def _partial_merges_no_reset(x, w, s):
+    x = np.asarray(x, dtype=float)
+    return np.cumsum(w[:, None] * x, axis=0)
+
+
+def _append_token_always_add(cache, x_t, w_t, t, s):
+    b = O.slot_of(t, s)
+    cache[b - 1] = cache[b - 1] + w_t * np.asarray(x_t, dtype=float)
+
+
+def _decode_absorbed_no_rope(q_c, q_r, slots, w_uk, w_uv, d_c, scale):
+    return _ORIG["decode_absorbed"](q_c, np.zeros_like(np.asarray(q_r, dtype=float)), slots, w_uk, w_uv, d_c, scale)
+
+
+def _decode_absorbed_uv_from_uk(q_c, q_r, slots, w_uk, w_uv, d_c, scale):
+    return _ORIG["decode_absorbed"](q_c, q_r, slots, w_uk, w_uk, d_c, scale)
+
+
+def _decode_absorbed_scale_sq(q_c, q_r, slots, w_uk, w_uv, d_c, scale):
+    return _ORIG["decode_absorbed"](q_c, q_r, slots, w_uk, w_uv, d_c, scale * scale)
+
+
+def _gate_product(c, pe, w_hyp):
+    return O.sigmoid((np.asarray(c) * np.asarray(pe)) @ np.asarray(w_hyp))
+
+
+def _gate_no_pe(c, pe, w_hyp):
+    return O.sigmoid(np.asarray(c, dtype=float) @ np.asarray(w_hyp, dtype=float))
+
+
+def _softmax_no_max(z):
+    e = np.exp(np.asarray(z, dtype=float))
+    return e / e.sum(axis=-1, keepdims=True) * 0.999
+
+
+def _rope_sign(x, p):
+    return _ORIG["rope"](x, -p) if p else np.asarray(x, dtype=float) * 1.0
+
+
+def _pe_swapped(n, d):
+    pe = _ORIG["sinusoidal_pe"](n, d)
+    return pe[:, ::-1].copy()
+
+
+def _cache_elements_floor(n, s, d_c, d_r):
+    from fractions import Fraction
+    return Fraction((n // s) * (d_c + d_r), n)
+
+
+def _row_bytes_no_rope(d_c, d_r, e):
+    return d_c * e
+
+
+_ORIG = {name: getattr(O, name) for name in
+         ("decode_absorbed", "rope", "sinusoidal_pe")}
+
+MUTATIONS = {
+    "visible_keys": [_visible_keys_block_starts, _visible_keys_off_by_one, _visible_keys_no_diag],
+    "opens_slot": [_opens_slot_wrong],
+    "slot_of": [_slot_of_floor],
+    "partial_merges": [_partial_merges_no_reset],
+    "append_token": [_append_token_always_add],
+    "decode_absorbed": [_decode_absorbed_no_rope, _decode_absorbed_uv_from_uk, _decode_absorbed_scale_sq],
+    "gate": [_gate_product, _gate_no_pe],
+    "softmax": [_softmax_no_max],
+    "rope": [_rope_sign],
+    "sinusoidal_pe": [_pe_swapped],
+    "cache_elements_per_token": [_cache_elements_floor],
+    "cache_row_bytes": [_row_bytes_no_rope],
+}
+
+CASES = [(name, fn) for name, fns in MUTATIONS.items() for fn in fns]
+
+
+def _pins_fail(o):
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError, IndexError) as e:  # a pin caught it
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name,fn", CASES, ids=[f"{n}:{f.__name__}" for n, f in CASES])
+def test_mutation_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    failed = _pins_fail(O)
+    assert failed, f"mutation {fn.__name__} of {name} survived every pin"
