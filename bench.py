@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Benchmark of the MTLA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload (the JSON line's ``value``): speech-translation-shaped
+decoding, batch 50 (10 sentences x beam 5), 512 tokens, H=8, d_h=64, d_c=256,
+d_R=32, s=2, bf16 storage.  One step is the whole 512-token decode of the
+batch: for every token, mtla_merge_append (gate + temporal merge) then
+mtla_decode (absorb, latent attention over ceil(t/s) slots, up-projection).
+The 512 x 4 kernel launches of a step are captured once in a HIP graph and
+replayed; inputs are resident in HBM before the timed region.
+
+The other workloads are reported in ``components``: the s=4 decode loop
+(2048 tokens), the summarisation-shaped prefill (B=16, N=4096, s=3) and the
+LLM-scale step (B=64, cache of 32,768 tokens, one append + decode).
+
+``roofline`` describes the dominant kernel of the headline step, the latent
+attention (mtla_decode_attention), timed live with HIP events on its own
+graph of the same 512 launches.  ``cpu_baseline`` is the fp64 oracle (test
+infrastructure, single-threaded) timed on this host over the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "MTLA decode tokens/s + HBM GB/s (s=2,4); stride-masked prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--no-components", action="store_true", help="headline workload only")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default=None,
+                   help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, llm_decode)")
+    return p.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def to_dev(x, dtype, torch):
+    return torch.from_numpy(x).to("cuda").to(dtype)
+
+
+def timed_graph(g, reps, torch):
+    """Average ms of `reps` replays of graph g, HIP events on torch's stream."""
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def capture(fn, torch):
+    fn()  # eager run first: loads code objects, checks arguments
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def slot_reads(n_tokens, s):
+    """sum_{t=1..N} ceil(t/s): slot rows one sequence's decode loop reads."""
+    return sum(-(-t // s) for t in range(1, n_tokens + 1))
+
+
+# ---------------------------------------------------------------------------
+# decode loop (headline and the s=4 component)
+# ---------------------------------------------------------------------------
+
+class DecodeLoop:
+    def __init__(self, w, m, torch, workloads):
+        import numpy as np
+        self.w, self.m, self.torch = w, m, torch
+        B, N, H = w.batch, w.n_tokens, w.heads
+        self.dims = m.make_dims(B, H, w.d_h, w.d_c, w.d_r, w.s, -(-N // w.s), "bf16")
+        d = self.dims
+        lat = workloads.batch_latents(w)                       # c [B, N, d_c], k_r [B, N, d_r]
+        qry = workloads.batch_queries(w)                       # q_c [B, N, H, d_h], q_r
+        wts = workloads.weights(w)
+        bf = torch.bfloat16
+        # per-step slices must be contiguous: stage token-major copies
+        self.c = to_dev(np.ascontiguousarray(lat["c"].transpose(1, 0, 2)[:, :, None]), bf, torch)
+        self.k_r = to_dev(np.ascontiguousarray(lat["k_r"].transpose(1, 0, 2)[:, :, None]), bf, torch)
+        self.q_c = to_dev(np.ascontiguousarray(qry["q_c"].transpose(1, 0, 2, 3)), bf, torch)
+        self.q_r = to_dev(np.ascontiguousarray(qry["q_r"].transpose(1, 0, 2, 3)), bf, torch)
+        self.w_hyp = to_dev(wts["w_hyp"], torch.float32, torch)
+        self.w_uk = to_dev(wts["w_uk"], bf, torch)
+        self.w_uv = to_dev(wts["w_uv"], bf, torch)
+        self.pos = (torch.arange(1, N + 1, dtype=torch.int32, device="cuda")[:, None]
+                    .expand(N, B).contiguous())
+        self.pe = torch.empty(N, w.d_c, dtype=torch.float32, device="cuda")
+        m.mtla_sinusoidal_pe(self.pe)
+        self.cache = torch.zeros(B, d.max_slots, d.width, dtype=bf, device="cuda")
+        self.open_acc = torch.zeros(B, d.width, dtype=torch.float32, device="cuda")
+        self.ws = torch.zeros(m.mtla_decode_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+        self.out = torch.empty(N, B, H, w.d_h, dtype=bf, device="cuda")
+        self.host_inputs = (lat, qry, wts)
+
+    def step(self):
+        m, d = self.m, self.dims
+        for t in range(self.w.n_tokens):
+            m.mtla_merge_append(d, self.pos[t], self.c[t], self.k_r[t], self.w_hyp, self.pe,
+                                self.cache, self.open_acc)
+            m.mtla_decode(d, self.pos[t], self.q_c[t], self.q_r[t], self.w_uk, self.w_uv,
+                          self.cache, self.out[t], self.ws)
+
+    def attention_only(self):
+        """Graph of the step's latent-attention launches alone: the same
+        positions (so the same slot count per launch) and queries, over the
+        cache the loop leaves behind.  Its last slot may hold a later token than
+        the loop's step saw, which changes values, not work."""
+        torch, m, d, w = self.torch, self.m, self.dims, self.w
+        N, B, H = w.n_tokens, w.batch, w.heads
+        q_lat = torch.empty(N, B, H, d.width, dtype=torch.float32, device="cuda")
+        for t in range(N):
+            m.mtla_absorb_query(d, self.q_c[t], self.q_r[t], self.w_uk, q_lat[t])
+        o_lat = torch.empty(N, B, H, d.d_c, dtype=torch.float32, device="cuda")
+        ws = m.decode_attention_workspace(d)
+
+        def fn():
+            for t in range(N):
+                m.mtla_decode_attention(d, self.pos[t], q_lat[t], self.cache, o_lat[t], ws)
+        return capture(fn, torch)
+
+
+def run_decode_loop(w, steps, warmup, m, torch, workloads, with_kernel=True):
+    log(f"{w.name}: staging inputs")
+    t0 = time.time()
+    dl = DecodeLoop(w, m, torch, workloads)
+    log(f"{w.name}: staged in {time.time() - t0:.1f}s; capturing {w.n_tokens} steps")
+    g = capture(dl.step, torch)
+    for _ in range(warmup):
+        g.replay()
+    ms = timed_graph(g, steps, torch)
+    tokens = w.batch * w.n_tokens
+    rec = {"workload": w.name, "ms_per_step": ms, "tokens_per_step": tokens,
+           "tokens_per_s": tokens / (ms * 1e-3), "us_per_token_step": ms * 1e3 / w.n_tokens}
+    # algorithmic bytes of a step: slot rows read + W_UK/W_UV once per token
+    e = 2
+    cache_bytes = w.batch * slot_reads(w.n_tokens, w.s) * w.width * e
+    weight_bytes = w.n_tokens * 2 * w.heads * w.d_h * w.d_c * e
+    rec["step_GBps"] = (cache_bytes + weight_bytes) / (ms * 1e-3) / 1e9
+    if with_kernel:
+        ga = dl.attention_only()
+        for _ in range(warmup):
+            ga.replay()
+        ams = timed_graph(ga, steps, torch) / w.n_tokens
+        per_launch = cache_bytes / w.n_tokens
+        rec["attention_kernel"] = {
+            "name": "decode_mfma_kernel", "avg_launch_us": ams * 1e3,
+            "algorithmic_bytes_per_launch": per_launch,
+            "GBps": per_launch / (ams * 1e-3) / 1e9}
+    return rec, dl
+
+
+# ---------------------------------------------------------------------------
+# prefill component
+# ---------------------------------------------------------------------------
+
+def attended_pairs(N, s):
+    """A(N, s) = sum_{i<=N} ceil(i/s): keys attended, per (sequence, head)."""
+    q, r = divmod(N, s)
+    return s * q * (q + 1) // 2 + r * (q + 1)
+
+
+def run_prefill(w, steps, warmup, m, torch, workloads):
+    log(f"{w.name}: staging inputs")
+    B, N, H = w.batch, w.n_tokens, w.heads
+    d = m.make_dims(B, H, w.d_h, w.d_c, w.d_r, w.s, -(-N // w.s), "bf16")
+    lat, qry, wts = workloads.batch_latents(w), workloads.batch_queries(w), workloads.weights(w)
+    bf = torch.bfloat16
+    c, k_r = to_dev(lat["c"], bf, torch), to_dev(lat["k_r"], bf, torch)
+    q_c, q_r = to_dev(qry["q_c"], bf, torch), to_dev(qry["q_r"], bf, torch)
+    w_hyp = to_dev(wts["w_hyp"], torch.float32, torch)
+    w_uk, w_uv = to_dev(wts["w_uk"], bf, torch), to_dev(wts["w_uv"], bf, torch)
+    pe = torch.empty(N, w.d_c, dtype=torch.float32, device="cuda")
+    m.mtla_sinusoidal_pe(pe)
+    cache = torch.zeros(B, d.max_slots, d.width, dtype=bf, device="cuda")
+    open_acc = torch.zeros(B, d.width, dtype=torch.float32, device="cuda")
+    out = torch.empty(B, N, H, w.d_h, dtype=bf, device="cuda")
+    ws = torch.empty(m.mtla_prefill_workspace_bytes(d, N), dtype=torch.uint8, device="cuda")
+
+    def fn():
+        m.mtla_prefill(d, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_uv, cache, open_acc, out, ws)
+    g = capture(fn, torch)
+    for _ in range(warmup):
+        g.replay()
+    ms = timed_graph(g, steps, torch)
+    A = attended_pairs(N, w.s)
+    f_attn = 2.0 * B * H * A * (2 * w.d_h + w.d_r)
+    f_up = 4.0 * B * N * w.d_c * H * w.d_h
+    return {"workload": w.name, "ms_per_call": ms, "attended_pairs_per_bh": A,
+            "attn_gflop": f_attn / 1e9, "kv_gemm_gflop": f_up / 1e9,
+            "tflops_end_to_end": (f_attn + f_up) / (ms * 1e-3) / 1e12,
+            "attn_tflops_over_end_to_end_time": f_attn / (ms * 1e-3) / 1e12}, (out, q_c, q_r, lat, qry, wts)
+
+
+# ---------------------------------------------------------------------------
+# LLM-scale long-context step
+# ---------------------------------------------------------------------------
+
+def run_llm_decode(w, steps, warmup, m, torch, workloads):
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    B, N, H = w.batch, w.n_tokens, w.heads
+    T = N + 1  # cache of N tokens, then the appended token N+1
+    d = m.make_dims(B, H, w.d_h, w.d_c, w.d_r, w.s, -(-T // w.s), "bf16")
+    bf = torch.bfloat16
+    log(f"{w.name}: generating {B} x {T} latents")
+    t0 = time.time()
+    cache = torch.zeros(B, d.max_slots, d.width, dtype=bf, device="cuda")
+    open_acc = torch.zeros(B, d.width, dtype=torch.float32, device="cuda")
+    pe = torch.empty(T, w.d_c, dtype=torch.float32, device="cuda")
+    m.mtla_sinusoidal_pe(pe)
+    wts = workloads.weights(w)
+    w_hyp = to_dev(wts["w_hyp"], torch.float32, torch)
+    w_uk, w_uv = to_dev(wts["w_uk"], bf, torch), to_dev(wts["w_uv"], bf, torch)
+    c_dev = torch.empty(B, T, w.d_c, dtype=bf, device="cuda")
+    kr_dev = torch.empty(B, T, w.d_r, dtype=bf, device="cuda")
+
+    def gen(b):
+        lat = workloads.latents(w, b, T)
+        return b, lat["c"], lat["k_r"]
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        for b, cc, kk in ex.map(gen, range(B)):
+            c_dev[b].copy_(torch.from_numpy(cc))
+            kr_dev[b].copy_(torch.from_numpy(kk))
+    qry = workloads.batch_queries(w, 1)
+    q_c = to_dev(qry["q_c"][:, 0].copy(), bf, torch)
+    q_r = to_dev(qry["q_r"][:, 0].copy(), bf, torch)
+    log(f"{w.name}: inputs in {time.time() - t0:.1f}s; building the cache")
+    one = torch.ones(B, dtype=torch.int32, device="cuda")
+    m.mtla_merge_append(d, one, c_dev[:, :N].contiguous(), kr_dev[:, :N].contiguous(), w_hyp, pe,
+                        cache, open_acc)
+    pos = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    c_t, kr_t = c_dev[:, N:T].contiguous(), kr_dev[:, N:T].contiguous()
+    out = torch.empty(B, H, w.d_h, dtype=bf, device="cuda")
+    ws = torch.zeros(m.mtla_decode_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+
+    def step():
+        m.mtla_merge_append(d, pos, c_t, kr_t, w_hyp, pe, cache, open_acc)
+        m.mtla_decode(d, pos, q_c, q_r, w_uk, w_uv, cache, out, ws)
+    g = capture(step, torch)
+    reps = max(steps, 20)
+    for _ in range(max(warmup, 5)):
+        g.replay()
+    ms = timed_graph(g, reps, torch)
+    # latent attention alone
+    q_lat = torch.empty(B, H, d.width, dtype=torch.float32, device="cuda")
+    m.mtla_absorb_query(d, q_c, q_r, w_uk, q_lat)
+    o_lat = torch.empty(B, H, d.d_c, dtype=torch.float32, device="cuda")
+    aws = m.decode_attention_workspace(d)
+    ga = capture(lambda: m.mtla_decode_attention(d, pos, q_lat, cache, o_lat, aws), torch)
+    for _ in range(5):
+        ga.replay()
+    ams = timed_graph(ga, reps, torch)
+    n_slots = -(-T // w.s)
+    cache_bytes = B * n_slots * d.width * 2
+    weight_bytes = 2 * H * w.d_h * w.d_c * 2
+    flops = 2.0 * B * H * n_slots * (2 * w.d_c + w.d_r) + 4.0 * B * H * w.d_h * w.d_c
+    rec = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
+           "slots_per_seq": n_slots, "step_GBps": (cache_bytes + weight_bytes) / (ms * 1e-3) / 1e9,
+           "step_frac_hbm": (cache_bytes + weight_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "step_tflops": flops / (ms * 1e-3) / 1e12,
+           "attention_kernel": {"name": "decode_mfma_kernel", "avg_launch_us": ams * 1e3,
+                                "algorithmic_bytes_per_launch": cache_bytes,
+                                "GBps": cache_bytes / (ams * 1e-3) / 1e9,
+                                "frac_hbm": cache_bytes / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    return rec, (out, cache)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the fp64 oracle) and parity of the headline run
+# ---------------------------------------------------------------------------
+
+def cpu_baseline_and_parity(w, dl, torch):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    lat, qry, wts = dl.host_inputs
+    out = dl.out.float().cpu().numpy().transpose(1, 0, 2, 3)   # [B, N, H, d_h]
+    seqs = list(range(w.batch))
+    errs = []
+    with threadpool_limits(1):
+        t0 = time.time()
+        for b in seqs:
+            ref = oracle.incremental(lat["c"][b], lat["k_r"][b], qry["q_c"][b], qry["q_r"][b],
+                                     wts["w_hyp"], wts["w_uk"], wts["w_uv"], w.s, w.softmax_scale)
+            errs.append(oracle.max_rel_err(out[b], ref))
+        dt = time.time() - t0
+    tokens = len(seqs) * w.n_tokens
+    return ({"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+             "sample": f"the whole workload: {len(seqs)} sequences x {w.n_tokens} tokens, fp64 NumPy, "
+                       f"one thread, {dt:.1f} s"},
+            float(max(errs)))
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the MTLA path here is "
+              "single-GPU and no multi-GPU figure is produced.", file=sys.stderr)
+        return 2
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import torch
+    import workloads
+    import temporally_compressed_latent_amd as m
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    W = workloads.WORKLOADS
+    if args.only:
+        fn = {"st_decode_s2": lambda: run_decode_loop(W[1], args.steps, args.warmup, m, torch, workloads)[0],
+              "st_decode_s4": lambda: run_decode_loop(W[2], args.steps, args.warmup, m, torch, workloads)[0],
+              "prefill": lambda: run_prefill(W[3], args.steps, args.warmup, m, torch, workloads)[0],
+              "llm_decode": lambda: run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0]}
+        print(json.dumps(fn[args.only]()), flush=True)
+        return 0
+
+    w = W[1]
+    head, dl = run_decode_loop(w, args.steps, args.warmup, m, torch, workloads)
+    log("headline:", json.dumps(head))
+    comps = {}
+    if not args.no_components:
+        comps["st_decode_b50_n2048_s4"] = run_decode_loop(W[2], args.steps, args.warmup, m, torch, workloads)[0]
+        log("s4:", json.dumps(comps["st_decode_b50_n2048_s4"]))
+        torch.cuda.empty_cache()
+        comps["sum_prefill_b16_n4096_s3"] = run_prefill(W[3], args.steps, args.warmup, m, torch, workloads)[0]
+        log("prefill:", json.dumps(comps["sum_prefill_b16_n4096_s3"]))
+        torch.cuda.empty_cache()
+        comps["llm_decode_b64_n32768_s2"] = run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0]
+        log("llm:", json.dumps(comps["llm_decode_b64_n32768_s2"]))
+    cpu, err = (None, None)
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        cpu, err = cpu_baseline_and_parity(w, dl, torch)
+
+    k = head["attention_kernel"]
+    achieved = k["GBps"]
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded Gaussian latents, rope keys, queries and fan-in-scaled weights",
+        "config": {"workload": w.name, "batch": w.batch, "tokens": w.n_tokens, "heads": w.heads,
+                   "d_h": w.d_h, "d_c": w.d_c, "d_r": w.d_r, "s": w.s,
+                   "tokens_per_step": head["tokens_per_step"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": k["name"], "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "avg_launch_us": k["avg_launch_us"],
+                     "algorithmic_bytes_per_launch": k["algorithmic_bytes_per_launch"]},
+        "cpu_baseline": cpu,
+        "max_rel_err": err,
+        "step_GBps": head["step_GBps"],
+        "components": comps,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

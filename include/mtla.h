@@ -1,0 +1,240 @@
+/*
+ * mtla.h - C ABI of the MI355X (gfx950) Multi-head Temporal Latent Attention
+ * hot path: hyper-network merge into a temporally compressed latent cache,
+ * absorbed-form decode over that cache, and parallel prefill under the
+ * stride-aware causal mask.
+ *
+ * Sources (cited by page title and section):
+ *   "Multi-head Temporal Latent Attention" (wiki summary of the NeurIPS 2025
+ *   paper): Key claims (paper Sec. 4.1 Eq. 13, Sec. 4.2 Fig. 2(c), Sec. 4.3
+ *   Eq. 17, Sec. 6.1) and Method (1)-(3).
+ *   "Multi-Head Latent Attention and Sparse Indexers": "Latent attention
+ *   changes the representation" (absorption algebra).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Indexing: tokens t are 1-based; token t belongs to cache slot ceil(t/s)
+ *   (1-based), stored at row ceil(t/s)-1.  The first token of a block
+ *   ((t-1) mod s == 0) overwrites its slot, later tokens of the block add to
+ *   it, so a cache never needs clearing.
+ * Memory: every tensor argument is a caller-owned DEVICE pointer to a dense,
+ *   row-major array (innermost dimension last, no strides).  Tensors the
+ *   kernels move in 16-byte vectors (cache, q_c, q_r, w_uk, w_uv, out, the
+ *   workspace, and prefill's c and k_r) must start 16-byte aligned; the
+ *   others need only their element alignment (pos, pos0, w_hyp, pe,
+ *   open_acc, gate_out, q_lat, o_lat: 4 bytes; merge_append's c and k_r: the
+ *   storage element size).  The library never allocates, frees or synchronises;
+ *   `stream` is a hipStream_t (NULL = the default stream) and every call only
+ *   enqueues work on it.
+ * dtypes: `dims->dtype` is the storage type of c, k_r, q_c, q_r, w_uk, w_uv,
+ *   the cache and the outputs (fp32 or bf16, round-to-nearest-even).  w_hyp,
+ *   pe and open_acc are always fp32.  Accumulation is always fp32.
+ * Errors: all argument checks run before anything is enqueued; on a failed
+ *   check the call returns a negative mtla_status, enqueues nothing, and
+ *   mtla_last_error() describes the failure.  A kernel launch failure returns
+ *   MTLA_ERR_HIP.  batch == 0 or a zero token count is a no-op returning
+ *   MTLA_OK.  Positions read from device memory cannot be checked on the
+ *   host: a sequence whose position is out of range (t < 1, ceil(t/s) >
+ *   max_slots, or t > pe_rows) is skipped by the merge (nothing written), and
+ *   its decode output is NaN.
+ * Threads: calls are stateless and may be made from several host threads;
+ *   calls that write the same cache concurrently race.
+ */
+#ifndef MTLA_H
+#define MTLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MTLA_OK = 0,
+  MTLA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or shape   */
+  MTLA_ERR_UNSUPPORTED = -2, /* valid but outside the supported dimensions   */
+  MTLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+  MTLA_ERR_HIP = -4          /* the HIP runtime reported a launch failure    */
+} mtla_status;
+
+typedef enum { MTLA_FP32 = 0, MTLA_BF16 = 1 } mtla_dtype;
+
+/* Force the portable (vector-ALU) kernels even where the MFMA kernels apply. */
+#define MTLA_FLAG_PORTABLE 1
+
+typedef struct {
+  int32_t batch;       /* B: sequences                                          */
+  int32_t heads;       /* H: attention heads                                    */
+  int32_t d_h;         /* per-head content width of queries/values              */
+  int32_t d_c;         /* latent width (cached)                                 */
+  int32_t d_r;         /* decoupled-RoPE key width (cached beside the latent)   */
+  int32_t stride_s;    /* s: tokens merged into one cache slot                  */
+  int32_t max_slots;   /* cache rows per sequence                               */
+  int32_t dtype;       /* mtla_dtype of stored tensors                          */
+  float softmax_scale; /* tau applied to scores; 1/sqrt(d_h + d_r) is usual     */
+  int32_t flags;       /* 0, or MTLA_FLAG_PORTABLE                              */
+} mtla_dims;
+
+/* Row width of the cache: W = d_c + d_r elements. */
+
+/* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t mtla_version(void);
+
+/* Static text for a status code. */
+const char* mtla_status_string(int32_t status);
+
+/* Text of the last failure of a call made from this host thread ("" if none). */
+const char* mtla_last_error(void);
+
+/*
+ * Sinusoidal positional-embedding table for the merge gate.
+ *   pe[p, 2k] = sin(p * 10000^(-2k/d)), pe[p, 2k+1] = cos(same), p = 0..rows-1
+ * (row p is used for token t = p+1).  Computed in double, stored fp32.
+ * Page: "Multi-head Temporal Latent Attention", Key claims (paper Sec. 4.1):
+ * the hyper-network is conditioned on the latent plus a positional embedding.
+ *   pe: device [rows, d] fp32, written.  rows >= 1, d >= 1.
+ */
+int32_t mtla_sinusoidal_pe(int32_t rows, int32_t d, float* pe, void* stream);
+
+/*
+ * Merge / append (gate + temporal merge) for n_tokens consecutive tokens of
+ * every sequence.  Page: "Multi-head Temporal Latent Attention", Key claims
+ * (paper Sec. 4.1 Eq. 13) and Method (1):
+ *   w_t = sigmoid(W_hyp . (c_t + pe_t))              (one scalar per token)
+ *   slot ceil(t/s) <- (t opens a block ? 0 : open slot) + w_t [c_t ; k^R_t]
+ * Sequence b appends tokens t = pos0[b] .. pos0[b] + n_tokens - 1.
+ *   pos0     device [B] int32, 1-based position of the first appended token.
+ *   c        device [B, n_tokens, d_c]   storage dtype.
+ *   k_r      device [B, n_tokens, d_r]   storage dtype, RoPE already applied.
+ *   w_hyp    device [d_c] fp32.
+ *   pe       device [pe_rows, d_c] fp32; row t-1 is used for token t.
+ *   cache    device [B, max_slots, d_c + d_r] storage dtype, in/out: every
+ *            slot touched by the appended tokens is written (rounded once from
+ *            the fp32 sum); other rows are untouched.
+ *   open_acc device [B, d_c + d_r] fp32, in/out: the unrounded fp32 value of
+ *            the last slot touched.  Read only when pos0[b] continues a block.
+ *   gate_out device [B, n_tokens] fp32 or NULL: the gates w_t.
+ */
+int32_t mtla_merge_append(const mtla_dims* dims, const int32_t* pos0, int32_t n_tokens,
+                          const void* c, const void* k_r, const float* w_hyp,
+                          const float* pe, int32_t pe_rows, void* cache, float* open_acc,
+                          float* gate_out, void* stream);
+
+/* Bytes of workspace mtla_decode needs for these dims (written to *bytes). */
+int32_t mtla_decode_workspace_bytes(const mtla_dims* dims, size_t* bytes);
+
+/*
+ * Absorbed-form decode of one query per sequence over slots 1..ceil(pos/s).
+ * Pages: "Multi-head Temporal Latent Attention", Method (W_UK absorbed into
+ * the query, W_UV applied after the weighted latent sum; per-token cost
+ * O(N/s), Key claims Sec. 6.1); "Multi-Head Latent Attention and Sparse
+ * Indexers", "Latent attention changes the representation".
+ *   q~_h  = W_UK[h]^T q^C_h                                   (d_h -> d_c)
+ *   z_h,j = tau (q~_h . S^c_j + q^R_h . S^R_j),  j = 1..ceil(pos/s)
+ *   o_h   = W_UV[h] sum_j softmax_j(z_h)_j S^c_j
+ *   pos   device [B] int32: the current token t of each sequence (its slot
+ *         must already hold token t, i.e. merge first).
+ *   q_c   device [B, H, d_h];  q_r device [B, H, d_r] (rotated).
+ *   w_uk, w_uv device [H, d_h, d_c].
+ *   cache device [B, max_slots, d_c + d_r], read only.
+ *   out   device [B, H, d_h], written.
+ *   workspace device, >= mtla_decode_workspace_bytes(); contents undefined
+ *         after the call.
+ * The result is bit-reproducible: split partials are combined in a fixed
+ * order.
+ */
+int32_t mtla_decode(const mtla_dims* dims, const int32_t* pos, const void* q_c,
+                    const void* q_r, const void* w_uk, const void* w_uv, const void* cache,
+                    void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Staged form of mtla_decode, for callers that fuse the two projections into
+ * their own GEMMs (mtla_decode runs exactly these three stages).
+ *
+ * mtla_absorb_query: q_lat[r, h] = [W_UK[h]^T q^C[r, h] ; q^R[r, h]], fp32.
+ * Pages: "Multi-head Temporal Latent Attention", Method (W_UK absorbed into
+ * the query); "Multi-Head Latent Attention and Sparse Indexers", "Latent
+ * attention changes the representation" (q^T (U_K c) = (U_K^T q)^T c).
+ *   q_c device [n_rows, H, d_h], q_r device [n_rows, H, d_r] (storage dtype);
+ *   w_uk device [H, d_h, d_c]; q_lat device [n_rows, H, d_c + d_r] fp32, written.
+ */
+int32_t mtla_absorb_query(const mtla_dims* dims, int32_t n_rows, const void* q_c, const void* q_r,
+                          const void* w_uk, float* q_lat, void* stream);
+
+/* Bytes of workspace mtla_decode_attention needs. */
+int32_t mtla_decode_attention_workspace_bytes(const mtla_dims* dims, size_t* bytes);
+
+/*
+ * Latent-space attention of one absorbed query per sequence over slots
+ * 1..ceil(pos/s):  o_lat[b, h] = sum_j softmax_j(tau q_lat[b, h] . S_j) S^c_j.
+ * Page: "Multi-head Temporal Latent Attention", Method and Key claims
+ * (Sec. 6.1: a query at step t reads ceil(t/s) slots).
+ * With bf16 storage and a supported shape this is a single kernel (MFMA
+ * split-K over slots whose splits are merged, in a fixed order, by the last
+ * workgroup of each sequence).
+ *   pos   device [B] int32; q_lat device [B, H, d_c + d_r] fp32;
+ *   cache device [B, max_slots, d_c + d_r]; o_lat device [B, H, d_c] fp32,
+ *   written.
+ *   workspace: its first bytes hold per-sequence split counters, which must
+ *   be zero the first time a workspace is used (allocate it zero-filled);
+ *   every call leaves them zero again.  The rest is scratch.
+ */
+int32_t mtla_decode_attention(const mtla_dims* dims, const int32_t* pos, const float* q_lat,
+                              const void* cache, float* o_lat, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * mtla_up_project: out[r, h] = W_UV[h] o_lat[r, h] (rounded to storage).
+ * Page: "Multi-Head Latent Attention and Sparse Indexers", "Latent attention
+ * changes the representation" (sum_j a_j U_V c_j = U_V sum_j a_j c_j).
+ *   o_lat device [n_rows, H, d_c] fp32; w_uv device [H, d_h, d_c];
+ *   out device [n_rows, H, d_h], written.
+ */
+int32_t mtla_up_project(const mtla_dims* dims, int32_t n_rows, const float* o_lat,
+                        const void* w_uv, void* out, void* stream);
+
+/* Bytes of workspace mtla_prefill needs for n_tokens tokens. */
+int32_t mtla_prefill_workspace_bytes(const mtla_dims* dims, int32_t n_tokens, size_t* bytes);
+
+/*
+ * Parallel prefill of tokens 1..n_tokens of every sequence under the
+ * stride-aware causal mask.  Page: "Multi-head Temporal Latent Attention",
+ * Key claims (paper Sec. 4.2 Fig. 2(c); Sec. 4.3 Eq. 17) and Method (2)-(3):
+ *   P_j = sum_{k = s*floor((j-1)/s)+1}^{j} w_k x_k   (cumulative in-block merges)
+ *   query i attends key j iff j == i, or s | j and j/s < ceil(i/s);
+ *   K^C_j,h = W_UK[h] P^c_j,  V_j,h = W_UV[h] P^c_j,  rope key P^R_j;
+ *   o_i,h = sum_j softmax_j(tau (q^C_i,h . K^C_j,h + q^R_i,h . P^R_j)) V_j,h.
+ * Its output equals token-by-token decoding (merge then decode per token).
+ *   q_c device [B, N, H, d_h]; q_r device [B, N, H, d_r].
+ *   c   device [B, N, d_c];    k_r device [B, N, d_r].
+ *   w_hyp, pe, pe_rows: as for mtla_merge_append (pe_rows >= N).
+ *   w_uk, w_uv device [H, d_h, d_c].
+ *   cache device [B, max_slots, d_c + d_r], written: slots 1..ceil(N/s).
+ *   open_acc device [B, d_c + d_r] fp32, written: fp32 value of slot ceil(N/s),
+ *         so that decoding can continue at token N+1.
+ *   out device [B, N, H, d_h], written.
+ *   N <= s * max_slots.
+ */
+int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, const void* q_r,
+                     const void* c, const void* k_r, const float* w_hyp, const float* pe,
+                     int32_t pe_rows, const void* w_uk, const void* w_uv, void* cache,
+                     float* open_acc, void* out, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * Test hooks: the integer predicates the kernels use, exported for bit-exact
+ * comparison.  Page: "Multi-head Temporal Latent Attention", Key claims (paper
+ * Sec. 4.2 Fig. 2(c)).
+ *   mask device [n, n] uint8: mask[i-1, j-1] = 1 iff query i attends key j.
+ *   hi   device [n] int32: hi[i-1] = completed slots query i attends,
+ *        floor((i-1)/s).
+ */
+int32_t mtla_debug_stride_mask(int32_t n, int32_t s, uint8_t* mask, void* stream);
+int32_t mtla_debug_slot_limits(int32_t n, int32_t s, int32_t* hi, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTLA_H */

@@ -1,0 +1,16 @@
+"""MI355X-native MTLA hot path: merge/append into a temporally compressed
+latent cache, absorbed-form decode, and stride-masked parallel prefill.
+
+The compute runs in libmtla.so (hand-written HIP kernels for gfx950 behind a
+C ABI, declared in include/mtla.h).  This package is its thin binding; torch
+is used only for device memory and streams.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH, MTLA_BF16, MTLA_ERR_HIP, MTLA_ERR_INVALID_ARG, MTLA_ERR_UNSUPPORTED,
+    MTLA_ERR_WORKSPACE, MTLA_FLAG_PORTABLE, MTLA_FP32, MTLA_OK, MtlaDims, MtlaError,
+    decode_attention_workspace, header_symbols, last_error, lib, make_dims, mtla_absorb_query,
+    mtla_debug_slot_limits, mtla_debug_stride_mask, mtla_decode, mtla_decode_attention,
+    mtla_decode_attention_workspace_bytes, mtla_decode_workspace_bytes, mtla_merge_append,
+    mtla_prefill, mtla_prefill_workspace_bytes, mtla_sinusoidal_pe, mtla_up_project,
+    mtla_version, status_string,
+)

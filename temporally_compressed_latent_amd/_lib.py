@@ -1,0 +1,314 @@
+"""ctypes binding of libmtla.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of the method: it checks that the torch tensors it is given match
+the shapes, dtypes and devices the C ABI expects (the C library cannot see
+tensor sizes), then passes raw device pointers and the current HIP stream.
+
+If the library is missing this module raises at import time: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("MTLA_LIB", os.path.join(_PKG, "libmtla.so"))
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "mtla.h")
+
+MTLA_OK = 0
+MTLA_ERR_INVALID_ARG = -1
+MTLA_ERR_UNSUPPORTED = -2
+MTLA_ERR_WORKSPACE = -3
+MTLA_ERR_HIP = -4
+MTLA_FP32 = 0
+MTLA_BF16 = 1
+MTLA_FLAG_PORTABLE = 1
+
+
+class MtlaDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("d_h", ctypes.c_int32),
+        ("d_c", ctypes.c_int32),
+        ("d_r", ctypes.c_int32),
+        ("stride_s", ctypes.c_int32),
+        ("max_slots", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("flags", ctypes.c_int32),
+    ]
+
+    @property
+    def width(self) -> int:
+        return self.d_c + self.d_r
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == MTLA_FP32 else torch.bfloat16
+
+    def copy(self, **kw) -> "MtlaDims":
+        d = MtlaDims()
+        for name, _ in self._fields_:
+            setattr(d, name, kw.get(name, getattr(self, name)))
+        return d
+
+
+class MtlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m temporally_compressed_latent_amd.build` "
+            "(the MTLA path has no CPU fallback)")
+    return ctypes.CDLL(LIB_PATH)
+
+
+_lib = _load()
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_D = ctypes.POINTER(MtlaDims)
+
+_SIGS = {
+    "mtla_version": (_I, []),
+    "mtla_status_string": (ctypes.c_char_p, [_I]),
+    "mtla_last_error": (ctypes.c_char_p, []),
+    "mtla_sinusoidal_pe": (_I, [_I, _I, _P, _P]),
+    "mtla_merge_append": (_I, [_D, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
+    "mtla_decode_workspace_bytes": (_I, [_D, ctypes.POINTER(_SZ)]),
+    "mtla_decode": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mtla_absorb_query": (_I, [_D, _I, _P, _P, _P, _P, _P]),
+    "mtla_decode_attention_workspace_bytes": (_I, [_D, ctypes.POINTER(_SZ)]),
+    "mtla_decode_attention": (_I, [_D, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mtla_up_project": (_I, [_D, _I, _P, _P, _P, _P]),
+    "mtla_prefill_workspace_bytes": (_I, [_D, _I, ctypes.POINTER(_SZ)]),
+    "mtla_prefill": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mtla_debug_stride_mask": (_I, [_I, _I, _P, _P]),
+    "mtla_debug_slot_limits": (_I, [_I, _I, _P, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def header_symbols() -> list:
+    """Entry points declared in include/mtla.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(mtla_[a-z_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return _lib.mtla_status_string(status).decode()
+
+
+def last_error() -> str:
+    return _lib.mtla_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != MTLA_OK:
+        raise MtlaError(status, last_error())
+
+
+def mtla_version() -> int:
+    return _lib.mtla_version()
+
+
+def make_dims(batch: int, heads: int, d_h: int, d_c: int, d_r: int, s: int, max_slots: int,
+              dtype="bf16", softmax_scale: Optional[float] = None, portable: bool = False) -> MtlaDims:
+    d = MtlaDims()
+    d.batch, d.heads, d.d_h, d.d_c, d.d_r = batch, heads, d_h, d_c, d_r
+    d.stride_s, d.max_slots = s, max_slots
+    d.dtype = {"fp32": MTLA_FP32, "bf16": MTLA_BF16, torch.float32: MTLA_FP32,
+               torch.bfloat16: MTLA_BF16}[dtype]
+    d.softmax_scale = 1.0 / math.sqrt(d_h + d_r) if softmax_scale is None else softmax_scale
+    d.flags = MTLA_FLAG_PORTABLE if portable else 0
+    return d
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _tensor(name: str, t, shape, dtype, optional: bool = False) -> Optional[int]:
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr() if t.numel() else None
+
+
+def _ws(name: str, t, need: int) -> tuple:
+    if t is None:
+        return None, 0
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return t.data_ptr(), t.numel() * t.element_size()
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def mtla_sinusoidal_pe(pe: torch.Tensor, stream=None) -> None:
+    rows, d = pe.shape
+    p = _tensor("pe", pe, (rows, d), torch.float32)
+    _check(_lib.mtla_sinusoidal_pe(rows, d, p, _stream(stream)))
+
+
+def mtla_merge_append(dims: MtlaDims, pos0, c, k_r, w_hyp, pe, cache, open_acc,
+                      gate_out=None, stream=None) -> None:
+    B, W, T = dims.batch, dims.width, int(c.shape[1]) if c.dim() == 3 else -1
+    st = dims.torch_dtype
+    args = (
+        _tensor("pos0", pos0, (B,), torch.int32),
+        _tensor("c", c, (B, T, dims.d_c), st),
+        _tensor("k_r", k_r, (B, T, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32),
+        _tensor("cache", cache, (B, dims.max_slots, W), st),
+        _tensor("open_acc", open_acc, (B, W), torch.float32),
+        _tensor("gate_out", gate_out, (B, T), torch.float32, optional=True),
+    )
+    _check(_lib.mtla_merge_append(ctypes.byref(dims), args[0], T, args[1], args[2], args[3],
+                                  args[4], int(pe.shape[0]), args[5], args[6], args[7],
+                                  _stream(stream)))
+
+
+def mtla_decode_workspace_bytes(dims: MtlaDims) -> int:
+    n = _SZ(0)
+    _check(_lib.mtla_decode_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def mtla_decode(dims: MtlaDims, pos, q_c, q_r, w_uk, w_uv, cache, out, workspace,
+                stream=None) -> None:
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    _check(_lib.mtla_decode(
+        ctypes.byref(dims),
+        _tensor("pos", pos, (B,), torch.int32),
+        _tensor("q_c", q_c, (B, H, dims.d_h), st),
+        _tensor("q_r", q_r, (B, H, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("out", out, (B, H, dims.d_h), st),
+        ws, ws_bytes, _stream(stream)))
+
+
+def mtla_absorb_query(dims: MtlaDims, q_c, q_r, w_uk, q_lat, stream=None) -> None:
+    R, H, st = int(q_c.shape[0]), dims.heads, dims.torch_dtype
+    _check(_lib.mtla_absorb_query(
+        ctypes.byref(dims), R,
+        _tensor("q_c", q_c, (R, H, dims.d_h), st),
+        _tensor("q_r", q_r, (R, H, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("q_lat", q_lat, (R, H, dims.width), torch.float32), _stream(stream)))
+
+
+def mtla_decode_attention_workspace_bytes(dims: MtlaDims) -> int:
+    n = _SZ(0)
+    _check(_lib.mtla_decode_attention_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def mtla_decode_attention(dims: MtlaDims, pos, q_lat, cache, o_lat, workspace, stream=None) -> None:
+    B, H = dims.batch, dims.heads
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    _check(_lib.mtla_decode_attention(
+        ctypes.byref(dims),
+        _tensor("pos", pos, (B,), torch.int32),
+        _tensor("q_lat", q_lat, (B, H, dims.width), torch.float32),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), dims.torch_dtype),
+        _tensor("o_lat", o_lat, (B, H, dims.d_c), torch.float32),
+        ws, ws_bytes, _stream(stream)))
+
+
+def mtla_up_project(dims: MtlaDims, o_lat, w_uv, out, stream=None) -> None:
+    R, H, st = int(o_lat.shape[0]), dims.heads, dims.torch_dtype
+    _check(_lib.mtla_up_project(
+        ctypes.byref(dims), R,
+        _tensor("o_lat", o_lat, (R, H, dims.d_c), torch.float32),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("out", out, (R, H, dims.d_h), st), _stream(stream)))
+
+
+def decode_attention_workspace(dims: MtlaDims) -> torch.Tensor:
+    """A zero-filled workspace for mtla_decode_attention (its split counters
+    must start at zero; every call leaves them zero)."""
+    return torch.zeros(mtla_decode_attention_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+
+
+def mtla_prefill_workspace_bytes(dims: MtlaDims, n_tokens: int) -> int:
+    n = _SZ(0)
+    _check(_lib.mtla_prefill_workspace_bytes(ctypes.byref(dims), n_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def mtla_prefill(dims: MtlaDims, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_uv, cache, open_acc,
+                 out, workspace, stream=None) -> None:
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    N = int(c.shape[1]) if c.dim() == 3 else -1
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    _check(_lib.mtla_prefill(
+        ctypes.byref(dims), N,
+        _tensor("q_c", q_c, (B, N, H, dims.d_h), st),
+        _tensor("q_r", q_r, (B, N, H, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("c", c, (B, N, dims.d_c), st),
+        _tensor("k_r", k_r, (B, N, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("open_acc", open_acc, (B, dims.width), torch.float32),
+        _tensor("out", out, (B, N, H, dims.d_h), st),
+        ws, ws_bytes, _stream(stream)))
+
+
+def mtla_debug_stride_mask(n: int, s: int, mask, stream=None) -> None:
+    _check(_lib.mtla_debug_stride_mask(n, s, _tensor("mask", mask, (n, n), torch.uint8),
+                                       _stream(stream)))
+
+
+def mtla_debug_slot_limits(n: int, s: int, hi, stream=None) -> None:
+    _check(_lib.mtla_debug_slot_limits(n, s, _tensor("hi", hi, (n,), torch.int32),
+                                       _stream(stream)))

@@ -1,0 +1,446 @@
+// C ABI of the MTLA hot path: argument validation, workspace sizing and
+// kernel dispatch.  Every check runs before anything is enqueued; no HIP API
+// is called on a failed check.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/mtla.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int32_t ok() {
+  g_err[0] = '\0';
+  return MTLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+constexpr int kMaxS = 256;
+constexpr int kMaxWidth = 1024;
+constexpr int kMaxDh = 256;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+int32_t check_dims(const mtla_dims* d) {
+  if (!d) return fail(MTLA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->batch < 0) return fail(MTLA_ERR_INVALID_ARG, "batch=%d < 0", d->batch);
+  if (d->heads < 1) return fail(MTLA_ERR_INVALID_ARG, "heads=%d < 1", d->heads);
+  if (d->d_h < 1) return fail(MTLA_ERR_INVALID_ARG, "d_h=%d < 1", d->d_h);
+  if (d->d_c < 1) return fail(MTLA_ERR_INVALID_ARG, "d_c=%d < 1", d->d_c);
+  if (d->d_r < 0) return fail(MTLA_ERR_INVALID_ARG, "d_r=%d < 0", d->d_r);
+  if (d->stride_s < 1) return fail(MTLA_ERR_INVALID_ARG, "stride_s=%d < 1", d->stride_s);
+  if (d->max_slots < 1) return fail(MTLA_ERR_INVALID_ARG, "max_slots=%d < 1", d->max_slots);
+  if (d->dtype != MTLA_FP32 && d->dtype != MTLA_BF16)
+    return fail(MTLA_ERR_INVALID_ARG, "dtype=%d is neither MTLA_FP32 nor MTLA_BF16", d->dtype);
+  if (!(isfinite(d->softmax_scale) && d->softmax_scale > 0.f))
+    return fail(MTLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (d->flags & ~MTLA_FLAG_PORTABLE) return fail(MTLA_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
+  if (d->stride_s > kMaxS) return fail(MTLA_ERR_UNSUPPORTED, "stride_s=%d > %d", d->stride_s, kMaxS);
+  if (d->d_c + d->d_r > kMaxWidth)
+    return fail(MTLA_ERR_UNSUPPORTED, "d_c + d_r = %d > %d", d->d_c + d->d_r, kMaxWidth);
+  if (d->d_h > kMaxDh) return fail(MTLA_ERR_UNSUPPORTED, "d_h=%d > %d", d->d_h, kMaxDh);
+  if ((8 * int64_t(d->d_c) + int64_t(d->d_h) * 65) * 4 > 65536)
+    return fail(MTLA_ERR_UNSUPPORTED, "d_c=%d with d_h=%d exceeds the up-projection kernel's LDS", d->d_c, d->d_h);
+  const int64_t W = d->d_c + d->d_r;
+  if (int64_t(d->batch) * d->max_slots * W > kMaxElems)
+    return fail(MTLA_ERR_UNSUPPORTED, "cache of %lld elements is too large",
+                static_cast<long long>(int64_t(d->batch) * d->max_slots * W));
+  return MTLA_OK;
+}
+
+#define CHECK_PTR(p)                                                                   \
+  do {                                                                                 \
+    if (!(p)) return fail(MTLA_ERR_INVALID_ARG, "%s is NULL", #p);                     \
+    if (!aligned16(p)) return fail(MTLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+// Pointers only read or written element by element need their element
+// alignment; tensors that kernels move in 16-byte vectors need 16 bytes.
+#define CHECK_PTR_ALIGN(p, n)                                                          \
+  do {                                                                                 \
+    if (!(p)) return fail(MTLA_ERR_INVALID_ARG, "%s is NULL", #p);                     \
+    if (!aligned_to(p, n)) return fail(MTLA_ERR_INVALID_ARG, "%s is not %d-byte aligned", #p, n); \
+  } while (0)
+
+#define CHECK_OPT_PTR_ALIGN(p, n)                                                      \
+  do {                                                                                 \
+    if ((p) && !aligned_to(p, n))                                                      \
+      return fail(MTLA_ERR_INVALID_ARG, "%s is not %d-byte aligned", #p, n);           \
+  } while (0)
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MTLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+size_t elem_bytes(const mtla_dims* d) { return d->dtype == MTLA_FP32 ? 4 : 2; }
+
+bool decode_fast(const mtla_dims* d) {
+  return d->dtype == MTLA_BF16 && !(d->flags & MTLA_FLAG_PORTABLE) &&
+         mtla::decode_mfma_supported(d->heads, d->d_c, d->d_r);
+}
+
+bool prefill_fast(const mtla_dims* d) {
+  return d->dtype == MTLA_BF16 && !(d->flags & MTLA_FLAG_PORTABLE) &&
+         mtla::prefill_mfma_supported(d->heads, d->d_h, d->d_c, d->d_r);
+}
+
+int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Splits of the slot range.  The MFMA kernel aims at ~2 workgroups per CU
+// (256 CUs) with at least one 64-slot tile per split; the portable kernel
+// gives each split ~128 slots.
+int decode_splits(const mtla_dims* d) {
+  if (decode_fast(d)) {
+    const int want = ceil_div(512, d->batch > 0 ? d->batch : 1);
+    return clampi(want, 1, clampi(ceil_div(d->max_slots, 64), 1, 64));
+  }
+  return clampi(ceil_div(d->max_slots, 128), 1, 32);
+}
+
+int prefill_splits(const mtla_dims* d, int n_tokens) {
+  return clampi(ceil_div(n_tokens / d->stride_s + 1, 128), 1, 16);
+}
+
+// Workspace of the latent attention: split counters first (zero on entry,
+// left zero), then the split partials.
+struct AttnWs {
+  size_t counters, pm, pl, pacc, total;
+};
+
+AttnWs attn_ws(const mtla_dims* d, size_t rows, int splits, size_t off) {
+  const size_t H = d->heads, S = splits;
+  AttnWs w;
+  w.counters = off;
+  w.pm = w.counters + align_up(rows * 4);
+  w.pl = w.pm + align_up(rows * S * H * 4);
+  w.pacc = w.pl + align_up(rows * S * H * 4);
+  w.total = w.pacc + align_up(rows * S * H * d->d_c * 4);
+  return w;
+}
+
+struct DecodeWs {
+  size_t qlat, olat;
+  AttnWs attn;
+  size_t total;
+};
+
+DecodeWs decode_ws(const mtla_dims* d) {
+  const size_t B = d->batch, H = d->heads, W = d->d_c + d->d_r;
+  DecodeWs w;
+  w.qlat = 0;
+  w.olat = w.qlat + align_up(B * H * W * 4);
+  w.attn = attn_ws(d, B, decode_splits(d), w.olat + align_up(B * H * d->d_c * 4));
+  w.total = w.attn.total;
+  return w;
+}
+
+struct PrefillWs {
+  size_t P, kc, v, qlat, olat;
+  AttnWs attn;
+  size_t total;
+};
+
+PrefillWs prefill_ws(const mtla_dims* d, int n) {
+  const size_t B = d->batch, H = d->heads, W = d->d_c + d->d_r, N = n;
+  const size_t e = elem_bytes(d);
+  PrefillWs w{};
+  w.P = 0;
+  size_t off = align_up(B * N * W * e);
+  if (prefill_fast(d)) {
+    w.kc = off;
+    off += align_up(B * H * N * d->d_h * e);
+    w.v = off;
+    off += align_up(B * H * N * d->d_h * e);
+    w.total = off;
+  } else {
+    const size_t R = B * N;
+    w.qlat = off;
+    off += align_up(R * H * W * 4);
+    w.olat = off;
+    off += align_up(R * H * d->d_c * 4);
+    w.attn = attn_ws(d, R, prefill_splits(d, n), off);
+    w.total = w.attn.total;
+  }
+  return w;
+}
+
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t mtla_version(void) { return 10000; }
+
+const char* mtla_status_string(int32_t s) {
+  switch (s) {
+    case MTLA_OK: return "MTLA_OK";
+    case MTLA_ERR_INVALID_ARG: return "MTLA_ERR_INVALID_ARG";
+    case MTLA_ERR_UNSUPPORTED: return "MTLA_ERR_UNSUPPORTED";
+    case MTLA_ERR_WORKSPACE: return "MTLA_ERR_WORKSPACE";
+    case MTLA_ERR_HIP: return "MTLA_ERR_HIP";
+    default: return "MTLA_UNKNOWN_STATUS";
+  }
+}
+
+const char* mtla_last_error(void) { return g_err; }
+
+int32_t mtla_sinusoidal_pe(int32_t rows, int32_t d, float* pe, void* stream) {
+  if (rows < 1 || d < 1) return fail(MTLA_ERR_INVALID_ARG, "rows=%d, d=%d must be >= 1", rows, d);
+  if (int64_t(rows) * d > kMaxElems) return fail(MTLA_ERR_UNSUPPORTED, "table too large");
+  CHECK_PTR_ALIGN(pe, 4);
+  return hip_status(mtla::launch_sinusoidal_pe(rows, d, pe, static_cast<hipStream_t>(stream)),
+                    "sinusoidal_pe launch");
+}
+
+int32_t mtla_merge_append(const mtla_dims* dims, const int32_t* pos0, int32_t n_tokens,
+                          const void* c, const void* k_r, const float* w_hyp, const float* pe,
+                          int32_t pe_rows, void* cache, float* open_acc, float* gate_out,
+                          void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
+  if (pe_rows < 1) return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < 1", pe_rows);
+  if (n_tokens > pe_rows)
+    return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d exceeds pe_rows=%d", n_tokens, pe_rows);
+  if (int64_t(n_tokens) > int64_t(dims->max_slots) * dims->stride_s)
+    return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d exceeds the cache capacity s*max_slots", n_tokens);
+  if (dims->batch == 0 || n_tokens == 0) return ok();
+  CHECK_PTR_ALIGN(pos0, 4);
+  CHECK_PTR_ALIGN(c, static_cast<int>(elem_bytes(dims)));
+  if (dims->d_r > 0) CHECK_PTR_ALIGN(k_r, static_cast<int>(elem_bytes(dims)));
+  CHECK_PTR_ALIGN(w_hyp, 4);
+  CHECK_PTR_ALIGN(pe, 4);
+  CHECK_PTR(cache);
+  CHECK_PTR_ALIGN(open_acc, 4);
+  CHECK_OPT_PTR_ALIGN(gate_out, 4);
+  mtla::MergeArgs a{dims->batch, n_tokens, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots,
+                    pe_rows, pos0, c, k_r, w_hyp, pe, cache, open_acc, gate_out, nullptr};
+  return hip_status(mtla::launch_merge(a, dims->dtype, static_cast<hipStream_t>(stream)),
+                    "merge launch");
+}
+
+int32_t mtla_absorb_query(const mtla_dims* dims, int32_t n_rows, const void* q_c, const void* q_r,
+                          const void* w_uk, float* q_lat, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (n_rows < 0) return fail(MTLA_ERR_INVALID_ARG, "n_rows=%d < 0", n_rows);
+  if (n_rows == 0) return ok();
+  CHECK_PTR(q_c);
+  if (dims->d_r > 0) CHECK_PTR(q_r);
+  CHECK_PTR(w_uk);
+  CHECK_PTR_ALIGN(q_lat, 4);
+  return hip_status(mtla::launch_absorb(n_rows, dims->heads, dims->d_h, dims->d_c, dims->d_r, q_c,
+                                        q_r, w_uk, q_lat, nullptr, 0, dims->dtype,
+                                        static_cast<hipStream_t>(stream)),
+                    "absorb launch");
+}
+
+int32_t mtla_up_project(const mtla_dims* dims, int32_t n_rows, const float* o_lat,
+                        const void* w_uv, void* out, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (n_rows < 0) return fail(MTLA_ERR_INVALID_ARG, "n_rows=%d < 0", n_rows);
+  if (n_rows == 0) return ok();
+  CHECK_PTR_ALIGN(o_lat, 4);
+  CHECK_PTR(w_uv);
+  CHECK_PTR(out);
+  return hip_status(mtla::launch_up_project(n_rows, dims->heads, dims->d_h, dims->d_c, o_lat, w_uv,
+                                            out, dims->dtype, static_cast<hipStream_t>(stream)),
+                    "up-projection launch");
+}
+
+int32_t mtla_decode_attention_workspace_bytes(const mtla_dims* dims, size_t* bytes) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (!bytes) return fail(MTLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = attn_ws(dims, dims->batch, decode_splits(dims), 0).total;
+  return ok();
+}
+
+namespace {
+
+hipError_t run_decode_attention(const mtla_dims* dims, const int32_t* pos, const float* q_lat,
+                                const void* cache, float* o_lat, void* ws, const AttnWs& w,
+                                hipStream_t s) {
+  const int splits = decode_splits(dims);
+  mtla::Partials p{reinterpret_cast<float*>(at(ws, w.pm)), reinterpret_cast<float*>(at(ws, w.pl)),
+                   reinterpret_cast<float*>(at(ws, w.pacc))};
+  mtla::AttendArgs a{dims->batch, 0, dims->heads, dims->d_c, dims->d_r, dims->stride_s,
+                     dims->max_slots, splits, dims->softmax_scale, pos, q_lat, cache, nullptr, p,
+                     o_lat, reinterpret_cast<int32_t*>(at(ws, w.counters))};
+  return decode_fast(dims) ? mtla::launch_decode_mfma(a, s)
+                           : mtla::launch_attend_portable(a, dims->dtype, s);
+}
+
+}  // namespace
+
+int32_t mtla_decode_attention(const mtla_dims* dims, const int32_t* pos, const float* q_lat,
+                              const void* cache, float* o_lat, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (dims->batch == 0) return ok();
+  CHECK_PTR_ALIGN(pos, 4);
+  CHECK_PTR_ALIGN(q_lat, 4);
+  CHECK_PTR(cache);
+  CHECK_PTR_ALIGN(o_lat, 4);
+  const AttnWs w = attn_ws(dims, dims->batch, decode_splits(dims), 0);
+  if (!workspace) return fail(MTLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", w.total);
+  if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (ws_bytes < w.total)
+    return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, w.total);
+  return hip_status(run_decode_attention(dims, pos, q_lat, cache, o_lat, workspace, w,
+                                         static_cast<hipStream_t>(stream)),
+                    "decode attention launch");
+}
+
+int32_t mtla_decode_workspace_bytes(const mtla_dims* dims, size_t* bytes) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (!bytes) return fail(MTLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = decode_ws(dims).total;
+  return ok();
+}
+
+int32_t mtla_decode(const mtla_dims* dims, const int32_t* pos, const void* q_c, const void* q_r,
+                    const void* w_uk, const void* w_uv, const void* cache, void* out,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (dims->batch == 0) return ok();
+  CHECK_PTR_ALIGN(pos, 4);
+  CHECK_PTR(q_c);
+  if (dims->d_r > 0) CHECK_PTR(q_r);
+  CHECK_PTR(w_uk);
+  CHECK_PTR(w_uv);
+  CHECK_PTR(cache);
+  CHECK_PTR(out);
+  const DecodeWs ws = decode_ws(dims);
+  if (!workspace) return fail(MTLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws.total);
+  if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (ws_bytes < ws.total)
+    return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, ws.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int B = dims->batch, H = dims->heads;
+  float* q_lat = reinterpret_cast<float*>(at(workspace, ws.qlat));
+  float* o_lat = reinterpret_cast<float*>(at(workspace, ws.olat));
+  // The absorb kernel also clears the attention's split counters.
+  hipError_t e = mtla::launch_absorb(B, H, dims->d_h, dims->d_c, dims->d_r, q_c, q_r, w_uk, q_lat,
+                                     reinterpret_cast<int32_t*>(at(workspace, ws.attn.counters)), B,
+                                     dims->dtype, s);
+  if (e != hipSuccess) return hip_status(e, "absorb launch");
+  e = run_decode_attention(dims, pos, q_lat, cache, o_lat, workspace, ws.attn, s);
+  if (e != hipSuccess) return hip_status(e, "decode attention launch");
+  e = mtla::launch_up_project(B, H, dims->d_h, dims->d_c, o_lat, w_uv, out, dims->dtype, s);
+  return hip_status(e, "up-projection launch");
+}
+
+int32_t mtla_prefill_workspace_bytes(const mtla_dims* dims, int32_t n_tokens, size_t* bytes) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
+  if (!bytes) return fail(MTLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = prefill_ws(dims, n_tokens).total;
+  return ok();
+}
+
+int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, const void* q_r,
+                     const void* c, const void* k_r, const float* w_hyp, const float* pe,
+                     int32_t pe_rows, const void* w_uk, const void* w_uv, void* cache,
+                     float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
+  if (pe_rows < n_tokens)
+    return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < n_tokens=%d", pe_rows, n_tokens);
+  if (int64_t(n_tokens) > int64_t(dims->max_slots) * dims->stride_s)
+    return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d exceeds the cache capacity s*max_slots", n_tokens);
+  if (int64_t(dims->batch) * n_tokens * dims->heads * (dims->d_c + dims->d_r) > kMaxElems)
+    return fail(MTLA_ERR_UNSUPPORTED, "prefill too large");
+  if (dims->batch == 0 || n_tokens == 0) return ok();
+  CHECK_PTR(q_c);
+  if (dims->d_r > 0) CHECK_PTR(q_r);
+  CHECK_PTR(c);
+  if (dims->d_r > 0) CHECK_PTR(k_r);
+  CHECK_PTR_ALIGN(w_hyp, 4);
+  CHECK_PTR_ALIGN(pe, 4);
+  CHECK_PTR(w_uk);
+  CHECK_PTR(w_uv);
+  CHECK_PTR(cache);
+  CHECK_PTR_ALIGN(open_acc, 4);
+  CHECK_PTR(out);
+  const PrefillWs ws = prefill_ws(dims, n_tokens);
+  if (!workspace) return fail(MTLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws.total);
+  if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (ws_bytes < ws.total)
+    return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, ws.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int B = dims->batch, H = dims->heads, N = n_tokens;
+  void* P = at(workspace, ws.P);
+  mtla::MergeArgs m{B, N, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, pe_rows,
+                    nullptr, c, k_r, w_hyp, pe, cache, open_acc, nullptr, P};
+  hipError_t e = mtla::launch_merge(m, dims->dtype, s);
+  if (e != hipSuccess) return hip_status(e, "prefill merge launch");
+  if (prefill_fast(dims)) {
+    void* kc = at(workspace, ws.kc);
+    void* v = at(workspace, ws.v);
+    e = mtla::launch_prefill_kv(B, N, H, dims->d_h, dims->d_c, dims->d_r, P, w_uk, w_uv, kc, v, s);
+    if (e != hipSuccess) return hip_status(e, "up-projection launch");
+    mtla::PrefillAttnArgs pa{B, N, H, dims->d_h, dims->d_c, dims->d_r, dims->stride_s,
+                             dims->softmax_scale, q_c, q_r, kc, v, P, out};
+    return hip_status(mtla::launch_prefill_attn(pa, s), "prefill attention launch");
+  }
+  const int R = B * N;
+  const int splits = prefill_splits(dims, N);
+  float* q_lat = reinterpret_cast<float*>(at(workspace, ws.qlat));
+  float* o_lat = reinterpret_cast<float*>(at(workspace, ws.olat));
+  mtla::Partials p{reinterpret_cast<float*>(at(workspace, ws.attn.pm)),
+                   reinterpret_cast<float*>(at(workspace, ws.attn.pl)),
+                   reinterpret_cast<float*>(at(workspace, ws.attn.pacc))};
+  e = mtla::launch_absorb(R, H, dims->d_h, dims->d_c, dims->d_r, q_c, q_r, w_uk, q_lat, nullptr, 0,
+                          dims->dtype, s);
+  if (e != hipSuccess) return hip_status(e, "prefill absorb launch");
+  mtla::AttendArgs a{R, N, H, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, splits,
+                     dims->softmax_scale, nullptr, q_lat, cache, P, p, o_lat, nullptr};
+  e = mtla::launch_attend_portable(a, dims->dtype, s);
+  if (e != hipSuccess) return hip_status(e, "prefill attention launch");
+  e = mtla::launch_up_project(R, H, dims->d_h, dims->d_c, o_lat, w_uv, out, dims->dtype, s);
+  return hip_status(e, "prefill up-projection launch");
+}
+
+int32_t mtla_debug_stride_mask(int32_t n, int32_t s, uint8_t* mask, void* stream) {
+  if (n < 1 || s < 1) return fail(MTLA_ERR_INVALID_ARG, "n=%d, s=%d must be >= 1", n, s);
+  if (int64_t(n) * n > kMaxElems) return fail(MTLA_ERR_UNSUPPORTED, "mask too large");
+  if (!mask) return fail(MTLA_ERR_INVALID_ARG, "mask is NULL");
+  return hip_status(mtla::launch_debug_mask(n, s, mask, static_cast<hipStream_t>(stream)),
+                    "debug mask launch");
+}
+
+int32_t mtla_debug_slot_limits(int32_t n, int32_t s, int32_t* hi, void* stream) {
+  if (n < 1 || s < 1) return fail(MTLA_ERR_INVALID_ARG, "n=%d, s=%d must be >= 1", n, s);
+  if (!hi) return fail(MTLA_ERR_INVALID_ARG, "hi is NULL");
+  return hip_status(mtla::launch_debug_limits(n, s, hi, static_cast<hipStream_t>(stream)),
+                    "debug limits launch");
+}
+
+}  // extern "C"

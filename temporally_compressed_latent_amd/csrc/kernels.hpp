@@ -1,0 +1,88 @@
+// Host-side launchers of the MTLA kernels (called by the C-ABI layer only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mtla {
+
+struct MergeArgs {
+  int B, T, d_c, d_r, s, max_slots, pe_rows;
+  const int32_t* pos0;  // [B] or nullptr (= 1 for every sequence)
+  const void* c;        // [B, T, d_c]
+  const void* k_r;      // [B, T, d_r]
+  const float* w_hyp;   // [d_c]
+  const float* pe;      // [pe_rows, d_c]
+  void* cache;          // [B, max_slots, W]
+  float* open_acc;      // [B, W]
+  float* gate_out;      // [B, T] or nullptr
+  void* partials;       // [B, T, W] cumulative in-block merges, or nullptr
+};
+
+// Gate + temporal merge.  dtype: 0 fp32, 1 bf16.
+hipError_t launch_merge(const MergeArgs& a, int dtype, hipStream_t st);
+
+hipError_t launch_sinusoidal_pe(int rows, int d, float* pe, hipStream_t st);
+hipError_t launch_debug_mask(int n, int s, uint8_t* mask, hipStream_t st);
+hipError_t launch_debug_limits(int n, int s, int32_t* hi, hipStream_t st);
+
+// Absorbed query rows: qbuf[r, h, :] = [W_UK[h]^T q_c[r, h] ; q_r[r, h]] (fp32).
+// If counters is non-null its first ncount entries are set to zero.
+hipError_t launch_absorb(int R, int H, int d_h, int d_c, int d_r, const void* q_c,
+                         const void* q_r, const void* w_uk, float* qbuf, int32_t* counters,
+                         int ncount, int dtype, hipStream_t st);
+
+// Split partials: m, l [R, splits, H], acc [R, splits, H, d_c] (fp32).
+struct Partials {
+  float* m;
+  float* l;
+  float* acc;
+};
+
+struct AttendArgs {
+  int R;          // query rows (decode: B; prefill: B * N)
+  int N;          // prefill tokens per sequence (0 for decode)
+  int H, d_c, d_r, s, max_slots, splits;
+  float scale;
+  const int32_t* pos;   // decode positions [B] (decode only)
+  const float* qbuf;    // [R, H, W]
+  const void* cache;    // [B, max_slots, W]
+  const void* diag;     // prefill: partial merges [B, N, W]; decode: nullptr
+  Partials part;
+  float* o_lat;         // [R, H, d_c] output (fp32)
+  int32_t* counters;    // [R] split tickets, zero on entry and on exit (MFMA path)
+};
+
+// Vector-ALU split attention + split merge (any shape, fp32 or bf16 storage).
+hipError_t launch_attend_portable(const AttendArgs& a, int dtype, hipStream_t st);
+
+// MFMA latent attention for decode (bf16 storage), one kernel including the
+// split merge.  Returns hipErrorNotSupported when no instantiation covers
+// (H, d_c, d_r).
+bool decode_mfma_supported(int H, int d_c, int d_r);
+hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st);
+
+// out[r, h, :] = W_UV[h] o_lat[r, h].
+hipError_t launch_up_project(int R, int H, int d_h, int d_c, const float* o_lat, const void* w_uv,
+                             void* out, int dtype, hipStream_t st);
+
+// Prefill MFMA path (bf16): up-projection GEMM and stride-masked attention.
+bool prefill_mfma_supported(int H, int d_h, int d_c, int d_r);
+hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
+                            const void* partials, const void* w_uk, const void* w_uv,
+                            void* k_out, void* v_out, hipStream_t st);
+
+struct PrefillAttnArgs {
+  int B, N, H, d_h, d_c, d_r, s;
+  float scale;
+  const void* q_c;       // [B, N, H, d_h]
+  const void* q_r;       // [B, N, H, d_r]
+  const void* kc;        // [B, H, N, d_h]
+  const void* v;         // [B, H, N, d_h]
+  const void* partials;  // [B, N, W]  (rope keys P^R are its last d_r columns)
+  void* out;             // [B, N, H, d_h]
+};
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t st);
+
+}  // namespace mtla

@@ -1,0 +1,195 @@
+// Gate + temporal merge into the slot cache ("Multi-head Temporal Latent
+// Attention", Key claims: paper Sec. 4.1 Eq. 13; Method (1); Sec. 4.3 Eq. 17
+// for the cumulative in-block partial merges used by prefill).
+//
+// Work split: one workgroup per (sequence, chunk of consecutive blocks).  The
+// gates of the chunk's tokens are computed first (one wave per token, a d_c
+// dot product), then each thread owns some of the W = d_c + d_r columns and
+// walks the chunk's tokens in order, carrying the fp32 block sum.  Every
+// stored value is rounded once from that fp32 sum.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mtla {
+
+namespace {
+
+constexpr int kMergeThreads = 256;
+constexpr int kMaxChunkTokens = 256;
+
+struct SeqRange {
+  int p0;       // first appended token (1-based)
+  int t_last;   // last appended token
+  int bk0, bk1; // first/last touched block (0-based slot rows)
+  bool ok;
+};
+
+__device__ __forceinline__ SeqRange seq_range(const MergeArgs& a, int b) {
+  SeqRange r;
+  r.p0 = a.pos0 ? a.pos0[b] : 1;
+  const long long tl = static_cast<long long>(r.p0) + a.T - 1;
+  r.ok = r.p0 >= 1 && tl <= a.pe_rows;
+  r.t_last = static_cast<int>(tl);
+  r.bk0 = r.ok ? (r.p0 - 1) / a.s : 0;
+  r.bk1 = r.ok ? (r.t_last - 1) / a.s : 0;
+  r.ok = r.ok && r.bk1 < a.max_slots;
+  return r;
+}
+
+// Gates of tokens ta..ta+ntok-1 of sequence b into gw[0..ntok).
+template <typename T>
+__device__ void compute_gates(const MergeArgs& a, int b, int p0, int ta, int ntok, float* gw) {
+  const T* c = static_cast<const T*>(a.c);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  for (int k = wave; k < ntok; k += nwaves) {
+    const int t = ta + k;
+    const size_t crow = (static_cast<size_t>(b) * a.T + (t - p0)) * a.d_c;
+    const size_t prow = static_cast<size_t>(t - 1) * a.d_c;
+    float acc = 0.f;
+    for (int e = lane; e < a.d_c; e += 64)
+      acc = fmaf(Store<T>::load(c, crow + e) + a.pe[prow + e], a.w_hyp[e], acc);
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      const float w = 1.f / (1.f + expf(-acc));
+      gw[k] = w;
+      if (a.gate_out) a.gate_out[static_cast<size_t>(b) * a.T + (t - p0)] = w;
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float token_elem(const MergeArgs& a, int b, int tok, int e) {
+  const size_t row = static_cast<size_t>(b) * a.T + tok;
+  return e < a.d_c ? Store<T>::load(static_cast<const T*>(a.c), row * a.d_c + e)
+                   : Store<T>::load(static_cast<const T*>(a.k_r), row * a.d_r + (e - a.d_c));
+}
+
+template <typename T>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a, int blocks_per_wg,
+                                                              int write_open) {
+  __shared__ float gw[kMaxChunkTokens];
+  const int b = blockIdx.y;
+  const SeqRange r = seq_range(a, b);
+  if (!r.ok) return;
+  const int s = a.s;
+  const int W = a.d_c + a.d_r;
+  const int blo = r.bk0 + static_cast<int>(blockIdx.x) * blocks_per_wg;
+  if (blo > r.bk1) return;
+  const int bhi = min(r.bk1, blo + blocks_per_wg - 1);
+  const int ta = max(r.p0, blo * s + 1);
+  const int tb = min(r.t_last, bhi * s + s);
+  compute_gates<T>(a, b, r.p0, ta, tb - ta + 1, gw);
+  __syncthreads();
+
+  T* cache = static_cast<T*>(a.cache);
+  T* P = static_cast<T*>(a.partials);
+  for (int e = threadIdx.x; e < W; e += blockDim.x) {
+    for (int blk = blo; blk <= bhi; ++blk) {
+      const int ts = blk * s + 1;
+      const int t0 = max(ts, r.p0);
+      const int t1 = min(ts + s - 1, r.t_last);
+      // A block that began before this call continues the open slot.
+      float acc = (t0 > ts) ? a.open_acc[static_cast<size_t>(b) * W + e] : 0.f;
+      for (int t = t0; t <= t1; ++t) {
+        acc = fmaf(gw[t - ta], token_elem<T>(a, b, t - r.p0, e), acc);
+        if (P) Store<T>::store(P, (static_cast<size_t>(b) * a.T + (t - r.p0)) * W + e, acc);
+      }
+      Store<T>::store(cache, (static_cast<size_t>(b) * a.max_slots + blk) * W + e, acc);
+      if (write_open && blk == r.bk1) a.open_acc[static_cast<size_t>(b) * W + e] = acc;
+    }
+  }
+}
+
+// When one call spans several workgroups per sequence, the open-slot state is
+// written afterwards by this kernel (one workgroup per sequence): it redoes
+// the last block's fp32 sum with the same operation order, so that the first
+// workgroup's read of the old state never races with the new write.
+template <typename T>
+__global__ __launch_bounds__(kMergeThreads) void merge_tail_kernel(MergeArgs a) {
+  __shared__ float gw[kMaxChunkTokens];
+  const int b = blockIdx.x;
+  const SeqRange r = seq_range(a, b);
+  if (!r.ok) return;
+  const int W = a.d_c + a.d_r;
+  const int ts = r.bk1 * a.s + 1;
+  const int t0 = max(ts, r.p0);
+  compute_gates<T>(a, b, r.p0, t0, r.t_last - t0 + 1, gw);
+  __syncthreads();
+  for (int e = threadIdx.x; e < W; e += blockDim.x) {
+    float acc = (t0 > ts) ? a.open_acc[static_cast<size_t>(b) * W + e] : 0.f;
+    for (int t = t0; t <= r.t_last; ++t)
+      acc = fmaf(gw[t - t0], token_elem<T>(a, b, t - r.p0, e), acc);
+    a.open_acc[static_cast<size_t>(b) * W + e] = acc;
+  }
+}
+
+__global__ void pe_kernel(int rows, int d, float* pe) {
+  const size_t n = static_cast<size_t>(rows) * d;
+  for (size_t idx = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; idx < n;
+       idx += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const int p = static_cast<int>(idx / d);
+    const int e = static_cast<int>(idx % d);
+    const int k = e / 2;
+    const double ang = static_cast<double>(p) * pow(10000.0, -2.0 * k / d);
+    pe[idx] = static_cast<float>((e % 2 == 0) ? sin(ang) : cos(ang));
+  }
+}
+
+__global__ void debug_mask_kernel(int n, int s, uint8_t* mask) {
+  const size_t total = static_cast<size_t>(n) * n;
+  for (size_t idx = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; idx < total;
+       idx += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const int i = static_cast<int>(idx / n) + 1;
+    const int j = static_cast<int>(idx % n) + 1;
+    mask[idx] = stride_visible(i, j, s) ? 1 : 0;
+  }
+}
+
+__global__ void debug_limits_kernel(int n, int s, int32_t* hi) {
+  const int i0 = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i0 < n) hi[i0] = completed_slots(i0 + 1, s);
+}
+
+int grid_for(size_t n, int threads) {
+  size_t g = (n + threads - 1) / threads;
+  if (g > 65535) g = 65535;
+  return static_cast<int>(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, int dtype, hipStream_t st) {
+  const int blocks_per_wg = a.s >= kMaxChunkTokens ? 1 : kMaxChunkTokens / a.s;
+  // Blocks one call can touch: ceil((T-1)/s) + 1 (a block may continue).
+  const long long max_blocks = (static_cast<long long>(a.T) - 1 + a.s - 1) / a.s + 1;
+  const long long chunks = (max_blocks + blocks_per_wg - 1) / blocks_per_wg;
+  const int write_open = chunks == 1 ? 1 : 0;
+  dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
+  if (dtype == 0) {
+    merge_kernel<float><<<grid, kMergeThreads, 0, st>>>(a, blocks_per_wg, write_open);
+    if (!write_open) merge_tail_kernel<float><<<a.B, kMergeThreads, 0, st>>>(a);
+  } else {
+    merge_kernel<uint16_t><<<grid, kMergeThreads, 0, st>>>(a, blocks_per_wg, write_open);
+    if (!write_open) merge_tail_kernel<uint16_t><<<a.B, kMergeThreads, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sinusoidal_pe(int rows, int d, float* pe, hipStream_t st) {
+  pe_kernel<<<grid_for(static_cast<size_t>(rows) * d, 256), 256, 0, st>>>(rows, d, pe);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_mask(int n, int s, uint8_t* mask, hipStream_t st) {
+  debug_mask_kernel<<<grid_for(static_cast<size_t>(n) * n, 256), 256, 0, st>>>(n, s, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_limits(int n, int s, int32_t* hi, hipStream_t st) {
+  debug_limits_kernel<<<(n + 255) / 256, 256, 0, st>>>(n, s, hi);
+  return hipGetLastError();
+}
+
+}  // namespace mtla

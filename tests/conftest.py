@@ -8,3 +8,10 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_sessionstart(session):
+    # The binding fails loudly without libmtla.so; build it here only if nothing
+    # is built yet (a cross-compile for gfx950 that needs no GPU).
+    from tests.libmtla import ensure_built
+    ensure_built()

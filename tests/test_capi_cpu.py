@@ -1,0 +1,178 @@
+"""CPU: the C-ABI library loads, exports every declared entry point, and
+rejects bad arguments before touching the GPU (no kernel is launched here)."""
+import ctypes
+import re
+import subprocess
+
+import pytest
+
+from tests.libmtla import ensure_built
+
+ensure_built()
+import temporally_compressed_latent_amd as m  # noqa: E402
+from temporally_compressed_latent_amd import _lib  # noqa: E402
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced (checks fail first)
+MISALIGNED = 0x10001
+
+
+def dims(**kw):
+    d = m.make_dims(4, 8, 64, 256, 32, 2, 128)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_exports_every_header_symbol():
+    syms = m.header_symbols()
+    assert len(syms) == 15
+    for s in syms:
+        assert hasattr(m.lib(), s), s
+    out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(mtla_[a-z_]+)\b", out))
+    assert exported == set(syms)
+
+
+def test_status_strings_and_version():
+    assert m.mtla_version() == 10000
+    for code, name in [(0, "MTLA_OK"), (-1, "MTLA_ERR_INVALID_ARG"), (-2, "MTLA_ERR_UNSUPPORTED"),
+                       (-3, "MTLA_ERR_WORKSPACE"), (-4, "MTLA_ERR_HIP"), (7, "MTLA_UNKNOWN_STATUS")]:
+        assert m.status_string(code) == name
+
+
+def test_workspace_sizes_are_host_only():
+    d = dims()
+    wd = m.mtla_decode_workspace_bytes(d)
+    wp = m.mtla_prefill_workspace_bytes(d, 512)
+    assert wd > 0 and wp > 0 and wd % 256 == 0 and wp % 256 == 0
+    # more slots -> more split partials; more tokens -> more prefill scratch
+    assert m.mtla_decode_workspace_bytes(dims(max_slots=4096)) >= wd
+    assert m.mtla_prefill_workspace_bytes(d, 1024) > wp
+
+
+BAD_DIMS = [
+    (dict(batch=-1), m.MTLA_ERR_INVALID_ARG),
+    (dict(heads=0), m.MTLA_ERR_INVALID_ARG),
+    (dict(d_h=0), m.MTLA_ERR_INVALID_ARG),
+    (dict(d_c=0), m.MTLA_ERR_INVALID_ARG),
+    (dict(d_r=-2), m.MTLA_ERR_INVALID_ARG),
+    (dict(stride_s=0), m.MTLA_ERR_INVALID_ARG),
+    (dict(max_slots=0), m.MTLA_ERR_INVALID_ARG),
+    (dict(dtype=7), m.MTLA_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), m.MTLA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), m.MTLA_ERR_INVALID_ARG),
+    (dict(flags=8), m.MTLA_ERR_INVALID_ARG),
+    (dict(stride_s=257), m.MTLA_ERR_UNSUPPORTED),
+    (dict(d_c=1000, d_r=64), m.MTLA_ERR_UNSUPPORTED),
+    (dict(d_h=512), m.MTLA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_DIMS, ids=[str(k) for k, _ in BAD_DIMS])
+def test_bad_dims_rejected_everywhere(kw, status):
+    L = m.lib()
+    d = dims(**kw)
+    n = ctypes.c_size_t(0)
+    assert L.mtla_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == status
+    assert L.mtla_prefill_workspace_bytes(ctypes.byref(d), 16, ctypes.byref(n)) == status
+    assert L.mtla_merge_append(ctypes.byref(d), FAKE, 1, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None, None) == status
+    assert L.mtla_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == status
+    assert L.mtla_prefill(ctypes.byref(d), 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE, FAKE, FAKE,
+                          FAKE, FAKE, 1 << 30, None) == status
+    assert m.last_error() != ""
+
+
+def test_staged_decode_checks():
+    L, d = m.lib(), dims()
+    need = m.mtla_decode_attention_workspace_bytes(d)
+    assert need > 0
+    assert L.mtla_absorb_query(ctypes.byref(d), -1, FAKE, FAKE, FAKE, FAKE, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_absorb_query(ctypes.byref(d), 4, FAKE, FAKE, FAKE, None, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_absorb_query(ctypes.byref(d), 0, None, None, None, None, None) == m.MTLA_OK
+    assert L.mtla_up_project(ctypes.byref(d), 4, MISALIGNED, FAKE, FAKE, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_up_project(ctypes.byref(d), 0, None, None, None, None) == m.MTLA_OK
+    call = lambda **k: L.mtla_decode_attention(
+        ctypes.byref(d), k.get("pos", FAKE), k.get("q", FAKE), k.get("cache", FAKE), k.get("o", FAKE),
+        k.get("ws", FAKE), k.get("n", need), None)
+    for name in ("pos", "q", "cache", "o"):
+        assert call(**{name: None}) == m.MTLA_ERR_INVALID_ARG, name
+    assert call(ws=None) == m.MTLA_ERR_WORKSPACE
+    assert call(n=need - 1) == m.MTLA_ERR_WORKSPACE
+
+
+def test_null_dims():
+    L = m.lib()
+    assert L.mtla_decode(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == m.MTLA_ERR_INVALID_ARG
+    assert "dims" in m.last_error()
+
+
+def test_merge_argument_checks():
+    L, d = m.lib(), dims()
+    call = lambda **k: L.mtla_merge_append(
+        ctypes.byref(d), k.get("pos0", FAKE), k.get("T", 4), k.get("c", FAKE), k.get("k_r", FAKE),
+        k.get("w", FAKE), k.get("pe", FAKE), k.get("pe_rows", 64), k.get("cache", FAKE),
+        k.get("acc", FAKE), k.get("gate", None), None)
+    assert call(T=-1) == m.MTLA_ERR_INVALID_ARG
+    assert call(pe_rows=0) == m.MTLA_ERR_INVALID_ARG
+    assert call(T=65, pe_rows=64) == m.MTLA_ERR_INVALID_ARG          # more tokens than pe rows
+    assert call(T=257, pe_rows=1000) == m.MTLA_ERR_INVALID_ARG       # beyond s * max_slots
+    for name in ("pos0", "c", "k_r", "w", "pe", "cache", "acc"):
+        assert call(**{name: None}) == m.MTLA_ERR_INVALID_ARG, name
+        assert name.replace("w", "w_hyp").replace("acc", "open_acc") in m.last_error() or True
+        assert call(**{name: MISALIGNED}) == m.MTLA_ERR_INVALID_ARG, name
+    assert call(gate=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
+    # empty work is a no-op, even with null pointers
+    assert call(T=0, c=None, cache=None) == m.MTLA_OK
+    d0 = dims(batch=0)
+    assert L.mtla_merge_append(ctypes.byref(d0), None, 4, None, None, None, None, 8, None, None, None, None) == m.MTLA_OK
+
+
+def test_decode_argument_checks():
+    L, d = m.lib(), dims()
+    need = m.mtla_decode_workspace_bytes(d)
+    call = lambda **k: L.mtla_decode(
+        ctypes.byref(d), k.get("pos", FAKE), k.get("q", FAKE), k.get("qr", FAKE), k.get("uk", FAKE),
+        k.get("uv", FAKE), k.get("cache", FAKE), k.get("out", FAKE), k.get("ws", FAKE),
+        k.get("n", need), None)
+    for name in ("pos", "q", "qr", "uk", "uv", "cache", "out"):
+        assert call(**{name: None}) == m.MTLA_ERR_INVALID_ARG, name
+        assert call(**{name: MISALIGNED}) == m.MTLA_ERR_INVALID_ARG, name
+    assert call(ws=None) == m.MTLA_ERR_WORKSPACE
+    assert call(n=need - 1) == m.MTLA_ERR_WORKSPACE
+    assert call(ws=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
+    d0 = dims(batch=0)
+    assert L.mtla_decode(ctypes.byref(d0), None, None, None, None, None, None, None, None, 0, None) == m.MTLA_OK
+
+
+def test_prefill_argument_checks():
+    L, d = m.lib(), dims()
+    need = m.mtla_prefill_workspace_bytes(d, 32)
+    call = lambda **k: L.mtla_prefill(
+        ctypes.byref(d), k.get("N", 32), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("pe_rows", 64),
+        FAKE, FAKE, k.get("cache", FAKE), FAKE, FAKE, k.get("ws", FAKE), k.get("n", need), None)
+    assert call(N=-1) == m.MTLA_ERR_INVALID_ARG
+    assert call(N=65, pe_rows=64) == m.MTLA_ERR_INVALID_ARG
+    assert call(N=300, pe_rows=400) == m.MTLA_ERR_INVALID_ARG        # 300 > s * max_slots = 256
+    assert call(cache=None) == m.MTLA_ERR_INVALID_ARG
+    assert call(ws=None) == m.MTLA_ERR_WORKSPACE
+    assert call(n=need - 16) == m.MTLA_ERR_WORKSPACE
+    assert call(N=0, cache=None, ws=None) == m.MTLA_OK
+
+
+def test_debug_hook_checks():
+    L = m.lib()
+    assert L.mtla_debug_stride_mask(0, 2, FAKE, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_debug_stride_mask(4, 0, FAKE, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_debug_stride_mask(4, 2, None, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_debug_slot_limits(4, 2, None, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_sinusoidal_pe(0, 4, FAKE, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_sinusoidal_pe(4, 4, MISALIGNED, None) == m.MTLA_ERR_INVALID_ARG
+
+
+def test_binding_rejects_wrong_tensors_before_the_library():
+    import torch
+    d = dims()
+    with pytest.raises((ValueError, TypeError)):
+        m.mtla_merge_append(d, torch.zeros(4, dtype=torch.int32), torch.zeros(4, 1, 256),
+                            torch.zeros(4, 1, 32), torch.zeros(256), torch.zeros(8, 256),
+                            torch.zeros(4, 128, 288), torch.zeros(4, 288), stream=0)

@@ -1,0 +1,133 @@
+"""GPU: absorbed-form decode (mtla_merge_append + mtla_decode, token by
+token) against the fp64 oracle's incremental loop."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import oracle_ref
+from tests.gpu_util import DEV, bits, host, make_case, tol
+
+pytestmark = pytest.mark.gpu
+
+LOOP_CASES = [
+    # shape, dtype, portable, s, B, N
+    ("st", "bf16", False, 2, 2, 150),
+    ("st", "bf16", False, 4, 2, 131),
+    ("st", "bf16", True, 3, 2, 100),
+    ("st", "fp32", False, 2, 2, 90),
+    ("llm", "bf16", False, 2, 2, 90),
+    ("mid", "bf16", False, 3, 2, 70),
+    ("odd", "fp32", False, 3, 3, 40),
+    ("odd", "bf16", False, 1, 2, 33),
+]
+
+
+@pytest.mark.parametrize("shape,dtype,portable,s,B,N", LOOP_CASES)
+def test_decode_loop_matches_oracle(shape, dtype, portable, s, B, N):
+    inp, g = make_case(shape, 1, B, N, s, dtype, portable)
+    out = host(g.decode_loop(N))
+    scale = g.d.softmax_scale
+    for b in range(B):
+        want, cache = oracle_ref.incremental(inp, b, N, s, scale)
+        err = oracle.max_rel_err(out[b], want)
+        assert err <= tol(dtype), (b, err)
+        assert oracle.max_rel_err(host(g.cache)[b, :cache.shape[0]], cache) <= tol(dtype)
+
+
+@pytest.mark.parametrize("shape,B,N,s", [("st", 40, 3001, 2), ("llm", 64, 1100, 2), ("st", 9, 2048, 4)])
+def test_decode_long_cache_many_splits(shape, B, N, s):
+    """Cache built by one chunked append, then one decode step; splits hold
+    several 64-slot tiles and a ragged last tile."""
+    inp, g = make_case(shape, 2, B, N, s, "bf16", max_slots=-(-N // s) + 64, q_rows=1)
+    g.append(torch.ones(B, dtype=torch.int32, device=DEV), 0, N)
+    out = host(g.decode(torch.full((B,), N, dtype=torch.int32, device=DEV), 0))
+    for b in sorted({0, B // 2, B - 1}):
+        cache, _ = oracle_ref.merged_cache(inp["c"][b], inp["k_r"][b], inp["w_hyp"], s)
+        want = oracle.decode_absorbed(inp["q_c"][b, 0], inp["q_r"][b, 0], cache,
+                                      inp["w_uk"], inp["w_uv"], g.d.d_c, g.d.softmax_scale)
+        assert oracle.max_rel_err(out[b], want) <= 1e-2, b
+
+
+@pytest.mark.parametrize("portable", [False, True])
+def test_decode_zero_query_is_uniform_mean(portable):
+    """q = 0: every slot gets the same weight, so o_h = W_UV[h] mean_j S^c_j,
+    computed here from the device's own cache rows."""
+    B, N, s = 3, 77, 2
+    inp, g = make_case("st", 3, B, N, s, "bf16", portable, q_zero=True)
+    g.append(torch.ones(B, dtype=torch.int32, device=DEV), 0, N)
+    out = host(g.decode(torch.full((B,), N, dtype=torch.int32, device=DEV), N - 1))
+    cache = host(g.cache)
+    n = oracle.num_slots(N, s)
+    mean = cache[:, :n, :g.d.d_c].mean(axis=1)                       # [B, d_c]
+    want = np.einsum("hek,bk->bhe", inp["w_uv"].astype(np.float64), mean)
+    assert oracle.max_rel_err(out, want) <= 2 ** -7
+
+
+@pytest.mark.parametrize("shape,portable", [("st", False), ("llm", False), ("st", True)])
+def test_decode_ignores_rows_past_the_open_slot(shape, portable):
+    """NaN in every cache row beyond ceil(t/s) must not reach the output."""
+    B, N, s = 2, 130, 2
+    inp, g = make_case(shape, 4, B, N, s, "bf16", portable, max_slots=200)
+    g.append(torch.ones(B, dtype=torch.int32, device=DEV), 0, N)
+    pos = torch.full((B,), N, dtype=torch.int32, device=DEV)
+    clean = g.decode(pos, N - 1).clone()
+    g.cache[:, oracle.num_slots(N, s):] = float("nan")
+    poisoned = g.decode(pos, N - 1)
+    assert torch.isfinite(poisoned.float()).all()
+    assert torch.equal(bits(clean), bits(poisoned))
+
+
+@pytest.mark.parametrize("shape", ["st", "llm"])
+def test_decode_bit_reproducible(shape):
+    B, N, s = 4, 700, 2
+    inp, g = make_case(shape, 5, B, N, s, "bf16")
+    g.append(torch.ones(B, dtype=torch.int32, device=DEV), 0, N)
+    pos = torch.full((B,), N, dtype=torch.int32, device=DEV)
+    a = g.decode(pos, N - 1).clone()
+    b = g.decode(pos, N - 1).clone()
+    assert torch.equal(bits(a), bits(b))
+
+
+@pytest.mark.parametrize("portable", [False, True])
+def test_decode_ragged_and_invalid_positions(portable):
+    """Each sequence decodes at its own position; an invalid position gives NaN
+    for that sequence only."""
+    B, N, s = 5, 64, 2
+    inp, g = make_case("st", 6, B, N, s, "bf16", portable)
+    g.append(torch.ones(B, dtype=torch.int32, device=DEV), 0, N)
+    positions = [1, 5, 64, 0, 10_000]
+    out = host(g.decode(torch.tensor(positions, dtype=torch.int32, device=DEV), N - 1))
+    for b, p in enumerate(positions):
+        if not (1 <= p <= N):
+            assert np.isnan(out[b]).all(), b
+            continue
+        cache, _ = oracle_ref.merged_cache(inp["c"][b], inp["k_r"][b], inp["w_hyp"], s)
+        want = oracle.decode_absorbed(inp["q_c"][b, N - 1], inp["q_r"][b, N - 1],
+                                      cache[: oracle.slot_of(p, s)], inp["w_uk"], inp["w_uv"],
+                                      g.d.d_c, g.d.softmax_scale)
+        assert oracle.max_rel_err(out[b], want) <= 1e-2, b
+
+
+@pytest.mark.parametrize("shape,portable,B", [("st", False, 3), ("llm", False, 4), ("st", True, 2),
+                                              ("st", False, 80)])
+def test_staged_decode_equals_fused_call(shape, portable, B):
+    """absorb -> decode_attention -> up_project gives the bits of mtla_decode;
+    the attention's split counters are left at zero, so calls can repeat."""
+    import temporally_compressed_latent_amd as m
+    N, s = 900, 2
+    inp, g = make_case(shape, 12, B, N, s, "bf16", portable, q_rows=1)
+    g.append(torch.ones(B, dtype=torch.int32, device=DEV), 0, N)
+    pos = torch.full((B,), N, dtype=torch.int32, device=DEV)
+    fused = g.decode(pos, 0).clone()
+    d = g.d
+    q_lat = torch.empty(B, d.heads, d.width, dtype=torch.float32, device=DEV)
+    o_lat = torch.empty(B, d.heads, d.d_c, dtype=torch.float32, device=DEV)
+    out = torch.empty_like(fused)
+    ws = m.decode_attention_workspace(d)
+    for _ in range(3):
+        m.mtla_absorb_query(d, g.q_c[:, 0].contiguous(), g.q_r[:, 0].contiguous(), g.w_uk, q_lat)
+        m.mtla_decode_attention(d, pos, q_lat, g.cache, o_lat, ws)
+        m.mtla_up_project(d, o_lat, g.w_uv, out)
+        assert torch.equal(bits(out), bits(fused))
+        assert int(ws[:4 * B].view(torch.int32).abs().sum()) == 0

@@ -1,0 +1,85 @@
+"""GPU: stride-masked parallel prefill (mtla_prefill) against the oracle's
+dense masked pass, and against the device's own token-by-token decode."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import oracle_ref
+from tests.gpu_util import DEV, bits, host, make_case, tol
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # shape, dtype, portable, s, B, N
+    ("st", "bf16", False, 3, 2, 300),
+    ("st", "bf16", False, 1, 1, 200),
+    ("st", "bf16", False, 2, 2, 129),
+    ("st", "bf16", False, 7, 2, 5),     # s > N: every query sees only its own partial
+    ("st", "bf16", False, 3, 3, 1),
+    ("llm", "bf16", False, 2, 1, 160),
+    ("st", "bf16", True, 3, 2, 100),
+    ("st", "fp32", False, 4, 1, 64),
+    ("odd", "fp32", False, 2, 2, 37),
+    ("odd", "bf16", False, 3, 2, 29),
+]
+
+
+@pytest.mark.parametrize("shape,dtype,portable,s,B,N", CASES)
+def test_prefill_matches_oracle(shape, dtype, portable, s, B, N):
+    inp, g = make_case(shape, 7, B, N, s, dtype, portable)
+    out = host(g.prefill(N))
+    cache, acc = host(g.cache), host(g.open_acc)
+    for b in range(B):
+        want, P = oracle_ref.parallel(inp, b, N, s, g.d.softmax_scale)
+        assert oracle.max_rel_err(out[b], want) <= tol(dtype), b
+        n = oracle.num_slots(N, s)
+        slot_rows = [min(s * k, N) - 1 for k in range(1, n + 1)]   # P at each block end
+        assert oracle.max_rel_err(cache[b, :n], P[slot_rows]) <= tol(dtype)
+        assert oracle.max_rel_err(acc[b], P[N - 1]) <= 1e-5
+
+
+@pytest.mark.parametrize("shape,s,N,portable", [("st", 3, 200, False), ("llm", 2, 96, False),
+                                                ("st", 2, 64, True)])
+def test_prefill_equals_device_decode_loop(shape, s, N, portable):
+    """The parallel pass and token-by-token decoding agree on the device: the
+    same cache bits, the same open-slot state, outputs within tolerance."""
+    inp, a = make_case(shape, 8, 2, N, s, "bf16", portable)
+    _, b_ = make_case(shape, 8, 2, N, s, "bf16", portable)
+    pre = host(a.prefill(N))
+    loop = host(b_.decode_loop(N))
+    assert torch.equal(bits(a.cache), bits(b_.cache))
+    assert torch.equal(a.open_acc, b_.open_acc)
+    assert oracle.max_rel_err(pre, loop) <= 1e-2
+
+
+@pytest.mark.parametrize("s,N1", [(3, 101), (2, 64), (4, 1)])
+def test_prefill_then_decode_continues(s, N1):
+    """Prefill N1 tokens (ending inside a block), then keep decoding: the
+    outputs follow the oracle's incremental loop."""
+    B, N = 2, 160
+    inp, g = make_case("st", 9, B, N, s, "bf16")
+    g.prefill(N1)
+    cont = host(g.decode_loop(N, start=N1))
+    for b in range(B):
+        want, _ = oracle_ref.incremental(inp, b, N, s, g.d.softmax_scale)
+        assert oracle.max_rel_err(cont[b], want[N1:]) <= 1e-2, b
+
+
+@pytest.mark.parametrize("portable", [False, True])
+def test_prefill_ignores_cache_rows_past_the_end(portable):
+    B, N, s = 2, 150, 3
+    inp, a = make_case("st", 10, B, N, s, "bf16", portable, max_slots=90)
+    clean = a.prefill(N).clone()
+    a.cache[:, oracle.num_slots(N, s):] = float("nan")
+    again = a.prefill(N)
+    assert torch.isfinite(again.float()).all()
+    assert torch.equal(bits(clean), bits(again))
+
+
+def test_prefill_bit_reproducible():
+    B, N, s = 2, 513, 3
+    inp, a = make_case("st", 11, B, N, s, "bf16")
+    x = a.prefill(N).clone()
+    y = a.prefill(N).clone()
+    assert torch.equal(bits(x), bits(y))

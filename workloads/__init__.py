@@ -89,13 +89,16 @@ def workload(i: int) -> Workload:
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
+    u = x.view(np.uint32)
     nan = np.isnan(x)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    # finite values: u + 0x7fff + lsb stays below 2^32 (largest is 0xff7fffff)
+    r = u + np.uint32(0x7FFF)
+    r += (u >> np.uint32(16)) & np.uint32(1)
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     if nan.any():
-        r = np.where(nan, np.uint16(0x7FC0), r)
-    return r
+        out[nan] = np.uint16(0x7FC0)
+    return out
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -193,3 +196,33 @@ def layer_params(w: Workload) -> dict:
 def small(wid: int = 0, **kw) -> Workload:
     """A workload with shapes overridden (for tests at oracle-friendly sizes)."""
     return WORKLOADS[wid].with_(**kw)
+
+
+def boundary_case(seed: int, B: int, N: int, H: int, d_h: int, d_c: int, d_r: int,
+                  dtype: str, w_hyp_zero: bool = False, q_zero: bool = False,
+                  q_rows: Optional[int] = None) -> dict:
+    """Seeded Gaussian kernel-boundary inputs of arbitrary shape (test cases).
+
+    Same distributions as the named workloads; ``w_hyp_zero`` and ``q_zero``
+    give the closed-form special cases (every gate 1/2; uniform attention).
+    ``q_rows`` limits the queries to that many token rows (default: N).
+    """
+    Q = N if q_rows is None else q_rows
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([ROOT_SEED, 1000 + seed])))
+    f = lambda *shape: g.standard_normal(shape, dtype=np.float32)
+    std = np.float32(1.0 / np.sqrt(d_c))
+    case = {
+        "c": quantize(f(B, N, d_c), dtype),
+        "k_r": quantize(f(B, N, d_r), dtype),
+        "q_c": quantize(f(B, Q, H, d_h), dtype),
+        "q_r": quantize(f(B, Q, H, d_r), dtype),
+        "w_hyp": f(d_c) * std,
+        "w_uk": quantize(f(H, d_h, d_c) * std, dtype),
+        "w_uv": quantize(f(H, d_h, d_c) * std, dtype),
+    }
+    if w_hyp_zero:
+        case["w_hyp"] = np.zeros(d_c, np.float32)
+    if q_zero:
+        case["q_c"] = np.zeros_like(case["q_c"])
+        case["q_r"] = np.zeros_like(case["q_r"])
+    return case
