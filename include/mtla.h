@@ -63,6 +63,8 @@ typedef enum { MTLA_FP32 = 0, MTLA_BF16 = 1 } mtla_dtype;
 /* Force the portable (vector-ALU) kernels even where the MFMA kernels apply. */
 #define MTLA_FLAG_PORTABLE 1
 
+/* Supported dimensions: d_c and d_r multiples of 8, d_c + d_r <= 1024,
+ * d_h <= 256, s <= 256 (MTLA_ERR_UNSUPPORTED otherwise). */
 typedef struct {
   int32_t batch;       /* B: sequences                                          */
   int32_t heads;       /* H: attention heads                                    */
@@ -170,15 +172,13 @@ int32_t mtla_decode_attention_workspace_bytes(const mtla_dims* dims, size_t* byt
  * 1..ceil(pos/s):  o_lat[b, h] = sum_j softmax_j(tau q_lat[b, h] . S_j) S^c_j.
  * Page: "Multi-head Temporal Latent Attention", Method and Key claims
  * (Sec. 6.1: a query at step t reads ceil(t/s) slots).
- * With bf16 storage and a supported shape this is a single kernel (MFMA
- * split-K over slots whose splits are merged, in a fixed order, by the last
- * workgroup of each sequence).
+ * With bf16 storage and a supported shape it runs an MFMA split-K kernel over
+ * the slots (one split, hence one kernel, for caches up to ~512 slots; more
+ * splits, merged in a fixed order by a second kernel, for longer ones).
  *   pos   device [B] int32; q_lat device [B, H, d_c + d_r] fp32;
  *   cache device [B, max_slots, d_c + d_r]; o_lat device [B, H, d_c] fp32,
  *   written.
- *   workspace: its first bytes hold per-sequence split counters, which must
- *   be zero the first time a workspace is used (allocate it zero-filled);
- *   every call leaves them zero again.  The rest is scratch.
+ *   workspace device, >= mtla_decode_attention_workspace_bytes(); scratch.
  */
 int32_t mtla_decode_attention(const mtla_dims* dims, const int32_t* pos, const float* q_lat,
                               const void* cache, float* o_lat, void* workspace, size_t ws_bytes,

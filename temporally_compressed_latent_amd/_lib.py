@@ -272,9 +272,8 @@ def mtla_up_project(dims: MtlaDims, o_lat, w_uv, out, stream=None) -> None:
 
 
 def decode_attention_workspace(dims: MtlaDims) -> torch.Tensor:
-    """A zero-filled workspace for mtla_decode_attention (its split counters
-    must start at zero; every call leaves them zero)."""
-    return torch.zeros(mtla_decode_attention_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    """A workspace of the size mtla_decode_attention needs."""
+    return torch.empty(mtla_decode_attention_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
 
 
 def mtla_prefill_workspace_bytes(dims: MtlaDims, n_tokens: int) -> int:

@@ -54,6 +54,8 @@ int32_t check_dims(const mtla_dims* d) {
   if (d->d_c + d->d_r > kMaxWidth)
     return fail(MTLA_ERR_UNSUPPORTED, "d_c + d_r = %d > %d", d->d_c + d->d_r, kMaxWidth);
   if (d->d_h > kMaxDh) return fail(MTLA_ERR_UNSUPPORTED, "d_h=%d > %d", d->d_h, kMaxDh);
+  if (d->d_c % 8 != 0 || d->d_r % 8 != 0)
+    return fail(MTLA_ERR_UNSUPPORTED, "d_c=%d and d_r=%d must be multiples of 8", d->d_c, d->d_r);
   if ((8 * int64_t(d->d_c) + int64_t(d->d_h) * 65) * 4 > 65536)
     return fail(MTLA_ERR_UNSUPPORTED, "d_c=%d with d_h=%d exceeds the up-projection kernel's LDS", d->d_c, d->d_h);
   const int64_t W = d->d_c + d->d_r;
@@ -103,13 +105,14 @@ bool prefill_fast(const mtla_dims* d) {
 int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// Splits of the slot range.  The MFMA kernel aims at ~2 workgroups per CU
-// (256 CUs) with at least one 64-slot tile per split; the portable kernel
-// gives each split ~128 slots.
+// Splits of the slot range.  The MFMA kernel gives each split at least ~512
+// slots (a short cache is one workgroup per sequence, with no merge pass) and
+// otherwise aims at ~2 workgroups per CU over the chip's 256 CUs; the portable
+// kernel gives each split ~128 slots.
 int decode_splits(const mtla_dims* d) {
   if (decode_fast(d)) {
     const int want = ceil_div(512, d->batch > 0 ? d->batch : 1);
-    return clampi(want, 1, clampi(ceil_div(d->max_slots, 64), 1, 64));
+    return clampi(want, 1, clampi(ceil_div(d->max_slots, 512), 1, 64));
   }
   return clampi(ceil_div(d->max_slots, 128), 1, 32);
 }
@@ -118,17 +121,15 @@ int prefill_splits(const mtla_dims* d, int n_tokens) {
   return clampi(ceil_div(n_tokens / d->stride_s + 1, 128), 1, 16);
 }
 
-// Workspace of the latent attention: split counters first (zero on entry,
-// left zero), then the split partials.
+// Workspace of the latent attention: the split partials.
 struct AttnWs {
-  size_t counters, pm, pl, pacc, total;
+  size_t pm, pl, pacc, total;
 };
 
 AttnWs attn_ws(const mtla_dims* d, size_t rows, int splits, size_t off) {
   const size_t H = d->heads, S = splits;
   AttnWs w;
-  w.counters = off;
-  w.pm = w.counters + align_up(rows * 4);
+  w.pm = off;
   w.pl = w.pm + align_up(rows * S * H * 4);
   w.pacc = w.pl + align_up(rows * S * H * 4);
   w.total = w.pacc + align_up(rows * S * H * d->d_c * 4);
@@ -248,7 +249,7 @@ int32_t mtla_absorb_query(const mtla_dims* dims, int32_t n_rows, const void* q_c
   CHECK_PTR(w_uk);
   CHECK_PTR_ALIGN(q_lat, 4);
   return hip_status(mtla::launch_absorb(n_rows, dims->heads, dims->d_h, dims->d_c, dims->d_r, q_c,
-                                        q_r, w_uk, q_lat, nullptr, 0, dims->dtype,
+                                        q_r, w_uk, q_lat, dims->dtype,
                                         static_cast<hipStream_t>(stream)),
                     "absorb launch");
 }
@@ -285,7 +286,7 @@ hipError_t run_decode_attention(const mtla_dims* dims, const int32_t* pos, const
                    reinterpret_cast<float*>(at(ws, w.pacc))};
   mtla::AttendArgs a{dims->batch, 0, dims->heads, dims->d_c, dims->d_r, dims->stride_s,
                      dims->max_slots, splits, dims->softmax_scale, pos, q_lat, cache, nullptr, p,
-                     o_lat, reinterpret_cast<int32_t*>(at(ws, w.counters))};
+                     o_lat};
   return decode_fast(dims) ? mtla::launch_decode_mfma(a, s)
                            : mtla::launch_attend_portable(a, dims->dtype, s);
 }
@@ -343,9 +344,7 @@ int32_t mtla_decode(const mtla_dims* dims, const int32_t* pos, const void* q_c, 
   const int B = dims->batch, H = dims->heads;
   float* q_lat = reinterpret_cast<float*>(at(workspace, ws.qlat));
   float* o_lat = reinterpret_cast<float*>(at(workspace, ws.olat));
-  // The absorb kernel also clears the attention's split counters.
   hipError_t e = mtla::launch_absorb(B, H, dims->d_h, dims->d_c, dims->d_r, q_c, q_r, w_uk, q_lat,
-                                     reinterpret_cast<int32_t*>(at(workspace, ws.attn.counters)), B,
                                      dims->dtype, s);
   if (e != hipSuccess) return hip_status(e, "absorb launch");
   e = run_decode_attention(dims, pos, q_lat, cache, o_lat, workspace, ws.attn, s);
@@ -417,11 +416,11 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
   mtla::Partials p{reinterpret_cast<float*>(at(workspace, ws.attn.pm)),
                    reinterpret_cast<float*>(at(workspace, ws.attn.pl)),
                    reinterpret_cast<float*>(at(workspace, ws.attn.pacc))};
-  e = mtla::launch_absorb(R, H, dims->d_h, dims->d_c, dims->d_r, q_c, q_r, w_uk, q_lat, nullptr, 0,
+  e = mtla::launch_absorb(R, H, dims->d_h, dims->d_c, dims->d_r, q_c, q_r, w_uk, q_lat,
                           dims->dtype, s);
   if (e != hipSuccess) return hip_status(e, "prefill absorb launch");
   mtla::AttendArgs a{R, N, H, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, splits,
-                     dims->softmax_scale, nullptr, q_lat, cache, P, p, o_lat, nullptr};
+                     dims->softmax_scale, nullptr, q_lat, cache, P, p, o_lat};
   e = mtla::launch_attend_portable(a, dims->dtype, s);
   if (e != hipSuccess) return hip_status(e, "prefill attention launch");
   e = mtla::launch_up_project(R, H, dims->d_h, dims->d_c, o_lat, w_uv, out, dims->dtype, s);

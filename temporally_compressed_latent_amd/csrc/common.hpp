@@ -42,6 +42,24 @@ template <> struct Store<uint16_t> {
   }
 };
 
+// Eight consecutive stored elements (16-byte aligned for bf16, 32 for fp32)
+// as fp32.
+__device__ __forceinline__ void load8(const uint16_t* p, float* out) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* out) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
 // ---------------------------------------------------------------------------
 // Slot arithmetic and the stride-aware mask (integers, exact).
 //   Token t (1-based) lives in slot ceil(t/s) (1-based).  Query i attends key

@@ -20,45 +20,62 @@ namespace mtla {
 namespace {
 
 // ---------------------------------------------------------------------------
-// absorb: one workgroup per (head, block of RB rows).  Threads own latent
-// columns k; W_UK[h] rows are read coalesced, query values come from LDS.
+// absorb: one workgroup per (head, block of RB rows).
+//   q~[r, k] = sum_e q_c[r, e] W_UK[h, e, k]
+// Thread t owns the 8 latent columns of chunk kc = t % KC (KC = d_c / 8) for
+// the rows e = eg, eg + EG, ... (EG = 256 / KC groups); each W_UK row chunk
+// is one 16-byte load, reused for all RB query rows.  The EG partial sums are
+// added in group order through LDS.
 // ---------------------------------------------------------------------------
-constexpr int kAbsorbRB = 8;
-
-template <typename T>
+template <typename T, int RB>
 __global__ __launch_bounds__(256) void absorb_kernel(int R, int H, int d_h, int d_c, int d_r,
                                                      const T* __restrict__ q_c,
                                                      const T* __restrict__ q_r,
                                                      const T* __restrict__ w_uk,
-                                                     float* __restrict__ qbuf,
-                                                     int32_t* __restrict__ counters, int ncount) {
-  extern __shared__ float sq[];  // [RB][d_h]
+                                                     float* __restrict__ qbuf) {
+  extern __shared__ float smem[];
+  float* sq = smem;               // [RB][d_h]
+  float* red = smem + RB * d_h;   // [EG][RB][d_c]
   const int h = blockIdx.x;
-  const int r0 = blockIdx.y * kAbsorbRB;
+  const int r0 = blockIdx.y * RB;
   const int W = d_c + d_r;
-  // Split counters of the attention kernel that follows on the stream.
-  if (counters && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < ncount; i += blockDim.x) counters[i] = 0;
-  for (int idx = threadIdx.x; idx < kAbsorbRB * d_h; idx += blockDim.x) {
+  const int KC = d_c / 8, EG = 256 / KC;
+  const int t = threadIdx.x, kc = t % KC, eg = t / KC;
+  for (int idx = t; idx < RB * d_h; idx += 256) {
     const int rr = idx / d_h, e = idx % d_h;
     const int r = r0 + rr;
     sq[idx] = r < R ? Store<T>::load(q_c, (static_cast<size_t>(r) * H + h) * d_h + e) : 0.f;
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < d_c; k += blockDim.x) {
-    float acc[kAbsorbRB];
+  if (eg < EG) {
+    float acc[RB][8];
 #pragma unroll
-    for (int rr = 0; rr < kAbsorbRB; ++rr) acc[rr] = 0.f;
-    for (int e = 0; e < d_h; ++e) {
-      const float w = Store<T>::load(w_uk, (static_cast<size_t>(h) * d_h + e) * d_c + k);
+    for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
-      for (int rr = 0; rr < kAbsorbRB; ++rr) acc[rr] = fmaf(sq[rr * d_h + e], w, acc[rr]);
+      for (int j = 0; j < 8; ++j) acc[rr][j] = 0.f;
+    for (int e = eg; e < d_h; e += EG) {
+      float w[8];
+      load8(w_uk + (static_cast<size_t>(h) * d_h + e) * d_c + kc * 8, w);
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const float q = sq[rr * d_h + e];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[rr][j] = fmaf(q, w[j], acc[rr][j]);
+      }
     }
 #pragma unroll
-    for (int rr = 0; rr < kAbsorbRB; ++rr)
-      if (r0 + rr < R) qbuf[(static_cast<size_t>(r0 + rr) * H + h) * W + k] = acc[rr];
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[(eg * RB + rr) * d_c + kc * 8 + j] = acc[rr][j];
   }
-  for (int idx = threadIdx.x; idx < kAbsorbRB * d_r; idx += blockDim.x) {
+  __syncthreads();
+  for (int idx = t; idx < RB * d_c; idx += 256) {
+    const int rr = idx / d_c, k = idx % d_c;
+    float v = 0.f;
+    for (int g2 = 0; g2 < EG; ++g2) v += red[(g2 * RB + rr) * d_c + k];
+    if (r0 + rr < R) qbuf[(static_cast<size_t>(r0 + rr) * H + h) * W + k] = v;
+  }
+  for (int idx = t; idx < RB * d_r; idx += 256) {
     const int rr = idx / d_r, e = idx % d_r;
     const int r = r0 + rr;
     if (r < R)
@@ -185,62 +202,51 @@ __global__ __launch_bounds__(256) void split_merge_kernel(int H, int d_c, int sp
 
 // ---------------------------------------------------------------------------
 // Up-projection: out[r, h, e] = sum_k W_UV[h, e, k] o_lat[r, h, k].
-// One workgroup per (head, block of RB rows); W_UV[h] is staged through LDS
-// in 64-column tiles so global reads coalesce.
+// One workgroup per (head, block of RB rows).  TPO consecutive threads share
+// output row e and split its d_c / 8 chunks; each chunk is one 16-byte load of
+// W_UV, reused for all RB rows, and the TPO partial dots are added with
+// butterfly shuffles.
 // ---------------------------------------------------------------------------
-constexpr int kUpRB = 8;
-constexpr int kUpKT = 64;
-
-template <typename T>
-__global__ __launch_bounds__(256) void up_project_kernel(int R, int H, int d_h, int d_c,
+template <typename T, int RB>
+__global__ __launch_bounds__(256) void up_project_kernel(int R, int H, int d_h, int d_c, int tpo,
                                                          const float* __restrict__ o_lat,
                                                          const T* __restrict__ w_uv,
                                                          T* __restrict__ out) {
-  extern __shared__ float smem[];
-  float* olat = smem;                 // [RB][d_c]
-  float* wt = smem + kUpRB * d_c;     // [d_h][kUpKT + 1]
+  extern __shared__ float olat[];  // [RB][d_c]
   const int h = blockIdx.x;
-  const int r0 = blockIdx.y * kUpRB;
-  for (int idx = threadIdx.x; idx < kUpRB * d_c; idx += blockDim.x) {
+  const int r0 = blockIdx.y * RB;
+  const int t = threadIdx.x;
+  for (int idx = t; idx < RB * d_c; idx += 256) {
     const int rr = idx / d_c, k = idx % d_c;
     const int r = r0 + rr;
     olat[idx] = r < R ? o_lat[(static_cast<size_t>(r) * H + h) * d_c + k] : 0.f;
   }
-  constexpr int kMaxOut = 8;  // (kUpRB * d_h) / 256 with d_h <= 256
-  float acc[kMaxOut];
+  __syncthreads();
+  const int e = t / tpo, p = t % tpo;
+  const int KC = d_c / 8;
+  float acc[RB];
 #pragma unroll
-  for (int j = 0; j < kMaxOut; ++j) acc[j] = 0.f;
-  const int nout = kUpRB * d_h;
-  for (int k0 = 0; k0 < d_c; k0 += kUpKT) {
-    const int kt = min(kUpKT, d_c - k0);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < d_h * kUpKT; idx += blockDim.x) {
-      const int e = idx / kUpKT, kk = idx % kUpKT;
-      wt[e * (kUpKT + 1) + kk] =
-          kk < kt ? Store<T>::load(w_uv, (static_cast<size_t>(h) * d_h + e) * d_c + k0 + kk) : 0.f;
-    }
-    __syncthreads();
+  for (int rr = 0; rr < RB; ++rr) acc[rr] = 0.f;
+  if (e < d_h) {
+    for (int c = p; c < KC; c += tpo) {
+      float w[8];
+      load8(w_uv + (static_cast<size_t>(h) * d_h + e) * d_c + c * 8, w);
 #pragma unroll
-    for (int j = 0; j < kMaxOut; ++j) {
-      const int idx = threadIdx.x + 256 * j;
-      if (idx < nout) {
-        const int rr = idx / d_h, e = idx % d_h;
-        const float* wrow = wt + e * (kUpKT + 1);
-        const float* orow = olat + rr * d_c + k0;
-        float s = acc[j];
-        for (int kk = 0; kk < kt; ++kk) s = fmaf(wrow[kk], orow[kk], s);
-        acc[j] = s;
+      for (int rr = 0; rr < RB; ++rr) {
+        const float* o = olat + rr * d_c + c * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[rr] = fmaf(w[j], o[j], acc[rr]);
       }
     }
   }
+  for (int off = tpo / 2; off >= 1; off >>= 1) {
 #pragma unroll
-  for (int j = 0; j < kMaxOut; ++j) {
-    const int idx = threadIdx.x + 256 * j;
-    if (idx < nout) {
-      const int rr = idx / d_h, e = idx % d_h;
-      const int r = r0 + rr;
-      if (r < R) Store<T>::store(out, (static_cast<size_t>(r) * H + h) * d_h + e, acc[j]);
-    }
+    for (int rr = 0; rr < RB; ++rr) acc[rr] += __shfl_xor(acc[rr], off, 64);
+  }
+  if (p == 0 && e < d_h) {
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+      if (r0 + rr < R) Store<T>::store(out, (static_cast<size_t>(r0 + rr) * H + h) * d_h + e, acc[rr]);
   }
 }
 
@@ -260,10 +266,12 @@ __global__ __launch_bounds__(256) void up_project_kernel(int R, int H, int d_h, 
 //      from two ds_read_b64_tr_b16 transposing loads of the row-major tile.
 // Scores are carried in the log2 domain (queries pre-scaled by tau*log2 e).
 //
-// Split merge: each workgroup stores its (m, l, acc) partial, then takes a
-// ticket on its sequence's counter; the last one to arrive merges all splits
-// in split order into o_lat[b] and resets the counter to zero.  With a single
-// split the workgroup writes o_lat directly.
+// With a single split the workgroup normalises and writes o_lat itself;
+// otherwise it stores its (m, l, acc) partial and split_merge_kernel, launched
+// next on the stream, merges the splits in split order.  (A last-arriving-
+// workgroup merge inside this kernel would need device-scope release/acquire
+// fences per workgroup, which on this multi-XCD part write back and invalidate
+// L2 and cost far more than the extra launch.)
 // ---------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -292,7 +300,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
   __shared__ __align__(16) uint16_t sK[TS * PITCH];
   __shared__ __align__(16) uint16_t sP[HP * PP];
   __shared__ float sRed[4][HP];
-  __shared__ int sLast;
 
   const int split = blockIdx.x, b = blockIdx.y;
   const int nsplit = gridDim.x;
@@ -503,49 +510,30 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
     }
   }
 
-  // Ticket: make this workgroup's partial visible device-wide, then count it.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sLast = atomicAdd(&a.counters[b], 1) == nsplit - 1;
-  __syncthreads();
-  if (!sLast) return;
-  __threadfence();
+}
 
-  // Last workgroup of sequence b: merge the splits in split order.
-  float* wsc = reinterpret_cast<float*>(sK);  // [H][nsplit] merge weights (sK is free now)
-  for (int hh = tid; hh < H; hh += 256) {
-    const size_t base = static_cast<size_t>(b) * nsplit * H + hh;
-    float M = -INFINITY;
-    for (int k = 0; k < nsplit; ++k) M = fmaxf(M, a.part.m[base + static_cast<size_t>(k) * H]);
-    float L = 0.f;
-    for (int k = 0; k < nsplit; ++k) {
-      const float wk = expf(a.part.m[base + static_cast<size_t>(k) * H] - M);
-      wsc[hh * nsplit + k] = wk;
-      L += a.part.l[base + static_cast<size_t>(k) * H] * wk;
-    }
-    const float inv = 1.f / L;
-    for (int k = 0; k < nsplit; ++k) wsc[hh * nsplit + k] *= inv;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < H * DC; idx += 256) {
-    const int hh = idx / DC, e = idx % DC;
-    float v = 0.f;
-    for (int k = 0; k < nsplit; ++k)
-      v = fmaf(a.part.acc[((static_cast<size_t>(b) * nsplit + k) * H + hh) * DC + e],
-               wsc[hh * nsplit + k], v);
-    a.o_lat[(static_cast<size_t>(b) * H + hh) * DC + e] = v;
-  }
-  if (tid == 0) a.counters[b] = 0;
+// Rows per workgroup of absorb / up-projection: one row while there are few
+// (row, head) pairs, so the launch fills the chip; four when there are many,
+// so each W_UK / W_UV chunk loaded serves four rows.
+int rows_per_wg(int R, int H) { return static_cast<long long>(R) * H > 1024 ? 4 : 1; }
+
+template <typename T, int RB>
+hipError_t absorb_rb(int R, int H, int d_h, int d_c, int d_r, const void* q_c, const void* q_r,
+                     const void* w_uk, float* qbuf, hipStream_t st) {
+  dim3 grid(H, (R + RB - 1) / RB);
+  const size_t smem = (static_cast<size_t>(RB) * d_h + static_cast<size_t>(256 / (d_c / 8)) * RB * d_c) *
+                      sizeof(float);
+  absorb_kernel<T, RB><<<grid, 256, smem, st>>>(R, H, d_h, d_c, d_r, static_cast<const T*>(q_c),
+                                                static_cast<const T*>(q_r),
+                                                static_cast<const T*>(w_uk), qbuf);
+  return hipGetLastError();
 }
 
 template <typename T>
 hipError_t absorb_t(int R, int H, int d_h, int d_c, int d_r, const void* q_c, const void* q_r,
-                    const void* w_uk, float* qbuf, int32_t* counters, int ncount, hipStream_t st) {
-  dim3 grid(H, (R + kAbsorbRB - 1) / kAbsorbRB);
-  absorb_kernel<T><<<grid, 256, kAbsorbRB * d_h * sizeof(float), st>>>(
-      R, H, d_h, d_c, d_r, static_cast<const T*>(q_c), static_cast<const T*>(q_r),
-      static_cast<const T*>(w_uk), qbuf, counters, ncount);
-  return hipGetLastError();
+                    const void* w_uk, float* qbuf, hipStream_t st) {
+  return rows_per_wg(R, H) == 4 ? absorb_rb<T, 4>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st)
+                                : absorb_rb<T, 1>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st);
 }
 
 template <typename T>
@@ -564,25 +552,31 @@ hipError_t attend_t(const AttendArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename T, int RB>
+hipError_t up_project_rb(int R, int H, int d_h, int d_c, const float* o_lat, const void* w_uv,
+                         void* out, hipStream_t st) {
+  int tpo = 1;
+  while (tpo < 64 && 2 * tpo * d_h <= 256) tpo *= 2;
+  dim3 grid(H, (R + RB - 1) / RB);
+  up_project_kernel<T, RB><<<grid, 256, static_cast<size_t>(RB) * d_c * sizeof(float), st>>>(
+      R, H, d_h, d_c, tpo, o_lat, static_cast<const T*>(w_uv), static_cast<T*>(out));
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t up_project_t(int R, int H, int d_h, int d_c, const float* o_lat, const void* w_uv,
                         void* out, hipStream_t st) {
-  dim3 grid(H, (R + kUpRB - 1) / kUpRB);
-  const size_t smem =
-      (static_cast<size_t>(kUpRB) * d_c + static_cast<size_t>(d_h) * (kUpKT + 1)) * sizeof(float);
-  up_project_kernel<T><<<grid, 256, smem, st>>>(R, H, d_h, d_c, o_lat,
-                                                static_cast<const T*>(w_uv), static_cast<T*>(out));
-  return hipGetLastError();
+  return rows_per_wg(R, H) == 4 ? up_project_rb<T, 4>(R, H, d_h, d_c, o_lat, w_uv, out, st)
+                                : up_project_rb<T, 1>(R, H, d_h, d_c, o_lat, w_uv, out, st);
 }
 
 }  // namespace
 
 hipError_t launch_absorb(int R, int H, int d_h, int d_c, int d_r, const void* q_c,
-                         const void* q_r, const void* w_uk, float* qbuf, int32_t* counters,
-                         int ncount, int dtype, hipStream_t st) {
-  return dtype == 0
-             ? absorb_t<float>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, counters, ncount, st)
-             : absorb_t<uint16_t>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, counters, ncount, st);
+                         const void* q_r, const void* w_uk, float* qbuf, int dtype,
+                         hipStream_t st) {
+  return dtype == 0 ? absorb_t<float>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st)
+                    : absorb_t<uint16_t>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st);
 }
 
 hipError_t launch_attend_portable(const AttendArgs& a, int dtype, hipStream_t st) {
@@ -616,6 +610,9 @@ hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st) {
   } else {
     return hipErrorNotSupported;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  split_merge_kernel<<<dim3(a.H, a.R), 256, 0, st>>>(a.H, a.d_c, a.splits, a.part, a.o_lat);
   return hipGetLastError();
 }
 

@@ -28,10 +28,9 @@ hipError_t launch_debug_mask(int n, int s, uint8_t* mask, hipStream_t st);
 hipError_t launch_debug_limits(int n, int s, int32_t* hi, hipStream_t st);
 
 // Absorbed query rows: qbuf[r, h, :] = [W_UK[h]^T q_c[r, h] ; q_r[r, h]] (fp32).
-// If counters is non-null its first ncount entries are set to zero.
 hipError_t launch_absorb(int R, int H, int d_h, int d_c, int d_r, const void* q_c,
-                         const void* q_r, const void* w_uk, float* qbuf, int32_t* counters,
-                         int ncount, int dtype, hipStream_t st);
+                         const void* q_r, const void* w_uk, float* qbuf, int dtype,
+                         hipStream_t st);
 
 // Split partials: m, l [R, splits, H], acc [R, splits, H, d_c] (fp32).
 struct Partials {
@@ -51,14 +50,13 @@ struct AttendArgs {
   const void* diag;     // prefill: partial merges [B, N, W]; decode: nullptr
   Partials part;
   float* o_lat;         // [R, H, d_c] output (fp32)
-  int32_t* counters;    // [R] split tickets, zero on entry and on exit (MFMA path)
 };
 
 // Vector-ALU split attention + split merge (any shape, fp32 or bf16 storage).
 hipError_t launch_attend_portable(const AttendArgs& a, int dtype, hipStream_t st);
 
-// MFMA latent attention for decode (bf16 storage), one kernel including the
-// split merge.  Returns hipErrorNotSupported when no instantiation covers
+// MFMA latent attention for decode (bf16 storage); a split-merge kernel
+// follows when splits > 1.  Returns hipErrorNotSupported when no instantiation covers
 // (H, d_c, d_r).
 bool decode_mfma_supported(int H, int d_c, int d_r);
 hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st);

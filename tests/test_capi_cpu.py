@@ -65,6 +65,8 @@ BAD_DIMS = [
     (dict(stride_s=257), m.MTLA_ERR_UNSUPPORTED),
     (dict(d_c=1000, d_r=64), m.MTLA_ERR_UNSUPPORTED),
     (dict(d_h=512), m.MTLA_ERR_UNSUPPORTED),
+    (dict(d_c=252), m.MTLA_ERR_UNSUPPORTED),
+    (dict(d_r=30), m.MTLA_ERR_UNSUPPORTED),
 ]
 
 

@@ -109,13 +109,13 @@ def test_decode_ragged_and_invalid_positions(portable):
         assert oracle.max_rel_err(out[b], want) <= 1e-2, b
 
 
-@pytest.mark.parametrize("shape,portable,B", [("st", False, 3), ("llm", False, 4), ("st", True, 2),
-                                              ("st", False, 80)])
-def test_staged_decode_equals_fused_call(shape, portable, B):
-    """absorb -> decode_attention -> up_project gives the bits of mtla_decode;
-    the attention's split counters are left at zero, so calls can repeat."""
+@pytest.mark.parametrize("shape,portable,B,N", [("st", False, 3, 900), ("llm", False, 4, 2500),
+                                                ("st", True, 2, 900), ("st", False, 80, 3000)])
+def test_staged_decode_equals_fused_call(shape, portable, B, N):
+    """absorb -> decode_attention -> up_project gives the bits of mtla_decode,
+    with one split and with several, call after call."""
     import temporally_compressed_latent_amd as m
-    N, s = 900, 2
+    s = 2
     inp, g = make_case(shape, 12, B, N, s, "bf16", portable, q_rows=1)
     g.append(torch.ones(B, dtype=torch.int32, device=DEV), 0, N)
     pos = torch.full((B,), N, dtype=torch.int32, device=DEV)
@@ -130,4 +130,18 @@ def test_staged_decode_equals_fused_call(shape, portable, B):
         m.mtla_decode_attention(d, pos, q_lat, g.cache, o_lat, ws)
         m.mtla_up_project(d, o_lat, g.w_uv, out)
         assert torch.equal(bits(out), bits(fused))
-        assert int(ws[:4 * B].view(torch.int32).abs().sum()) == 0
+
+
+def test_positions_need_only_element_alignment():
+    """pos / pos0 may start at any 4-byte boundary (rows of a [T, B] array)."""
+    B, N, s = 3, 20, 2
+    inp, g = make_case("st", 13, B, N, s, "bf16")
+    _, ref = make_case("st", 13, B, N, s, "bf16")
+    table = torch.arange(0, N + 1, dtype=torch.int32, device=DEV)[:, None].expand(N + 1, B).contiguous()
+    assert table[1].data_ptr() % 16 != 0
+    for t in range(1, N + 1):
+        g.append(table[t], t - 1, t)
+        ref.append(torch.full((B,), t, dtype=torch.int32, device=DEV), t - 1, t)
+    a = g.decode(table[N], N - 1)
+    b = ref.decode(torch.full((B,), N, dtype=torch.int32, device=DEV), N - 1)
+    assert torch.equal(bits(a), bits(b))
