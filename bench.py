@@ -6,18 +6,18 @@
 Headline workload (the JSON line's ``value``): speech-translation-shaped
 decoding, batch 50 (10 sentences x beam 5), 512 tokens, H=8, d_h=64, d_c=256,
 d_R=32, s=2, bf16 storage.  One step is the whole 512-token decode of the
-batch: for every token, mtla_merge_append (gate + temporal merge) then
-mtla_decode (absorb, latent attention over ceil(t/s) slots, up-projection).
-The 512 x 4 kernel launches of a step are captured once in a HIP graph and
-replayed; inputs are resident in HBM before the timed region.
+batch: for every token, mtla_decode_step (gate + temporal merge of the token,
+query absorption, latent attention over ceil(t/s) slots, up-projection).
+The 512 launches of a step are captured once in a HIP graph and replayed;
+inputs are resident in HBM before the timed region.
 
 The other workloads are reported in ``components``: the s=4 decode loop
 (2048 tokens), the summarisation-shaped prefill (B=16, N=4096, s=3) and the
 LLM-scale step (B=64, cache of 32,768 tokens, one append + decode).
 
-``roofline`` describes the dominant kernel of the headline step, the latent
-attention (mtla_decode_attention), timed live with HIP events on its own
-graph of the same 512 launches.  ``cpu_baseline`` is the fp64 oracle (test
+``roofline`` describes the dominant kernel of the headline step: the fused
+decode-step kernel, the step's only kernel, so its average launch duration is
+the timed graph replay (HIP events) divided by the 512 launches.  ``cpu_baseline`` is the fp64 oracle (test
 infrastructure, single-threaded) timed on this host over the same workload.
 """
 from __future__ import annotations
@@ -101,8 +101,8 @@ class DecodeLoop:
         wts = workloads.weights(w)
         bf = torch.bfloat16
         # per-step slices must be contiguous: stage token-major copies
-        self.c = to_dev(np.ascontiguousarray(lat["c"].transpose(1, 0, 2)[:, :, None]), bf, torch)
-        self.k_r = to_dev(np.ascontiguousarray(lat["k_r"].transpose(1, 0, 2)[:, :, None]), bf, torch)
+        self.c = to_dev(np.ascontiguousarray(lat["c"].transpose(1, 0, 2)), bf, torch)
+        self.k_r = to_dev(np.ascontiguousarray(lat["k_r"].transpose(1, 0, 2)), bf, torch)
         self.q_c = to_dev(np.ascontiguousarray(qry["q_c"].transpose(1, 0, 2, 3)), bf, torch)
         self.q_r = to_dev(np.ascontiguousarray(qry["q_r"].transpose(1, 0, 2, 3)), bf, torch)
         self.w_hyp = to_dev(wts["w_hyp"], torch.float32, torch)
@@ -121,57 +121,51 @@ class DecodeLoop:
     def step(self):
         m, d = self.m, self.dims
         for t in range(self.w.n_tokens):
-            m.mtla_merge_append(d, self.pos[t], self.c[t], self.k_r[t], self.w_hyp, self.pe,
-                                self.cache, self.open_acc)
-            m.mtla_decode(d, self.pos[t], self.q_c[t], self.q_r[t], self.w_uk, self.w_uv,
-                          self.cache, self.out[t], self.ws)
-
-    def attention_only(self):
-        """Graph of the step's latent-attention launches alone: the same
-        positions (so the same slot count per launch) and queries, over the
-        cache the loop leaves behind.  Its last slot may hold a later token than
-        the loop's step saw, which changes values, not work."""
-        torch, m, d, w = self.torch, self.m, self.dims, self.w
-        N, B, H = w.n_tokens, w.batch, w.heads
-        q_lat = torch.empty(N, B, H, d.width, dtype=torch.float32, device="cuda")
-        for t in range(N):
-            m.mtla_absorb_query(d, self.q_c[t], self.q_r[t], self.w_uk, q_lat[t])
-        o_lat = torch.empty(N, B, H, d.d_c, dtype=torch.float32, device="cuda")
-        ws = m.decode_attention_workspace(d)
-
-        def fn():
-            for t in range(N):
-                m.mtla_decode_attention(d, self.pos[t], q_lat[t], self.cache, o_lat[t], ws)
-        return capture(fn, torch)
+            m.mtla_decode_step(d, self.pos[t], self.c[t], self.k_r[t], self.w_hyp, self.pe,
+                               self.q_c[t], self.q_r[t], self.w_uk, self.w_uv, self.cache,
+                               self.open_acc, self.out[t], self.ws)
 
 
-def run_decode_loop(w, steps, warmup, m, torch, workloads, with_kernel=True):
+def step_bytes(w, t):
+    """Algorithmic HBM bytes of one decode-step launch at token t (bf16
+    storage): slot rows read, W_UK and W_UV, and the per-token terms (token
+    latent and rope key, queries, outputs, the written slot row, the fp32
+    open-slot state read and written, the pe row and W_hyp)."""
+    e, B, H = 2, w.batch, w.heads
+    n = -(-t // w.s)
+    cache = B * n * w.width * e
+    weights = 2 * H * w.d_h * w.d_c * e + w.d_c * 4
+    token = B * (w.width * e + H * (w.d_h + w.d_r) * e + H * w.d_h * e + w.width * e
+                 + 2 * w.width * 4 + w.d_c * 4)
+    return cache, weights, token
+
+
+def run_decode_loop(w, steps, warmup, m, torch, workloads):
     log(f"{w.name}: staging inputs")
     t0 = time.time()
     dl = DecodeLoop(w, m, torch, workloads)
-    log(f"{w.name}: staged in {time.time() - t0:.1f}s; capturing {w.n_tokens} steps")
+    splits, fused = m.mtla_decode_plan(dl.dims)
+    log(f"{w.name}: staged in {time.time() - t0:.1f}s; plan splits={splits} fused={fused}; "
+        f"capturing {w.n_tokens} steps")
     g = capture(dl.step, torch)
     for _ in range(warmup):
         g.replay()
     ms = timed_graph(g, steps, torch)
     tokens = w.batch * w.n_tokens
+    per_t = [step_bytes(w, t) for t in range(1, w.n_tokens + 1)]
+    cache_b = sum(p[0] for p in per_t)
+    all_b = sum(sum(p) for p in per_t)
     rec = {"workload": w.name, "ms_per_step": ms, "tokens_per_step": tokens,
-           "tokens_per_s": tokens / (ms * 1e-3), "us_per_token_step": ms * 1e3 / w.n_tokens}
-    # algorithmic bytes of a step: slot rows read + W_UK/W_UV once per token
-    e = 2
-    cache_bytes = w.batch * slot_reads(w.n_tokens, w.s) * w.width * e
-    weight_bytes = w.n_tokens * 2 * w.heads * w.d_h * w.d_c * e
-    rec["step_GBps"] = (cache_bytes + weight_bytes) / (ms * 1e-3) / 1e9
-    if with_kernel:
-        ga = dl.attention_only()
-        for _ in range(warmup):
-            ga.replay()
-        ams = timed_graph(ga, steps, torch) / w.n_tokens
-        per_launch = cache_bytes / w.n_tokens
-        rec["attention_kernel"] = {
-            "name": "decode_mfma_kernel", "avg_launch_us": ams * 1e3,
-            "algorithmic_bytes_per_launch": per_launch,
-            "GBps": per_launch / (ams * 1e-3) / 1e9}
+           "tokens_per_s": tokens / (ms * 1e-3), "us_per_token": ms * 1e3 / w.n_tokens,
+           "plan": {"splits": splits, "fused": fused},
+           "step_GBps": all_b / (ms * 1e-3) / 1e9,
+           "cache_GBps": cache_b / (ms * 1e-3) / 1e9}
+    if fused:
+        per_launch = all_b / w.n_tokens
+        us = ms * 1e3 / w.n_tokens
+        rec["dominant_kernel"] = {
+            "name": "decode_step_kernel", "launches_per_step": w.n_tokens, "avg_launch_us": us,
+            "algorithmic_bytes_per_launch": per_launch, "GBps": per_launch / (us * 1e-6) / 1e9}
     return rec, dl
 
 
@@ -255,13 +249,13 @@ def run_llm_decode(w, steps, warmup, m, torch, workloads):
     m.mtla_merge_append(d, one, c_dev[:, :N].contiguous(), kr_dev[:, :N].contiguous(), w_hyp, pe,
                         cache, open_acc)
     pos = torch.full((B,), T, dtype=torch.int32, device="cuda")
-    c_t, kr_t = c_dev[:, N:T].contiguous(), kr_dev[:, N:T].contiguous()
+    c_t, kr_t = c_dev[:, N].contiguous(), kr_dev[:, N].contiguous()
     out = torch.empty(B, H, w.d_h, dtype=bf, device="cuda")
     ws = torch.zeros(m.mtla_decode_workspace_bytes(d), dtype=torch.uint8, device="cuda")
 
     def step():
-        m.mtla_merge_append(d, pos, c_t, kr_t, w_hyp, pe, cache, open_acc)
-        m.mtla_decode(d, pos, q_c, q_r, w_uk, w_uv, cache, out, ws)
+        m.mtla_decode_step(d, pos, c_t, kr_t, w_hyp, pe, q_c, q_r, w_uk, w_uv, cache, open_acc,
+                           out, ws)
     g = capture(step, torch)
     reps = max(steps, 20)
     for _ in range(max(warmup, 5)):
@@ -280,11 +274,13 @@ def run_llm_decode(w, steps, warmup, m, torch, workloads):
     cache_bytes = B * n_slots * d.width * 2
     weight_bytes = 2 * H * w.d_h * w.d_c * 2
     flops = 2.0 * B * H * n_slots * (2 * w.d_c + w.d_r) + 4.0 * B * H * w.d_h * w.d_c
+    splits, fused = m.mtla_decode_plan(d)
     rec = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
+           "plan": {"splits": splits, "fused": fused},
            "slots_per_seq": n_slots, "step_GBps": (cache_bytes + weight_bytes) / (ms * 1e-3) / 1e9,
            "step_frac_hbm": (cache_bytes + weight_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "step_tflops": flops / (ms * 1e-3) / 1e12,
-           "attention_kernel": {"name": "decode_mfma_kernel", "avg_launch_us": ams * 1e3,
+           "attention": {"kernels": "decode_mfma_kernel + split_merge_kernel", "avg_call_us": ams * 1e3,
                                 "algorithmic_bytes_per_launch": cache_bytes,
                                 "GBps": cache_bytes / (ams * 1e-3) / 1e9,
                                 "frac_hbm": cache_bytes / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS}}
@@ -360,7 +356,7 @@ def main():
         log("timing the oracle on the host")
         cpu, err = cpu_baseline_and_parity(w, dl, torch)
 
-    k = head["attention_kernel"]
+    k = head["dominant_kernel"]
     achieved = k["GBps"]
     line = {
         "metric": METRIC,
@@ -382,9 +378,11 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "avg_launch_us": k["avg_launch_us"],
                      "algorithmic_bytes_per_launch": k["algorithmic_bytes_per_launch"]},
+        "plan": head["plan"],
         "cpu_baseline": cpu,
         "max_rel_err": err,
         "step_GBps": head["step_GBps"],
+        "us_per_token": head["us_per_token"],
         "components": comps,
     }
     print(json.dumps(line), flush=True)

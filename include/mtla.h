@@ -151,6 +151,29 @@ int32_t mtla_decode(const mtla_dims* dims, const int32_t* pos, const void* q_c,
                     void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Host-only query of how mtla_decode / mtla_decode_step will run for these
+ * dims: *splits = slot splits of the latent attention, *fused = 1 when one
+ * kernel (one workgroup per sequence) does the whole step.
+ */
+int32_t mtla_decode_plan(const mtla_dims* dims, int32_t* splits, int32_t* fused);
+
+/*
+ * One decode step: merge token pos[b] (mtla_merge_append with n_tokens = 1)
+ * and decode it (mtla_decode), in one call.  Same arguments as those two
+ * calls: c [B, d_c], k_r [B, d_r] are the token's latent and rotated rope
+ * key; everything else as above (workspace: mtla_decode_workspace_bytes()).
+ * Page: "Multi-head Temporal Latent Attention", Method (1): during inference
+ * each step updates the open slot (or opens a new one) and attends
+ * ceil(t/s) slots.  For a short cache (one split) with bf16 storage this is
+ * a single kernel with one workgroup per sequence.
+ */
+int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
+                         const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                         const void* q_r, const void* w_uk, const void* w_uv, void* cache,
+                         float* open_acc, void* out, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/*
  * Staged form of mtla_decode, for callers that fuse the two projections into
  * their own GEMMs (mtla_decode runs exactly these three stages).
  *

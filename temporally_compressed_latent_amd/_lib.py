@@ -70,7 +70,7 @@ class MtlaError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m temporally_compressed_latent_amd.build` "
+            f"{LIB_PATH} is not built; run `python temporally_compressed_latent_amd/build.py` "
             "(the MTLA path has no CPU fallback)")
     return ctypes.CDLL(LIB_PATH)
 
@@ -90,6 +90,8 @@ _SIGS = {
     "mtla_merge_append": (_I, [_D, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
     "mtla_decode_workspace_bytes": (_I, [_D, ctypes.POINTER(_SZ)]),
     "mtla_decode": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mtla_decode_plan": (_I, [_D, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "mtla_decode_step": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_absorb_query": (_I, [_D, _I, _P, _P, _P, _P, _P]),
     "mtla_decode_attention_workspace_bytes": (_I, [_D, ctypes.POINTER(_SZ)]),
     "mtla_decode_attention": (_I, [_D, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -230,6 +232,34 @@ def mtla_decode(dims: MtlaDims, pos, q_c, q_r, w_uk, w_uv, cache, out, workspace
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
         _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("out", out, (B, H, dims.d_h), st),
+        ws, ws_bytes, _stream(stream)))
+
+
+def mtla_decode_plan(dims: MtlaDims) -> tuple:
+    """(splits, fused) of the decode path these dims take."""
+    sp, fu = _I(0), _I(0)
+    _check(_lib.mtla_decode_plan(ctypes.byref(dims), ctypes.byref(sp), ctypes.byref(fu)))
+    return sp.value, bool(fu.value)
+
+
+def mtla_decode_step(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w_uk, w_uv, cache, open_acc,
+                     out, workspace, stream=None) -> None:
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    _check(_lib.mtla_decode_step(
+        ctypes.byref(dims),
+        _tensor("pos", pos, (B,), torch.int32),
+        _tensor("c", c, (B, dims.d_c), st),
+        _tensor("k_r", k_r, (B, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("q_c", q_c, (B, H, dims.d_h), st),
+        _tensor("q_r", q_r, (B, H, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("open_acc", open_acc, (B, dims.width), torch.float32),
         _tensor("out", out, (B, H, dims.d_h), st),
         ws, ws_bytes, _stream(stream)))
 

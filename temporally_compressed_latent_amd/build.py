@@ -1,6 +1,6 @@
 """Build libmtla.so (HIP kernels + C ABI) for gfx950, in-tree.
 
-    python -m temporally_compressed_latent_amd.build
+    python temporally_compressed_latent_amd/build.py
 
 Each source compiles to its own object (in parallel), then hipcc links the
 shared library next to this file.  Packed-fp32 instruction forms are disabled

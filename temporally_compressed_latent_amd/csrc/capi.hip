@@ -117,6 +117,13 @@ int decode_splits(const mtla_dims* d) {
   return clampi(ceil_div(d->max_slots, 128), 1, 32);
 }
 
+// One workgroup per sequence runs the whole step (merge, absorb, attention,
+// up-projection) when the cache needs a single split and the weights are small.
+bool decode_fused(const mtla_dims* d) {
+  return decode_fast(d) && decode_splits(d) == 1 &&
+         mtla::decode_step_supported(d->heads, d->d_h, d->d_c, d->d_r);
+}
+
 int prefill_splits(const mtla_dims* d, int n_tokens) {
   return clampi(ceil_div(n_tokens / d->stride_s + 1, 128), 1, 16);
 }
@@ -268,6 +275,15 @@ int32_t mtla_up_project(const mtla_dims* dims, int32_t n_rows, const float* o_la
                     "up-projection launch");
 }
 
+int32_t mtla_decode_plan(const mtla_dims* dims, int32_t* splits, int32_t* fused) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (!splits || !fused) return fail(MTLA_ERR_INVALID_ARG, "splits and fused must be non-NULL");
+  *splits = decode_splits(dims);
+  *fused = decode_fused(dims) ? 1 : 0;
+  return ok();
+}
+
 int32_t mtla_decode_attention_workspace_bytes(const mtla_dims* dims, size_t* bytes) {
   int32_t st = check_dims(dims);
   if (st != MTLA_OK) return st;
@@ -321,6 +337,38 @@ int32_t mtla_decode_workspace_bytes(const mtla_dims* dims, size_t* bytes) {
   return ok();
 }
 
+namespace {
+
+mtla::StepArgs step_args(const mtla_dims* d, const int32_t* pos, const void* c, const void* k_r,
+                         const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                         const void* q_r, const void* w_uk, const void* w_uv, void* cache,
+                         float* open_acc, void* out, int merge) {
+  return mtla::StepArgs{d->batch, d->heads, d->d_h, d->d_c, d->d_r, d->stride_s, d->max_slots,
+                        pe_rows, merge, d->softmax_scale, pos,
+                        static_cast<const uint16_t*>(c), static_cast<const uint16_t*>(k_r), w_hyp,
+                        pe, static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
+                        static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv),
+                        static_cast<uint16_t*>(cache), open_acc, static_cast<uint16_t*>(out)};
+}
+
+// absorb -> latent attention (-> split merge) -> up-projection
+hipError_t run_decode_pipeline(const mtla_dims* dims, const int32_t* pos, const void* q_c,
+                               const void* q_r, const void* w_uk, const void* w_uv,
+                               const void* cache, void* out, void* workspace, const DecodeWs& ws,
+                               hipStream_t s) {
+  const int B = dims->batch, H = dims->heads;
+  float* q_lat = reinterpret_cast<float*>(at(workspace, ws.qlat));
+  float* o_lat = reinterpret_cast<float*>(at(workspace, ws.olat));
+  hipError_t e = mtla::launch_absorb(B, H, dims->d_h, dims->d_c, dims->d_r, q_c, q_r, w_uk, q_lat,
+                                     dims->dtype, s);
+  if (e != hipSuccess) return e;
+  e = run_decode_attention(dims, pos, q_lat, cache, o_lat, workspace, ws.attn, s);
+  if (e != hipSuccess) return e;
+  return mtla::launch_up_project(B, H, dims->d_h, dims->d_c, o_lat, w_uv, out, dims->dtype, s);
+}
+
+}  // namespace
+
 int32_t mtla_decode(const mtla_dims* dims, const int32_t* pos, const void* q_c, const void* q_r,
                     const void* w_uk, const void* w_uv, const void* cache, void* out,
                     void* workspace, size_t ws_bytes, void* stream) {
@@ -339,18 +387,54 @@ int32_t mtla_decode(const mtla_dims* dims, const int32_t* pos, const void* q_c, 
   if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   if (ws_bytes < ws.total)
     return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, ws.total);
-
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int B = dims->batch, H = dims->heads;
-  float* q_lat = reinterpret_cast<float*>(at(workspace, ws.qlat));
-  float* o_lat = reinterpret_cast<float*>(at(workspace, ws.olat));
-  hipError_t e = mtla::launch_absorb(B, H, dims->d_h, dims->d_c, dims->d_r, q_c, q_r, w_uk, q_lat,
-                                     dims->dtype, s);
-  if (e != hipSuccess) return hip_status(e, "absorb launch");
-  e = run_decode_attention(dims, pos, q_lat, cache, o_lat, workspace, ws.attn, s);
-  if (e != hipSuccess) return hip_status(e, "decode attention launch");
-  e = mtla::launch_up_project(B, H, dims->d_h, dims->d_c, o_lat, w_uv, out, dims->dtype, s);
-  return hip_status(e, "up-projection launch");
+  if (decode_fused(dims)) {
+    const mtla::StepArgs a = step_args(dims, pos, nullptr, nullptr, nullptr, nullptr, 0, q_c, q_r,
+                                       w_uk, w_uv, const_cast<void*>(cache), nullptr, out, 0);
+    return hip_status(mtla::launch_decode_step(a, s), "decode step launch");
+  }
+  return hip_status(run_decode_pipeline(dims, pos, q_c, q_r, w_uk, w_uv, cache, out, workspace, ws, s),
+                    "decode launch");
+}
+
+int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
+                         const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                         const void* q_r, const void* w_uk, const void* w_uv, void* cache,
+                         float* open_acc, void* out, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (pe_rows < 1) return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < 1", pe_rows);
+  if (dims->batch == 0) return ok();
+  CHECK_PTR_ALIGN(pos, 4);
+  CHECK_PTR(c);
+  if (dims->d_r > 0) CHECK_PTR(k_r);
+  CHECK_PTR_ALIGN(w_hyp, 4);
+  CHECK_PTR_ALIGN(pe, 4);
+  CHECK_PTR(q_c);
+  if (dims->d_r > 0) CHECK_PTR(q_r);
+  CHECK_PTR(w_uk);
+  CHECK_PTR(w_uv);
+  CHECK_PTR(cache);
+  CHECK_PTR_ALIGN(open_acc, 4);
+  CHECK_PTR(out);
+  const DecodeWs ws = decode_ws(dims);
+  if (!workspace) return fail(MTLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws.total);
+  if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (ws_bytes < ws.total)
+    return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, ws.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (decode_fused(dims)) {
+    const mtla::StepArgs a = step_args(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv,
+                                       cache, open_acc, out, 1);
+    return hip_status(mtla::launch_decode_step(a, s), "decode step launch");
+  }
+  mtla::MergeArgs m{dims->batch, 1, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, pe_rows,
+                    pos, c, k_r, w_hyp, pe, cache, open_acc, nullptr, nullptr};
+  hipError_t e = mtla::launch_merge(m, dims->dtype, s);
+  if (e != hipSuccess) return hip_status(e, "merge launch");
+  return hip_status(run_decode_pipeline(dims, pos, q_c, q_r, w_uk, w_uv, cache, out, workspace, ws, s),
+                    "decode launch");
 }
 
 int32_t mtla_prefill_workspace_bytes(const mtla_dims* dims, int32_t n_tokens, size_t* bytes) {

@@ -8,6 +8,10 @@ namespace mtla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -87,5 +91,70 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Gates of NTOK tokens, computed by one wave ("Multi-head Temporal Latent
+// Attention", Key claims, paper Sec. 4.1 Eq. 13):
+//   w_t = sigmoid(W_hyp . (c_t + pe_t)).
+// For each token, lane l accumulates columns l, l+64, ... in order and the
+// lanes are then added with a butterfly; the NTOK tokens are independent
+// instruction streams, so their loads are in flight together.  Every kernel
+// that gates a token uses this arithmetic, so a token gets bit-identical
+// gates whichever entry point merges it.  Tokens with c_rows[k] == nullptr
+// are skipped (their gate is 0).
+template <int NTOK, typename T>
+__device__ __forceinline__ void gates_of_tokens(const T* const (&c_rows)[NTOK],
+                                                const float* const (&pe_rows)[NTOK],
+                                                const float* w_hyp, int d_c, int lane,
+                                                float (&w)[NTOK]) {
+  float acc[NTOK];
+#pragma unroll
+  for (int k = 0; k < NTOK; ++k) acc[k] = 0.f;
+  for (int e = lane; e < d_c; e += 64) {
+    const float wh = w_hyp[e];
+#pragma unroll
+    for (int k = 0; k < NTOK; ++k)
+      if (c_rows[k]) acc[k] = fmaf(Store<T>::load(c_rows[k], e) + pe_rows[k][e], wh, acc[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < NTOK; ++k) {
+    const float z = wave_sum(acc[k]);
+    w[k] = c_rows[k] ? 1.f / (1.f + expf(-z)) : 0.f;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float gate_of_token(const T* c_row, const float* pe_row,
+                                               const float* w_hyp, int d_c, int lane) {
+  const T* const rows[1] = {c_row};
+  const float* const pes[1] = {pe_row};
+  float w[1];
+  gates_of_tokens<1, T>(rows, pes, w_hyp, d_c, lane, w);
+  return w[0];
+}
+
+// Eight consecutive fp32 values stored to the storage type (16-byte aligned
+// for bf16, 32 for fp32), rounded to nearest even.
+__device__ __forceinline__ void store8(uint16_t* p, const float* v) {
+  uint4 u;
+  u.x = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+  u.y = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+  u.z = static_cast<uint32_t>(f32_to_bf16_bits(v[4])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[5])) << 16);
+  u.w = static_cast<uint32_t>(f32_to_bf16_bits(v[6])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[7])) << 16);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<float4*>(p + 4) = float4{v[4], v[5], v[6], v[7]};
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane k supplies the address of 4 consecutive 16-bit values; lane i receives
+// as element r the (i % 4)-th value of lane 4r + i/4.  With lane k pointing at
+// row base + k/4, columns col0 + 4*(k%4) of a row-major tile, lane i gets
+// rows base..base+3 of column col0 + i: a K-contiguous MFMA operand read from
+// a tile whose contiguous dimension is the MFMA's M or N.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
 
 }  // namespace mtla

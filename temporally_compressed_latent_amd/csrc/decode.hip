@@ -251,56 +251,240 @@ __global__ __launch_bounds__(256) void up_project_kernel(int R, int H, int d_h, 
 }
 
 // ---------------------------------------------------------------------------
-// MFMA latent attention for decode (bf16 cache).  One workgroup (4 waves) per
-// (split, sequence), all heads padded to HT*16 MFMA rows.
+// MFMA latent attention core (bf16 cache), shared by the split-K decode
+// kernel and the fused one-token step kernel.  A workgroup of NW waves takes
+// all heads of one sequence (padded to HT*16 MFMA rows) over a slot range.
 //
-// Per 64-slot tile:
-//   1. the tile (64 rows x W bf16) is copied HBM -> registers -> LDS, and the
+// Per TS-slot tile:
+//   1. the tile (TS rows x W bf16) is copied HBM -> registers -> LDS, and the
 //      next tile's loads are issued before this tile is used;
-//   2. scores S[head, slot] = Q~ . row via v_mfma_f32_16x16x32_bf16; wave w
-//      owns slots 16w..16w+15, A = scaled queries (LDS), B = slot rows (LDS);
+//   2. scores S[head, slot] = Q~ . row via v_mfma_f32_16x16x32_bf16; the first
+//      TS/16 waves own 16 slots each, A = scaled queries (LDS), B = rows (LDS);
 //   3. the tile max per head is shared through LDS, p = exp2(S - m) goes to
-//      LDS as bf16, and the running (m, l, acc) are rescaled;
+//      LDS as bf16, and every wave rescales its running (m, acc);
 //   4. acc[head, col] += P . rows, wave w owning latent columns
-//      w*DC/4 .. (w+1)*DC/4-1.  The B operand (8 slots of one column) comes
+//      w*DC/NW .. (w+1)*DC/NW-1.  The B operand (8 slots of one column) comes
 //      from two ds_read_b64_tr_b16 transposing loads of the row-major tile.
 // Scores are carried in the log2 domain (queries pre-scaled by tau*log2 e).
-//
-// With a single split the workgroup normalises and writes o_lat itself;
-// otherwise it stores its (m, l, acc) partial and split_merge_kernel, launched
-// next on the stream, merges the splits in split order.  (A last-arriving-
-// workgroup merge inside this kernel would need device-scope release/acquire
-// fences per workgroup, which on this multi-XCD part write back and invalidate
-// L2 and cost far more than the extra launch.)
 // ---------------------------------------------------------------------------
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+template <int HT, int DC, int DR, int NW, int TS>
+struct MfmaAttn {
+  static constexpr int W = DC + DR;
+  static constexpr int KS = W / 32;
+  static constexpr int HP = HT * 16;
+  static constexpr int PITCH = W + 8;  // LDS row pitch (elements)
+  static constexpr int PP = TS + 8;    // probability tile pitch
+  static constexpr int QKW = TS / 16;  // waves that score
+  static constexpr int CPW = DC / NW;  // PV latent columns per wave
+  static constexpr int CT = CPW / 16;
+  static constexpr int CPR = W / 8;    // 16-byte chunks per row
+  static constexpr int NT = NW * 64;
+  static constexpr int CHUNKS = TS * CPR;
+  static constexpr int CPT = (CHUNKS + NT - 1) / NT;
+  static_assert(W % 32 == 0 && TS % 32 == 0 && QKW <= NW, "tile shape");
+  static_assert(DC % NW == 0 && CPW % 16 == 0, "column split");
 
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-}
+  struct __align__(16) Smem {
+    uint16_t q[HP * PITCH];
+    uint16_t k[TS * PITCH];
+    uint16_t p[HP * PP];
+    float red[NW][HP];
+  };
 
+  struct State {
+    float m[HT][4];
+    float l[HT][4];
+    f32x4 acc[HT][CT];
+  };
+
+  __device__ __forceinline__ static void init(State& st) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st.m[ht][i] = -INFINITY;
+        st.l[ht][i] = 0.f;
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) st.acc[ht][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Issue the loads of tile j0 of slots [lo, hi) into registers.  Rows past
+  // hi are zero; the row patch_row is skipped (it is filled from LDS when the
+  // tile is stored).
+  __device__ __forceinline__ static void load_tile(uint4* pre, const uint16_t* rows, int j0, int hi,
+                                   int patch_row) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int id = tid + NT * k;
+      if (CHUNKS % NT == 0 || id < CHUNKS) {
+        const int row = id / CPR, ch = id % CPR;
+        const int slot = j0 + row;
+        if (slot >= hi)
+          pre[k] = uint4{0u, 0u, 0u, 0u};
+        else if (slot != patch_row)
+          pre[k] = *reinterpret_cast<const uint4*>(rows + static_cast<size_t>(slot) * W + ch * 8);
+      }
+    }
+  }
+
+  // Slots [lo, hi) of the sequence's rows `rows` (W bf16 each), the first
+  // tile already loaded into `pre` by load_tile.  When patch_row >= 0 that row
+  // is taken from `patch` (LDS) instead of memory.
+  template <bool kPatch>
+  __device__ __forceinline__ static void run(State& st, Smem& sm, const uint16_t* rows, int lo, int hi,
+                                             int patch_row, const uint16_t* patch, uint4* pre) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    auto store_tile = [&](int j0) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int id = tid + NT * k;
+        if (CHUNKS % NT == 0 || id < CHUNKS) {
+          const int row = id / CPR, ch = id % CPR;
+          uint4 v = pre[k];
+          if constexpr (kPatch) {
+            if (j0 + row == patch_row) v = *reinterpret_cast<const uint4*>(patch + ch * 8);
+          }
+          *reinterpret_cast<uint4*>(sm.k + row * PITCH + ch * 8) = v;
+        }
+      }
+    };
+
+    for (int j0 = lo; j0 < hi; j0 += TS) {
+      store_tile(j0);
+      __syncthreads();
+      if (j0 + TS < hi) load_tile(pre, rows, j0 + TS, hi, patch_row);
+
+      f32x4 sc[HT];
+      if (wave < QKW) {
+        // scores: wave owns slots 16*wave .. 16*wave+15 of the tile
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) sc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 bk =
+              *reinterpret_cast<const bf16x8*>(sm.k + (16 * wave + c16) * PITCH + ks * 32 + 8 * g);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            const bf16x8 aq =
+                *reinterpret_cast<const bf16x8*>(sm.q + (ht * 16 + c16) * PITCH + ks * 32 + 8 * g);
+            sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, sc[ht], 0, 0, 0);
+          }
+        }
+        // sc[ht][i] = score of head ht*16 + 4g + i against slot j0 + 16*wave + c16
+        const bool valid = j0 + 16 * wave + c16 < hi;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = valid ? sc[ht][i] : -INFINITY;
+            sc[ht][i] = v;
+            v = fmaxf(v, __shfl_xor(v, 1, 64));
+            v = fmaxf(v, __shfl_xor(v, 2, 64));
+            v = fmaxf(v, __shfl_xor(v, 4, 64));
+            v = fmaxf(v, __shfl_xor(v, 8, 64));
+            if (c16 == 0) sm.red[wave][ht * 16 + 4 * g + i] = v;
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int head = ht * 16 + 4 * g + i;
+          float mt = sm.red[0][head];
+#pragma unroll
+          for (int w = 1; w < QKW; ++w) mt = fmaxf(mt, sm.red[w][head]);
+          const float mn = fmaxf(st.m[ht][i], mt);
+          const float alpha = fast_exp2(st.m[ht][i] - mn);
+          st.m[ht][i] = mn;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) st.acc[ht][ct][i] *= alpha;
+          if (wave < QKW) {
+            const float pv = fast_exp2(sc[ht][i] - mn);
+            st.l[ht][i] = st.l[ht][i] * alpha + pv;
+            sm.p[head * PP + 16 * wave + c16] = f32_to_bf16_bits(pv);
+          }
+        }
+      }
+      __syncthreads();
+
+      // acc[head, col] += sum_slot P[head, slot] * row[slot, col]
+#pragma unroll
+      for (int ks2 = 0; ks2 < TS / 32; ++ks2) {
+        bf16x8 ap[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          ap[ht] = *reinterpret_cast<const bf16x8*>(sm.p + (ht * 16 + c16) * PP + ks2 * 32 + 8 * g);
+        // Lane (g, c16) needs rows ks2*32 + 8g + 0..7 of column col0 + c16.  A
+        // transposing read covers 4 rows: lane k of a 16-lane group points at
+        // row base + k/4, columns col0 + 4*(k%4) .. +3; lane i then receives as
+        // element r the (i%4)-th value of lane 4r + i/4, i.e. row base + r of
+        // column col0 + i.
+        const uint16_t* rbase = sm.k + (ks2 * 32 + 8 * g + (c16 >> 2)) * PITCH + 4 * (c16 & 3);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int col0 = wave * CPW + ct * 16;
+          const s16x4 lo4 = lds_read_tr16(rbase + col0);
+          const s16x4 hi4 = lds_read_tr16(rbase + 4 * PITCH + col0);
+          const s16x8 v8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 bb = __builtin_bit_cast(bf16x8, v8);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+            st.acc[ht][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[ht], bb, st.acc[ht][ct], 0, 0, 0);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // Softmax denominators: sum over the 16 slot lanes and the scoring waves,
+  // in a fixed order.  Leaves L of head h in sm.red[0][h].
+  __device__ __forceinline__ static void finish(State& st, Smem& sm) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    if (wave < QKW) {
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = st.l[ht][i];
+          v += __shfl_xor(v, 1, 64);
+          v += __shfl_xor(v, 2, 64);
+          v += __shfl_xor(v, 4, 64);
+          v += __shfl_xor(v, 8, 64);
+          if (c16 == 0) sm.red[wave][ht * 16 + 4 * g + i] = v;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < HP) {
+      float L = 0.f;
+      for (int w = 0; w < QKW; ++w) L += sm.red[w][tid];
+      sm.red[0][tid] = L;  // row 0 was read above by this thread only
+    }
+    __syncthreads();
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Split-K latent attention for long caches: one workgroup of 4 waves per
+// (split, sequence), 64-slot tiles.  With a single split the workgroup
+// normalises and writes o_lat itself; otherwise it stores its (m, l, acc)
+// partial and split_merge_kernel, launched next on the stream, merges the
+// splits in split order.  (Merging inside this kernel, by the last workgroup
+// to finish, would need device-scope release/acquire fences per workgroup,
+// which on this multi-XCD part write back and invalidate L2.)
+// ---------------------------------------------------------------------------
 template <int HT, int DC, int DR>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
-  constexpr int W = DC + DR;
-  constexpr int KS = W / 32;
-  constexpr int HP = HT * 16;
-  constexpr int TS = 64;
-  constexpr int PITCH = W + 8;
-  constexpr int PP = TS + 8;
-  constexpr int CPW = DC / 4;
-  constexpr int CT = CPW / 16;
-  constexpr int CPR = W / 8;  // 16-byte chunks per row
-  static_assert(W % 32 == 0 && DC % 64 == 0, "tile shape");
-  static_assert((TS * CPR) % 256 == 0, "tile copy");
-  constexpr int CPT = TS * CPR / 256;  // chunks per thread
-
-  __shared__ __align__(16) uint16_t sQ[HP * PITCH];
-  __shared__ __align__(16) uint16_t sK[TS * PITCH];
-  __shared__ __align__(16) uint16_t sP[HP * PP];
-  __shared__ float sRed[4][HP];
-
+  using A = MfmaAttn<HT, DC, DR, 4, 64>;
+  constexpr int W = A::W, HP = A::HP, PITCH = A::PITCH, CPW = A::CPW, CT = A::CT;
+  __shared__ typename A::Smem sm;
   const int split = blockIdx.x, b = blockIdx.y;
   const int nsplit = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -322,177 +506,45 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
   for (int idx = tid; idx < HP * W; idx += 256) {
     const int hh = idx / W, e = idx % W;
     const float v = hh < H ? a.qbuf[(static_cast<size_t>(b) * H + hh) * W + e] * qscale : 0.f;
-    sQ[hh * PITCH + e] = f32_to_bf16_bits(v);
+    sm.q[hh * PITCH + e] = f32_to_bf16_bits(v);
   }
-
-  float m_run[HT][4], l_part[HT][4];
-  f32x4 acc[HT][CT];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m_run[ht][i] = -INFINITY;
-      l_part[ht][i] = 0.f;
-    }
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[ht][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const uint16_t* cache_b =
+  typename A::State st;
+  A::init(st);
+  const uint16_t* rows =
       static_cast<const uint16_t*>(a.cache) + static_cast<size_t>(b) * a.max_slots * W;
-  uint4 pre[CPT];
-  auto load_tile = [&](int j0) {
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int id = tid + 256 * k;
-      const int row = id / CPR, ch = id % CPR;
-      const int slot = j0 + row;
-      if (slot < hi)
-        pre[k] = *reinterpret_cast<const uint4*>(cache_b + static_cast<size_t>(slot) * W + ch * 8);
-      else
-        pre[k] = uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int id = tid + 256 * k;
-      const int row = id / CPR, ch = id % CPR;
-      *reinterpret_cast<uint4*>(sK + row * PITCH + ch * 8) = pre[k];
-    }
-  };
-
-  if (lo < hi) load_tile(lo);
-  for (int j0 = lo; j0 < hi; j0 += TS) {
-    store_tile();
-    __syncthreads();
-    if (j0 + TS < hi) load_tile(j0 + TS);
-
-    // scores: wave owns slots 16*wave .. 16*wave+15 of the tile
-    f32x4 sc[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) sc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 bk =
-          *reinterpret_cast<const bf16x8*>(sK + (16 * wave + c16) * PITCH + ks * 32 + 8 * g);
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        const bf16x8 aq =
-            *reinterpret_cast<const bf16x8*>(sQ + (ht * 16 + c16) * PITCH + ks * 32 + 8 * g);
-        sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, sc[ht], 0, 0, 0);
-      }
-    }
-    // sc[ht][i] = score of head ht*16 + 4g + i against slot j0 + 16*wave + c16
-    const bool valid = j0 + 16 * wave + c16 < hi;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = valid ? sc[ht][i] : -INFINITY;
-        sc[ht][i] = v;
-        v = fmaxf(v, __shfl_xor(v, 1, 64));
-        v = fmaxf(v, __shfl_xor(v, 2, 64));
-        v = fmaxf(v, __shfl_xor(v, 4, 64));
-        v = fmaxf(v, __shfl_xor(v, 8, 64));
-        if (c16 == 0) sRed[wave][ht * 16 + 4 * g + i] = v;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int head = ht * 16 + 4 * g + i;
-        const float mt =
-            fmaxf(fmaxf(sRed[0][head], sRed[1][head]), fmaxf(sRed[2][head], sRed[3][head]));
-        const float mn = fmaxf(m_run[ht][i], mt);
-        const float alpha = fast_exp2(m_run[ht][i] - mn);
-        m_run[ht][i] = mn;
-        const float pv = fast_exp2(sc[ht][i] - mn);
-        l_part[ht][i] = l_part[ht][i] * alpha + pv;
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[ht][ct][i] *= alpha;
-        sP[head * PP + 16 * wave + c16] = f32_to_bf16_bits(pv);
-      }
-    }
-    __syncthreads();
-
-    // acc[head, col] += sum_slot P[head, slot] * row[slot, col]
-#pragma unroll
-    for (int ks2 = 0; ks2 < TS / 32; ++ks2) {
-      bf16x8 ap[HT];
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        ap[ht] = *reinterpret_cast<const bf16x8*>(sP + (ht * 16 + c16) * PP + ks2 * 32 + 8 * g);
-      // Lane (g, c16) needs rows ks2*32 + 8g + 0..7 of column col0 + c16.  A
-      // transposing read covers 4 rows: lane k of a 16-lane group points at
-      // row base + k/4, columns col0 + 4*(k%4) .. +3; lane i then receives as
-      // element r the (i%4)-th value of lane 4r + i/4, i.e. row base + r of
-      // column col0 + i.
-      const uint16_t* rbase = sK + (ks2 * 32 + 8 * g + (c16 >> 2)) * PITCH + 4 * (c16 & 3);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int col0 = wave * CPW + ct * 16;
-        const s16x4 lo4 = lds_read_tr16(rbase + col0);
-        const s16x4 hi4 = lds_read_tr16(rbase + 4 * PITCH + col0);
-        const s16x8 v8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 bb = __builtin_bit_cast(bf16x8, v8);
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-          acc[ht][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[ht], bb, acc[ht][ct], 0, 0, 0);
-      }
-    }
-    __syncthreads();
-  }
-
-  // l: sum over the 16 slot lanes and the 4 waves
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = l_part[ht][i];
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
-      v += __shfl_xor(v, 4, 64);
-      v += __shfl_xor(v, 8, 64);
-      if (c16 == 0) sRed[wave][ht * 16 + 4 * g + i] = v;
-    }
-  }
-  __syncthreads();
+  uint4 pre[A::CPT];
+  if (lo < hi) A::load_tile(pre, rows, lo, hi, -1);
+  A::template run<false>(st, sm, rows, lo, hi, -1, nullptr, pre);
+  A::finish(st, sm);
 
   if (nsplit == 1) {
-    // single split: normalise in registers and write o_lat directly
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int head = ht * 16 + 4 * g + i;
         if (head < H) {
-          const float L = (sRed[0][head] + sRed[1][head]) + (sRed[2][head] + sRed[3][head]);
-          const float inv = 1.f / L;
+          const float inv = 1.f / sm.red[0][head];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
             a.o_lat[(static_cast<size_t>(b) * H + head) * DC + wave * CPW + ct * 16 + c16] =
-                acc[ht][ct][i] * inv;
+                st.acc[ht][ct][i] * inv;
         }
       }
     }
     return;
   }
-
   const size_t pbase = (static_cast<size_t>(b) * nsplit + split) * H;
   if (wave == 0 && c16 == 0) {
+    // the running max is in log2 units; partials use natural-log units
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int head = ht * 16 + 4 * g + i;
         if (head < H) {
-          // the running max is in log2 units; partials use natural-log units
-          a.part.m[pbase + head] = m_run[ht][i] * kLn2;
-          a.part.l[pbase + head] =
-              (sRed[0][head] + sRed[1][head]) + (sRed[2][head] + sRed[3][head]);
+          a.part.m[pbase + head] = st.m[ht][i] * kLn2;
+          a.part.l[pbase + head] = sm.red[0][head];
         }
       }
     }
@@ -505,11 +557,177 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
       if (head < H) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
-          a.part.acc[(pbase + head) * DC + wave * CPW + ct * 16 + c16] = acc[ht][ct][i];
+          a.part.acc[(pbase + head) * DC + wave * CPW + ct * 16 + c16] = st.acc[ht][ct][i];
       }
     }
   }
+}
 
+// ---------------------------------------------------------------------------
+// Fused decode step for short caches: one workgroup of 16 waves per sequence
+// does everything for one token, so no other workgroup depends on it:
+//   merge (optional) : gate w_t, slot ceil(t/s) <- reset ? w x : acc + w x,
+//                      written to the cache and kept in LDS for the tile;
+//   absorb           : q~[h] = W_UK[h]^T q_c[h], scaled, bf16, into LDS;
+//   attention        : the MFMA core over slots 1..ceil(t/s);
+//   up-projection    : out[h] = W_UV[h] o_lat[h], o_lat kept in LDS.
+// The absorb and up-projection loads (16 bytes each) are spread over 1024
+// threads so each thread issues a single round of them.
+// ---------------------------------------------------------------------------
+// Loads per thread the fused step keeps in flight for W_UK and for W_UV.
+constexpr int kStepMaxLoads = 16;
+
+template <int HT, int DC, int DR, int TS>
+__global__ __launch_bounds__(1024) void decode_step_kernel(StepArgs a) {
+  using A = MfmaAttn<HT, DC, DR, 16, TS>;
+  constexpr int W = A::W, HP = A::HP, PITCH = A::PITCH, CPW = A::CPW, CT = A::CT, NT = A::NT;
+  constexpr int KC = DC / 8;
+  constexpr int MAXL = kStepMaxLoads;
+  static_assert(TS * PITCH * 2 >= HP * DC * 4, "o_lat must fit in the tile buffer");
+  __shared__ typename A::Smem sm;
+  __shared__ __align__(16) uint16_t s_new[W];
+  __shared__ float s_gate;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int H = a.H, d_h = a.d_h;
+
+  const int pos = a.pos[b];
+  const int n = pos >= 1 ? slot_of(pos, a.s) : 0;
+  const bool ok = pos >= 1 && n <= a.max_slots && (!a.merge || pos <= a.pe_rows);
+  uint16_t* out = a.out + static_cast<size_t>(b) * H * d_h;
+  if (!ok) {
+    for (int idx = tid; idx < H * d_h; idx += NT) out[idx] = 0x7fc0u;  // NaN
+    return;
+  }
+  // merge: gate of the token (one wave), then slot ceil(t/s) <- (reset ? 0 :
+  // open slot) + w x, written to the cache and kept in LDS for the tile.
+  float* qin = reinterpret_cast<float*>(sm.k);  // [H][d_h], scratch in the tile buffer
+  for (int idx = tid; idx < H * d_h; idx += NT)
+    qin[idx] = bf16_bits_to_f32(a.q_c[static_cast<size_t>(b) * H * d_h + idx]);
+  if (a.merge && wave == 0) {
+    const float w = gate_of_token(a.c + static_cast<size_t>(b) * DC,
+                                  a.pe + static_cast<size_t>(pos - 1) * DC, a.w_hyp, DC, lane);
+    if (lane == 0) s_gate = w;
+  }
+  __syncthreads();
+  if (a.merge && tid < W) {
+    const int e = tid;
+    const float x = e < DC ? bf16_bits_to_f32(a.c[static_cast<size_t>(b) * DC + e])
+                           : bf16_bits_to_f32(a.k_r[static_cast<size_t>(b) * DR + e - DC]);
+    float acc = (pos - 1) % a.s == 0 ? 0.f : a.open_acc[static_cast<size_t>(b) * W + e];
+    acc = fmaf(s_gate, x, acc);
+    a.open_acc[static_cast<size_t>(b) * W + e] = acc;
+    const uint16_t u = f32_to_bf16_bits(acc);
+    a.cache[(static_cast<size_t>(b) * a.max_slots + n - 1) * W + e] = u;
+    s_new[e] = u;
+  }
+
+  // absorb: thread t owns 8-column chunk kc of head hh for the rows
+  // e = eg, eg + eg_n, ... (one pass over all heads); W_UK chunks are 16-byte
+  // loads, the eg_n partial sums are added in order through LDS.
+  const int eg_n = NT / (KC * H);
+  const int kc = tid % KC, hh = (tid / KC) % H, eg = tid / (KC * H);
+  const int nl = eg < eg_n ? (d_h - eg + eg_n - 1) / eg_n : 0;
+  float* red = qin + H * d_h;  // [H][eg_n][DC]
+  uint4 wk[MAXL];
+#pragma unroll
+  for (int i = 0; i < MAXL; ++i)
+    if (i < nl)
+      wk[i] = *reinterpret_cast<const uint4*>(a.w_uk + (static_cast<size_t>(hh) * d_h + eg + i * eg_n) * DC + kc * 8);
+  // absorb: q~[h, k] = sum_e q_c[h, e] W_UK[h, e, k], partial sums per row group
+  if (nl > 0) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXL; ++i) {
+      if (i < nl) {
+        const float q = qin[hh * d_h + eg + i * eg_n];
+        const uint32_t wv[4] = {wk[i].x, wk[i].y, wk[i].z, wk[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] = fmaf(q, __uint_as_float(wv[j] << 16), acc[2 * j]);
+          acc[2 * j + 1] = fmaf(q, __uint_as_float(wv[j] & 0xffff0000u), acc[2 * j + 1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[(hh * eg_n + eg) * DC + kc * 8 + j] = acc[j];
+  }
+  __syncthreads();
+  const float qscale = a.scale * kLog2e;
+  for (int idx = tid; idx < H * DC; idx += NT) {
+    const int h = idx / DC, k = idx % DC;
+    float v = 0.f;
+    for (int r = 0; r < eg_n; ++r) v += red[(h * eg_n + r) * DC + k];
+    sm.q[h * PITCH + k] = f32_to_bf16_bits(v * qscale);
+  }
+  for (int idx = tid; idx < HP * DR; idx += NT) {
+    const int h = idx / DR, e = idx % DR;
+    sm.q[h * PITCH + DC + e] =
+        h < H ? f32_to_bf16_bits(bf16_bits_to_f32(a.q_r[(static_cast<size_t>(b) * H + h) * DR + e]) * qscale)
+              : uint16_t(0);
+  }
+  for (int idx = tid; idx < (HP - H) * DC; idx += NT)
+    sm.q[(H + idx / DC) * PITCH + idx % DC] = 0;
+
+  __syncthreads();
+
+  typename A::State st;
+  A::init(st);
+  const uint16_t* rows = a.cache + static_cast<size_t>(b) * a.max_slots * W;
+  const int patch_row = a.merge ? n - 1 : -1;
+  uint4 pre[A::CPT];
+  A::load_tile(pre, rows, 0, n, patch_row);
+  A::template run<true>(st, sm, rows, 0, n, patch_row, s_new, pre);
+  A::finish(st, sm);
+
+  // Up-projection assignment: tpo threads per output row (h, e), chunks
+  // c = p, p + tpo, ...; its W_UV loads go out before o_lat is staged.
+  const int nout = H * d_h;
+  int tpo = 1;
+  while (tpo < 64 && 2 * tpo * nout <= NT) tpo *= 2;
+  const int o = tid / tpo, p = tid % tpo;
+  const int nv = o < nout ? (KC - p + tpo - 1) / tpo : 0;
+  const uint16_t* wrow = a.w_uv + static_cast<size_t>(o < nout ? o : 0) * DC;
+  uint4 wv[MAXL];
+#pragma unroll
+  for (int i = 0; i < MAXL; ++i)
+    if (i < nv) wv[i] = *reinterpret_cast<const uint4*>(wrow + (p + i * tpo) * 8);
+
+  // o_lat (fp32, normalised) into the tile buffer, then the up-projection
+  float* olat = reinterpret_cast<float*>(sm.k);  // [HP][DC]
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int head = ht * 16 + 4 * g + i;
+      const float inv = 1.f / sm.red[0][head];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        olat[head * DC + wave * CPW + ct * 16 + c16] = st.acc[ht][ct][i] * inv;
+    }
+  }
+  __syncthreads();
+  float acc = 0.f;
+  if (nv > 0) {
+    const float* orow = olat + (o / d_h) * DC;
+#pragma unroll
+    for (int i = 0; i < MAXL; ++i) {
+      if (i < nv) {
+        const int c = p + i * tpo;
+        const uint32_t w4[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc = fmaf(__uint_as_float(w4[j] << 16), orow[c * 8 + 2 * j], acc);
+          acc = fmaf(__uint_as_float(w4[j] & 0xffff0000u), orow[c * 8 + 2 * j + 1], acc);
+        }
+      }
+    }
+  }
+  for (int off = tpo / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (p == 0 && o < nout) out[o] = f32_to_bf16_bits(acc);
 }
 
 // Rows per workgroup of absorb / up-projection: one row while there are few
@@ -587,6 +805,33 @@ hipError_t launch_up_project(int R, int H, int d_h, int d_c, const float* o_lat,
                              void* out, int dtype, hipStream_t st) {
   return dtype == 0 ? up_project_t<float>(R, H, d_h, d_c, o_lat, w_uv, out, st)
                     : up_project_t<uint16_t>(R, H, d_h, d_c, o_lat, w_uv, out, st);
+}
+
+bool decode_step_supported(int H, int d_h, int d_c, int d_r) {
+  const bool shape = (d_c == 256 && d_r == 32) || (d_c == 512 && d_r == 64);
+  const int KC = d_c / 8, NT = 1024;
+  if (!shape || H > 32 || H * KC > NT) return false;  // one absorb pass over all heads
+  const int eg_n = NT / (KC * H);
+  int tpo = 1;
+  while (tpo < 64 && 2 * tpo * H * d_h <= NT) tpo *= 2;
+  // each thread's W_UK and W_UV chunks fit the in-flight register arrays, and
+  // every output row has a thread
+  return (d_h + eg_n - 1) / eg_n <= kStepMaxLoads && (KC + tpo - 1) / tpo <= kStepMaxLoads &&
+         H * d_h <= NT && d_c + d_r <= NT;
+}
+
+hipError_t launch_decode_step(const StepArgs& a, hipStream_t st) {
+  if (a.d_c == 256 && a.d_r == 32) {
+    if (a.H <= 16)
+      decode_step_kernel<1, 256, 32, 128><<<a.B, 1024, 0, st>>>(a);
+    else
+      decode_step_kernel<2, 256, 32, 128><<<a.B, 1024, 0, st>>>(a);
+  } else if (a.d_c == 512 && a.d_r == 64 && a.H <= 16) {  // H * d_c / 8 <= 1024 threads
+    decode_step_kernel<1, 512, 64, 64><<<a.B, 1024, 0, st>>>(a);
+  } else {
+    return hipErrorNotSupported;
+  }
+  return hipGetLastError();
 }
 
 bool decode_mfma_supported(int H, int d_c, int d_r) {

@@ -61,6 +61,28 @@ hipError_t launch_attend_portable(const AttendArgs& a, int dtype, hipStream_t st
 bool decode_mfma_supported(int H, int d_c, int d_r);
 hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st);
 
+// Fused one-token decode step (bf16, short caches): optional merge of the
+// token, absorb, latent attention and up-projection in one kernel, one
+// workgroup per sequence.
+struct StepArgs {
+  int B, H, d_h, d_c, d_r, s, max_slots, pe_rows, merge;
+  float scale;
+  const int32_t* pos;     // [B]
+  const uint16_t* c;      // [B, d_c]  token to merge (merge only)
+  const uint16_t* k_r;    // [B, d_r]
+  const float* w_hyp;     // [d_c]
+  const float* pe;        // [pe_rows, d_c]
+  const uint16_t* q_c;    // [B, H, d_h]
+  const uint16_t* q_r;    // [B, H, d_r]
+  const uint16_t* w_uk;   // [H, d_h, d_c]
+  const uint16_t* w_uv;   // [H, d_h, d_c]
+  uint16_t* cache;        // [B, max_slots, W]
+  float* open_acc;        // [B, W]
+  uint16_t* out;          // [B, H, d_h]
+};
+bool decode_step_supported(int H, int d_h, int d_c, int d_r);
+hipError_t launch_decode_step(const StepArgs& a, hipStream_t st);
+
 // out[r, h, :] = W_UV[h] o_lat[r, h].
 hipError_t launch_up_project(int R, int H, int d_h, int d_c, const float* o_lat, const void* w_uv,
                              void* out, int dtype, hipStream_t st);

@@ -47,12 +47,8 @@ __device__ void compute_gates(const MergeArgs& a, int b, int p0, int ta, int nto
     const int t = ta + k;
     const size_t crow = (static_cast<size_t>(b) * a.T + (t - p0)) * a.d_c;
     const size_t prow = static_cast<size_t>(t - 1) * a.d_c;
-    float acc = 0.f;
-    for (int e = lane; e < a.d_c; e += 64)
-      acc = fmaf(Store<T>::load(c, crow + e) + a.pe[prow + e], a.w_hyp[e], acc);
-    acc = wave_sum(acc);
+    const float w = gate_of_token(c + crow, a.pe + prow, a.w_hyp, a.d_c, lane);
     if (lane == 0) {
-      const float w = 1.f / (1.f + expf(-acc));
       gw[k] = w;
       if (a.gate_out) a.gate_out[static_cast<size_t>(b) * a.T + (t - p0)] = w;
     }

@@ -100,64 +100,86 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
     __syncthreads();
   }
 
-  // acc[i][j][q]: row wm*64 + i*16 + 4g + q, column wn*64 + j*16 + c16
+  // Epilogue: stage the 128x128 tile as bf16 in LDS (reusing the operand
+  // buffers), then write each (token, head) row of d_h values with 16-byte
+  // stores.  acc[i][j][q] is row wm*64 + i*16 + 4g + q, column wn*64 + j*16 + c16.
+  constexpr int CP = GBN + 8;
+  static_assert(GBM * CP <= 2 * 2 * GBM * GP, "C tile must fit in the operand buffers");
+  uint16_t* sC = &sA[0][0];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = col0 + wn * 64 + j * 16 + c16;
-    const bool isk = col < HD;
-    const int cc = isk ? col : col - HD;
-    const int hh = cc / d_h, e = cc % d_h;
-    uint16_t* dst = isk ? kout : vout;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = row0 + wm * 64 + i * 16 + 4 * g + q;
-        if (m < M) {
-          const int bb = m / N, nn = m % N;
-          dst[((static_cast<size_t>(bb) * H + hh) * N + nn) * d_h + e] = f32_to_bf16_bits(acc[i][j][q]);
-        }
-      }
+      for (int q = 0; q < 4; ++q)
+        sC[(wm * 64 + i * 16 + 4 * g + q) * CP + wn * 64 + j * 16 + c16] = f32_to_bf16_bits(acc[i][j][q]);
+  __syncthreads();
+  const bool isk = col0 < HD;
+  uint16_t* dst = isk ? kout : vout;
+  const int cbase = isk ? col0 : col0 - HD;
+  for (int id = tid; id < GBM * (GBN / 8); id += 256) {
+    const int r = id / (GBN / 8), cc = id % (GBN / 8);
+    const int m = row0 + r;
+    if (m < M) {
+      const int col = cbase + cc * 8;
+      const int hh = col / d_h, e = col % d_h;
+      const int bb = m / N, nn = m % N;
+      *reinterpret_cast<uint4*>(dst + ((static_cast<size_t>(bb) * H + hh) * N + nn) * d_h + e) =
+          *reinterpret_cast<const uint4*>(sC + r * CP + cc * 8);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Stride-masked attention, explicit per-head form, bf16 in / fp32 accumulate.
-// Workgroup: 128 queries of one (sequence, head); wave w owns queries
-// 32w..32w+31 as two 16-query MFMA column tiles.  Scores are computed
-// transposed, S^T[slot, query] = K . Q^T, so that each lane holds a query
-// column: the row max is in-lane plus two shuffles, and the probabilities
-// are already in the B-operand layout of O^T += V^T . P^T (no LDS trip).
-// The MFMA contraction index kappa = 8g + r maps to slot
-//   r < 4 : 32*ks2 + 4g + r          (score tile 2*ks2)
-//   r >= 4: 32*ks2 + 16 + 4g + r - 4 (score tile 2*ks2 + 1)
-// and the V^T operand is read from a transposed LDS tile with that mapping.
+// Stride-masked attention, explicit per-head form, bf16 in / fp32 accumulate,
+// on v_mfma_f32_32x32x16_bf16.
+//
+// Workgroup: 256 queries of one (sequence, head); wave w owns queries
+// 64w..64w+63 as two 32-query MFMA column tiles.  Scores are computed
+// transposed, S^T[slot, query] = K . Q^T (A = key rows from LDS, B = the
+// wave's queries, held in registers for the whole kernel), so each lane holds
+// one query column: the row max is in-lane plus one shuffle, and the
+// probabilities are already laid out as the B operand of O^T += V^T . P^T.
+// For a 16-slot chunk c of the tile the MFMA contraction index
+// kappa = 8*grp + r (grp = lane / 32) maps to slot
+//   r < 4 : 16c + 4*grp + r,      r >= 4 : 16c + 8 + 4*grp + (r - 4),
+// which is exactly where the score tile left those probabilities; the V^T
+// operand is read with that mapping by transposing LDS loads of the
+// row-major value tile.
+//
+// The keys are the completed slots (token s*b - 1, 0-based, of slot b - 1),
+// loaded 64 at a time; the next tile is fetched into registers while the
+// current one is used.  Tiles past a wave's last visible slot are skipped by
+// that wave, and only tiles that cross its staircase are masked.
 // ---------------------------------------------------------------------------
-template <int DH, int DR>
-__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
+template <int DH, int DR, int NQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 && DH == 64 ? 2 : 1)))
+void prefill_attn_kernel(PrefillAttnArgs a) {
   constexpr int DQK = DH + DR;
-  constexpr int KSQ = DQK / 32;
-  constexpr int DT = DH / 16;
-  constexpr int TS = 64;
-  constexpr int QT = 128;
-  constexpr int KP = DQK + 8;  // sK pitch
-  constexpr int VTP = TS + 4;  // sVT pitch
-  static_assert(DH % 32 == 0 && DR % 32 == 0, "shape");
-  constexpr int KCH = DQK / 8;  // 16-byte chunks per key row
-  constexpr int VCH = DH / 8;   // 16-byte chunks per value row
+  constexpr int KK = DQK / 16;       // k-chunks of the score MFMA
+  constexpr int DT = DH / 32;        // 32-row tiles of O^T
+  constexpr int TS = 64;             // slots per tile
+  constexpr int QW = 32 * NQ;        // queries per wave (NQ column tiles of 32)
+  constexpr int QT = 4 * QW;         // queries per workgroup
+  constexpr int KP = DQK + 8;        // key tile pitch (elements)
+  constexpr int VP = DH + 8;         // value tile pitch
+  constexpr int KCH = DQK / 8, VCH = DH / 8;
+  constexpr int NCH = TS * (KCH + VCH);    // 16-byte chunks per tile
+  constexpr int CPT = (NCH + 255) / 256;
+  static_assert(DH % 32 == 0 && DR % 16 == 0, "shape");
 
   __shared__ __align__(16) uint16_t sK[TS * KP];
-  __shared__ __align__(16) uint16_t sVT[DH * VTP];
+  __shared__ __align__(16) uint16_t sV[TS * VP];
 
   const int nqt = gridDim.x;
   const int qt = nqt - 1 - static_cast<int>(blockIdx.x);  // heavy tiles first
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int grp = lane >> 5, c32 = lane & 31;
   const int N = a.N, H = a.H, s = a.s;
   const int W = a.d_c + DR;
   const int q0 = qt * QT;
+  const int qw0 = q0 + wave * QW;
   const float qk_scale = a.scale * kLog2e;
 
   const uint16_t* qc = static_cast<const uint16_t*>(a.q_c);
@@ -166,156 +188,193 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
   const uint16_t* vv = static_cast<const uint16_t*>(a.v) + (static_cast<size_t>(b) * H + h) * N * DH;
   const uint16_t* Pb = static_cast<const uint16_t*>(a.partials) + static_cast<size_t>(b) * N * W;
 
-  // Query operands (registers for the whole kernel) and the diagonal state.
-  bf16x8 qreg[2][KSQ];
-  float m[2], lp[2];
-  f32x4 acc[DT][2];
+  // Queries (B operands, registers) and the diagonal key j = i as the initial
+  // online-softmax state: m = score(i, i), l = 1, O = V_i.
+  bf16x8 qreg[NQ][KK];
+  float m[NQ], lp[NQ];
+  f32x16 acc[DT][NQ];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int qi = q0 + 32 * wave + 16 * t + c16;  // 0-based query token
+  for (int t = 0; t < NQ; ++t) {
+    const int qi = qw0 + 32 * t + c32;  // 0-based query token
     const bool qok = qi < N;
     float dpart = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) {
-      const int d0 = ks * 32 + 8 * g;
+    for (int kk = 0; kk < KK; ++kk) {
+      const int d0 = 16 * kk + 8 * grp;
       uint4 qv = uint4{0u, 0u, 0u, 0u}, kv = uint4{0u, 0u, 0u, 0u};
       if (qok) {
         if (d0 < DH) {
-          qv = *reinterpret_cast<const uint4*>(qc + (static_cast<size_t>(b) * N + qi) * H * DH +
-                                               static_cast<size_t>(h) * DH + d0);
+          qv = *reinterpret_cast<const uint4*>(qc + ((static_cast<size_t>(b) * N + qi) * H + h) * DH + d0);
           kv = *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(qi) * DH + d0);
         } else {
-          qv = *reinterpret_cast<const uint4*>(qr + (static_cast<size_t>(b) * N + qi) * H * DR +
-                                               static_cast<size_t>(h) * DR + (d0 - DH));
+          qv = *reinterpret_cast<const uint4*>(qr + ((static_cast<size_t>(b) * N + qi) * H + h) * DR + (d0 - DH));
           kv = *reinterpret_cast<const uint4*>(Pb + static_cast<size_t>(qi) * W + a.d_c + (d0 - DH));
         }
       }
-      qreg[t][ks] = __builtin_bit_cast(bf16x8, qv);
-      const u16x8 qs = __builtin_bit_cast(u16x8, qv), kk = __builtin_bit_cast(u16x8, kv);
+      qreg[t][kk] = __builtin_bit_cast(bf16x8, qv);
+      const u16x8 qs = __builtin_bit_cast(u16x8, qv), ks = __builtin_bit_cast(u16x8, kv);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) dpart = fmaf(bf16_bits_to_f32(qs[r]), bf16_bits_to_f32(kk[r]), dpart);
+      for (int r = 0; r < 8; ++r) dpart = fmaf(bf16_bits_to_f32(qs[r]), bf16_bits_to_f32(ks[r]), dpart);
     }
-    dpart += __shfl_xor(dpart, 16, 64);
     dpart += __shfl_xor(dpart, 32, 64);
     m[t] = dpart * qk_scale;
-    lp[t] = g == 0 ? 1.f : 0.f;
+    lp[t] = grp == 0 ? 1.f : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      uint2 v2 = uint2{0u, 0u};
-      if (qok) v2 = *reinterpret_cast<const uint2*>(vv + static_cast<size_t>(qi) * DH + dt * 16 + 4 * g);
-      acc[dt][t][0] = bf16_bits_to_f32(static_cast<uint16_t>(v2.x & 0xffffu));
-      acc[dt][t][1] = bf16_bits_to_f32(static_cast<uint16_t>(v2.x >> 16));
-      acc[dt][t][2] = bf16_bits_to_f32(static_cast<uint16_t>(v2.y & 0xffffu));
-      acc[dt][t][3] = bf16_bits_to_f32(static_cast<uint16_t>(v2.y >> 16));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint2 v2 = uint2{0u, 0u};
+        if (qok)
+          v2 = *reinterpret_cast<const uint2*>(vv + static_cast<size_t>(qi) * DH + 32 * dt + 8 * j + 4 * grp);
+        acc[dt][t][4 * j + 0] = __uint_as_float(v2.x << 16);
+        acc[dt][t][4 * j + 1] = __uint_as_float(v2.x & 0xffff0000u);
+        acc[dt][t][4 * j + 2] = __uint_as_float(v2.y << 16);
+        acc[dt][t][4 * j + 3] = __uint_as_float(v2.y & 0xffff0000u);
+      }
     }
   }
 
-  const int qlast = min(q0 + QT, N) - 1;
-  const int nk = qlast / s;     // completed slots seen by the tile's last query
-  const int full = q0 / s;      // slots < full are seen by every query of the tile
-  for (int j0 = 0; j0 < nk; j0 += TS) {
-    // K tile [slot][K^C | P^R] and transposed V tile [d][slot]
-    for (int id = tid; id < TS * KCH; id += 256) {
-      const int row = id / KCH, ch = id % KCH;
-      const int slot = j0 + row;
-      uint4 v = uint4{0u, 0u, 0u, 0u};
-      if (slot < nk) {
-        const int tk = s * slot + s - 1;  // token holding the completed slot
-        v = ch < DH / 8
-                ? *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(tk) * DH + ch * 8)
-                : *reinterpret_cast<const uint4*>(Pb + static_cast<size_t>(tk) * W + a.d_c + (ch - DH / 8) * 8);
-      }
-      *reinterpret_cast<uint4*>(sK + row * KP + ch * 8) = v;
-    }
-    for (int id = tid; id < TS * VCH; id += 256) {
-      const int row = id / VCH, ch = id % VCH;
-      const int slot = j0 + row;
-      uint4 v = uint4{0u, 0u, 0u, 0u};
-      if (slot < nk) v = *reinterpret_cast<const uint4*>(vv + static_cast<size_t>(s * slot + s - 1) * DH + ch * 8);
-      const u16x8 e = __builtin_bit_cast(u16x8, v);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) sVT[(ch * 8 + r) * VTP + row] = e[r];
-    }
-    __syncthreads();
+  // completed slots seen by the workgroup's / this wave's last query, and the
+  // slots every query of this wave sees
+  const int nk = (min(q0 + QT, N) - 1) / s;
+  const int nk_w = qw0 < N ? (min(qw0 + QW, N) - 1) / s : 0;
+  const int full_w = qw0 / s;
 
-    // S^T = K Q^T: sc[mt][t][i] = score(slot j0 + 16mt + 4g + i, query col t)
-    f32x4 sc[4][2];
+  uint4 pre[CPT];
+  auto load_tile = [&](int j0) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) sc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sK + (mt * 16 + c16) * KP + ks * 32 + 8 * g);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          sc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, qreg[t][ks], sc[mt][t], 0, 0, 0);
-      }
-    }
-    const bool boundary = j0 + TS > full;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int qi = q0 + 32 * wave + 16 * t + c16;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sc[mt][t][i] * qk_scale;
-          if (boundary) {
-            const int slot = j0 + mt * 16 + 4 * g + i;
-            // completed slot (0-based) visible to query qi (0-based): s*(slot+1) <= qi
-            if (s * (slot + 1) > qi) v = -INFINITY;
+    for (int k = 0; k < CPT; ++k) {
+      const int id = tid + 256 * k;
+      if (NCH % 256 == 0 || id < NCH) {
+        uint4 v = uint4{0u, 0u, 0u, 0u};
+        if (id < TS * KCH) {
+          const int row = id / KCH, ch = id % KCH;
+          const int slot = j0 + row;
+          if (slot < nk) {
+            const int tk = s * slot + s - 1;  // token holding the completed slot
+            v = ch < DH / 8
+                    ? *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(tk) * DH + ch * 8)
+                    : *reinterpret_cast<const uint4*>(Pb + static_cast<size_t>(tk) * W + a.d_c + (ch - DH / 8) * 8);
           }
-          sc[mt][t][i] = v;
-          mx = fmaxf(mx, v);
+        } else {
+          const int id2 = id - TS * KCH;
+          const int row = id2 / VCH, ch = id2 % VCH;
+          const int slot = j0 + row;
+          if (slot < nk)
+            v = *reinterpret_cast<const uint4*>(vv + static_cast<size_t>(s * slot + s - 1) * DH + ch * 8);
         }
+        pre[k] = v;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m[t], mx);
-      const float alpha = fast_exp2(m[t] - mn);
-      m[t] = mn;
-      float ls = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(sc[mt][t][i] - mn);
-          sc[mt][t][i] = p;
-          ls += p;
-        }
-      }
-      lp[t] = lp[t] * alpha + ls;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt][t] *= alpha;
     }
-
-    // O^T += V^T P^T over the tile's 64 slots (two 32-slot k steps)
+  };
+  auto store_tile = [&]() {
 #pragma unroll
-    for (int ks2 = 0; ks2 < TS / 32; ++ks2) {
-      bf16x8 pb[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u16x8 pk;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pk[i] = f32_to_bf16_bits(sc[2 * ks2][t][i]);
-          pk[4 + i] = f32_to_bf16_bits(sc[2 * ks2 + 1][t][i]);
+    for (int k = 0; k < CPT; ++k) {
+      const int id = tid + 256 * k;
+      if (NCH % 256 == 0 || id < NCH) {
+        if (id < TS * KCH) {
+          const int row = id / KCH, ch = id % KCH;
+          *reinterpret_cast<uint4*>(sK + row * KP + ch * 8) = pre[k];
+        } else {
+          const int id2 = id - TS * KCH;
+          const int row = id2 / VCH, ch = id2 % VCH;
+          *reinterpret_cast<uint4*>(sV + row * VP + ch * 8) = pre[k];
         }
-        pb[t] = __builtin_bit_cast(bf16x8, pk);
       }
+    }
+  };
+
+  if (nk > 0) load_tile(0);
+  for (int j0 = 0; j0 < nk; j0 += TS) {
+    store_tile();
+    __syncthreads();
+    if (j0 + TS < nk) load_tile(j0 + TS);
+
+    if (j0 < nk_w) {
+      // S^T = K Q^T: sc[rt][t][i] = score(slot j0 + 32rt + 8(i/4) + 4grp + i%4, query t)
+      f32x16 sc[2][NQ];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* src = sVT + (dt * 16 + c16) * VTP + ks2 * 32 + 4 * g;
-        const uint2 lo4 = *reinterpret_cast<const uint2*>(src);
-        const uint2 hi4 = *reinterpret_cast<const uint2*>(src + 16);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, uint4{lo4.x, lo4.y, hi4.x, hi4.y});
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t], acc[dt][t], 0, 0, 0);
+        for (int t = 0; t < NQ; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[rt][t][i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sK + (32 * rt + c32) * KP + 16 * kk + 8 * grp);
+#pragma unroll
+          for (int t = 0; t < NQ; ++t)
+            sc[rt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[t][kk], sc[rt][t], 0, 0, 0);
+        }
+      }
+      const bool boundary = j0 + TS > full_w;
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {
+        const int qi = qw0 + 32 * t + c32;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float v = sc[rt][t][i] * qk_scale;
+            if (boundary) {
+              const int slot = j0 + 32 * rt + 8 * (i / 4) + 4 * grp + (i % 4);
+              // completed slot (0-based) visible to query qi (0-based): s*(slot+1) <= qi
+              if (s * (slot + 1) > qi) v = -INFINITY;
+            }
+            sc[rt][t][i] = v;
+            mx = fmaxf(mx, v);
+          }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m[t], mx);
+        const float alpha = fast_exp2(m[t] - mn);
+        m[t] = mn;
+        float ls = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float pv = fast_exp2(sc[rt][t][i] - mn);
+            sc[rt][t][i] = pv;
+            ls += pv;
+          }
+        }
+        lp[t] = lp[t] * alpha + ls;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt][t] *= alpha;
+      }
+
+      // O^T += V^T P^T over the tile's four 16-slot chunks
+      const int q16 = lane >> 4, k16 = lane & 15;
+#pragma unroll
+      for (int c = 0; c < TS / 16; ++c) {
+        const int rt = c / 2, jb = 2 * (c % 2);
+        bf16x8 pb[NQ];
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+          u16x8 pk;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pk[r] = f32_to_bf16_bits(sc[rt][t][4 * jb + r]);
+            pk[4 + r] = f32_to_bf16_bits(sc[rt][t][4 * (jb + 1) + r]);
+          }
+          pb[t] = __builtin_bit_cast(bf16x8, pk);
+        }
+        const int sb0 = 16 * c + 4 * (q16 >> 1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int col0 = 32 * dt + 16 * (q16 & 1);
+          const uint16_t* base = sV + (sb0 + (k16 >> 2)) * VP + col0 + 4 * (k16 & 3);
+          const s16x4 lo4 = lds_read_tr16(base);
+          const s16x4 hi4 = lds_read_tr16(base + 8 * VP);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int t = 0; t < NQ; ++t)
+            acc[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[t], acc[dt][t], 0, 0, 0);
+        }
       }
     }
     __syncthreads();
@@ -323,31 +382,39 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
 
   uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    float l = lp[t];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+  for (int t = 0; t < NQ; ++t) {
+    const float l = lp[t] + __shfl_xor(lp[t], 32, 64);
     const float inv = 1.f / l;
-    const int qi = q0 + 32 * wave + 16 * t + c16;
+    const int qi = qw0 + 32 * t + c32;
     if (qi < N) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        uint16_t* dst = out + ((static_cast<size_t>(b) * N + qi) * H + h) * DH + dt * 16 + 4 * g;
-        const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][0] * inv)) |
-                            (static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][1] * inv)) << 16);
-        const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][2] * inv)) |
-                            (static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(dst) = uint2{w0, w1};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint16_t* dst = out + ((static_cast<size_t>(b) * N + qi) * H + h) * DH + 32 * dt + 8 * j + 4 * grp;
+          const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][4 * j + 0] * inv)) |
+                              (static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][4 * j + 1] * inv)) << 16);
+          const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][4 * j + 2] * inv)) |
+                              (static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][4 * j + 3] * inv)) << 16);
+          *reinterpret_cast<uint2*>(dst) = uint2{w0, w1};
+        }
       }
     }
   }
 }
 
+// 32-query column tiles per wave of the d_h = 64 attention kernel.
+#ifndef MTLA_PREFILL_QUERY_TILES
+#define MTLA_PREFILL_QUERY_TILES 2
+#endif
+constexpr int kPrefillQueryTiles = MTLA_PREFILL_QUERY_TILES;
+
 }  // namespace
 
 bool prefill_mfma_supported(int H, int d_h, int d_c, int d_r) {
   const bool shape = (d_h == 64 && d_r == 32) || (d_h == 128 && d_r == 64);
-  return shape && d_c % GBK == 0 && (2 * H * d_h) % GBN == 0;
+  // the GEMM's 128-column tiles must not straddle the K^C / V halves
+  return shape && d_c % GBK == 0 && (H * d_h) % GBN == 0;
 }
 
 hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
@@ -364,13 +431,14 @@ hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
 }
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t st) {
-  dim3 grid((a.N + 127) / 128, a.H, a.B);
-  if (a.d_h == 64 && a.d_r == 32)
-    prefill_attn_kernel<64, 32><<<grid, 256, 0, st>>>(a);
-  else if (a.d_h == 128 && a.d_r == 64)
-    prefill_attn_kernel<128, 64><<<grid, 256, 0, st>>>(a);
-  else
+  if (a.d_h == 64 && a.d_r == 32) {
+    constexpr int nq = kPrefillQueryTiles;
+    prefill_attn_kernel<64, 32, nq><<<dim3((a.N + 128 * nq - 1) / (128 * nq), a.H, a.B), 256, 0, st>>>(a);
+  } else if (a.d_h == 128 && a.d_r == 64) {
+    prefill_attn_kernel<128, 64, 1><<<dim3((a.N + 127) / 128, a.H, a.B), 256, 0, st>>>(a);
+  } else {
     return hipErrorNotSupported;
+  }
   return hipGetLastError();
 }
 

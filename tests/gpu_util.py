@@ -69,6 +69,20 @@ class Case:
             outs[:, t - 1 - start] = self.decode(pos, t - 1)
         return outs
 
+    def step_loop(self, n_steps: int, start: int = 0) -> torch.Tensor:
+        """Token-by-token with mtla_decode_step (merge + decode in one call)."""
+        d = self.d
+        outs = torch.empty(d.batch, n_steps - start, d.heads, d.d_h, dtype=self.st, device=DEV)
+        for t in range(start + 1, n_steps + 1):
+            pos = torch.full((d.batch,), t, dtype=torch.int32, device=DEV)
+            o = torch.empty(d.batch, d.heads, d.d_h, dtype=self.st, device=DEV)
+            m.mtla_decode_step(d, pos, self.c[:, t - 1].contiguous(), self.k_r[:, t - 1].contiguous(),
+                               self.w_hyp, self.pe, self.q_c[:, t - 1].contiguous(),
+                               self.q_r[:, t - 1].contiguous(), self.w_uk, self.w_uv, self.cache,
+                               self.open_acc, o, self.ws_dec)
+            outs[:, t - 1 - start] = o
+        return outs
+
     def prefill(self, n: int) -> torch.Tensor:
         d = self.d
         out = torch.empty(d.batch, n, d.heads, d.d_h, dtype=self.st, device=DEV)

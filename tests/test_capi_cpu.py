@@ -25,7 +25,7 @@ def dims(**kw):
 
 def test_exports_every_header_symbol():
     syms = m.header_symbols()
-    assert len(syms) == 15
+    assert len(syms) == 17
     for s in syms:
         assert hasattr(m.lib(), s), s
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
@@ -100,6 +100,18 @@ def test_staged_decode_checks():
         assert call(**{name: None}) == m.MTLA_ERR_INVALID_ARG, name
     assert call(ws=None) == m.MTLA_ERR_WORKSPACE
     assert call(n=need - 1) == m.MTLA_ERR_WORKSPACE
+
+
+def test_decode_plan():
+    # short cache with the workload shapes: one split, fused step kernel
+    assert m.mtla_decode_plan(m.make_dims(50, 8, 64, 256, 32, 2, 256)) == (1, True)
+    assert m.mtla_decode_plan(m.make_dims(50, 8, 64, 256, 32, 4, 512)) == (1, True)
+    # long cache: several splits, staged kernels
+    sp, fused = m.mtla_decode_plan(m.make_dims(64, 32, 128, 512, 64, 2, 16385))
+    assert sp == 8 and not fused
+    # fp32 storage and the portable flag never take the MFMA kernels
+    assert not m.mtla_decode_plan(m.make_dims(1, 4, 64, 256, 32, 2, 32, "fp32"))[1]
+    assert not m.mtla_decode_plan(m.make_dims(2, 8, 64, 256, 32, 2, 32, portable=True))[1]
 
 
 def test_null_dims():

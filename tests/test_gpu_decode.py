@@ -112,8 +112,9 @@ def test_decode_ragged_and_invalid_positions(portable):
 @pytest.mark.parametrize("shape,portable,B,N", [("st", False, 3, 900), ("llm", False, 4, 2500),
                                                 ("st", True, 2, 900), ("st", False, 80, 3000)])
 def test_staged_decode_equals_fused_call(shape, portable, B, N):
-    """absorb -> decode_attention -> up_project gives the bits of mtla_decode,
-    with one split and with several, call after call."""
+    """absorb -> decode_attention -> up_project gives the bits of mtla_decode
+    whenever mtla_decode runs the same staged kernels (several splits, or the
+    portable path), and agrees within tolerance with the single-kernel step."""
     import temporally_compressed_latent_amd as m
     s = 2
     inp, g = make_case(shape, 12, B, N, s, "bf16", portable, q_rows=1)
@@ -125,11 +126,15 @@ def test_staged_decode_equals_fused_call(shape, portable, B, N):
     o_lat = torch.empty(B, d.heads, d.d_c, dtype=torch.float32, device=DEV)
     out = torch.empty_like(fused)
     ws = m.decode_attention_workspace(d)
+    splits, one_kernel = m.mtla_decode_plan(d)
     for _ in range(3):
         m.mtla_absorb_query(d, g.q_c[:, 0].contiguous(), g.q_r[:, 0].contiguous(), g.w_uk, q_lat)
         m.mtla_decode_attention(d, pos, q_lat, g.cache, o_lat, ws)
         m.mtla_up_project(d, o_lat, g.w_uv, out)
-        assert torch.equal(bits(out), bits(fused))
+        if one_kernel:
+            assert oracle.max_rel_err(host(out), host(fused)) <= 1e-2
+        else:
+            assert torch.equal(bits(out), bits(fused))
 
 
 def test_positions_need_only_element_alignment():
@@ -145,3 +150,43 @@ def test_positions_need_only_element_alignment():
     a = g.decode(table[N], N - 1)
     b = ref.decode(torch.full((B,), N, dtype=torch.int32, device=DEV), N - 1)
     assert torch.equal(bits(a), bits(b))
+
+
+@pytest.mark.parametrize("shape,portable,s,B,N,max_slots", [
+    ("st", False, 2, 4, 130, None),       # fused single-kernel step
+    ("mid", False, 3, 3, 100, None),      # fused, 32-row MFMA instance
+    ("st", False, 4, 2, 90, 700),         # several splits: merge kernel + staged decode
+    ("st", True, 2, 2, 60, None),         # portable kernels
+])
+def test_decode_step_equals_merge_then_decode(shape, portable, s, B, N, max_slots):
+    """mtla_decode_step gives the bits of mtla_merge_append + mtla_decode, and
+    both follow the oracle's incremental loop."""
+    inp, a = make_case(shape, 14, B, N, s, "bf16", portable, max_slots=max_slots)
+    _, b_ = make_case(shape, 14, B, N, s, "bf16", portable, max_slots=max_slots)
+    x = a.step_loop(N)
+    y = b_.decode_loop(N)
+    assert torch.equal(bits(x), bits(y))
+    assert torch.equal(bits(a.cache), bits(b_.cache))
+    assert torch.equal(a.open_acc, b_.open_acc)
+    out = host(x)
+    for b in range(B):
+        want, _ = oracle_ref.incremental(inp, b, N, s, a.d.softmax_scale)
+        assert oracle.max_rel_err(out[b], want) <= 1e-2, b
+
+
+def test_decode_step_invalid_positions():
+    """A position the cache cannot hold gives NaN and leaves that sequence's
+    cache untouched; the other sequences are unaffected."""
+    import temporally_compressed_latent_amd as m
+    B, N, s = 3, 16, 2
+    inp, g = make_case("st", 15, B, N, s, "bf16")
+    before = g.cache.clone()
+    pos = torch.tensor([1, 0, 10_000], dtype=torch.int32, device=DEV)
+    o = torch.empty(B, g.d.heads, g.d.d_h, dtype=torch.bfloat16, device=DEV)
+    m.mtla_decode_step(g.d, pos, g.c[:, 0].contiguous(), g.k_r[:, 0].contiguous(), g.w_hyp, g.pe,
+                       g.q_c[:, 0].contiguous(), g.q_r[:, 0].contiguous(), g.w_uk, g.w_uv, g.cache,
+                       g.open_acc, o, g.ws_dec)
+    out = host(o)
+    assert np.isfinite(out[0]).all()
+    assert np.isnan(out[1]).all() and np.isnan(out[2]).all()
+    assert torch.equal(g.cache[1:], before[1:])
