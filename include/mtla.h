@@ -19,11 +19,10 @@
  *   it, so a cache never needs clearing.
  * Memory: every tensor argument is a caller-owned DEVICE pointer to a dense,
  *   row-major array (innermost dimension last, no strides).  Tensors the
- *   kernels move in 16-byte vectors (cache, q_c, q_r, w_uk, w_uv, out, the
- *   workspace, and prefill's c and k_r) must start 16-byte aligned; the
+ *   kernels move in 16-byte vectors (cache, open_acc, c, k_r, q_c, q_r,
+ *   w_uk, w_uv, out and the workspace) must start 16-byte aligned; the
  *   others need only their element alignment (pos, pos0, w_hyp, pe,
- *   open_acc, gate_out, q_lat, o_lat: 4 bytes; merge_append's c and k_r: the
- *   storage element size).  The library never allocates, frees or synchronises;
+ *   gate_out, q_lat, o_lat: 4 bytes).  The library never allocates, frees or synchronises;
  *   `stream` is a hipStream_t (NULL = the default stream) and every call only
  *   enqueues work on it.
  * dtypes: `dims->dtype` is the storage type of c, k_r, q_c, q_r, w_uk, w_uv,

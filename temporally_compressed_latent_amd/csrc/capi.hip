@@ -232,12 +232,12 @@ int32_t mtla_merge_append(const mtla_dims* dims, const int32_t* pos0, int32_t n_
     return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d exceeds the cache capacity s*max_slots", n_tokens);
   if (dims->batch == 0 || n_tokens == 0) return ok();
   CHECK_PTR_ALIGN(pos0, 4);
-  CHECK_PTR_ALIGN(c, static_cast<int>(elem_bytes(dims)));
-  if (dims->d_r > 0) CHECK_PTR_ALIGN(k_r, static_cast<int>(elem_bytes(dims)));
+  CHECK_PTR(c);
+  if (dims->d_r > 0) CHECK_PTR(k_r);
   CHECK_PTR_ALIGN(w_hyp, 4);
   CHECK_PTR_ALIGN(pe, 4);
   CHECK_PTR(cache);
-  CHECK_PTR_ALIGN(open_acc, 4);
+  CHECK_PTR(open_acc);
   CHECK_OPT_PTR_ALIGN(gate_out, 4);
   mtla::MergeArgs a{dims->batch, n_tokens, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots,
                     pe_rows, pos0, c, k_r, w_hyp, pe, cache, open_acc, gate_out, nullptr};
@@ -416,7 +416,7 @@ int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* 
   CHECK_PTR(w_uk);
   CHECK_PTR(w_uv);
   CHECK_PTR(cache);
-  CHECK_PTR_ALIGN(open_acc, 4);
+  CHECK_PTR(open_acc);
   CHECK_PTR(out);
   const DecodeWs ws = decode_ws(dims);
   if (!workspace) return fail(MTLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws.total);
@@ -469,7 +469,7 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
   CHECK_PTR(w_uk);
   CHECK_PTR(w_uv);
   CHECK_PTR(cache);
-  CHECK_PTR_ALIGN(open_acc, 4);
+  CHECK_PTR(open_acc);
   CHECK_PTR(out);
   const PrefillWs ws = prefill_ws(dims, n_tokens);
   if (!workspace) return fail(MTLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws.total);

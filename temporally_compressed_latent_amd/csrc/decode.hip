@@ -310,11 +310,12 @@ struct MfmaAttn {
     }
   }
 
-  // Issue the loads of tile j0 of slots [lo, hi) into registers.  Rows past
-  // hi are zero; the row patch_row is skipped (it is filled from LDS when the
-  // tile is stored).
-  __device__ __forceinline__ static void load_tile(uint4* pre, const uint16_t* rows, int j0, int hi,
-                                   int patch_row) {
+  // Issue the loads of tile j0 of slots [.., hi) into registers (hi >= 1).
+  // Branch-free, so all of a thread's loads are in flight together: every
+  // chunk loads from row min(slot, hi - 1).  Rows past hi are zeroed, and the
+  // row patch_row (if any) replaced from LDS, when the tile is stored, so no
+  // loaded value is consumed before then.
+  __device__ __forceinline__ static void load_tile(uint4* pre, const uint16_t* rows, int j0, int hi) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
@@ -322,10 +323,7 @@ struct MfmaAttn {
       if (CHUNKS % NT == 0 || id < CHUNKS) {
         const int row = id / CPR, ch = id % CPR;
         const int slot = j0 + row;
-        if (slot >= hi)
-          pre[k] = uint4{0u, 0u, 0u, 0u};
-        else if (slot != patch_row)
-          pre[k] = *reinterpret_cast<const uint4*>(rows + static_cast<size_t>(slot) * W + ch * 8);
+        pre[k] = *reinterpret_cast<const uint4*>(rows + static_cast<size_t>(min(slot, hi - 1)) * W + ch * 8);
       }
     }
   }
@@ -344,7 +342,8 @@ struct MfmaAttn {
         const int id = tid + NT * k;
         if (CHUNKS % NT == 0 || id < CHUNKS) {
           const int row = id / CPR, ch = id % CPR;
-          uint4 v = pre[k];
+          const bool in = j0 + row < hi;
+          uint4 v = uint4{in ? pre[k].x : 0u, in ? pre[k].y : 0u, in ? pre[k].z : 0u, in ? pre[k].w : 0u};
           if constexpr (kPatch) {
             if (j0 + row == patch_row) v = *reinterpret_cast<const uint4*>(patch + ch * 8);
           }
@@ -356,7 +355,7 @@ struct MfmaAttn {
     for (int j0 = lo; j0 < hi; j0 += TS) {
       store_tile(j0);
       __syncthreads();
-      if (j0 + TS < hi) load_tile(pre, rows, j0 + TS, hi, patch_row);
+      if (j0 + TS < hi) load_tile(pre, rows, j0 + TS, hi);
 
       f32x4 sc[HT];
       if (wave < QKW) {
@@ -513,7 +512,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
   const uint16_t* rows =
       static_cast<const uint16_t*>(a.cache) + static_cast<size_t>(b) * a.max_slots * W;
   uint4 pre[A::CPT];
-  if (lo < hi) A::load_tile(pre, rows, lo, hi, -1);
+  if (lo < hi) A::load_tile(pre, rows, lo, hi);
   A::template run<false>(st, sm, rows, lo, hi, -1, nullptr, pre);
   A::finish(st, sm);
 
@@ -679,7 +678,7 @@ __global__ __launch_bounds__(1024) void decode_step_kernel(StepArgs a) {
   const uint16_t* rows = a.cache + static_cast<size_t>(b) * a.max_slots * W;
   const int patch_row = a.merge ? n - 1 : -1;
   uint4 pre[A::CPT];
-  A::load_tile(pre, rows, 0, n, patch_row);
+  A::load_tile(pre, rows, 0, n);
   A::template run<true>(st, sm, rows, 0, n, patch_row, s_new, pre);
   A::finish(st, sm);
 

@@ -2,11 +2,11 @@
 // Attention", Key claims: paper Sec. 4.1 Eq. 13; Method (1); Sec. 4.3 Eq. 17
 // for the cumulative in-block partial merges used by prefill).
 //
-// Work split: one workgroup per (sequence, chunk of consecutive blocks).  The
-// gates of the chunk's tokens are computed first (one wave per token, a d_c
-// dot product), then each thread owns some of the W = d_c + d_r columns and
-// walks the chunk's tokens in order, carrying the fp32 block sum.  Every
-// stored value is rounded once from that fp32 sum.
+// Work split: one workgroup per (sequence, run of consecutive blocks).  The
+// gates of the run's tokens are computed first (a wave takes four tokens at a
+// time, a d_c dot product each), then every (block, 8-column chunk) pair is
+// independent: a thread walks its block's tokens in order, carrying the fp32
+// block sum.  Every stored value is rounded once from that fp32 sum.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,32 +36,56 @@ __device__ __forceinline__ SeqRange seq_range(const MergeArgs& a, int b) {
   return r;
 }
 
-// Gates of tokens ta..ta+ntok-1 of sequence b into gw[0..ntok).
+// Gates of tokens ta..ta+ntok-1 of sequence b into gw[0..ntok): each wave
+// takes kGateTok tokens at a time (independent streams, loads in flight
+// together).
+constexpr int kGateTok = 4;
+
 template <typename T>
 __device__ void compute_gates(const MergeArgs& a, int b, int p0, int ta, int ntok, float* gw) {
   const T* c = static_cast<const T*>(a.c);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
-  for (int k = wave; k < ntok; k += nwaves) {
-    const int t = ta + k;
-    const size_t crow = (static_cast<size_t>(b) * a.T + (t - p0)) * a.d_c;
-    const size_t prow = static_cast<size_t>(t - 1) * a.d_c;
-    const float w = gate_of_token(c + crow, a.pe + prow, a.w_hyp, a.d_c, lane);
+  for (int k0 = wave * kGateTok; k0 < ntok; k0 += nwaves * kGateTok) {
+    const T* rows[kGateTok];
+    const float* pes[kGateTok];
+#pragma unroll
+    for (int k = 0; k < kGateTok; ++k) {
+      const int t = ta + k0 + k;
+      const bool in = k0 + k < ntok;
+      rows[k] = in ? c + (static_cast<size_t>(b) * a.T + (t - p0)) * a.d_c : nullptr;
+      pes[k] = in ? a.pe + static_cast<size_t>(t - 1) * a.d_c : a.pe;
+    }
+    float w[kGateTok];
+    gates_of_tokens<kGateTok, T>(rows, pes, a.w_hyp, a.d_c, lane, w);
     if (lane == 0) {
-      gw[k] = w;
-      if (a.gate_out) a.gate_out[static_cast<size_t>(b) * a.T + (t - p0)] = w;
+#pragma unroll
+      for (int k = 0; k < kGateTok; ++k) {
+        if (k0 + k < ntok) {
+          gw[k0 + k] = w[k];
+          if (a.gate_out) a.gate_out[static_cast<size_t>(b) * a.T + (ta + k0 + k - p0)] = w[k];
+        }
+      }
     }
   }
 }
 
+// Eight elements of x_t = [c_t ; k^R_t] starting at column e (e % 8 == 0, and
+// d_c % 8 == 0, so a chunk never straddles c and k^R).
 template <typename T>
-__device__ __forceinline__ float token_elem(const MergeArgs& a, int b, int tok, int e) {
+__device__ __forceinline__ void token_chunk(const MergeArgs& a, int b, int tok, int e, float* x) {
   const size_t row = static_cast<size_t>(b) * a.T + tok;
-  return e < a.d_c ? Store<T>::load(static_cast<const T*>(a.c), row * a.d_c + e)
-                   : Store<T>::load(static_cast<const T*>(a.k_r), row * a.d_r + (e - a.d_c));
+  if (e < a.d_c)
+    load8(static_cast<const T*>(a.c) + row * a.d_c + e, x);
+  else
+    load8(static_cast<const T*>(a.k_r) + row * a.d_r + (e - a.d_c), x);
 }
 
+// One workgroup per (sequence, run of blocks_per_wg consecutive blocks).
+// After the gates, thread t takes 8-column chunk ch of block blo + bb for
+// (bb, ch) = (t / CPB, t % CPB), CPB = W / 8 (and further blocks in steps of
+// 256 / CPB), and walks that block's tokens in order carrying the fp32 sums.
 template <typename T>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a, int blocks_per_wg,
                                                               int write_open) {
@@ -81,20 +105,36 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a, int b
 
   T* cache = static_cast<T*>(a.cache);
   T* P = static_cast<T*>(a.partials);
-  for (int e = threadIdx.x; e < W; e += blockDim.x) {
-    for (int blk = blo; blk <= bhi; ++blk) {
-      const int ts = blk * s + 1;
-      const int t0 = max(ts, r.p0);
-      const int t1 = min(ts + s - 1, r.t_last);
-      // A block that began before this call continues the open slot.
-      float acc = (t0 > ts) ? a.open_acc[static_cast<size_t>(b) * W + e] : 0.f;
-      for (int t = t0; t <= t1; ++t) {
-        acc = fmaf(gw[t - ta], token_elem<T>(a, b, t - r.p0, e), acc);
-        if (P) Store<T>::store(P, (static_cast<size_t>(b) * a.T + (t - r.p0)) * W + e, acc);
-      }
-      Store<T>::store(cache, (static_cast<size_t>(b) * a.max_slots + blk) * W + e, acc);
-      if (write_open && blk == r.bk1) a.open_acc[static_cast<size_t>(b) * W + e] = acc;
+  const int CPB = W / 8;
+  const int bpp = kMergeThreads / CPB;  // blocks per pass
+  const int ch = threadIdx.x % CPB, bb0 = threadIdx.x / CPB;
+  if (bb0 >= bpp) return;
+  const int e = ch * 8;
+  for (int blk = blo + bb0; blk <= bhi; blk += bpp) {
+    const int ts = blk * s + 1;
+    const int t0 = max(ts, r.p0);
+    const int t1 = min(ts + s - 1, r.t_last);
+    float acc[8];
+    if (t0 > ts) {  // a block that began before this call continues the open slot
+      const float* oa = a.open_acc + static_cast<size_t>(b) * W + e;
+      const float4 lo = *reinterpret_cast<const float4*>(oa);
+      const float4 hi = *reinterpret_cast<const float4*>(oa + 4);
+      acc[0] = lo.x; acc[1] = lo.y; acc[2] = lo.z; acc[3] = lo.w;
+      acc[4] = hi.x; acc[5] = hi.y; acc[6] = hi.z; acc[7] = hi.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0.f;
     }
+    for (int t = t0; t <= t1; ++t) {
+      float x[8];
+      token_chunk<T>(a, b, t - r.p0, e, x);
+      const float w = gw[t - ta];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, x[j], acc[j]);
+      if (P) store8(P + (static_cast<size_t>(b) * a.T + (t - r.p0)) * W + e, acc);
+    }
+    store8(cache + (static_cast<size_t>(b) * a.max_slots + blk) * W + e, acc);
+    if (write_open && blk == r.bk1) store8(a.open_acc + static_cast<size_t>(b) * W + e, acc);
   }
 }
 
@@ -113,12 +153,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_tail_kernel(MergeArgs a) 
   const int t0 = max(ts, r.p0);
   compute_gates<T>(a, b, r.p0, t0, r.t_last - t0 + 1, gw);
   __syncthreads();
-  for (int e = threadIdx.x; e < W; e += blockDim.x) {
-    float acc = (t0 > ts) ? a.open_acc[static_cast<size_t>(b) * W + e] : 0.f;
-    for (int t = t0; t <= r.t_last; ++t)
-      acc = fmaf(gw[t - t0], token_elem<T>(a, b, t - r.p0, e), acc);
-    a.open_acc[static_cast<size_t>(b) * W + e] = acc;
+  const int ch = threadIdx.x;
+  if (ch >= W / 8) return;
+  const int e = ch * 8;
+  float acc[8];
+  if (t0 > ts) {
+    const float* oa = a.open_acc + static_cast<size_t>(b) * W + e;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = oa[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
   }
+  for (int t = t0; t <= r.t_last; ++t) {
+    float x[8];
+    token_chunk<T>(a, b, t - r.p0, e, x);
+    const float w = gw[t - t0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, x[j], acc[j]);
+  }
+  store8(a.open_acc + static_cast<size_t>(b) * W + e, acc);
 }
 
 __global__ void pe_kernel(int rows, int d, float* pe) {
@@ -157,9 +211,13 @@ int grid_for(size_t n, int threads) {
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int dtype, hipStream_t st) {
-  const int blocks_per_wg = a.s >= kMaxChunkTokens ? 1 : kMaxChunkTokens / a.s;
   // Blocks one call can touch: ceil((T-1)/s) + 1 (a block may continue).
   const long long max_blocks = (static_cast<long long>(a.T) - 1 + a.s - 1) / a.s + 1;
+  // Blocks per workgroup: enough workgroups (~2048) to fill the chip, at most
+  // kMaxChunkTokens tokens of gates per workgroup.
+  const int cap = a.s >= kMaxChunkTokens ? 1 : kMaxChunkTokens / a.s;
+  long long per = (max_blocks * a.B + 2047) / 2048;
+  const int blocks_per_wg = static_cast<int>(per < 1 ? 1 : (per > cap ? cap : per));
   const long long chunks = (max_blocks + blocks_per_wg - 1) / blocks_per_wg;
   const int write_open = chunks == 1 ? 1 : 0;
   dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));

@@ -151,6 +151,14 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
 // loaded 64 at a time; the next tile is fetched into registers while the
 // current one is used.  Tiles past a wave's last visible slot are skipped by
 // that wave, and only tiles that cross its staircase are masked.
+//
+// Vector-ALU budget (a wave64 VALU instruction takes 4 cycles, exp 16, and a
+// 32x32x16 MFMA 32): the queries are pre-scaled by tau*log2(e), the score
+// accumulators start at -m so the MFMA returns s - m directly, and the
+// running max m is only moved (with the rescale of O and l) when some score
+// of the wave exceeds it by more than 2^kLazyLog2; otherwise probabilities
+// are taken against the stale max, which is exact after the final division
+// by l and stays far from fp32 overflow.
 // ---------------------------------------------------------------------------
 template <int DH, int DR, int NQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 && DH == 64 ? 2 : 1)))
@@ -167,6 +175,7 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   constexpr int NCH = TS * (KCH + VCH);    // 16-byte chunks per tile
   constexpr int CPT = (NCH + 255) / 256;
   static_assert(DH % 32 == 0 && DR % 16 == 0, "shape");
+  constexpr float kLazyLog2 = 8.f;
 
   __shared__ __align__(16) uint16_t sK[TS * KP];
   __shared__ __align__(16) uint16_t sV[TS * VP];
@@ -211,10 +220,15 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
           kv = *reinterpret_cast<const uint4*>(Pb + static_cast<size_t>(qi) * W + a.d_c + (d0 - DH));
         }
       }
-      qreg[t][kk] = __builtin_bit_cast(bf16x8, qv);
       const u16x8 qs = __builtin_bit_cast(u16x8, qv), ks = __builtin_bit_cast(u16x8, kv);
+      u16x8 qsc;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) dpart = fmaf(bf16_bits_to_f32(qs[r]), bf16_bits_to_f32(ks[r]), dpart);
+      for (int r = 0; r < 8; ++r) {
+        const float qf = bf16_bits_to_f32(qs[r]);
+        dpart = fmaf(qf, bf16_bits_to_f32(ks[r]), dpart);
+        qsc[r] = f32_to_bf16_bits(qf * qk_scale);
+      }
+      qreg[t][kk] = __builtin_bit_cast(bf16x8, qsc);
     }
     dpart += __shfl_xor(dpart, 32, 64);
     m[t] = dpart * qk_scale;
@@ -240,65 +254,66 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   const int nk_w = qw0 < N ? (min(qw0 + QW, N) - 1) / s : 0;
   const int full_w = qw0 / s;
 
+  // Branch-free tile loads (all in flight together): every chunk reads row
+  // min(slot, nk - 1) (nk >= 1 whenever this runs); rows past nk are zeroed
+  // when the tile is stored, so no value is consumed before then.
   uint4 pre[CPT];
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int id = tid + 256 * k;
       if (NCH % 256 == 0 || id < NCH) {
-        uint4 v = uint4{0u, 0u, 0u, 0u};
-        if (id < TS * KCH) {
-          const int row = id / KCH, ch = id % KCH;
-          const int slot = j0 + row;
-          if (slot < nk) {
-            const int tk = s * slot + s - 1;  // token holding the completed slot
-            v = ch < DH / 8
-                    ? *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(tk) * DH + ch * 8)
-                    : *reinterpret_cast<const uint4*>(Pb + static_cast<size_t>(tk) * W + a.d_c + (ch - DH / 8) * 8);
-          }
-        } else {
-          const int id2 = id - TS * KCH;
-          const int row = id2 / VCH, ch = id2 % VCH;
-          const int slot = j0 + row;
-          if (slot < nk)
-            v = *reinterpret_cast<const uint4*>(vv + static_cast<size_t>(s * slot + s - 1) * DH + ch * 8);
-        }
-        pre[k] = v;
+        const bool is_k = id < TS * KCH;
+        const int id2 = is_k ? id : id - TS * KCH;
+        const int row = is_k ? id2 / KCH : id2 / VCH;
+        const int ch = is_k ? id2 % KCH : id2 % VCH;
+        const int slot = j0 + row;
+        const int tk = s * min(slot, nk - 1) + s - 1;  // token holding the completed slot
+        const uint16_t* src;
+        if (!is_k)
+          src = vv + static_cast<size_t>(tk) * DH + ch * 8;
+        else if (ch < DH / 8)
+          src = kc + static_cast<size_t>(tk) * DH + ch * 8;
+        else
+          src = Pb + static_cast<size_t>(tk) * W + a.d_c + (ch - DH / 8) * 8;
+        pre[k] = *reinterpret_cast<const uint4*>(src);
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int j0) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int id = tid + 256 * k;
       if (NCH % 256 == 0 || id < NCH) {
-        if (id < TS * KCH) {
-          const int row = id / KCH, ch = id % KCH;
-          *reinterpret_cast<uint4*>(sK + row * KP + ch * 8) = pre[k];
-        } else {
-          const int id2 = id - TS * KCH;
-          const int row = id2 / VCH, ch = id2 % VCH;
-          *reinterpret_cast<uint4*>(sV + row * VP + ch * 8) = pre[k];
-        }
+        const bool is_k = id < TS * KCH;
+        const int id2 = is_k ? id : id - TS * KCH;
+        const int row = is_k ? id2 / KCH : id2 / VCH;
+        const int ch = is_k ? id2 % KCH : id2 % VCH;
+        const bool in = j0 + row < nk;
+        const uint4 v = pre[k];
+        const uint4 z = uint4{in ? v.x : 0u, in ? v.y : 0u, in ? v.z : 0u, in ? v.w : 0u};
+        uint16_t* dst = is_k ? sK + row * KP + ch * 8 : sV + row * VP + ch * 8;
+        *reinterpret_cast<uint4*>(dst) = z;
       }
     }
   };
 
   if (nk > 0) load_tile(0);
   for (int j0 = 0; j0 < nk; j0 += TS) {
-    store_tile();
+    store_tile(j0);
     __syncthreads();
     if (j0 + TS < nk) load_tile(j0 + TS);
 
     if (j0 < nk_w) {
-      // S^T = K Q^T: sc[rt][t][i] = score(slot j0 + 32rt + 8(i/4) + 4grp + i%4, query t)
+      // S^T = K Q^T - m: sc[rt][t][i] = score(slot j0 + 32rt + 8(i/4) + 4grp + i%4,
+      // query t) - m[t], in log2 units
       f32x16 sc[2][NQ];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int t = 0; t < NQ; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sc[rt][t][i] = 0.f;
+          for (int i = 0; i < 16; ++i) sc[rt][t][i] = -m[t];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -312,39 +327,47 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
       const bool boundary = j0 + TS > full_w;
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
-        const int qi = qw0 + 32 * t + c32;
-        float mx = -INFINITY;
+        if (boundary) {
+          const int qi = qw0 + 32 * t + c32;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+          for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float v = sc[rt][t][i] * qk_scale;
-            if (boundary) {
+            for (int i = 0; i < 16; ++i) {
               const int slot = j0 + 32 * rt + 8 * (i / 4) + 4 * grp + (i % 4);
               // completed slot (0-based) visible to query qi (0-based): s*(slot+1) <= qi
-              if (s * (slot + 1) > qi) v = -INFINITY;
+              if (s * (slot + 1) > qi) sc[rt][t][i] = -INFINITY;
             }
-            sc[rt][t][i] = v;
-            mx = fmaxf(mx, v);
           }
         }
+        float mx = sc[0][t][0];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[rt][t][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mn = fmaxf(m[t], mx);
-        const float alpha = fast_exp2(m[t] - mn);
-        m[t] = mn;
+        if (__any(mx > kLazyLog2)) {
+          const float d = fmaxf(mx, 0.f);
+          const float alpha = fast_exp2(-d);
+          m[t] += d;
+          lp[t] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[dt][t] *= alpha;
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[rt][t][i] -= d;
+        }
         float ls = 0.f;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float pv = fast_exp2(sc[rt][t][i] - mn);
+            const float pv = fast_exp2(sc[rt][t][i]);
             sc[rt][t][i] = pv;
             ls += pv;
           }
         }
-        lp[t] = lp[t] * alpha + ls;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[dt][t] *= alpha;
+        lp[t] += ls;
       }
 
       // O^T += V^T P^T over the tile's four 16-slot chunks
@@ -405,7 +428,7 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 
 // 32-query column tiles per wave of the d_h = 64 attention kernel.
 #ifndef MTLA_PREFILL_QUERY_TILES
-#define MTLA_PREFILL_QUERY_TILES 2
+#define MTLA_PREFILL_QUERY_TILES 1
 #endif
 constexpr int kPrefillQueryTiles = MTLA_PREFILL_QUERY_TILES;
 
