@@ -42,7 +42,8 @@ def parse_args():
     p.add_argument("--no-components", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default=None,
-                   help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, llm_decode)")
+                   help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, llm_decode, "
+                        "copy: the counter-calibration copy kernel)")
     return p.parse_args()
 
 
@@ -288,6 +289,32 @@ def run_llm_decode(w, steps, warmup, m, torch, workloads):
 
 
 # ---------------------------------------------------------------------------
+# copy kernel of known size: calibrates the HBM byte counters
+# ---------------------------------------------------------------------------
+
+def run_copy(steps, warmup, torch):
+    """A plain elementwise copy (torch.neg) of 1 GiB of bf16: its FETCH_SIZE and
+    WRITE_SIZE counters are divided into the known byte count to give the
+    factor applied to the same counters of the MTLA kernels."""
+    n = 1 << 29
+    x = torch.randn(n, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    for _ in range(max(warmup, 1)):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.neg(x, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = x.numel() * x.element_size()
+    return {"workload": "copy_bf16_1GiB", "kernel": "torch.neg", "bytes_read": nbytes,
+            "bytes_written": nbytes, "ms_per_call": ms, "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline (the fp64 oracle) and parity of the headline run
 # ---------------------------------------------------------------------------
 
@@ -314,6 +341,34 @@ def cpu_baseline_and_parity(w, dl, torch):
 
 
 # ---------------------------------------------------------------------------
+# measured HBM traffic of the headline kernel (rocprofv3 counter passes)
+# ---------------------------------------------------------------------------
+
+def measured_traffic(kernel):
+    """Bytes per launch of `kernel` from profiles/traffic.json (two rocprofv3
+    --pmc passes, FETCH_SIZE and WRITE_SIZE, scaled by the factors a plain copy
+    of known size gives).  None when there is no record for this kernel or when
+    its sources have changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter record"
+    if rec.get("kernel") != kernel:
+        return None, "no counter record for this kernel"
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(root, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None, "kernel sources changed since the counters were taken"
+    return rec["bytes_per_launch"], rec["profile"]
+
+
+# ---------------------------------------------------------------------------
 
 def main():
     args = parse_args()
@@ -334,7 +389,8 @@ def main():
         fn = {"st_decode_s2": lambda: run_decode_loop(W[1], args.steps, args.warmup, m, torch, workloads)[0],
               "st_decode_s4": lambda: run_decode_loop(W[2], args.steps, args.warmup, m, torch, workloads)[0],
               "prefill": lambda: run_prefill(W[3], args.steps, args.warmup, m, torch, workloads)[0],
-              "llm_decode": lambda: run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0]}
+              "llm_decode": lambda: run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0],
+              "copy": lambda: run_copy(args.steps, args.warmup, torch)}
         print(json.dumps(fn[args.only]()), flush=True)
         return 0
 
@@ -358,6 +414,7 @@ def main():
 
     k = head["dominant_kernel"]
     achieved = k["GBps"]
+    traffic, traffic_src = measured_traffic(k["name"])
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -376,7 +433,8 @@ def main():
                    "tokens_per_step": head["tokens_per_step"], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": k["name"], "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "avg_launch_us": k["avg_launch_us"],
+                     "traffic": traffic, "traffic_unit": "bytes per launch",
+                     "traffic_source": traffic_src, "avg_launch_us": k["avg_launch_us"],
                      "algorithmic_bytes_per_launch": k["algorithmic_bytes_per_launch"]},
         "plan": head["plan"],
         "cpu_baseline": cpu,
