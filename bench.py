@@ -114,7 +114,7 @@ class DecodeLoop:
         self.pe = torch.empty(N, w.d_c, dtype=torch.float32, device="cuda")
         m.mtla_sinusoidal_pe(self.pe)
         self.cache = torch.zeros(B, d.max_slots, d.width, dtype=bf, device="cuda")
-        self.open_acc = torch.zeros(B, d.width, dtype=torch.float32, device="cuda")
+        self.open_acc = torch.zeros(B, 2, d.width, dtype=torch.float32, device="cuda")
         self.ws = torch.zeros(m.mtla_decode_workspace_bytes(d), dtype=torch.uint8, device="cuda")
         self.out = torch.empty(N, B, H, w.d_h, dtype=bf, device="cuda")
         self.host_inputs = (lat, qry, wts)
@@ -193,7 +193,7 @@ def run_prefill(w, steps, warmup, m, torch, workloads):
     pe = torch.empty(N, w.d_c, dtype=torch.float32, device="cuda")
     m.mtla_sinusoidal_pe(pe)
     cache = torch.zeros(B, d.max_slots, d.width, dtype=bf, device="cuda")
-    open_acc = torch.zeros(B, d.width, dtype=torch.float32, device="cuda")
+    open_acc = torch.zeros(B, 2, d.width, dtype=torch.float32, device="cuda")
     out = torch.empty(B, N, H, w.d_h, dtype=bf, device="cuda")
     ws = torch.empty(m.mtla_prefill_workspace_bytes(d, N), dtype=torch.uint8, device="cuda")
 
@@ -226,7 +226,7 @@ def run_llm_decode(w, steps, warmup, m, torch, workloads):
     log(f"{w.name}: generating {B} x {T} latents")
     t0 = time.time()
     cache = torch.zeros(B, d.max_slots, d.width, dtype=bf, device="cuda")
-    open_acc = torch.zeros(B, d.width, dtype=torch.float32, device="cuda")
+    open_acc = torch.zeros(B, 2, d.width, dtype=torch.float32, device="cuda")
     pe = torch.empty(T, w.d_c, dtype=torch.float32, device="cuda")
     m.mtla_sinusoidal_pe(pe)
     wts = workloads.weights(w)

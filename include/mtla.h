@@ -28,6 +28,13 @@
  * dtypes: `dims->dtype` is the storage type of c, k_r, q_c, q_r, w_uk, w_uv,
  *   the cache and the outputs (fp32 or bf16, round-to-nearest-even).  w_hyp,
  *   pe and open_acc are always fp32.  Accumulation is always fp32.
+ * Open-slot state: open_acc is [B, 2, d_c + d_r] fp32.  The unrounded fp32
+ *   value of the open slot after token t is kept at open_acc[b, t % 2]; a call
+ *   that continues a block at token t reads open_acc[b, (t-1) % 2].  (Keeping
+ *   the state by token parity lets the several workgroups that decode one
+ *   sequence in mtla_decode_step read the old state while one of them writes
+ *   the new one.)  Only the half for the last token a call appends is
+ *   written; the other half is left as it was.
  * Errors: all argument checks run before anything is enqueued; on a failed
  *   check the call returns a negative mtla_status, enqueues nothing, and
  *   mtla_last_error() describes the failure.  A kernel launch failure returns
@@ -113,8 +120,10 @@ int32_t mtla_sinusoidal_pe(int32_t rows, int32_t d, float* pe, void* stream);
  *   cache    device [B, max_slots, d_c + d_r] storage dtype, in/out: every
  *            slot touched by the appended tokens is written (rounded once from
  *            the fp32 sum); other rows are untouched.
- *   open_acc device [B, d_c + d_r] fp32, in/out: the unrounded fp32 value of
- *            the last slot touched.  Read only when pos0[b] continues a block.
+ *   open_acc device [B, 2, d_c + d_r] fp32, in/out: open-slot state (see
+ *            the conventions above): [b, (pos0[b]-1) % 2] is read only when
+ *            pos0[b] continues a block; [b, t_last % 2] is written, t_last =
+ *            pos0[b] + n_tokens - 1.
  *   gate_out device [B, n_tokens] fp32 or NULL: the gates w_t.
  */
 int32_t mtla_merge_append(const mtla_dims* dims, const int32_t* pos0, int32_t n_tokens,
@@ -164,7 +173,9 @@ int32_t mtla_decode_plan(const mtla_dims* dims, int32_t* splits, int32_t* fused)
  * Page: "Multi-head Temporal Latent Attention", Method (1): during inference
  * each step updates the open slot (or opens a new one) and attends
  * ceil(t/s) slots.  For a short cache (one split) with bf16 storage this is
- * a single kernel with one workgroup per sequence.
+ * a single kernel with one workgroup per (sequence, group of heads); the
+ * open-slot state is read at [b, (pos[b]-1) % 2] and written at
+ * [b, pos[b] % 2].
  */
 int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
                          const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
@@ -233,8 +244,9 @@ int32_t mtla_prefill_workspace_bytes(const mtla_dims* dims, int32_t n_tokens, si
  *   w_hyp, pe, pe_rows: as for mtla_merge_append (pe_rows >= N).
  *   w_uk, w_uv device [H, d_h, d_c].
  *   cache device [B, max_slots, d_c + d_r], written: slots 1..ceil(N/s).
- *   open_acc device [B, d_c + d_r] fp32, written: fp32 value of slot ceil(N/s),
- *         so that decoding can continue at token N+1.
+ *   open_acc device [B, 2, d_c + d_r] fp32: [b, N % 2] is written with the
+ *         fp32 value of slot ceil(N/s), so that decoding can continue at
+ *         token N+1.
  *   out device [B, N, H, d_h], written.
  *   N <= s * max_slots.
  */

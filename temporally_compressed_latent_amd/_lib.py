@@ -206,7 +206,7 @@ def mtla_merge_append(dims: MtlaDims, pos0, c, k_r, w_hyp, pe, cache, open_acc,
         _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
         _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32),
         _tensor("cache", cache, (B, dims.max_slots, W), st),
-        _tensor("open_acc", open_acc, (B, W), torch.float32),
+        _tensor("open_acc", open_acc, (B, 2, W), torch.float32),
         _tensor("gate_out", gate_out, (B, T), torch.float32, optional=True),
     )
     _check(_lib.mtla_merge_append(ctypes.byref(dims), args[0], T, args[1], args[2], args[3],
@@ -259,7 +259,7 @@ def mtla_decode_step(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w_uk, w_u
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
         _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
-        _tensor("open_acc", open_acc, (B, dims.width), torch.float32),
+        _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
         _tensor("out", out, (B, H, dims.d_h), st),
         ws, ws_bytes, _stream(stream)))
 
@@ -328,7 +328,7 @@ def mtla_prefill(dims: MtlaDims, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_uv, cache,
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
         _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
-        _tensor("open_acc", open_acc, (B, dims.width), torch.float32),
+        _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
         _tensor("out", out, (B, N, H, dims.d_h), st),
         ws, ws_bytes, _stream(stream)))
 

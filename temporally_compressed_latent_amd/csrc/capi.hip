@@ -1,6 +1,7 @@
 // C ABI of the MTLA hot path: argument validation, workspace sizing and
 // kernel dispatch.  Every check runs before anything is enqueued; no HIP API
 // is called on a failed check.
+#include <climits>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -59,6 +60,11 @@ int32_t check_dims(const mtla_dims* d) {
   if ((8 * int64_t(d->d_c) + int64_t(d->d_h) * 65) * 4 > 65536)
     return fail(MTLA_ERR_UNSUPPORTED, "d_c=%d with d_h=%d exceeds the up-projection kernel's LDS", d->d_c, d->d_h);
   const int64_t W = d->d_c + d->d_r;
+  // one sequence's rows are addressed through a buffer resource whose size
+  // is a 32-bit byte count
+  if (int64_t(d->max_slots) * W * 4 > INT32_MAX)
+    return fail(MTLA_ERR_UNSUPPORTED, "max_slots=%d rows of %lld elements exceed 2^31 bytes per sequence",
+                d->max_slots, static_cast<long long>(W));
   if (int64_t(d->batch) * d->max_slots * W > kMaxElems)
     return fail(MTLA_ERR_UNSUPPORTED, "cache of %lld elements is too large",
                 static_cast<long long>(int64_t(d->batch) * d->max_slots * W));
@@ -344,7 +350,7 @@ mtla::StepArgs step_args(const mtla_dims* d, const int32_t* pos, const void* c, 
                          const void* q_r, const void* w_uk, const void* w_uv, void* cache,
                          float* open_acc, void* out, int merge) {
   return mtla::StepArgs{d->batch, d->heads, d->d_h, d->d_c, d->d_r, d->stride_s, d->max_slots,
-                        pe_rows, merge, d->softmax_scale, pos,
+                        pe_rows, merge, /*groups, set by the launcher*/ 0, d->softmax_scale, pos,
                         static_cast<const uint16_t*>(c), static_cast<const uint16_t*>(k_r), w_hyp,
                         pe, static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
                         static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv),
@@ -459,6 +465,10 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
     return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d exceeds the cache capacity s*max_slots", n_tokens);
   if (int64_t(dims->batch) * n_tokens * dims->heads * (dims->d_c + dims->d_r) > kMaxElems)
     return fail(MTLA_ERR_UNSUPPORTED, "prefill too large");
+  // the partial merges [B, N, W] are read through a buffer resource (32-bit size)
+  if (int64_t(dims->batch) * n_tokens * (dims->d_c + dims->d_r) * 4 > INT32_MAX)
+    return fail(MTLA_ERR_UNSUPPORTED, "prefill of %d x %d tokens exceeds the 2^31-byte partial-merge buffer",
+                dims->batch, n_tokens);
   if (dims->batch == 0 || n_tokens == 0) return ok();
   CHECK_PTR(q_c);
   if (dims->d_r > 0) CHECK_PTR(q_r);

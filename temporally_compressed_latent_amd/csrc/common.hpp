@@ -76,10 +76,41 @@ __device__ __forceinline__ bool stride_visible(int i, int j, int s) {
 // ---------------------------------------------------------------------------
 // Wave64 reductions.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Reductions over the 16 lanes of each DPP row (lanes 16r .. 16r+15); every
+// lane of the row receives the result.  Four DPP moves, no LDS traffic:
+// swap neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), then
+// row_half_mirror (lane i <- 7 - i within 8) and row_mirror (lane i <- 15 - i)
+// bring in the other quad and the other half.  The pairs combined at each
+// step are the same for every lane, so all lanes hold bit-identical sums.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
   return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+
+// Sum over the 64 lanes of a wave, returned to every lane: the four 16-lane
+// row sums (DPP), then (row0 + row1) + (row2 + row3) from lanes 0, 16, 32, 48.
+// The order is fixed, so every kernel that uses it gets the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (a0 + a1) + (a2 + a3);
 }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -88,6 +119,10 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Word 3 of a raw buffer resource on gfx9-family parts (CDNA): 32-bit data
+// format, no swizzle, offsets checked against num_records.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // Gates of NTOK tokens, computed by one wave ("Multi-head Temporal Latent
 // Attention", Key claims, paper Sec. 4.1 Eq. 13):
@@ -117,6 +152,19 @@ __device__ __forceinline__ void gates_of_tokens(const T* const (&c_rows)[NTOK],
     const float z = wave_sum(acc[k]);
     w[k] = c_rows[k] ? 1.f / (1.f + expf(-z)) : 0.f;
   }
+}
+
+// The same gate from values a lane has already loaded: x[j], pe[j] and wh[j]
+// are element lane + 64 j of c_t, pe_t and W_hyp (GE = d_c / 64).  Same
+// operation order as gates_of_tokens, so the result is bit-identical.
+template <int GE>
+__device__ __forceinline__ float gate_from_lane_values(const float (&x)[GE], const float (&pe)[GE],
+                                                       const float (&wh)[GE]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < GE; ++j) acc = fmaf(x[j] + pe[j], wh[j], acc);
+  const float z = wave_sum(acc);
+  return 1.f / (1.f + expf(-z));
 }
 
 template <typename T>

@@ -12,6 +12,8 @@
 // Every head reads the same slot rows, so the MFMA decode kernel puts all
 // heads of a sequence in one workgroup (heads are the MFMA M dimension) and
 // reads each cache row from HBM once.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -310,52 +312,67 @@ struct MfmaAttn {
     }
   }
 
-  // Issue the loads of tile j0 of slots [.., hi) into registers (hi >= 1).
-  // Branch-free, so all of a thread's loads are in flight together: every
-  // chunk loads from row min(slot, hi - 1).  Rows past hi are zeroed, and the
-  // row patch_row (if any) replaced from LDS, when the tile is stored, so no
-  // loaded value is consumed before then.
-  __device__ __forceinline__ static void load_tile(uint4* pre, const uint16_t* rows, int j0, int hi) {
+  // Buffer resource over the memory rows [0, hm) of a sequence (hm * W bf16
+  // from `rows`): a load past them returns zero and touches no memory.
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* rows, int hm) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(rows), static_cast<short>(0),
+                                             hm * W * 2, kBufferRsrcWord3);
+  }
+
+  // Issue the loads of the tile of slots j0 .. j0+TS-1 into registers: chunk
+  // id = tid + NT*k of the tile is 16 bytes at byte j0*W*2 + id*16 of the
+  // rows (the tile's rows are contiguous), so every load shares one offset
+  // register.  All of a thread's loads are in flight together; rows at or
+  // past hm read as zero.
+  __device__ __forceinline__ static void load_tile(uint4* pre, __amdgpu_buffer_rsrc_t rs, int j0) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      const int id = tid + NT * k;
-      if (CHUNKS % NT == 0 || id < CHUNKS) {
-        const int row = id / CPR, ch = id % CPR;
-        const int slot = j0 + row;
-        pre[k] = *reinterpret_cast<const uint4*>(rows + static_cast<size_t>(min(slot, hi - 1)) * W + ch * 8);
-      }
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, j0 * (W * 2) + k * (NT * 16), 0);
+      pre[k] = uint4{v[0], v[1], v[2], v[3]};
     }
   }
 
-  // Slots [lo, hi) of the sequence's rows `rows` (W bf16 each), the first
-  // tile already loaded into `pre` by load_tile.  When patch_row >= 0 that row
-  // is taken from `patch` (LDS) instead of memory.
-  template <bool kPatch>
-  __device__ __forceinline__ static void run(State& st, Smem& sm, const uint16_t* rows, int lo, int hi,
-                                             int patch_row, const uint16_t* patch, uint4* pre) {
+  // Issue the loads of the first PD tiles of slots [lo, ..).
+  template <int PD>
+  __device__ __forceinline__ static void prefetch(uint4* pre, __amdgpu_buffer_rsrc_t rs, int lo) {
+#pragma unroll
+    for (int d = 0; d < PD; ++d) load_tile(pre + d * CPT, rs, lo + d * TS);
+  }
+
+  // Slots [lo, hi) of one sequence.  Rows below hm come from memory through
+  // the buffer resource rs (rows_rsrc(rows, hm)), via the PD register tiles
+  // `pre` (PD * CPT vectors) that prefetch<PD> filled; the next PD-th tile's
+  // loads are issued as soon as a tile has been stored to LDS.  With kPatch
+  // the row hm (== hi - 1) is taken from `patch` (LDS).
+  template <bool kPatch, int PD>
+  __device__ __forceinline__ static void run(State& st, Smem& sm, __amdgpu_buffer_rsrc_t rs, int lo, int hi,
+                                             int hm, const uint16_t* patch, uint4* pre) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    auto store_tile = [&](int j0) {
+    // The registers are only ever stored (never selected against another
+    // source), so they stay registers: the patch row is skipped here and
+    // copied into its place by CPR threads, at disjoint addresses.
+    auto store_tile = [&](int j0, const uint4* p) {
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
         const int id = tid + NT * k;
         if (CHUNKS % NT == 0 || id < CHUNKS) {
           const int row = id / CPR, ch = id % CPR;
-          const bool in = j0 + row < hi;
-          uint4 v = uint4{in ? pre[k].x : 0u, in ? pre[k].y : 0u, in ? pre[k].z : 0u, in ? pre[k].w : 0u};
-          if constexpr (kPatch) {
-            if (j0 + row == patch_row) v = *reinterpret_cast<const uint4*>(patch + ch * 8);
-          }
-          *reinterpret_cast<uint4*>(sm.k + row * PITCH + ch * 8) = v;
+          if (!kPatch || j0 + row != hm) *reinterpret_cast<uint4*>(sm.k + row * PITCH + ch * 8) = p[k];
         }
+      }
+      if constexpr (kPatch) {
+        if (tid < CPR && hm >= j0 && hm < j0 + TS)
+          *reinterpret_cast<uint4*>(sm.k + (hm - j0) * PITCH + tid * 8) =
+              *reinterpret_cast<const uint4*>(patch + tid * 8);
       }
     };
 
-    for (int j0 = lo; j0 < hi; j0 += TS) {
-      store_tile(j0);
+    auto tile = [&](int j0, uint4* p) {
+      store_tile(j0, p);
       __syncthreads();
-      if (j0 + TS < hi) load_tile(pre, rows, j0 + TS, hi);
+      if (j0 + PD * TS < hm) load_tile(p, rs, j0 + PD * TS);
 
       f32x4 sc[HT];
       if (wave < QKW) {
@@ -381,10 +398,7 @@ struct MfmaAttn {
           for (int i = 0; i < 4; ++i) {
             float v = valid ? sc[ht][i] : -INFINITY;
             sc[ht][i] = v;
-            v = fmaxf(v, __shfl_xor(v, 1, 64));
-            v = fmaxf(v, __shfl_xor(v, 2, 64));
-            v = fmaxf(v, __shfl_xor(v, 4, 64));
-            v = fmaxf(v, __shfl_xor(v, 8, 64));
+            v = row16_max(v);
             if (c16 == 0) sm.red[wave][ht * 16 + 4 * g + i] = v;
           }
         }
@@ -438,6 +452,13 @@ struct MfmaAttn {
         }
       }
       __syncthreads();
+    };
+
+    for (int j0 = lo; j0 < hi; j0 += PD * TS) {
+      tile(j0, pre);
+      if constexpr (PD == 2) {
+        if (j0 + TS < hi) tile(j0 + TS, pre + CPT);
+      }
     }
   }
 
@@ -452,10 +473,7 @@ struct MfmaAttn {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = st.l[ht][i];
-          v += __shfl_xor(v, 1, 64);
-          v += __shfl_xor(v, 2, 64);
-          v += __shfl_xor(v, 4, 64);
-          v += __shfl_xor(v, 8, 64);
+          v = row16_sum(v);
           if (c16 == 0) sm.red[wave][ht * 16 + 4 * g + i] = v;
         }
       }
@@ -511,9 +529,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
   A::init(st);
   const uint16_t* rows =
       static_cast<const uint16_t*>(a.cache) + static_cast<size_t>(b) * a.max_slots * W;
+  const auto rs = A::rows_rsrc(rows, hi);
   uint4 pre[A::CPT];
-  if (lo < hi) A::load_tile(pre, rows, lo, hi);
-  A::template run<false>(st, sm, rows, lo, hi, -1, nullptr, pre);
+  A::template prefetch<1>(pre, rs, lo);
+  A::template run<false, 1>(st, sm, rs, lo, hi, hi, nullptr, pre);
   A::finish(st, sm);
 
   if (nsplit == 1) {
@@ -563,159 +582,210 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Fused decode step for short caches: one workgroup of 16 waves per sequence
-// does everything for one token, so no other workgroup depends on it:
-//   merge (optional) : gate w_t, slot ceil(t/s) <- reset ? w x : acc + w x,
-//                      written to the cache and kept in LDS for the tile;
-//   absorb           : q~[h] = W_UK[h]^T q_c[h], scaled, bf16, into LDS;
-//   attention        : the MFMA core over slots 1..ceil(t/s);
+// Fused decode step for short caches.  One workgroup of 16 waves per
+// (sequence, group of HG heads) does everything for one token:
+//   merge            : gate w_t and slot ceil(t/s) <- reset ? w x : acc + w x,
+//                      computed by every group of the sequence; group 0 writes
+//                      the cache row and the fp32 state, the others only use
+//                      the row (kept in LDS) as the tile's last key;
+//   absorb           : q~[h] = W_UK[h]^T q_c[h] for the group's heads, scaled,
+//                      bf16, into LDS;
+//   attention        : the MFMA core over slots 1..ceil(t/s), two tiles of
+//                      cache rows in flight in registers;
 //   up-projection    : out[h] = W_UV[h] o_lat[h], o_lat kept in LDS.
-// The absorb and up-projection loads (16 bytes each) are spread over 1024
-// threads so each thread issues a single round of them.
+// Splitting the heads spreads the per-step weight traffic (W_UK and W_UV, the
+// largest reads at short caches) over more compute units; every group reads
+// the sequence's cache rows, and all groups of a sequence run on one XCD so
+// those rows are fetched into one L2.  The open slot's fp32 state is double
+// buffered by token parity: step t reads [b, (t-1) % 2] and writes
+// [b, t % 2], so no group reads what another is writing.
 // ---------------------------------------------------------------------------
-// Loads per thread the fused step keeps in flight for W_UK and for W_UV.
-constexpr int kStepMaxLoads = 16;
+// W_UK / W_UV load shapes of the step kernel (nth threads) for a group of hg
+// heads of width d_h: absorb row groups eg_n and W_UK rows per thread nl;
+// up-projection threads per output tpo and W_UV chunks per thread nv.
+struct StepShape {
+  int eg_n, nl, tpo, nv;
+};
+__host__ __device__ constexpr StepShape step_shape(int nth, int hg, int d_h, int d_c) {
+  const int KC = d_c / 8;
+  const int eg_n = nth / (KC * hg);
+  const int nout = hg * d_h;
+  int tpo = 1;
+  while (tpo < 64 && 2 * tpo * nout <= nth) tpo *= 2;
+  return StepShape{eg_n, eg_n > 0 ? (d_h + eg_n - 1) / eg_n : 1 << 30, tpo,
+                   nout <= nth ? (KC + tpo - 1) / tpo : 1 << 30};
+}
 
-template <int HT, int DC, int DR, int TS>
-__global__ __launch_bounds__(1024) void decode_step_kernel(StepArgs a) {
-  using A = MfmaAttn<HT, DC, DR, 16, TS>;
+// Instances: (d_c, d_R, tile slots, heads per group, largest d_h, threads,
+// cache tiles in flight, merge the token first).
+template <int DC, int DR, int TS, int HG, int DH, int NTH, int PD, bool MERGE>
+__global__ __launch_bounds__(NTH) void decode_step_kernel(StepArgs a) {
+  using A = MfmaAttn<1, DC, DR, NTH / 64, TS>;
   constexpr int W = A::W, HP = A::HP, PITCH = A::PITCH, CPW = A::CPW, CT = A::CT, NT = A::NT;
   constexpr int KC = DC / 8;
-  constexpr int MAXL = kStepMaxLoads;
-  static_assert(TS * PITCH * 2 >= HP * DC * 4, "o_lat must fit in the tile buffer");
+  constexpr int GE = DC / 64;
+  constexpr StepShape SMAX = step_shape(NTH, HG, DH, DC);
+  constexpr int MAXK = SMAX.nl, MAXV = SMAX.nv;  // in-flight W_UK / W_UV vectors per thread
+  static_assert(NT == NTH, "thread count");
+  static_assert(MAXK <= 16 && MAXV <= 16, "load shape");
   __shared__ typename A::Smem sm;
   __shared__ __align__(16) uint16_t s_new[W];
-  __shared__ float s_gate;
-  const int b = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id: id L runs on
+  // XCD L % 8.  Sequence b goes to XCD b % 8 with all of its head groups.
+  const int G = a.groups;
+  const int L = blockIdx.x, xcd = L & 7, k8 = L >> 3;
+  const int grp = k8 % G, b = 8 * (k8 / G) + xcd;
+  if (b >= a.B) return;
+  const int H = a.H, d_h = a.d_h, h0 = grp * HG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int H = a.H, d_h = a.d_h;
+  const StepShape sh = step_shape(NTH, HG, d_h, DC);
 
   const int pos = a.pos[b];
-  const int n = pos >= 1 ? slot_of(pos, a.s) : 0;
-  const bool ok = pos >= 1 && n <= a.max_slots && (!a.merge || pos <= a.pe_rows);
-  uint16_t* out = a.out + static_cast<size_t>(b) * H * d_h;
-  if (!ok) {
-    for (int idx = tid; idx < H * d_h; idx += NT) out[idx] = 0x7fc0u;  // NaN
-    return;
+  // Every load below is issued unconditionally (indices clamped into the
+  // tensors, unused values dropped at their use), so the compiler can count
+  // the loads in flight and wait only for the ones each phase needs.
+  // Loads that do not depend on the position go out first: W_UK rows and the
+  // matching query elements (absorb), and the merge's token values and W_hyp.
+  const int kc = tid % KC, hl = (tid / KC) % HG, eg = tid / (KC * HG);
+  const int nl = eg < sh.eg_n ? (d_h - eg + sh.eg_n - 1) / sh.eg_n : 0;
+  uint4 wk[MAXK];
+  uint16_t qb[MAXK];
+#pragma unroll
+  for (int i = 0; i < MAXK; ++i) {
+    const int e = min(eg + i * sh.eg_n, d_h - 1);
+    wk[i] = *reinterpret_cast<const uint4*>(a.w_uk + (static_cast<size_t>(h0 + hl) * d_h + e) * DC + kc * 8);
+    qb[i] = a.q_c[(static_cast<size_t>(b) * H + h0 + hl) * d_h + e];
   }
-  // merge: gate of the token (one wave), then slot ceil(t/s) <- (reset ? 0 :
-  // open slot) + w x, written to the cache and kept in LDS for the tile.
-  float* qin = reinterpret_cast<float*>(sm.k);  // [H][d_h], scratch in the tile buffer
-  for (int idx = tid; idx < H * d_h; idx += NT)
-    qin[idx] = bf16_bits_to_f32(a.q_c[static_cast<size_t>(b) * H * d_h + idx]);
-  if (a.merge && wave == 0) {
-    const float w = gate_of_token(a.c + static_cast<size_t>(b) * DC,
-                                  a.pe + static_cast<size_t>(pos - 1) * DC, a.w_hyp, DC, lane);
-    if (lane == 0) s_gate = w;
-  }
-  __syncthreads();
-  if (a.merge && tid < W) {
-    const int e = tid;
-    const float x = e < DC ? bf16_bits_to_f32(a.c[static_cast<size_t>(b) * DC + e])
-                           : bf16_bits_to_f32(a.k_r[static_cast<size_t>(b) * DR + e - DC]);
-    float acc = (pos - 1) % a.s == 0 ? 0.f : a.open_acc[static_cast<size_t>(b) * W + e];
-    acc = fmaf(s_gate, x, acc);
-    a.open_acc[static_cast<size_t>(b) * W + e] = acc;
-    const uint16_t u = f32_to_bf16_bits(acc);
-    a.cache[(static_cast<size_t>(b) * a.max_slots + n - 1) * W + e] = u;
-    s_new[e] = u;
+  // W_UV rows of the up-projection, in flight until the end: tpo threads per
+  // output (hl, e), chunks c = p, p + tpo, ...
+  const int nout = HG * d_h;
+  const int o = tid / sh.tpo, p = tid % sh.tpo;
+  const int nv = o < nout ? (KC - p + sh.tpo - 1) / sh.tpo : 0;
+  const uint16_t* wrow = a.w_uv + (static_cast<size_t>(h0) * d_h + (o < nout ? o : 0)) * DC;
+  uint4 wv[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) wv[i] = *reinterpret_cast<const uint4*>(wrow + min(p + i * sh.tpo, KC - 1) * 8);
+  const int te = min(tid, W - 1);  // merge column of this thread (tid < W)
+  uint16_t gxb[GE], mxb = 0;
+  float gw[GE];
+  if constexpr (MERGE) {
+#pragma unroll
+    for (int j = 0; j < GE; ++j) {
+      gxb[j] = a.c[static_cast<size_t>(b) * DC + lane + 64 * j];
+      gw[j] = a.w_hyp[lane + 64 * j];
+    }
+    mxb = te < DC ? a.c[static_cast<size_t>(b) * DC + te] : a.k_r[static_cast<size_t>(b) * DR + te - DC];
   }
 
-  // absorb: thread t owns 8-column chunk kc of head hh for the rows
-  // e = eg, eg + eg_n, ... (one pass over all heads); W_UK chunks are 16-byte
-  // loads, the eg_n partial sums are added in order through LDS.
-  const int eg_n = NT / (KC * H);
-  const int kc = tid % KC, hh = (tid / KC) % H, eg = tid / (KC * H);
-  const int nl = eg < eg_n ? (d_h - eg + eg_n - 1) / eg_n : 0;
-  float* red = qin + H * d_h;  // [H][eg_n][DC]
-  uint4 wk[MAXL];
+  const int n = pos >= 1 ? slot_of(pos, a.s) : 0;
+  const bool ok = pos >= 1 && n <= a.max_slots && (!MERGE || pos <= a.pe_rows);
+  uint16_t* out = a.out + (static_cast<size_t>(b) * H + h0) * d_h;
+  if (!ok) {
+    for (int idx = tid; idx < HG * d_h; idx += NT) out[idx] = 0x7fc0u;  // NaN
+    return;
+  }
+  // Position-dependent loads: pe row, the open slot's state, then the first
+  // PD tiles of cache rows.  Memory rows are the completed slots 0..n-2 when
+  // merging (row n-1 is the new one, taken from LDS; group 0 writes it to
+  // memory meanwhile), else 0..n-1.
+  float gp[GE], macc = 0.f;
+  const bool cont = (pos - 1) % a.s != 0;  // the token continues an open block
+  if constexpr (MERGE) {
 #pragma unroll
-  for (int i = 0; i < MAXL; ++i)
-    if (i < nl)
-      wk[i] = *reinterpret_cast<const uint4*>(a.w_uk + (static_cast<size_t>(hh) * d_h + eg + i * eg_n) * DC + kc * 8);
-  // absorb: q~[h, k] = sum_e q_c[h, e] W_UK[h, e, k], partial sums per row group
+    for (int j = 0; j < GE; ++j) gp[j] = a.pe[static_cast<size_t>(pos - 1) * DC + lane + 64 * j];
+    macc = a.open_acc[(static_cast<size_t>(b) * 2 + (pos - 1) % 2) * W + te];
+  }
+  const uint16_t* rows = a.cache + static_cast<size_t>(b) * a.max_slots * W;
+  const int hm = MERGE ? n - 1 : n;
+  // rope query element of this group's heads (thread tid < HP * DR takes
+  // element tid % DR of local head tid / DR)
+  static_assert(HP * DR <= NT, "one rope query element per thread");
+  const int tq = min(tid, HP * DR - 1);
+  const uint16_t qrb = a.q_r[(static_cast<size_t>(b) * H + h0 + min(tq / DR, HG - 1)) * DR + tq % DR];
+  const auto rs = A::rows_rsrc(rows, hm);
+  uint4 pre[PD * A::CPT];
+  A::template prefetch<PD>(pre, rs, 0);
+
+  // absorb: partial sums of q~[hl, kc*8 .. +8] over this thread's rows
+  float* red = reinterpret_cast<float*>(sm.k);  // [HG][eg_n][DC], scratch in the tile buffer
   if (nl > 0) {
     float acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 #pragma unroll
-    for (int i = 0; i < MAXL; ++i) {
+    for (int i = 0; i < MAXK; ++i) {
       if (i < nl) {
-        const float q = qin[hh * d_h + eg + i * eg_n];
-        const uint32_t wv[4] = {wk[i].x, wk[i].y, wk[i].z, wk[i].w};
+        const float q = bf16_bits_to_f32(qb[i]);
+        const uint32_t w4[4] = {wk[i].x, wk[i].y, wk[i].z, wk[i].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          acc[2 * j] = fmaf(q, __uint_as_float(wv[j] << 16), acc[2 * j]);
-          acc[2 * j + 1] = fmaf(q, __uint_as_float(wv[j] & 0xffff0000u), acc[2 * j + 1]);
+          acc[2 * j] = fmaf(q, __uint_as_float(w4[j] << 16), acc[2 * j]);
+          acc[2 * j + 1] = fmaf(q, __uint_as_float(w4[j] & 0xffff0000u), acc[2 * j + 1]);
         }
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) red[(hh * eg_n + eg) * DC + kc * 8 + j] = acc[j];
+    for (int j = 0; j < 8; ++j) red[(hl * sh.eg_n + eg) * DC + kc * 8 + j] = acc[j];
+  }
+  // every wave computes the gate (same values, same order: the same bits)
+  float gate = 0.f;
+  if constexpr (MERGE) {
+    float gx[GE];
+#pragma unroll
+    for (int j = 0; j < GE; ++j) gx[j] = bf16_bits_to_f32(gxb[j]);
+    gate = gate_from_lane_values<GE>(gx, gp, gw);
   }
   __syncthreads();
+  if constexpr (MERGE) {
+    if (tid < W) {
+      const float v = fmaf(gate, bf16_bits_to_f32(mxb), cont ? macc : 0.f);
+      const uint16_t u = f32_to_bf16_bits(v);
+      if (grp == 0) {
+        a.open_acc[(static_cast<size_t>(b) * 2 + pos % 2) * W + tid] = v;
+        a.cache[(static_cast<size_t>(b) * a.max_slots + n - 1) * W + tid] = u;
+      }
+      s_new[tid] = u;
+    }
+  } else if (tid < W) {
+    s_new[tid] = 0;  // row n of the last tile (past the slots) reads as zero
+  }
   const float qscale = a.scale * kLog2e;
-  for (int idx = tid; idx < H * DC; idx += NT) {
+  for (int idx = tid; idx < HP * DC; idx += NT) {
     const int h = idx / DC, k = idx % DC;
     float v = 0.f;
-    for (int r = 0; r < eg_n; ++r) v += red[(h * eg_n + r) * DC + k];
+    if (h < HG)
+      for (int r = 0; r < sh.eg_n; ++r) v += red[(h * sh.eg_n + r) * DC + k];
     sm.q[h * PITCH + k] = f32_to_bf16_bits(v * qscale);
   }
-  for (int idx = tid; idx < HP * DR; idx += NT) {
-    const int h = idx / DR, e = idx % DR;
-    sm.q[h * PITCH + DC + e] =
-        h < H ? f32_to_bf16_bits(bf16_bits_to_f32(a.q_r[(static_cast<size_t>(b) * H + h) * DR + e]) * qscale)
-              : uint16_t(0);
+  if (tid < HP * DR) {
+    const int h = tid / DR, e = tid % DR;
+    sm.q[h * PITCH + DC + e] = h < HG ? f32_to_bf16_bits(bf16_bits_to_f32(qrb) * qscale) : uint16_t(0);
   }
-  for (int idx = tid; idx < (HP - H) * DC; idx += NT)
-    sm.q[(H + idx / DC) * PITCH + idx % DC] = 0;
-
   __syncthreads();
 
   typename A::State st;
   A::init(st);
-  const uint16_t* rows = a.cache + static_cast<size_t>(b) * a.max_slots * W;
-  const int patch_row = a.merge ? n - 1 : -1;
-  uint4 pre[A::CPT];
-  A::load_tile(pre, rows, 0, n);
-  A::template run<true>(st, sm, rows, 0, n, patch_row, s_new, pre);
+  A::template run<true, PD>(st, sm, rs, 0, n, hm, s_new, pre);
   A::finish(st, sm);
-
-  // Up-projection assignment: tpo threads per output row (h, e), chunks
-  // c = p, p + tpo, ...; its W_UV loads go out before o_lat is staged.
-  const int nout = H * d_h;
-  int tpo = 1;
-  while (tpo < 64 && 2 * tpo * nout <= NT) tpo *= 2;
-  const int o = tid / tpo, p = tid % tpo;
-  const int nv = o < nout ? (KC - p + tpo - 1) / tpo : 0;
-  const uint16_t* wrow = a.w_uv + static_cast<size_t>(o < nout ? o : 0) * DC;
-  uint4 wv[MAXL];
-#pragma unroll
-  for (int i = 0; i < MAXL; ++i)
-    if (i < nv) wv[i] = *reinterpret_cast<const uint4*>(wrow + (p + i * tpo) * 8);
 
   // o_lat (fp32, normalised) into the tile buffer, then the up-projection
   float* olat = reinterpret_cast<float*>(sm.k);  // [HP][DC]
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
+  for (int i = 0; i < 4; ++i) {
+    const int head = 4 * g + i;
+    const float inv = 1.f / sm.red[0][head];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int head = ht * 16 + 4 * g + i;
-      const float inv = 1.f / sm.red[0][head];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        olat[head * DC + wave * CPW + ct * 16 + c16] = st.acc[ht][ct][i] * inv;
-    }
+    for (int ct = 0; ct < CT; ++ct) olat[head * DC + wave * CPW + ct * 16 + c16] = st.acc[0][ct][i] * inv;
   }
   __syncthreads();
   float acc = 0.f;
   if (nv > 0) {
     const float* orow = olat + (o / d_h) * DC;
 #pragma unroll
-    for (int i = 0; i < MAXL; ++i) {
+    for (int i = 0; i < MAXV; ++i) {
       if (i < nv) {
-        const int c = p + i * tpo;
+        const int c = p + i * sh.tpo;
         const uint32_t w4[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -725,7 +795,7 @@ __global__ __launch_bounds__(1024) void decode_step_kernel(StepArgs a) {
       }
     }
   }
-  for (int off = tpo / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  for (int off = sh.tpo / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (p == 0 && o < nout) out[o] = f32_to_bf16_bits(acc);
 }
 
@@ -806,27 +876,60 @@ hipError_t launch_up_project(int R, int H, int d_h, int d_c, const float* o_lat,
                     : up_project_t<uint16_t>(R, H, d_h, d_c, o_lat, w_uv, out, st);
 }
 
-bool decode_step_supported(int H, int d_h, int d_c, int d_r) {
-  const bool shape = (d_c == 256 && d_r == 32) || (d_c == 512 && d_r == 64);
-  const int KC = d_c / 8, NT = 1024;
-  if (!shape || H > 32 || H * KC > NT) return false;  // one absorb pass over all heads
-  const int eg_n = NT / (KC * H);
-  int tpo = 1;
-  while (tpo < 64 && 2 * tpo * H * d_h <= NT) tpo *= 2;
-  // each thread's W_UK and W_UV chunks fit the in-flight register arrays, and
-  // every output row has a thread
-  return (d_h + eg_n - 1) / eg_n <= kStepMaxLoads && (KC + tpo - 1) / tpo <= kStepMaxLoads &&
-         H * d_h <= NT && d_c + d_r <= NT;
+namespace {
+template <int DC, int DR, int TS, int HG, int DH, int NTH, int PD>
+void step_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
+  if (a.merge)
+    decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, true><<<grid, NTH, 0, st>>>(a);
+  else
+    decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, false><<<grid, NTH, 0, st>>>(a);
 }
 
-hipError_t launch_decode_step(const StepArgs& a, hipStream_t st) {
-  if (a.d_c == 256 && a.d_r == 32) {
-    if (a.H <= 16)
-      decode_step_kernel<1, 256, 32, 128><<<a.B, 1024, 0, st>>>(a);
-    else
-      decode_step_kernel<2, 256, 32, 128><<<a.B, 1024, 0, st>>>(a);
-  } else if (a.d_c == 512 && a.d_r == 64 && a.H <= 16) {  // H * d_c / 8 <= 1024 threads
-    decode_step_kernel<1, 512, 64, 64><<<a.B, 1024, 0, st>>>(a);
+// Heads per group the step kernel is instantiated for, per latent shape.
+bool step_hg_instantiated(int d_c, int d_r, int hg, int d_h) {
+  if (d_c == 256 && d_r == 32) return (hg == 1 || hg == 2) && d_h <= 64;
+  if (d_c == 512 && d_r == 64) return hg == 1 && d_h <= 128;
+  return false;
+}
+}  // namespace
+
+bool decode_step_supported(int H, int d_h, int d_c, int d_r) {
+  return d_h >= 1 && step_hg_instantiated(d_c, d_r, 1, d_h) && H >= 1;
+}
+
+int decode_step_groups(int B, int H, int d_h, int d_c) {
+  // Most head groups that still fit the launch in one round of workgroups
+  // (B * groups <= 256: one 512-thread workgroup fills a compute unit's
+  // registers), among the instantiated group sizes; the fewest groups when
+  // even that does not fit.  MTLA_STEP_GROUPS overrides the choice when it
+  // names a valid group count.
+  const int d_r = d_c == 256 ? 32 : 64;
+  auto ok = [&](int g) { return g >= 1 && H % g == 0 && step_hg_instantiated(d_c, d_r, H / g, d_h); };
+  if (const char* env = getenv("MTLA_STEP_GROUPS")) {
+    const int g = atoi(env);
+    if (ok(g)) return g;
+  }
+  int fewest = 0, best = 0;
+  for (int g = 1; g <= H; ++g) {
+    if (!ok(g)) continue;
+    if (fewest == 0) fewest = g;
+    if (static_cast<long long>(B) * g <= 256) best = g;
+  }
+  return best ? best : fewest;
+}
+
+hipError_t launch_decode_step(const StepArgs& a0, hipStream_t st) {
+  StepArgs a = a0;
+  a.groups = decode_step_groups(a.B, a.H, a.d_h, a.d_c);
+  if (a.groups < 1) return hipErrorNotSupported;
+  const int hg = a.H / a.groups;
+  const unsigned grid = 8u * static_cast<unsigned>(a.groups) * static_cast<unsigned>((a.B + 7) / 8);
+  if (a.d_c == 256 && a.d_r == 32 && hg == 1) {
+    step_launch<256, 32, 128, 1, 64, 512, 2>(a, grid, st);
+  } else if (a.d_c == 256 && a.d_r == 32 && hg == 2) {
+    step_launch<256, 32, 128, 2, 64, 512, 2>(a, grid, st);
+  } else if (a.d_c == 512 && a.d_r == 64 && hg == 1) {
+    step_launch<512, 64, 64, 1, 128, 1024, 1>(a, grid, st);
   } else {
     return hipErrorNotSupported;
   }

@@ -15,7 +15,7 @@ struct MergeArgs {
   const float* w_hyp;   // [d_c]
   const float* pe;      // [pe_rows, d_c]
   void* cache;          // [B, max_slots, W]
-  float* open_acc;      // [B, W]
+  float* open_acc;      // [B, 2, W]: state after token t at [b, t % 2]
   float* gate_out;      // [B, T] or nullptr
   void* partials;       // [B, T, W] cumulative in-block merges, or nullptr
 };
@@ -66,6 +66,7 @@ hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st);
 // workgroup per sequence.
 struct StepArgs {
   int B, H, d_h, d_c, d_r, s, max_slots, pe_rows, merge;
+  int groups;             // head groups per sequence (set by launch_decode_step)
   float scale;
   const int32_t* pos;     // [B]
   const uint16_t* c;      // [B, d_c]  token to merge (merge only)
@@ -77,10 +78,12 @@ struct StepArgs {
   const uint16_t* w_uk;   // [H, d_h, d_c]
   const uint16_t* w_uv;   // [H, d_h, d_c]
   uint16_t* cache;        // [B, max_slots, W]
-  float* open_acc;        // [B, W]
+  float* open_acc;        // [B, 2, W]: state after token t at [b, t % 2]
   uint16_t* out;          // [B, H, d_h]
 };
 bool decode_step_supported(int H, int d_h, int d_c, int d_r);
+// Head groups per sequence the step kernel uses for a batch of B sequences.
+int decode_step_groups(int B, int H, int d_h, int d_c);
 hipError_t launch_decode_step(const StepArgs& a, hipStream_t st);
 
 // out[r, h, :] = W_UV[h] o_lat[r, h].

@@ -6,7 +6,8 @@
 // gates of the run's tokens are computed first (a wave takes four tokens at a
 // time, a d_c dot product each), then every (block, 8-column chunk) pair is
 // independent: a thread walks its block's tokens in order, carrying the fp32
-// block sum.  Every stored value is rounded once from that fp32 sum.
+// block sum.  Every stored value is rounded once from that fp32 sum.  The fp32
+// state of the open slot after token t lives at open_acc[b, t % 2].
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a, int b
     const int t1 = min(ts + s - 1, r.t_last);
     float acc[8];
     if (t0 > ts) {  // a block that began before this call continues the open slot
-      const float* oa = a.open_acc + static_cast<size_t>(b) * W + e;
+      const float* oa = a.open_acc + (static_cast<size_t>(b) * 2 + (r.p0 - 1) % 2) * W + e;
       const float4 lo = *reinterpret_cast<const float4*>(oa);
       const float4 hi = *reinterpret_cast<const float4*>(oa + 4);
       acc[0] = lo.x; acc[1] = lo.y; acc[2] = lo.z; acc[3] = lo.w;
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a, int b
       if (P) store8(P + (static_cast<size_t>(b) * a.T + (t - r.p0)) * W + e, acc);
     }
     store8(cache + (static_cast<size_t>(b) * a.max_slots + blk) * W + e, acc);
-    if (write_open && blk == r.bk1) store8(a.open_acc + static_cast<size_t>(b) * W + e, acc);
+    if (write_open && blk == r.bk1) store8(a.open_acc + (static_cast<size_t>(b) * 2 + r.t_last % 2) * W + e, acc);
   }
 }
 
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_tail_kernel(MergeArgs a) 
   const int e = ch * 8;
   float acc[8];
   if (t0 > ts) {
-    const float* oa = a.open_acc + static_cast<size_t>(b) * W + e;
+    const float* oa = a.open_acc + (static_cast<size_t>(b) * 2 + (r.p0 - 1) % 2) * W + e;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = oa[j];
   } else {
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_tail_kernel(MergeArgs a) 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, x[j], acc[j]);
   }
-  store8(a.open_acc + static_cast<size_t>(b) * W + e, acc);
+  store8(a.open_acc + (static_cast<size_t>(b) * 2 + r.t_last % 2) * W + e, acc);
 }
 
 __global__ void pe_kernel(int rows, int d, float* pe) {

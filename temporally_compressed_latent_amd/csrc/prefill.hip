@@ -41,34 +41,43 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;
-  const int col0 = blockIdx.x * GBN;
-  const int row0 = blockIdx.y * GBM;
+  // Tile order: workgroups are dealt to the 8 XCDs round-robin by linear id
+  // (id L runs on XCD L % 8).  Tiles are numbered row-major (the column tiles
+  // of a row tile consecutive) and XCD x takes the x-th eighth of them, so
+  // the column tiles that share an A row tile run on one XCD and read it from
+  // one L2.  (When the tile count is not a multiple of 8, linear order.)
+  const int ncol = gridDim.x, ntiles = gridDim.x * gridDim.y;
+  const int L = blockIdx.x + gridDim.x * blockIdx.y;
+  const int t = ntiles % 8 == 0 ? (L % 8) * (ntiles / 8) + L / 8 : L;
+  const int col0 = (t % ncol) * GBN;
+  const int row0 = (t / ncol) * GBM;
   const int HD = H * d_h;
 
-  // Each thread copies 2 chunks of A and 2 of B per K step (16 B each).
-  uint4 ra[2], rb[2];
+  // Each thread copies 2 chunks of A and 2 of B per K step (16 B each).  A
+  // goes through a buffer resource over its M rows (rows past M read as
+  // zero); the B tile lies wholly in W_UK or in W_UV (HD is a multiple of
+  // GBN), so its base is uniform.
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A), static_cast<short>(0), M * W * 2, kBufferRsrcWord3);
+  const uint16_t* bmat = col0 < HD ? w_uk + static_cast<size_t>(col0) * d_c
+                                   : w_uv + static_cast<size_t>(col0 - HD) * d_c;
+  // Named registers (not arrays), so they are never placed in scratch.
+  uint4 ra0, ra1, rb0, rb1;
+  const int r0 = tid >> 2, r1 = (tid + 256) >> 2, ch = tid & 3;  // chunk (r, ch), two per thread
   auto gload = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int id = tid + 256 * j;
-      const int r = id >> 2, ch = id & 3;
-      const int m = row0 + r;
-      ra[j] = m < M ? *reinterpret_cast<const uint4*>(A + static_cast<size_t>(m) * W + k0 + ch * 8)
-                    : uint4{0u, 0u, 0u, 0u};
-      const int col = col0 + r;
-      const uint16_t* bsrc = col < HD ? w_uk + static_cast<size_t>(col) * d_c
-                                      : w_uv + static_cast<size_t>(col - HD) * d_c;
-      rb[j] = *reinterpret_cast<const uint4*>(bsrc + k0 + ch * 8);
-    }
+    const int so = (row0 * W + k0) * 2;
+    const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rs_a, (r0 * W + ch * 8) * 2, so, 0);
+    const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rs_a, (r1 * W + ch * 8) * 2, so, 0);
+    ra0 = uint4{v0[0], v0[1], v0[2], v0[3]};
+    ra1 = uint4{v1[0], v1[1], v1[2], v1[3]};
+    rb0 = *reinterpret_cast<const uint4*>(bmat + static_cast<size_t>(r0) * d_c + k0 + ch * 8);
+    rb1 = *reinterpret_cast<const uint4*>(bmat + static_cast<size_t>(r1) * d_c + k0 + ch * 8);
   };
   auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int id = tid + 256 * j;
-      const int r = id >> 2, ch = id & 3;
-      *reinterpret_cast<uint4*>(&sA[buf][r * GP + ch * 8]) = ra[j];
-      *reinterpret_cast<uint4*>(&sB[buf][r * GP + ch * 8]) = rb[j];
-    }
+    *reinterpret_cast<uint4*>(&sA[buf][r0 * GP + ch * 8]) = ra0;
+    *reinterpret_cast<uint4*>(&sA[buf][r1 * GP + ch * 8]) = ra1;
+    *reinterpret_cast<uint4*>(&sB[buf][r0 * GP + ch * 8]) = rb0;
+    *reinterpret_cast<uint4*>(&sB[buf][r1 * GP + ch * 8]) = rb1;
   };
 
   f32x4 acc[4][4];

@@ -42,8 +42,13 @@ class Case:
         self.pe = torch.empty(pe_rows, dims.d_c, dtype=torch.float32, device=DEV)
         m.mtla_sinusoidal_pe(self.pe)
         self.cache = torch.zeros(B, dims.max_slots, W, dtype=st, device=DEV)
-        self.open_acc = torch.zeros(B, W, dtype=torch.float32, device=DEV)
+        # open-slot state: the fp32 value after token t is kept at [b, t % 2]
+        self.open_acc = torch.zeros(B, 2, W, dtype=torch.float32, device=DEV)
         self.ws_dec = torch.empty(m.mtla_decode_workspace_bytes(dims), dtype=torch.uint8, device=DEV)
+
+    def open_state(self, t: int) -> torch.Tensor:
+        """fp32 state of the open slot after token t, [B, W]."""
+        return self.open_acc[:, t % 2]
 
     def append(self, pos0: torch.Tensor, t_lo: int, t_hi: int, gate_out=None):
         """merge_append tokens t_lo..t_hi-1 (array rows) at device positions pos0."""

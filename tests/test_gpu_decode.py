@@ -154,7 +154,7 @@ def test_positions_need_only_element_alignment():
 
 @pytest.mark.parametrize("shape,portable,s,B,N,max_slots", [
     ("st", False, 2, 4, 130, None),       # fused single-kernel step
-    ("mid", False, 3, 3, 100, None),      # fused, 32-row MFMA instance
+    ("mid", False, 3, 3, 100, None),      # fused, 20 heads in groups of 2
     ("st", False, 4, 2, 90, 700),         # several splits: merge kernel + staged decode
     ("st", True, 2, 2, 60, None),         # portable kernels
 ])
@@ -172,6 +172,27 @@ def test_decode_step_equals_merge_then_decode(shape, portable, s, B, N, max_slot
     for b in range(B):
         want, _ = oracle_ref.incremental(inp, b, N, s, a.d.softmax_scale)
         assert oracle.max_rel_err(out[b], want) <= 1e-2, b
+
+
+@pytest.mark.parametrize("groups", [4, 8])
+def test_decode_step_head_groups(groups, monkeypatch):
+    """The fused step with the heads of a sequence split over 4 or 8
+    workgroups: outputs follow the oracle, and the merged cache and open-slot
+    state are the same bits whatever the split (the merge arithmetic does not
+    depend on it)."""
+    B, N, s = 5, 70, 3
+    outs, caches, states = [], [], []
+    for g_ in (groups, 8 if groups == 4 else 4):
+        monkeypatch.setenv("MTLA_STEP_GROUPS", str(g_))
+        inp, g = make_case("st", 16, B, N, s, "bf16")
+        outs.append(host(g.step_loop(N)))
+        caches.append(bits(g.cache))
+        states.append(g.open_acc.clone())
+    assert torch.equal(caches[0], caches[1])
+    assert torch.equal(states[0], states[1])
+    for b in range(B):
+        want, _ = oracle_ref.incremental(inp, b, N, s, g.d.softmax_scale)
+        assert oracle.max_rel_err(outs[0][b], want) <= 1e-2, b
 
 
 def test_decode_step_invalid_positions():

@@ -37,7 +37,7 @@ def test_merge_matches_oracle(dtype, s):
         assert oracle.max_rel_err(cache[b, :n], want) <= tol(dtype)
         assert np.max(np.abs(host(gates)[b] - w)) <= 2e-6
         # fp32 open-slot state holds the unrounded value of the last slot
-        assert oracle.max_rel_err(host(g.open_acc)[b], want[n - 1]) <= 1e-5
+        assert oracle.max_rel_err(host(g.open_state(N))[b], want[n - 1]) <= 1e-5
         assert np.all(cache[b, n:] == 0)  # rows past the last slot untouched
 
 
@@ -93,7 +93,7 @@ def test_chunked_append_equals_tokenwise_bit_exact(dtype, s):
     assert t == N + 1
     assert torch.equal(a.cache.view(torch.int16 if dtype == "bf16" else torch.int32),
                        b_.cache.view(torch.int16 if dtype == "bf16" else torch.int32))
-    assert torch.equal(a.open_acc, b_.open_acc)
+    assert torch.equal(a.open_state(N), b_.open_state(N))
 
 
 def test_ragged_positions_and_invalid_sequences():

@@ -29,7 +29,7 @@ CASES = [
 def test_prefill_matches_oracle(shape, dtype, portable, s, B, N):
     inp, g = make_case(shape, 7, B, N, s, dtype, portable)
     out = host(g.prefill(N))
-    cache, acc = host(g.cache), host(g.open_acc)
+    cache, acc = host(g.cache), host(g.open_state(N))
     for b in range(B):
         want, P = oracle_ref.parallel(inp, b, N, s, g.d.softmax_scale)
         assert oracle.max_rel_err(out[b], want) <= tol(dtype), b
@@ -49,7 +49,7 @@ def test_prefill_equals_device_decode_loop(shape, s, N, portable):
     pre = host(a.prefill(N))
     loop = host(b_.decode_loop(N))
     assert torch.equal(bits(a.cache), bits(b_.cache))
-    assert torch.equal(a.open_acc, b_.open_acc)
+    assert torch.equal(a.open_state(N), b_.open_state(N))
     assert oracle.max_rel_err(pre, loop) <= 1e-2
 
 
