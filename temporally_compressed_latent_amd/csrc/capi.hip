@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/mtla.h"
@@ -117,8 +118,18 @@ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 // kernel gives each split ~128 slots.
 int decode_splits(const mtla_dims* d) {
   if (decode_fast(d)) {
-    const int want = ceil_div(512, d->batch > 0 ? d->batch : 1);
-    return clampi(want, 1, clampi(ceil_div(d->max_slots, 512), 1, 64));
+    const int cap = clampi(ceil_div(d->max_slots, 512), 1, 64);
+    // MTLA_DECODE_SPLITS (1..64) overrides the default; it must be the same
+    // when the workspace is sized and when decode runs.
+    if (const char* env = getenv("MTLA_DECODE_SPLITS")) {
+      const int k = atoi(env);
+      if (k >= 1) return clampi(k, 1, cap);
+    }
+    // one workgroup per compute unit: the split kernel's registers allow one
+    // 256-thread workgroup per CU, so a second round of workgroups would run
+    // on a quarter-full chip
+    const int want = ceil_div(256, d->batch > 0 ? d->batch : 1);
+    return clampi(want, 1, cap);
   }
   return clampi(ceil_div(d->max_slots, 128), 1, 32);
 }

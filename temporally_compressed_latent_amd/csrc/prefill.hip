@@ -180,18 +180,17 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   constexpr int QT = 4 * QW;         // queries per workgroup
   constexpr int KP = DQK + 8;        // key tile pitch (elements)
   constexpr int VP = DH + 8;         // value tile pitch
-  constexpr int KCH = DQK / 8, VCH = DH / 8;
-  constexpr int NCH = TS * (KCH + VCH);    // 16-byte chunks per tile
-  constexpr int CPT = (NCH + 255) / 256;
   static_assert(DH % 32 == 0 && DR % 16 == 0, "shape");
   constexpr float kLazyLog2 = 8.f;
 
   __shared__ __align__(16) uint16_t sK[TS * KP];
   __shared__ __align__(16) uint16_t sV[TS * VP];
 
-  const int nqt = gridDim.x;
-  const int qt = nqt - 1 - static_cast<int>(blockIdx.x);  // heavy tiles first
-  const int h = blockIdx.y, b = blockIdx.z;
+  // Grid (H, B, query tiles): dispatch runs x fastest, so every (head,
+  // sequence) takes its heaviest query tile before any lighter one.
+  const int nqt = gridDim.z;
+  const int qt = nqt - 1 - static_cast<int>(blockIdx.z);
+  const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 5, c32 = lane & 31;
   const int N = a.N, H = a.H, s = a.s;
@@ -263,48 +262,62 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   const int nk_w = qw0 < N ? (min(qw0 + QW, N) - 1) / s : 0;
   const int full_w = qw0 / s;
 
-  // Branch-free tile loads (all in flight together): every chunk reads row
-  // min(slot, nk - 1) (nk >= 1 whenever this runs); rows past nk are zeroed
-  // when the tile is stored, so no value is consumed before then.
-  uint4 pre[CPT];
-  auto load_tile = [&](int j0) {
+  // Tile loads through buffer resources bounded at the last completed slot's
+  // token (s*nk tokens): slot rows past nk read as zero and touch no memory.
+  // Each load instruction uses one resource, so the chunks are split by kind:
+  // per thread KN chunks of K^C, RN of the rope key and KN of V (16 bytes
+  // each); their offsets within a tile are loop invariant and the tile offset
+  // is a scalar.  Slot j is token s*j + s - 1.
+  constexpr int KN = TS * DH / 8 / 256, RN = TS * DR / 8 / 256;
+  static_assert(KN * 256 == TS * DH / 8 && RN * 256 == TS * DR / 8, "chunks per thread");
+  const int tok_end = s * nk;
+  const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kc), static_cast<short>(0), tok_end * DH * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vv), static_cast<short>(0), tok_end * DH * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Pb + a.d_c), static_cast<short>(0),
+      tok_end > 0 ? (tok_end - 1) * W * 2 + DR * 2 : 0, kBufferRsrcWord3);
+  int off_k[KN], off_r[RN], lds_k[KN], lds_r[RN], lds_v[KN];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int id = tid + 256 * k;
-      if (NCH % 256 == 0 || id < NCH) {
-        const bool is_k = id < TS * KCH;
-        const int id2 = is_k ? id : id - TS * KCH;
-        const int row = is_k ? id2 / KCH : id2 / VCH;
-        const int ch = is_k ? id2 % KCH : id2 % VCH;
-        const int slot = j0 + row;
-        const int tk = s * min(slot, nk - 1) + s - 1;  // token holding the completed slot
-        const uint16_t* src;
-        if (!is_k)
-          src = vv + static_cast<size_t>(tk) * DH + ch * 8;
-        else if (ch < DH / 8)
-          src = kc + static_cast<size_t>(tk) * DH + ch * 8;
-        else
-          src = Pb + static_cast<size_t>(tk) * W + a.d_c + (ch - DH / 8) * 8;
-        pre[k] = *reinterpret_cast<const uint4*>(src);
-      }
+  for (int i = 0; i < KN; ++i) {
+    const int c = tid + 256 * i, row = c / (DH / 8), cc = c % (DH / 8);
+    off_k[i] = ((s * row + s - 1) * DH + cc * 8) * 2;
+    lds_k[i] = row * KP + cc * 8;
+    lds_v[i] = row * VP + cc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < RN; ++i) {
+    const int c = tid + 256 * i, row = c / (DR / 8), cc = c % (DR / 8);
+    off_r[i] = ((s * row + s - 1) * W + cc * 8) * 2;
+    lds_r[i] = row * KP + DH + cc * 8;
+  }
+  uint4 pk[KN], pr[RN], pv[KN];
+  auto load_tile = [&](int j0) {
+    const int so_kv = s * j0 * DH * 2, so_r = s * j0 * W * 2;
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_k, off_k[i], so_kv, 0);
+      pk[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < RN; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_r, off_r[i], so_r, 0);
+      pr[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_v, off_k[i], so_kv, 0);
+      pv[i] = uint4{v[0], v[1], v[2], v[3]};
     }
   };
-  auto store_tile = [&](int j0) {
+  auto store_tile = [&](int) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int id = tid + 256 * k;
-      if (NCH % 256 == 0 || id < NCH) {
-        const bool is_k = id < TS * KCH;
-        const int id2 = is_k ? id : id - TS * KCH;
-        const int row = is_k ? id2 / KCH : id2 / VCH;
-        const int ch = is_k ? id2 % KCH : id2 % VCH;
-        const bool in = j0 + row < nk;
-        const uint4 v = pre[k];
-        const uint4 z = uint4{in ? v.x : 0u, in ? v.y : 0u, in ? v.z : 0u, in ? v.w : 0u};
-        uint16_t* dst = is_k ? sK + row * KP + ch * 8 : sV + row * VP + ch * 8;
-        *reinterpret_cast<uint4*>(dst) = z;
-      }
-    }
+    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sK + lds_k[i]) = pk[i];
+#pragma unroll
+    for (int i = 0; i < RN; ++i) *reinterpret_cast<uint4*>(sK + lds_r[i]) = pr[i];
+#pragma unroll
+    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sV + lds_v[i]) = pv[i];
   };
 
   if (nk > 0) load_tile(0);
@@ -465,9 +478,9 @@ hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t st) {
   if (a.d_h == 64 && a.d_r == 32) {
     constexpr int nq = kPrefillQueryTiles;
-    prefill_attn_kernel<64, 32, nq><<<dim3((a.N + 128 * nq - 1) / (128 * nq), a.H, a.B), 256, 0, st>>>(a);
+    prefill_attn_kernel<64, 32, nq><<<dim3(a.H, a.B, (a.N + 128 * nq - 1) / (128 * nq)), 256, 0, st>>>(a);
   } else if (a.d_h == 128 && a.d_r == 64) {
-    prefill_attn_kernel<128, 64, 1><<<dim3((a.N + 127) / 128, a.H, a.B), 256, 0, st>>>(a);
+    prefill_attn_kernel<128, 64, 1><<<dim3(a.H, a.B, (a.N + 127) / 128), 256, 0, st>>>(a);
   } else {
     return hipErrorNotSupported;
   }
