@@ -183,8 +183,9 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   static_assert(DH % 32 == 0 && DR % 16 == 0, "shape");
   constexpr float kLazyLog2 = 8.f;
 
-  __shared__ __align__(16) uint16_t sK[TS * KP];
-  __shared__ __align__(16) uint16_t sV[TS * VP];
+  // two K/V tile buffers: the next tile is stored while this one is used
+  __shared__ __align__(16) uint16_t sKb[2][TS * KP];
+  __shared__ __align__(16) uint16_t sVb[2][TS * VP];
 
   // Grid (H, B, query tiles): dispatch runs x fastest, so every (head,
   // sequence) takes its heaviest query tile before any lighter one.
@@ -311,20 +312,33 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
       pv[i] = uint4{v[0], v[1], v[2], v[3]};
     }
   };
-  auto store_tile = [&](int) {
+  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sK + lds_k[i]) = pk[i];
+    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sKb[buf] + lds_k[i]) = pk[i];
 #pragma unroll
-    for (int i = 0; i < RN; ++i) *reinterpret_cast<uint4*>(sK + lds_r[i]) = pr[i];
+    for (int i = 0; i < RN; ++i) *reinterpret_cast<uint4*>(sKb[buf] + lds_r[i]) = pr[i];
 #pragma unroll
-    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sV + lds_v[i]) = pv[i];
+    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sVb[buf] + lds_v[i]) = pv[i];
   };
 
-  if (nk > 0) load_tile(0);
-  for (int j0 = 0; j0 < nk; j0 += TS) {
-    store_tile(j0);
-    __syncthreads();
-    if (j0 + TS < nk) load_tile(j0 + TS);
+  // Tile j0 sits in buffer `buf` at the top of each iteration and the loads
+  // of tile j0+TS are in flight; the iteration stores tile j0+TS into the
+  // other buffer, issues the loads of j0+2TS, uses tile j0, and ends with the
+  // tile loop's only barrier.
+  int buf = 0;
+  if (nk > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (TS < nk) load_tile(TS);
+  }
+  __syncthreads();
+  for (int j0 = 0; j0 < nk; j0 += TS, buf ^= 1) {
+    if (j0 + TS < nk) {
+      store_tile(buf ^ 1);
+      if (j0 + 2 * TS < nk) load_tile(j0 + 2 * TS);
+    }
+    const uint16_t* sK = sKb[buf];
+    const uint16_t* sV = sVb[buf];
 
     if (j0 < nk_w) {
       // S^T = K Q^T - m: sc[rt][t][i] = score(slot j0 + 32rt + 8(i/4) + 4grp + i%4,
@@ -361,13 +375,17 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
             }
           }
         }
-        float mx = sc[0][t][0];
+        // this lane's maximum over its 32 scores (four independent chains);
+        // the other half of the query's slots sits in lane ^ 32, which only
+        // the rare rescale below needs
+        float m4[4];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int u = 0; u < 4; ++u) m4[u] = fmaxf(sc[0][t][u], sc[1][t][u]);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[rt][t][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int i = 4; i < 16; ++i) m4[i % 4] = fmaxf(m4[i % 4], fmaxf(sc[0][t][i], sc[1][t][i]));
+        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
         if (__any(mx > kLazyLog2)) {
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
           const float d = fmaxf(mx, 0.f);
           const float alpha = fast_exp2(-d);
           m[t] += d;
@@ -379,17 +397,17 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) sc[rt][t][i] -= d;
         }
-        float ls = 0.f;
+        float l4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float pv = fast_exp2(sc[rt][t][i]);
             sc[rt][t][i] = pv;
-            ls += pv;
+            l4[i % 4] += pv;
           }
         }
-        lp[t] += ls;
+        lp[t] += (l4[0] + l4[1]) + (l4[2] + l4[3]);
       }
 
       // O^T += V^T P^T over the tile's four 16-slot chunks
