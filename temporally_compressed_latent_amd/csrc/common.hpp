@@ -120,6 +120,41 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// vector-memory loads still in flight (__syncthreads' fence waits for those
+// too, which would drain a ring of tiles being loaded straight into LDS).
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 16-byte load from a raw buffer straight into LDS: lane i's 16 bytes, at
+// byte voff (+ soff) of the buffer `rsrc`, go to LDS byte lds_base + 16 * i
+// (lds_base wave-uniform).  Offsets past the buffer's num_records read zero.
+// Issued in inline asm so that the compiler does not insert its own waits for
+// it before every later LDS read (it cannot tell the LDS range apart): the
+// caller waits for these loads itself, by count, with wait_vmcnt() before the
+// barrier that publishes the data.  The asm has no output register; its
+// operands are read when it issues.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void buffer_load_lds16(i32x4_t rsrc, uint32_t lds_base, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+// Raw buffer resource words for a wave-uniform base address and size.
+__device__ __forceinline__ i32x4_t make_rsrc_words(const void* base, int nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane(nbytes);
+  r.w = 0x00020000;
+  return r;
+}
+// LDS byte address of a pointer into shared memory, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p))));
+}
+
 // Word 3 of a raw buffer resource on gfx9-family parts (CDNA): 32-bit data
 // format, no swizzle, offsets checked against num_records.
 constexpr int kBufferRsrcWord3 = 0x00020000;

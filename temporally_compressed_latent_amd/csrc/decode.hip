@@ -13,6 +13,7 @@
 // heads of a sequence in one workgroup (heads are the MFMA M dimension) and
 // reads each cache row from HBM once.
 #include <cstdlib>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -582,6 +583,274 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Split-K latent attention for long caches of the 576-wide row (d_c = 512,
+// d_R = 64).  One workgroup of 8 waves per (split, sequence), all heads
+// (HT*16 MFMA rows), 64-slot tiles.
+//
+// The cache streams HBM -> LDS through buffer loads that write LDS directly
+// (no staging registers), double buffered: the loads of tile it+2 go out as
+// soon as every wave is done with tile it, so one tile (74 KB) is always in
+// flight.  The loads are waited for by count (the compiler does not track
+// them, see buffer_load_lds16); barriers inside the tile loop wait only for
+// LDS operations.
+//
+// LDS tile layout: 16-byte chunk c of row r sits at chunk slot
+// r * 72 + (c ^ ((r >> 1) & 7)).  The XOR (within 8-chunk groups, so a row
+// stays within its 72 slots) spreads the 16 rows an MFMA operand read touches
+// over all LDS banks; load instruction i of wave w fills slots
+// (9w + i) * 64 + lane, so each lane fetches the chunk that belongs there.
+//
+// Per tile: eight score items (head tile, 16-slot group), one per wave, with
+// the wave's scaled query rows held in registers; the tile max per head is
+// shared through LDS, probabilities go to LDS as bf16, then each wave
+// accumulates its 64 latent columns for all heads.  Scores are in log2 units
+// (queries pre-scaled by tau * log2 e).
+// ---------------------------------------------------------------------------
+template <int HT>
+__global__ __launch_bounds__(512) void decode_stream_kernel(AttendArgs a) {
+  constexpr int DC = 512, DR = 64, W = DC + DR, NW = 8;
+  constexpr int TS = 64;
+  constexpr int CPR = W / 8;                // chunks per row
+  constexpr int TCH = TS * CPR;             // chunks per tile
+  constexpr int LPW = TCH / (64 * NW);      // load instructions per wave per tile
+  static_assert(LPW * 64 * NW == TCH && CPR % 8 == 0 && LPW == 9, "tile shape");
+  constexpr int HP = HT * 16, PP = TS + 8;
+  constexpr int KS = W / 32;                // score k-steps
+  constexpr int NSG = TS / 16;              // 16-slot groups per tile
+  constexpr int ITEMS = HT * NSG;           // score items per tile
+  static_assert(ITEMS <= NW, "one score item per wave");
+  constexpr int CPW = DC / NW, CT = CPW / 16;
+  __shared__ __align__(16) uint16_t sp[HP * PP];
+  __shared__ float red[NSG][HP];
+  // the two tile buffers are separate objects, each named statically (the
+  // tile loop is unrolled by two)
+  __shared__ __align__(16) uint16_t kb0[TCH * 8];
+  __shared__ __align__(16) uint16_t kb1[TCH * 8];
+
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int nsplit = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int H = a.H;
+
+  int n = 0;
+  {
+    const int pos = a.pos[b];
+    if (pos >= 1) {
+      n = slot_of(pos, a.s);
+      if (n > a.max_slots) n = 0;
+    }
+  }
+  const int lo = static_cast<int>((static_cast<long long>(split) * n) / nsplit);
+  const int hi = static_cast<int>((static_cast<long long>(split + 1) * n) / nsplit);
+
+  // rows of this sequence up to hi; past them the loads read zero
+  const uint16_t* rows = static_cast<const uint16_t*>(a.cache) + static_cast<size_t>(b) * a.max_slots * W;
+  const i32x4_t rs = make_rsrc_words(rows, hi * W * 2);
+  auto swz = [](int r) { return (r >> 1) & 7; };
+  int voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int slot = (wave * LPW + i) * 64 + lane;
+    const int r = slot / CPR, c = (slot % CPR) ^ swz(r);
+    voff[i] = (r * W + c * 8) * 2;
+  }
+  auto issue_tile = [&](int j0, uint16_t* dst) {
+    const uint32_t base = lds_addr(dst + wave * LPW * 64 * 8);
+    const int so = __builtin_amdgcn_readfirstlane(j0 * (W * 2));
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) buffer_load_lds16(rs, base + i * 64 * 16, voff[i], so);
+  };
+
+  if (lo < hi) issue_tile(lo, kb0);
+  if (lo + TS < hi) issue_tile(lo + TS, kb1);
+
+  // this wave's score item and its query rows (A operand, bf16, scaled)
+  const int item_ht = wave % HT, item_sg = wave / HT;
+  const bool scorer = wave < ITEMS;
+  const float qscale = a.scale * kLog2e;
+  bf16x8 qa[KS];
+  {
+    const int head = item_ht * 16 + c16;
+    const float* qrow = a.qbuf + (static_cast<size_t>(b) * H + (head < H ? head : 0)) * W;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float v[8];
+      load8(qrow + ks * 32 + 8 * g, v);
+      u16x8 u;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) u[r] = head < H ? f32_to_bf16_bits(v[r] * qscale) : uint16_t(0);
+      qa[ks] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  float m[HT][4], l[4];
+  f32x4 acc[HT][CT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[ht][i] = -INFINITY;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ht][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l[i] = 0.f;
+
+  // one tile: `kt` holds slots j0 .. j0+TS-1; afterwards it receives slots
+  // j0+2TS .. (loads issued once every wave is done with it)
+  auto tile = [&](int j0, uint16_t* kt) {
+    // at most one later tile (j0+TS) of this wave's loads may still be in flight
+    if (j0 + TS < hi)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // this tile visible to every wave
+
+    // scores of item (item_ht, item_sg): sc[i] = head item_ht*16 + 4g + i
+    // against slot j0 + 16*item_sg + c16
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (scorer) {
+      const int r = 16 * item_sg + c16;
+      const uint16_t* krow = kt + r * CPR * 8;
+      const int sr = swz(r);
+      f32x4 s2 = f32x4{0.f, 0.f, 0.f, 0.f};  // two accumulation chains
+#pragma unroll
+      for (int ks = 0; ks < KS; ks += 2) {
+        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(krow + ((4 * ks + g) ^ sr) * 8);
+        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(krow + ((4 * (ks + 1) + g) ^ sr) * 8);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], b0, sc, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks + 1], b1, s2, 0, 0, 0);
+      }
+      const bool valid = j0 + 16 * item_sg + c16 < hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = valid ? sc[i] + s2[i] : -INFINITY;
+        sc[i] = v;
+        const float mx = row16_max(v);
+        if (c16 == 0) red[item_sg][item_ht * 16 + 4 * g + i] = mx;
+      }
+    }
+    lds_barrier();
+    // new running max per head (the same values in every wave), rescale
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int head = ht * 16 + 4 * g + i;
+        float mt = red[0][head];
+#pragma unroll
+        for (int sg = 1; sg < NSG; ++sg) mt = fmaxf(mt, red[sg][head]);
+        const float mn = fmaxf(m[ht][i], mt);
+        const float alpha = fast_exp2(m[ht][i] - mn);
+        m[ht][i] = mn;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ht][ct][i] *= alpha;
+        if (scorer && ht == item_ht) {
+          const float pv = fast_exp2(sc[i] - mn);
+          l[i] = l[i] * alpha + pv;
+          sp[head * PP + 16 * item_sg + c16] = f32_to_bf16_bits(pv);
+        }
+      }
+    }
+    lds_barrier();
+    // acc[head, col] += sum_slot P[head, slot] row[slot, col]; the B operand
+    // (8 slots of one column) comes from two transposing reads
+#pragma unroll
+    for (int ks2 = 0; ks2 < TS / 32; ++ks2) {
+      bf16x8 ap[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        ap[ht] = *reinterpret_cast<const bf16x8*>(sp + (ht * 16 + c16) * PP + ks2 * 32 + 8 * g);
+      const int r0 = ks2 * 32 + 8 * g + (c16 >> 2), r1 = r0 + 4;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int col = wave * CPW + ct * 16 + 4 * (c16 & 3);
+        const int ch = col >> 3, wi = col & 7;
+        const s16x4 lo4 = lds_read_tr16(kt + (r0 * CPR + (ch ^ swz(r0))) * 8 + wi);
+        const s16x4 hi4 = lds_read_tr16(kt + (r1 * CPR + (ch ^ swz(r1))) * 8 + wi);
+        const bf16x8 bb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          acc[ht][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[ht], bb, acc[ht][ct], 0, 0, 0);
+      }
+    }
+    lds_barrier();  // every wave is done with kt (and with sp, red)
+    if (j0 + 2 * TS < hi) issue_tile(j0 + 2 * TS, kt);
+  };
+  for (int j0 = lo; j0 < hi; j0 += 2 * TS) {
+    tile(j0, kb0);
+    if (j0 + TS < hi) tile(j0 + TS, kb1);
+  }
+
+  // softmax denominators: sum over the slot lanes, then over the slot groups
+  // in order
+  if (scorer) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = row16_sum(l[i]);
+      if (c16 == 0) red[item_sg][item_ht * 16 + 4 * g + i] = v;
+    }
+  }
+  __syncthreads();
+  float L[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int head = ht * 16 + 4 * g + i;
+      float v = 0.f;
+#pragma unroll
+      for (int sg = 0; sg < NSG; ++sg) v += red[sg][head];
+      L[ht][i] = v;
+    }
+  }
+
+  if (nsplit == 1) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int head = ht * 16 + 4 * g + i;
+        if (head < H) {
+          const float inv = 1.f / L[ht][i];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            a.o_lat[(static_cast<size_t>(b) * H + head) * DC + wave * CPW + ct * 16 + c16] = acc[ht][ct][i] * inv;
+        }
+      }
+    }
+    return;
+  }
+  const size_t pbase = (static_cast<size_t>(b) * nsplit + split) * H;
+  if (wave == 0 && c16 == 0) {
+    // the running max is in log2 units; partials use natural-log units
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int head = ht * 16 + 4 * g + i;
+        if (head < H) {
+          a.part.m[pbase + head] = m[ht][i] * kLn2;
+          a.part.l[pbase + head] = L[ht][i];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int head = ht * 16 + 4 * g + i;
+      if (head < H) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          a.part.acc[(pbase + head) * DC + wave * CPW + ct * 16 + c16] = acc[ht][ct][i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Fused decode step for short caches.  One workgroup of 16 waves per
 // (sequence, group of HG heads) does everything for one token:
 //   merge            : gate w_t and slot ceil(t/s) <- reset ? w x : acc + w x,
@@ -951,9 +1220,9 @@ hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st) {
       decode_mfma_kernel<2, 256, 32><<<grid, 256, 0, st>>>(a);
   } else if (a.d_c == 512 && a.d_r == 64) {
     if (a.H <= 16)
-      decode_mfma_kernel<1, 512, 64><<<grid, 256, 0, st>>>(a);
+      decode_stream_kernel<1><<<grid, 512, 0, st>>>(a);
     else
-      decode_mfma_kernel<2, 512, 64><<<grid, 256, 0, st>>>(a);
+      decode_stream_kernel<2><<<grid, 512, 0, st>>>(a);
   } else {
     return hipErrorNotSupported;
   }
