@@ -56,14 +56,24 @@ __global__ __launch_bounds__(256) void absorb_kernel(int R, int H, int d_h, int 
     for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[rr][j] = 0.f;
-    for (int e = eg; e < d_h; e += EG) {
-      float w[8];
-      load8(w_uk + (static_cast<size_t>(h) * d_h + e) * d_c + kc * 8, w);
+    // rows e = eg, eg + EG, ... in batches of 8 loads issued together (the
+    // index is clamped, and rows past d_h get a zero query)
+    for (int e0 = eg; e0 < d_h; e0 += 8 * EG) {
+      float w[8][8];
 #pragma unroll
-      for (int rr = 0; rr < RB; ++rr) {
-        const float q = sq[rr * d_h + e];
+      for (int u = 0; u < 8; ++u) {
+        const int e = min(e0 + u * EG, d_h - 1);
+        load8(w_uk + (static_cast<size_t>(h) * d_h + e) * d_c + kc * 8, w[u]);
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[rr][j] = fmaf(q, w[j], acc[rr][j]);
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * EG;
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+          const float q = e < d_h ? sq[rr * d_h + e] : 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[rr][j] = fmaf(q, w[u][j], acc[rr][j]);
+        }
       }
     }
 #pragma unroll
@@ -231,14 +241,24 @@ __global__ __launch_bounds__(256) void up_project_kernel(int R, int H, int d_h, 
 #pragma unroll
   for (int rr = 0; rr < RB; ++rr) acc[rr] = 0.f;
   if (e < d_h) {
-    for (int c = p; c < KC; c += tpo) {
-      float w[8];
-      load8(w_uv + (static_cast<size_t>(h) * d_h + e) * d_c + c * 8, w);
+    // chunks c = p, p + tpo, ... in batches of 8 loads issued together (the
+    // index is clamped; chunks past KC are skipped)
+    for (int c0 = p; c0 < KC; c0 += 8 * tpo) {
+      float w[8][8];
 #pragma unroll
-      for (int rr = 0; rr < RB; ++rr) {
-        const float* o = olat + rr * d_c + c * 8;
+      for (int u = 0; u < 8; ++u)
+        load8(w_uv + (static_cast<size_t>(h) * d_h + e) * d_c + min(c0 + u * tpo, KC - 1) * 8, w[u]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[rr] = fmaf(w[j], o[j], acc[rr]);
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u * tpo;
+        if (c < KC) {
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr) {
+            const float* o = olat + rr * d_c + c * 8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[rr] = fmaf(w[u][j], o[j], acc[rr]);
+          }
+        }
       }
     }
   }
@@ -1088,8 +1108,10 @@ hipError_t absorb_rb(int R, int H, int d_h, int d_c, int d_r, const void* q_c, c
 template <typename T>
 hipError_t absorb_t(int R, int H, int d_h, int d_c, int d_r, const void* q_c, const void* q_r,
                     const void* w_uk, float* qbuf, hipStream_t st) {
-  return rows_per_wg(R, H) == 4 ? absorb_rb<T, 4>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st)
-                                : absorb_rb<T, 1>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st);
+  switch (rows_per_wg(R, H)) {
+    case 4: return absorb_rb<T, 4>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st);
+    default: return absorb_rb<T, 1>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st);
+  }
 }
 
 template <typename T>
@@ -1122,8 +1144,10 @@ hipError_t up_project_rb(int R, int H, int d_h, int d_c, const float* o_lat, con
 template <typename T>
 hipError_t up_project_t(int R, int H, int d_h, int d_c, const float* o_lat, const void* w_uv,
                         void* out, hipStream_t st) {
-  return rows_per_wg(R, H) == 4 ? up_project_rb<T, 4>(R, H, d_h, d_c, o_lat, w_uv, out, st)
-                                : up_project_rb<T, 1>(R, H, d_h, d_c, o_lat, w_uv, out, st);
+  switch (rows_per_wg(R, H)) {
+    case 4: return up_project_rb<T, 4>(R, H, d_h, d_c, o_lat, w_uv, out, st);
+    default: return up_project_rb<T, 1>(R, H, d_h, d_c, o_lat, w_uv, out, st);
+  }
 }
 
 }  // namespace
