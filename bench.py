@@ -281,7 +281,9 @@ def run_llm_decode(w, steps, warmup, m, torch, workloads):
            "slots_per_seq": n_slots, "step_GBps": (cache_bytes + weight_bytes) / (ms * 1e-3) / 1e9,
            "step_frac_hbm": (cache_bytes + weight_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "step_tflops": flops / (ms * 1e-3) / 1e12,
-           "attention": {"kernels": "decode_mfma_kernel + split_merge_kernel", "avg_call_us": ams * 1e3,
+           "attention": {"kernels": ("decode_stream_kernel" if (w.d_c, w.d_r) == (512, 64) else "decode_mfma_kernel")
+                                        + (" + split_merge_kernel" if splits > 1 else ""),
+                         "avg_call_us": ams * 1e3,
                                 "algorithmic_bytes_per_launch": cache_bytes,
                                 "GBps": cache_bytes / (ams * 1e-3) / 1e9,
                                 "frac_hbm": cache_bytes / (ams * 1e-3) / 1e9 / HBM_PEAK_GBS}}
@@ -326,17 +328,22 @@ def cpu_baseline_and_parity(w, dl, torch):
     out = dl.out.float().cpu().numpy().transpose(1, 0, 2, 3)   # [B, N, H, d_h]
     seqs = list(range(w.batch))
     errs = []
+    passes = 0
     with threadpool_limits(1):
         t0 = time.time()
-        for b in seqs:
-            ref = oracle.incremental(lat["c"][b], lat["k_r"][b], qry["q_c"][b], qry["q_r"][b],
-                                     wts["w_hyp"], wts["w_uk"], wts["w_uv"], w.s, w.softmax_scale)
-            errs.append(oracle.max_rel_err(out[b], ref))
+        # whole passes over the workload until at least 10 s of CPU work
+        while passes == 0 or time.time() - t0 < 10.0:
+            for b in seqs:
+                ref = oracle.incremental(lat["c"][b], lat["k_r"][b], qry["q_c"][b], qry["q_r"][b],
+                                         wts["w_hyp"], wts["w_uk"], wts["w_uv"], w.s, w.softmax_scale)
+                if passes == 0:
+                    errs.append(oracle.max_rel_err(out[b], ref))
+            passes += 1
         dt = time.time() - t0
-    tokens = len(seqs) * w.n_tokens
+    tokens = passes * len(seqs) * w.n_tokens
     return ({"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-             "sample": f"the whole workload: {len(seqs)} sequences x {w.n_tokens} tokens, fp64 NumPy, "
-                       f"one thread, {dt:.1f} s"},
+             "sample": f"{passes} pass(es) over the whole workload ({len(seqs)} sequences x {w.n_tokens} "
+                       f"tokens), fp64 NumPy, one thread, {dt:.1f} s"},
             float(max(errs)))
 
 
