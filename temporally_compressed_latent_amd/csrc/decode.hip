@@ -1088,6 +1088,374 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(StepArgs a) {
   if (p == 0 && o < nout) out[o] = f32_to_bf16_bits(acc);
 }
 
+// ---------------------------------------------------------------------------
+// Fused decode step for 256-wide latents (rows of d_c + d_R = 288): one
+// workgroup of 8 waves per (sequence, group of HG heads).
+//   absorb        : q~[h] = W_UK[h]^T q_c[h]; each thread takes 8 latent
+//                   columns and pairs of W_UK rows, v_dot2 on bf16 pairs;
+//   merge         : as in the kernel above (group 0 writes the cache row and
+//                   the fp32 state, every group keeps the row in LDS);
+//   attention     : wave-private flash decoding.  Wave w takes slot chunks
+//                   w, w + 8, ... of 16 slots and keeps its own running max,
+//                   sum and o_lat accumulator, with no barrier:
+//                     S^T[slot, head] = rows . q~^T  (16x16x32 MFMA; rows
+//                       straight from memory in the A layout, q~ from LDS),
+//                     O^T[col, head] += V^T P^T      (16x16x16 MFMA; P^T
+//                       stays in the score registers, V^T is read transposed
+//                       from a wave-private copy of the chunk's rows);
+//                   the 8 waves' partial results are merged once, in wave
+//                   order;
+//   up-projection : out[h] = W_UV[h] o_lat[h] on MFMA, one 16-row tile of
+//                   W_UV per wave; o_lat goes in as bf16 hi + lo parts
+//                   (o_lat = hi + lo to 16 bits), two products per k-step.
+// Heads occupy the MFMA's 16-wide N dimension; the rows past HG read q~
+// from a zero row.
+// ---------------------------------------------------------------------------
+template <int DC, int DR, int HG, int DH, bool MERGE>
+__global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
+  constexpr int NT = 512, NWV = 8;
+  constexpr int W = DC + DR;
+  constexpr int KSW = W / 32;                            // score k-steps
+  constexpr int KSU = DC / 32;                           // up-projection k-steps
+  constexpr int CTW = DC / 16;                           // PV column tiles
+  constexpr int KC = DC / 8;                             // 8-column chunks of a latent row
+  constexpr int GE = DC / 64;
+  constexpr int EGN = NT / (KC * HG);                    // absorb row groups
+  constexpr int NP = (DH + 2 * EGN - 1) / (2 * EGN);     // W_UK row pairs per thread
+  constexpr int MT = (DH + 15) / 16;                     // up-projection tiles per head
+  constexpr int RP = DC + 16;                            // row buffer pitch (elements)
+  constexpr int QP = W + 8;                              // q~ pitch (elements)
+  static_assert(W % 32 == 0 && NT % (KC * HG) == 0 && EGN >= 1, "shape");
+  static_assert(HG * DC <= NT && HG * DR <= NT && HG <= 16, "one q~ element per thread");
+  static_assert(HG * MT <= NWV, "one up-projection tile per wave");
+
+  struct Absorb {
+    float red[HG][EGN][DC];
+  };
+  struct Rows {
+    uint16_t r[NWV][16][RP];
+  };
+  struct Combine {
+    float o[NWV][HG][DC];
+    float m[NWV][HG];
+    float l[NWV][HG];
+    uint16_t ob[2][HG][DC];  // o_lat: bf16 hi, bf16 lo
+    uint16_t zero[DC];
+  };
+  union Phases {
+    Absorb ab;
+    Rows rw;
+    Combine cb;
+  };
+  __shared__ __align__(16) Phases u;
+  __shared__ __align__(16) uint16_t sq[HG + 1][QP];  // q~ rows, scaled, bf16; row HG is zero
+  __shared__ __align__(16) uint16_t s_new[W];
+
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id: id L runs on
+  // XCD L % 8.  Sequence b goes to XCD b % 8 with all of its head groups.
+  const int G = a.groups;
+  const int L = blockIdx.x, xcd = L & 7, k8 = L >> 3;
+  const int grp = k8 % G, b = 8 * (k8 / G) + xcd;
+  if (b >= a.B) return;
+  const int H = a.H, d_h = a.d_h, h0 = grp * HG;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+
+  const int pos = a.pos[b];
+  // Loads that do not depend on the position go out first, unconditionally
+  // (indices clamped into the tensors, unused values dropped at their use).
+  // absorb: thread (kc, hl, eg) takes columns kc*8 .. +7 of head hl and the
+  // row pairs e = 2 (eg + j EGN) + {0, 1}
+  const int kc = tid % KC, hl = (tid / KC) % HG, eg = tid / (KC * HG);
+  const auto r_uk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w_uk + static_cast<size_t>(h0) * d_h * DC), static_cast<short>(0), HG * d_h * DC * 2,
+      kBufferRsrcWord3);
+  const auto r_q = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.q_c + (static_cast<size_t>(b) * H + h0) * d_h), static_cast<short>(0), HG * d_h * 2,
+      kBufferRsrcWord3);
+  uint4 wk0[NP], wk1[NP];
+  uint32_t qp[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int e0 = 2 * (eg + j * EGN);
+    const int r0 = min(e0, d_h - 1), r1 = min(e0 + 1, d_h - 1);
+    auto v0 = __builtin_amdgcn_raw_buffer_load_b128(r_uk, ((hl * d_h + r0) * DC + kc * 8) * 2, 0, 0);
+    auto v1 = __builtin_amdgcn_raw_buffer_load_b128(r_uk, ((hl * d_h + r1) * DC + kc * 8) * 2, 0, 0);
+    wk0[j] = uint4{v0[0], v0[1], v0[2], v0[3]};
+    wk1[j] = uint4{v1[0], v1[1], v1[2], v1[3]};
+    // rows past d_h read as zero (the resource ends at the group's last row)
+    const uint32_t q0 = __builtin_amdgcn_raw_buffer_load_b16(r_q, (hl * d_h + e0) * 2, 0, 0);
+    const uint32_t q1 = __builtin_amdgcn_raw_buffer_load_b16(r_q, (hl * d_h + e0 + 1) * 2, 0, 0);
+    qp[j] = (e0 < d_h ? q0 : 0u) | ((e0 + 1 < d_h ? q1 : 0u) << 16);
+  }
+  // up-projection: wave w takes rows mt*16 .. +15 of head hu (waves past
+  // HG * ceil(d_h / 16) load a clamped tile and store nothing); lane (g, c16)
+  // holds row mt*16 + c16, columns 32 ks + 8g .. +7: the MFMA A layout
+  const int mt_n = (d_h + 15) / 16;
+  const int hu = min(wave / mt_n, HG - 1), mt = wave % mt_n;
+  const bool up_wave = wave < HG * mt_n;
+  const auto r_uv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w_uv + static_cast<size_t>(h0) * d_h * DC), static_cast<short>(0), HG * d_h * DC * 2,
+      kBufferRsrcWord3);
+  const int vu = ((hu * d_h + min(mt * 16 + c16, d_h - 1)) * DC + 8 * g) * 2;
+  uint4 wv[KSU];  // loaded once the absorb is done (see below)
+  const int te = min(tid, W - 1);  // merge column of this thread (tid < W)
+  uint16_t gxb[GE], mxb = 0;
+  float gw[GE];
+  if constexpr (MERGE) {
+#pragma unroll
+    for (int j = 0; j < GE; ++j) {
+      gxb[j] = a.c[static_cast<size_t>(b) * DC + lane + 64 * j];
+      gw[j] = a.w_hyp[lane + 64 * j];
+    }
+    mxb = te < DC ? a.c[static_cast<size_t>(b) * DC + te] : a.k_r[static_cast<size_t>(b) * DR + te - DC];
+  }
+
+  const int n = pos >= 1 ? slot_of(pos, a.s) : 0;
+  const bool ok = pos >= 1 && n <= a.max_slots && (!MERGE || pos <= a.pe_rows);
+  uint16_t* out = a.out + (static_cast<size_t>(b) * H + h0) * d_h;
+  if (!ok) {
+    for (int idx = tid; idx < HG * d_h; idx += NT) out[idx] = 0x7fc0u;  // NaN
+    return;
+  }
+  // Position-dependent loads: pe row, the open slot's state, the rope query
+  // and the first two chunks of cache rows.  Memory rows are the completed
+  // slots 0..n-2 when merging (row n-1 is the new one, taken from LDS), else
+  // 0..n-1.
+  float gp[GE], macc = 0.f;
+  const bool cont = (pos - 1) % a.s != 0;  // the token continues an open block
+  if constexpr (MERGE) {
+#pragma unroll
+    for (int j = 0; j < GE; ++j) gp[j] = a.pe[static_cast<size_t>(pos - 1) * DC + lane + 64 * j];
+    macc = a.open_acc[(static_cast<size_t>(b) * 2 + (pos - 1) % 2) * W + te];
+  }
+  const int tq = min(tid, HG * DR - 1);
+  const uint16_t qrb = a.q_r[(static_cast<size_t>(b) * H + h0 + tq / DR) * DR + tq % DR];
+  const uint16_t* rows = a.cache + static_cast<size_t>(b) * a.max_slots * W;
+  const int hm = MERGE ? n - 1 : n;
+  // rows [0, hm) of the sequence; a load past them reads zero
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(rows), static_cast<short>(0), hm * W * 2,
+                                                    kBufferRsrcWord3);
+  // chunk ci = slots 16 ci .. +15; lane (g, c16) holds row c16, elements
+  // 32 ks + 8g .. +7: the MFMA A layout
+  uint4 ra[KSW], rb[KSW];
+  auto load_chunk = [&](int ci, uint4 (&r)[KSW]) {
+    const int so = __builtin_amdgcn_readfirstlane(ci * 16 * W * 2);
+#pragma unroll
+    for (int ks = 0; ks < KSW; ++ks) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (c16 * W + 8 * g) * 2 + ks * 64, so, 0);
+      r[ks] = uint4{v[0], v[1], v[2], v[3]};
+    }
+  };
+  load_chunk(wave, ra);
+  load_chunk(wave + NWV, rb);
+
+  // absorb: partial sums over this thread's rows, W_UK row pairs against
+  // (q_c[e0], q_c[e0 + 1]) pairs
+  {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const uint32_t x0[4] = {wk0[j].x, wk0[j].y, wk0[j].z, wk0[j].w};
+      const uint32_t x1[4] = {wk1[j].x, wk1[j].y, wk1[j].z, wk1[j].w};
+      const bf16x2 qv = __builtin_bit_cast(bf16x2, qp[j]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        // (row e0, row e0 + 1) of column 2d, then of column 2d + 1
+        const uint32_t lo = __builtin_amdgcn_perm(x1[d], x0[d], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(x1[d], x0[d], 0x07060302u);
+        acc[2 * d] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lo), qv, acc[2 * d], false);
+        acc[2 * d + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hi), qv, acc[2 * d + 1], false);
+      }
+    }
+    float* dst = &u.ab.red[hl][eg][kc * 8];
+    *reinterpret_cast<float4*>(dst) = float4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<float4*>(dst + 4) = float4{acc[4], acc[5], acc[6], acc[7]};
+  }
+  // every wave computes the gate (same values, same order: the same bits)
+  float gate = 0.f;
+  if constexpr (MERGE) {
+    float gx[GE];
+#pragma unroll
+    for (int j = 0; j < GE; ++j) gx[j] = bf16_bits_to_f32(gxb[j]);
+    gate = gate_from_lane_values<GE>(gx, gp, gw);
+  }
+  __syncthreads();
+  // W_UV is needed last: its loads go out only now, so that they do not
+  // queue ahead of the W_UK and cache-row loads in the compute unit's
+  // memory pipeline
+#pragma unroll
+  for (int ks = 0; ks < KSU; ++ks) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_uv, vu + ks * 64, 0, 0);
+    wv[ks] = uint4{v[0], v[1], v[2], v[3]};
+  }
+  if constexpr (MERGE) {
+    if (tid < W) {
+      const float v = fmaf(gate, bf16_bits_to_f32(mxb), cont ? macc : 0.f);
+      const uint16_t w16 = f32_to_bf16_bits(v);
+      if (grp == 0) {
+        a.open_acc[(static_cast<size_t>(b) * 2 + pos % 2) * W + tid] = v;
+        a.cache[(static_cast<size_t>(b) * a.max_slots + n - 1) * W + tid] = w16;
+      }
+      s_new[tid] = w16;
+    }
+  }
+  const float qscale = a.scale * kLog2e;
+  if (tid < HG * DC) {
+    const int h = tid / DC, k = tid % DC;
+    float v = 0.f;
+#pragma unroll
+    for (int r = 0; r < EGN; ++r) v += u.ab.red[h][r][k];
+    sq[h][k] = f32_to_bf16_bits(v * qscale);
+  }
+  if (tid < HG * DR) sq[tid / DR][DC + tid % DR] = f32_to_bf16_bits(bf16_bits_to_f32(qrb) * qscale);
+  for (int e = tid; e < W; e += NT) sq[HG][e] = 0;
+  __syncthreads();
+
+  // attention
+  bf16x8 qk[KSW];
+  {
+    const uint16_t* qrow = sq[c16 < HG ? c16 : HG];
+#pragma unroll
+    for (int ks = 0; ks < KSW; ++ks) qk[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + 8 * g);
+  }
+  constexpr float kLazyLog2 = 8.f;
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc[CTW];
+#pragma unroll
+  for (int ct = 0; ct < CTW; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* wb = &u.rw.r[wave][0][0];
+  const uint16_t* vb = wb + (4 * g + (c16 >> 2)) * RP + 4 * (c16 & 3);
+  auto do_chunk = [&](int ci, uint4 (&r)[KSW]) {
+    const int base = 16 * ci;
+    if (base >= n) return;
+    // the new row (slot hm, merging) comes from LDS
+    if (MERGE && hm >= base && hm < base + 16 && c16 == hm - base) {
+#pragma unroll
+      for (int ks = 0; ks < KSW; ++ks) r[ks] = *reinterpret_cast<const uint4*>(s_new + ks * 32 + 8 * g);
+    }
+    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSW; ++ks) {
+      const bf16x8 ar = __builtin_bit_cast(bf16x8, r[ks]);
+      if (ks % 2 == 0)
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, qk[ks], sa, 0, 0, 0);
+      else
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, qk[ks], sb, 0, 0, 0);
+    }
+    // sa[i] + sb[i]: score of slot base + 4g + i against head c16 (log2 units)
+    float sc[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = base + 4 * g + i < n ? sa[i] + sb[i] : -INFINITY;
+      mx = fmaxf(mx, sc[i]);
+    }
+    // The running max moves only when a score passes it by 2^kLazyLog2; it
+    // then becomes the head's exact maximum so far.  Any reference point
+    // gives the same softmax after the final division by the sum, and the
+    // terms stay below 2^kLazyLog2.
+    if (__any(mx > m + kLazyLog2)) {
+      float mh = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mh = fmaxf(mh, __shfl_xor(mh, 32, 64));
+      const float mn = fmaxf(m, mh);
+      if (ci != wave) {  // nothing accumulated before this wave's first chunk
+        const float alpha = fast_exp2(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) acc[ct] *= alpha;
+      }
+      m = mn;
+    }
+    s16x4 pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = fast_exp2(sc[i] - m);
+      l += pv;
+      pb[i] = static_cast<short>(f32_to_bf16_bits(pv));
+    }
+    // the chunk's latent columns into the wave's buffer, then V^T: lane
+    // (g, k) of a 16-lane group points at row 4g + k/4, columns
+    // 16 ct + 4 (k%4) .. +3, and receives rows 4g .. 4g+3 of column 16 ct + k
+#pragma unroll
+    for (int ks = 0; ks < DC / 32; ++ks) *reinterpret_cast<uint4*>(wb + c16 * RP + ks * 32 + 8 * g) = r[ks];
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+      const s16x4 va = lds_read_tr16(vb + ct * 16);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[ct], 0, 0, 0);
+    }
+  };
+  // Two chunks in flight per wave.  Loads past the last chunk are issued
+  // anyway (they read zero past row hm and touch no memory): unconditional
+  // loads let each wait cover only the chunk it needs.
+  const int nch = (n + 15) / 16;
+  for (int j = 0; wave + NWV * j < nch; j += 2) {
+    do_chunk(wave + NWV * j, ra);
+    load_chunk(wave + NWV * (j + 2), ra);
+    do_chunk(wave + NWV * (j + 1), rb);
+    load_chunk(wave + NWV * (j + 3), rb);
+  }
+  // this wave's sum for head c16: the four lane groups, in a fixed order
+  float lw = l + __shfl_xor(l, 16, 64);
+  lw = lw + __shfl_xor(lw, 32, 64);
+  __syncthreads();  // every wave is done with its row buffer
+  if (c16 < HG) {
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) *reinterpret_cast<f32x4*>(&u.cb.o[wave][c16][ct * 16 + 4 * g]) = acc[ct];
+    if (g == 0) {
+      u.cb.m[wave][c16] = m;
+      u.cb.l[wave][c16] = lw;
+    }
+  }
+  __syncthreads();
+  // o_lat[h, col]: the waves' partial results rescaled to a common max and
+  // summed in wave order, normalised, split into bf16 hi + lo
+  if (tid < HG * DC) {
+    const int h = tid / DC, col = tid % DC;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, u.cb.m[w][h]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const float f = fast_exp2(u.cb.m[w][h] - M);
+      Ls += f * u.cb.l[w][h];
+      O += f * u.cb.o[w][h][col];
+    }
+    const float v = O / Ls;
+    const uint16_t hi = f32_to_bf16_bits(v);
+    u.cb.ob[0][h][col] = hi;
+    u.cb.ob[1][h][col] = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+  }
+  for (int e = tid; e < DC; e += NT) u.cb.zero[e] = 0;
+  __syncthreads();
+
+  // up-projection: C[e, n] = sum_k W_UV[hu][mt*16 + e][k] B[k, n], with
+  // column 0 of B = o_lat hi (first product) or lo (second), the other
+  // columns zero
+  if (up_wave) {
+    const uint16_t* bh = c16 == 0 ? &u.cb.ob[0][hu][8 * g] : &u.cb.zero[8 * g];
+    const uint16_t* bl = c16 == 0 ? &u.cb.ob[1][hu][8 * g] : &u.cb.zero[8 * g];
+    f32x4 co = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSU; ++ks) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, wv[ks]);
+      co = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, *reinterpret_cast<const bf16x8*>(bh + ks * 32), co, 0, 0, 0);
+      co = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, *reinterpret_cast<const bf16x8*>(bl + ks * 32), co, 0, 0, 0);
+    }
+    // lane (g, 0) holds rows 4g .. 4g+3 of column 0
+    if (c16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = mt * 16 + 4 * g + i;
+        if (e < d_h) out[hu * d_h + e] = f32_to_bf16_bits(co[i]);
+      }
+    }
+  }
+}
+
 // Rows per workgroup of absorb / up-projection: one row while there are few
 // (row, head) pairs, so the launch fills the chip; four when there are many,
 // so each W_UK / W_UV chunk loaded serves four rows.
@@ -1177,6 +1545,13 @@ void step_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
   else
     decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, false><<<grid, NTH, 0, st>>>(a);
 }
+template <int DC, int DR, int HG, int DH>
+void step_wave_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
+  if (a.merge)
+    decode_step_wave_kernel<DC, DR, HG, DH, true><<<grid, 512, 0, st>>>(a);
+  else
+    decode_step_wave_kernel<DC, DR, HG, DH, false><<<grid, 512, 0, st>>>(a);
+}
 
 // Heads per group the step kernel is instantiated for, per latent shape.
 bool step_hg_instantiated(int d_c, int d_r, int hg, int d_h) {
@@ -1218,9 +1593,9 @@ hipError_t launch_decode_step(const StepArgs& a0, hipStream_t st) {
   const int hg = a.H / a.groups;
   const unsigned grid = 8u * static_cast<unsigned>(a.groups) * static_cast<unsigned>((a.B + 7) / 8);
   if (a.d_c == 256 && a.d_r == 32 && hg == 1) {
-    step_launch<256, 32, 128, 1, 64, 512, 2>(a, grid, st);
+    step_wave_launch<256, 32, 1, 64>(a, grid, st);
   } else if (a.d_c == 256 && a.d_r == 32 && hg == 2) {
-    step_launch<256, 32, 128, 2, 64, 512, 2>(a, grid, st);
+    step_wave_launch<256, 32, 2, 64>(a, grid, st);
   } else if (a.d_c == 512 && a.d_r == 64 && hg == 1) {
     step_launch<512, 64, 64, 1, 128, 1024, 1>(a, grid, st);
   } else {
