@@ -102,6 +102,41 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Across the four 16-lane rows of a wave, for each lane position: the max
+// (sum) of the value at lanes c, c+16, c+32, c+48, returned to all four.
+// v_permlane16_swap exchanges rows 1 <-> 0 and 3 <-> 2 between its two
+// operands, v_permlane32_swap the halves; with both operands holding the
+// same value, afterwards each holds a row's own value or its partner's, and
+// combining the two gives every lane the same pair.  Sums are
+// (r0 + r1) + (r2 + r3).  Written as VALU asm (two read-write operands in
+// distinct registers): the builtins' two results were folded into one by
+// the compiler when both inputs are the same value.  s_nop 1 covers the
+// VALU-write to permlane-read hazard.
+__device__ __forceinline__ void permlane16_swap_regs(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap_regs(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float cross_row_max(float v) {
+  float a = v, b = v;
+  permlane16_swap_regs(a, b);
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  permlane32_swap_regs(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float cross_row_sum(float v) {
+  float a = v, b = v;
+  permlane16_swap_regs(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  permlane32_swap_regs(a, b);
+  return a + b;
+}
+
 // Sum over the 64 lanes of a wave, returned to every lane: the four 16-lane
 // row sums (DPP), then (row0 + row1) + (row2 + row3) from lanes 0, 16, 32, 48.
 // The order is fixed, so every kernel that uses it gets the same bits.

@@ -1240,6 +1240,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
   // 32 ks + 8g .. +7: the MFMA A layout
   uint4 ra[KSW], rb[KSW];
   auto load_chunk = [&](int ci, uint4 (&r)[KSW]) {
+    if (16 * ci >= hm) return;  // no memory rows (a load past them would still take issue slots)
     const int so = __builtin_amdgcn_readfirstlane(ci * 16 * W * 2);
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
@@ -1331,6 +1332,10 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
   auto do_chunk = [&](int ci, uint4 (&r)[KSW]) {
     const int base = 16 * ci;
     if (base >= n) return;
+    if (MERGE && base >= hm) {  // only the new row: nothing was loaded
+#pragma unroll
+      for (int ks = 0; ks < KSW; ++ks) r[ks] = uint4{0u, 0u, 0u, 0u};
+    }
     // the new row (slot hm, merging) comes from LDS
     if (MERGE && hm >= base && hm < base + 16 && c16 == hm - base) {
 #pragma unroll
@@ -1358,9 +1363,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
     // gives the same softmax after the final division by the sum, and the
     // terms stay below 2^kLazyLog2.
     if (__any(mx > m + kLazyLog2)) {
-      float mh = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mh = fmaxf(mh, __shfl_xor(mh, 32, 64));
-      const float mn = fmaxf(m, mh);
+      const float mn = fmaxf(m, cross_row_max(mx));
       if (ci != wave) {  // nothing accumulated before this wave's first chunk
         const float alpha = fast_exp2(m - mn);
         l *= alpha;
@@ -1387,9 +1390,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
       acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[ct], 0, 0, 0);
     }
   };
-  // Two chunks in flight per wave.  Loads past the last chunk are issued
-  // anyway (they read zero past row hm and touch no memory): unconditional
-  // loads let each wait cover only the chunk it needs.
+  // Two chunks in flight per wave.
   const int nch = (n + 15) / 16;
   for (int j = 0; wave + NWV * j < nch; j += 2) {
     do_chunk(wave + NWV * j, ra);
@@ -1398,8 +1399,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
     load_chunk(wave + NWV * (j + 3), rb);
   }
   // this wave's sum for head c16: the four lane groups, in a fixed order
-  float lw = l + __shfl_xor(l, 16, 64);
-  lw = lw + __shfl_xor(lw, 32, 64);
+  const float lw = cross_row_sum(l);
   __syncthreads();  // every wave is done with its row buffer
   if (c16 < HG) {
 #pragma unroll
@@ -1438,19 +1438,24 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
   if (up_wave) {
     const uint16_t* bh = c16 == 0 ? &u.cb.ob[0][hu][8 * g] : &u.cb.zero[8 * g];
     const uint16_t* bl = c16 == 0 ? &u.cb.ob[1][hu][8 * g] : &u.cb.zero[8 * g];
-    f32x4 co = f32x4{0.f, 0.f, 0.f, 0.f};
+    // four independent accumulation chains (hi / lo x even / odd k-steps)
+    f32x4 co[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) co[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KSU; ++ks) {
       const bf16x8 av = __builtin_bit_cast(bf16x8, wv[ks]);
-      co = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, *reinterpret_cast<const bf16x8*>(bh + ks * 32), co, 0, 0, 0);
-      co = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, *reinterpret_cast<const bf16x8*>(bl + ks * 32), co, 0, 0, 0);
+      co[ks % 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, *reinterpret_cast<const bf16x8*>(bh + ks * 32),
+                                                           co[ks % 2], 0, 0, 0);
+      co[2 + ks % 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, *reinterpret_cast<const bf16x8*>(bl + ks * 32),
+                                                               co[2 + ks % 2], 0, 0, 0);
     }
     // lane (g, 0) holds rows 4g .. 4g+3 of column 0
     if (c16 == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = mt * 16 + 4 * g + i;
-        if (e < d_h) out[hu * d_h + e] = f32_to_bf16_bits(co[i]);
+        if (e < d_h) out[hu * d_h + e] = f32_to_bf16_bits((co[0][i] + co[1][i]) + (co[2][i] + co[3][i]));
       }
     }
   }
