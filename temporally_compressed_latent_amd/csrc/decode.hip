@@ -1327,8 +1327,12 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
   f32x4 acc[CTW];
 #pragma unroll
   for (int ct = 0; ct < CTW; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Row buffer layout: the 16-byte chunk q of row r sits at chunk
+  // q ^ ((r >> 2) & 1), so that the row writes (8 lanes = rows r .. r+7 at
+  // one chunk) and the transposing reads both spread over the banks.
   uint16_t* wb = &u.rw.r[wave][0][0];
-  const uint16_t* vb = wb + (4 * g + (c16 >> 2)) * RP + 4 * (c16 & 3);
+  uint16_t* wrow = wb + c16 * RP + 8 * (g ^ ((c16 >> 2) & 1));
+  const uint16_t* vb = wb + (4 * g + (c16 >> 2)) * RP + 8 * (((c16 >> 1) & 1) ^ (g & 1)) + 4 * (c16 & 1);
   auto do_chunk = [&](int ci, uint4 (&r)[KSW]) {
     const int base = 16 * ci;
     if (base >= n) return;
@@ -1381,9 +1385,10 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
     }
     // the chunk's latent columns into the wave's buffer, then V^T: lane
     // (g, k) of a 16-lane group points at row 4g + k/4, columns
-    // 16 ct + 4 (k%4) .. +3, and receives rows 4g .. 4g+3 of column 16 ct + k
+    // 16 ct + 4 (k%4) .. +3 (in chunk 2 ct + (k%4)/2, swizzled), and
+    // receives rows 4g .. 4g+3 of column 16 ct + k
 #pragma unroll
-    for (int ks = 0; ks < DC / 32; ++ks) *reinterpret_cast<uint4*>(wb + c16 * RP + ks * 32 + 8 * g) = r[ks];
+    for (int ks = 0; ks < DC / 32; ++ks) *reinterpret_cast<uint4*>(wrow + ks * 32) = r[ks];
 #pragma unroll
     for (int ct = 0; ct < CTW; ++ct) {
       const s16x4 va = lds_read_tr16(vb + ct * 16);
