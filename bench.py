@@ -165,7 +165,8 @@ def run_decode_loop(w, steps, warmup, m, torch, workloads):
         per_launch = all_b / w.n_tokens
         us = ms * 1e3 / w.n_tokens
         rec["dominant_kernel"] = {
-            "name": "decode_step_kernel", "launches_per_step": w.n_tokens, "avg_launch_us": us,
+            "name": "decode_step_wave_kernel" if w.d_c == 256 else "decode_step_kernel",
+            "launches_per_step": w.n_tokens, "avg_launch_us": us,
             "algorithmic_bytes_per_launch": per_launch, "GBps": per_launch / (us * 1e-6) / 1e9}
     return rec, dl
 
