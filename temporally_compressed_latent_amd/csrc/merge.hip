@@ -72,6 +72,56 @@ __device__ void compute_gates(const MergeArgs& a, int b, int p0, int ta, int nto
   }
 }
 
+// The same gates with every load of a pass in flight together, for
+// d_c = 64 GE: wave w takes tokens w, w + nwaves, ... (NTOK of them per pass),
+// lane l holds elements l + 64 j of c_t, pe_t and W_hyp, and the sum runs in
+// the order of gate_from_lane_values (the same bits as gates_of_tokens and
+// the decode-step kernels).  Token indices past the last are clamped (their
+// gates are computed and dropped), so the loads are unconditional.
+template <typename T, int GE, int NTOK>
+__device__ void compute_gates_lanes(const MergeArgs& a, int b, int p0, int ta, int ntok, float* gw) {
+  const T* c = static_cast<const T*>(a.c);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  float wh[GE];
+#pragma unroll
+  for (int j = 0; j < GE; ++j) wh[j] = a.w_hyp[lane + 64 * j];
+  for (int k0 = wave; k0 < ntok; k0 += nwaves * NTOK) {
+    float x[NTOK][GE], pv[NTOK][GE];
+#pragma unroll
+    for (int k = 0; k < NTOK; ++k) {
+      const int t = ta + min(k0 + k * nwaves, ntok - 1);
+      const T* row = c + (static_cast<size_t>(b) * a.T + (t - p0)) * a.d_c;
+      const float* per = a.pe + static_cast<size_t>(t - 1) * a.d_c;
+#pragma unroll
+      for (int j = 0; j < GE; ++j) {
+        x[k][j] = Store<T>::load(row, lane + 64 * j);
+        pv[k][j] = per[lane + 64 * j];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NTOK; ++k) {
+      const float w = gate_from_lane_values<GE>(x[k], pv[k], wh);
+      const int kk = k0 + k * nwaves;
+      if (lane == 0 && kk < ntok) {
+        gw[kk] = w;
+        if (a.gate_out) a.gate_out[static_cast<size_t>(b) * a.T + (ta + kk - p0)] = w;
+      }
+    }
+  }
+}
+
+template <typename T>
+__device__ void merge_gates(const MergeArgs& a, int b, int p0, int ta, int ntok, float* gw) {
+  if (a.d_c == 256)
+    compute_gates_lanes<T, 4, 8>(a, b, p0, ta, ntok, gw);
+  else if (a.d_c == 512)
+    compute_gates_lanes<T, 8, 4>(a, b, p0, ta, ntok, gw);
+  else
+    compute_gates<T>(a, b, p0, ta, ntok, gw);
+}
+
 // Eight elements of x_t = [c_t ; k^R_t] starting at column e (e % 8 == 0, and
 // d_c % 8 == 0, so a chunk never straddles c and k^R).
 template <typename T>
@@ -101,7 +151,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a, int b
   const int bhi = min(r.bk1, blo + blocks_per_wg - 1);
   const int ta = max(r.p0, blo * s + 1);
   const int tb = min(r.t_last, bhi * s + s);
-  compute_gates<T>(a, b, r.p0, ta, tb - ta + 1, gw);
+  merge_gates<T>(a, b, r.p0, ta, tb - ta + 1, gw);
   __syncthreads();
 
   T* cache = static_cast<T*>(a.cache);
@@ -126,13 +176,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a, int b
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = 0.f;
     }
-    for (int t = t0; t <= t1; ++t) {
-      float x[8];
-      token_chunk<T>(a, b, t - r.p0, e, x);
-      const float w = gw[t - ta];
+    // four tokens' chunks in flight at a time (indices clamped to the block)
+    for (int t = t0; t <= t1; t += 4) {
+      float x[4][8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, x[j], acc[j]);
-      if (P) store8(P + (static_cast<size_t>(b) * a.T + (t - r.p0)) * W + e, acc);
+      for (int u = 0; u < 4; ++u) token_chunk<T>(a, b, min(t + u, t1) - r.p0, e, x[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (t + u <= t1) {
+          const float w = gw[t + u - ta];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, x[u][j], acc[j]);
+          if (P) store8(P + (static_cast<size_t>(b) * a.T + (t + u - r.p0)) * W + e, acc);
+        }
+      }
     }
     store8(cache + (static_cast<size_t>(b) * a.max_slots + blk) * W + e, acc);
     if (write_open && blk == r.bk1) store8(a.open_acc + (static_cast<size_t>(b) * 2 + r.t_last % 2) * W + e, acc);
@@ -152,7 +209,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_tail_kernel(MergeArgs a) 
   const int W = a.d_c + a.d_r;
   const int ts = r.bk1 * a.s + 1;
   const int t0 = max(ts, r.p0);
-  compute_gates<T>(a, b, r.p0, t0, r.t_last - t0 + 1, gw);
+  merge_gates<T>(a, b, r.p0, t0, r.t_last - t0 + 1, gw);
   __syncthreads();
   const int ch = threadIdx.x;
   if (ch >= W / 8) return;
@@ -215,8 +272,9 @@ hipError_t launch_merge(const MergeArgs& a, int dtype, hipStream_t st) {
   // Blocks one call can touch: ceil((T-1)/s) + 1 (a block may continue).
   const long long max_blocks = (static_cast<long long>(a.T) - 1 + a.s - 1) / a.s + 1;
   // Blocks per workgroup: enough workgroups (~2048) to fill the chip, at most
-  // kMaxChunkTokens tokens of gates per workgroup.
-  const int cap = a.s >= kMaxChunkTokens ? 1 : kMaxChunkTokens / a.s;
+  // 32 tokens of gates per workgroup (one pass of the gate loads) unless one
+  // block is longer.
+  const int cap = a.s >= 32 ? 1 : 32 / a.s;
   long long per = (max_blocks * a.B + 2047) / 2048;
   const int blocks_per_wg = static_cast<int>(per < 1 ? 1 : (per > cap ? cap : per));
   const long long chunks = (max_blocks + blocks_per_wg - 1) / blocks_per_wg;
