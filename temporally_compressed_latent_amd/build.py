@@ -38,9 +38,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmtla.so)")
 
 
+# Per-file additions.  prefill.hip: the attention's softmax takes maxima of
+# raw MFMA results; without NaN semantics (no input here is NaN) fmaxf needs
+# no canonicalising move per value and pairs into v_max3_f32.
+FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

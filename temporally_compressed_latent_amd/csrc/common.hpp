@@ -156,6 +156,7 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+
 // Workgroup barrier that waits only for this wave's LDS operations, not for
 // vector-memory loads still in flight (__syncthreads' fence waits for those
 // too, which would drain a ring of tiles being loaded straight into LDS).

@@ -375,9 +375,11 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
             }
           }
         }
-        // this lane's maximum over its 32 scores (four independent chains);
-        // the other half of the query's slots sits in lane ^ 32, which only
-        // the rare rescale below needs
+        // this lane's maximum over its 32 scores (four independent chains;
+        // the file is built without NaN semantics, so these become
+        // three-input maxima on the raw MFMA results); the other half of
+        // the query's slots sits in lane ^ 32, which only the rare rescale
+        // below needs
         float m4[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) m4[u] = fmaxf(sc[0][t][u], sc[1][t][u]);
@@ -397,21 +399,18 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) sc[rt][t][i] -= d;
         }
-        float l4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float pv = fast_exp2(sc[rt][t][i]);
-            sc[rt][t][i] = pv;
-            l4[i % 4] += pv;
-          }
+          for (int i = 0; i < 16; ++i) sc[rt][t][i] = fast_exp2(sc[rt][t][i]);
         }
-        lp[t] += (l4[0] + l4[1]) + (l4[2] + l4[3]);
       }
 
       // O^T += V^T P^T over the tile's four 16-slot chunks
       const int q16 = lane >> 4, k16 = lane & 15;
+      float lsum[NQ][2];
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) lsum[t][0] = lsum[t][1] = 0.f;
 #pragma unroll
       for (int c = 0; c < TS / 16; ++c) {
         const int rt = c / 2, jb = 2 * (c % 2);
@@ -425,6 +424,14 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
             pk[4 + r] = f32_to_bf16_bits(sc[rt][t][4 * (jb + 1) + r]);
           }
           pb[t] = __builtin_bit_cast(bf16x8, pk);
+          // the row sum takes the bf16 probabilities the product uses: one
+          // v_dot2 against (1, 1) per pair
+          const uint4 pw = __builtin_bit_cast(uint4, pk);
+          const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+          lsum[t][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), one2, lsum[t][0], false);
+          lsum[t][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), one2, lsum[t][1], false);
+          lsum[t][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), one2, lsum[t][0], false);
+          lsum[t][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), one2, lsum[t][1], false);
         }
         const int sb0 = 16 * c + 4 * (q16 >> 1);
 #pragma unroll
@@ -439,6 +446,8 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
             acc[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[t], acc[dt][t], 0, 0, 0);
         }
       }
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) lp[t] += lsum[t][0] + lsum[t][1];
     }
     __syncthreads();
   }
