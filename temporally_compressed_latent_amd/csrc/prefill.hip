@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
 // by l and stays far from fp32 overflow.
 // ---------------------------------------------------------------------------
 template <int DH, int DR, int NQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 && DH == 64 ? 2 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NQ == 1 && DH == 64 ? 3 : 1)))
 void prefill_attn_kernel(PrefillAttnArgs a) {
   constexpr int DQK = DH + DR;
   constexpr int KK = DQK / 16;       // k-chunks of the score MFMA
