@@ -510,7 +510,7 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
     void* v = at(workspace, ws.v);
     e = mtla::launch_prefill_kv(B, N, H, dims->d_h, dims->d_c, dims->d_r, P, w_uk, w_uv, kc, v, s);
     if (e != hipSuccess) return hip_status(e, "up-projection launch");
-    mtla::PrefillAttnArgs pa{B, N, H, dims->d_h, dims->d_c, dims->d_r, dims->stride_s,
+    mtla::PrefillAttnArgs pa{B, N, H, dims->d_h, dims->d_c, dims->d_r, dims->stride_s, 0,
                              dims->softmax_scale, q_c, q_r, kc, v, P, out};
     return hip_status(mtla::launch_prefill_attn(pa, s), "prefill attention launch");
   }

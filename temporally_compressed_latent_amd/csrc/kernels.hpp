@@ -98,6 +98,7 @@ hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
 
 struct PrefillAttnArgs {
   int B, N, H, d_h, d_c, d_r, s;
+  int nqt;               // query tiles per (sequence, head) (set at launch)
   float scale;
   const void* q_c;       // [B, N, H, d_h]
   const void* q_r;       // [B, N, H, d_r]

@@ -187,11 +187,27 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   __shared__ __align__(16) uint16_t sKb[2][TS * KP];
   __shared__ __align__(16) uint16_t sVb[2][TS * VP];
 
-  // Grid (H, B, query tiles): dispatch runs x fastest, so every (head,
-  // sequence) takes its heaviest query tile before any lighter one.
-  const int nqt = gridDim.z;
-  const int qt = nqt - 1 - static_cast<int>(blockIdx.z);
-  const int h = blockIdx.x, b = blockIdx.y;
+  // One-dimensional grid of B*H*nqt workgroups.  Workgroups are dealt to the
+  // 8 XCDs round-robin by linear id (id L runs on XCD L % 8).  When B*H is a
+  // multiple of 8, XCD x takes the (sequence, head) pairs x, x+8, ... one
+  // after another, each pair's query tiles heaviest first: the workgroups an
+  // XCD runs at once then share the K/V rows of two or three pairs, which stay
+  // in its L2 (dealt by head instead, an XCD's working set was 16 sequences'
+  // rows, several times its L2).  Otherwise every pair takes its heaviest
+  // query tile before any lighter one.
+  const int nqt = a.nqt;
+  const int npair = a.B * a.H;
+  const int L = blockIdx.x;
+  int pair, qt;
+  if (npair % 8 == 0) {
+    const int k = L >> 3;
+    pair = (L & 7) + 8 * (k / nqt);
+    qt = nqt - 1 - k % nqt;
+  } else {
+    pair = L % npair;
+    qt = nqt - 1 - L / npair;
+  }
+  const int h = pair % a.H, b = pair / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 5, c32 = lane & 31;
   const int N = a.N, H = a.H, s = a.s;
@@ -505,9 +521,13 @@ hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t st) {
   if (a.d_h == 64 && a.d_r == 32) {
     constexpr int nq = kPrefillQueryTiles;
-    prefill_attn_kernel<64, 32, nq><<<dim3(a.H, a.B, (a.N + 128 * nq - 1) / (128 * nq)), 256, 0, st>>>(a);
+    PrefillAttnArgs b = a;
+    b.nqt = (a.N + 128 * nq - 1) / (128 * nq);
+    prefill_attn_kernel<64, 32, nq><<<b.nqt * a.B * a.H, 256, 0, st>>>(b);
   } else if (a.d_h == 128 && a.d_r == 64) {
-    prefill_attn_kernel<128, 64, 1><<<dim3(a.H, a.B, (a.N + 127) / 128), 256, 0, st>>>(a);
+    PrefillAttnArgs b = a;
+    b.nqt = (a.N + 127) / 128;
+    prefill_attn_kernel<128, 64, 1><<<b.nqt * a.B * a.H, 256, 0, st>>>(b);
   } else {
     return hipErrorNotSupported;
   }
