@@ -256,6 +256,38 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
                      float* open_acc, void* out, void* workspace, size_t ws_bytes,
                      void* stream);
 
+/* Bytes of workspace mtla_prefill_at needs for n_tokens tokens after t0. */
+int32_t mtla_prefill_at_workspace_bytes(const mtla_dims* dims, int32_t t0, int32_t n_tokens,
+                                        size_t* bytes);
+
+/*
+ * Chunked prefill: tokens t0+1 .. t0+n_tokens of every sequence, after t0
+ * tokens already merged into `cache` and `open_acc` (by mtla_prefill,
+ * mtla_prefill_at or token-by-token merges; t0 need not end a block).  Page:
+ * "Multi-head Temporal Latent Attention", Key claims (paper Sec. 4.2
+ * Fig. 2(c), Sec. 4.3 Eq. 17) and Method (2)-(3): the same mask and keys as
+ * mtla_prefill with queries i = t0+1 .. t0+n_tokens; the block open at t0
+ * continues from its fp32 state, and completed slots written before the
+ * call are keys like the new ones.  The result equals token-by-token
+ * decoding of the same tokens.
+ *   t0 >= 0, uniform over the batch (0: the same as mtla_prefill).
+ *   q_c, q_r, c, k_r, out: the new tokens only, as for mtla_prefill with
+ *         N = n_tokens.
+ *   pe_rows >= t0 + n_tokens; t0 + n_tokens <= s * max_slots.
+ *   cache device [B, max_slots, d_c + d_r]: slots 1..ceil(t0/s) read (the
+ *         last one, if open, is rewritten), slots ..ceil((t0+n_tokens)/s)
+ *         written.
+ *   open_acc device [B, 2, d_c + d_r] fp32: [b, t0 % 2] read when t0 is not
+ *         at a block boundary; [b, (t0 + n_tokens) % 2] written.
+ *   workspace device, >= mtla_prefill_at_workspace_bytes(); scratch.  With
+ *         the MFMA path and t0 > 0 it holds K^C and V of every cache slot.
+ */
+int32_t mtla_prefill_at(const mtla_dims* dims, int32_t t0, int32_t n_tokens, const void* q_c,
+                        const void* q_r, const void* c, const void* k_r, const float* w_hyp,
+                        const float* pe, int32_t pe_rows, const void* w_uk, const void* w_uv,
+                        void* cache, float* open_acc, void* out, void* workspace, size_t ws_bytes,
+                        void* stream);
+
 /*
  * Test hooks: the integer predicates the kernels use, exported for bit-exact
  * comparison.  Page: "Multi-head Temporal Latent Attention", Key claims (paper

@@ -98,6 +98,8 @@ _SIGS = {
     "mtla_up_project": (_I, [_D, _I, _P, _P, _P, _P]),
     "mtla_prefill_workspace_bytes": (_I, [_D, _I, ctypes.POINTER(_SZ)]),
     "mtla_prefill": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mtla_prefill_at_workspace_bytes": (_I, [_D, _I, _I, ctypes.POINTER(_SZ)]),
+    "mtla_prefill_at": (_I, [_D, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_debug_stride_mask": (_I, [_I, _I, _P, _P]),
     "mtla_debug_slot_limits": (_I, [_I, _I, _P, _P]),
 }
@@ -319,6 +321,33 @@ def mtla_prefill(dims: MtlaDims, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_uv, cache,
     ws, ws_bytes = _ws("workspace", workspace, 0)
     _check(_lib.mtla_prefill(
         ctypes.byref(dims), N,
+        _tensor("q_c", q_c, (B, N, H, dims.d_h), st),
+        _tensor("q_r", q_r, (B, N, H, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("c", c, (B, N, dims.d_c), st),
+        _tensor("k_r", k_r, (B, N, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
+        _tensor("out", out, (B, N, H, dims.d_h), st),
+        ws, ws_bytes, _stream(stream)))
+
+
+def mtla_prefill_at_workspace_bytes(dims: MtlaDims, t0: int, n_tokens: int) -> int:
+    n = _SZ(0)
+    _check(_lib.mtla_prefill_at_workspace_bytes(ctypes.byref(dims), t0, n_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def mtla_prefill_at(dims: MtlaDims, t0: int, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_uv, cache,
+                    open_acc, out, workspace, stream=None) -> None:
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    N = int(c.shape[1]) if c.dim() == 3 else -1
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    _check(_lib.mtla_prefill_at(
+        ctypes.byref(dims), int(t0), N,
         _tensor("q_c", q_c, (B, N, H, dims.d_h), st),
         _tensor("q_r", q_r, (B, N, H, dims.d_r), st, optional=dims.d_r == 0),
         _tensor("c", c, (B, N, dims.d_c), st),

@@ -177,12 +177,16 @@ DecodeWs decode_ws(const mtla_dims* d) {
 }
 
 struct PrefillWs {
-  size_t P, kc, v, qlat, olat;
+  size_t P, kc, v, kslot, vslot, qlat, olat;
   AttnWs attn;
   size_t total;
 };
 
-PrefillWs prefill_ws(const mtla_dims* d, int n) {
+// Workspace of a prefill of n tokens after t0 cached ones.  The MFMA path
+// with t0 > 0 also holds K^C and V of every cache slot ([B, H, max_slots,
+// d_h] each): slot keys then come from the cache rows, not from this call's
+// partial merges.
+PrefillWs prefill_ws(const mtla_dims* d, int n, int t0 = 0) {
   const size_t B = d->batch, H = d->heads, W = d->d_c + d->d_r, N = n;
   const size_t e = elem_bytes(d);
   PrefillWs w{};
@@ -193,6 +197,13 @@ PrefillWs prefill_ws(const mtla_dims* d, int n) {
     off += align_up(B * H * N * d->d_h * e);
     w.v = off;
     off += align_up(B * H * N * d->d_h * e);
+    if (t0 > 0) {
+      const size_t S = d->max_slots;
+      w.kslot = off;
+      off += align_up(B * H * S * d->d_h * e);
+      w.vslot = off;
+      off += align_up(B * H * S * d->d_h * e);
+    }
     w.total = off;
   } else {
     const size_t R = B * N;
@@ -200,7 +211,7 @@ PrefillWs prefill_ws(const mtla_dims* d, int n) {
     off += align_up(R * H * W * 4);
     w.olat = off;
     off += align_up(R * H * d->d_c * 4);
-    w.attn = attn_ws(d, R, prefill_splits(d, n), off);
+    w.attn = attn_ws(d, R, prefill_splits(d, t0 + n), off);
     w.total = w.attn.total;
   }
   return w;
@@ -463,23 +474,33 @@ int32_t mtla_prefill_workspace_bytes(const mtla_dims* dims, int32_t n_tokens, si
   return ok();
 }
 
-int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, const void* q_r,
-                     const void* c, const void* k_r, const float* w_hyp, const float* pe,
-                     int32_t pe_rows, const void* w_uk, const void* w_uv, void* cache,
-                     float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream) {
+// Prefill of tokens t0+1 .. t0+n_tokens of every sequence (t0 = 0: from an
+// empty cache).
+static int32_t prefill_impl(const mtla_dims* dims, int32_t t0, int32_t n_tokens, const void* q_c,
+                            const void* q_r, const void* c, const void* k_r, const float* w_hyp,
+                            const float* pe, int32_t pe_rows, const void* w_uk, const void* w_uv,
+                            void* cache, float* open_acc, void* out, void* workspace, size_t ws_bytes,
+                            void* stream) {
   int32_t st = check_dims(dims);
   if (st != MTLA_OK) return st;
+  if (t0 < 0) return fail(MTLA_ERR_INVALID_ARG, "t0=%d < 0", t0);
   if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
-  if (pe_rows < n_tokens)
-    return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < n_tokens=%d", pe_rows, n_tokens);
-  if (int64_t(n_tokens) > int64_t(dims->max_slots) * dims->stride_s)
-    return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d exceeds the cache capacity s*max_slots", n_tokens);
+  const int64_t t_end = int64_t(t0) + n_tokens;
+  if (pe_rows < t_end)
+    return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < t0 + n_tokens = %lld", pe_rows, static_cast<long long>(t_end));
+  if (t_end > int64_t(dims->max_slots) * dims->stride_s)
+    return fail(MTLA_ERR_INVALID_ARG, "t0 + n_tokens = %lld exceeds the cache capacity s*max_slots",
+                static_cast<long long>(t_end));
   if (int64_t(dims->batch) * n_tokens * dims->heads * (dims->d_c + dims->d_r) > kMaxElems)
     return fail(MTLA_ERR_UNSUPPORTED, "prefill too large");
   // the partial merges [B, N, W] are read through a buffer resource (32-bit size)
   if (int64_t(dims->batch) * n_tokens * (dims->d_c + dims->d_r) * 4 > INT32_MAX)
     return fail(MTLA_ERR_UNSUPPORTED, "prefill of %d x %d tokens exceeds the 2^31-byte partial-merge buffer",
                 dims->batch, n_tokens);
+  // with t0 > 0 the cache rows of all sequences are one GEMM operand (32-bit size)
+  if (t0 > 0 && int64_t(dims->batch) * dims->max_slots * (dims->d_c + dims->d_r) * 2 > INT32_MAX)
+    return fail(MTLA_ERR_UNSUPPORTED, "cache of %d x %d slots exceeds the 2^31-byte operand buffer",
+                dims->batch, dims->max_slots);
   if (dims->batch == 0 || n_tokens == 0) return ok();
   CHECK_PTR(q_c);
   if (dims->d_r > 0) CHECK_PTR(q_r);
@@ -492,7 +513,7 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
   CHECK_PTR(cache);
   CHECK_PTR(open_acc);
   CHECK_PTR(out);
-  const PrefillWs ws = prefill_ws(dims, n_tokens);
+  const PrefillWs ws = prefill_ws(dims, n_tokens, t0);
   if (!workspace) return fail(MTLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws.total);
   if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   if (ws_bytes < ws.total)
@@ -502,7 +523,7 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
   const int B = dims->batch, H = dims->heads, N = n_tokens;
   void* P = at(workspace, ws.P);
   mtla::MergeArgs m{B, N, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, pe_rows,
-                    nullptr, c, k_r, w_hyp, pe, cache, open_acc, nullptr, P};
+                    nullptr, c, k_r, w_hyp, pe, cache, open_acc, nullptr, P, t0 + 1};
   hipError_t e = mtla::launch_merge(m, dims->dtype, s);
   if (e != hipSuccess) return hip_status(e, "prefill merge launch");
   if (prefill_fast(dims)) {
@@ -512,10 +533,26 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
     if (e != hipSuccess) return hip_status(e, "up-projection launch");
     mtla::PrefillAttnArgs pa{B, N, H, dims->d_h, dims->d_c, dims->d_r, dims->stride_s, 0,
                              dims->softmax_scale, q_c, q_r, kc, v, P, out};
+    if (t0 > 0) {
+      // slot keys from the cache rows (the merge has written this call's
+      // slots): K^C and V of every slot row by the same GEMM
+      void* ks = at(workspace, ws.kslot);
+      void* vs = at(workspace, ws.vslot);
+      e = mtla::launch_prefill_kv(B, dims->max_slots, H, dims->d_h, dims->d_c, dims->d_r, cache, w_uk, w_uv,
+                                  ks, vs, s);
+      if (e != hipSuccess) return hip_status(e, "slot up-projection launch");
+      pa.t0 = t0;
+      pa.kslot = ks;
+      pa.vslot = vs;
+      pa.rslot = cache;
+      pa.slot_rows = pa.rslot_rows = dims->max_slots;
+      pa.slot_mul = 1;
+      pa.slot_add = 0;
+    }
     return hip_status(mtla::launch_prefill_attn(pa, s), "prefill attention launch");
   }
   const int R = B * N;
-  const int splits = prefill_splits(dims, N);
+  const int splits = prefill_splits(dims, t0 + N);
   float* q_lat = reinterpret_cast<float*>(at(workspace, ws.qlat));
   float* o_lat = reinterpret_cast<float*>(at(workspace, ws.olat));
   mtla::Partials p{reinterpret_cast<float*>(at(workspace, ws.attn.pm)),
@@ -525,11 +562,37 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
                           dims->dtype, s);
   if (e != hipSuccess) return hip_status(e, "prefill absorb launch");
   mtla::AttendArgs a{R, N, H, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, splits,
-                     dims->softmax_scale, nullptr, q_lat, cache, P, p, o_lat};
+                     dims->softmax_scale, nullptr, q_lat, cache, P, p, o_lat, t0};
   e = mtla::launch_attend_portable(a, dims->dtype, s);
   if (e != hipSuccess) return hip_status(e, "prefill attention launch");
   e = mtla::launch_up_project(R, H, dims->d_h, dims->d_c, o_lat, w_uv, out, dims->dtype, s);
   return hip_status(e, "prefill up-projection launch");
+}
+
+int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, const void* q_r,
+                     const void* c, const void* k_r, const float* w_hyp, const float* pe,
+                     int32_t pe_rows, const void* w_uk, const void* w_uv, void* cache,
+                     float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  return prefill_impl(dims, 0, n_tokens, q_c, q_r, c, k_r, w_hyp, pe, pe_rows, w_uk, w_uv, cache, open_acc,
+                      out, workspace, ws_bytes, stream);
+}
+
+int32_t mtla_prefill_at_workspace_bytes(const mtla_dims* dims, int32_t t0, int32_t n_tokens, size_t* bytes) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (t0 < 0) return fail(MTLA_ERR_INVALID_ARG, "t0=%d < 0", t0);
+  if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
+  if (!bytes) return fail(MTLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = prefill_ws(dims, n_tokens, t0).total;
+  return ok();
+}
+
+int32_t mtla_prefill_at(const mtla_dims* dims, int32_t t0, int32_t n_tokens, const void* q_c,
+                        const void* q_r, const void* c, const void* k_r, const float* w_hyp,
+                        const float* pe, int32_t pe_rows, const void* w_uk, const void* w_uv, void* cache,
+                        float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  return prefill_impl(dims, t0, n_tokens, q_c, q_r, c, k_r, w_hyp, pe, pe_rows, w_uk, w_uv, cache, open_acc,
+                      out, workspace, ws_bytes, stream);
 }
 
 int32_t mtla_debug_stride_mask(int32_t n, int32_t s, uint8_t* mask, void* stream) {

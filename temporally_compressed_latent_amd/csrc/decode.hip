@@ -124,7 +124,7 @@ __device__ __forceinline__ KeySet key_set(const AttendArgs& a, int r) {
     k.diag = nullptr;
   } else {
     k.b = r / a.N;
-    const int i = r % a.N + 1;
+    const int i = a.t0 + r % a.N + 1;
     k.n = completed_slots(i, a.s);
     k.diag = static_cast<const T*>(a.diag) + static_cast<size_t>(r) * W;
     k.ok = true;

@@ -18,6 +18,7 @@ struct MergeArgs {
   float* open_acc;      // [B, 2, W]: state after token t at [b, t % 2]
   float* gate_out;      // [B, T] or nullptr
   void* partials;       // [B, T, W] cumulative in-block merges, or nullptr
+  int p0_all = 1;       // first appended token of every sequence when pos0 is nullptr
 };
 
 // Gate + temporal merge.  dtype: 0 fp32, 1 bf16.
@@ -50,6 +51,7 @@ struct AttendArgs {
   const void* diag;     // prefill: partial merges [B, N, W]; decode: nullptr
   Partials part;
   float* o_lat;         // [R, H, d_c] output (fp32)
+  int t0 = 0;           // prefill: tokens already in the cache (queries are t0+1 ..)
 };
 
 // Vector-ALU split attention + split merge (any shape, fp32 or bf16 storage).
@@ -106,6 +108,16 @@ struct PrefillAttnArgs {
   const void* v;         // [B, H, N, d_h]
   const void* partials;  // [B, N, W]  (rope keys P^R are its last d_r columns)
   void* out;             // [B, N, H, d_h]
+  // Queries are tokens t0+1 .. t0+N.  Keys of completed slot j (0-based):
+  // row slot_mul*j + slot_add of kslot / vslot ([B, H, slot_rows, d_h]) and
+  // of rslot ([B, rslot_rows, W], rope key in the last d_r columns).  Left
+  // null, they are the token-indexed kc / v / partials (slot j = token
+  // s*j + s - 1, t0 = 0).
+  int t0 = 0;
+  const void* kslot = nullptr;
+  const void* vslot = nullptr;
+  const void* rslot = nullptr;
+  int slot_rows = 0, rslot_rows = 0, slot_mul = 0, slot_add = 0;
 };
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t st);
 

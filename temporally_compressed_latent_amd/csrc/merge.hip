@@ -27,7 +27,7 @@ struct SeqRange {
 
 __device__ __forceinline__ SeqRange seq_range(const MergeArgs& a, int b) {
   SeqRange r;
-  r.p0 = a.pos0 ? a.pos0[b] : 1;
+  r.p0 = a.pos0 ? a.pos0[b] : a.p0_all;
   const long long tl = static_cast<long long>(r.p0) + a.T - 1;
   r.ok = r.p0 >= 1 && tl <= a.pe_rows;
   r.t_last = static_cast<int>(tl);

@@ -221,6 +221,14 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + (static_cast<size_t>(b) * H + h) * N * DH;
   const uint16_t* vv = static_cast<const uint16_t*>(a.v) + (static_cast<size_t>(b) * H + h) * N * DH;
   const uint16_t* Pb = static_cast<const uint16_t*>(a.partials) + static_cast<size_t>(b) * N * W;
+  // completed slot j (0-based) has its keys at row sm*j + sa of the slot
+  // arrays; the queries are tokens t0+1 .. t0+N
+  const int t0 = a.t0, sm = a.slot_mul, sa = a.slot_add;
+  const uint16_t* ksl =
+      static_cast<const uint16_t*>(a.kslot) + (static_cast<size_t>(b) * H + h) * a.slot_rows * DH;
+  const uint16_t* vsl =
+      static_cast<const uint16_t*>(a.vslot) + (static_cast<size_t>(b) * H + h) * a.slot_rows * DH;
+  const uint16_t* Rb = static_cast<const uint16_t*>(a.rslot) + static_cast<size_t>(b) * a.rslot_rows * W;
 
   // Queries (B operands, registers) and the diagonal key j = i as the initial
   // online-softmax state: m = score(i, i), l = 1, O = V_i.
@@ -275,43 +283,43 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 
   // completed slots seen by the workgroup's / this wave's last query, and the
   // slots every query of this wave sees
-  const int nk = (min(q0 + QT, N) - 1) / s;
-  const int nk_w = qw0 < N ? (min(qw0 + QW, N) - 1) / s : 0;
-  const int full_w = qw0 / s;
+  const int nk = (t0 + min(q0 + QT, N) - 1) / s;
+  const int nk_w = qw0 < N ? (t0 + min(qw0 + QW, N) - 1) / s : 0;
+  const int full_w = (t0 + qw0) / s;
 
   // Tile loads through buffer resources bounded at the last completed slot's
-  // token (s*nk tokens): slot rows past nk read as zero and touch no memory.
-  // Each load instruction uses one resource, so the chunks are split by kind:
-  // per thread KN chunks of K^C, RN of the rope key and KN of V (16 bytes
-  // each); their offsets within a tile are loop invariant and the tile offset
-  // is a scalar.  Slot j is token s*j + s - 1.
+  // key row (rows_end rows): slot rows past nk read as zero and touch no
+  // memory.  Each load instruction uses one resource, so the chunks are split
+  // by kind: per thread KN chunks of K^C, RN of the rope key and KN of V (16
+  // bytes each); their offsets within a tile are loop invariant and the tile
+  // offset is a scalar.
   constexpr int KN = TS * DH / 8 / 256, RN = TS * DR / 8 / 256;
   static_assert(KN * 256 == TS * DH / 8 && RN * 256 == TS * DR / 8, "chunks per thread");
-  const int tok_end = s * nk;
+  const int rows_end = nk > 0 ? sm * (nk - 1) + sa + 1 : 0;
   const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(kc), static_cast<short>(0), tok_end * DH * 2, kBufferRsrcWord3);
+      const_cast<uint16_t*>(ksl), static_cast<short>(0), rows_end * DH * 2, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(vv), static_cast<short>(0), tok_end * DH * 2, kBufferRsrcWord3);
+      const_cast<uint16_t*>(vsl), static_cast<short>(0), rows_end * DH * 2, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_r = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Pb + a.d_c), static_cast<short>(0),
-      tok_end > 0 ? (tok_end - 1) * W * 2 + DR * 2 : 0, kBufferRsrcWord3);
+      const_cast<uint16_t*>(Rb + a.d_c), static_cast<short>(0),
+      rows_end > 0 ? (rows_end - 1) * W * 2 + DR * 2 : 0, kBufferRsrcWord3);
   int off_k[KN], off_r[RN], lds_k[KN], lds_r[RN], lds_v[KN];
 #pragma unroll
   for (int i = 0; i < KN; ++i) {
     const int c = tid + 256 * i, row = c / (DH / 8), cc = c % (DH / 8);
-    off_k[i] = ((s * row + s - 1) * DH + cc * 8) * 2;
+    off_k[i] = ((sm * row + sa) * DH + cc * 8) * 2;
     lds_k[i] = row * KP + cc * 8;
     lds_v[i] = row * VP + cc * 8;
   }
 #pragma unroll
   for (int i = 0; i < RN; ++i) {
     const int c = tid + 256 * i, row = c / (DR / 8), cc = c % (DR / 8);
-    off_r[i] = ((s * row + s - 1) * W + cc * 8) * 2;
+    off_r[i] = ((sm * row + sa) * W + cc * 8) * 2;
     lds_r[i] = row * KP + DH + cc * 8;
   }
   uint4 pk[KN], pr[RN], pv[KN];
   auto load_tile = [&](int j0) {
-    const int so_kv = s * j0 * DH * 2, so_r = s * j0 * W * 2;
+    const int so_kv = sm * j0 * DH * 2, so_r = sm * j0 * W * 2;
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_k, off_k[i], so_kv, 0);
@@ -386,8 +394,9 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int slot = j0 + 32 * rt + 8 * (i / 4) + 4 * grp + (i % 4);
-              // completed slot (0-based) visible to query qi (0-based): s*(slot+1) <= qi
-              if (s * (slot + 1) > qi) sc[rt][t][i] = -INFINITY;
+              // completed slot (0-based) visible to query token t0 + qi + 1:
+              // s*(slot+1) <= t0 + qi
+              if (s * (slot + 1) > t0 + qi) sc[rt][t][i] = -INFINITY;
             }
           }
         }
@@ -518,7 +527,16 @@ hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t st) {
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a0, hipStream_t st) {
+  PrefillAttnArgs a = a0;
+  if (!a.kslot) {  // slot keys from the token-indexed arrays: slot j is token s*j + s - 1
+    a.kslot = a.kc;
+    a.vslot = a.v;
+    a.rslot = a.partials;
+    a.slot_rows = a.rslot_rows = a.N;
+    a.slot_mul = a.s;
+    a.slot_add = a.s - 1;
+  }
   if (a.d_h == 64 && a.d_r == 32) {
     constexpr int nq = kPrefillQueryTiles;
     PrefillAttnArgs b = a;

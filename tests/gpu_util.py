@@ -98,6 +98,18 @@ class Case:
         return out
 
 
+    def prefill_at(self, t0: int, n: int) -> torch.Tensor:
+        """mtla_prefill_at of tokens t0+1 .. t0+n (array rows t0 .. t0+n-1)."""
+        d = self.d
+        out = torch.empty(d.batch, n, d.heads, d.d_h, dtype=self.st, device=DEV)
+        ws = torch.empty(m.mtla_prefill_at_workspace_bytes(d, t0, n), dtype=torch.uint8, device=DEV)
+        sl = slice(t0, t0 + n)
+        m.mtla_prefill_at(d, t0, self.q_c[:, sl].contiguous(), self.q_r[:, sl].contiguous(),
+                          self.c[:, sl].contiguous(), self.k_r[:, sl].contiguous(), self.w_hyp,
+                          self.pe, self.w_uk, self.w_uv, self.cache, self.open_acc, out, ws)
+        return out
+
+
 # (H, d_h, d_c, d_r): the two layer shapes of the workloads, a padded-head
 # shape for the 32-row MFMA instance, and an odd shape only the portable
 # kernels take.

@@ -25,7 +25,7 @@ def dims(**kw):
 
 def test_exports_every_header_symbol():
     syms = m.header_symbols()
-    assert len(syms) == 17
+    assert len(syms) == 19
     for s in syms:
         assert hasattr(m.lib(), s), s
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
@@ -173,6 +173,28 @@ def test_prefill_argument_checks():
     assert call(ws=None) == m.MTLA_ERR_WORKSPACE
     assert call(n=need - 16) == m.MTLA_ERR_WORKSPACE
     assert call(N=0, cache=None, ws=None) == m.MTLA_OK
+
+
+def test_prefill_at_argument_checks():
+    L, d = m.lib(), dims()
+    need = m.mtla_prefill_at_workspace_bytes(d, 40, 32)
+    # continuing after cached tokens: the fast path also holds K^C and V of every slot
+    assert need > m.mtla_prefill_workspace_bytes(d, 32)
+    assert m.mtla_prefill_at_workspace_bytes(d, 0, 32) == m.mtla_prefill_workspace_bytes(d, 32)
+    call = lambda **k: L.mtla_prefill_at(
+        ctypes.byref(d), k.get("t0", 40), k.get("N", 32), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        k.get("pe_rows", 128), FAKE, FAKE, k.get("cache", FAKE), FAKE, FAKE, k.get("ws", FAKE),
+        k.get("n", need), None)
+    assert call(t0=-1) == m.MTLA_ERR_INVALID_ARG
+    assert call(N=-1) == m.MTLA_ERR_INVALID_ARG
+    assert call(t0=100, pe_rows=128) == m.MTLA_ERR_INVALID_ARG        # t0 + N = 132 > pe_rows
+    assert call(t0=240, pe_rows=400) == m.MTLA_ERR_INVALID_ARG        # 272 > s * max_slots = 256
+    assert call(cache=None) == m.MTLA_ERR_INVALID_ARG
+    assert call(ws=None) == m.MTLA_ERR_WORKSPACE
+    assert call(n=need - 16) == m.MTLA_ERR_WORKSPACE
+    assert call(N=0, cache=None, ws=None) == m.MTLA_OK
+    n = ctypes.c_size_t(0)
+    assert L.mtla_prefill_at_workspace_bytes(ctypes.byref(d), -1, 4, ctypes.byref(n)) == m.MTLA_ERR_INVALID_ARG
 
 
 def test_debug_hook_checks():

@@ -1,5 +1,6 @@
 """GPU: stride-masked parallel prefill (mtla_prefill) against the oracle's
-dense masked pass, and against the device's own token-by-token decode."""
+dense masked pass, and against the device's own token-by-token decode; chunked
+prefill (mtla_prefill_at) against the oracle's incremental loop."""
 import numpy as np
 import pytest
 import torch
@@ -83,3 +84,65 @@ def test_prefill_bit_reproducible():
     x = a.prefill(N).clone()
     y = a.prefill(N).clone()
     assert torch.equal(bits(x), bits(y))
+
+
+AT_CASES = [
+    # shape, dtype, portable, s, B, t0, N
+    ("st", "bf16", False, 3, 2, 100, 200),   # t0 inside a block (100 = 3*33 + 1)
+    ("st", "bf16", False, 2, 2, 128, 129),   # t0 at a block boundary
+    ("st", "bf16", False, 4, 1, 63, 1),      # one new token, block still open
+    ("st", "bf16", False, 3, 1, 2, 300),     # short prefix, long chunk
+    ("st", "bf16", True, 3, 2, 50, 60),
+    ("st", "fp32", False, 3, 1, 40, 50),
+    ("llm", "bf16", False, 2, 1, 70, 90),
+    ("odd", "bf16", False, 3, 2, 17, 20),
+]
+
+
+@pytest.mark.parametrize("shape,dtype,portable,s,B,t0,N", AT_CASES)
+def test_prefill_at_matches_oracle(shape, dtype, portable, s, B, t0, N):
+    """Prefill t0 tokens, then tokens t0+1 .. t0+N in one mtla_prefill_at
+    call: outputs, slot rows and the open-slot state follow the oracle's
+    token-by-token loop over all t0+N tokens."""
+    T = t0 + N
+    inp, g = make_case(shape, 12, B, T, s, dtype, portable)
+    g.prefill(t0)
+    out = host(g.prefill_at(t0, N))
+    cache, acc = host(g.cache), host(g.open_state(T))
+    n = oracle.num_slots(T, s)
+    for b in range(B):
+        want, slots = oracle_ref.incremental(inp, b, T, s, g.d.softmax_scale)
+        assert oracle.max_rel_err(out[b], want[t0:]) <= tol(dtype), b
+        assert oracle.max_rel_err(cache[b, :n], slots) <= tol(dtype), b
+        assert oracle.max_rel_err(acc[b], slots[n - 1].astype(np.float64)) <= tol(dtype), b
+
+
+@pytest.mark.parametrize("shape,s,cuts,portable", [("st", 3, (0, 97, 230, 301), False),
+                                                   ("st", 2, (0, 64, 65, 200), False),
+                                                   ("llm", 2, (0, 33, 96), False),
+                                                   ("st", 3, (0, 40, 101), True)])
+def test_prefill_in_chunks_equals_one_pass(shape, s, cuts, portable):
+    """Chunked prefill and one pass over the same tokens: the same cache bits
+    and open-slot state (the merge continues the open block from its fp32
+    state), outputs within tolerance."""
+    T = cuts[-1]
+    inp, a = make_case(shape, 13, 2, T, s, "bf16", portable)
+    _, b_ = make_case(shape, 13, 2, T, s, "bf16", portable)
+    one = host(a.prefill(T))
+    parts = [host(b_.prefill_at(lo, hi - lo)) for lo, hi in zip(cuts[:-1], cuts[1:])]
+    assert torch.equal(bits(a.cache), bits(b_.cache))
+    assert torch.equal(a.open_state(T), b_.open_state(T))
+    assert oracle.max_rel_err(np.concatenate(parts, axis=1), one) <= 1e-2
+
+
+def test_prefill_at_then_decode_continues():
+    """Chunked prefill, then token-by-token decoding: the outputs follow the
+    oracle's incremental loop."""
+    B, s, T = 2, 3, 180
+    inp, g = make_case("st", 14, B, T, s, "bf16")
+    g.prefill(50)
+    g.prefill_at(50, 71)
+    cont = host(g.decode_loop(T, start=121))
+    for b in range(B):
+        want, _ = oracle_ref.incremental(inp, b, T, s, g.d.softmax_scale)
+        assert oracle.max_rel_err(cont[b], want[121:]) <= 1e-2, b
