@@ -12,8 +12,10 @@ The 512 launches of a step are captured once in a HIP graph and replayed;
 inputs are resident in HBM before the timed region.
 
 The other workloads are reported in ``components``: the s=4 decode loop
-(2048 tokens), the summarisation-shaped prefill (B=16, N=4096, s=3) and the
-LLM-scale step (B=64, cache of 32,768 tokens, one append + decode).
+(2048 tokens), the summarisation-shaped prefill (B=16, N=4096, s=3), the same
+prefill's second half as one chunked call after the first half
+(mtla_prefill_at), and the LLM-scale step (B=64, cache of 32,768 tokens, one
+append + decode).
 
 ``roofline`` describes the dominant kernel of the headline step: the fused
 decode-step kernel, the step's only kernel, so its average launch duration is
@@ -42,8 +44,8 @@ def parse_args():
     p.add_argument("--no-components", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default=None,
-                   help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, llm_decode, "
-                        "copy: the counter-calibration copy kernel)")
+                   help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, "
+                        "prefill_chunk, llm_decode, copy: the counter-calibration copy kernel)")
     return p.parse_args()
 
 
@@ -211,6 +213,50 @@ def run_prefill(w, steps, warmup, m, torch, workloads):
             "attn_gflop": f_attn / 1e9, "kv_gemm_gflop": f_up / 1e9,
             "tflops_end_to_end": (f_attn + f_up) / (ms * 1e-3) / 1e12,
             "attn_tflops_over_end_to_end_time": f_attn / (ms * 1e-3) / 1e12}, (out, q_c, q_r, lat, qry, wts)
+
+
+def run_prefill_chunk(w, steps, warmup, m, torch, workloads):
+    """Chunked prefill of the summarisation shape: the first t0 tokens by
+    mtla_prefill (untimed), then tokens t0+1..N by one mtla_prefill_at call
+    (timed, replayed from a graph).  t0 ends a block, so every replay reads the
+    same cache rows and no open-slot state."""
+    B, N, H, s = w.batch, w.n_tokens, w.heads, w.s
+    t0 = (N // 2) // s * s
+    n2 = N - t0
+    log(f"{w.name} chunked: staging inputs (t0={t0}, chunk={n2})")
+    d = m.make_dims(B, H, w.d_h, w.d_c, w.d_r, s, -(-N // s), "bf16")
+    lat, qry, wts = workloads.batch_latents(w), workloads.batch_queries(w), workloads.weights(w)
+    bf = torch.bfloat16
+    c, k_r = to_dev(lat["c"], bf, torch), to_dev(lat["k_r"], bf, torch)
+    q_c, q_r = to_dev(qry["q_c"], bf, torch), to_dev(qry["q_r"], bf, torch)
+    w_hyp = to_dev(wts["w_hyp"], torch.float32, torch)
+    w_uk, w_uv = to_dev(wts["w_uk"], bf, torch), to_dev(wts["w_uv"], bf, torch)
+    pe = torch.empty(N, w.d_c, dtype=torch.float32, device="cuda")
+    m.mtla_sinusoidal_pe(pe)
+    cache = torch.zeros(B, d.max_slots, d.width, dtype=bf, device="cuda")
+    open_acc = torch.zeros(B, 2, d.width, dtype=torch.float32, device="cuda")
+    out1 = torch.empty(B, t0, H, w.d_h, dtype=bf, device="cuda")
+    out2 = torch.empty(B, n2, H, w.d_h, dtype=bf, device="cuda")
+    ws1 = torch.empty(m.mtla_prefill_workspace_bytes(d, t0), dtype=torch.uint8, device="cuda")
+    m.mtla_prefill(d, q_c[:, :t0].contiguous(), q_r[:, :t0].contiguous(), c[:, :t0].contiguous(),
+                   k_r[:, :t0].contiguous(), w_hyp, pe, w_uk, w_uv, cache, open_acc, out1, ws1)
+    del ws1
+    ws = torch.empty(m.mtla_prefill_at_workspace_bytes(d, t0, n2), dtype=torch.uint8, device="cuda")
+    args2 = [x[:, t0:].contiguous() for x in (q_c, q_r, c, k_r)]
+
+    def fn():
+        m.mtla_prefill_at(d, t0, *args2, w_hyp, pe, w_uk, w_uv, cache, open_acc, out2, ws)
+    g = capture(fn, torch)
+    for _ in range(warmup):
+        g.replay()
+    ms = timed_graph(g, steps, torch)
+    A = attended_pairs(N, s) - attended_pairs(t0, s)
+    f_attn = 2.0 * B * H * A * (2 * w.d_h + w.d_r)
+    f_up = 4.0 * B * (n2 + d.max_slots) * w.d_c * H * w.d_h
+    return {"workload": w.name + "_chunk2", "t0": t0, "tokens": n2, "ms_per_call": ms,
+            "attended_pairs_per_bh": A, "attn_gflop": f_attn / 1e9, "kv_gemm_gflop": f_up / 1e9,
+            "tflops_end_to_end": (f_attn + f_up) / (ms * 1e-3) / 1e12,
+            "attn_tflops_over_end_to_end_time": f_attn / (ms * 1e-3) / 1e12}
 
 
 # ---------------------------------------------------------------------------
@@ -397,6 +443,7 @@ def main():
         fn = {"st_decode_s2": lambda: run_decode_loop(W[1], args.steps, args.warmup, m, torch, workloads)[0],
               "st_decode_s4": lambda: run_decode_loop(W[2], args.steps, args.warmup, m, torch, workloads)[0],
               "prefill": lambda: run_prefill(W[3], args.steps, args.warmup, m, torch, workloads)[0],
+              "prefill_chunk": lambda: run_prefill_chunk(W[3], args.steps, args.warmup, m, torch, workloads),
               "llm_decode": lambda: run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0],
               "copy": lambda: run_copy(args.steps, args.warmup, torch)}
         print(json.dumps(fn[args.only]()), flush=True)
@@ -412,6 +459,10 @@ def main():
         torch.cuda.empty_cache()
         comps["sum_prefill_b16_n4096_s3"] = run_prefill(W[3], args.steps, args.warmup, m, torch, workloads)[0]
         log("prefill:", json.dumps(comps["sum_prefill_b16_n4096_s3"]))
+        torch.cuda.empty_cache()
+        comps["sum_prefill_b16_n4096_s3_chunk2"] = run_prefill_chunk(W[3], args.steps, args.warmup, m, torch,
+                                                                     workloads)
+        log("prefill chunk:", json.dumps(comps["sum_prefill_b16_n4096_s3_chunk2"]))
         torch.cuda.empty_cache()
         comps["llm_decode_b64_n32768_s2"] = run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0]
         log("llm:", json.dumps(comps["llm_decode_b64_n32768_s2"]))
