@@ -13,6 +13,8 @@ Sources (web pages on MTLA; cited by page title and section):
   [MLA-expl]   "Multi-Head Latent Attention and Sparse Indexers": "Latent
                attention changes the representation" (absorption algebra) and
                "Work the bytes with units and scope" (row bytes).
+  [MTLA-repo]  The MTLA repository summary page, "Highlighted Details"
+               (evaluation with Fairseq-style parallel beam search).
 
 Indexing.  Tokens and slots are 1-based in the formulas (t, i, j in 1..N;
 slot b in 1..ceil(N/s)), as the pages write ceil(t/s).  Arrays are 0-based;
@@ -222,6 +224,41 @@ def partial_merges(x: np.ndarray, w: np.ndarray, s: int) -> np.ndarray:
             acc = acc + w[k - 1] * x[k - 1]
         P[j - 1] = acc
     return P
+
+
+# ---------------------------------------------------------------------------
+# Beam reorder: the decode state follows the surviving hypotheses
+# ---------------------------------------------------------------------------
+
+def reorder_state(cache: np.ndarray, open_state: np.ndarray, pos: np.ndarray, src: np.ndarray,
+                  s: int):
+    """Beam-search reorder of the per-sequence decode state.
+
+    [MTLA-repo] "Highlighted Details": the models are evaluated with
+    Fairseq-style parallel beam search, where after each step every kept
+    hypothesis b continues hypothesis src[b] (a parent may be kept several
+    times, or dropped).  The state a hypothesis carries is its slot cache
+    (slots 1..ceil(pos/s)), its open-slot fp32 value and its token count, so
+    the reorder is a gather:
+
+        cache'[b, :ceil(pos[src[b]]/s)] = cache[src[b], :ceil(pos[src[b]]/s)]
+        open'[b] = open[src[b]],   pos'[b] = pos[src[b]].
+
+    cache: [B, S, W]; open_state: [B, ...]; pos, src: [B] ints.  Rows of
+    cache' past the copied slots are zero (they are never read).
+    """
+    cache = np.asarray(cache)
+    B = cache.shape[0]
+    out = np.zeros_like(cache)
+    open_out = np.empty_like(np.asarray(open_state))
+    pos_out = np.empty(B, dtype=np.int64)
+    for b in range(B):
+        a = int(src[b])
+        n = num_slots(int(pos[a]), s) if pos[a] > 0 else 0
+        out[b, :n] = cache[a, :n]
+        open_out[b] = open_state[a]
+        pos_out[b] = pos[a]
+    return out, open_out, pos_out
 
 
 # ---------------------------------------------------------------------------

@@ -330,6 +330,43 @@ def pin_layer_schedules(o):
     assert np.all(o.layer(h, p0, H, d_h, d_r, s, 0.4) == 0)
 
 
+def pin_beam_reorder_follows_history(o):
+    """A reordered hypothesis carries its parent's state: its slots are the
+    merge of the parent's token history (built here from that history, not
+    by gathering), the unused rows stay zero, and appending a new token to
+    the reordered state equals merging parent history + token from scratch."""
+    g = np.random.default_rng(21)
+    for s in (1, 2, 3, 5):
+        B, W = 6, 4
+        lens = g.integers(1, 4 * s + 3, size=B)
+        S = o.num_slots(int(lens.max()) + 1, s)
+        hist = [g.standard_normal((int(n), W)) for n in lens]
+        gates = [g.uniform(0.1, 0.9, int(n)) for n in lens]
+        cache = np.zeros((B, S, W))
+        open_state = np.zeros((B, W))
+        for b in range(B):
+            m = o.merge_incremental(hist[b], gates[b], s)
+            cache[b, :m.shape[0]] = m
+            open_state[b] = m[-1]
+        src = g.integers(0, B, size=B)
+        src[0] = src[1]                          # a parent kept twice
+        out, open_out, pos_out = o.reorder_state(cache, open_state, lens, src, s)
+        for b in range(B):
+            a = int(src[b])
+            want = o.merge_incremental(hist[a], gates[a], s)
+            n = want.shape[0]
+            np.testing.assert_allclose(out[b, :n], want, rtol=0, atol=1e-12)
+            assert not out[b, n:].any()
+            assert pos_out[b] == lens[a]
+            np.testing.assert_allclose(open_out[b], want[-1], rtol=0, atol=1e-12)
+            x_new, w_new = g.standard_normal(W), 0.6
+            grown = np.zeros((o.num_slots(int(lens[a]) + 1, s), W))
+            grown[:n] = out[b, :n]
+            o.append_token(grown, x_new, w_new, int(lens[a]) + 1, s)
+            ref = o.merge_incremental(np.vstack([hist[a], x_new]), np.append(gates[a], w_new), s)
+            np.testing.assert_allclose(grown, ref, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_slot_index, pin_block_starts, pin_slot_count, pin_mask_special_cases,
     pin_mask_structure, pin_mask_matches_incremental_cache, pin_cache_ratio,
@@ -337,4 +374,5 @@ ALL_PINS = [
     pin_uniform_attention_keyset, pin_absorption, pin_decode_single_slot,
     pin_s1_equals_causal_sdpa, pin_parallel_equals_incremental,
     pin_prefill_query_rows, pin_rope, pin_pe, pin_layer_schedules,
+    pin_beam_reorder_follows_history,
 ]

@@ -88,8 +88,35 @@ def _row_bytes_no_rope(d_c, d_r, e):
     return d_c * e
 
 
+def _reorder_own_length(cache, open_state, pos, src, s):
+    # copies as many slots as the destination held before, not its parent
+    out, op, po = _ORIG["reorder_state"](cache, open_state, pos, np.arange(len(src)), s)
+    for b in range(len(src)):
+        a = int(src[b])
+        n = O.num_slots(int(pos[b]), s) if pos[b] > 0 else 0
+        out[b] = 0
+        out[b, :n] = cache[a, :n]
+        op[b] = open_state[a]
+        po[b] = pos[a]
+    return out, op, po
+
+
+def _reorder_scatter(cache, open_state, pos, src, s):
+    # treats src as destinations (scatter) instead of parents (gather)
+    out = np.zeros_like(cache)
+    op = np.empty_like(open_state)
+    po = np.empty(len(src), dtype=np.int64)
+    for a in range(len(src)):
+        b = int(src[a])
+        n = O.num_slots(int(pos[a]), s)
+        out[b, :n] = cache[a, :n]
+        op[b] = open_state[a]
+        po[b] = pos[a]
+    return out, op, po
+
+
 _ORIG = {name: getattr(O, name) for name in
-         ("decode_absorbed", "rope", "sinusoidal_pe")}
+         ("decode_absorbed", "rope", "sinusoidal_pe", "reorder_state")}
 
 MUTATIONS = {
     "visible_keys": [_visible_keys_block_starts, _visible_keys_off_by_one, _visible_keys_no_diag],
@@ -104,6 +131,7 @@ MUTATIONS = {
     "sinusoidal_pe": [_pe_swapped],
     "cache_elements_per_token": [_cache_elements_floor],
     "cache_row_bytes": [_row_bytes_no_rope],
+    "reorder_state": [_reorder_own_length, _reorder_scatter],
 }
 
 CASES = [(name, fn) for name, fns in MUTATIONS.items() for fn in fns]
