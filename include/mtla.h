@@ -289,6 +289,28 @@ int32_t mtla_prefill_at(const mtla_dims* dims, int32_t t0, int32_t n_tokens, con
                         void* stream);
 
 /*
+ * Beam-search reorder of the decode state, out of place.  Page: the MTLA
+ * repository summary, "Highlighted Details" (models are evaluated with
+ * Fairseq-style parallel beam search: after a step every kept hypothesis b
+ * continues hypothesis src[b]; a parent may be kept several times or
+ * dropped).  Destination b receives
+ *   cache_out[b, 0 .. ceil(pos[src[b]]/s) - 1] = cache_in[src[b], same rows]
+ *   open_out[b] = open_in[src[b]]            (both parity rows)
+ *   pos_out[b] = pos[src[b]]                 (when pos_out is not NULL)
+ * Rows of cache_out past the copied slots are untouched.  A destination
+ * whose src is outside [0, B) is left untouched.
+ *   src     device [B] int32, parent index per destination.
+ *   pos     device [B] int32, tokens each sequence holds before the reorder.
+ *   cache_in, cache_out  device [B, max_slots, d_c + d_r] storage dtype.
+ *   open_in, open_out    device [B, 2, d_c + d_r] fp32.
+ *   pos_out device [B] int32 or NULL.
+ * The outputs must not alias the inputs (checked for equal pointers only).
+ */
+int32_t mtla_reorder_state(const mtla_dims* dims, const int32_t* src, const int32_t* pos,
+                           const void* cache_in, const float* open_in, void* cache_out,
+                           float* open_out, int32_t* pos_out, void* stream);
+
+/*
  * Test hooks: the integer predicates the kernels use, exported for bit-exact
  * comparison.  Page: "Multi-head Temporal Latent Attention", Key claims (paper
  * Sec. 4.2 Fig. 2(c)).

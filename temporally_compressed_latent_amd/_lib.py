@@ -99,6 +99,7 @@ _SIGS = {
     "mtla_prefill_workspace_bytes": (_I, [_D, _I, ctypes.POINTER(_SZ)]),
     "mtla_prefill": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_prefill_at_workspace_bytes": (_I, [_D, _I, _I, ctypes.POINTER(_SZ)]),
+    "mtla_reorder_state": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "mtla_prefill_at": (_I, [_D, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_debug_stride_mask": (_I, [_I, _I, _P, _P]),
     "mtla_debug_slot_limits": (_I, [_I, _I, _P, _P]),
@@ -360,6 +361,21 @@ def mtla_prefill_at(dims: MtlaDims, t0: int, q_c, q_r, c, k_r, w_hyp, pe, w_uk, 
         _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
         _tensor("out", out, (B, N, H, dims.d_h), st),
         ws, ws_bytes, _stream(stream)))
+
+
+def mtla_reorder_state(dims: MtlaDims, src, pos, cache_in, open_in, cache_out, open_out,
+                       pos_out=None, stream=None) -> None:
+    B, st = dims.batch, dims.torch_dtype
+    _check(_lib.mtla_reorder_state(
+        ctypes.byref(dims),
+        _tensor("src", src, (B,), torch.int32),
+        _tensor("pos", pos, (B,), torch.int32),
+        _tensor("cache_in", cache_in, (B, dims.max_slots, dims.width), st),
+        _tensor("open_in", open_in, (B, 2, dims.width), torch.float32),
+        _tensor("cache_out", cache_out, (B, dims.max_slots, dims.width), st),
+        _tensor("open_out", open_out, (B, 2, dims.width), torch.float32),
+        _tensor("pos_out", pos_out, (B,), torch.int32, optional=True),
+        _stream(stream)))
 
 
 def mtla_debug_stride_mask(n: int, s: int, mask, stream=None) -> None:

@@ -273,6 +273,28 @@ int32_t mtla_merge_append(const mtla_dims* dims, const int32_t* pos0, int32_t n_
                     "merge launch");
 }
 
+int32_t mtla_reorder_state(const mtla_dims* dims, const int32_t* src, const int32_t* pos,
+                           const void* cache_in, const float* open_in, void* cache_out, float* open_out,
+                           int32_t* pos_out, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (dims->batch == 0) return ok();
+  CHECK_PTR_ALIGN(src, 4);
+  CHECK_PTR_ALIGN(pos, 4);
+  CHECK_PTR(cache_in);
+  CHECK_PTR(cache_out);
+  CHECK_PTR_ALIGN(open_in, 4);
+  CHECK_PTR_ALIGN(open_out, 4);
+  CHECK_OPT_PTR_ALIGN(pos_out, 4);
+  if (cache_in == cache_out || open_in == open_out || (pos_out && pos_out == pos))
+    return fail(MTLA_ERR_INVALID_ARG, "the reorder is out of place: outputs must not be the inputs");
+  const int W = dims->d_c + dims->d_r;
+  const int row_bytes = W * static_cast<int>(elem_bytes(dims));
+  mtla::ReorderArgs a{dims->batch, dims->stride_s, dims->max_slots, row_bytes, 2 * W, src, pos,
+                      cache_in, cache_out, open_in, open_out, pos_out};
+  return hip_status(mtla::launch_reorder(a, static_cast<hipStream_t>(stream)), "reorder launch");
+}
+
 int32_t mtla_absorb_query(const mtla_dims* dims, int32_t n_rows, const void* q_c, const void* q_r,
                           const void* w_uk, float* q_lat, void* stream) {
   int32_t st = check_dims(dims);

@@ -24,6 +24,23 @@ struct MergeArgs {
 // Gate + temporal merge.  dtype: 0 fp32, 1 bf16.
 hipError_t launch_merge(const MergeArgs& a, int dtype, hipStream_t st);
 
+// Beam reorder of the decode state (out of place): destination b takes the
+// slots 1..ceil(pos[src[b]]/s), both open-slot rows and the token count of
+// sequence src[b].
+struct ReorderArgs {
+  int B, s, max_slots;
+  int row_bytes;         // bytes of one cache row, (d_c + d_r) * element size
+  int open_floats;       // floats of one sequence's open-slot state (2 * W)
+  const int32_t* src;    // [B]
+  const int32_t* pos;    // [B] tokens held by each sequence before the reorder
+  const void* cache_in;  // [B, max_slots, W]
+  void* cache_out;
+  const float* open_in;  // [B, 2, W]
+  float* open_out;
+  int32_t* pos_out;      // [B] or nullptr
+};
+hipError_t launch_reorder(const ReorderArgs& a, hipStream_t st);
+
 hipError_t launch_sinusoidal_pe(int rows, int d, float* pe, hipStream_t st);
 hipError_t launch_debug_mask(int n, int s, uint8_t* mask, hipStream_t st);
 hipError_t launch_debug_limits(int n, int s, int32_t* hi, hipStream_t st);

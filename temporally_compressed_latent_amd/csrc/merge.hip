@@ -233,6 +233,50 @@ __global__ __launch_bounds__(kMergeThreads) void merge_tail_kernel(MergeArgs a) 
   store8(a.open_acc + (static_cast<size_t>(b) * 2 + r.t_last % 2) * W + e, acc);
 }
 
+// Beam reorder ([MTLA-repo]: evaluation by Fairseq-style parallel beam
+// search; a kept hypothesis b continues hypothesis src[b]).  One workgroup
+// per (destination b, run of kReorderSlots slots); 16-byte units (d_c and d_r
+// are multiples of 8, so a row is), four units in flight per thread.  The
+// x == 0 workgroup also copies the open-slot state and the token count.  A
+// destination whose parent index is out of range is left untouched.
+constexpr int kReorderSlots = 64;
+
+template <typename U>
+__global__ __launch_bounds__(256) void reorder_kernel(ReorderArgs a) {
+  const int b = blockIdx.y;
+  const int parent = a.src[b];
+  if (parent < 0 || parent >= a.B) return;
+  const int p = a.pos[parent];
+  int n = p >= 1 ? slot_of(p, a.s) : 0;
+  if (n > a.max_slots) n = a.max_slots;
+  const int r0 = blockIdx.x * kReorderSlots;
+  const int r1 = min(n, r0 + kReorderSlots);
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < a.open_floats; i += blockDim.x)
+      a.open_out[static_cast<size_t>(b) * a.open_floats + i] = a.open_in[static_cast<size_t>(parent) * a.open_floats + i];
+    if (a.pos_out && threadIdx.x == 0) a.pos_out[b] = p;
+  }
+  if (r0 >= r1) return;
+  const size_t seq_bytes = static_cast<size_t>(a.max_slots) * a.row_bytes;
+  const U* in = reinterpret_cast<const U*>(static_cast<const char*>(a.cache_in) + parent * seq_bytes +
+                                           static_cast<size_t>(r0) * a.row_bytes);
+  U* out = reinterpret_cast<U*>(static_cast<char*>(a.cache_out) + b * seq_bytes +
+                                static_cast<size_t>(r0) * a.row_bytes);
+  const int units = (r1 - r0) * (a.row_bytes / static_cast<int>(sizeof(U)));
+  constexpr int K = 4;
+  for (int i0 = threadIdx.x; i0 < units; i0 += K * 256) {
+    U v[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int i = min(i0 + k * 256, units - 1);
+      v[k] = in[i];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (i0 + k * 256 < units) out[i0 + k * 256] = v[k];
+  }
+}
+
 __global__ void pe_kernel(int rows, int d, float* pe) {
   const size_t n = static_cast<size_t>(rows) * d;
   for (size_t idx = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; idx < n;
@@ -287,6 +331,13 @@ hipError_t launch_merge(const MergeArgs& a, int dtype, hipStream_t st) {
     merge_kernel<uint16_t><<<grid, kMergeThreads, 0, st>>>(a, blocks_per_wg, write_open);
     if (!write_open) merge_tail_kernel<uint16_t><<<a.B, kMergeThreads, 0, st>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_reorder(const ReorderArgs& a, hipStream_t st) {
+  if (a.row_bytes % 16 != 0) return hipErrorInvalidValue;
+  dim3 grid((a.max_slots + kReorderSlots - 1) / kReorderSlots, a.B);
+  reorder_kernel<uint4><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ def dims(**kw):
 
 def test_exports_every_header_symbol():
     syms = m.header_symbols()
-    assert len(syms) == 19
+    assert len(syms) == 20
     for s in syms:
         assert hasattr(m.lib(), s), s
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
@@ -195,6 +195,24 @@ def test_prefill_at_argument_checks():
     assert call(N=0, cache=None, ws=None) == m.MTLA_OK
     n = ctypes.c_size_t(0)
     assert L.mtla_prefill_at_workspace_bytes(ctypes.byref(d), -1, 4, ctypes.byref(n)) == m.MTLA_ERR_INVALID_ARG
+
+
+def test_reorder_argument_checks():
+    L, d = m.lib(), dims()
+    A = FAKE
+    B_ = FAKE + 4096
+    call = lambda **k: L.mtla_reorder_state(
+        ctypes.byref(d), k.get("src", A), k.get("pos", A), k.get("ci", A), k.get("oi", A),
+        k.get("co", B_), k.get("oo", B_), k.get("po", None), None)
+    assert call(src=None) == m.MTLA_ERR_INVALID_ARG
+    assert call(pos=None) == m.MTLA_ERR_INVALID_ARG
+    assert call(ci=None) == m.MTLA_ERR_INVALID_ARG
+    assert call(co=A) == m.MTLA_ERR_INVALID_ARG          # in place
+    assert call(oo=A) == m.MTLA_ERR_INVALID_ARG          # in place
+    assert call(po=A) == m.MTLA_ERR_INVALID_ARG          # pos_out aliases pos
+    assert call(co=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
+    d0 = dims(batch=0)
+    assert L.mtla_reorder_state(ctypes.byref(d0), None, None, None, None, None, None, None, None) == m.MTLA_OK
 
 
 def test_debug_hook_checks():
