@@ -14,8 +14,9 @@ inputs are resident in HBM before the timed region.
 The other workloads are reported in ``components``: the s=4 decode loop
 (2048 tokens), the summarisation-shaped prefill (B=16, N=4096, s=3), the same
 prefill's second half as one chunked call after the first half
-(mtla_prefill_at), and the LLM-scale step (B=64, cache of 32,768 tokens, one
-append + decode).
+(mtla_prefill_at), the LLM-scale step (B=64, cache of 32,768 tokens, one
+append + decode), and a beam-search reorder of that LLM-scale decode state
+(mtla_reorder_state).
 
 ``roofline`` describes the dominant kernel of the headline step: the fused
 decode-step kernel, the step's only kernel, so its average launch duration is
@@ -45,7 +46,7 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default=None,
                    help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, "
-                        "prefill_chunk, llm_decode, copy: the counter-calibration copy kernel)")
+                        "prefill_chunk, llm_decode, reorder, copy: the counter-calibration copy kernel)")
     return p.parse_args()
 
 
@@ -259,6 +260,34 @@ def run_prefill_chunk(w, steps, warmup, m, torch, workloads):
             "attn_tflops_over_end_to_end_time": f_attn / (ms * 1e-3) / 1e12}
 
 
+def run_reorder(w, steps, warmup, m, torch):
+    """Beam-search reorder of a full decode state at the LLM shape: every
+    sequence holds N+1 tokens (16,385 slots); each destination takes a random
+    parent.  Pure data movement: the slot rows are read once and written once
+    (cache contents are random, their values do not matter to a copy)."""
+    B, N, H = w.batch, w.n_tokens, w.heads
+    T = N + 1
+    d = m.make_dims(B, H, w.d_h, w.d_c, w.d_r, w.s, -(-T // w.s), "bf16")
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    cache_in = torch.randn(B, d.max_slots, d.width, device="cuda", generator=gen).to(torch.bfloat16)
+    cache_out = torch.empty_like(cache_in)
+    open_in = torch.randn(B, 2, d.width, device="cuda", generator=gen)
+    open_out = torch.empty_like(open_in)
+    pos = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    pos_out = torch.empty_like(pos)
+    src = torch.randint(0, B, (B,), dtype=torch.int32, device="cuda", generator=gen)
+
+    def fn():
+        m.mtla_reorder_state(d, src, pos, cache_in, open_in, cache_out, open_out, pos_out)
+    g = capture(fn, torch)
+    for _ in range(warmup):
+        g.replay()
+    ms = timed_graph(g, steps, torch)
+    moved = 2 * B * (-(-T // w.s)) * d.width * 2 + 2 * B * 2 * d.width * 4
+    return {"workload": "beam_reorder_" + w.name, "ms_per_call": ms, "bytes_moved": moved,
+            "GBps": moved / (ms * 1e-3) / 1e9, "frac_hbm": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 # ---------------------------------------------------------------------------
 # LLM-scale long-context step
 # ---------------------------------------------------------------------------
@@ -444,6 +473,7 @@ def main():
               "st_decode_s4": lambda: run_decode_loop(W[2], args.steps, args.warmup, m, torch, workloads)[0],
               "prefill": lambda: run_prefill(W[3], args.steps, args.warmup, m, torch, workloads)[0],
               "prefill_chunk": lambda: run_prefill_chunk(W[3], args.steps, args.warmup, m, torch, workloads),
+              "reorder": lambda: run_reorder(W[4], args.steps, args.warmup, m, torch),
               "llm_decode": lambda: run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0],
               "copy": lambda: run_copy(args.steps, args.warmup, torch)}
         print(json.dumps(fn[args.only]()), flush=True)
@@ -466,6 +496,9 @@ def main():
         torch.cuda.empty_cache()
         comps["llm_decode_b64_n32768_s2"] = run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0]
         log("llm:", json.dumps(comps["llm_decode_b64_n32768_s2"]))
+        torch.cuda.empty_cache()
+        comps["beam_reorder_llm_decode_b64_n32768_s2"] = run_reorder(W[4], args.steps, args.warmup, m, torch)
+        log("reorder:", json.dumps(comps["beam_reorder_llm_decode_b64_n32768_s2"]))
     cpu, err = (None, None)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
