@@ -311,6 +311,75 @@ int32_t mtla_reorder_state(const mtla_dims* dims, const int32_t* src, const int3
                            float* open_out, int32_t* pos_out, void* stream);
 
 /*
+ * The decoder layer around the MTLA core.  Page: "Multi-head Temporal Latent
+ * Attention", Method (the latent c_t = W_DKV h_t is what is merged and
+ * cached; decoupled RoPE keys as in MLA), and "Multi-Head Latent Attention and
+ * Sparse Indexers", "Latent attention changes the representation" (queries
+ * and the output projection W_O over the heads).  Per token t of sequence b:
+ *   c_t = W_DKV h_t;  [q^C_t,h ; q^R_t,h] = (W_Q h_t) split per head;
+ *   k^R_t = W_R h_t;  q^R and k^R rotated by RoPE at position t-1:
+ *     interleaved pairs (2k, 2k+1) turned by (t-1) * 10000^(-2k/d_r);
+ *   y_t = W_O [o_t,1 ; ... ; o_t,H].
+ * Weights (storage dtype, row-major): w_dkv [d_c, d_model];
+ * w_q [H * (d_h + d_r), d_model] (per head the d_h query rows, then the d_r
+ * rope rows); w_r [d_r, d_model]; w_o [d_model, H * d_h].
+ * d_model and H * d_h must be multiples of 8, d_h even.
+ *
+ * mtla_project_inputs: the input projections of n_tokens consecutive tokens
+ * of every sequence; row t of sequence b is token pos0[b] + t.
+ *   pos0 device [B] int32 (1-based position of each sequence's first row);
+ *   h device [B, n_tokens, d_model]; outputs c [B, n_tokens, d_c],
+ *   k_r [B, n_tokens, d_r], q_c [B, n_tokens, H, d_h],
+ *   q_r [B, n_tokens, H, d_r], written (the layouts mtla_merge_append,
+ *   mtla_decode_step and mtla_prefill take).
+ */
+int32_t mtla_project_inputs(const mtla_dims* dims, int32_t d_model, int32_t n_tokens, const int32_t* pos0,
+                            const void* h, const void* w_dkv, const void* w_q, const void* w_r, void* c,
+                            void* k_r, void* q_c, void* q_r, void* stream);
+
+/*
+ * mtla_output_project: y[r] = W_O o[r] for n_rows rows.
+ *   o device [n_rows, H, d_h]; w_o device [d_model, H * d_h];
+ *   y device [n_rows, d_model], written.
+ */
+int32_t mtla_output_project(const mtla_dims* dims, int32_t d_model, int32_t n_rows, const void* o,
+                            const void* w_o, void* y, void* stream);
+
+/* Bytes of workspace mtla_layer_decode_step needs. */
+int32_t mtla_layer_decode_workspace_bytes(const mtla_dims* dims, int32_t d_model, size_t* bytes);
+
+/*
+ * One decode step of the whole layer from h: input projections of token
+ * pos[b] of every sequence, mtla_decode_step (merge + attention), output
+ * projection.  All checks run before anything is enqueued.
+ *   pos device [B] int32 as for mtla_decode_step; h device [B, d_model];
+ *   y device [B, d_model], written; cache, open_acc as for mtla_decode_step;
+ *   workspace device, >= mtla_layer_decode_workspace_bytes(); scratch.
+ */
+int32_t mtla_layer_decode_step(const mtla_dims* dims, int32_t d_model, const int32_t* pos, const void* h,
+                               const void* w_dkv, const void* w_q, const void* w_r, const void* w_o,
+                               const float* w_hyp, const float* pe, int32_t pe_rows, const void* w_uk,
+                               const void* w_uv, void* cache, float* open_acc, void* y, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* Bytes of workspace mtla_layer_prefill needs. */
+int32_t mtla_layer_prefill_workspace_bytes(const mtla_dims* dims, int32_t d_model, int32_t t0,
+                                           int32_t n_tokens, size_t* bytes);
+
+/*
+ * The whole layer over tokens t0+1 .. t0+n_tokens of every sequence from h:
+ * input projections, mtla_prefill_at (t0 = 0: mtla_prefill), output
+ * projection.  All checks run before anything is enqueued.
+ *   h device [B, n_tokens, d_model]; y device [B, n_tokens, d_model],
+ *   written; the rest as for mtla_prefill_at.
+ */
+int32_t mtla_layer_prefill(const mtla_dims* dims, int32_t d_model, int32_t t0, int32_t n_tokens, const void* h,
+                           const void* w_dkv, const void* w_q, const void* w_r, const void* w_o,
+                           const float* w_hyp, const float* pe, int32_t pe_rows, const void* w_uk,
+                           const void* w_uv, void* cache, float* open_acc, void* y, void* workspace,
+                           size_t ws_bytes, void* stream);
+
+/*
  * Test hooks: the integer predicates the kernels use, exported for bit-exact
  * comparison.  Page: "Multi-head Temporal Latent Attention", Key claims (paper
  * Sec. 4.2 Fig. 2(c)).

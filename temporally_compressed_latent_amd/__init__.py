@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     mtla_debug_slot_limits, mtla_debug_stride_mask, mtla_decode, mtla_decode_attention,
     mtla_decode_attention_workspace_bytes, mtla_decode_plan, mtla_decode_step, mtla_decode_workspace_bytes, mtla_merge_append,
     mtla_prefill, mtla_prefill_at, mtla_prefill_at_workspace_bytes, mtla_prefill_workspace_bytes,
-    mtla_reorder_state, mtla_sinusoidal_pe, mtla_up_project,
+    mtla_reorder_state, mtla_sinusoidal_pe, mtla_up_project, mtla_project_inputs, mtla_output_project,
+    mtla_layer_decode_workspace_bytes, mtla_layer_decode_step, mtla_layer_prefill_workspace_bytes,
+    mtla_layer_prefill,
     mtla_version, status_string,
 )

@@ -100,6 +100,14 @@ _SIGS = {
     "mtla_prefill": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_prefill_at_workspace_bytes": (_I, [_D, _I, _I, ctypes.POINTER(_SZ)]),
     "mtla_reorder_state": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mtla_project_inputs": (_I, [_D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mtla_output_project": (_I, [_D, _I, _I, _P, _P, _P, _P]),
+    "mtla_layer_decode_workspace_bytes": (_I, [_D, _I, ctypes.POINTER(_SZ)]),
+    "mtla_layer_decode_step": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ,
+                                    _P]),
+    "mtla_layer_prefill_workspace_bytes": (_I, [_D, _I, _I, _I, ctypes.POINTER(_SZ)]),
+    "mtla_layer_prefill": (_I, [_D, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ,
+                                _P]),
     "mtla_prefill_at": (_I, [_D, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_debug_stride_mask": (_I, [_I, _I, _P, _P]),
     "mtla_debug_slot_limits": (_I, [_I, _I, _P, _P]),
@@ -376,6 +384,93 @@ def mtla_reorder_state(dims: MtlaDims, src, pos, cache_in, open_in, cache_out, o
         _tensor("open_out", open_out, (B, 2, dims.width), torch.float32),
         _tensor("pos_out", pos_out, (B,), torch.int32, optional=True),
         _stream(stream)))
+
+
+def _layer_weights(dims: MtlaDims, d_model: int, w_dkv, w_q, w_r, w_o):
+    H, st = dims.heads, dims.torch_dtype
+    return (_tensor("w_dkv", w_dkv, (dims.d_c, d_model), st),
+            _tensor("w_q", w_q, (H * (dims.d_h + dims.d_r), d_model), st),
+            _tensor("w_r", w_r, (dims.d_r, d_model), st, optional=dims.d_r == 0),
+            _tensor("w_o", w_o, (d_model, H * dims.d_h), st))
+
+
+def mtla_project_inputs(dims: MtlaDims, pos0, h, w_dkv, w_q, w_r, c, k_r, q_c, q_r, stream=None) -> None:
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    T, dm = (int(h.shape[1]), int(h.shape[2])) if h.dim() == 3 else (-1, -1)
+    _check(_lib.mtla_project_inputs(
+        ctypes.byref(dims), dm, T,
+        _tensor("pos0", pos0, (B,), torch.int32),
+        _tensor("h", h, (B, T, dm), st),
+        _tensor("w_dkv", w_dkv, (dims.d_c, dm), st),
+        _tensor("w_q", w_q, (H * (dims.d_h + dims.d_r), dm), st),
+        _tensor("w_r", w_r, (dims.d_r, dm), st, optional=dims.d_r == 0),
+        _tensor("c", c, (B, T, dims.d_c), st),
+        _tensor("k_r", k_r, (B, T, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("q_c", q_c, (B, T, H, dims.d_h), st),
+        _tensor("q_r", q_r, (B, T, H, dims.d_r), st, optional=dims.d_r == 0),
+        _stream(stream)))
+
+
+def mtla_output_project(dims: MtlaDims, o, w_o, y, stream=None) -> None:
+    H, st = dims.heads, dims.torch_dtype
+    R, dm = int(o.shape[0]), int(y.shape[-1])
+    _check(_lib.mtla_output_project(
+        ctypes.byref(dims), dm, R,
+        _tensor("o", o, (R, H, dims.d_h), st),
+        _tensor("w_o", w_o, (dm, H * dims.d_h), st),
+        _tensor("y", y, (R, dm), st),
+        _stream(stream)))
+
+
+def mtla_layer_decode_workspace_bytes(dims: MtlaDims, d_model: int) -> int:
+    n = _SZ(0)
+    _check(_lib.mtla_layer_decode_workspace_bytes(ctypes.byref(dims), d_model, ctypes.byref(n)))
+    return n.value
+
+
+def mtla_layer_decode_step(dims: MtlaDims, pos, h, w_dkv, w_q, w_r, w_o, w_hyp, pe, w_uk, w_uv, cache,
+                           open_acc, y, workspace, stream=None) -> None:
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    dm = int(h.shape[-1])
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    wd, wq, wr, wo = _layer_weights(dims, dm, w_dkv, w_q, w_r, w_o)
+    _check(_lib.mtla_layer_decode_step(
+        ctypes.byref(dims), dm,
+        _tensor("pos", pos, (B,), torch.int32),
+        _tensor("h", h, (B, dm), st), wd, wq, wr, wo,
+        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
+        _tensor("y", y, (B, dm), st),
+        ws, ws_bytes, _stream(stream)))
+
+
+def mtla_layer_prefill_workspace_bytes(dims: MtlaDims, d_model: int, t0: int, n_tokens: int) -> int:
+    n = _SZ(0)
+    _check(_lib.mtla_layer_prefill_workspace_bytes(ctypes.byref(dims), d_model, t0, n_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def mtla_layer_prefill(dims: MtlaDims, t0: int, h, w_dkv, w_q, w_r, w_o, w_hyp, pe, w_uk, w_uv, cache,
+                       open_acc, y, workspace, stream=None) -> None:
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    N, dm = (int(h.shape[1]), int(h.shape[2])) if h.dim() == 3 else (-1, -1)
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    wd, wq, wr, wo = _layer_weights(dims, dm, w_dkv, w_q, w_r, w_o)
+    _check(_lib.mtla_layer_prefill(
+        ctypes.byref(dims), dm, int(t0), N,
+        _tensor("h", h, (B, N, dm), st), wd, wq, wr, wo,
+        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
+        _tensor("y", y, (B, N, dm), st),
+        ws, ws_bytes, _stream(stream)))
 
 
 def mtla_debug_stride_mask(n: int, s: int, mask, stream=None) -> None:

@@ -1,6 +1,7 @@
 // C ABI of the MTLA hot path: argument validation, workspace sizing and
 // kernel dispatch.  Every check runs before anything is enqueued; no HIP API
 // is called on a failed check.
+#include <algorithm>
 #include <climits>
 #include <math.h>
 #include <stdarg.h>
@@ -447,11 +448,26 @@ int32_t mtla_decode(const mtla_dims* dims, const int32_t* pos, const void* q_c, 
                     "decode launch");
 }
 
+static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
+                                const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                                const void* q_r, const void* w_uk, const void* w_uv, void* cache,
+                                float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream,
+                                bool check_only);
+
 int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
                          const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
                          const void* q_r, const void* w_uk, const void* w_uv, void* cache,
                          float* open_acc, void* out, void* workspace, size_t ws_bytes,
                          void* stream) {
+  return decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, out,
+                          workspace, ws_bytes, stream, false);
+}
+
+static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
+                                const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                                const void* q_r, const void* w_uk, const void* w_uv, void* cache,
+                                float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream,
+                                bool check_only) {
   int32_t st = check_dims(dims);
   if (st != MTLA_OK) return st;
   if (pe_rows < 1) return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < 1", pe_rows);
@@ -473,6 +489,7 @@ int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* 
   if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   if (ws_bytes < ws.total)
     return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, ws.total);
+  if (check_only) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (decode_fused(dims)) {
     const mtla::StepArgs a = step_args(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv,
@@ -502,7 +519,7 @@ static int32_t prefill_impl(const mtla_dims* dims, int32_t t0, int32_t n_tokens,
                             const void* q_r, const void* c, const void* k_r, const float* w_hyp,
                             const float* pe, int32_t pe_rows, const void* w_uk, const void* w_uv,
                             void* cache, float* open_acc, void* out, void* workspace, size_t ws_bytes,
-                            void* stream) {
+                            void* stream, bool check_only = false) {
   int32_t st = check_dims(dims);
   if (st != MTLA_OK) return st;
   if (t0 < 0) return fail(MTLA_ERR_INVALID_ARG, "t0=%d < 0", t0);
@@ -540,6 +557,7 @@ static int32_t prefill_impl(const mtla_dims* dims, int32_t t0, int32_t n_tokens,
   if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   if (ws_bytes < ws.total)
     return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, ws.total);
+  if (check_only) return ok();
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int B = dims->batch, H = dims->heads, N = n_tokens;
@@ -615,6 +633,238 @@ int32_t mtla_prefill_at(const mtla_dims* dims, int32_t t0, int32_t n_tokens, con
                         float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream) {
   return prefill_impl(dims, t0, n_tokens, q_c, q_r, c, k_r, w_hyp, pe, pe_rows, w_uk, w_uv, cache, open_acc,
                       out, workspace, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The decoder layer around the core: input and output projections, and a
+// whole layer step / prefill from h.
+// ---------------------------------------------------------------------------
+
+static int32_t check_layer(const mtla_dims* d, int32_t d_model) {
+  if (d_model < 8 || d_model % 8 != 0)
+    return fail(MTLA_ERR_UNSUPPORTED, "d_model=%d must be a positive multiple of 8", d_model);
+  if ((int64_t(d->heads) * d->d_h) % 8 != 0)
+    return fail(MTLA_ERR_UNSUPPORTED, "heads*d_h=%lld must be a multiple of 8",
+                static_cast<long long>(int64_t(d->heads) * d->d_h));
+  if (d->d_h % 2 != 0) return fail(MTLA_ERR_UNSUPPORTED, "d_h=%d must be even", d->d_h);
+  return ok();
+}
+
+static mtla::LayerGemmArgs input_gemm(const mtla_dims* d, int32_t d_model, int32_t n_tokens,
+                                      const int32_t* pos0, int32_t p0_all, const void* h, const void* w_dkv,
+                                      const void* w_q, const void* w_r, void* c, void* k_r, void* q_c,
+                                      void* q_r) {
+  mtla::LayerGemmArgs g{};
+  g.M = d->batch * n_tokens;
+  g.N = d->d_c + d->heads * (d->d_h + d->d_r) + d->d_r;
+  g.K = d_model;
+  g.A = h;
+  g.w0 = w_dkv;
+  g.n0 = d->d_c;
+  g.w1 = w_q;
+  g.n1 = d->heads * (d->d_h + d->d_r);
+  g.w2 = w_r;
+  g.mode = 1;
+  g.T = n_tokens;
+  g.H = d->heads;
+  g.d_h = d->d_h;
+  g.d_r = d->d_r;
+  g.d_c = d->d_c;
+  g.pos0 = pos0;
+  g.p0_all = p0_all;
+  g.c = c;
+  g.k_r = k_r;
+  g.q_c = q_c;
+  g.q_r = q_r;
+  return g;
+}
+
+static mtla::LayerGemmArgs output_gemm(const mtla_dims* d, int32_t d_model, int32_t n_rows, const void* o,
+                                       const void* w_o, void* y) {
+  mtla::LayerGemmArgs g{};
+  g.M = n_rows;
+  g.N = d_model;
+  g.K = d->heads * d->d_h;
+  g.A = o;
+  g.w0 = w_o;
+  g.n0 = d_model;
+  g.w1 = w_o;
+  g.w2 = w_o;
+  g.mode = 0;
+  g.out = y;
+  return g;
+}
+
+static int32_t check_rows(const mtla_dims* d, int64_t rows, int32_t d_model) {
+  const int64_t width = std::max<int64_t>(d_model, d->d_c + int64_t(d->heads) * (d->d_h + d->d_r) + d->d_r);
+  if (rows > INT32_MAX || rows * width > kMaxElems)
+    return fail(MTLA_ERR_UNSUPPORTED, "%lld rows of width %lld are too many", static_cast<long long>(rows),
+                static_cast<long long>(width));
+  return ok();
+}
+
+int32_t mtla_project_inputs(const mtla_dims* dims, int32_t d_model, int32_t n_tokens, const int32_t* pos0,
+                            const void* h, const void* w_dkv, const void* w_q, const void* w_r, void* c,
+                            void* k_r, void* q_c, void* q_r, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if ((st = check_layer(dims, d_model)) != MTLA_OK) return st;
+  if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
+  if ((st = check_rows(dims, int64_t(dims->batch) * n_tokens, d_model)) != MTLA_OK) return st;
+  if (dims->batch == 0 || n_tokens == 0) return ok();
+  CHECK_PTR_ALIGN(pos0, 4);
+  CHECK_PTR(h);
+  CHECK_PTR(w_dkv);
+  CHECK_PTR(w_q);
+  if (dims->d_r > 0) {
+    CHECK_PTR(w_r);
+    CHECK_PTR_ALIGN(k_r, 4);
+    CHECK_PTR_ALIGN(q_r, 4);
+  }
+  CHECK_PTR_ALIGN(c, 4);
+  CHECK_PTR_ALIGN(q_c, 4);
+  const mtla::LayerGemmArgs g = input_gemm(dims, d_model, n_tokens, pos0, 1, h, w_dkv, w_q, w_r, c, k_r, q_c, q_r);
+  return hip_status(mtla::launch_layer_gemm(g, dims->dtype, static_cast<hipStream_t>(stream)),
+                    "input projection launch");
+}
+
+int32_t mtla_output_project(const mtla_dims* dims, int32_t d_model, int32_t n_rows, const void* o,
+                            const void* w_o, void* y, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if ((st = check_layer(dims, d_model)) != MTLA_OK) return st;
+  if (n_rows < 0) return fail(MTLA_ERR_INVALID_ARG, "n_rows=%d < 0", n_rows);
+  if ((st = check_rows(dims, n_rows, d_model)) != MTLA_OK) return st;
+  if (n_rows == 0) return ok();
+  CHECK_PTR(o);
+  CHECK_PTR(w_o);
+  CHECK_PTR_ALIGN(y, 4);
+  const mtla::LayerGemmArgs g = output_gemm(dims, d_model, n_rows, o, w_o, y);
+  return hip_status(mtla::launch_layer_gemm(g, dims->dtype, static_cast<hipStream_t>(stream)),
+                    "output projection launch");
+}
+
+namespace {
+// Workspace of a layer call over R rows: c, k_r, q_c, q_r and the heads'
+// outputs o (storage dtype), then the core call's own workspace.
+struct LayerWs {
+  size_t c, k_r, q_c, q_r, o, core, total;
+};
+LayerWs layer_ws(const mtla_dims* d, size_t R, size_t core_bytes) {
+  const size_t e = elem_bytes(d), H = d->heads;
+  LayerWs w;
+  size_t off = 0;
+  w.c = off;
+  off += align_up(R * d->d_c * e);
+  w.k_r = off;
+  off += align_up(R * d->d_r * e);
+  w.q_c = off;
+  off += align_up(R * H * d->d_h * e);
+  w.q_r = off;
+  off += align_up(R * H * d->d_r * e);
+  w.o = off;
+  off += align_up(R * H * d->d_h * e);
+  w.core = off;
+  w.total = off + core_bytes;
+  return w;
+}
+}  // namespace
+
+int32_t mtla_layer_decode_workspace_bytes(const mtla_dims* dims, int32_t d_model, size_t* bytes) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if ((st = check_layer(dims, d_model)) != MTLA_OK) return st;
+  if (!bytes) return fail(MTLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layer_ws(dims, dims->batch, decode_ws(dims).total).total;
+  return ok();
+}
+
+int32_t mtla_layer_decode_step(const mtla_dims* dims, int32_t d_model, const int32_t* pos, const void* h,
+                               const void* w_dkv, const void* w_q, const void* w_r, const void* w_o,
+                               const float* w_hyp, const float* pe, int32_t pe_rows, const void* w_uk,
+                               const void* w_uv, void* cache, float* open_acc, void* y, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if ((st = check_layer(dims, d_model)) != MTLA_OK) return st;
+  if (pe_rows < 1) return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < 1", pe_rows);
+  if ((st = check_rows(dims, dims->batch, d_model)) != MTLA_OK) return st;
+  if (dims->batch == 0) return ok();
+  CHECK_PTR(h);
+  CHECK_PTR(w_o);
+  CHECK_PTR_ALIGN(y, 4);
+  const DecodeWs dw = decode_ws(dims);
+  const LayerWs lw = layer_ws(dims, dims->batch, dw.total);
+  if (!workspace) return fail(MTLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", lw.total);
+  if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (ws_bytes < lw.total)
+    return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, lw.total);
+  void *c = at(workspace, lw.c), *k_r = at(workspace, lw.k_r), *q_c = at(workspace, lw.q_c),
+       *q_r = at(workspace, lw.q_r), *o = at(workspace, lw.o);
+  // the core's own checks run before anything is enqueued
+  if ((st = decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, o,
+                             at(workspace, lw.core), dw.total, nullptr, true)) != MTLA_OK)
+    return st;
+  if ((st = mtla_project_inputs(dims, d_model, 1, pos, h, w_dkv, w_q, w_r, c, k_r, q_c, q_r, stream)) != MTLA_OK)
+    return st;
+  if ((st = mtla_decode_step(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, o,
+                             at(workspace, lw.core), dw.total, stream)) != MTLA_OK)
+    return st;
+  return mtla_output_project(dims, d_model, dims->batch, o, w_o, y, stream);
+}
+
+int32_t mtla_layer_prefill_workspace_bytes(const mtla_dims* dims, int32_t d_model, int32_t t0, int32_t n_tokens,
+                                           size_t* bytes) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if ((st = check_layer(dims, d_model)) != MTLA_OK) return st;
+  if (t0 < 0) return fail(MTLA_ERR_INVALID_ARG, "t0=%d < 0", t0);
+  if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
+  if (!bytes) return fail(MTLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layer_ws(dims, size_t(dims->batch) * n_tokens, prefill_ws(dims, n_tokens, t0).total).total;
+  return ok();
+}
+
+int32_t mtla_layer_prefill(const mtla_dims* dims, int32_t d_model, int32_t t0, int32_t n_tokens, const void* h,
+                           const void* w_dkv, const void* w_q, const void* w_r, const void* w_o,
+                           const float* w_hyp, const float* pe, int32_t pe_rows, const void* w_uk,
+                           const void* w_uv, void* cache, float* open_acc, void* y, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if ((st = check_layer(dims, d_model)) != MTLA_OK) return st;
+  if (t0 < 0) return fail(MTLA_ERR_INVALID_ARG, "t0=%d < 0", t0);
+  if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
+  if ((st = check_rows(dims, int64_t(dims->batch) * n_tokens, d_model)) != MTLA_OK) return st;
+  if (dims->batch == 0 || n_tokens == 0) return ok();
+  CHECK_PTR(h);
+  CHECK_PTR(w_dkv);
+  CHECK_PTR(w_q);
+  if (dims->d_r > 0) CHECK_PTR(w_r);
+  CHECK_PTR(w_o);
+  CHECK_PTR_ALIGN(y, 4);
+  const size_t R = size_t(dims->batch) * n_tokens;
+  const PrefillWs pw = prefill_ws(dims, n_tokens, t0);
+  const LayerWs lw = layer_ws(dims, R, pw.total);
+  if (!workspace) return fail(MTLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", lw.total);
+  if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (ws_bytes < lw.total)
+    return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, lw.total);
+  void *c = at(workspace, lw.c), *k_r = at(workspace, lw.k_r), *q_c = at(workspace, lw.q_c),
+       *q_r = at(workspace, lw.q_r), *o = at(workspace, lw.o);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // run the core's own checks before anything is enqueued
+  if ((st = prefill_impl(dims, t0, n_tokens, q_c, q_r, c, k_r, w_hyp, pe, pe_rows, w_uk, w_uv, cache, open_acc,
+                         o, at(workspace, lw.core), pw.total, nullptr, /*check_only=*/true)) != MTLA_OK)
+    return st;
+  const mtla::LayerGemmArgs g =
+      input_gemm(dims, d_model, n_tokens, nullptr, t0 + 1, h, w_dkv, w_q, w_r, c, k_r, q_c, q_r);
+  hipError_t e = mtla::launch_layer_gemm(g, dims->dtype, s);
+  if (e != hipSuccess) return hip_status(e, "input projection launch");
+  if ((st = prefill_impl(dims, t0, n_tokens, q_c, q_r, c, k_r, w_hyp, pe, pe_rows, w_uk, w_uv, cache, open_acc,
+                         o, at(workspace, lw.core), pw.total, stream)) != MTLA_OK)
+    return st;
+  return mtla_output_project(dims, d_model, n_tokens * dims->batch, o, w_o, y, stream);
 }
 
 int32_t mtla_debug_stride_mask(int32_t n, int32_t s, uint8_t* mask, void* stream) {

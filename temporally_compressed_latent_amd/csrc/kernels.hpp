@@ -41,6 +41,33 @@ struct ReorderArgs {
 };
 hipError_t launch_reorder(const ReorderArgs& a, hipStream_t st);
 
+// Layer projections: one NT GEMM C[m, n] = sum_k A[m, k] Wt[n, k], with the
+// weight rows Wt = [w0 (n0 rows) ; w1 (n1 rows) ; w2 (the rest)].
+//   mode 0: out [M, N] row-major (the output projection).
+//   mode 1: the input projection; rows m = (b, t) of B sequences of T tokens,
+//           columns [c (d_c) | per head q^C (d_h), q^R (d_r) | k^R (d_r)],
+//           q^R and k^R rotated at position pos0[b] + t - 1 (p0_all when
+//           pos0 is null).
+struct LayerGemmArgs {
+  int M, N, K;
+  const void* A;
+  const void* w0;
+  int n0;
+  const void* w1;
+  int n1;
+  const void* w2;
+  int mode;
+  void* out;
+  int T, H, d_h, d_r, d_c;
+  const int32_t* pos0;
+  int p0_all;
+  void* c;
+  void* k_r;
+  void* q_c;
+  void* q_r;
+};
+hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st);
+
 hipError_t launch_sinusoidal_pe(int rows, int d, float* pe, hipStream_t st);
 hipError_t launch_debug_mask(int n, int s, uint8_t* mask, hipStream_t st);
 hipError_t launch_debug_limits(int n, int s, int32_t* hi, hipStream_t st);

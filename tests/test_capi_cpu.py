@@ -25,7 +25,7 @@ def dims(**kw):
 
 def test_exports_every_header_symbol():
     syms = m.header_symbols()
-    assert len(syms) == 20
+    assert len(syms) == 26
     for s in syms:
         assert hasattr(m.lib(), s), s
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
@@ -213,6 +213,52 @@ def test_reorder_argument_checks():
     assert call(co=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
     d0 = dims(batch=0)
     assert L.mtla_reorder_state(ctypes.byref(d0), None, None, None, None, None, None, None, None) == m.MTLA_OK
+
+
+def test_layer_argument_checks():
+    L, d = m.lib(), dims()
+    n = ctypes.c_size_t(0)
+    assert L.mtla_layer_decode_workspace_bytes(ctypes.byref(d), 512, ctypes.byref(n)) == m.MTLA_OK
+    dec = n.value
+    assert dec >= m.mtla_decode_workspace_bytes(d)
+    assert L.mtla_layer_decode_workspace_bytes(ctypes.byref(d), 500, ctypes.byref(n)) == m.MTLA_ERR_UNSUPPORTED
+    assert L.mtla_layer_prefill_workspace_bytes(ctypes.byref(d), 512, 0, 32, ctypes.byref(n)) == m.MTLA_OK
+    assert n.value > m.mtla_prefill_workspace_bytes(d, 32)
+    assert L.mtla_layer_prefill_workspace_bytes(ctypes.byref(d), 512, -1, 32, ctypes.byref(n)) == \
+        m.MTLA_ERR_INVALID_ARG
+    proj = lambda **k: L.mtla_project_inputs(
+        ctypes.byref(k.get("d", d)), k.get("dm", 512), k.get("T", 4), k.get("pos0", FAKE), k.get("h", FAKE),
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert proj(dm=0) == m.MTLA_ERR_UNSUPPORTED
+    assert proj(dm=12) == m.MTLA_ERR_UNSUPPORTED
+    assert proj(d=dims(d_h=63)) == m.MTLA_ERR_UNSUPPORTED              # odd d_h: rope pairs
+    assert proj(T=-1) == m.MTLA_ERR_INVALID_ARG
+    assert proj(pos0=None) == m.MTLA_ERR_INVALID_ARG
+    assert proj(h=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
+    assert proj(T=0, pos0=None, h=None) == m.MTLA_OK
+    outp = lambda **k: L.mtla_output_project(ctypes.byref(d), k.get("dm", 512), k.get("R", 4),
+                                             k.get("o", FAKE), k.get("w", FAKE), k.get("y", FAKE), None)
+    assert outp(R=-1) == m.MTLA_ERR_INVALID_ARG
+    assert outp(o=None) == m.MTLA_ERR_INVALID_ARG
+    assert outp(R=0, o=None) == m.MTLA_OK
+    step = lambda **k: L.mtla_layer_decode_step(
+        ctypes.byref(d), 512, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("pe_rows", 64), FAKE, FAKE,
+        k.get("cache", FAKE), FAKE, FAKE, k.get("ws", FAKE), k.get("n", dec), None)
+    assert step(pe_rows=0) == m.MTLA_ERR_INVALID_ARG
+    assert step(cache=None) == m.MTLA_ERR_INVALID_ARG                  # the core's check, before any launch
+    assert step(ws=None) == m.MTLA_ERR_WORKSPACE
+    assert step(n=dec - 16) == m.MTLA_ERR_WORKSPACE
+    assert L.mtla_layer_prefill_workspace_bytes(ctypes.byref(d), 512, 40, 32, ctypes.byref(n)) == m.MTLA_OK
+    pre_n = n.value
+    pre = lambda **k: L.mtla_layer_prefill(
+        ctypes.byref(d), 512, k.get("t0", 40), k.get("N", 32), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        k.get("pe_rows", 128), FAKE, FAKE, k.get("cache", FAKE), FAKE, FAKE, k.get("ws", FAKE),
+        k.get("n", pre_n), None)
+    assert pre(t0=240, pe_rows=400) == m.MTLA_ERR_INVALID_ARG          # beyond s * max_slots
+    assert pre(t0=100) == m.MTLA_ERR_INVALID_ARG                       # t0 + N > pe_rows
+    assert pre(cache=None) == m.MTLA_ERR_INVALID_ARG
+    assert pre(n=pre_n - 16) == m.MTLA_ERR_WORKSPACE
+    assert pre(N=0, cache=None, ws=None) == m.MTLA_OK
 
 
 def test_debug_hook_checks():

@@ -1,0 +1,122 @@
+"""GPU: the decoder layer around the core (mtla_project_inputs,
+mtla_output_project, mtla_layer_prefill, mtla_layer_decode_step) against the
+oracle's full layer (projections, RoPE, merge, attention, output projection)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import temporally_compressed_latent_amd as m
+from tests.gpu_util import DEV, host, tdev, tol
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(wid, **kw):
+    w = workloads.small(wid, **kw)
+    p = workloads.layer_params(w)
+    d = m.make_dims(w.batch, w.heads, w.d_h, w.d_c, w.d_r, w.s, -(-w.n_tokens // w.s) + 1, w.dtype)
+    st = d.torch_dtype
+    dev = {k: tdev(v, torch.float32 if k == "w_hyp" else st) for k, v in p.items()}
+    pe = torch.empty(w.n_tokens + 2, w.d_c, dtype=torch.float32, device=DEV)
+    m.mtla_sinusoidal_pe(pe)
+    cache = torch.zeros(w.batch, d.max_slots, d.width, dtype=st, device=DEV)
+    open_acc = torch.zeros(w.batch, 2, d.width, dtype=torch.float32, device=DEV)
+    return w, p, d, dev, pe, cache, open_acc
+
+
+def _oracle_layer(w, p, b, schedule, n=None):
+    n = w.n_tokens if n is None else n
+    return oracle.layer(p["h"][b, :n], p, w.heads, w.d_h, w.d_r, w.s, w.softmax_scale, schedule)
+
+
+# (workload, overrides): the fp32 single-layer case as it stands, and the
+# speech-translation shape (bf16, d_model 512) at a test-sized batch and length
+LAYER_CASES = [(0, {}), (1, dict(batch=2, n_tokens=100)), (1, dict(batch=2, n_tokens=70, s=3))]
+
+
+@pytest.mark.parametrize("wid,kw", LAYER_CASES)
+def test_project_inputs_matches_oracle(wid, kw):
+    w, p, d, dev, *_ = _setup(wid, **kw)
+    B, T, H = w.batch, w.n_tokens, w.heads
+    st = d.torch_dtype
+    pos0_h = np.array([1 + 5 * b for b in range(B)], dtype=np.int32)    # sequences start at different tokens
+    c = torch.empty(B, T, w.d_c, dtype=st, device=DEV)
+    k_r = torch.empty(B, T, w.d_r, dtype=st, device=DEV)
+    q_c = torch.empty(B, T, H, w.d_h, dtype=st, device=DEV)
+    q_r = torch.empty(B, T, H, w.d_r, dtype=st, device=DEV)
+    m.mtla_project_inputs(d, torch.from_numpy(pos0_h).to(DEV), dev["h"], dev["w_dkv"], dev["w_q"], dev["w_r"],
+                          c, k_r, q_c, q_r)
+    for b in range(B):
+        lead = int(pos0_h[b]) - 1          # rows before the first token: RoPE position pos0 - 1 + t
+        hf = np.zeros((lead + T, w.d_model))
+        hf[lead:] = p["h"][b]
+        want = oracle.project(hf, p, H, w.d_h, w.d_r)
+        for got, ref in zip((c, k_r, q_c, q_r), want):
+            assert oracle.max_rel_err(host(got)[b], ref[lead:]) <= tol(w.dtype), b
+
+
+@pytest.mark.parametrize("wid,kw", LAYER_CASES)
+def test_output_project_matches_oracle(wid, kw):
+    w, p, d, dev, *_ = _setup(wid, **kw)
+    R, H = 37, w.heads
+    g = np.random.default_rng(3)
+    o = workloads.quantize(g.standard_normal((R, H, w.d_h)).astype(np.float32), w.dtype)
+    y = torch.empty(R, w.d_model, dtype=d.torch_dtype, device=DEV)
+    m.mtla_output_project(d, tdev(o, d.torch_dtype), dev["w_o"], y)
+    want = o.reshape(R, -1).astype(np.float64) @ p["w_o"].astype(np.float64).T    # the layer's last step
+    assert oracle.max_rel_err(host(y), want) <= tol(w.dtype)
+
+
+@pytest.mark.parametrize("wid,kw", LAYER_CASES)
+def test_layer_prefill_matches_oracle(wid, kw):
+    w, p, d, dev, pe, cache, open_acc = _setup(wid, **kw)
+    B, N = w.batch, w.n_tokens
+    y = torch.empty(B, N, w.d_model, dtype=d.torch_dtype, device=DEV)
+    ws = torch.empty(m.mtla_layer_prefill_workspace_bytes(d, w.d_model, 0, N), dtype=torch.uint8, device=DEV)
+    m.mtla_layer_prefill(d, 0, dev["h"], dev["w_dkv"], dev["w_q"], dev["w_r"], dev["w_o"], dev["w_hyp"], pe,
+                         dev["w_uk"], dev["w_uv"], cache, open_acc, y, ws)
+    for b in range(B):
+        assert oracle.max_rel_err(host(y)[b], _oracle_layer(w, p, b, "parallel")) <= tol(w.dtype), b
+
+
+@pytest.mark.parametrize("wid,kw", LAYER_CASES)
+def test_layer_decode_loop_matches_oracle(wid, kw):
+    w, p, d, dev, pe, cache, open_acc = _setup(wid, **kw)
+    B, N = w.batch, w.n_tokens
+    ws = torch.empty(m.mtla_layer_decode_workspace_bytes(d, w.d_model), dtype=torch.uint8, device=DEV)
+    ys = []
+    for t in range(1, N + 1):
+        pos = torch.full((B,), t, dtype=torch.int32, device=DEV)
+        y = torch.empty(B, w.d_model, dtype=d.torch_dtype, device=DEV)
+        m.mtla_layer_decode_step(d, pos, dev["h"][:, t - 1].contiguous(), dev["w_dkv"], dev["w_q"], dev["w_r"],
+                                 dev["w_o"], dev["w_hyp"], pe, dev["w_uk"], dev["w_uv"], cache, open_acc, y, ws)
+        ys.append(host(y))
+    got = np.stack(ys, axis=1)
+    for b in range(B):
+        assert oracle.max_rel_err(got[b], _oracle_layer(w, p, b, "incremental")) <= tol(w.dtype), b
+
+
+def test_layer_prefill_in_chunks_then_decode():
+    """Layer prefill of tokens 1..40, then 41..70 as a chunk, then two decode
+    steps: every output follows the oracle's layer over tokens 1..72."""
+    w, p, d, dev, pe, cache, open_acc = _setup(1, batch=2, n_tokens=72, s=3)
+    B, dm = w.batch, w.d_model
+    outs = []
+    for t0, n in ((0, 40), (40, 30)):
+        y = torch.empty(B, n, dm, dtype=d.torch_dtype, device=DEV)
+        ws = torch.empty(m.mtla_layer_prefill_workspace_bytes(d, dm, t0, n), dtype=torch.uint8, device=DEV)
+        m.mtla_layer_prefill(d, t0, dev["h"][:, t0:t0 + n].contiguous(), dev["w_dkv"], dev["w_q"], dev["w_r"],
+                             dev["w_o"], dev["w_hyp"], pe, dev["w_uk"], dev["w_uv"], cache, open_acc, y, ws)
+        outs.append(host(y))
+    ws = torch.empty(m.mtla_layer_decode_workspace_bytes(d, dm), dtype=torch.uint8, device=DEV)
+    for t in (71, 72):
+        y = torch.empty(B, dm, dtype=d.torch_dtype, device=DEV)
+        m.mtla_layer_decode_step(d, torch.full((B,), t, dtype=torch.int32, device=DEV),
+                                 dev["h"][:, t - 1].contiguous(), dev["w_dkv"], dev["w_q"], dev["w_r"], dev["w_o"],
+                                 dev["w_hyp"], pe, dev["w_uk"], dev["w_uv"], cache, open_acc, y, ws)
+        outs.append(host(y)[:, None])
+    got = np.concatenate(outs, axis=1)
+    for b in range(B):
+        assert oracle.max_rel_err(got[b], _oracle_layer(w, p, b, "incremental")) <= tol(w.dtype), b
