@@ -15,8 +15,9 @@ The other workloads are reported in ``components``: the s=4 decode loop
 (2048 tokens), the summarisation-shaped prefill (B=16, N=4096, s=3), the same
 prefill's second half as one chunked call after the first half
 (mtla_prefill_at), the LLM-scale step (B=64, cache of 32,768 tokens, one
-append + decode), and a beam-search reorder of that LLM-scale decode state
-(mtla_reorder_state).
+append + decode), a beam-search reorder of that LLM-scale decode state
+(mtla_reorder_state), and the whole layer from h (input projections + RoPE,
+the core, output projection) for the s=2 decode loop and the prefill.
 
 ``roofline`` describes the dominant kernel of the headline step: the fused
 decode-step kernel, the step's only kernel, so its average launch duration is
@@ -46,7 +47,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default=None,
                    help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, "
-                        "prefill_chunk, llm_decode, reorder, copy: the counter-calibration copy kernel)")
+                        "prefill_chunk, llm_decode, reorder, layer_decode, layer_prefill, copy: the "
+                        "counter-calibration copy kernel)")
     return p.parse_args()
 
 
@@ -258,6 +260,69 @@ def run_prefill_chunk(w, steps, warmup, m, torch, workloads):
             "attended_pairs_per_bh": A, "attn_gflop": f_attn / 1e9, "kv_gemm_gflop": f_up / 1e9,
             "tflops_end_to_end": (f_attn + f_up) / (ms * 1e-3) / 1e12,
             "attn_tflops_over_end_to_end_time": f_attn / (ms * 1e-3) / 1e12}
+
+
+def run_layer_decode(w, steps, warmup, m, torch, workloads):
+    """The whole layer from h at the speech-translation decode shape: for every
+    token, mtla_layer_decode_step (input projections + RoPE, the fused core
+    step, output projection), 512 steps per replay.  Weights and h are the
+    seeded layer parameters at d_model = 512."""
+    B, N = w.batch, w.n_tokens
+    d = m.make_dims(B, w.heads, w.d_h, w.d_c, w.d_r, w.s, -(-N // w.s), "bf16")
+    p = workloads.layer_params(w)
+    bf = torch.bfloat16
+    dev = {k: to_dev(v, torch.float32 if k == "w_hyp" else bf, torch) for k, v in p.items()}
+    h_t = dev["h"].transpose(0, 1).contiguous()          # token-major: [N, B, d_model]
+    pe = torch.empty(N, w.d_c, dtype=torch.float32, device="cuda")
+    m.mtla_sinusoidal_pe(pe)
+    cache = torch.zeros(B, d.max_slots, d.width, dtype=bf, device="cuda")
+    open_acc = torch.zeros(B, 2, d.width, dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.mtla_layer_decode_workspace_bytes(d, w.d_model), dtype=torch.uint8, device="cuda")
+    y = torch.empty(N, B, w.d_model, dtype=bf, device="cuda")
+    pos = (torch.arange(1, N + 1, dtype=torch.int32, device="cuda")[:, None].expand(N, B).contiguous())
+
+    def fn():
+        for t in range(N):
+            m.mtla_layer_decode_step(d, pos[t], h_t[t], dev["w_dkv"], dev["w_q"], dev["w_r"], dev["w_o"],
+                                     dev["w_hyp"], pe, dev["w_uk"], dev["w_uv"], cache, open_acc, y[t], ws)
+    g = capture(fn, torch)
+    for _ in range(warmup):
+        g.replay()
+    ms = timed_graph(g, steps, torch)
+    return {"workload": "layer_" + w.name, "d_model": w.d_model, "ms_per_step": ms,
+            "tokens_per_s": B * N / (ms * 1e-3), "us_per_token_step": ms * 1e3 / N}
+
+
+def run_layer_prefill(w, steps, warmup, m, torch, workloads):
+    """The whole layer from h over the summarisation prefill (B=16, N=4096,
+    d_model=512): input projections, mtla_prefill, output projection."""
+    B, N = w.batch, w.n_tokens
+    d = m.make_dims(B, w.heads, w.d_h, w.d_c, w.d_r, w.s, -(-N // w.s), "bf16")
+    p = workloads.layer_params(w)
+    bf = torch.bfloat16
+    dev = {k: to_dev(v, torch.float32 if k == "w_hyp" else bf, torch) for k, v in p.items()}
+    pe = torch.empty(N, w.d_c, dtype=torch.float32, device="cuda")
+    m.mtla_sinusoidal_pe(pe)
+    cache = torch.zeros(B, d.max_slots, d.width, dtype=bf, device="cuda")
+    open_acc = torch.zeros(B, 2, d.width, dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.mtla_layer_prefill_workspace_bytes(d, w.d_model, 0, N), dtype=torch.uint8, device="cuda")
+    y = torch.empty(B, N, w.d_model, dtype=bf, device="cuda")
+
+    def fn():
+        m.mtla_layer_prefill(d, 0, dev["h"], dev["w_dkv"], dev["w_q"], dev["w_r"], dev["w_o"], dev["w_hyp"], pe,
+                             dev["w_uk"], dev["w_uv"], cache, open_acc, y, ws)
+    g = capture(fn, torch)
+    for _ in range(warmup):
+        g.replay()
+    ms = timed_graph(g, steps, torch)
+    Nq = w.heads * (w.d_h + w.d_r)
+    f_proj = 2.0 * B * N * w.d_model * (w.d_c + Nq + w.d_r + w.heads * w.d_h)
+    A = attended_pairs(N, w.s)
+    f_attn = 2.0 * B * w.heads * A * (2 * w.d_h + w.d_r)
+    f_up = 4.0 * B * N * w.d_c * w.heads * w.d_h
+    return {"workload": "layer_" + w.name, "d_model": w.d_model, "ms_per_call": ms,
+            "gflop": (f_proj + f_attn + f_up) / 1e9,
+            "tflops_end_to_end": (f_proj + f_attn + f_up) / (ms * 1e-3) / 1e12}
 
 
 def run_reorder(w, steps, warmup, m, torch):
@@ -474,6 +539,8 @@ def main():
               "prefill": lambda: run_prefill(W[3], args.steps, args.warmup, m, torch, workloads)[0],
               "prefill_chunk": lambda: run_prefill_chunk(W[3], args.steps, args.warmup, m, torch, workloads),
               "reorder": lambda: run_reorder(W[4], args.steps, args.warmup, m, torch),
+              "layer_decode": lambda: run_layer_decode(W[1], args.steps, args.warmup, m, torch, workloads),
+              "layer_prefill": lambda: run_layer_prefill(W[3], args.steps, args.warmup, m, torch, workloads),
               "llm_decode": lambda: run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0],
               "copy": lambda: run_copy(args.steps, args.warmup, torch)}
         print(json.dumps(fn[args.only]()), flush=True)
@@ -493,6 +560,12 @@ def main():
         comps["sum_prefill_b16_n4096_s3_chunk2"] = run_prefill_chunk(W[3], args.steps, args.warmup, m, torch,
                                                                      workloads)
         log("prefill chunk:", json.dumps(comps["sum_prefill_b16_n4096_s3_chunk2"]))
+        torch.cuda.empty_cache()
+        comps["layer_st_decode_b50_n512_s2"] = run_layer_decode(W[1], args.steps, args.warmup, m, torch, workloads)
+        log("layer decode:", json.dumps(comps["layer_st_decode_b50_n512_s2"]))
+        comps["layer_sum_prefill_b16_n4096_s3"] = run_layer_prefill(W[3], args.steps, args.warmup, m, torch,
+                                                                    workloads)
+        log("layer prefill:", json.dumps(comps["layer_sum_prefill_b16_n4096_s3"]))
         torch.cuda.empty_cache()
         comps["llm_decode_b64_n32768_s2"] = run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0]
         log("llm:", json.dumps(comps["llm_decode_b64_n32768_s2"]))

@@ -13,8 +13,10 @@
 // ([W_DKV ; W_Q ; W_R]) and scatters its columns to c, q^C, q^R and k^R,
 // rotating the rope pairs on the way.  64x64 output tiles, 4 waves, K step 32,
 // double-buffered LDS; 16x16x32 bf16 MFMA for bf16 storage, fp32 FMA for fp32
-// storage.  The C tile is staged in LDS, so a rope pair (2k, 2k+1) - two
-// adjacent columns of one tile - is read by the thread that writes it.
+// storage.  The C tile is staged in LDS and stored by column pairs, so a rope
+// pair (2k, 2k+1) - two adjacent columns of one tile - is rotated by the one
+// thread that stores both.  Few rows (decode) take a skinny variant that
+// splits K over the waves instead.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -47,32 +49,91 @@ __device__ __forceinline__ void store_val(void* p, size_t i, float v) {
   Store<T>::store(static_cast<T*>(p), i, v);
 }
 
-// Epilogue for one output element (row m, column n) of the input projection.
-// x is C[m, n]; xp its rope partner C[m, n ^ 1] (used on rope columns only).
-template <typename T>
-__device__ __forceinline__ void project_store(const LayerGemmArgs& g, int m, int n, float x, float xp) {
-  const int QW = g.d_h + g.d_r;
-  const int HQ = g.H * QW;
-  auto rotate = [&](int e) {  // e: index in the rope vector of width d_r
-    const int b = m / g.T, t = m % g.T;
-    const int pos = (g.pos0 ? g.pos0[b] : g.p0_all) + t - 1;  // 0-based position of the token
-    const int k = e >> 1;
-    const double ang = static_cast<double>(pos) * pow(10000.0, -2.0 * k / g.d_r);
-    const float cs = static_cast<float>(cos(ang)), sn = static_cast<float>(sin(ang));
-    // pair (x_even, x_odd) -> (x_even cos - x_odd sin, x_even sin + x_odd cos)
-    return (e & 1) == 0 ? x * cs - xp * sn : xp * sn + x * cs;
-  };
+// Where the even output column n of a GEMM goes: plain output (mode 0), or, for
+// the input projection, c, q^C, q^R or k^R; a rope pair carries its frequency
+// 10000^(-2k/d_r), k the pair's index in the rope vector.
+struct PairDest {
+  int kind;      // 0 plain, 1 c, 2 q^C, 3 q^R, 4 k^R
+  int head, e;   // head and element index inside its section
+  double theta;  // rope frequency (kinds 3 and 4)
+};
+
+__device__ __forceinline__ PairDest pair_dest(const LayerGemmArgs& g, int n) {
+  PairDest p{0, 0, n, 0.0};
+  if (g.mode == 0) return p;
+  const int QW = g.d_h + g.d_r, HQ = g.H * QW;
   if (n < g.d_c) {
-    store_val<T>(g.c, static_cast<size_t>(m) * g.d_c + n, x);
+    p.kind = 1;
   } else if (n < g.d_c + HQ) {
-    const int hh = (n - g.d_c) / QW, e = (n - g.d_c) % QW;
-    if (e < g.d_h)
-      store_val<T>(g.q_c, (static_cast<size_t>(m) * g.H + hh) * g.d_h + e, x);
-    else
-      store_val<T>(g.q_r, (static_cast<size_t>(m) * g.H + hh) * g.d_r + (e - g.d_h), rotate(e - g.d_h));
+    p.head = (n - g.d_c) / QW;
+    p.e = (n - g.d_c) % QW;
+    if (p.e < g.d_h) {
+      p.kind = 2;
+    } else {
+      p.kind = 3;
+      p.e -= g.d_h;
+    }
   } else {
-    const int e = n - g.d_c - HQ;
-    store_val<T>(g.k_r, static_cast<size_t>(m) * g.d_r + e, rotate(e));
+    p.kind = 4;
+    p.e = n - g.d_c - HQ;
+  }
+  if (p.kind >= 3) p.theta = pow(10000.0, -static_cast<double>(p.e) / g.d_r);  // e = 2k
+  return p;
+}
+
+// Rotate the pair (x0, x1) by the angle pos * theta: the angle is formed and
+// reduced to [-pi, pi] in double, so that large positions keep their
+// accuracy, and its sine and cosine are taken in float.
+__device__ __forceinline__ void rope_rotate(int pos, double theta, float& x0, float& x1) {
+  constexpr double kTwoPi = 6.283185307179586476925286766559;
+  const double ang = static_cast<double>(pos) * theta;
+  const double rev = rint(ang * (1.0 / kTwoPi));
+  const float r = static_cast<float>(fma(-rev, kTwoPi, ang));
+  float sn, cs;
+  sincosf(r, &sn, &cs);
+  const float y0 = x0 * cs - x1 * sn;
+  const float y1 = x0 * sn + x1 * cs;
+  x0 = y0;
+  x1 = y1;
+}
+
+// 0-based position of the token in GEMM row m (sequence m / T, token m % T).
+__device__ __forceinline__ int row_position(const LayerGemmArgs& g, int m) {
+  const int b = m / g.T, t = m % g.T;
+  return (g.pos0 ? g.pos0[b] : g.p0_all) + t - 1;
+}
+
+// Store the output pair C[m, n], C[m, n + 1] (n even) at its destination; pos
+// is row m's token position (used by rope pairs only).
+template <typename T>
+__device__ __forceinline__ void store_pair(const LayerGemmArgs& g, const PairDest& p, int m, int n, int pos,
+                                           float x0, float x1) {
+  size_t i;
+  switch (p.kind) {
+    case 0:
+      i = static_cast<size_t>(m) * g.N + n;
+      store_val<T>(g.out, i, x0);
+      if (n + 1 < g.N) store_val<T>(g.out, i + 1, x1);
+      return;
+    case 1:
+      i = static_cast<size_t>(m) * g.d_c + n;
+      store_val<T>(g.c, i, x0);
+      store_val<T>(g.c, i + 1, x1);
+      return;
+    case 2:
+      i = (static_cast<size_t>(m) * g.H + p.head) * g.d_h + p.e;
+      store_val<T>(g.q_c, i, x0);
+      store_val<T>(g.q_c, i + 1, x1);
+      return;
+    default: {
+      rope_rotate(pos, p.theta, x0, x1);
+      void* dst = p.kind == 3 ? g.q_r : g.k_r;
+      i = p.kind == 3 ? (static_cast<size_t>(m) * g.H + p.head) * g.d_r + p.e
+                      : static_cast<size_t>(m) * g.d_r + p.e;
+      store_val<T>(dst, i, x0);
+      store_val<T>(dst, i + 1, x1);
+      return;
+    }
   }
 }
 
@@ -191,15 +252,99 @@ __global__ __launch_bounds__(256) void layer_gemm_kernel(LayerGemmArgs g) {
       for (int j = 0; j < 4; ++j) sC[(ty * 4 + i) * LCP + tx * 4 + j] = accv[i][j];
   }
   __syncthreads();
-  for (int idx = tid; idx < LBM * LBN; idx += 256) {
-    const int r = idx / LBN, cc = idx % LBN;
-    const int m = m0 + r, n = n0 + cc;
-    if (m >= M || n >= N) continue;
-    const float x = sC[r * LCP + cc];
-    if (g.mode == 0)
-      store_val<T>(g.out, static_cast<size_t>(m) * N + n, x);
-    else
-      project_store<T>(g, m, n, x, sC[r * LCP + (cc ^ 1)]);
+  // each thread stores one column pair of the tile on every 8th row
+  const int pc = tid & (LBN / 2 - 1), n = n0 + 2 * pc;
+  if (n >= N) return;
+  const PairDest pd = pair_dest(g, n);
+  for (int r = tid / (LBN / 2); r < LBM; r += 256 / (LBN / 2)) {
+    const int m = m0 + r;
+    if (m >= M) break;
+    store_pair<T>(g, pd, m, n, pd.kind >= 3 ? row_position(g, m) : 0, sC[r * LCP + 2 * pc],
+                  sC[r * LCP + 2 * pc + 1]);
+  }
+}
+
+// The same product for few rows (M <= 16 * NB <= 64, one token per sequence in
+// decode), in bf16: every lane loads its MFMA operand fragments straight from
+// memory (A row c16 and weight row c16, 8 consecutive k at 8 * g16), the
+// workgroup's four waves split K between them (wave w takes the 32-wide
+// k-steps w, w + 4, ...) with sixteen k-steps' loads in flight per round, and
+// the four partial tiles are summed through LDS.  One workgroup per 16 output
+// columns.
+constexpr int SKN = 16;
+
+template <int NB>
+__global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(LayerGemmArgs g) {
+  __shared__ float sP[4][16 * NB * (SKN + 1)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g16 = lane >> 4, c16 = lane & 15;
+  const int M = g.M, N = g.N, K = g.K;
+  const int n0 = blockIdx.x * SKN;
+  // epilogue item of this thread: column pair pc on rows er[0], er[1]; their
+  // token positions are loaded first, so that they arrive with the operands
+  constexpr int ER = (16 * NB + 31) / 32;
+  const int pc = tid & (SKN / 2 - 1), n = n0 + 2 * pc;
+  int er[ER], epos[ER];
+#pragma unroll
+  for (int j = 0; j < ER; ++j) {
+    er[j] = tid / (SKN / 2) + 32 * j;
+    epos[j] = g.mode != 0 ? row_position(g, min(er[j], M - 1)) : 0;
+  }
+  const uint16_t* wr = weight_row<uint16_t>(g, min(n0 + c16, N - 1)) + 8 * g16;
+  const uint16_t* ar[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    ar[i] = static_cast<const uint16_t*>(g.A) + static_cast<size_t>(min(16 * i + c16, M - 1)) * K + 8 * g16;
+  f32x4 acc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 zero = {};
+  bf16x8 wf[4], af[4][NB];
+  auto load_round = [&](int kb) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = kb + 128 * s;
+      const bool in = k + 8 * g16 < K;  // K is a multiple of 8: a fragment is wholly in or out
+      wf[s] = in ? *reinterpret_cast<const bf16x8*>(wr + k) : zero;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) af[s][i] = in ? *reinterpret_cast<const bf16x8*>(ar[i] + k) : zero;
+    }
+  };
+  auto mma_round = [&]() {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][i], wf[s], acc[i], 0, 0, 0);
+  };
+  // wave w takes the 32-wide k-steps w, w + 4, ...: sixteen per round
+  int kb = 32 * wave;
+  load_round(kb);
+  __builtin_amdgcn_sched_barrier(0);
+  const PairDest pd = pair_dest(g, min(n, N - 2));  // the rope frequency is computed under the loads
+  __builtin_amdgcn_sched_barrier(0);
+  mma_round();
+  for (kb += 512; kb < K; kb += 512) {
+    load_round(kb);
+    mma_round();
+  }
+  // acc[i][q]: row 16 i + 4 g16 + q, column c16
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sP[wave][(16 * i + 4 * g16 + q) * (SKN + 1) + c16] = acc[i][q];
+  __syncthreads();
+  if (n >= N) return;
+#pragma unroll
+  for (int j = 0; j < ER; ++j) {
+    const int r = er[j];
+    if (r >= M || r >= 16 * NB) break;
+    float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      x0 += sP[w][r * (SKN + 1) + 2 * pc];
+      x1 += sP[w][r * (SKN + 1) + 2 * pc + 1];
+    }
+    store_pair<uint16_t>(g, pd, r, n, epos[j], x0, x1);
   }
 }
 
@@ -207,6 +352,16 @@ __global__ __launch_bounds__(256) void layer_gemm_kernel(LayerGemmArgs g) {
 
 hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (dtype != 0 && g.M <= 64) {
+    const dim3 sgrid((g.N + SKN - 1) / SKN);
+    switch ((g.M + 15) / 16) {
+      case 1: layer_gemm_skinny_kernel<1><<<sgrid, 256, 0, st>>>(g); break;
+      case 2: layer_gemm_skinny_kernel<2><<<sgrid, 256, 0, st>>>(g); break;
+      case 3: layer_gemm_skinny_kernel<3><<<sgrid, 256, 0, st>>>(g); break;
+      default: layer_gemm_skinny_kernel<4><<<sgrid, 256, 0, st>>>(g); break;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((g.N + LBN - 1) / LBN, (g.M + LBM - 1) / LBM);
   if (dtype == 0)
     layer_gemm_kernel<float><<<grid, 256, 0, st>>>(g);

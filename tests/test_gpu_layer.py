@@ -57,10 +57,38 @@ def test_project_inputs_matches_oracle(wid, kw):
             assert oracle.max_rel_err(host(got)[b], ref[lead:]) <= tol(w.dtype), b
 
 
+# one token per sequence (a decode step's projection) at batch sizes on both
+# sides of the few-row GEMM's limits (16, 32, 48, 64 rows), at positions up to
+# 2^15 so that the RoPE angle's range reduction is exercised
+@pytest.mark.parametrize("wid,B", [(1, 1), (1, 17), (1, 50), (1, 64), (1, 65), (0, 50)])
+def test_project_one_token_large_positions(wid, B):
+    w, p, d, dev, *_ = _setup(wid, batch=B)
+    H = w.heads
+    st = d.torch_dtype
+    g = np.random.default_rng(11 + B)
+    pos0_h = g.integers(1, 1 << 15, size=B).astype(np.int32)
+    pos0_h[0] = (1 << 15) - 1
+    h1 = dev["h"][:, :1].contiguous()
+    c = torch.empty(B, 1, w.d_c, dtype=st, device=DEV)
+    k_r = torch.empty(B, 1, w.d_r, dtype=st, device=DEV)
+    q_c = torch.empty(B, 1, H, w.d_h, dtype=st, device=DEV)
+    q_r = torch.empty(B, 1, H, w.d_r, dtype=st, device=DEV)
+    m.mtla_project_inputs(d, torch.from_numpy(pos0_h).to(DEV), h1, dev["w_dkv"], dev["w_q"], dev["w_r"],
+                          c, k_r, q_c, q_r)
+    for b in range(B):
+        # projection of the one row (RoPE at position 0 is the identity), then
+        # RoPE at the token's position pos0 - 1
+        c0, kr0, qc0, qr0 = oracle.project(p["h"][b, :1], p, H, w.d_h, w.d_r)
+        pos = int(pos0_h[b]) - 1
+        want = (c0, oracle.rope(kr0, pos), qc0, oracle.rope(qr0, pos))
+        for got, ref in zip((c, k_r, q_c, q_r), want):
+            assert oracle.max_rel_err(host(got)[b], ref) <= tol(w.dtype), (b, pos)
+
+
 @pytest.mark.parametrize("wid,kw", LAYER_CASES)
 def test_output_project_matches_oracle(wid, kw):
     w, p, d, dev, *_ = _setup(wid, **kw)
-    R, H = 37, w.heads
+    R, H = 37, w.heads          # 37 rows: three 16-row blocks, the last one ragged
     g = np.random.default_rng(3)
     o = workloads.quantize(g.standard_normal((R, H, w.d_h)).astype(np.float32), w.dtype)
     y = torch.empty(R, w.d_model, dtype=d.torch_dtype, device=DEV)
