@@ -33,6 +33,10 @@ reason, in the design notes):
   * softmax scale 1/sqrt(d_h + d_R);
   * no biases, no query compression, no latent normalisation.
 
+Training backward.  ``parallel_backward`` takes reverse mode through the
+steps of ``parallel`` (gate, partial merges, explicit keys/values, masked
+softmax attention); its pin is central differences of ``parallel`` itself.
+
 Parity status of the conventions (gate input, pe and RoPE formulas, scale):
 "parity unpinned" against the pages, which print no worked example.  Every
 structural part (slot index, mask, merge, absorption, attention) is pinned by
@@ -365,6 +369,104 @@ def parallel(c, k_r, q_c, q_r, w_hyp, w_uk, w_uv, s: int, scale: float,
         z = np.where(M, z, -np.inf)
         o[:, h] = softmax(z) @ V
     return (o, P) if return_partials else o
+
+
+# ---------------------------------------------------------------------------
+# Training backward of the parallel pass (reverse mode through its steps)
+# ---------------------------------------------------------------------------
+
+def softmax_backward(a: np.ndarray, da: np.ndarray) -> np.ndarray:
+    """dz for a = softmax(z) along the last axis: a * (da - sum(a * da)).
+
+    Masked entries have a = 0, so their dz is 0.
+    """
+    a, da = np.asarray(a, dtype=F), np.asarray(da, dtype=F)
+    return a * (da - np.sum(a * da, axis=-1, keepdims=True))
+
+
+def partial_merges_backward(dP: np.ndarray, s: int) -> np.ndarray:
+    """Adjoint of ``partial_merges`` in the weighted rows y_k = w_k x_k.
+
+    Token k enters every partial merge P_j of its own block with j >= k (the
+    sum that defines P_j starts at the block's first token), so its gradient
+    is the sum of dP_j over j = k .. last token of the block (or N).  Written
+    as that sum.
+    """
+    dP = np.asarray(dP, dtype=F)
+    N = dP.shape[0]
+    G = np.zeros_like(dP)
+    for k in range(1, N + 1):
+        end = min(s * slot_of(k, s), N)
+        for j in range(k, end + 1):
+            G[k - 1] = G[k - 1] + dP[j - 1]
+    return G
+
+
+def gate_backward(c, pe, w_hyp, w, dw):
+    """Through w_k = sigmoid(u_k), u_k = W_hyp . (c_k + pe_k): returns the
+    gate's share of dc ([N, d_c]) and dW_hyp ([d_c]) given dw ([N])."""
+    c, pe, w_hyp = (np.asarray(a, dtype=F) for a in (c, pe, w_hyp))
+    du = np.asarray(dw, dtype=F) * w * (1.0 - w)
+    return du[:, None] * w_hyp[None, :], (c + pe).T @ du
+
+
+def parallel_backward(c, k_r, q_c, q_r, w_hyp, w_uk, w_uv, s: int, scale: float,
+                      d_o, pe: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Gradients of L = sum(d_o * parallel(...)) for one sequence.
+
+    The training use of the stride-aware mask ([MTLA-wiki] Key claims, paper
+    Sec. 4.2-4.3).  Reverse mode through the steps of ``parallel``, last step
+    first: the masked softmax attention per head (scores from explicit keys
+    K^C_j = W_UK[h] P^c_j and rope keys P^R_j, values W_UV[h] P^c_j), the
+    explicit key/value up-projection, the cumulative in-block partial merges,
+    and the gate.  d_o [N, H, d_h].  Returns dc, dk_r, dq_c, dq_r, dw_hyp,
+    dw_uk, dw_uv, shaped like the inputs.
+    """
+    c, k_r = np.asarray(c, dtype=F), np.asarray(k_r, dtype=F)
+    q_c, q_r = np.asarray(q_c, dtype=F), np.asarray(q_r, dtype=F)
+    w_uk, w_uv, d_o = (np.asarray(a, dtype=F) for a in (w_uk, w_uv, d_o))
+    N, d_c = c.shape
+    H = q_c.shape[1]
+    if pe is None:
+        pe = sinusoidal_pe(N, d_c)
+    pe = np.asarray(pe, dtype=F)[:N]
+    # forward, kept for the backward
+    w = gate(c, pe, w_hyp)
+    x = np.concatenate([c, k_r], axis=1)
+    P = partial_merges(x, w, s)
+    Pc, Pr = P[:, :d_c], P[:, d_c:]
+    M = stride_mask(N, s)
+    dPc = np.zeros_like(Pc)
+    dPr = np.zeros_like(Pr)
+    dq_c = np.zeros_like(q_c)
+    dq_r = np.zeros_like(q_r)
+    dw_uk = np.zeros_like(w_uk)
+    dw_uv = np.zeros_like(w_uv)
+    for h in range(H):
+        K = Pc @ w_uk[h].T
+        V = Pc @ w_uv[h].T
+        z = np.where(M, scale * (q_c[:, h] @ K.T + q_r[:, h] @ Pr.T), -np.inf)
+        A = softmax(z)
+        # o_h = A V
+        dA = d_o[:, h] @ V.T
+        dV = A.T @ d_o[:, h]
+        dz = scale * softmax_backward(A, dA)
+        # z = scale (q^C K^T + q^R P^R^T)
+        dq_c[:, h] = dz @ K
+        dq_r[:, h] = dz @ Pr
+        dK = dz.T @ q_c[:, h]
+        dPr += dz.T @ q_r[:, h]
+        # K = P^c W_UK[h]^T, V = P^c W_UV[h]^T
+        dPc += dK @ w_uk[h] + dV @ w_uv[h]
+        dw_uk[h] = dK.T @ Pc
+        dw_uv[h] = dV.T @ Pc
+    # P_j = sum over the block's tokens k <= j of w_k x_k
+    G = partial_merges_backward(np.concatenate([dPc, dPr], axis=1), s)
+    dx = w[:, None] * G
+    dw = np.sum(G * x, axis=1)
+    dc_gate, dw_hyp = gate_backward(c, pe, w_hyp, w, dw)
+    return {"dc": dx[:, :d_c] + dc_gate, "dk_r": dx[:, d_c:], "dq_c": dq_c, "dq_r": dq_r,
+            "dw_hyp": dw_hyp, "dw_uk": dw_uk, "dw_uv": dw_uv}
 
 
 def prefill_query(P: np.ndarray, i: int, q_c_i, q_r_i, w_uk, w_uv, s: int,

@@ -367,6 +367,36 @@ def pin_beam_reorder_follows_history(o):
             np.testing.assert_allclose(grown, ref, rtol=0, atol=1e-12)
 
 
+def pin_backward_finite_differences(o):
+    """The training backward equals central differences of the forward:
+    every element of every gradient of L = sum(d_o * parallel(...)) against
+    (L(x + e) - L(x - e)) / 2e, at N a multiple of s, N not a multiple, s = 1
+    (the causal mask) and s >= N (the diagonal alone)."""
+    H, d_h, d_c, d_r, scale, eps = 2, 3, 4, 2, 0.4, 1e-6
+    names = ("dc", "dk_r", "dq_c", "dq_r", "dw_hyp", "dw_uk", "dw_uv")
+    for seed, N, s in ((61, 7, 3), (62, 6, 2), (63, 5, 1), (64, 4, 5)):
+        args = list(_rand_case(seed, N, s, H, d_h, d_c, d_r, w_scale=0.5))
+        g = np.random.default_rng(seed + 100)
+        d_o = g.standard_normal((N, H, d_h))
+        pe = g.standard_normal((N, d_c))
+        grads = o.parallel_backward(*args, s, scale, d_o, pe=pe)
+
+        def loss(a):
+            return float(np.sum(d_o * o.parallel(*a, s, scale, pe=pe)))
+
+        for i, name in enumerate(names):
+            fd = np.zeros_like(args[i])
+            for idx in np.ndindex(args[i].shape):
+                a = [x.copy() for x in args]
+                a[i][idx] += eps
+                lp = loss(a)
+                a[i][idx] -= 2 * eps
+                fd[idx] = (lp - loss(a)) / (2 * eps)
+            got = np.asarray(grads[name])
+            assert got.shape == fd.shape, (name, got.shape)
+            assert np.max(np.abs(got - fd)) <= 1e-6 * max(1.0, np.max(np.abs(fd))), (seed, name)
+
+
 ALL_PINS = [
     pin_slot_index, pin_block_starts, pin_slot_count, pin_mask_special_cases,
     pin_mask_structure, pin_mask_matches_incremental_cache, pin_cache_ratio,
@@ -374,5 +404,5 @@ ALL_PINS = [
     pin_uniform_attention_keyset, pin_absorption, pin_decode_single_slot,
     pin_s1_equals_causal_sdpa, pin_parallel_equals_incremental,
     pin_prefill_query_rows, pin_rope, pin_pe, pin_layer_schedules,
-    pin_beam_reorder_follows_history,
+    pin_beam_reorder_follows_history, pin_backward_finite_differences,
 ]

@@ -115,8 +115,38 @@ def _reorder_scatter(cache, open_state, pos, src, s):
     return out, op, po
 
 
+def _merges_backward_prefix(dP, s):
+    # sums the block's tokens up to k (the forward's own direction) instead of from k on
+    dP = np.asarray(dP, dtype=float)
+    G = np.zeros_like(dP)
+    for k in range(1, dP.shape[0] + 1):
+        for j in range(s * ((k - 1) // s) + 1, k + 1):
+            G[k - 1] += dP[j - 1]
+    return G
+
+
+def _merges_backward_no_reset(dP, s):
+    # suffix sum over the whole sequence, ignoring block ends
+    return np.cumsum(np.asarray(dP, dtype=float)[::-1], axis=0)[::-1]
+
+
+def _softmax_backward_no_rowsum(a, da):
+    return np.asarray(a, dtype=float) * np.asarray(da, dtype=float)
+
+
+def _gate_backward_no_pe(c, pe, w_hyp, w, dw):
+    return _ORIG["gate_backward"](c, np.zeros_like(np.asarray(pe, dtype=float)), w_hyp, w, dw)
+
+
+def _gate_backward_no_sigmoid_slope(c, pe, w_hyp, w, dw):
+    # takes dw as du (drops the sigmoid's derivative w (1 - w))
+    du = np.asarray(dw, dtype=float)
+    w_hyp = np.asarray(w_hyp, dtype=float)
+    return du[:, None] * w_hyp[None, :], (np.asarray(c) + np.asarray(pe)).T @ du
+
+
 _ORIG = {name: getattr(O, name) for name in
-         ("decode_absorbed", "rope", "sinusoidal_pe", "reorder_state")}
+         ("decode_absorbed", "rope", "sinusoidal_pe", "reorder_state", "gate_backward")}
 
 MUTATIONS = {
     "visible_keys": [_visible_keys_block_starts, _visible_keys_off_by_one, _visible_keys_no_diag],
@@ -132,6 +162,9 @@ MUTATIONS = {
     "cache_elements_per_token": [_cache_elements_floor],
     "cache_row_bytes": [_row_bytes_no_rope],
     "reorder_state": [_reorder_own_length, _reorder_scatter],
+    "partial_merges_backward": [_merges_backward_prefix, _merges_backward_no_reset],
+    "softmax_backward": [_softmax_backward_no_rowsum],
+    "gate_backward": [_gate_backward_no_pe, _gate_backward_no_sigmoid_slope],
 }
 
 CASES = [(name, fn) for name, fns in MUTATIONS.items() for fn in fns]
