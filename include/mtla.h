@@ -379,6 +379,46 @@ int32_t mtla_layer_prefill(const mtla_dims* dims, int32_t d_model, int32_t t0, i
                            const void* w_uv, void* cache, float* open_acc, void* y, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* Bytes of workspace mtla_prefill_backward needs for n_tokens tokens. */
+int32_t mtla_prefill_backward_workspace_bytes(const mtla_dims* dims, int32_t n_tokens, size_t* bytes);
+
+/*
+ * Training backward of the parallel pass that mtla_prefill computes (tokens
+ * 1..n_tokens of every sequence, no cache involved).  Page: "Multi-head
+ * Temporal Latent Attention", Key claims (paper Sec. 4.2 Fig. 2(c), Sec. 4.3
+ * Eq. 17: training in parallel under the stride-aware mask) and Method
+ * (1)-(3).  With L = sum(grad_out * o), it writes the gradients of L:
+ *   p_ij = softmax_j(z_ij), dp_ij = dO_i . V_j, D_i = sum_j p_ij dp_ij,
+ *   ds_ij = tau p_ij (dp_ij - D_i);
+ *   grad_q_c_i = sum_j ds_ij K^C_j, grad_q_r_i = sum_j ds_ij P^R_j;
+ *   dK^C_j = sum_i ds_ij q^C_i, dV_j = sum_i p_ij dO_i, dP^R_j = sum_h,i ds_ij q^R_i;
+ *   dP^c_j = sum_h W_UK[h]^T dK^C_j + W_UV[h]^T dV_j;
+ *   grad_w_uk[h] = sum_j dK^C_j (P^c_j)^T, grad_w_uv[h] = sum_j dV_j (P^c_j)^T;
+ *   G_k = sum of dP_j over j = k .. the end of k's block (reverse in-block sum);
+ *   du_k = (G_k . x_k) w_k (1 - w_k);
+ *   grad_c_k = w_k G^c_k + du_k W_hyp,  grad_k_r_k = w_k G^R_k,
+ *   grad_w_hyp = sum_k du_k (c_k + pe_k).
+ * The forward pieces it needs (gates, partial merges, K^C and V, softmax
+ * normalisers) are recomputed from the inputs.
+ *   q_c, q_r, c, k_r, w_hyp, pe, pe_rows, w_uk, w_uv: as for mtla_prefill.
+ *   grad_out  device [B, N, H, d_h] (storage dtype): dL/do.
+ *   grad_q_c  device [B, N, H, d_h], grad_q_r [B, N, H, d_r],
+ *   grad_c    device [B, N, d_c],    grad_k_r [B, N, d_r] (storage dtype),
+ *             written.
+ *   grad_w_hyp device [d_c] fp32; grad_w_uk, grad_w_uv device [H, d_h, d_c]
+ *             fp32: written (not accumulated), summed over the B sequences.
+ *   workspace device, >= mtla_prefill_backward_workspace_bytes(), 16-byte
+ *             aligned; scratch.
+ * Requires heads * d_h a multiple of 4, batch and heads <= 65535.  With
+ * batch or n_tokens 0 only the weight gradients are written (as zeros).
+ * All checks run before anything is enqueued.
+ */
+int32_t mtla_prefill_backward(const mtla_dims* dims, int32_t n_tokens, const void* q_c, const void* q_r,
+                              const void* c, const void* k_r, const float* w_hyp, const float* pe,
+                              int32_t pe_rows, const void* w_uk, const void* w_uv, const void* grad_out,
+                              void* grad_q_c, void* grad_q_r, void* grad_c, void* grad_k_r, float* grad_w_hyp,
+                              float* grad_w_uk, float* grad_w_uv, void* workspace, size_t ws_bytes, void* stream);
+
 /*
  * Test hooks: the integer predicates the kernels use, exported for bit-exact
  * comparison.  Page: "Multi-head Temporal Latent Attention", Key claims (paper

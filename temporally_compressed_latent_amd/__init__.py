@@ -1,5 +1,6 @@
 """MI355X-native MTLA hot path: merge/append into a temporally compressed
-latent cache, absorbed-form decode, and stride-masked parallel prefill.
+latent cache, absorbed-form decode, stride-masked parallel prefill, the
+decoder layer around them, and the training backward of the parallel pass.
 
 The compute runs in libmtla.so (hand-written HIP kernels for gfx950 behind a
 C ABI, declared in include/mtla.h).  This package is its thin binding; torch
@@ -14,6 +15,6 @@ from ._lib import (  # noqa: F401
     mtla_prefill, mtla_prefill_at, mtla_prefill_at_workspace_bytes, mtla_prefill_workspace_bytes,
     mtla_reorder_state, mtla_sinusoidal_pe, mtla_up_project, mtla_project_inputs, mtla_output_project,
     mtla_layer_decode_workspace_bytes, mtla_layer_decode_step, mtla_layer_prefill_workspace_bytes,
-    mtla_layer_prefill,
+    mtla_layer_prefill, mtla_prefill_backward, mtla_prefill_backward_workspace_bytes,
     mtla_version, status_string,
 )

@@ -109,6 +109,9 @@ _SIGS = {
     "mtla_layer_prefill": (_I, [_D, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ,
                                 _P]),
     "mtla_prefill_at": (_I, [_D, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mtla_prefill_backward_workspace_bytes": (_I, [_D, _I, ctypes.POINTER(_SZ)]),
+    "mtla_prefill_backward": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _P, _SZ, _P]),
     "mtla_debug_stride_mask": (_I, [_I, _I, _P, _P]),
     "mtla_debug_slot_limits": (_I, [_I, _I, _P, _P]),
 }
@@ -341,6 +344,40 @@ def mtla_prefill(dims: MtlaDims, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_uv, cache,
         _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
         _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
         _tensor("out", out, (B, N, H, dims.d_h), st),
+        ws, ws_bytes, _stream(stream)))
+
+
+def mtla_prefill_backward_workspace_bytes(dims: MtlaDims, n_tokens: int) -> int:
+    n = _SZ(0)
+    _check(_lib.mtla_prefill_backward_workspace_bytes(ctypes.byref(dims), n_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def mtla_prefill_backward(dims: MtlaDims, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_uv, grad_out,
+                          grad_q_c, grad_q_r, grad_c, grad_k_r, grad_w_hyp, grad_w_uk, grad_w_uv,
+                          workspace, stream=None) -> None:
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    N = int(c.shape[1]) if c.dim() == 3 else -1
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    nr = dims.d_r == 0
+    _check(_lib.mtla_prefill_backward(
+        ctypes.byref(dims), N,
+        _tensor("q_c", q_c, (B, N, H, dims.d_h), st),
+        _tensor("q_r", q_r, (B, N, H, dims.d_r), st, optional=nr),
+        _tensor("c", c, (B, N, dims.d_c), st),
+        _tensor("k_r", k_r, (B, N, dims.d_r), st, optional=nr),
+        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("grad_out", grad_out, (B, N, H, dims.d_h), st),
+        _tensor("grad_q_c", grad_q_c, (B, N, H, dims.d_h), st),
+        _tensor("grad_q_r", grad_q_r, (B, N, H, dims.d_r), st, optional=nr),
+        _tensor("grad_c", grad_c, (B, N, dims.d_c), st),
+        _tensor("grad_k_r", grad_k_r, (B, N, dims.d_r), st, optional=nr),
+        _tensor("grad_w_hyp", grad_w_hyp, (dims.d_c,), torch.float32),
+        _tensor("grad_w_uk", grad_w_uk, (H, dims.d_h, dims.d_c), torch.float32),
+        _tensor("grad_w_uv", grad_w_uv, (H, dims.d_h, dims.d_c), torch.float32),
         ws, ws_bytes, _stream(stream)))
 
 

@@ -867,6 +867,198 @@ int32_t mtla_layer_prefill(const mtla_dims* dims, int32_t d_model, int32_t t0, i
   return mtla_output_project(dims, d_model, n_tokens * dims->batch, o, w_o, y, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Training backward of the parallel pass.
+// ---------------------------------------------------------------------------
+namespace {
+struct BwdWs {
+  size_t P, gate, KV, lse, D, dKV, Wt, dPc, wg_part, wh_part, total;
+  int wg_splits, wh_parts;
+};
+
+BwdWs bwd_ws(const mtla_dims* d, int n) {
+  const size_t B = d->batch, H = d->heads, N = n, R = B * N, W = d->d_c + d->d_r;
+  const size_t KV2 = 2 * H * d->d_h, e = elem_bytes(d);
+  BwdWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  w.P = take(R * W * e);
+  w.gate = take(R * 4);
+  w.KV = take(R * KV2 * e);
+  w.lse = take(B * H * N * 4);
+  w.D = take(B * H * N * 4);
+  w.dKV = take(R * (KV2 + H * d->d_r) * e);
+  w.Wt = take(size_t(d->d_c) * KV2 * e);
+  w.dPc = take(R * d->d_c * 4);
+  // split the weight-gradient product over rows so that ~2048 workgroups run
+  const size_t tiles = ((KV2 + 63) / 64) * ((d->d_c + 63) / 64);
+  w.wg_splits = static_cast<int>(std::max<size_t>(1, std::min<size_t>((2048 + tiles - 1) / tiles, (R + 255) / 256)));
+  w.wg_part = take(size_t(w.wg_splits) * KV2 * d->d_c * 4);
+  const size_t blocks = B * ((N + d->stride_s - 1) / d->stride_s);
+  w.wh_parts = static_cast<int>(std::max<size_t>(1, std::min<size_t>(blocks, 1024)));
+  w.wh_part = take(size_t(w.wh_parts) * d->d_c * 4);
+  w.total = off;
+  return w;
+}
+
+int32_t check_backward(const mtla_dims* dims, int32_t n_tokens) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
+  if ((int64_t(dims->heads) * dims->d_h) % 4 != 0)
+    return fail(MTLA_ERR_UNSUPPORTED, "heads*d_h=%lld must be a multiple of 4",
+                static_cast<long long>(int64_t(dims->heads) * dims->d_h));
+  if (dims->batch > 65535 || dims->heads > 65535)
+    return fail(MTLA_ERR_UNSUPPORTED, "batch=%d and heads=%d must be <= 65535", dims->batch, dims->heads);
+  if (2 * int64_t(dims->heads) * dims->d_h * dims->d_c > INT32_MAX)
+    return fail(MTLA_ERR_UNSUPPORTED, "W_UK and W_UV of %d x %d x %d are too large", dims->heads, dims->d_h,
+                dims->d_c);
+  const int64_t R = int64_t(dims->batch) * n_tokens;
+  const int64_t width = 2 * int64_t(dims->heads) * dims->d_h + int64_t(dims->heads) * dims->d_r;
+  if (R > INT32_MAX || R * std::max<int64_t>(width, dims->d_c + dims->d_r) > kMaxElems)
+    return fail(MTLA_ERR_UNSUPPORTED, "%lld token rows are too many", static_cast<long long>(R));
+  return ok();
+}
+}  // namespace
+
+int32_t mtla_prefill_backward_workspace_bytes(const mtla_dims* dims, int32_t n_tokens, size_t* bytes) {
+  int32_t st = check_backward(dims, n_tokens);
+  if (st != MTLA_OK) return st;
+  if (!bytes) return fail(MTLA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = bwd_ws(dims, n_tokens).total;
+  return ok();
+}
+
+int32_t mtla_prefill_backward(const mtla_dims* dims, int32_t n_tokens, const void* q_c, const void* q_r,
+                              const void* c, const void* k_r, const float* w_hyp, const float* pe,
+                              int32_t pe_rows, const void* w_uk, const void* w_uv, const void* grad_out,
+                              void* grad_q_c, void* grad_q_r, void* grad_c, void* grad_k_r, float* grad_w_hyp,
+                              float* grad_w_uk, float* grad_w_uv, void* workspace, size_t ws_bytes, void* stream) {
+  int32_t st = check_backward(dims, n_tokens);
+  if (st != MTLA_OK) return st;
+  if (pe_rows < n_tokens) return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < n_tokens=%d", pe_rows, n_tokens);
+  CHECK_PTR_ALIGN(w_hyp, 4);
+  CHECK_PTR(w_uk);
+  CHECK_PTR(w_uv);
+  CHECK_PTR_ALIGN(grad_w_hyp, 4);
+  CHECK_PTR_ALIGN(grad_w_uk, 4);
+  CHECK_PTR_ALIGN(grad_w_uv, 4);
+  const BwdWs ws = bwd_ws(dims, n_tokens);
+  const bool empty = dims->batch == 0 || n_tokens == 0;
+  if (!empty) {
+    CHECK_PTR(q_c);
+    CHECK_PTR(c);
+    CHECK_PTR_ALIGN(pe, 4);
+    CHECK_PTR(grad_out);
+    CHECK_PTR(grad_q_c);
+    CHECK_PTR(grad_c);
+    if (dims->d_r > 0) {
+      CHECK_PTR(q_r);
+      CHECK_PTR(k_r);
+      CHECK_PTR(grad_q_r);
+      CHECK_PTR(grad_k_r);
+    }
+    if (!workspace) return fail(MTLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws.total);
+    if (!aligned16(workspace)) return fail(MTLA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (ws_bytes < ws.total)
+      return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, ws.total);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = dims->heads, d_h = dims->d_h, dc = dims->d_c, dr = dims->d_r, W = dc + dr;
+  const int KV2 = 2 * H * d_h;
+  hipError_t e;
+  if (empty) {
+    // the gradients of the weights are sums over no tokens
+    if ((e = mtla::launch_sum_parts(nullptr, 0, dc, grad_w_hyp, s)) != hipSuccess)
+      return hip_status(e, "backward zero-fill launch");
+    if ((e = mtla::launch_sum_parts(nullptr, 0, H * d_h * dc, grad_w_uk, s)) != hipSuccess)
+      return hip_status(e, "backward zero-fill launch");
+    return hip_status(mtla::launch_sum_parts(nullptr, 0, H * d_h * dc, grad_w_uv, s), "backward zero-fill launch");
+  }
+  const int R = dims->batch * n_tokens;
+  mtla::BwdArgs a{};
+  a.B = dims->batch;
+  a.N = n_tokens;
+  a.H = H;
+  a.d_h = d_h;
+  a.d_c = dc;
+  a.d_r = dr;
+  a.s = dims->stride_s;
+  a.scale = dims->softmax_scale;
+  a.q_c = q_c;
+  a.q_r = q_r;
+  a.c = c;
+  a.k_r = k_r;
+  a.w_hyp = w_hyp;
+  a.pe = pe;
+  a.d_o = grad_out;
+  a.P = at(workspace, ws.P);
+  a.gate = reinterpret_cast<float*>(at(workspace, ws.gate));
+  a.KV = at(workspace, ws.KV);
+  a.lse = reinterpret_cast<float*>(at(workspace, ws.lse));
+  a.D = reinterpret_cast<float*>(at(workspace, ws.D));
+  a.dKV = at(workspace, ws.dKV);
+  a.dPc = reinterpret_cast<float*>(at(workspace, ws.dPc));
+  a.g_q_c = grad_q_c;
+  a.g_q_r = grad_q_r;
+  a.g_c = grad_c;
+  a.g_k_r = grad_k_r;
+  a.wh_part = reinterpret_cast<float*>(at(workspace, ws.wh_part));
+  a.wh_parts = ws.wh_parts;
+  const int ldk = KV2 + H * dr;
+  // forward recomputation: gates and partial merges, then K^C and V of every token
+  if ((e = mtla::launch_bwd_partials(a, dims->dtype, s)) != hipSuccess)
+    return hip_status(e, "backward partials launch");
+  mtla::LayerGemmArgs kv{};
+  kv.M = R;
+  kv.N = KV2;
+  kv.K = dc;
+  kv.A = a.P;
+  kv.lda = W;
+  kv.w0 = w_uk;
+  kv.n0 = H * d_h;
+  kv.w1 = w_uv;
+  kv.n1 = H * d_h;
+  kv.w2 = w_uv;
+  kv.mode = 0;
+  kv.out = at(workspace, ws.KV);
+  if ((e = mtla::launch_layer_gemm(kv, dims->dtype, s)) != hipSuccess)
+    return hip_status(e, "backward K/V up-projection launch");
+  // attention backward: dq (with lse and D), then dK^C, dK^R, dV of every key token
+  if ((e = mtla::launch_bwd_attention(a, dims->dtype, s)) != hipSuccess)
+    return hip_status(e, "backward attention launch");
+  // dP^c = [dK^C | dV] [W_UK ; W_UV]
+  void* wt = at(workspace, ws.Wt);
+  if ((e = mtla::launch_bwd_transpose_w(H * d_h, dc, w_uk, w_uv, wt, dims->dtype, s)) != hipSuccess)
+    return hip_status(e, "backward weight transpose launch");
+  mtla::LayerGemmArgs dp{};
+  dp.M = R;
+  dp.N = dc;
+  dp.K = KV2;
+  dp.A = a.dKV;
+  dp.lda = ldk;
+  dp.w0 = wt;
+  dp.n0 = dc;
+  dp.w1 = wt;
+  dp.w2 = wt;
+  dp.mode = 0;
+  dp.out = at(workspace, ws.dPc);
+  dp.out_f32 = 1;
+  if ((e = mtla::launch_layer_gemm(dp, dims->dtype, s)) != hipSuccess)
+    return hip_status(e, "backward dP launch");
+  // dW_UK, dW_UV = [dK^C | dV]^T P^c, summed over every token of the batch
+  if ((e = mtla::launch_bwd_wgrad(R, KV2, dc, a.dKV, ldk, a.P, W, reinterpret_cast<float*>(at(workspace, ws.wg_part)),
+                                  ws.wg_splits, grad_w_uk, H * d_h, grad_w_uv, dims->dtype, s)) != hipSuccess)
+    return hip_status(e, "backward weight-gradient launch");
+  // reverse in-block sums, gate backward, dc, dk^R and dW_hyp
+  if ((e = mtla::launch_bwd_scan(a, dims->dtype, s)) != hipSuccess) return hip_status(e, "backward scan launch");
+  return hip_status(mtla::launch_sum_parts(a.wh_part, ws.wh_parts, dc, grad_w_hyp, s), "backward dW_hyp launch");
+}
+
 int32_t mtla_debug_stride_mask(int32_t n, int32_t s, uint8_t* mask, void* stream) {
   if (n < 1 || s < 1) return fail(MTLA_ERR_INVALID_ARG, "n=%d, s=%d must be >= 1", n, s);
   if (int64_t(n) * n > kMaxElems) return fail(MTLA_ERR_UNSUPPORTED, "mask too large");

@@ -65,8 +65,50 @@ struct LayerGemmArgs {
   void* k_r;
   void* q_c;
   void* q_r;
+  int lda = 0;          // row stride of A in elements (0: K)
+  int out_f32 = 0;      // mode 0: out is fp32 whatever the storage type
 };
 hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st);
+
+// Training backward of the parallel pass.  Rows r = b * N + t (token t,
+// 0-based, of sequence b); R = B * N; QW = d_h + d_r; KV2 = 2 * H * d_h.
+struct BwdArgs {
+  int B, N, H, d_h, d_c, d_r, s;
+  float scale;
+  const void* q_c;    // [B, N, H, d_h]
+  const void* q_r;    // [B, N, H, d_r]
+  const void* c;      // [R, d_c]
+  const void* k_r;    // [R, d_r]
+  const float* w_hyp; // [d_c]
+  const float* pe;    // [>= N, d_c], row t for token t
+  const void* d_o;    // [B, N, H, d_h]
+  void* P;            // [R, d_c + d_r] partial merges (written by the partials kernel)
+  float* gate;        // [R]
+  const void* KV;     // [R, KV2]: K^C of (h, e) at column h d_h + e, V at H d_h + h d_h + e
+  float* lse;         // [B, H, N] natural-log softmax normaliser of each query
+  float* D;           // [B, H, N] sum_j p_ij (dO_i . V_j) = dO_i . o_i
+  void* dKV;          // [R, KV2 + H d_r]: dK^C, dV as KV, then dK^R of (h, r) at KV2 + h d_r + r
+  const float* dPc;   // [R, d_c] fp32: gradient of P^c through the up-projection
+  void* g_q_c;        // gradients written: [B, N, H, d_h], [B, N, H, d_r], [R, d_c], [R, d_r]
+  void* g_q_r;
+  void* g_c;
+  void* g_k_r;
+  float* wh_part;     // [wh_parts, d_c] fp32 per-wave partial sums of dW_hyp
+  int wh_parts;
+};
+hipError_t launch_bwd_partials(const BwdArgs& a, int dtype, hipStream_t st);
+hipError_t launch_bwd_attention(const BwdArgs& a, int dtype, hipStream_t st);
+hipError_t launch_bwd_scan(const BwdArgs& a, int dtype, hipStream_t st);
+// Wt[n, k] = stacked [W_UK ; W_UV] ([KV2, d_c]) transposed: [d_c, KV2].
+hipError_t launch_bwd_transpose_w(int KV2h, int d_c, const void* w_uk, const void* w_uv, void* wt, int dtype,
+                                  hipStream_t st);
+// out[m, n] = sum over rows r of A[r, m] Bm[r, n] (m < M, n < N), rows split
+// into `splits` chunks whose fp32 partial products go to part[split, M, N];
+// then out = the fixed-order sum of the partials.
+hipError_t launch_bwd_wgrad(int R, int M, int N, const void* A, int lda, const void* Bm, int ldb, float* part,
+                            int splits, float* out0, int m0_rows, float* out1, int dtype, hipStream_t st);
+// out[i] = sum_{p < parts} part[p * n + i], in order of p.
+hipError_t launch_sum_parts(const float* part, int parts, int n, float* out, hipStream_t st);
 
 hipError_t launch_sinusoidal_pe(int rows, int d, float* pe, hipStream_t st);
 hipError_t launch_debug_mask(int n, int s, uint8_t* mask, hipStream_t st);

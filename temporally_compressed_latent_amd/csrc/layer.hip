@@ -112,8 +112,13 @@ __device__ __forceinline__ void store_pair(const LayerGemmArgs& g, const PairDes
   switch (p.kind) {
     case 0:
       i = static_cast<size_t>(m) * g.N + n;
-      store_val<T>(g.out, i, x0);
-      if (n + 1 < g.N) store_val<T>(g.out, i + 1, x1);
+      if (g.out_f32) {
+        static_cast<float*>(g.out)[i] = x0;
+        if (n + 1 < g.N) static_cast<float*>(g.out)[i + 1] = x1;
+      } else {
+        store_val<T>(g.out, i, x0);
+        if (n + 1 < g.N) store_val<T>(g.out, i + 1, x1);
+      }
       return;
     case 1:
       i = static_cast<size_t>(m) * g.d_c + n;
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(256) void layer_gemm_kernel(LayerGemmArgs g) {
   for (int i = 0; i < CPT; ++i) {
     const int c = tid + 256 * i, r = c / CPR;
     kofs[i] = (c % CPR) * EPC;
-    arow[i] = static_cast<const T*>(g.A) + static_cast<size_t>(min(m0 + r, M - 1)) * K;
+    arow[i] = static_cast<const T*>(g.A) + static_cast<size_t>(min(m0 + r, M - 1)) * (g.lda ? g.lda : K);
     wrow[i] = weight_row<T>(g, min(n0 + r, N - 1));
   }
   uint4 ra[CPT], rw[CPT];
@@ -294,7 +299,8 @@ __global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(LayerGemmArgs g)
   const uint16_t* ar[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    ar[i] = static_cast<const uint16_t*>(g.A) + static_cast<size_t>(min(16 * i + c16, M - 1)) * K + 8 * g16;
+    ar[i] = static_cast<const uint16_t*>(g.A) + static_cast<size_t>(min(16 * i + c16, M - 1)) * (g.lda ? g.lda : K) +
+            8 * g16;
   f32x4 acc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};

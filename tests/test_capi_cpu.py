@@ -25,7 +25,7 @@ def dims(**kw):
 
 def test_exports_every_header_symbol():
     syms = m.header_symbols()
-    assert len(syms) == 26
+    assert len(syms) == 28
     for s in syms:
         assert hasattr(m.lib(), s), s
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
@@ -278,3 +278,29 @@ def test_binding_rejects_wrong_tensors_before_the_library():
         m.mtla_merge_append(d, torch.zeros(4, dtype=torch.int32), torch.zeros(4, 1, 256),
                             torch.zeros(4, 1, 32), torch.zeros(256), torch.zeros(8, 256),
                             torch.zeros(4, 128, 288), torch.zeros(4, 288), stream=0)
+
+
+def test_backward_argument_checks():
+    L, d = m.lib(), dims()
+    n = ctypes.c_size_t(0)
+    assert L.mtla_prefill_backward_workspace_bytes(ctypes.byref(d), 32, ctypes.byref(n)) == m.MTLA_OK
+    need = n.value
+    assert need > 0
+    assert L.mtla_prefill_backward_workspace_bytes(ctypes.byref(d), -1, ctypes.byref(n)) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_prefill_backward_workspace_bytes(ctypes.byref(d), 32, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_prefill_backward_workspace_bytes(ctypes.byref(dims(heads=3, d_h=6)), 32, ctypes.byref(n)) == \
+        m.MTLA_ERR_UNSUPPORTED                                            # heads * d_h not a multiple of 4
+    bwd = lambda **k: L.mtla_prefill_backward(
+        ctypes.byref(k.get("d", d)), k.get("N", 32), k.get("q_c", FAKE), FAKE, FAKE, FAKE, k.get("w_hyp", FAKE),
+        FAKE, k.get("pe_rows", 64), FAKE, FAKE, k.get("g_out", FAKE), FAKE, FAKE, k.get("g_c", FAKE), FAKE,
+        k.get("g_wh", FAKE), FAKE, FAKE, k.get("ws", FAKE), k.get("n", need), None)
+    assert bwd(N=-1) == m.MTLA_ERR_INVALID_ARG
+    assert bwd(pe_rows=16) == m.MTLA_ERR_INVALID_ARG                     # pe shorter than the sequence
+    assert bwd(w_hyp=None) == m.MTLA_ERR_INVALID_ARG
+    assert bwd(g_wh=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
+    assert bwd(q_c=None) == m.MTLA_ERR_INVALID_ARG
+    assert bwd(g_out=None) == m.MTLA_ERR_INVALID_ARG
+    assert bwd(g_c=None) == m.MTLA_ERR_INVALID_ARG
+    assert bwd(ws=None) == m.MTLA_ERR_WORKSPACE
+    assert bwd(ws=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
+    assert bwd(n=need - 16) == m.MTLA_ERR_WORKSPACE
