@@ -218,6 +218,46 @@ def run_prefill(w, steps, warmup, m, torch, workloads):
             "attn_tflops_over_end_to_end_time": f_attn / (ms * 1e-3) / 1e12}, (out, q_c, q_r, lat, qry, wts)
 
 
+def run_backward(w, steps, warmup, m, torch, workloads):
+    """Training backward of the summarisation prefill (B=16, N=4096, s=3):
+    one mtla_prefill_backward call (forward recomputation included) from the
+    same inputs as the prefill and a seeded upstream gradient."""
+    log(f"{w.name} backward: staging inputs")
+    B, N, H = w.batch, w.n_tokens, w.heads
+    d = m.make_dims(B, H, w.d_h, w.d_c, w.d_r, w.s, -(-N // w.s), "bf16")
+    lat, qry, wts = workloads.batch_latents(w), workloads.batch_queries(w), workloads.weights(w)
+    bf, f32 = torch.bfloat16, torch.float32
+    c, k_r = to_dev(lat["c"], bf, torch), to_dev(lat["k_r"], bf, torch)
+    q_c, q_r = to_dev(qry["q_c"], bf, torch), to_dev(qry["q_r"], bf, torch)
+    w_hyp = to_dev(wts["w_hyp"], f32, torch)
+    w_uk, w_uv = to_dev(wts["w_uk"], bf, torch), to_dev(wts["w_uv"], bf, torch)
+    d_o = to_dev(workloads.batch_grad_out(w), bf, torch)
+    pe = torch.empty(N, w.d_c, dtype=f32, device="cuda")
+    m.mtla_sinusoidal_pe(pe)
+    g_qc, g_qr = torch.empty_like(q_c), torch.empty_like(q_r)
+    g_c, g_kr = torch.empty_like(c), torch.empty_like(k_r)
+    g_wh = torch.empty(w.d_c, dtype=f32, device="cuda")
+    g_uk = torch.empty(H, w.d_h, w.d_c, dtype=f32, device="cuda")
+    g_uv = torch.empty_like(g_uk)
+    ws = torch.empty(m.mtla_prefill_backward_workspace_bytes(d, N), dtype=torch.uint8, device="cuda")
+
+    def fn():
+        m.mtla_prefill_backward(d, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_uv, d_o, g_qc, g_qr, g_c, g_kr, g_wh,
+                                g_uk, g_uv, ws)
+    g = capture(fn, torch)
+    for _ in range(warmup):
+        g.replay()
+    ms = timed_graph(g, steps, torch)
+    A = attended_pairs(N, w.s)
+    QW = w.d_h + w.d_r
+    # per attended pair and head: the score recomputation, dP = dO V^T, dV,
+    # dK and dQ products; plus the K/V recomputation, dP^c and dW products
+    f_attn = 2.0 * B * H * A * (3 * QW + 2 * w.d_h)
+    f_gemm = 3 * 4.0 * B * N * w.d_c * H * w.d_h
+    return {"workload": w.name + "_backward", "ms_per_call": ms, "attn_gflop": f_attn / 1e9,
+            "gemm_gflop": f_gemm / 1e9, "tflops_end_to_end": (f_attn + f_gemm) / (ms * 1e-3) / 1e12}
+
+
 def run_prefill_chunk(w, steps, warmup, m, torch, workloads):
     """Chunked prefill of the summarisation shape: the first t0 tokens by
     mtla_prefill (untimed), then tokens t0+1..N by one mtla_prefill_at call
@@ -540,6 +580,7 @@ def main():
               "prefill_chunk": lambda: run_prefill_chunk(W[3], args.steps, args.warmup, m, torch, workloads),
               "reorder": lambda: run_reorder(W[4], args.steps, args.warmup, m, torch),
               "layer_decode": lambda: run_layer_decode(W[1], args.steps, args.warmup, m, torch, workloads),
+              "backward": lambda: run_backward(W[3], args.steps, args.warmup, m, torch, workloads),
               "layer_prefill": lambda: run_layer_prefill(W[3], args.steps, args.warmup, m, torch, workloads),
               "llm_decode": lambda: run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0],
               "copy": lambda: run_copy(args.steps, args.warmup, torch)}

@@ -241,65 +241,74 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(BwdArgs a) {
 }
 
 // Reverse in-block sum of dP and the gate backward: one wave per (sequence,
-// block), blocks dealt out to wh_parts waves in turn; each wave keeps its own
-// fp32 partial sum of dW_hyp.
+// block of s tokens), its tokens last to first; lane l holds columns l,
+// l + 64, ... of the running sum G.  Writes dc, dk^R and du of every token.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = (blockIdx.x * 256 + threadIdx.x) >> 6;
-  if (wv >= a.wh_parts) return;
   const int nblk = (a.N + a.s - 1) / a.s;
+  if (wv >= a.B * nblk) return;
+  const int b = wv / nblk, blk = wv % nblk;
   const int W = a.d_c + a.d_r, KV2 = 2 * a.H * a.d_h, ldk = KV2 + a.H * a.d_r;
-  float whp[16];
+  const int t0 = blk * a.s, t1 = min(t0 + a.s, a.N);
+  float G[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) whp[j] = 0.f;
-  for (int blkid = wv; blkid < a.B * nblk; blkid += a.wh_parts) {
-    const int b = blkid / nblk, blk = blkid % nblk;
-    const int t0 = blk * a.s, t1 = min(t0 + a.s, a.N);
-    float G[16];
+  for (int j = 0; j < 16; ++j) G[j] = 0.f;
+  for (int t = t1 - 1; t >= t0; --t) {
+    const size_t row = static_cast<size_t>(b) * a.N + t;
+    const float w = a.gate[row];
+    float x[16], dwl = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) G[j] = 0.f;
-    for (int t = t1 - 1; t >= t0; --t) {
-      const size_t row = static_cast<size_t>(b) * a.N + t;
-      const float w = a.gate[row];
-      float x[16], dwl = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int e = lane + 64 * j;
-        x[j] = 0.f;
-        if (e >= W) continue;
-        float dP;
-        if (e < a.d_c) {
-          dP = a.dPc[row * a.d_c + e];
-          x[j] = ld<T>(a.c, row * a.d_c + e);
-        } else {
-          const int r = e - a.d_c;
-          dP = 0.f;
-          for (int hh = 0; hh < a.H; ++hh) dP += ld<T>(a.dKV, row * ldk + KV2 + hh * a.d_r + r);
-          x[j] = ld<T>(a.k_r, row * a.d_r + r);
-        }
-        G[j] += dP;
-        dwl = fmaf(G[j], x[j], dwl);
+    for (int j = 0; j < 16; ++j) {
+      const int e = lane + 64 * j;
+      x[j] = 0.f;
+      if (e >= W) continue;
+      float dP;
+      if (e < a.d_c) {
+        dP = a.dPc[row * a.d_c + e];
+        x[j] = ld<T>(a.c, row * a.d_c + e);
+      } else {
+        const int r = e - a.d_c;
+        dP = 0.f;
+        for (int hh = 0; hh < a.H; ++hh) dP += ld<T>(a.dKV, row * ldk + KV2 + hh * a.d_r + r);
+        x[j] = ld<T>(a.k_r, row * a.d_r + r);
       }
-      const float du = wave_sum(dwl) * w * (1.f - w);
+      G[j] += dP;
+      dwl = fmaf(G[j], x[j], dwl);
+    }
+    const float du = wave_sum(dwl) * w * (1.f - w);
+    if (lane == 0) a.du[row] = du;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int e = lane + 64 * j;
-        if (e >= W) continue;
-        if (e < a.d_c) {
-          st<T>(a.g_c, row * a.d_c + e, fmaf(du, a.w_hyp[e], w * G[j]));
-          whp[j] = fmaf(du, x[j] + a.pe[static_cast<size_t>(t) * a.d_c + e], whp[j]);
-        } else {
-          st<T>(a.g_k_r, row * a.d_r + (e - a.d_c), w * G[j]);
-        }
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int e = lane + 64 * j;
+      if (e >= W) continue;
+      if (e < a.d_c)
+        st<T>(a.g_c, row * a.d_c + e, fmaf(du, a.w_hyp[e], w * G[j]));
+      else
+        st<T>(a.g_k_r, row * a.d_r + (e - a.d_c), w * G[j]);
     }
   }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int e = lane + 64 * j;
-    if (e < a.d_c) a.wh_part[static_cast<size_t>(wv) * a.d_c + e] = whp[j];
-  }
+}
+
+// Partial sums of dW_hyp = sum_r du_r (c_r + pe_t(r)) over one chunk of rows:
+// 64 columns x 4 row groups per workgroup, the groups added in a fixed order.
+template <typename T>
+__global__ __launch_bounds__(256) void dwhyp_kernel(BwdArgs a, int rows_per_split) {
+  __shared__ float red[4][64];
+  const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + cl;
+  const int R = a.B * a.N;
+  const int r0 = blockIdx.y * rows_per_split, r1 = min(R, r0 + rows_per_split);
+  float acc = 0.f;
+  if (col < a.d_c)
+    for (int r = r0 + rg; r < r1; r += 4)
+      acc = fmaf(a.du[r], ld<T>(a.c, static_cast<size_t>(r) * a.d_c + col) + a.pe[static_cast<size_t>(r % a.N) * a.d_c + col],
+                 acc);
+  red[rg][cl] = acc;
+  __syncthreads();
+  if (rg == 0 && col < a.d_c)
+    a.wh_part[static_cast<size_t>(blockIdx.y) * a.d_c + col] = (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]);
 }
 
 template <typename T>
@@ -379,12 +388,717 @@ __global__ __launch_bounds__(256) void sum_split_rows_kernel(const float* part, 
     out1[idx - static_cast<size_t>(m0_rows) * N] = acc;
 }
 
+// out[i] = sum over p of part[p n + i]: 64 columns x 4 groups of parts per
+// workgroup, the groups added in a fixed order.
 __global__ __launch_bounds__(256) void sum_parts_kernel(const float* part, int parts, int n, float* out) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+  __shared__ float red[4][64];
+  const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + cl;
   float acc = 0.f;
-  for (int p = 0; p < parts; ++p) acc += part[static_cast<size_t>(p) * n + i];
-  out[i] = acc;
+  if (col < n)
+    for (int p = rg; p < parts; p += 4) acc += part[static_cast<size_t>(p) * n + col];
+  red[rg][cl] = acc;
+  __syncthreads();
+  if (rg == 0 && col < n) out[col] = (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA pieces (bf16 storage, 32x32x16 bf16 MFMA with fp32 accumulation).
+//
+// Accumulator layout of a 32x32 product C (f32x16 per lane): lane
+// (grp = lane / 32, c32 = lane % 32) holds column c32, rows 8 (i / 4) +
+// 4 grp + i % 4 for i = 0..15.  A product that contracts over those 32 rows
+// takes them 16 at a time (chunk c) as the B operand, with contraction index
+// kappa = 8 grp + r standing for row 16 c + 4 grp + r (r < 4) or
+// 16 c + 8 + 4 grp + (r - 4) (r >= 4); its A operand is read from a
+// row-major LDS tile with that same row order by transposing LDS reads.  The
+// same transposing read gives the B operand of a product whose two operands
+// both contract over the rows of LDS tiles.
+// ---------------------------------------------------------------------------
+constexpr int BTS = 64;  // rows of one LDS tile: slots (dQ) or queries (dK, dV)
+
+// Chunk c (0 or 1) of one 32-row accumulator x: its rows 16 c .. 16 c + 15.
+__device__ __forceinline__ bf16x8 acc_chunk_bf16(const f32x16& x, int c) {
+  const int jb = 2 * c;
+  u16x8 pk;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pk[r] = f32_to_bf16_bits(x[4 * jb + r]);
+    pk[4 + r] = f32_to_bf16_bits(x[4 * (jb + 1) + r]);
+  }
+  return __builtin_bit_cast(bf16x8, pk);
+}
+
+// Operand with rows (A) or columns (B) = tile columns 32 ft .. 32 ft + 31,
+// contraction over the tile's rows 16 c .. 16 c + 15 in acc_chunk_bf16's order.
+__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* tile, int pitch, int c, int ft, int lane) {
+  const int q16 = lane >> 4, k16 = lane & 15;
+  const int sb0 = 16 * c + 4 * (q16 >> 1);
+  const int col0 = 32 * ft + 16 * (q16 & 1);
+  const uint16_t* base = tile + (sb0 + (k16 >> 2)) * pitch + col0 + 4 * (k16 & 3);
+  const s16x4 lo4 = lds_read_tr16(base);
+  const s16x4 hi4 = lds_read_tr16(base + 8 * pitch);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ float dot8_bf16(const uint4 x, const uint4 y) {
+  const u16x8 a = __builtin_bit_cast(u16x8, x), b = __builtin_bit_cast(u16x8, y);
+  float acc = 0.f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc = fmaf(bf16_bits_to_f32(a[r]), bf16_bits_to_f32(b[r]), acc);
+  return acc;
+}
+
+__device__ __forceinline__ uint4 scale8_bf16(const uint4 x, float f) {
+  const u16x8 a = __builtin_bit_cast(u16x8, x);
+  u16x8 o;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) o[r] = f32_to_bf16_bits(bf16_bits_to_f32(a[r]) * f);
+  return __builtin_bit_cast(uint4, o);
+}
+
+__device__ __forceinline__ uint2 pack4_bf16(float x0, float x1, float x2, float x3) {
+  return uint2{static_cast<uint32_t>(f32_to_bf16_bits(x0)) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16),
+               static_cast<uint32_t>(f32_to_bf16_bits(x2)) | (static_cast<uint32_t>(f32_to_bf16_bits(x3)) << 16)};
+}
+
+__device__ __forceinline__ void unpack4_bf16(const uint2 v, float (&x)[4]) {
+  x[0] = __uint_as_float(v.x << 16);
+  x[1] = __uint_as_float(v.x & 0xffff0000u);
+  x[2] = __uint_as_float(v.y << 16);
+  x[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+// Workgroup -> (pair, tile), XCD-aware.  Workgroup L runs on XCD L % 8; with
+// B*H a multiple of 8 an XCD takes the (sequence, head) pairs x, x + 8, ...
+// one after another, so its concurrent workgroups share a few pairs' rows in
+// its L2.  `high_first` deals a pair's tiles from the last one down.
+__device__ __forceinline__ void pair_and_tile(int L, int npair, int ntile, bool high_first, int& pair, int& tile) {
+  int k;
+  if (npair % 8 == 0) {
+    k = L >> 3;
+    pair = (L & 7) + 8 * (k / ntile);
+    k %= ntile;
+  } else {
+    pair = L % npair;
+    k = L / npair;
+  }
+  tile = high_first ? ntile - 1 - k : k;
+}
+
+// Split-K product over rows on MFMA (bf16): part[split][m][n] = sum over the
+// split's rows r of A[r, m] Bm[r, n], a 128 x 128 tile per workgroup (four
+// waves of 64 x 64, 32x32x16 MFMA).  Both operands contract over the token
+// rows, which run along the rows of their LDS tiles, so both are read by the
+// transposing LDS read in one and the same row order.  Rows past the split's
+// end read as zero through bounded buffer resources.
+constexpr int WGT = 64;  // token rows per LDS stage
+
+__global__ __launch_bounds__(256) void wgrad_mfma_kernel(int R, int M, int N, const uint16_t* A, int lda,
+                                                         const uint16_t* Bm, int ldb, float* part,
+                                                         int rows_per_split) {
+  constexpr int TP = 128 + 8;
+  __shared__ __align__(16) uint16_t sA[2][WGT * TP];
+  __shared__ __align__(16) uint16_t sB[2][WGT * TP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int grp = lane >> 5, c32 = lane & 31;
+  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 128, split = blockIdx.z;
+  const int r0 = split * rows_per_split, nrows = max(0, min(R, r0 + rows_per_split) - r0);
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A + static_cast<size_t>(r0) * lda + m0), static_cast<short>(0),
+      nrows > 0 ? ((nrows - 1) * lda + 128) * 2 : 0, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Bm + static_cast<size_t>(r0) * ldb + n0), static_cast<short>(0),
+      nrows > 0 ? ((nrows - 1) * ldb + 128) * 2 : 0, kBufferRsrcWord3);
+  constexpr int CPT = WGT * 128 / 8 / 256;  // 16-byte chunks per thread and operand
+  int off_a[CPT], off_b[CPT], lds_o[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i, row = c / 16, cc = c % 16;
+    off_a[i] = (row * lda + cc * 8) * 2;
+    off_b[i] = (row * ldb + cc * 8) * 2;
+    lds_o[i] = row * TP + cc * 8;
+  }
+  uint4 ra[CPT], rb[CPT];
+  auto load = [&](int k0) {
+    const int sa = k0 * lda * 2, sb = k0 * ldb * 2;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_a, off_a[i], sa, 0);
+      ra[i] = uint4{v[0], v[1], v[2], v[3]};
+      const auto u = __builtin_amdgcn_raw_buffer_load_b128(rs_b, off_b[i], sb, 0);
+      rb[i] = uint4{u[0], u[1], u[2], u[3]};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      *reinterpret_cast<uint4*>(sA[buf] + lds_o[i]) = ra[i];
+      *reinterpret_cast<uint4*>(sB[buf] + lds_o[i]) = rb[i];
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  int buf = 0;
+  if (nrows > 0) {
+    load(0);
+    store(0);
+    if (WGT < nrows) load(WGT);
+  }
+  __syncthreads();
+  for (int k0 = 0; k0 < nrows; k0 += WGT, buf ^= 1) {
+    if (k0 + WGT < nrows) {
+      store(buf ^ 1);
+      if (k0 + 2 * WGT < nrows) load(k0 + 2 * WGT);
+    }
+#pragma unroll
+    for (int c = 0; c < WGT / 16; ++c) {
+      bf16x8 av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        av[i] = lds_tr_operand(sA[buf], TP, c, 2 * wm + i, lane);
+        bv[i] = lds_tr_operand(sB[buf], TP, c, 2 * wn + i, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // acc[i][j][e]: row m0 + 64 wm + 32 i + 8 (e / 4) + 4 grp + e % 4, column n0 + 64 wn + 32 j + c32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 64 * wm + 32 * i + 8 * (e / 4) + 4 * grp + (e % 4);
+        const int n = n0 + 64 * wn + 32 * j + c32;
+        part[(static_cast<size_t>(split) * M + m) * N + n] = acc[i][j][e];
+      }
+}
+
+// dQ of 128 queries of one (sequence, head): 4 waves of 32 queries, two
+// passes over 64-slot tiles (K^C | P^R and V in LDS, the next tile in flight).
+//   Pass 1: S^T = K Q^T and dP^T = V dO^T give, with an online maximum, each
+//           query's normaliser lse (log2 domain, the diagonal key included)
+//           and D_i = sum_j p_ij dp_ij from the same fp32 probabilities, so
+//           that every row of dS sums to zero as it should.
+//   Pass 2: dS^T = tau P^T (dP^T - D), dQ^T += [K^C | P^R]^T dS^T.
+// Between them each query's diagonal key (j = i) gives p_ii and ds_ii (kept
+// for the dK/dV kernel), the whole dK/dV rows of tokens that are not a
+// completed slot's key, and dQ's diagonal term ds_ii [K^C_i ; P^R_i].
+template <int DH, int DR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_mfma_kernel(BwdArgs a) {
+  constexpr int DQK = DH + DR, KK = DQK / 16, KD = DH / 16, FT = DQK / 32;
+  constexpr int KP = DQK + 8, VP = DH + 8;
+  __shared__ __align__(16) uint16_t sKb[2][BTS * KP];
+  __shared__ __align__(16) uint16_t sVb[2][BTS * VP];
+
+  int pair, qt;
+  pair_and_tile(blockIdx.x, a.B * a.H, a.nqt, true, pair, qt);
+  const int h = pair % a.H, b = pair / a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 5, c32 = lane & 31;
+  const int N = a.N, H = a.H, s = a.s, W = a.d_c + DR, KV2 = 2 * H * DH, ldk = KV2 + H * DR;
+  const int q0 = qt * 128, qw0 = q0 + wave * 32;
+  const float qk = a.scale * kLog2e;
+  const int qi = qw0 + c32;
+  const bool qok = qi < N;
+
+  const uint16_t* qc = static_cast<const uint16_t*>(a.q_c);
+  const uint16_t* qr = static_cast<const uint16_t*>(a.q_r);
+  const uint16_t* dO = static_cast<const uint16_t*>(a.d_o);
+  const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + (static_cast<size_t>(b) * H + h) * N * DH;
+  const uint16_t* vv = static_cast<const uint16_t*>(a.v) + (static_cast<size_t>(b) * H + h) * N * DH;
+  const uint16_t* Pb = static_cast<const uint16_t*>(a.P) + static_cast<size_t>(b) * N * W;
+  const size_t qrow = (static_cast<size_t>(b) * N + (qok ? qi : 0)) * H + h;
+
+  // prologue: operands of this lane's query and its diagonal key
+  bf16x8 qreg[KK], dreg[KD];
+  float zp = 0.f, dpp = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int d0 = 16 * kk + 8 * grp;
+    uint4 qv = uint4{0u, 0u, 0u, 0u}, kv = uint4{0u, 0u, 0u, 0u};
+    if (qok) {
+      if (d0 < DH) {
+        qv = *reinterpret_cast<const uint4*>(qc + qrow * DH + d0);
+        kv = *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(qi) * DH + d0);
+      } else {
+        qv = *reinterpret_cast<const uint4*>(qr + qrow * DR + (d0 - DH));
+        kv = *reinterpret_cast<const uint4*>(Pb + static_cast<size_t>(qi) * W + a.d_c + (d0 - DH));
+      }
+    }
+    qreg[kk] = __builtin_bit_cast(bf16x8, qv);
+    zp += dot8_bf16(qv, kv);
+  }
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) {
+    const int d0 = 16 * kk + 8 * grp;
+    uint4 dv = uint4{0u, 0u, 0u, 0u}, vr = uint4{0u, 0u, 0u, 0u};
+    if (qok) {
+      dv = *reinterpret_cast<const uint4*>(dO + qrow * DH + d0);
+      vr = *reinterpret_cast<const uint4*>(vv + static_cast<size_t>(qi) * DH + d0);
+    }
+    dreg[kk] = __builtin_bit_cast(bf16x8, dv);
+    dpp += dot8_bf16(dv, vr);
+  }
+  zp += __shfl_xor(zp, 32, 64);
+  dpp += __shfl_xor(dpp, 32, 64);
+
+  // completed slots seen by the workgroup's / this wave's last query, and by
+  // every query of this wave
+  const int nk = (min(q0 + 128, N) - 1) / s;
+  const int nk_w = qw0 < N ? (min(qw0 + 32, N) - 1) / s : 0;
+  const int full_w = qw0 / s;
+
+  // slot m's keys are token row s m + s - 1; loads past the last completed
+  // slot's row read as zero through bounded buffer resources
+  constexpr int KN = BTS * DH / 8 / 256, RN = BTS * DR / 8 / 256;
+  static_assert(KN * 256 == BTS * DH / 8 && RN * 256 == BTS * DR / 8, "chunks per thread");
+  const int rows_end = s * nk;
+  const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kc), static_cast<short>(0), rows_end * DH * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vv), static_cast<short>(0), rows_end * DH * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Pb + a.d_c), static_cast<short>(0), rows_end > 0 ? (rows_end - 1) * W * 2 + DR * 2 : 0,
+      kBufferRsrcWord3);
+  int off_k[KN], off_r[RN], lds_k[KN], lds_r[RN], lds_v[KN];
+#pragma unroll
+  for (int i = 0; i < KN; ++i) {
+    const int c = tid + 256 * i, row = c / (DH / 8), cc = c % (DH / 8);
+    off_k[i] = ((s * row + s - 1) * DH + cc * 8) * 2;
+    lds_k[i] = row * KP + cc * 8;
+    lds_v[i] = row * VP + cc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < RN; ++i) {
+    const int c = tid + 256 * i, row = c / (DR / 8), cc = c % (DR / 8);
+    off_r[i] = ((s * row + s - 1) * W + cc * 8) * 2;
+    lds_r[i] = row * KP + DH + cc * 8;
+  }
+  uint4 pk[KN], pr[RN], pv[KN];
+  auto load_tile = [&](int j0) {
+    const int so_kv = s * j0 * DH * 2, so_r = s * j0 * W * 2;
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_k, off_k[i], so_kv, 0);
+      pk[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < RN; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_r, off_r[i], so_r, 0);
+      pr[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_v, off_k[i], so_kv, 0);
+      pv[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sKb[buf] + lds_k[i]) = pk[i];
+#pragma unroll
+    for (int i = 0; i < RN; ++i) *reinterpret_cast<uint4*>(sKb[buf] + lds_r[i]) = pr[i];
+#pragma unroll
+    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sVb[buf] + lds_v[i]) = pv[i];
+  };
+  // S^T and dP^T of one 32-slot half (rt) of the tile in LDS
+  auto scores = [&](const uint16_t* sK, const uint16_t* sV, int rt, f32x16& sc, f32x16& dp) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sK + (32 * rt + c32) * KP + 16 * kk + 8 * grp);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[kk], sc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(sV + (32 * rt + c32) * VP + 16 * kk + 8 * grp);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dreg[kk], dp, 0, 0, 0);
+    }
+  };
+  // one sweep over the slot tiles; body(sK, sV, j0) runs on the tiles this
+  // wave's queries see
+  auto sweep = [&](auto body) {
+    int buf = 0;
+    if (nk > 0) {
+      load_tile(0);
+      store_tile(0);
+      if (BTS < nk) load_tile(BTS);
+    }
+    __syncthreads();
+    for (int j0 = 0; j0 < nk; j0 += BTS, buf ^= 1) {
+      if (j0 + BTS < nk) {
+        store_tile(buf ^ 1);
+        if (j0 + 2 * BTS < nk) load_tile(j0 + 2 * BTS);
+      }
+      if (j0 < nk_w) body(sKb[buf], sVb[buf], j0);
+      __syncthreads();
+    }
+  };
+
+  // pass 1: online normaliser and D, starting from the diagonal key
+  float m = zp * qk;                  // running maximum (log2 units), the same in both lane halves
+  float ls = grp == 0 ? 1.f : 0.f;    // this lane's share of sum exp2(z - m)
+  float dsum = grp == 0 ? dpp : 0.f;  // and of sum exp2(z - m) dp
+  sweep([&](const uint16_t* sK, const uint16_t* sV, int j0) {
+    const bool boundary = j0 + BTS > full_w;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x16 sc, dp;
+      scores(sK, sV, rt, sc, dp);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float z = sc[i] * qk;
+        if (boundary) {
+          const int slot = j0 + 32 * rt + 8 * (i / 4) + 4 * grp + (i % 4);
+          if (s * (slot + 1) > qi) z = -INFINITY;
+        }
+        sc[i] = z;
+        mx = fmaxf(mx, z);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float f = fast_exp2(m - mn);
+      ls *= f;
+      dsum *= f;
+      m = mn;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(sc[i] - m);
+        ls += e;
+        dsum = fmaf(e, dp[i], dsum);
+      }
+    }
+  });
+  const float L = ls + __shfl_xor(ls, 32, 64);
+  const float lse2 = qok ? m + log2f(L) : INFINITY;
+  const float Dq = qok ? (dsum + __shfl_xor(dsum, 32, 64)) / L : 0.f;
+  const float pii = qok ? fast_exp2(fmaf(zp, qk, -lse2)) : 0.f;
+  const float dsii = a.scale * pii * (dpp - Dq);
+  const size_t si = (static_cast<size_t>(b) * H + h) * N + (qok ? qi : 0);
+  if (qok && grp == 0) {
+    a.lse[si] = lse2;
+    a.D[si] = Dq;
+    a.pd[si] = pii;
+    a.dsd[si] = dsii;
+  }
+  if (qok && (qi + 1) % s != 0) {
+    // not a completed slot's key: the diagonal is its only query
+    uint16_t* row = static_cast<uint16_t*>(a.dKV) + (static_cast<size_t>(b) * N + qi) * ldk;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int d0 = 16 * kk + 8 * grp;
+      uint16_t* dst = d0 < DH ? row + h * DH + d0 : row + KV2 + h * DR + (d0 - DH);
+      *reinterpret_cast<uint4*>(dst) = scale8_bf16(__builtin_bit_cast(uint4, qreg[kk]), dsii);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) {
+      const int d0 = 16 * kk + 8 * grp;
+      *reinterpret_cast<uint4*>(row + H * DH + h * DH + d0) = scale8_bf16(__builtin_bit_cast(uint4, dreg[kk]), pii);
+    }
+  }
+  // dQ^T (rows: features, column: this lane's query) starts at ds_ii K_i
+  f32x16 dq[FT];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f0 = 32 * ft + 8 * j + 4 * grp;
+      uint2 kv = uint2{0u, 0u};
+      if (qok)
+        kv = f0 < DH ? *reinterpret_cast<const uint2*>(kc + static_cast<size_t>(qi) * DH + f0)
+                     : *reinterpret_cast<const uint2*>(Pb + static_cast<size_t>(qi) * W + a.d_c + (f0 - DH));
+      float k4[4];
+      unpack4_bf16(kv, k4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dq[ft][4 * j + r] = dsii * k4[r];
+    }
+  }
+
+  // pass 2: dS^T and dQ^T
+  sweep([&](const uint16_t* sK, const uint16_t* sV, int j0) {
+    const bool boundary = j0 + BTS > full_w;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x16 sc, dp;
+      scores(sK, sV, rt, sc, dp);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(sc[i], qk, -lse2));
+        if (boundary) {
+          const int slot = j0 + 32 * rt + 8 * (i / 4) + 4 * grp + (i % 4);
+          if (s * (slot + 1) > qi) p = 0.f;
+        }
+        sc[i] = a.scale * p * (dp[i] - Dq);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 db = acc_chunk_bf16(sc, c);
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft)
+          dq[ft] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(sK, KP, 2 * rt + c, ft, lane), db, dq[ft],
+                                                           0, 0, 0);
+      }
+    }
+  });
+
+  if (qok) {
+    uint16_t* gqc = static_cast<uint16_t*>(a.g_q_c) + qrow * DH;
+    uint16_t* gqr = static_cast<uint16_t*>(a.g_q_r) + qrow * DR;
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int f0 = 32 * ft + 8 * j + 4 * grp;
+        const uint2 v = pack4_bf16(dq[ft][4 * j], dq[ft][4 * j + 1], dq[ft][4 * j + 2], dq[ft][4 * j + 3]);
+        *reinterpret_cast<uint2*>(f0 < DH ? gqc + f0 : gqr + (f0 - DH)) = v;
+      }
+  }
+}
+
+// dK^C, dK^R and dV of 128 completed slots of one (sequence, head): 4 waves
+// of 32 slots, the slot keys and values held in registers as B operands.  The
+// loop runs over 64-query tiles (q^C | q^R, dO, lse and D in LDS, the next
+// tile in flight) from the first query that sees the workgroup's first slot,
+// each tile as two 32-query halves:
+//   S = Q K^T, dP = dO V^T, P = exp2(S tau log2 e - lse) where visible,
+//   dS = tau P (dP - D),  dV^T += dO^T P,  dK^T += Q^T dS.
+// The epilogue adds each slot token's own diagonal query (p_jj dO_j and
+// ds_jj q_j) before storing the rows.
+template <int DH, int DR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkv_mfma_kernel(BwdArgs a, int nslots, int nst) {
+  constexpr int DQK = DH + DR, KK = DQK / 16, KD = DH / 16, FT = DQK / 32, DT = DH / 32;
+  constexpr int QP = DQK + 8, OP = DH + 8;
+  __shared__ __align__(16) uint16_t sQb[2][BTS * QP];
+  __shared__ __align__(16) uint16_t sOb[2][BTS * OP];
+  __shared__ __align__(16) float sLb[2][BTS];
+  __shared__ __align__(16) float sDb[2][BTS];
+
+  int pair, st;
+  pair_and_tile(blockIdx.x, a.B * a.H, nst, false, pair, st);
+  const int h = pair % a.H, b = pair / a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 5, c32 = lane & 31;
+  const int N = a.N, H = a.H, s = a.s, W = a.d_c + DR, KV2 = 2 * H * DH, ldk = KV2 + H * DR;
+  const float qk = a.scale * kLog2e;
+  const int ms0 = st * 128, msw = ms0 + 32 * wave;
+  const int m = msw + c32;
+  const bool mok = m < nslots;
+  const int jt = s * (m + 1) - 1;  // the slot's key token
+
+  const uint16_t* qc = static_cast<const uint16_t*>(a.q_c);
+  const uint16_t* qr = static_cast<const uint16_t*>(a.q_r);
+  const uint16_t* dO = static_cast<const uint16_t*>(a.d_o);
+  const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + (static_cast<size_t>(b) * H + h) * N * DH;
+  const uint16_t* vv = static_cast<const uint16_t*>(a.v) + (static_cast<size_t>(b) * H + h) * N * DH;
+  const uint16_t* Pb = static_cast<const uint16_t*>(a.P) + static_cast<size_t>(b) * N * W;
+  const float* lse2 = a.lse + (static_cast<size_t>(b) * H + h) * N;
+  const float* Dv = a.D + (static_cast<size_t>(b) * H + h) * N;
+
+  bf16x8 kreg[KK], vreg[KD];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int d0 = 16 * kk + 8 * grp;
+    uint4 kv = uint4{0u, 0u, 0u, 0u};
+    if (mok)
+      kv = d0 < DH ? *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(jt) * DH + d0)
+                   : *reinterpret_cast<const uint4*>(Pb + static_cast<size_t>(jt) * W + a.d_c + (d0 - DH));
+    kreg[kk] = __builtin_bit_cast(bf16x8, kv);
+  }
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) {
+    const int d0 = 16 * kk + 8 * grp;
+    uint4 vr = uint4{0u, 0u, 0u, 0u};
+    if (mok) vr = *reinterpret_cast<const uint4*>(vv + static_cast<size_t>(jt) * DH + d0);
+    vreg[kk] = __builtin_bit_cast(bf16x8, vr);
+  }
+  f32x16 dvt[DT], dkt[FT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dvt[t][i] = 0.f;
+#pragma unroll
+  for (int t = 0; t < FT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dkt[t][i] = 0.f;
+
+  // query tiles: queries of this (sequence, head) are rows q of q_c / q_r / dO
+  // at element (b N + q) H + h; rows past N read as zero
+  constexpr int CN = BTS * DH / 8 / 256, CR = BTS * DR / 8 / 256;
+  static_assert(CN * 256 == BTS * DH / 8 && CR * 256 == BTS * DR / 8, "chunks per thread");
+  const size_t rowbase = static_cast<size_t>(b) * N * H + h;
+  const __amdgpu_buffer_rsrc_t rs_qc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(qc + rowbase * DH), static_cast<short>(0), ((N - 1) * H * DH + DH) * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_qr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(qr + rowbase * DR), static_cast<short>(0), ((N - 1) * H * DR + DR) * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_do = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(dO + rowbase * DH), static_cast<short>(0), ((N - 1) * H * DH + DH) * 2, kBufferRsrcWord3);
+  int off_c[CN], off_rr[CR], lq_c[CN], lq_r[CR], lo_c[CN];
+#pragma unroll
+  for (int i = 0; i < CN; ++i) {
+    const int c = tid + 256 * i, row = c / (DH / 8), cc = c % (DH / 8);
+    off_c[i] = (row * H * DH + cc * 8) * 2;
+    lq_c[i] = row * QP + cc * 8;
+    lo_c[i] = row * OP + cc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < CR; ++i) {
+    const int c = tid + 256 * i, row = c / (DR / 8), cc = c % (DR / 8);
+    off_rr[i] = (row * H * DR + cc * 8) * 2;
+    lq_r[i] = row * QP + DH + cc * 8;
+  }
+  uint4 tq[CN], tr[CR], td[CN];
+  float tl = 0.f;
+  auto load_tile = [&](int q0) {
+    const int so_c = q0 * H * DH * 2, so_r = q0 * H * DR * 2;
+#pragma unroll
+    for (int i = 0; i < CN; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_qc, off_c[i], so_c, 0);
+      tq[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < CR; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_qr, off_rr[i], so_r, 0);
+      tr[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < CN; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_do, off_c[i], so_c, 0);
+      td[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+    // threads 0..63 take lse (+inf past N: probability 0), 64..127 take D
+    if (tid < 2 * BTS) {
+      const int q = q0 + (tid & (BTS - 1));
+      tl = tid < BTS ? (q < N ? lse2[q] : INFINITY) : (q < N ? Dv[q] : 0.f);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CN; ++i) *reinterpret_cast<uint4*>(sQb[buf] + lq_c[i]) = tq[i];
+#pragma unroll
+    for (int i = 0; i < CR; ++i) *reinterpret_cast<uint4*>(sQb[buf] + lq_r[i]) = tr[i];
+#pragma unroll
+    for (int i = 0; i < CN; ++i) *reinterpret_cast<uint4*>(sOb[buf] + lo_c[i]) = td[i];
+    if (tid < BTS)
+      sLb[buf][tid] = tl;
+    else if (tid < 2 * BTS)
+      sDb[buf][tid - BTS] = tl;
+  };
+
+  // the first query that sees slot m is token s (m + 1) (0-based)
+  const int qbeg = (s * (ms0 + 1)) / BTS * BTS;
+  const bool wave_on = msw < nslots;
+  const int qfirst_w = s * (msw + 1);  // first query that sees this wave's first slot
+  const int qfull_w = s * (msw + 32);  // from here on every query sees all 32 slots
+  int buf = 0;
+  if (qbeg < N) {
+    load_tile(qbeg);
+    store_tile(0);
+    if (qbeg + BTS < N) load_tile(qbeg + BTS);
+  }
+  __syncthreads();
+  for (int q0 = qbeg; q0 < N; q0 += BTS, buf ^= 1) {
+    if (q0 + BTS < N) {
+      store_tile(buf ^ 1);
+      if (q0 + 2 * BTS < N) load_tile(q0 + 2 * BTS);
+    }
+    const uint16_t* sQ = sQb[buf];
+    const uint16_t* sO = sOb[buf];
+    if (wave_on && q0 + BTS > qfirst_w) {
+      const bool boundary = q0 < qfull_w;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        // S and dP of the tile's 32-query half rt (rows) against this wave's slots (columns)
+        f32x16 sc, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + (32 * rt + c32) * QP + 16 * kk + 8 * grp);
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[kk], sc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          const bf16x8 ao = *reinterpret_cast<const bf16x8*>(sO + (32 * rt + c32) * OP + 16 * kk + 8 * grp);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[kk], dp, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int r0 = 32 * rt + 8 * i4 + 4 * grp;
+          const float4 L4 = *reinterpret_cast<const float4*>(&sLb[buf][r0]);
+          const float4 D4 = *reinterpret_cast<const float4*>(&sDb[buf][r0]);
+          const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * i4 + r;
+            float p = fast_exp2(fmaf(sc[i], qk, -Lr[r]));
+            // completed slot m is visible to query q iff s (m + 1) <= q
+            if (boundary && s * (m + 1) > q0 + r0 + r) p = 0.f;
+            sc[i] = p;
+            dp[i] = a.scale * p * (dp[i] - Dr[r]);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 pb = acc_chunk_bf16(sc, c);
+          const bf16x8 db = acc_chunk_bf16(dp, c);
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+            dvt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(sO, OP, 2 * rt + c, t, lane), pb, dvt[t],
+                                                             0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < FT; ++t)
+            dkt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(sQ, QP, 2 * rt + c, t, lane), db, dkt[t],
+                                                             0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!mok) return;
+  // the slot token's own (diagonal) query, then the rows
+  const size_t si = (static_cast<size_t>(b) * H + h) * N + jt;
+  const float pjj = a.pd[si], dsjj = a.dsd[si];
+  const size_t qrow = (static_cast<size_t>(b) * N + jt) * H + h;
+  uint16_t* row = static_cast<uint16_t*>(a.dKV) + (static_cast<size_t>(b) * N + jt) * ldk;
+#pragma unroll
+  for (int t = 0; t < FT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f0 = 32 * t + 8 * j + 4 * grp;
+      float q4[4];
+      unpack4_bf16(f0 < DH ? *reinterpret_cast<const uint2*>(qc + qrow * DH + f0)
+                           : *reinterpret_cast<const uint2*>(qr + qrow * DR + (f0 - DH)), q4);
+      const uint2 v = pack4_bf16(fmaf(dsjj, q4[0], dkt[t][4 * j]), fmaf(dsjj, q4[1], dkt[t][4 * j + 1]),
+                                 fmaf(dsjj, q4[2], dkt[t][4 * j + 2]), fmaf(dsjj, q4[3], dkt[t][4 * j + 3]));
+      *reinterpret_cast<uint2*>(f0 < DH ? row + h * DH + f0 : row + KV2 + h * DR + (f0 - DH)) = v;
+    }
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f0 = 32 * t + 8 * j + 4 * grp;
+      float d4[4];
+      unpack4_bf16(*reinterpret_cast<const uint2*>(dO + qrow * DH + f0), d4);
+      const uint2 v = pack4_bf16(fmaf(pjj, d4[0], dvt[t][4 * j]), fmaf(pjj, d4[1], dvt[t][4 * j + 1]),
+                                 fmaf(pjj, d4[2], dvt[t][4 * j + 2]), fmaf(pjj, d4[3], dvt[t][4 * j + 3]));
+      *reinterpret_cast<uint2*>(row + H * DH + h * DH + f0) = v;
+    }
 }
 
 }  // namespace
@@ -412,12 +1126,26 @@ hipError_t launch_bwd_attention(const BwdArgs& a, int dtype, hipStream_t st) {
 }
 
 hipError_t launch_bwd_scan(const BwdArgs& a, int dtype, hipStream_t st) {
-  const dim3 grid((a.wh_parts + 3) / 4);
+  const int waves = a.B * ((a.N + a.s - 1) / a.s);
+  const dim3 grid((waves + 3) / 4);
   if (dtype == 0)
     bwd_scan_kernel<float><<<grid, 256, 0, st>>>(a);
   else
     bwd_scan_kernel<uint16_t><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_dwhyp(const BwdArgs& a, float* out, int dtype, hipStream_t st) {
+  const int R = a.B * a.N;
+  const int rows_per_split = (R + a.wh_parts - 1) / a.wh_parts;
+  const dim3 grid((a.d_c + 63) / 64, a.wh_parts);
+  if (dtype == 0)
+    dwhyp_kernel<float><<<grid, 256, 0, st>>>(a, rows_per_split);
+  else
+    dwhyp_kernel<uint16_t><<<grid, 256, 0, st>>>(a, rows_per_split);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_sum_parts(a.wh_part, a.wh_parts, a.d_c, out, st);
 }
 
 hipError_t launch_bwd_transpose_w(int KV2h, int d_c, const void* w_uk, const void* w_uv, void* wt, int dtype,
@@ -433,11 +1161,20 @@ hipError_t launch_bwd_transpose_w(int KV2h, int d_c, const void* w_uk, const voi
   return hipGetLastError();
 }
 
+static bool wgrad_mfma(int M, int N, int dtype) { return dtype != 0 && M % 128 == 0 && N % 128 == 0; }
+
+int bwd_wgrad_tiles(int M, int N, int dtype) {
+  return wgrad_mfma(M, N, dtype) ? (M / 128) * (N / 128) : ((M + 63) / 64) * ((N + 63) / 64);
+}
+
 hipError_t launch_bwd_wgrad(int R, int M, int N, const void* A, int lda, const void* Bm, int ldb, float* part,
                             int splits, float* out0, int m0_rows, float* out1, int dtype, hipStream_t st) {
   const int rows_per_split = (R + splits - 1) / splits;
   const dim3 grid((N + 63) / 64, (M + 63) / 64, splits);
-  if (dtype == 0)
+  if (wgrad_mfma(M, N, dtype))
+    wgrad_mfma_kernel<<<dim3(N / 128, M / 128, splits), 256, 0, st>>>(
+        R, M, N, static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(Bm), ldb, part, rows_per_split);
+  else if (dtype == 0)
     wgrad_kernel<float><<<grid, 256, 0, st>>>(R, M, N, static_cast<const float*>(A), lda,
                                               static_cast<const float*>(Bm), ldb, part, rows_per_split);
   else
@@ -452,7 +1189,24 @@ hipError_t launch_bwd_wgrad(int R, int M, int N, const void* A, int lda, const v
 }
 
 hipError_t launch_sum_parts(const float* part, int parts, int n, float* out, hipStream_t st) {
-  sum_parts_kernel<<<dim3((n + 255) / 256), 256, 0, st>>>(part, parts, n, out);
+  sum_parts_kernel<<<dim3((n + 63) / 64), 256, 0, st>>>(part, parts, n, out);
+  return hipGetLastError();
+}
+
+bool bwd_mfma_supported(int d_h, int d_r) { return d_h == 64 && d_r == 32; }
+
+hipError_t launch_bwd_attention_mfma(const BwdArgs& a0, hipStream_t st) {
+  if (!bwd_mfma_supported(a0.d_h, a0.d_r)) return hipErrorNotSupported;
+  BwdArgs a = a0;
+  const int npair = a.B * a.H;
+  a.nqt = (a.N + 127) / 128;
+  bwd_dq_mfma_kernel<64, 32><<<a.nqt * npair, 256, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nslots = a.N / a.s;
+  if (nslots == 0) return hipSuccess;
+  const int nst = (nslots + 127) / 128;
+  bwd_dkv_mfma_kernel<64, 32><<<nst * npair, 256, 0, st>>>(a, nslots, nst);
   return hipGetLastError();
 }
 

@@ -872,9 +872,15 @@ int32_t mtla_layer_prefill(const mtla_dims* dims, int32_t d_model, int32_t t0, i
 // ---------------------------------------------------------------------------
 namespace {
 struct BwdWs {
-  size_t P, gate, KV, lse, D, dKV, Wt, dPc, wg_part, wh_part, total;
+  size_t P, gate, KV, lse, D, dKV, Wt, dPc, wg_part, du, wh_part, total;
+  size_t kc, v, pd, dsd;  // MFMA path
   int wg_splits, wh_parts;
+  bool fast;
 };
+
+// The MFMA attention backward runs where the forward's MFMA prefill does,
+// with d_h = 64 and d_r = 32.
+bool backward_fast(const mtla_dims* d) { return prefill_fast(d) && mtla::bwd_mfma_supported(d->d_h, d->d_r); }
 
 BwdWs bwd_ws(const mtla_dims* d, int n) {
   const size_t B = d->batch, H = d->heads, N = n, R = B * N, W = d->d_c + d->d_r;
@@ -886,20 +892,29 @@ BwdWs bwd_ws(const mtla_dims* d, int n) {
     off += align_up(bytes);
     return o;
   };
+  w.fast = backward_fast(d);
   w.P = take(R * W * e);
   w.gate = take(R * 4);
-  w.KV = take(R * KV2 * e);
+  if (w.fast) {
+    w.kc = take(B * H * N * d->d_h * e);
+    w.v = take(B * H * N * d->d_h * e);
+    w.pd = take(B * H * N * 4);
+    w.dsd = take(B * H * N * 4);
+  } else {
+    w.KV = take(R * KV2 * e);
+  }
   w.lse = take(B * H * N * 4);
   w.D = take(B * H * N * 4);
   w.dKV = take(R * (KV2 + H * d->d_r) * e);
   w.Wt = take(size_t(d->d_c) * KV2 * e);
   w.dPc = take(R * d->d_c * 4);
-  // split the weight-gradient product over rows so that ~2048 workgroups run
-  const size_t tiles = ((KV2 + 63) / 64) * ((d->d_c + 63) / 64);
-  w.wg_splits = static_cast<int>(std::max<size_t>(1, std::min<size_t>((2048 + tiles - 1) / tiles, (R + 255) / 256)));
+  // split the weight-gradient product over rows so that ~1024 workgroups run
+  const size_t tiles = mtla::bwd_wgrad_tiles(static_cast<int>(KV2), d->d_c, d->dtype);
+  w.wg_splits = static_cast<int>(std::max<size_t>(1, std::min<size_t>((1024 + tiles - 1) / tiles, (R + 255) / 256)));
   w.wg_part = take(size_t(w.wg_splits) * KV2 * d->d_c * 4);
-  const size_t blocks = B * ((N + d->stride_s - 1) / d->stride_s);
-  w.wh_parts = static_cast<int>(std::max<size_t>(1, std::min<size_t>(blocks, 1024)));
+  w.du = take(R * 4);
+  // dW_hyp: partial sums over chunks of ~256 rows
+  w.wh_parts = static_cast<int>(std::max<size_t>(1, std::min<size_t>((R + 255) / 256, 4096)));
   w.wh_part = take(size_t(w.wh_parts) * d->d_c * 4);
   w.total = off;
   return w;
@@ -919,6 +934,10 @@ int32_t check_backward(const mtla_dims* dims, int32_t n_tokens) {
                 dims->d_c);
   const int64_t R = int64_t(dims->batch) * n_tokens;
   const int64_t width = 2 * int64_t(dims->heads) * dims->d_h + int64_t(dims->heads) * dims->d_r;
+  // one sequence's query rows are addressed through 32-bit byte offsets
+  if (int64_t(n_tokens) * dims->heads * (dims->d_h + dims->d_r) * 4 > INT32_MAX ||
+      int64_t(n_tokens) * (dims->d_c + dims->d_r) * 4 > INT32_MAX)
+    return fail(MTLA_ERR_UNSUPPORTED, "n_tokens=%d is too long for one sequence's 2^31-byte rows", n_tokens);
   if (R > INT32_MAX || R * std::max<int64_t>(width, dims->d_c + dims->d_r) > kMaxElems)
     return fail(MTLA_ERR_UNSUPPORTED, "%lld token rows are too many", static_cast<long long>(R));
   return ok();
@@ -1007,30 +1026,45 @@ int32_t mtla_prefill_backward(const mtla_dims* dims, int32_t n_tokens, const voi
   a.g_q_r = grad_q_r;
   a.g_c = grad_c;
   a.g_k_r = grad_k_r;
+  a.du = reinterpret_cast<float*>(at(workspace, ws.du));
   a.wh_part = reinterpret_cast<float*>(at(workspace, ws.wh_part));
   a.wh_parts = ws.wh_parts;
   const int ldk = KV2 + H * dr;
   // forward recomputation: gates and partial merges, then K^C and V of every token
   if ((e = mtla::launch_bwd_partials(a, dims->dtype, s)) != hipSuccess)
     return hip_status(e, "backward partials launch");
-  mtla::LayerGemmArgs kv{};
-  kv.M = R;
-  kv.N = KV2;
-  kv.K = dc;
-  kv.A = a.P;
-  kv.lda = W;
-  kv.w0 = w_uk;
-  kv.n0 = H * d_h;
-  kv.w1 = w_uv;
-  kv.n1 = H * d_h;
-  kv.w2 = w_uv;
-  kv.mode = 0;
-  kv.out = at(workspace, ws.KV);
-  if ((e = mtla::launch_layer_gemm(kv, dims->dtype, s)) != hipSuccess)
-    return hip_status(e, "backward K/V up-projection launch");
-  // attention backward: dq (with lse and D), then dK^C, dK^R, dV of every key token
-  if ((e = mtla::launch_bwd_attention(a, dims->dtype, s)) != hipSuccess)
-    return hip_status(e, "backward attention launch");
+  if (ws.fast) {
+    // the forward's own K/V GEMM gives K^C and V of every token; then the
+    // MFMA dQ kernel (which also forms lse and D) and the dK/dV kernel
+    a.kc = at(workspace, ws.kc);
+    a.v = at(workspace, ws.v);
+    a.pd = reinterpret_cast<float*>(at(workspace, ws.pd));
+    a.dsd = reinterpret_cast<float*>(at(workspace, ws.dsd));
+    if ((e = mtla::launch_prefill_kv(a.B, n_tokens, H, d_h, dc, dr, a.P, w_uk, w_uv, at(workspace, ws.kc),
+                                     at(workspace, ws.v), s)) != hipSuccess)
+      return hip_status(e, "backward K/V up-projection launch");
+    if ((e = mtla::launch_bwd_attention_mfma(a, s)) != hipSuccess)
+      return hip_status(e, "backward attention launch");
+  } else {
+    mtla::LayerGemmArgs kv{};
+    kv.M = R;
+    kv.N = KV2;
+    kv.K = dc;
+    kv.A = a.P;
+    kv.lda = W;
+    kv.w0 = w_uk;
+    kv.n0 = H * d_h;
+    kv.w1 = w_uv;
+    kv.n1 = H * d_h;
+    kv.w2 = w_uv;
+    kv.mode = 0;
+    kv.out = at(workspace, ws.KV);
+    if ((e = mtla::launch_layer_gemm(kv, dims->dtype, s)) != hipSuccess)
+      return hip_status(e, "backward K/V up-projection launch");
+    // attention backward: dq (with lse and D), then dK^C, dK^R, dV of every key token
+    if ((e = mtla::launch_bwd_attention(a, dims->dtype, s)) != hipSuccess)
+      return hip_status(e, "backward attention launch");
+  }
   // dP^c = [dK^C | dV] [W_UK ; W_UV]
   void* wt = at(workspace, ws.Wt);
   if ((e = mtla::launch_bwd_transpose_w(H * d_h, dc, w_uk, w_uv, wt, dims->dtype, s)) != hipSuccess)
@@ -1056,7 +1090,7 @@ int32_t mtla_prefill_backward(const mtla_dims* dims, int32_t n_tokens, const voi
     return hip_status(e, "backward weight-gradient launch");
   // reverse in-block sums, gate backward, dc, dk^R and dW_hyp
   if ((e = mtla::launch_bwd_scan(a, dims->dtype, s)) != hipSuccess) return hip_status(e, "backward scan launch");
-  return hip_status(mtla::launch_sum_parts(a.wh_part, ws.wh_parts, dc, grad_w_hyp, s), "backward dW_hyp launch");
+  return hip_status(mtla::launch_bwd_dwhyp(a, grad_w_hyp, dims->dtype, s), "backward dW_hyp launch");
 }
 
 int32_t mtla_debug_stride_mask(int32_t n, int32_t s, uint8_t* mask, void* stream) {

@@ -85,7 +85,7 @@ struct BwdArgs {
   void* P;            // [R, d_c + d_r] partial merges (written by the partials kernel)
   float* gate;        // [R]
   const void* KV;     // [R, KV2]: K^C of (h, e) at column h d_h + e, V at H d_h + h d_h + e
-  float* lse;         // [B, H, N] natural-log softmax normaliser of each query
+  float* lse;         // [B, H, N] softmax normaliser of each query (log2 domain on the MFMA path)
   float* D;           // [B, H, N] sum_j p_ij (dO_i . V_j) = dO_i . o_i
   void* dKV;          // [R, KV2 + H d_r]: dK^C, dV as KV, then dK^R of (h, r) at KV2 + h d_r + r
   const float* dPc;   // [R, d_c] fp32: gradient of P^c through the up-projection
@@ -93,9 +93,19 @@ struct BwdArgs {
   void* g_q_r;
   void* g_c;
   void* g_k_r;
-  float* wh_part;     // [wh_parts, d_c] fp32 per-wave partial sums of dW_hyp
+  float* du;          // [R] gradient of each token's gate pre-activation u = W_hyp . (c + pe)
+  float* wh_part;     // [wh_parts, d_c] fp32 partial sums of dW_hyp over row chunks
   int wh_parts;
+  // MFMA path (bf16, d_h = 64, d_r = 32): K^C and V in the forward's layout,
+  // and lse in the log2 domain (scores scaled by tau log2 e)
+  const void* kc;     // [B, H, N, d_h] K^C of every token
+  const void* v;      // [B, H, N, d_h] V of every token
+  float* pd;          // [B, H, N] p_ii, the diagonal key's probability
+  float* dsd;         // [B, H, N] ds_ii
+  int nqt;            // query tiles per (sequence, head), set at launch
 };
+bool bwd_mfma_supported(int d_h, int d_r);
+hipError_t launch_bwd_attention_mfma(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_partials(const BwdArgs& a, int dtype, hipStream_t st);
 hipError_t launch_bwd_attention(const BwdArgs& a, int dtype, hipStream_t st);
 hipError_t launch_bwd_scan(const BwdArgs& a, int dtype, hipStream_t st);
@@ -107,6 +117,11 @@ hipError_t launch_bwd_transpose_w(int KV2h, int d_c, const void* w_uk, const voi
 // then out = the fixed-order sum of the partials.
 hipError_t launch_bwd_wgrad(int R, int M, int N, const void* A, int lda, const void* Bm, int ldb, float* part,
                             int splits, float* out0, int m0_rows, float* out1, int dtype, hipStream_t st);
+// Workgroup tiles of launch_bwd_wgrad's product for (M, N): it runs on MFMA
+// (128 x 128 tiles) for bf16 with M and N multiples of 128.
+int bwd_wgrad_tiles(int M, int N, int dtype);
+// dW_hyp = sum over rows r of du[r] (c_r + pe_t(r)), through wh_parts row-chunk partials.
+hipError_t launch_bwd_dwhyp(const BwdArgs& a, float* out, int dtype, hipStream_t st);
 // out[i] = sum_{p < parts} part[p * n + i], in order of p.
 hipError_t launch_sum_parts(const float* part, int parts, int n, float* out, hipStream_t st);
 

@@ -22,11 +22,13 @@ def _inputs(seed, B, N, H, d_h, d_c, d_r, dtype):
     return inp
 
 
-def _gpu_backward(inp, s, dtype, reps=1):
+def _gpu_backward(inp, s, dtype, reps=1, portable=False):
     B, N, d_c = inp["c"].shape
     H, d_h = inp["q_c"].shape[2], inp["q_c"].shape[3]
     d_r = inp["k_r"].shape[2]
     d = m.make_dims(B, H, d_h, d_c, d_r, s, max(1, -(-N // s)), dtype)
+    if portable:
+        d.flags = m.MTLA_FLAG_PORTABLE
     st = d.torch_dtype
     dev = {k: tdev(inp[k], torch.float32 if k == "w_hyp" else st)
            for k in ("c", "k_r", "q_c", "q_r", "w_hyp", "w_uk", "w_uv", "d_o")}
@@ -60,31 +62,44 @@ def _oracle_backward(inp, s, scale):
     return want
 
 
-# (seed, B, N, s, H, d_h, d_c, d_r, dtype): several 64-row tiles with a ragged
-# tail, s = 1 (the causal mask), s >= N (the diagonal alone), N a multiple of
-# s, no rope part, and the summarisation head shape in bf16
+# (seed, B, N, s, H, d_h, d_c, d_r, dtype, portable): several 64-row tiles
+# with a ragged tail, s = 1 (the causal mask), s >= N (the diagonal alone), N
+# a multiple of s, no rope part; in bf16 the summarisation head shape (the
+# MFMA path: several 128-query and 128-slot tiles, B*H a multiple of 8 or
+# not, no completed slot at all) and the same shape through the portable
+# kernels
 CASES = [
-    (1, 2, 37, 3, 2, 16, 32, 8, "fp32"),
-    (2, 1, 130, 2, 4, 8, 16, 8, "fp32"),
-    (3, 2, 20, 1, 2, 8, 16, 8, "fp32"),
-    (4, 1, 5, 8, 2, 8, 16, 8, "fp32"),
-    (5, 2, 33, 4, 2, 12, 24, 0, "fp32"),
-    (6, 2, 200, 3, 8, 64, 256, 32, "bf16"),
-    (7, 1, 131, 2, 8, 64, 256, 32, "bf16"),
+    (1, 2, 37, 3, 2, 16, 32, 8, "fp32", False),
+    (2, 1, 130, 2, 4, 8, 16, 8, "fp32", False),
+    (3, 2, 20, 1, 2, 8, 16, 8, "fp32", False),
+    (4, 1, 5, 8, 2, 8, 16, 8, "fp32", False),
+    (5, 2, 33, 4, 2, 12, 24, 0, "fp32", False),
+    (6, 2, 200, 3, 8, 64, 256, 32, "bf16", False),
+    (7, 1, 131, 2, 8, 64, 256, 32, "bf16", False),
+    (10, 1, 1000, 3, 8, 64, 256, 32, "bf16", False),
+    (11, 3, 300, 2, 2, 64, 256, 32, "bf16", False),
+    (12, 1, 7, 9, 8, 64, 256, 32, "bf16", False),
+    (13, 2, 257, 1, 8, 64, 256, 32, "bf16", False),
+    (14, 2, 200, 3, 8, 64, 256, 32, "bf16", True),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}_n{c[2]}_s{c[3]}_{c[8]}" for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}_n{c[2]}_s{c[3]}_{c[8]}{'_portable' if c[9] else ''}"
+                                             for c in CASES])
 def test_backward_matches_oracle(case):
-    seed, B, N, s, H, d_h, d_c, d_r, dtype = case
-    print(f"backward case seed={seed} B={B} N={N} s={s} H={H} d_h={d_h} d_c={d_c} d_r={d_r} {dtype}", flush=True)
+    seed, B, N, s, H, d_h, d_c, d_r, dtype, portable = case
+    print(f"backward case seed={seed} B={B} N={N} s={s} H={H} d_h={d_h} d_c={d_c} d_r={d_r} {dtype} "
+          f"portable={portable}", flush=True)
     inp = _inputs(seed, B, N, H, d_h, d_c, d_r, dtype)
-    d, (got,) = _gpu_backward(inp, s, dtype)
+    d, (got,) = _gpu_backward(inp, s, dtype, portable=portable)
     want = _oracle_backward(inp, s, d.softmax_scale)
+    errs = {}
     for k in NAMES:
         if want[k].size == 0:
             continue
-        err = oracle.max_rel_err(got[k], want[k])
+        errs[k] = oracle.max_rel_err(got[k], want[k])
+    print("max rel err", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, err in errs.items():
         assert err <= tol(dtype), (k, err)
 
 

@@ -30,6 +30,7 @@ ROOT_SEED = 20250513
 # Stream identifiers, one per tensor role.
 T_H, T_WDKV, T_WHYP, T_WUK, T_WUV, T_WQ, T_WR, T_WO = 0, 1, 2, 3, 4, 5, 6, 7
 T_C, T_KR, T_QC, T_QR = 10, 11, 12, 13
+T_DO = 14
 
 
 @dataclass(frozen=True)
@@ -177,6 +178,12 @@ def batch_queries(w: Workload, n_tokens: Optional[int] = None, seqs=None) -> dic
     seqs = range(w.batch) if seqs is None else seqs
     parts = [queries(w, b, n_tokens) for b in seqs]
     return {k: np.stack([p[k] for p in parts]) for k in ("q_c", "q_r")}
+
+
+def batch_grad_out(w: Workload) -> np.ndarray:
+    """Upstream gradient dL/do [B, N, H, d_h] for the training backward: N(0, 1)."""
+    return np.stack([quantize(normal(w.wid, T_DO, (w.n_tokens, w.heads, w.d_h), b=b), w.dtype)
+                     for b in range(w.batch)])
 
 
 def layer_params(w: Workload) -> dict:
