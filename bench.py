@@ -16,8 +16,9 @@ The other workloads are reported in ``components``: the s=4 decode loop
 prefill's second half as one chunked call after the first half
 (mtla_prefill_at), the LLM-scale step (B=64, cache of 32,768 tokens, one
 append + decode), a beam-search reorder of that LLM-scale decode state
-(mtla_reorder_state), and the whole layer from h (input projections + RoPE,
-the core, output projection) for the s=2 decode loop and the prefill.
+(mtla_reorder_state), the whole layer from h (input projections + RoPE,
+the core, output projection) for the s=2 decode loop and the prefill, and
+the training backward of the summarisation prefill (mtla_prefill_backward).
 
 ``roofline`` describes the dominant kernel of the headline step: the fused
 decode-step kernel, the step's only kernel, so its average launch duration is
@@ -47,8 +48,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default=None,
                    help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, "
-                        "prefill_chunk, llm_decode, reorder, layer_decode, layer_prefill, copy: the "
-                        "counter-calibration copy kernel)")
+                        "prefill_chunk, llm_decode, reorder, layer_decode, layer_prefill, backward, copy: "
+                        "the counter-calibration copy kernel)")
     return p.parse_args()
 
 
@@ -607,6 +608,9 @@ def main():
         comps["layer_sum_prefill_b16_n4096_s3"] = run_layer_prefill(W[3], args.steps, args.warmup, m, torch,
                                                                     workloads)
         log("layer prefill:", json.dumps(comps["layer_sum_prefill_b16_n4096_s3"]))
+        torch.cuda.empty_cache()
+        comps["sum_prefill_b16_n4096_s3_backward"] = run_backward(W[3], args.steps, args.warmup, m, torch, workloads)
+        log("backward:", json.dumps(comps["sum_prefill_b16_n4096_s3_backward"]))
         torch.cuda.empty_cache()
         comps["llm_decode_b64_n32768_s2"] = run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0]
         log("llm:", json.dumps(comps["llm_decode_b64_n32768_s2"]))

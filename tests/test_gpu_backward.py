@@ -115,3 +115,33 @@ def test_backward_empty_sequence_zeroes_weight_gradients():
     _, (got,) = _gpu_backward(inp, 2, "fp32")
     for k in ("dw_hyp", "dw_uk", "dw_uv"):
         assert not np.any(got[k]), k
+
+
+def _workload_inputs(w, seqs=None):
+    lat, qry = workloads.batch_latents(w, seqs=seqs), workloads.batch_queries(w, seqs=seqs)
+    wts = workloads.weights(w)
+    return {"c": lat["c"], "k_r": lat["k_r"], "q_c": qry["q_c"], "q_r": qry["q_r"], "w_hyp": wts["w_hyp"],
+            "w_uk": wts["w_uk"], "w_uv": wts["w_uv"], "d_o": workloads.batch_grad_out(w, seqs=seqs)}
+
+
+def test_backward_full_size_sampled():
+    """The summarisation shape (B=16, N=4096, s=3) in the launch configuration
+    the benchmark times: sequences 0 and 15 against the oracle's full-length
+    backward.  The weight gradients, summed over the batch, are checked on a
+    batch of those two sequences at full length."""
+    w = workloads.WORKLOADS[3]
+    assert (w.batch, w.n_tokens, w.s) == (16, 4096, 3)
+    print("full-size backward: GPU at B=16", flush=True)
+    d, (got,) = _gpu_backward(_workload_inputs(w), w.s, w.dtype)
+    sub = _workload_inputs(w, seqs=[0, 15])
+    print("full-size backward: oracle for sequences 0 and 15", flush=True)
+    want = _oracle_backward(sub, w.s, d.softmax_scale)
+    for k in ("dc", "dk_r", "dq_c", "dq_r"):
+        err = oracle.max_rel_err(got[k][[0, 15]], want[k])
+        print(k, f"{err:.2e}", flush=True)
+        assert err <= tol(w.dtype), (k, err)
+    _, (got2,) = _gpu_backward(sub, w.s, w.dtype)
+    for k in ("dw_hyp", "dw_uk", "dw_uv"):
+        err = oracle.max_rel_err(got2[k], want[k])
+        print(k, f"{err:.2e}", flush=True)
+        assert err <= tol(w.dtype), (k, err)

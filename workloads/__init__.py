@@ -180,10 +180,10 @@ def batch_queries(w: Workload, n_tokens: Optional[int] = None, seqs=None) -> dic
     return {k: np.stack([p[k] for p in parts]) for k in ("q_c", "q_r")}
 
 
-def batch_grad_out(w: Workload) -> np.ndarray:
+def batch_grad_out(w: Workload, seqs=None) -> np.ndarray:
     """Upstream gradient dL/do [B, N, H, d_h] for the training backward: N(0, 1)."""
-    return np.stack([quantize(normal(w.wid, T_DO, (w.n_tokens, w.heads, w.d_h), b=b), w.dtype)
-                     for b in range(w.batch)])
+    seqs = range(w.batch) if seqs is None else seqs
+    return np.stack([quantize(normal(w.wid, T_DO, (w.n_tokens, w.heads, w.d_h), b=b), w.dtype) for b in seqs])
 
 
 def layer_params(w: Workload) -> dict:
