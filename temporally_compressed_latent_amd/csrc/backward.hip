@@ -659,6 +659,9 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
   const int nk = (min(q0 + 128, N) - 1) / s;
   const int nk_w = qw0 < N ? (min(qw0 + 32, N) - 1) / s : 0;
   const int full_w = qw0 / s;
+  // completed slot j (0-based) is visible to this lane's query qi iff
+  // s (j + 1) <= qi, i.e. j < vis
+  const int vis = qi / s;
 
   // slot m's keys are token row s m + s - 1; loads past the last completed
   // slot's row read as zero through bounded buffer resources
@@ -759,13 +762,12 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
       f32x16 sc, dp;
       scores(sK, sV, rt, sc, dp);
       float mx = -INFINITY;
+      const int rel = vis - j0 - 32 * rt - 4 * grp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float z = sc[i] * qk;
-        if (boundary) {
-          const int slot = j0 + 32 * rt + 8 * (i / 4) + 4 * grp + (i % 4);
-          if (s * (slot + 1) > qi) z = -INFINITY;
-        }
+        // slot j0 + 32 rt + 8 (i / 4) + 4 grp + i % 4 is hidden iff >= vis
+        if (boundary && 8 * (i / 4) + (i % 4) >= rel) z = -INFINITY;
         sc[i] = z;
         mx = fmaxf(mx, z);
       }
@@ -835,13 +837,11 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
     for (int rt = 0; rt < 2; ++rt) {
       f32x16 sc, dp;
       scores(sK, sV, rt, sc, dp);
+      const int rel = vis - j0 - 32 * rt - 4 * grp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(fmaf(sc[i], qk, -lse2));
-        if (boundary) {
-          const int slot = j0 + 32 * rt + 8 * (i / 4) + 4 * grp + (i % 4);
-          if (s * (slot + 1) > qi) p = 0.f;
-        }
+        if (boundary && 8 * (i / 4) + (i % 4) >= rel) p = 0.f;
         sc[i] = a.scale * p * (dp[i] - Dq);
       }
 #pragma unroll
@@ -899,6 +899,7 @@ void bwd_dkv_mfma_kernel(BwdArgs a, int nslots, int nst) {
   const int m = msw + c32;
   const bool mok = m < nslots;
   const int jt = s * (m + 1) - 1;  // the slot's key token
+  const int qm = jt + 1;           // the first query that sees the slot
 
   const uint16_t* qc = static_cast<const uint16_t*>(a.q_c);
   const uint16_t* qr = static_cast<const uint16_t*>(a.q_r);
@@ -1036,6 +1037,9 @@ void bwd_dkv_mfma_kernel(BwdArgs a, int nslots, int nst) {
           const bf16x8 ao = *reinterpret_cast<const bf16x8*>(sO + (32 * rt + c32) * OP + 16 * kk + 8 * grp);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vreg[kk], dp, 0, 0, 0);
         }
+        // query q0 + 32 rt + 8 i4 + 4 grp + r is hidden from slot m iff it is
+        // below qm = s (m + 1): one per-lane bound against compile-time offsets
+        const int relq = qm - q0 - 32 * rt - 4 * grp;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int r0 = 32 * rt + 8 * i4 + 4 * grp;
@@ -1047,7 +1051,7 @@ void bwd_dkv_mfma_kernel(BwdArgs a, int nslots, int nst) {
             const int i = 4 * i4 + r;
             float p = fast_exp2(fmaf(sc[i], qk, -Lr[r]));
             // completed slot m is visible to query q iff s (m + 1) <= q
-            if (boundary && s * (m + 1) > q0 + r0 + r) p = 0.f;
+            if (boundary && 8 * i4 + r < relq) p = 0.f;
             sc[i] = p;
             dp[i] = a.scale * p * (dp[i] - Dr[r]);
           }

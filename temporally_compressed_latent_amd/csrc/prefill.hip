@@ -281,6 +281,11 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
     }
   }
 
+  // completed slots (0-based) visible to this lane's queries: slot j is seen
+  // by query token t0 + qi + 1 iff s (j + 1) <= t0 + qi, i.e. j < vis[t]
+  int vis[NQ];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) vis[t] = (t0 + qw0 + 32 * t + c32) / s;
   // completed slots seen by the workgroup's / this wave's last query, and the
   // slots every query of this wave sees
   const int nk = (t0 + min(q0 + QT, N) - 1) / s;
@@ -388,16 +393,14 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
         if (boundary) {
-          const int qi = qw0 + 32 * t + c32;
+          // slot j0 + 32 rt + 8 (i / 4) + 4 grp + i % 4 is hidden iff it is
+          // >= vis[t]: one per-lane bound against compile-time offsets
+          const int rel = vis[t] - j0 - 4 * grp;
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int slot = j0 + 32 * rt + 8 * (i / 4) + 4 * grp + (i % 4);
-              // completed slot (0-based) visible to query token t0 + qi + 1:
-              // s*(slot+1) <= t0 + qi
-              if (s * (slot + 1) > t0 + qi) sc[rt][t][i] = -INFINITY;
-            }
+            for (int i = 0; i < 16; ++i)
+              if (32 * rt + 8 * (i / 4) + (i % 4) >= rel) sc[rt][t][i] = -INFINITY;
           }
         }
         // this lane's maximum over its 32 scores (four independent chains;
