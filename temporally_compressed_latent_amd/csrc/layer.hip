@@ -16,7 +16,8 @@
 // storage.  The C tile is staged in LDS and stored by column pairs, so a rope
 // pair (2k, 2k+1) - two adjacent columns of one tile - is rotated by the one
 // thread that stores both.  Few rows (decode) take a skinny variant that
-// splits K over the waves instead.
+// splits K over the waves instead, many rows in bf16 a 128 x 128 MFMA
+// variant.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -269,6 +270,130 @@ __global__ __launch_bounds__(256) void layer_gemm_kernel(LayerGemmArgs g) {
   }
 }
 
+// The same product for many rows in bf16: 128 x 128 output tiles, four waves
+// of 64 x 64 (2 x 2 tiles of 32x32x16 MFMA), K step 64 through
+// double-buffered LDS with the next step's operands prefetched into
+// registers.  Workgroup L runs on XCD L % 8; the column tiles of one
+// 128-row stripe of A are dealt to one XCD, so the stripe is fetched into
+// that XCD's L2 once for all of them.  The C tile is staged in LDS in two
+// 64-row halves and stored by column pairs, as in the smaller kernel.
+constexpr int MBM = 128, MBN = 128, MBK = 64;
+constexpr int MP = MBK + 8;   // operand pitch (elements)
+constexpr int MCP = MBN + 4;  // C half-tile pitch (floats)
+
+__global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, int nrt, int nct) {
+  __shared__ __align__(16) uint16_t smem[2 * (MBM + MBN) * MP];
+  static_assert(64 * MCP * 4 <= sizeof(smem), "C half tile fits in the operand buffers");
+  const int L = blockIdx.x;
+  const int xcd = L & 7, k8 = L >> 3;
+  const int rt = 8 * (k8 / nct) + xcd, ct = k8 % nct;
+  if (rt >= nrt) return;
+  const int m0 = rt * MBM, n0 = ct * MBN;
+  const int M = g.M, N = g.N, K = g.K, lda = g.lda ? g.lda : K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, grp = lane >> 5, c32 = lane & 31;
+  // per stage and operand 128 rows x 64 k = 1024 chunks of 8: 4 per thread
+  constexpr int CPT = MBM * MBK / 8 / 256;
+  const uint16_t* arow[CPT];
+  const uint16_t* wrow[CPT];
+  int kofs[CPT], lofs[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i, r = c / (MBK / 8);
+    kofs[i] = (c % (MBK / 8)) * 8;
+    lofs[i] = r * MP + kofs[i];
+    arow[i] = static_cast<const uint16_t*>(g.A) + static_cast<size_t>(min(m0 + r, M - 1)) * lda;
+    wrow[i] = weight_row<uint16_t>(g, min(n0 + r, N - 1));
+  }
+  uint4 ra[CPT], rw[CPT];
+  // chunks past K read as zero (K is a multiple of 8); the address is kept
+  // inside the row and the value replaced, so no load sits under a branch
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int k = k0 + kofs[i];
+      const int kk = min(k, K - 8);
+      const uint4 va = *reinterpret_cast<const uint4*>(arow[i] + kk);
+      const uint4 vw = *reinterpret_cast<const uint4*>(wrow[i] + kk);
+      // (a mask, not a select of the vectors, which the compiler would
+      // route through scratch memory)
+      const uint32_t keep = k < K ? 0xffffffffu : 0u;
+      ra[i] = uint4{va.x & keep, va.y & keep, va.z & keep, va.w & keep};
+      rw[i] = uint4{vw.x & keep, vw.y & keep, vw.z & keep, vw.w & keep};
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* sA = smem + buf * (MBM + MBN) * MP;
+    uint16_t* sW = sA + MBM * MP;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      *reinterpret_cast<uint4*>(sA + lofs[i]) = ra[i];
+      *reinterpret_cast<uint4*>(sW + lofs[i]) = rw[i];
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int nk = (K + MBK - 1) / MBK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * MBK);
+    const uint16_t* sA = smem + buf * (MBM + MBN) * MP;
+    const uint16_t* sW = sA + MBM * MP;
+#pragma unroll
+    for (int kc = 0; kc < MBK / 16; ++kc) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8*>(sA + (64 * wm + 32 * i + c32) * MP + 16 * kc + 8 * grp);
+        b[i] = *reinterpret_cast<const bf16x8*>(sW + (64 * wn + 32 * i + c32) * MP + 16 * kc + 8 * grp);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    // the other buffer was last read before the previous barrier
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue, one 64-row half at a time: acc[i][j][e] is row
+  // 64 wm + 32 i + 8 (e / 4) + 4 grp + e % 4, column 64 wn + 32 j + c32
+  float* sC = reinterpret_cast<float*>(smem);
+  const int pc = tid & 63, n = n0 + 2 * pc;
+  const PairDest pd = pair_dest(g, min(n, N - 2));
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    if (wm == hh) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            sC[(32 * i + 8 * (e / 4) + 4 * grp + (e % 4)) * MCP + 64 * wn + 32 * j + c32] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (n < N) {
+      for (int r = tid >> 6; r < 64; r += 4) {
+        const int m = m0 + 64 * hh + r;
+        if (m >= M) break;
+        store_pair<uint16_t>(g, pd, m, n, pd.kind >= 3 ? row_position(g, m) : 0, sC[r * MCP + 2 * pc],
+                             sC[r * MCP + 2 * pc + 1]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // The same product for few rows (M <= 16 * NB <= 64, one token per sequence in
 // decode), in bf16: every lane loads its MFMA operand fragments straight from
 // memory (A row c16 and weight row c16, 8 consecutive k at 8 * g16), the
@@ -368,11 +493,13 @@ hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st) 
     }
     return hipGetLastError();
   }
+  if (dtype != 0) {
+    const int nrt = (g.M + MBM - 1) / MBM, nct = (g.N + MBN - 1) / MBN;
+    layer_gemm_mfma_kernel<<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);
+    return hipGetLastError();
+  }
   dim3 grid((g.N + LBN - 1) / LBN, (g.M + LBM - 1) / LBM);
-  if (dtype == 0)
-    layer_gemm_kernel<float><<<grid, 256, 0, st>>>(g);
-  else
-    layer_gemm_kernel<uint16_t><<<grid, 256, 0, st>>>(g);
+  layer_gemm_kernel<float><<<grid, 256, 0, st>>>(g);
   return hipGetLastError();
 }
 
