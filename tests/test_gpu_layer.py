@@ -33,7 +33,9 @@ def _oracle_layer(w, p, b, schedule, n=None):
 
 # (workload, overrides): the fp32 single-layer case as it stands, and the
 # speech-translation shape (bf16, d_model 512) at a test-sized batch and length
-LAYER_CASES = [(0, {}), (1, dict(batch=2, n_tokens=100)), (1, dict(batch=2, n_tokens=70, s=3))]
+LAYER_CASES = [(0, {}), (1, dict(batch=2, n_tokens=100)), (1, dict(batch=2, n_tokens=70, s=3)),
+               # d_model 200: the GEMMs' K is not a multiple of their 64-wide K step
+               (1, dict(batch=2, n_tokens=67, d_model=200))]
 
 
 @pytest.mark.parametrize("wid,kw", LAYER_CASES)
