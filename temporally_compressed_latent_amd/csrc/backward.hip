@@ -761,16 +761,18 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
     for (int rt = 0; rt < 2; ++rt) {
       f32x16 sc, dp;
       scores(sK, sV, rt, sc, dp);
-      float mx = -INFINITY;
-      const int rel = vis - j0 - 32 * rt - 4 * grp;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float z = sc[i] * qk;
+      for (int i = 0; i < 16; ++i) sc[i] *= qk;
+      if (boundary) {
         // slot j0 + 32 rt + 8 (i / 4) + 4 grp + i % 4 is hidden iff >= vis
-        if (boundary && 8 * (i / 4) + (i % 4) >= rel) z = -INFINITY;
-        sc[i] = z;
-        mx = fmaxf(mx, z);
+        const int rel = vis - j0 - 32 * rt - 4 * grp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i / 4) + (i % 4) >= rel) sc[i] = -INFINITY;
       }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mn = fmaxf(m, mx);
       const float f = fast_exp2(m - mn);
@@ -837,13 +839,16 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
     for (int rt = 0; rt < 2; ++rt) {
       f32x16 sc, dp;
       scores(sK, sV, rt, sc, dp);
-      const int rel = vis - j0 - 32 * rt - 4 * grp;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(sc[i], qk, -lse2));
-        if (boundary && 8 * (i / 4) + (i % 4) >= rel) p = 0.f;
-        sc[i] = a.scale * p * (dp[i] - Dq);
+      for (int i = 0; i < 16; ++i) sc[i] = fast_exp2(fmaf(sc[i], qk, -lse2));
+      if (boundary) {
+        const int rel = vis - j0 - 32 * rt - 4 * grp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i / 4) + (i % 4) >= rel) sc[i] = 0.f;
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = a.scale * sc[i] * (dp[i] - Dq);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 db = acc_chunk_bf16(sc, c);
@@ -1039,22 +1044,28 @@ void bwd_dkv_mfma_kernel(BwdArgs a, int nslots, int nst) {
         }
         // query q0 + 32 rt + 8 i4 + 4 grp + r is hidden from slot m iff it is
         // below qm = s (m + 1): one per-lane bound against compile-time offsets
-        const int relq = qm - q0 - 32 * rt - 4 * grp;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int r0 = 32 * rt + 8 * i4 + 4 * grp;
           const float4 L4 = *reinterpret_cast<const float4*>(&sLb[buf][r0]);
-          const float4 D4 = *reinterpret_cast<const float4*>(&sDb[buf][r0]);
-          const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+          const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * i4 + r;
-            float p = fast_exp2(fmaf(sc[i], qk, -Lr[r]));
-            // completed slot m is visible to query q iff s (m + 1) <= q
-            if (boundary && 8 * i4 + r < relq) p = 0.f;
-            sc[i] = p;
-            dp[i] = a.scale * p * (dp[i] - Dr[r]);
-          }
+          for (int r = 0; r < 4; ++r) sc[4 * i4 + r] = fast_exp2(fmaf(sc[4 * i4 + r], qk, -Lr[r]));
+        }
+        if (boundary) {
+          // completed slot m is visible to query q iff s (m + 1) <= q
+          const int relq = qm - q0 - 32 * rt - 4 * grp;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (8 * (i / 4) + (i % 4) < relq) sc[i] = 0.f;
+        }
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int r0 = 32 * rt + 8 * i4 + 4 * grp;
+          const float4 D4 = *reinterpret_cast<const float4*>(&sDb[buf][r0]);
+          const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dp[4 * i4 + r] = a.scale * sc[4 * i4 + r] * (dp[4 * i4 + r] - Dr[r]);
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
