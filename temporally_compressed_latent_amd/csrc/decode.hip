@@ -22,6 +22,8 @@ namespace mtla {
 
 namespace {
 
+constexpr int kAbsorbMaxDh = 256;  // rows of the staged W_UK tile (d_h bound)
+
 // ---------------------------------------------------------------------------
 // absorb: one workgroup per (head, block of RB rows).
 //   q~[r, k] = sum_e q_c[r, e] W_UK[h, e, k]
@@ -1466,6 +1468,147 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same two products on MFMA (bf16 storage), for long caches where they
+// run as their own launches.  A workgroup computes a 32 x 32 tile of the
+// output (32 rows r, 32 columns) with 32x32x16 MFMA; its four waves split the
+// contraction and add their partial tiles through LDS in wave order.
+// Accumulator layout: lane (grp, c32) holds column c32, rows
+// 8 (i / 4) + 4 grp + i % 4.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void reduce4_store(float (*part)[32 * 33], const f32x16& acc, int wave, int grp,
+                                              int c32) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) part[wave][(8 * (i / 4) + 4 * grp + (i % 4)) * 33 + c32] = acc[i];
+}
+
+// q~[r, h, n] = sum_e q_c[r, h, e] W_UK[h, e, n] for n in one 32-column tile.
+// W_UK is row-major in e, so its tile (d_h rows x 32 columns) is staged in
+// LDS and read by transposing reads, which take the contraction rows in the
+// order 16 c + 4 grp + r (r < 4), 16 c + 8 + 4 grp + (r - 4); the query
+// fragments are loaded in that same order.  Wave w takes the 16-row chunks
+// c = w, w + 4, ...  The rope part of the query is copied beside it.
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(int R, int H, int d_h, int d_c, int d_r,
+                                                          const uint16_t* __restrict__ q_c,
+                                                          const uint16_t* __restrict__ q_r,
+                                                          const uint16_t* __restrict__ w_uk,
+                                                          float* __restrict__ qbuf) {
+  constexpr int WP = 32 + 8;  // LDS pitch of the weight tile (elements)
+  __shared__ __align__(16) uint16_t sW[kAbsorbMaxDh * WP];
+  __shared__ float part[4][32 * 33];
+  const int n0 = blockIdx.x * 32, h = blockIdx.y, r0 = blockIdx.z * 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5, c32 = lane & 31;
+  const int W = d_c + d_r;
+  // this wave's query fragments for chunks c = wave + 4 u (u < d_h / 64 <= 4),
+  // loaded first: they do not wait for the weight tile
+  const int r = min(r0 + c32, R - 1);
+  const uint16_t* qrow = q_c + (static_cast<size_t>(r) * H + h) * d_h;
+  constexpr int UA = kAbsorbMaxDh / 64;
+  const int nu = d_h / 64;
+  uint4 qa[UA];
+#pragma unroll
+  for (int u = 0; u < UA; ++u) {
+    const int c = wave + 4 * min(u, nu - 1);
+    const uint2 lo = *reinterpret_cast<const uint2*>(qrow + 16 * c + 4 * grp);
+    const uint2 hi = *reinterpret_cast<const uint2*>(qrow + 16 * c + 8 + 4 * grp);
+    qa[u] = uint4{lo.x, lo.y, hi.x, hi.y};
+  }
+  // weight tile: d_h rows x 4 chunks of 8 columns
+  for (int c = tid; c < d_h * 4; c += 256) {
+    const int e = c >> 2, cc = c & 3;
+    *reinterpret_cast<uint4*>(sW + e * WP + cc * 8) =
+        *reinterpret_cast<const uint4*>(w_uk + (static_cast<size_t>(h) * d_h + e) * d_c + n0 + cc * 8);
+  }
+  __syncthreads();
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  const int q16 = lane >> 4, k16 = lane & 15;
+#pragma unroll
+  for (int u = 0; u < UA; ++u) {
+    if (u >= nu) break;
+    const int c = wave + 4 * u;
+    const uint16_t* base = sW + (16 * c + 4 * (q16 >> 1) + (k16 >> 2)) * WP + 16 * (q16 & 1) + 4 * (k16 & 3);
+    const s16x4 b0 = lds_read_tr16(base);
+    const s16x4 b1 = lds_read_tr16(base + 8 * WP);
+    const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[u]), b, acc, 0, 0, 0);
+  }
+  reduce4_store(part, acc, wave, grp, c32);
+  __syncthreads();
+  for (int idx = tid; idx < 32 * 32; idx += 256) {
+    const int rr = idx >> 5, col = idx & 31;
+    if (r0 + rr >= R) continue;
+    const float v = (part[0][rr * 33 + col] + part[1][rr * 33 + col]) + (part[2][rr * 33 + col] + part[3][rr * 33 + col]);
+    qbuf[(static_cast<size_t>(r0 + rr) * H + h) * W + n0 + col] = v;
+  }
+  if (blockIdx.x == 0) {
+    for (int idx = tid; idx < 32 * d_r; idx += 256) {
+      const int rr = idx / d_r, e = idx % d_r;
+      if (r0 + rr < R)
+        qbuf[(static_cast<size_t>(r0 + rr) * H + h) * W + d_c + e] =
+            bf16_bits_to_f32(q_r[(static_cast<size_t>(r0 + rr) * H + h) * d_r + e]);
+    }
+  }
+}
+
+// out[r, h, e] = sum_k W_UV[h, e, k] o_lat[r, h, k] for e in one 32-row tile
+// of W_UV.  Both operands are contiguous in k, so every lane loads its
+// fragments directly; the fp32 o_lat enters as a pair of bf16 operands whose
+// sum carries it to ~16 significant bits.  Wave w takes the 16-wide k-steps
+// w, w + 4, ...
+__global__ __launch_bounds__(256) void up_project_mfma_kernel(int R, int H, int d_h, int d_c,
+                                                              const float* __restrict__ o_lat,
+                                                              const uint16_t* __restrict__ w_uv,
+                                                              uint16_t* __restrict__ out) {
+  __shared__ float part[4][32 * 33];
+  const int e0 = blockIdx.x * 32, h = blockIdx.y, r0 = blockIdx.z * 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5, c32 = lane & 31;
+  const int r = min(r0 + c32, R - 1);
+  const float* orow = o_lat + (static_cast<size_t>(r) * H + h) * d_c + 8 * grp;
+  const uint16_t* wrow = w_uv + (static_cast<size_t>(h) * d_h + e0 + c32) * d_c + 8 * grp;
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  // rounds of UP k-steps with all their loads in flight; steps past d_c load
+  // a valid address and contribute zero
+  constexpr int UP = 8;
+  for (int kb = 16 * wave; kb < d_c; kb += 64 * UP) {
+    float4 x0[UP], x1[UP];
+    uint4 bw[UP];
+#pragma unroll
+    for (int u = 0; u < UP; ++u) {
+      const int k = min(kb + 64 * u, d_c - 16);
+      x0[u] = *reinterpret_cast<const float4*>(orow + k);
+      x1[u] = *reinterpret_cast<const float4*>(orow + k + 4);
+      bw[u] = *reinterpret_cast<const uint4*>(wrow + k);
+    }
+#pragma unroll
+    for (int u = 0; u < UP; ++u) {
+      const float keep = kb + 64 * u < d_c ? 1.f : 0.f;
+      const float xs[8] = {x0[u].x, x0[u].y, x0[u].z, x0[u].w, x1[u].x, x1[u].y, x1[u].z, x1[u].w};
+      u16x8 ah, al;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = xs[j] * keep;
+        ah[j] = f32_to_bf16_bits(x);
+        al[j] = f32_to_bf16_bits(x - bf16_bits_to_f32(ah[j]));
+      }
+      const bf16x8 b = __builtin_bit_cast(bf16x8, bw[u]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah), b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al), b, acc, 0, 0, 0);
+    }
+  }
+  reduce4_store(part, acc, wave, grp, c32);
+  __syncthreads();
+  for (int idx = tid; idx < 32 * 32; idx += 256) {
+    const int rr = idx >> 5, col = idx & 31;
+    if (r0 + rr >= R) continue;
+    const float v = (part[0][rr * 33 + col] + part[1][rr * 33 + col]) + (part[2][rr * 33 + col] + part[3][rr * 33 + col]);
+    out[(static_cast<size_t>(r0 + rr) * H + h) * d_h + e0 + col] = f32_to_bf16_bits(v);
+  }
+}
+
 // Rows per workgroup of absorb / up-projection: one row while there are few
 // (row, head) pairs, so the launch fills the chip; four when there are many,
 // so each W_UK / W_UV chunk loaded serves four rows.
@@ -1486,6 +1629,12 @@ hipError_t absorb_rb(int R, int H, int d_h, int d_c, int d_r, const void* q_c, c
 template <typename T>
 hipError_t absorb_t(int R, int H, int d_h, int d_c, int d_r, const void* q_c, const void* q_r,
                     const void* w_uk, float* qbuf, hipStream_t st) {
+  if (std::is_same<T, uint16_t>::value && d_h % 64 == 0 && d_h <= kAbsorbMaxDh && d_c % 32 == 0) {
+    absorb_mfma_kernel<<<dim3(d_c / 32, H, (R + 31) / 32), 256, 0, st>>>(
+        R, H, d_h, d_c, d_r, static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
+        static_cast<const uint16_t*>(w_uk), qbuf);
+    return hipGetLastError();
+  }
   switch (rows_per_wg(R, H)) {
     case 4: return absorb_rb<T, 4>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st);
     default: return absorb_rb<T, 1>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st);
@@ -1522,6 +1671,11 @@ hipError_t up_project_rb(int R, int H, int d_h, int d_c, const float* o_lat, con
 template <typename T>
 hipError_t up_project_t(int R, int H, int d_h, int d_c, const float* o_lat, const void* w_uv,
                         void* out, hipStream_t st) {
+  if (std::is_same<T, uint16_t>::value && d_h % 32 == 0 && d_c % 64 == 0) {
+    up_project_mfma_kernel<<<dim3(d_h / 32, H, (R + 31) / 32), 256, 0, st>>>(
+        R, H, d_h, d_c, o_lat, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out));
+    return hipGetLastError();
+  }
   switch (rows_per_wg(R, H)) {
     case 4: return up_project_rb<T, 4>(R, H, d_h, d_c, o_lat, w_uv, out, st);
     default: return up_project_rb<T, 1>(R, H, d_h, d_c, o_lat, w_uv, out, st);
