@@ -242,9 +242,13 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(BwdArgs a) {
 
 // Reverse in-block sum of dP and the gate backward: one wave per (sequence,
 // block of s tokens), its tokens last to first; lane l holds columns l,
-// l + 64, ... of the running sum G.  Writes dc, dk^R and du of every token.
-template <typename T>
+// l + 64, ... (JW of them) of the running sum G.  Tokens go in rounds of TB
+// whose loads are all issued before the round's sequential part (the
+// running sum, one wave reduction per token, the stores).  Writes dc, dk^R
+// and du of every token.
+template <typename T, int JW>
 __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
+  constexpr int TB = 4;
   const int lane = threadIdx.x & 63;
   const int wv = (blockIdx.x * 256 + threadIdx.x) >> 6;
   const int nblk = (a.N + a.s - 1) / a.s;
@@ -252,41 +256,55 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
   const int b = wv / nblk, blk = wv % nblk;
   const int W = a.d_c + a.d_r, KV2 = 2 * a.H * a.d_h, ldk = KV2 + a.H * a.d_r;
   const int t0 = blk * a.s, t1 = min(t0 + a.s, a.N);
-  float G[16];
+  float G[JW];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) G[j] = 0.f;
-  for (int t = t1 - 1; t >= t0; --t) {
-    const size_t row = static_cast<size_t>(b) * a.N + t;
-    const float w = a.gate[row];
-    float x[16], dwl = 0.f;
+  for (int j = 0; j < JW; ++j) G[j] = 0.f;
+  for (int tt = t1 - 1; tt >= t0; tt -= TB) {
+    float x[TB][JW], dP[TB][JW], w[TB];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int e = lane + 64 * j;
-      x[j] = 0.f;
-      if (e >= W) continue;
-      float dP;
-      if (e < a.d_c) {
-        dP = a.dPc[row * a.d_c + e];
-        x[j] = ld<T>(a.c, row * a.d_c + e);
-      } else {
-        const int r = e - a.d_c;
-        dP = 0.f;
-        for (int hh = 0; hh < a.H; ++hh) dP += ld<T>(a.dKV, row * ldk + KV2 + hh * a.d_r + r);
-        x[j] = ld<T>(a.k_r, row * a.d_r + r);
+    for (int u = 0; u < TB; ++u) {
+      // tokens before the block's first re-read that token (not used)
+      const size_t row = static_cast<size_t>(b) * a.N + max(tt - u, t0);
+      w[u] = a.gate[row];
+#pragma unroll
+      for (int j = 0; j < JW; ++j) {
+        const int e = lane + 64 * j;
+        x[u][j] = 0.f;
+        dP[u][j] = 0.f;
+        if (e < a.d_c) {
+          dP[u][j] = a.dPc[row * a.d_c + e];
+          x[u][j] = ld<T>(a.c, row * a.d_c + e);
+        } else if (e < W) {
+          const int r = e - a.d_c;
+          float acc = 0.f;
+#pragma unroll 8
+          for (int hh = 0; hh < a.H; ++hh) acc += ld<T>(a.dKV, row * ldk + KV2 + hh * a.d_r + r);
+          dP[u][j] = acc;
+          x[u][j] = ld<T>(a.k_r, row * a.d_r + r);
+        }
       }
-      G[j] += dP;
-      dwl = fmaf(G[j], x[j], dwl);
     }
-    const float du = wave_sum(dwl) * w * (1.f - w);
-    if (lane == 0) a.du[row] = du;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int e = lane + 64 * j;
-      if (e >= W) continue;
-      if (e < a.d_c)
-        st<T>(a.g_c, row * a.d_c + e, fmaf(du, a.w_hyp[e], w * G[j]));
-      else
-        st<T>(a.g_k_r, row * a.d_r + (e - a.d_c), w * G[j]);
+    for (int u = 0; u < TB; ++u) {
+      const int t = tt - u;
+      if (t < t0) break;
+      const size_t row = static_cast<size_t>(b) * a.N + t;
+      float dwl = 0.f;
+#pragma unroll
+      for (int j = 0; j < JW; ++j) {
+        G[j] += dP[u][j];
+        dwl = fmaf(G[j], x[u][j], dwl);
+      }
+      const float du = wave_sum(dwl) * w[u] * (1.f - w[u]);
+      if (lane == 0) a.du[row] = du;
+#pragma unroll
+      for (int j = 0; j < JW; ++j) {
+        const int e = lane + 64 * j;
+        if (e < a.d_c)
+          st<T>(a.g_c, row * a.d_c + e, fmaf(du, a.w_hyp[e], w[u] * G[j]));
+        else if (e < W)
+          st<T>(a.g_k_r, row * a.d_r + (e - a.d_c), w[u] * G[j]);
+      }
     }
   }
 }
@@ -1140,13 +1158,24 @@ hipError_t launch_bwd_attention(const BwdArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename T>
+static void scan_launch(const BwdArgs& a, dim3 grid, hipStream_t st) {
+  const int W = a.d_c + a.d_r;
+  if (W <= 5 * 64)
+    bwd_scan_kernel<T, 5><<<grid, 256, 0, st>>>(a);
+  else if (W <= 9 * 64)
+    bwd_scan_kernel<T, 9><<<grid, 256, 0, st>>>(a);
+  else
+    bwd_scan_kernel<T, 16><<<grid, 256, 0, st>>>(a);
+}
+
 hipError_t launch_bwd_scan(const BwdArgs& a, int dtype, hipStream_t st) {
   const int waves = a.B * ((a.N + a.s - 1) / a.s);
   const dim3 grid((waves + 3) / 4);
   if (dtype == 0)
-    bwd_scan_kernel<float><<<grid, 256, 0, st>>>(a);
+    scan_launch<float>(a, grid, st);
   else
-    bwd_scan_kernel<uint16_t><<<grid, 256, 0, st>>>(a);
+    scan_launch<uint16_t>(a, grid, st);
   return hipGetLastError();
 }
 
