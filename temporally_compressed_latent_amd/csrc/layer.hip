@@ -104,8 +104,20 @@ __device__ __forceinline__ int row_position(const LayerGemmArgs& g, int m) {
   return (g.pos0 ? g.pos0[b] : g.p0_all) + t - 1;
 }
 
+// Two consecutive elements at an even index i of a 16-byte aligned array, in
+// one store.
+__device__ __forceinline__ void store2(float* p, size_t i, float x0, float x1) {
+  *reinterpret_cast<float2*>(p + i) = float2{x0, x1};
+}
+__device__ __forceinline__ void store2(uint16_t* p, size_t i, float x0, float x1) {
+  *reinterpret_cast<uint32_t*>(p + i) =
+      static_cast<uint32_t>(f32_to_bf16_bits(x0)) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
+}
+
 // Store the output pair C[m, n], C[m, n + 1] (n even) at its destination; pos
-// is row m's token position (used by rope pairs only).
+// is row m's token position (used by rope pairs only).  Every destination
+// index is even (d_c, d_r, d_h and a plain output's N are even) and every
+// destination 16-byte aligned, so a pair is one store.
 template <typename T>
 __device__ __forceinline__ void store_pair(const LayerGemmArgs& g, const PairDest& p, int m, int n, int pos,
                                            float x0, float x1) {
@@ -113,31 +125,31 @@ __device__ __forceinline__ void store_pair(const LayerGemmArgs& g, const PairDes
   switch (p.kind) {
     case 0:
       i = static_cast<size_t>(m) * g.N + n;
-      if (g.out_f32) {
-        static_cast<float*>(g.out)[i] = x0;
-        if (n + 1 < g.N) static_cast<float*>(g.out)[i + 1] = x1;
+      if (n + 1 >= g.N) {  // (an odd N's last column)
+        if (g.out_f32)
+          static_cast<float*>(g.out)[i] = x0;
+        else
+          store_val<T>(g.out, i, x0);
+      } else if (g.out_f32) {
+        store2(static_cast<float*>(g.out), i, x0, x1);
       } else {
-        store_val<T>(g.out, i, x0);
-        if (n + 1 < g.N) store_val<T>(g.out, i + 1, x1);
+        store2(static_cast<T*>(g.out), i, x0, x1);
       }
       return;
     case 1:
       i = static_cast<size_t>(m) * g.d_c + n;
-      store_val<T>(g.c, i, x0);
-      store_val<T>(g.c, i + 1, x1);
+      store2(static_cast<T*>(g.c), i, x0, x1);
       return;
     case 2:
       i = (static_cast<size_t>(m) * g.H + p.head) * g.d_h + p.e;
-      store_val<T>(g.q_c, i, x0);
-      store_val<T>(g.q_c, i + 1, x1);
+      store2(static_cast<T*>(g.q_c), i, x0, x1);
       return;
     default: {
       rope_rotate(pos, p.theta, x0, x1);
       void* dst = p.kind == 3 ? g.q_r : g.k_r;
       i = p.kind == 3 ? (static_cast<size_t>(m) * g.H + p.head) * g.d_r + p.e
                       : static_cast<size_t>(m) * g.d_r + p.e;
-      store_val<T>(dst, i, x0);
-      store_val<T>(dst, i + 1, x1);
+      store2(static_cast<T*>(dst), i, x0, x1);
       return;
     }
   }
@@ -305,30 +317,35 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
     arow[i] = static_cast<const uint16_t*>(g.A) + static_cast<size_t>(min(m0 + r, M - 1)) * lda;
     wrow[i] = weight_row<uint16_t>(g, min(n0 + r, N - 1));
   }
-  uint4 ra[CPT], rw[CPT];
-  // chunks past K read as zero (K is a multiple of 8); the address is kept
-  // inside the row and the value replaced, so no load sits under a branch
-  auto gload = [&](int k0) {
+  // Two K steps are in flight: each step's chunks land in one of two register
+  // sets and go to LDS one step later.  Chunks past K read as zero (K is a
+  // multiple of 8): the address is kept inside the row and the value masked
+  // when it is stored, so no load sits under a branch or waits early.
+  struct Regs {
+    uint4 a[CPT], w[CPT];
+  };
+  auto gload = [&](Regs& R, int k0) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int k = k0 + kofs[i];
-      const int kk = min(k, K - 8);
-      const uint4 va = *reinterpret_cast<const uint4*>(arow[i] + kk);
-      const uint4 vw = *reinterpret_cast<const uint4*>(wrow[i] + kk);
-      // (a mask, not a select of the vectors, which the compiler would
-      // route through scratch memory)
-      const uint32_t keep = k < K ? 0xffffffffu : 0u;
-      ra[i] = uint4{va.x & keep, va.y & keep, va.z & keep, va.w & keep};
-      rw[i] = uint4{vw.x & keep, vw.y & keep, vw.z & keep, vw.w & keep};
+      const int kk = min(k0 + kofs[i], K - 8);
+      R.a[i] = *reinterpret_cast<const uint4*>(arow[i] + kk);
+      R.w[i] = *reinterpret_cast<const uint4*>(wrow[i] + kk);
     }
+    // keep the loads where they are issued (the scheduler would sink them
+    // towards their LDS stores, which then wait for a full round trip)
+    __builtin_amdgcn_sched_barrier(0);
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const Regs& R, int k0, int buf) {
     uint16_t* sA = smem + buf * (MBM + MBN) * MP;
     uint16_t* sW = sA + MBM * MP;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      *reinterpret_cast<uint4*>(sA + lofs[i]) = ra[i];
-      *reinterpret_cast<uint4*>(sW + lofs[i]) = rw[i];
+      // (a mask, not a select of the vectors, which the compiler would
+      // route through scratch memory)
+      const uint32_t keep = k0 + kofs[i] < K ? 0xffffffffu : 0u;
+      const uint4 va = R.a[i], vw = R.w[i];
+      *reinterpret_cast<uint4*>(sA + lofs[i]) = uint4{va.x & keep, va.y & keep, va.z & keep, va.w & keep};
+      *reinterpret_cast<uint4*>(sW + lofs[i]) = uint4{vw.x & keep, vw.y & keep, vw.z & keep, vw.w & keep};
     }
   };
   f32x16 acc[2][2];
@@ -338,13 +355,7 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  const int nk = (K + MBK - 1) / MBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * MBK);
+  auto compute = [&](int buf) {
     const uint16_t* sA = smem + buf * (MBM + MBN) * MP;
     const uint16_t* sW = sA + MBM * MP;
 #pragma unroll
@@ -360,8 +371,31 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    // the other buffer was last read before the previous barrier
-    if (kt + 1 < nk) lstore(buf ^ 1);
+  };
+  // step kt is computed from LDS buffer kt & 1; meanwhile step kt + 1 sits in
+  // registers (stored after the compute) and step kt + 2 is being loaded.
+  // Loads and stores are unconditional, steps past the end re-reading the
+  // last one, so that the waits before the stores count only the older set
+  // and the loads are not sunk next to their stores.
+  const int nk = (K + MBK - 1) / MBK;
+  Regs R0, R1;
+  gload(R0, 0);
+  gload(R1, min(1, nk - 1) * MBK);
+  lstore(R0, 0, 0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    gload(R0, min(kt + 2, nk - 1) * MBK);
+    compute(0);
+    lstore(R1, (kt + 1) * MBK, 1);
+    __syncthreads();
+    gload(R1, min(kt + 3, nk - 1) * MBK);
+    compute(1);
+    lstore(R0, min(kt + 2, nk - 1) * MBK, 0);
+    __syncthreads();
+  }
+  if (kt < nk) {  // odd step count: the last step is in buffer 0
+    compute(0);
     __syncthreads();
   }
 

@@ -61,23 +61,30 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
       const_cast<uint16_t*>(A), static_cast<short>(0), M * W * 2, kBufferRsrcWord3);
   const uint16_t* bmat = col0 < HD ? w_uk + static_cast<size_t>(col0) * d_c
                                    : w_uv + static_cast<size_t>(col0 - HD) * d_c;
-  // Named registers (not arrays), so they are never placed in scratch.
-  uint4 ra0, ra1, rb0, rb1;
+  // Two K steps are in flight: each step's chunks land in one of two named
+  // register sets (not arrays, so they are never placed in scratch) and go
+  // to LDS one step later.
   const int r0 = tid >> 2, r1 = (tid + 256) >> 2, ch = tid & 3;  // chunk (r, ch), two per thread
-  auto gload = [&](int k0) {
+  struct Regs {
+    uint4 a0, a1, b0, b1;
+  };
+  auto gload = [&](Regs& R, int k0) {
     const int so = (row0 * W + k0) * 2;
     const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rs_a, (r0 * W + ch * 8) * 2, so, 0);
     const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rs_a, (r1 * W + ch * 8) * 2, so, 0);
-    ra0 = uint4{v0[0], v0[1], v0[2], v0[3]};
-    ra1 = uint4{v1[0], v1[1], v1[2], v1[3]};
-    rb0 = *reinterpret_cast<const uint4*>(bmat + static_cast<size_t>(r0) * d_c + k0 + ch * 8);
-    rb1 = *reinterpret_cast<const uint4*>(bmat + static_cast<size_t>(r1) * d_c + k0 + ch * 8);
+    R.a0 = uint4{v0[0], v0[1], v0[2], v0[3]};
+    R.a1 = uint4{v1[0], v1[1], v1[2], v1[3]};
+    R.b0 = *reinterpret_cast<const uint4*>(bmat + static_cast<size_t>(r0) * d_c + k0 + ch * 8);
+    R.b1 = *reinterpret_cast<const uint4*>(bmat + static_cast<size_t>(r1) * d_c + k0 + ch * 8);
+    // keep the loads where they are issued (the scheduler would sink them
+    // towards their LDS stores, which then wait for a full round trip)
+    __builtin_amdgcn_sched_barrier(0);
   };
-  auto lstore = [&](int buf) {
-    *reinterpret_cast<uint4*>(&sA[buf][r0 * GP + ch * 8]) = ra0;
-    *reinterpret_cast<uint4*>(&sA[buf][r1 * GP + ch * 8]) = ra1;
-    *reinterpret_cast<uint4*>(&sB[buf][r0 * GP + ch * 8]) = rb0;
-    *reinterpret_cast<uint4*>(&sB[buf][r1 * GP + ch * 8]) = rb1;
+  auto lstore = [&](const Regs& R, int buf) {
+    *reinterpret_cast<uint4*>(&sA[buf][r0 * GP + ch * 8]) = R.a0;
+    *reinterpret_cast<uint4*>(&sA[buf][r1 * GP + ch * 8]) = R.a1;
+    *reinterpret_cast<uint4*>(&sB[buf][r0 * GP + ch * 8]) = R.b0;
+    *reinterpret_cast<uint4*>(&sB[buf][r1 * GP + ch * 8]) = R.b1;
   };
 
   f32x4 acc[4][4];
@@ -85,14 +92,7 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = d_c / GBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * GBK);
+  auto compute = [&](int buf) {
     bf16x8 af[4], bfr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -105,7 +105,31 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    if (kt + 1 < nk) lstore(buf ^ 1);
+  };
+
+  // step kt is computed from LDS buffer kt & 1; while it is, step kt + 1 sits
+  // in registers (stored after the compute) and step kt + 2 is being loaded
+  const int nk = d_c / GBK;
+  Regs R0, R1;
+  gload(R0, 0);
+  gload(R1, min(1, nk - 1) * GBK);
+  lstore(R0, 0);
+  __syncthreads();
+  // (the loads are issued unconditionally, steps past the end re-reading the
+  // last one, so that the waits before the LDS stores count only the older set)
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    gload(R0, min(kt + 2, nk - 1) * GBK);
+    compute(0);
+    lstore(R1, 1);
+    __syncthreads();
+    gload(R1, min(kt + 3, nk - 1) * GBK);
+    compute(1);
+    lstore(R0, 0);  // unconditional, or the loads would be sunk next to it
+    __syncthreads();
+  }
+  if (kt < nk) {  // odd step count: the last step is in buffer 0
+    compute(0);
     __syncthreads();
   }
 
