@@ -98,6 +98,20 @@ __device__ __forceinline__ void rope_rotate(int pos, double theta, float& x0, fl
   x1 = y1;
 }
 
+// The same rotation with the angle reduced, in double, to revolutions in
+// [-1/2, 1/2] and the hardware sine and cosine of 2 pi r: for bf16 outputs,
+// whose rounding (2^-9) is far above the hardware functions' error.
+__device__ __forceinline__ void rope_rotate_rev(int pos, double theta, float& x0, float& x1) {
+  constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+  const double rev = static_cast<double>(pos) * theta * kInvTwoPi;
+  const float r = static_cast<float>(rev - rint(rev));
+  const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
+  const float y0 = x0 * cs - x1 * sn;
+  const float y1 = x0 * sn + x1 * cs;
+  x0 = y0;
+  x1 = y1;
+}
+
 // 0-based position of the token in GEMM row m (sequence m / T, token m % T).
 __device__ __forceinline__ int row_position(const LayerGemmArgs& g, int m) {
   const int b = m / g.T, t = m % g.T;
@@ -118,7 +132,7 @@ __device__ __forceinline__ void store2(uint16_t* p, size_t i, float x0, float x1
 // is row m's token position (used by rope pairs only).  Every destination
 // index is even (d_c, d_r, d_h and a plain output's N are even) and every
 // destination 16-byte aligned, so a pair is one store.
-template <typename T>
+template <typename T, bool kRev = false>
 __device__ __forceinline__ void store_pair(const LayerGemmArgs& g, const PairDest& p, int m, int n, int pos,
                                            float x0, float x1) {
   size_t i;
@@ -145,7 +159,10 @@ __device__ __forceinline__ void store_pair(const LayerGemmArgs& g, const PairDes
       store2(static_cast<T*>(g.q_c), i, x0, x1);
       return;
     default: {
-      rope_rotate(pos, p.theta, x0, x1);
+      if constexpr (kRev)
+        rope_rotate_rev(pos, p.theta, x0, x1);
+      else
+        rope_rotate(pos, p.theta, x0, x1);
       void* dst = p.kind == 3 ? g.q_r : g.k_r;
       i = p.kind == 3 ? (static_cast<size_t>(m) * g.H + p.head) * g.d_r + p.e
                       : static_cast<size_t>(m) * g.d_r + p.e;
@@ -295,6 +312,7 @@ constexpr int MCP = MBN + 4;  // C half-tile pitch (floats)
 
 __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, int nrt, int nct) {
   __shared__ __align__(16) uint16_t smem[2 * (MBM + MBN) * MP];
+  __shared__ int sPos[MBM];
   static_assert(64 * MCP * 4 <= sizeof(smem), "C half tile fits in the operand buffers");
   const int L = blockIdx.x;
   const int xcd = L & 7, k8 = L >> 3;
@@ -400,10 +418,12 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
   }
 
   // epilogue, one 64-row half at a time: acc[i][j][e] is row
-  // 64 wm + 32 i + 8 (e / 4) + 4 grp + e % 4, column 64 wn + 32 j + c32
+  // 64 wm + 32 i + 8 (e / 4) + 4 grp + e % 4, column 64 wn + 32 j + c32.
+  // The rows' token positions (rope pairs) are computed once per row.
   float* sC = reinterpret_cast<float*>(smem);
   const int pc = tid & 63, n = n0 + 2 * pc;
   const PairDest pd = pair_dest(g, min(n, N - 2));
+  if (g.mode != 0 && tid < MBM) sPos[tid] = row_position(g, min(m0 + tid, M - 1));
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     if (wm == hh) {
@@ -420,8 +440,8 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
       for (int r = tid >> 6; r < 64; r += 4) {
         const int m = m0 + 64 * hh + r;
         if (m >= M) break;
-        store_pair<uint16_t>(g, pd, m, n, pd.kind >= 3 ? row_position(g, m) : 0, sC[r * MCP + 2 * pc],
-                             sC[r * MCP + 2 * pc + 1]);
+        store_pair<uint16_t, true>(g, pd, m, n, pd.kind >= 3 ? sPos[64 * hh + r] : 0, sC[r * MCP + 2 * pc],
+                                   sC[r * MCP + 2 * pc + 1]);
       }
     }
     __syncthreads();
