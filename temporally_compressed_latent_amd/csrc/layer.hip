@@ -35,12 +35,22 @@ struct LayerSmem {
   T w[2][LBN * LP];
 };
 
-// Weight row n of the virtual [N, K] matrix [w0 ; w1 ; w2].
+// Weight row n of the virtual [N, K] matrix [w0 ; w1 ; w2].  For the input
+// projection (mode 1) the rows of w1 = W_Q are taken grouped by kind: first
+// the q^C rows of every head, then the q^R rows of every head, so that a
+// column tile of the product holds one kind of output (c, q^C, q^R or k^R)
+// and only the q^R and k^R tiles rotate.
 template <typename T>
 __device__ __forceinline__ const T* weight_row(const LayerGemmArgs& g, int n) {
   if (n < g.n0) return static_cast<const T*>(g.w0) + static_cast<size_t>(n) * g.K;
   n -= g.n0;
-  if (n < g.n1) return static_cast<const T*>(g.w1) + static_cast<size_t>(n) * g.K;
+  if (n < g.n1) {
+    if (g.mode != 0) {
+      const int QW = g.d_h + g.d_r, HC = g.H * g.d_h;
+      n = n < HC ? (n / g.d_h) * QW + n % g.d_h : ((n - HC) / g.d_r) * QW + g.d_h + (n - HC) % g.d_r;
+    }
+    return static_cast<const T*>(g.w1) + static_cast<size_t>(n) * g.K;
+  }
   n -= g.n1;
   return static_cast<const T*>(g.w2) + static_cast<size_t>(n) * g.K;
 }
@@ -62,18 +72,19 @@ struct PairDest {
 __device__ __forceinline__ PairDest pair_dest(const LayerGemmArgs& g, int n) {
   PairDest p{0, 0, n, 0.0};
   if (g.mode == 0) return p;
-  const int QW = g.d_h + g.d_r, HQ = g.H * QW;
+  // columns in weight_row's order: c, then q^C of every head, then q^R of
+  // every head, then k^R
+  const int QW = g.d_h + g.d_r, HQ = g.H * QW, HC = g.H * g.d_h;
   if (n < g.d_c) {
     p.kind = 1;
+  } else if (n < g.d_c + HC) {
+    p.kind = 2;
+    p.head = (n - g.d_c) / g.d_h;
+    p.e = (n - g.d_c) % g.d_h;
   } else if (n < g.d_c + HQ) {
-    p.head = (n - g.d_c) / QW;
-    p.e = (n - g.d_c) % QW;
-    if (p.e < g.d_h) {
-      p.kind = 2;
-    } else {
-      p.kind = 3;
-      p.e -= g.d_h;
-    }
+    p.kind = 3;
+    p.head = (n - g.d_c - HC) / g.d_r;
+    p.e = (n - g.d_c - HC) % g.d_r;
   } else {
     p.kind = 4;
     p.e = n - g.d_c - HQ;
