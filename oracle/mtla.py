@@ -26,7 +26,8 @@ reason, in the design notes):
     embedding"; the Method paragraph says "multiplied");
   * one scalar gate per token, w_t = sigmoid(W_hyp . (c_t + pe_t)), no bias;
     the s gates of a block form the merge weights W in R^s, and the same w_t
-    scales both c_t and k^R_t;
+    scales both c_t and k^R_t.  A variant takes W_hyp in R^{s x d_c}, the
+    linear layer's s outputs, of which token t uses output (t - 1) mod s;
   * the first token of a block overwrites its slot, later tokens add to it;
   * sinusoidal pe and RoPE use interleaved (even, odd) pairs, base 10000,
     position t-1; RoPE is applied before merging;
@@ -168,14 +169,31 @@ def sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
-def gate(c: np.ndarray, pe: np.ndarray, w_hyp: np.ndarray) -> np.ndarray:
+def gate_rows(w_hyp: np.ndarray, T: int, t_first: int = 1) -> np.ndarray:
+    """The W_hyp row each of T consecutive tokens t_first.. takes: [T, d_c].
+
+    w_hyp [d_c] is one weight vector for every token.  w_hyp [s, d_c] is the
+    per-position variant: the hyper-network's linear layer has s outputs (the
+    merge weights W_t in R^s of [MTLA-wiki] Method (1)), and token t takes
+    output (t - 1) mod s, its own place in its block.
+    """
+    wh = np.asarray(w_hyp, dtype=F)
+    if wh.ndim == 1:
+        return np.broadcast_to(wh, (T, wh.shape[0]))
+    return wh[(t_first - 1 + np.arange(T)) % wh.shape[0]]
+
+
+def gate(c: np.ndarray, pe: np.ndarray, w_hyp: np.ndarray, t_first: int = 1) -> np.ndarray:
     """w_t = sigmoid(W_hyp . (c_t + pe_t)) for every token row.
 
-    [MTLA-wiki] Key claims, paper Sec. 4.1 Eq. 13.  c: [T, d_c]; pe: [T, d_c]
-    rows for the same positions; w_hyp: [d_c].  Returns [T].
+    [MTLA-wiki] Key claims, paper Sec. 4.1 Eq. 13.  c: [T, d_c] for tokens
+    t_first .. t_first + T - 1; pe: [T, d_c] rows for the same positions;
+    w_hyp: [d_c], or [s, d_c] per position in the block (see gate_rows).
+    Returns [T].
     """
     c = np.asarray(c, dtype=F)
-    return sigmoid((c + np.asarray(pe, dtype=F)) @ np.asarray(w_hyp, dtype=F))
+    x = c + np.asarray(pe, dtype=F)
+    return sigmoid(np.sum(x * gate_rows(w_hyp, c.shape[0], t_first), axis=1))
 
 
 # ---------------------------------------------------------------------------
@@ -402,12 +420,23 @@ def partial_merges_backward(dP: np.ndarray, s: int) -> np.ndarray:
     return G
 
 
-def gate_backward(c, pe, w_hyp, w, dw):
+def gate_backward(c, pe, w_hyp, w, dw, t_first: int = 1):
     """Through w_k = sigmoid(u_k), u_k = W_hyp . (c_k + pe_k): returns the
-    gate's share of dc ([N, d_c]) and dW_hyp ([d_c]) given dw ([N])."""
+    gate's share of dc ([N, d_c]) and dW_hyp (shaped like w_hyp) given dw
+    ([N]).  With one W_hyp row per position in the block, row r collects the
+    tokens that take it."""
     c, pe, w_hyp = (np.asarray(a, dtype=F) for a in (c, pe, w_hyp))
     du = np.asarray(dw, dtype=F) * w * (1.0 - w)
-    return du[:, None] * w_hyp[None, :], (c + pe).T @ du
+    rows = gate_rows(w_hyp, c.shape[0], t_first)
+    if w_hyp.ndim == 1:
+        return du[:, None] * rows, (c + pe).T @ du
+    s = w_hyp.shape[0]
+    which = (t_first - 1 + np.arange(c.shape[0])) % s
+    dwh = np.zeros_like(w_hyp)
+    for r in range(s):
+        sel = which == r
+        dwh[r] = (c[sel] + pe[sel]).T @ du[sel]
+    return du[:, None] * rows, dwh
 
 
 def parallel_backward(c, k_r, q_c, q_r, w_hyp, w_uk, w_uv, s: int, scale: float,

@@ -153,6 +153,34 @@ def pin_gate_zero_weights(o):
     assert wp[0] > 0.5 and abs(wp[0] - 1.0 / (1.0 + math.exp(-16.0))) < 1e-15
 
 
+def pin_gate_per_position(o):
+    """One W_hyp row per place in the block: with c + pe a basis vector e_k,
+    token t's logit is entry k of row (t - 1) mod s, written out here; rows
+    that are all equal give the one-row gate exactly; a continuation starting
+    at token t_first keeps its tokens' places."""
+    s, d_c, N = 3, 4, 8
+    w_hyp = np.arange(s * d_c, dtype=float).reshape(s, d_c) / 7.0 - 0.6
+    pe = o.sinusoidal_pe(N, d_c)
+    ks = [1, 3, 0, 2, 2, 1, 0, 3]
+    c = np.stack([np.eye(d_c)[k] for k in ks]) - pe
+    want = np.array([1.0 / (1.0 + math.exp(-w_hyp[(t - 1) % s, ks[t - 1]])) for t in range(1, N + 1)])
+    got = o.gate(c, pe, w_hyp)
+    assert np.max(np.abs(got - want)) <= 1e-15, (got, want)
+    # a continuation from token 5 gives the same gates to tokens 5..8
+    assert np.max(np.abs(o.gate(c[4:], pe[4:], w_hyp, t_first=5) - want[4:])) <= 1e-15
+    # equal rows: the one-row gate, and the same forward passes
+    g = np.random.default_rng(17)
+    row = g.standard_normal(d_c)
+    c2 = g.standard_normal((N, d_c))
+    assert np.array_equal(o.gate(c2, pe, np.tile(row, (s, 1))), o.gate(c2, pe, row))
+    args = list(_rand_case(18, 7, s, 2, 3, d_c, 2))
+    scale = 0.45
+    one = o.parallel(*args, s, scale)
+    args[4] = np.tile(args[4], (s, 1))
+    assert np.array_equal(o.parallel(*args, s, scale), one)
+    assert o.max_rel_err(o.incremental(*args, s, scale), one) <= 1e-12
+
+
 def pin_merge_half_sum(o):
     """With w = 1/2 the slot is half the block sum; integers keep it exact."""
     g = np.random.default_rng(5)
@@ -374,9 +402,13 @@ def pin_backward_finite_differences(o):
     (the causal mask) and s >= N (the diagonal alone)."""
     H, d_h, d_c, d_r, scale, eps = 2, 3, 4, 2, 0.4, 1e-6
     names = ("dc", "dk_r", "dq_c", "dq_r", "dw_hyp", "dw_uk", "dw_uv")
-    for seed, N, s in ((61, 7, 3), (62, 6, 2), (63, 5, 1), (64, 4, 5)):
+    # (the last case takes one W_hyp row per place in the block)
+    for seed, N, s, per_pos in ((61, 7, 3, False), (62, 6, 2, False), (63, 5, 1, False), (64, 4, 5, False),
+                                (65, 7, 3, True)):
         args = list(_rand_case(seed, N, s, H, d_h, d_c, d_r, w_scale=0.5))
         g = np.random.default_rng(seed + 100)
+        if per_pos:
+            args[4] = g.standard_normal((s, d_c)) * 0.5
         d_o = g.standard_normal((N, H, d_h))
         pe = g.standard_normal((N, d_c))
         grads = o.parallel_backward(*args, s, scale, d_o, pe=pe)
@@ -400,7 +432,8 @@ def pin_backward_finite_differences(o):
 ALL_PINS = [
     pin_slot_index, pin_block_starts, pin_slot_count, pin_mask_special_cases,
     pin_mask_structure, pin_mask_matches_incremental_cache, pin_cache_ratio,
-    pin_row_bytes, pin_gate_zero_weights, pin_merge_half_sum, pin_block_start_overwrites,
+    pin_row_bytes, pin_gate_zero_weights, pin_gate_per_position, pin_merge_half_sum,
+    pin_block_start_overwrites,
     pin_uniform_attention_keyset, pin_absorption, pin_decode_single_slot,
     pin_s1_equals_causal_sdpa, pin_parallel_equals_incremental,
     pin_prefill_query_rows, pin_rope, pin_pe, pin_layer_schedules,

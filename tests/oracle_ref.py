@@ -22,6 +22,6 @@ def merged_cache(c, k_r, w_hyp, s: int, t0: int = 1, cache=None):
     """Slot cache after appending tokens t0.. (rows of c, k_r) to ``cache``."""
     n = t0 + c.shape[0] - 1
     pe = oracle.sinusoidal_pe(n, c.shape[1])[t0 - 1:]
-    w = oracle.gate(c, pe, w_hyp)
+    w = oracle.gate(c, pe, w_hyp, t_first=t0)
     x = np.concatenate([np.asarray(c, np.float64), np.asarray(k_r, np.float64)], axis=1)
     return oracle.merge_incremental(x, w, s, cache=cache, t0=t0), w

@@ -57,12 +57,25 @@ def _decode_absorbed_scale_sq(q_c, q_r, slots, w_uk, w_uv, d_c, scale):
     return _ORIG["decode_absorbed"](q_c, q_r, slots, w_uk, w_uv, d_c, scale * scale)
 
 
-def _gate_product(c, pe, w_hyp):
+def _gate_product(c, pe, w_hyp, t_first=1):
     return O.sigmoid((np.asarray(c) * np.asarray(pe)) @ np.asarray(w_hyp))
 
 
-def _gate_no_pe(c, pe, w_hyp):
+def _gate_no_pe(c, pe, w_hyp, t_first=1):
     return O.sigmoid(np.asarray(c, dtype=float) @ np.asarray(w_hyp, dtype=float))
+
+
+def _gate_rows_place_off_by_one(w_hyp, T, t_first=1):
+    # token t takes row t mod s instead of its place (t - 1) mod s
+    wh = np.asarray(w_hyp, dtype=float)
+    if wh.ndim == 1:
+        return np.broadcast_to(wh, (T, wh.shape[0]))
+    return wh[(t_first + np.arange(T)) % wh.shape[0]]
+
+
+def _gate_rows_ignore_start(w_hyp, T, t_first=1):
+    # a continuation restarts the places at its first token
+    return _ORIG["gate_rows"](w_hyp, T, 1)
 
 
 def _softmax_no_max(z):
@@ -134,19 +147,27 @@ def _softmax_backward_no_rowsum(a, da):
     return np.asarray(a, dtype=float) * np.asarray(da, dtype=float)
 
 
-def _gate_backward_no_pe(c, pe, w_hyp, w, dw):
-    return _ORIG["gate_backward"](c, np.zeros_like(np.asarray(pe, dtype=float)), w_hyp, w, dw)
+def _gate_backward_no_pe(c, pe, w_hyp, w, dw, t_first=1):
+    return _ORIG["gate_backward"](c, np.zeros_like(np.asarray(pe, dtype=float)), w_hyp, w, dw, t_first)
 
 
-def _gate_backward_no_sigmoid_slope(c, pe, w_hyp, w, dw):
+def _gate_backward_no_sigmoid_slope(c, pe, w_hyp, w, dw, t_first=1):
     # takes dw as du (drops the sigmoid's derivative w (1 - w))
     du = np.asarray(dw, dtype=float)
     w_hyp = np.asarray(w_hyp, dtype=float)
     return du[:, None] * w_hyp[None, :], (np.asarray(c) + np.asarray(pe)).T @ du
 
 
+def _gate_backward_rows_summed(c, pe, w_hyp, w, dw, t_first=1):
+    # per-position W_hyp: every row receives the gradient of all the tokens
+    dc, dwh = _ORIG["gate_backward"](c, pe, w_hyp, w, dw, t_first)
+    if np.asarray(w_hyp).ndim == 2:
+        dwh = np.tile(dwh.sum(axis=0), (dwh.shape[0], 1))
+    return dc, dwh
+
+
 _ORIG = {name: getattr(O, name) for name in
-         ("decode_absorbed", "rope", "sinusoidal_pe", "reorder_state", "gate_backward")}
+         ("decode_absorbed", "rope", "sinusoidal_pe", "reorder_state", "gate_backward", "gate_rows")}
 
 MUTATIONS = {
     "visible_keys": [_visible_keys_block_starts, _visible_keys_off_by_one, _visible_keys_no_diag],
@@ -156,6 +177,7 @@ MUTATIONS = {
     "append_token": [_append_token_always_add],
     "decode_absorbed": [_decode_absorbed_no_rope, _decode_absorbed_uv_from_uk, _decode_absorbed_scale_sq],
     "gate": [_gate_product, _gate_no_pe],
+    "gate_rows": [_gate_rows_place_off_by_one, _gate_rows_ignore_start],
     "softmax": [_softmax_no_max],
     "rope": [_rope_sign],
     "sinusoidal_pe": [_pe_swapped],
@@ -164,7 +186,7 @@ MUTATIONS = {
     "reorder_state": [_reorder_own_length, _reorder_scatter],
     "partial_merges_backward": [_merges_backward_prefix, _merges_backward_no_reset],
     "softmax_backward": [_softmax_backward_no_rowsum],
-    "gate_backward": [_gate_backward_no_pe, _gate_backward_no_sigmoid_slope],
+    "gate_backward": [_gate_backward_no_pe, _gate_backward_no_sigmoid_slope, _gate_backward_rows_summed],
 }
 
 CASES = [(name, fn) for name, fns in MUTATIONS.items() for fn in fns]
