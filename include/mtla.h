@@ -68,6 +68,12 @@ typedef enum { MTLA_FP32 = 0, MTLA_BF16 = 1 } mtla_dtype;
 
 /* Force the portable (vector-ALU) kernels even where the MFMA kernels apply. */
 #define MTLA_FLAG_PORTABLE 1
+/* Per-position gate: W_hyp has s rows ([stride_s, d_c] fp32, and so has
+ * grad_w_hyp) and token t takes row (t-1) mod s, its place in its block:
+ *   w_t = sigmoid(W_hyp[(t-1) mod s] . (c_t + pe_t)).
+ * The reading of "Multi-head Temporal Latent Attention", Method (1), in which
+ * the hyper-network's linear layer outputs the merge weights W_t in R^s. */
+#define MTLA_FLAG_GATE_PER_POSITION 2
 
 /* Supported dimensions: d_c and d_r multiples of 8, d_c + d_r <= 1024,
  * d_h <= 256, s <= 256 (MTLA_ERR_UNSUPPORTED otherwise). */
@@ -81,7 +87,7 @@ typedef struct {
   int32_t max_slots;   /* cache rows per sequence                               */
   int32_t dtype;       /* mtla_dtype of stored tensors                          */
   float softmax_scale; /* tau applied to scores; 1/sqrt(d_h + d_r) is usual     */
-  int32_t flags;       /* 0, or MTLA_FLAG_PORTABLE                              */
+  int32_t flags;       /* 0, or MTLA_FLAG_PORTABLE | MTLA_FLAG_GATE_PER_POSITION */
 } mtla_dims;
 
 /* Row width of the cache: W = d_c + d_r elements. */
@@ -115,7 +121,7 @@ int32_t mtla_sinusoidal_pe(int32_t rows, int32_t d, float* pe, void* stream);
  *   pos0     device [B] int32, 1-based position of the first appended token.
  *   c        device [B, n_tokens, d_c]   storage dtype.
  *   k_r      device [B, n_tokens, d_r]   storage dtype, RoPE already applied.
- *   w_hyp    device [d_c] fp32.
+ *   w_hyp    device [d_c] fp32 ([s, d_c] with MTLA_FLAG_GATE_PER_POSITION).
  *   pe       device [pe_rows, d_c] fp32; row t-1 is used for token t.
  *   cache    device [B, max_slots, d_c + d_r] storage dtype, in/out: every
  *            slot touched by the appended tokens is written (rounded once from
@@ -397,7 +403,8 @@ int32_t mtla_prefill_backward_workspace_bytes(const mtla_dims* dims, int32_t n_t
  *   G_k = sum of dP_j over j = k .. the end of k's block (reverse in-block sum);
  *   du_k = (G_k . x_k) w_k (1 - w_k);
  *   grad_c_k = w_k G^c_k + du_k W_hyp,  grad_k_r_k = w_k G^R_k,
- *   grad_w_hyp = sum_k du_k (c_k + pe_k).
+ *   grad_w_hyp = sum_k du_k (c_k + pe_k)  (with MTLA_FLAG_GATE_PER_POSITION,
+ *   W_hyp and grad_w_hyp row r over the tokens k with (k-1) mod s = r).
  * The forward pieces it needs (gates, partial merges, K^C and V, softmax
  * normalisers) are recomputed from the inputs.
  *   q_c, q_r, c, k_r, w_hyp, pe, pe_rows, w_uk, w_uv: as for mtla_prefill.
@@ -405,7 +412,7 @@ int32_t mtla_prefill_backward_workspace_bytes(const mtla_dims* dims, int32_t n_t
  *   grad_q_c  device [B, N, H, d_h], grad_q_r [B, N, H, d_r],
  *   grad_c    device [B, N, d_c],    grad_k_r [B, N, d_r] (storage dtype),
  *             written.
- *   grad_w_hyp device [d_c] fp32; grad_w_uk, grad_w_uv device [H, d_h, d_c]
+ *   grad_w_hyp device [d_c] ([s, d_c] per position) fp32; grad_w_uk, grad_w_uv device [H, d_h, d_c]
  *             fp32: written (not accumulated), summed over the B sequences.
  *   workspace device, >= mtla_prefill_backward_workspace_bytes(), 16-byte
  *             aligned; scratch.

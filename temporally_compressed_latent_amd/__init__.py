@@ -8,7 +8,7 @@ is used only for device memory and streams.
 """
 from ._lib import (  # noqa: F401
     LIB_PATH, MTLA_BF16, MTLA_ERR_HIP, MTLA_ERR_INVALID_ARG, MTLA_ERR_UNSUPPORTED,
-    MTLA_ERR_WORKSPACE, MTLA_FLAG_PORTABLE, MTLA_FP32, MTLA_OK, MtlaDims, MtlaError,
+    MTLA_ERR_WORKSPACE, MTLA_FLAG_GATE_PER_POSITION, MTLA_FLAG_PORTABLE, MTLA_FP32, MTLA_OK, MtlaDims, MtlaError,
     decode_attention_workspace, header_symbols, last_error, lib, make_dims, mtla_absorb_query,
     mtla_debug_slot_limits, mtla_debug_stride_mask, mtla_decode, mtla_decode_attention,
     mtla_decode_attention_workspace_bytes, mtla_decode_plan, mtla_decode_step, mtla_decode_workspace_bytes, mtla_merge_append,

@@ -30,6 +30,7 @@ MTLA_ERR_HIP = -4
 MTLA_FP32 = 0
 MTLA_BF16 = 1
 MTLA_FLAG_PORTABLE = 1
+MTLA_FLAG_GATE_PER_POSITION = 2
 
 
 class MtlaDims(ctypes.Structure):
@@ -49,6 +50,13 @@ class MtlaDims(ctypes.Structure):
     @property
     def width(self) -> int:
         return self.d_c + self.d_r
+
+    @property
+    def gate_shape(self) -> tuple:
+        """Shape of W_hyp (and of its gradient): [d_c], or [s, d_c] per position."""
+        if self.flags & MTLA_FLAG_GATE_PER_POSITION:
+            return (self.stride_s, self.d_c)
+        return (self.d_c,)
 
     @property
     def torch_dtype(self):
@@ -150,14 +158,15 @@ def mtla_version() -> int:
 
 
 def make_dims(batch: int, heads: int, d_h: int, d_c: int, d_r: int, s: int, max_slots: int,
-              dtype="bf16", softmax_scale: Optional[float] = None, portable: bool = False) -> MtlaDims:
+              dtype="bf16", softmax_scale: Optional[float] = None, portable: bool = False,
+              gate_per_position: bool = False) -> MtlaDims:
     d = MtlaDims()
     d.batch, d.heads, d.d_h, d.d_c, d.d_r = batch, heads, d_h, d_c, d_r
     d.stride_s, d.max_slots = s, max_slots
     d.dtype = {"fp32": MTLA_FP32, "bf16": MTLA_BF16, torch.float32: MTLA_FP32,
                torch.bfloat16: MTLA_BF16}[dtype]
     d.softmax_scale = 1.0 / math.sqrt(d_h + d_r) if softmax_scale is None else softmax_scale
-    d.flags = MTLA_FLAG_PORTABLE if portable else 0
+    d.flags = (MTLA_FLAG_PORTABLE if portable else 0) | (MTLA_FLAG_GATE_PER_POSITION if gate_per_position else 0)
     return d
 
 
@@ -217,7 +226,7 @@ def mtla_merge_append(dims: MtlaDims, pos0, c, k_r, w_hyp, pe, cache, open_acc,
         _tensor("pos0", pos0, (B,), torch.int32),
         _tensor("c", c, (B, T, dims.d_c), st),
         _tensor("k_r", k_r, (B, T, dims.d_r), st, optional=dims.d_r == 0),
-        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
         _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32),
         _tensor("cache", cache, (B, dims.max_slots, W), st),
         _tensor("open_acc", open_acc, (B, 2, W), torch.float32),
@@ -266,7 +275,7 @@ def mtla_decode_step(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w_uk, w_u
         _tensor("pos", pos, (B,), torch.int32),
         _tensor("c", c, (B, dims.d_c), st),
         _tensor("k_r", k_r, (B, dims.d_r), st, optional=dims.d_r == 0),
-        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
         _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
         _tensor("q_c", q_c, (B, H, dims.d_h), st),
         _tensor("q_r", q_r, (B, H, dims.d_r), st, optional=dims.d_r == 0),
@@ -337,7 +346,7 @@ def mtla_prefill(dims: MtlaDims, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_uv, cache,
         _tensor("q_r", q_r, (B, N, H, dims.d_r), st, optional=dims.d_r == 0),
         _tensor("c", c, (B, N, dims.d_c), st),
         _tensor("k_r", k_r, (B, N, dims.d_r), st, optional=dims.d_r == 0),
-        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
         _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
@@ -366,7 +375,7 @@ def mtla_prefill_backward(dims: MtlaDims, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_u
         _tensor("q_r", q_r, (B, N, H, dims.d_r), st, optional=nr),
         _tensor("c", c, (B, N, dims.d_c), st),
         _tensor("k_r", k_r, (B, N, dims.d_r), st, optional=nr),
-        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
         _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
@@ -375,7 +384,7 @@ def mtla_prefill_backward(dims: MtlaDims, q_c, q_r, c, k_r, w_hyp, pe, w_uk, w_u
         _tensor("grad_q_r", grad_q_r, (B, N, H, dims.d_r), st, optional=nr),
         _tensor("grad_c", grad_c, (B, N, dims.d_c), st),
         _tensor("grad_k_r", grad_k_r, (B, N, dims.d_r), st, optional=nr),
-        _tensor("grad_w_hyp", grad_w_hyp, (dims.d_c,), torch.float32),
+        _tensor("grad_w_hyp", grad_w_hyp, dims.gate_shape, torch.float32),
         _tensor("grad_w_uk", grad_w_uk, (H, dims.d_h, dims.d_c), torch.float32),
         _tensor("grad_w_uv", grad_w_uv, (H, dims.d_h, dims.d_c), torch.float32),
         ws, ws_bytes, _stream(stream)))
@@ -398,7 +407,7 @@ def mtla_prefill_at(dims: MtlaDims, t0: int, q_c, q_r, c, k_r, w_hyp, pe, w_uk, 
         _tensor("q_r", q_r, (B, N, H, dims.d_r), st, optional=dims.d_r == 0),
         _tensor("c", c, (B, N, dims.d_c), st),
         _tensor("k_r", k_r, (B, N, dims.d_r), st, optional=dims.d_r == 0),
-        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
         _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
@@ -475,7 +484,7 @@ def mtla_layer_decode_step(dims: MtlaDims, pos, h, w_dkv, w_q, w_r, w_o, w_hyp, 
         ctypes.byref(dims), dm,
         _tensor("pos", pos, (B,), torch.int32),
         _tensor("h", h, (B, dm), st), wd, wq, wr, wo,
-        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
         _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
@@ -500,7 +509,7 @@ def mtla_layer_prefill(dims: MtlaDims, t0: int, h, w_dkv, w_q, w_r, w_o, w_hyp, 
     _check(_lib.mtla_layer_prefill(
         ctypes.byref(dims), dm, int(t0), N,
         _tensor("h", h, (B, N, dm), st), wd, wq, wr, wo,
-        _tensor("w_hyp", w_hyp, (dims.d_c,), torch.float32),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
         _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void bwd_partials_kernel(BwdArgs a) {
   for (int t = t0; t < t1; ++t) {
     const size_t row = static_cast<size_t>(b) * a.N + t;
     const float w = gate_of_token<T>(static_cast<const T*>(a.c) + row * a.d_c, a.pe + static_cast<size_t>(t) * a.d_c,
-                                     a.w_hyp, a.d_c, lane);
+                                     a.w_hyp + static_cast<size_t>(t % a.s) * a.wh_stride, a.d_c, lane);
     if (lane == 0) a.gate[row] = w;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -297,11 +297,12 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
       }
       const float du = wave_sum(dwl) * w[u] * (1.f - w[u]);
       if (lane == 0) a.du[row] = du;
+      const float* whr = a.w_hyp + static_cast<size_t>(t % a.s) * a.wh_stride;
 #pragma unroll
       for (int j = 0; j < JW; ++j) {
         const int e = lane + 64 * j;
         if (e < a.d_c)
-          st<T>(a.g_c, row * a.d_c + e, fmaf(du, a.w_hyp[e], w[u] * G[j]));
+          st<T>(a.g_c, row * a.d_c + e, fmaf(du, whr[e], w[u] * G[j]));
         else if (e < W)
           st<T>(a.g_k_r, row * a.d_r + (e - a.d_c), w[u] * G[j]);
       }
@@ -311,6 +312,8 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
 
 // Partial sums of dW_hyp = sum_r du_r (c_r + pe_t(r)) over one chunk of rows:
 // 64 columns x 4 row groups per workgroup, the groups added in a fixed order.
+// With one W_hyp row per place in the block (wh_rows = s), blockIdx.z is the
+// place and takes the tokens t with t mod s == blockIdx.z.
 template <typename T>
 __global__ __launch_bounds__(256) void dwhyp_kernel(BwdArgs a, int rows_per_split) {
   __shared__ float red[4][64];
@@ -318,15 +321,20 @@ __global__ __launch_bounds__(256) void dwhyp_kernel(BwdArgs a, int rows_per_spli
   const int col = blockIdx.x * 64 + cl;
   const int R = a.B * a.N;
   const int r0 = blockIdx.y * rows_per_split, r1 = min(R, r0 + rows_per_split);
+  const int place = blockIdx.z;
   float acc = 0.f;
   if (col < a.d_c)
-    for (int r = r0 + rg; r < r1; r += 4)
-      acc = fmaf(a.du[r], ld<T>(a.c, static_cast<size_t>(r) * a.d_c + col) + a.pe[static_cast<size_t>(r % a.N) * a.d_c + col],
+    for (int r = r0 + rg; r < r1; r += 4) {
+      const int t = r % a.N;
+      if (a.wh_rows > 1 && t % a.s != place) continue;
+      acc = fmaf(a.du[r], ld<T>(a.c, static_cast<size_t>(r) * a.d_c + col) + a.pe[static_cast<size_t>(t) * a.d_c + col],
                  acc);
+    }
   red[rg][cl] = acc;
   __syncthreads();
   if (rg == 0 && col < a.d_c)
-    a.wh_part[static_cast<size_t>(blockIdx.y) * a.d_c + col] = (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]);
+    a.wh_part[(static_cast<size_t>(blockIdx.y) * a.wh_rows + place) * a.d_c + col] =
+        (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]);
 }
 
 template <typename T>
@@ -1182,14 +1190,14 @@ hipError_t launch_bwd_scan(const BwdArgs& a, int dtype, hipStream_t st) {
 hipError_t launch_bwd_dwhyp(const BwdArgs& a, float* out, int dtype, hipStream_t st) {
   const int R = a.B * a.N;
   const int rows_per_split = (R + a.wh_parts - 1) / a.wh_parts;
-  const dim3 grid((a.d_c + 63) / 64, a.wh_parts);
+  const dim3 grid((a.d_c + 63) / 64, a.wh_parts, a.wh_rows);
   if (dtype == 0)
     dwhyp_kernel<float><<<grid, 256, 0, st>>>(a, rows_per_split);
   else
     dwhyp_kernel<uint16_t><<<grid, 256, 0, st>>>(a, rows_per_split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_sum_parts(a.wh_part, a.wh_parts, a.d_c, out, st);
+  return launch_sum_parts(a.wh_part, a.wh_parts, a.wh_rows * a.d_c, out, st);
 }
 
 hipError_t launch_bwd_transpose_w(int KV2h, int d_c, const void* w_uk, const void* w_uv, void* wt, int dtype,

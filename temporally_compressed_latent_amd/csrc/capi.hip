@@ -39,6 +39,11 @@ constexpr int kMaxWidth = 1024;
 constexpr int kMaxDh = 256;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
+// Element stride between W_hyp rows: 0 when every token takes the one row,
+// d_c when W_hyp has one row per place in the block.
+int gate_stride(const mtla_dims* d) { return (d->flags & MTLA_FLAG_GATE_PER_POSITION) ? d->d_c : 0; }
+int gate_rows(const mtla_dims* d) { return (d->flags & MTLA_FLAG_GATE_PER_POSITION) ? d->stride_s : 1; }
+
 int32_t check_dims(const mtla_dims* d) {
   if (!d) return fail(MTLA_ERR_INVALID_ARG, "dims is NULL");
   if (d->batch < 0) return fail(MTLA_ERR_INVALID_ARG, "batch=%d < 0", d->batch);
@@ -52,7 +57,8 @@ int32_t check_dims(const mtla_dims* d) {
     return fail(MTLA_ERR_INVALID_ARG, "dtype=%d is neither MTLA_FP32 nor MTLA_BF16", d->dtype);
   if (!(isfinite(d->softmax_scale) && d->softmax_scale > 0.f))
     return fail(MTLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
-  if (d->flags & ~MTLA_FLAG_PORTABLE) return fail(MTLA_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
+  if (d->flags & ~(MTLA_FLAG_PORTABLE | MTLA_FLAG_GATE_PER_POSITION))
+    return fail(MTLA_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
   if (d->stride_s > kMaxS) return fail(MTLA_ERR_UNSUPPORTED, "stride_s=%d > %d", d->stride_s, kMaxS);
   if (d->d_c + d->d_r > kMaxWidth)
     return fail(MTLA_ERR_UNSUPPORTED, "d_c + d_r = %d > %d", d->d_c + d->d_r, kMaxWidth);
@@ -270,6 +276,7 @@ int32_t mtla_merge_append(const mtla_dims* dims, const int32_t* pos0, int32_t n_
   CHECK_OPT_PTR_ALIGN(gate_out, 4);
   mtla::MergeArgs a{dims->batch, n_tokens, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots,
                     pe_rows, pos0, c, k_r, w_hyp, pe, cache, open_acc, gate_out, nullptr};
+  a.wh_stride = gate_stride(dims);
   return hip_status(mtla::launch_merge(a, dims->dtype, static_cast<hipStream_t>(stream)),
                     "merge launch");
 }
@@ -491,15 +498,24 @@ static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const
     return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, ws.total);
   if (check_only) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (decode_fused(dims)) {
+  // the fused step kernels merge with the one-row gate; with one W_hyp row
+  // per place in the block the merge runs first, on its own
+  const bool per_place = gate_stride(dims) != 0;
+  if (decode_fused(dims) && !per_place) {
     const mtla::StepArgs a = step_args(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv,
                                        cache, open_acc, out, 1);
     return hip_status(mtla::launch_decode_step(a, s), "decode step launch");
   }
   mtla::MergeArgs m{dims->batch, 1, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, pe_rows,
                     pos, c, k_r, w_hyp, pe, cache, open_acc, nullptr, nullptr};
+  m.wh_stride = gate_stride(dims);
   hipError_t e = mtla::launch_merge(m, dims->dtype, s);
   if (e != hipSuccess) return hip_status(e, "merge launch");
+  if (decode_fused(dims)) {
+    const mtla::StepArgs a = step_args(dims, pos, nullptr, nullptr, nullptr, nullptr, 0, q_c, q_r, w_uk, w_uv,
+                                       cache, nullptr, out, 0);
+    return hip_status(mtla::launch_decode_step(a, s), "decode step launch");
+  }
   return hip_status(run_decode_pipeline(dims, pos, q_c, q_r, w_uk, w_uv, cache, out, workspace, ws, s),
                     "decode launch");
 }
@@ -564,6 +580,7 @@ static int32_t prefill_impl(const mtla_dims* dims, int32_t t0, int32_t n_tokens,
   void* P = at(workspace, ws.P);
   mtla::MergeArgs m{B, N, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, pe_rows,
                     nullptr, c, k_r, w_hyp, pe, cache, open_acc, nullptr, P, t0 + 1};
+  m.wh_stride = gate_stride(dims);
   hipError_t e = mtla::launch_merge(m, dims->dtype, s);
   if (e != hipSuccess) return hip_status(e, "prefill merge launch");
   if (prefill_fast(dims)) {
@@ -915,7 +932,7 @@ BwdWs bwd_ws(const mtla_dims* d, int n) {
   w.du = take(R * 4);
   // dW_hyp: partial sums over chunks of ~256 rows
   w.wh_parts = static_cast<int>(std::max<size_t>(1, std::min<size_t>((R + 255) / 256, 4096)));
-  w.wh_part = take(size_t(w.wh_parts) * d->d_c * 4);
+  w.wh_part = take(size_t(w.wh_parts) * gate_rows(d) * d->d_c * 4);
   w.total = off;
   return w;
 }
@@ -992,7 +1009,7 @@ int32_t mtla_prefill_backward(const mtla_dims* dims, int32_t n_tokens, const voi
   hipError_t e;
   if (empty) {
     // the gradients of the weights are sums over no tokens
-    if ((e = mtla::launch_sum_parts(nullptr, 0, dc, grad_w_hyp, s)) != hipSuccess)
+    if ((e = mtla::launch_sum_parts(nullptr, 0, gate_rows(dims) * dc, grad_w_hyp, s)) != hipSuccess)
       return hip_status(e, "backward zero-fill launch");
     if ((e = mtla::launch_sum_parts(nullptr, 0, H * d_h * dc, grad_w_uk, s)) != hipSuccess)
       return hip_status(e, "backward zero-fill launch");
@@ -1029,6 +1046,8 @@ int32_t mtla_prefill_backward(const mtla_dims* dims, int32_t n_tokens, const voi
   a.du = reinterpret_cast<float*>(at(workspace, ws.du));
   a.wh_part = reinterpret_cast<float*>(at(workspace, ws.wh_part));
   a.wh_parts = ws.wh_parts;
+  a.wh_stride = gate_stride(dims);
+  a.wh_rows = gate_rows(dims);
   const int ldk = KV2 + H * dr;
   // forward recomputation: gates and partial merges, then K^C and V of every token
   if ((e = mtla::launch_bwd_partials(a, dims->dtype, s)) != hipSuccess)

@@ -205,19 +205,20 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 // that gates a token uses this arithmetic, so a token gets bit-identical
 // gates whichever entry point merges it.  Tokens with c_rows[k] == nullptr
 // are skipped (their gate is 0).
+// wh_rows[k] is the W_hyp row token k takes (the same row for every token
+// unless W_hyp has one row per place in the block).
 template <int NTOK, typename T>
 __device__ __forceinline__ void gates_of_tokens(const T* const (&c_rows)[NTOK],
                                                 const float* const (&pe_rows)[NTOK],
-                                                const float* w_hyp, int d_c, int lane,
+                                                const float* const (&wh_rows)[NTOK], int d_c, int lane,
                                                 float (&w)[NTOK]) {
   float acc[NTOK];
 #pragma unroll
   for (int k = 0; k < NTOK; ++k) acc[k] = 0.f;
   for (int e = lane; e < d_c; e += 64) {
-    const float wh = w_hyp[e];
 #pragma unroll
     for (int k = 0; k < NTOK; ++k)
-      if (c_rows[k]) acc[k] = fmaf(Store<T>::load(c_rows[k], e) + pe_rows[k][e], wh, acc[k]);
+      if (c_rows[k]) acc[k] = fmaf(Store<T>::load(c_rows[k], e) + pe_rows[k][e], wh_rows[k][e], acc[k]);
   }
 #pragma unroll
   for (int k = 0; k < NTOK; ++k) {
@@ -244,8 +245,9 @@ __device__ __forceinline__ float gate_of_token(const T* c_row, const float* pe_r
                                                const float* w_hyp, int d_c, int lane) {
   const T* const rows[1] = {c_row};
   const float* const pes[1] = {pe_row};
+  const float* const whs[1] = {w_hyp};
   float w[1];
-  gates_of_tokens<1, T>(rows, pes, w_hyp, d_c, lane, w);
+  gates_of_tokens<1, T>(rows, pes, whs, d_c, lane, w);
   return w[0];
 }
 

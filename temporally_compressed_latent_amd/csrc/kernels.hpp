@@ -12,13 +12,14 @@ struct MergeArgs {
   const int32_t* pos0;  // [B] or nullptr (= 1 for every sequence)
   const void* c;        // [B, T, d_c]
   const void* k_r;      // [B, T, d_r]
-  const float* w_hyp;   // [d_c]
+  const float* w_hyp;   // [d_c], or [s, d_c] (wh_stride = d_c)
   const float* pe;      // [pe_rows, d_c]
   void* cache;          // [B, max_slots, W]
   float* open_acc;      // [B, 2, W]: state after token t at [b, t % 2]
   float* gate_out;      // [B, T] or nullptr
   void* partials;       // [B, T, W] cumulative in-block merges, or nullptr
   int p0_all = 1;       // first appended token of every sequence when pos0 is nullptr
+  int wh_stride = 0;    // token t takes W_hyp row (t - 1) mod s at w_hyp + row * wh_stride
 };
 
 // Gate + temporal merge.  dtype: 0 fp32, 1 bf16.
@@ -79,7 +80,7 @@ struct BwdArgs {
   const void* q_r;    // [B, N, H, d_r]
   const void* c;      // [R, d_c]
   const void* k_r;    // [R, d_r]
-  const float* w_hyp; // [d_c]
+  const float* w_hyp; // [d_c], or [s, d_c] (wh_stride = d_c): token t (0-based) takes row t mod s
   const float* pe;    // [>= N, d_c], row t for token t
   const void* d_o;    // [B, N, H, d_h]
   void* P;            // [R, d_c + d_r] partial merges (written by the partials kernel)
@@ -94,8 +95,10 @@ struct BwdArgs {
   void* g_c;
   void* g_k_r;
   float* du;          // [R] gradient of each token's gate pre-activation u = W_hyp . (c + pe)
-  float* wh_part;     // [wh_parts, d_c] fp32 partial sums of dW_hyp over row chunks
+  float* wh_part;     // [wh_parts, wh_rows, d_c] fp32 partial sums of dW_hyp over row chunks
   int wh_parts;
+  int wh_stride;      // 0 (one W_hyp row) or d_c (one row per place in the block)
+  int wh_rows;        // W_hyp rows: 1, or s
   // MFMA path (bf16, d_h = 64, d_r = 32): K^C and V in the forward's layout,
   // and lse in the log2 domain (scores scaled by tau log2 e)
   const void* kc;     // [B, H, N, d_h] K^C of every token

@@ -51,15 +51,17 @@ __device__ void compute_gates(const MergeArgs& a, int b, int p0, int ta, int nto
   for (int k0 = wave * kGateTok; k0 < ntok; k0 += nwaves * kGateTok) {
     const T* rows[kGateTok];
     const float* pes[kGateTok];
+    const float* whs[kGateTok];
 #pragma unroll
     for (int k = 0; k < kGateTok; ++k) {
       const int t = ta + k0 + k;
       const bool in = k0 + k < ntok;
       rows[k] = in ? c + (static_cast<size_t>(b) * a.T + (t - p0)) * a.d_c : nullptr;
       pes[k] = in ? a.pe + static_cast<size_t>(t - 1) * a.d_c : a.pe;
+      whs[k] = in ? a.w_hyp + static_cast<size_t>((t - 1) % a.s) * a.wh_stride : a.w_hyp;
     }
     float w[kGateTok];
-    gates_of_tokens<kGateTok, T>(rows, pes, a.w_hyp, a.d_c, lane, w);
+    gates_of_tokens<kGateTok, T>(rows, pes, whs, a.d_c, lane, w);
     if (lane == 0) {
 #pragma unroll
       for (int k = 0; k < kGateTok; ++k) {
@@ -77,16 +79,19 @@ __device__ void compute_gates(const MergeArgs& a, int b, int p0, int ta, int nto
 // lane l holds elements l + 64 j of c_t, pe_t and W_hyp, and the sum runs in
 // the order of gate_from_lane_values (the same bits as gates_of_tokens and
 // the decode-step kernels).  Token indices past the last are clamped (their
-// gates are computed and dropped), so the loads are unconditional.
-template <typename T, int GE, int NTOK>
+// gates are computed and dropped), so the loads are unconditional.  PP: one
+// W_hyp row per place in the block, loaded with each token.
+template <typename T, int GE, int NTOK, bool PP>
 __device__ void compute_gates_lanes(const MergeArgs& a, int b, int p0, int ta, int ntok, float* gw) {
   const T* c = static_cast<const T*>(a.c);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
-  float wh[GE];
+  float wh[PP ? NTOK : 1][GE];
+  if constexpr (!PP) {
 #pragma unroll
-  for (int j = 0; j < GE; ++j) wh[j] = a.w_hyp[lane + 64 * j];
+    for (int j = 0; j < GE; ++j) wh[0][j] = a.w_hyp[lane + 64 * j];
+  }
   for (int k0 = wave; k0 < ntok; k0 += nwaves * NTOK) {
     float x[NTOK][GE], pv[NTOK][GE];
 #pragma unroll
@@ -94,15 +99,17 @@ __device__ void compute_gates_lanes(const MergeArgs& a, int b, int p0, int ta, i
       const int t = ta + min(k0 + k * nwaves, ntok - 1);
       const T* row = c + (static_cast<size_t>(b) * a.T + (t - p0)) * a.d_c;
       const float* per = a.pe + static_cast<size_t>(t - 1) * a.d_c;
+      const float* whr = a.w_hyp + static_cast<size_t>((t - 1) % a.s) * a.wh_stride;
 #pragma unroll
       for (int j = 0; j < GE; ++j) {
         x[k][j] = Store<T>::load(row, lane + 64 * j);
         pv[k][j] = per[lane + 64 * j];
+        if constexpr (PP) wh[k][j] = whr[lane + 64 * j];
       }
     }
 #pragma unroll
     for (int k = 0; k < NTOK; ++k) {
-      const float w = gate_from_lane_values<GE>(x[k], pv[k], wh);
+      const float w = gate_from_lane_values<GE>(x[k], pv[k], wh[PP ? k : 0]);
       const int kk = k0 + k * nwaves;
       if (lane == 0 && kk < ntok) {
         gw[kk] = w;
@@ -114,10 +121,14 @@ __device__ void compute_gates_lanes(const MergeArgs& a, int b, int p0, int ta, i
 
 template <typename T>
 __device__ void merge_gates(const MergeArgs& a, int b, int p0, int ta, int ntok, float* gw) {
-  if (a.d_c == 256)
-    compute_gates_lanes<T, 4, 8>(a, b, p0, ta, ntok, gw);
+  if (a.d_c == 256 && a.wh_stride == 0)
+    compute_gates_lanes<T, 4, 8, false>(a, b, p0, ta, ntok, gw);
+  else if (a.d_c == 256)
+    compute_gates_lanes<T, 4, 8, true>(a, b, p0, ta, ntok, gw);
+  else if (a.d_c == 512 && a.wh_stride == 0)
+    compute_gates_lanes<T, 8, 4, false>(a, b, p0, ta, ntok, gw);
   else if (a.d_c == 512)
-    compute_gates_lanes<T, 8, 4>(a, b, p0, ta, ntok, gw);
+    compute_gates_lanes<T, 8, 4, true>(a, b, p0, ta, ntok, gw);
   else
     compute_gates<T>(a, b, p0, ta, ntok, gw);
 }

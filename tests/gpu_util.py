@@ -122,12 +122,14 @@ SHAPES = {
 
 
 def make_case(shape: str, seed: int, B: int, N: int, s: int, dtype: str, portable: bool = False,
-              max_slots=None, **kw):
+              max_slots=None, gate_per_position: bool = False, **kw):
     import workloads
     H, d_h, d_c, d_r = SHAPES[shape]
-    inp = workloads.boundary_case(seed, B, N, H, d_h, d_c, d_r, dtype, **kw)
+    inp = workloads.boundary_case(seed, B, N, H, d_h, d_c, d_r, dtype,
+                                  gate_rows=s if gate_per_position else 0, **kw)
     ms = max_slots or (-(-N // s) + 2)
-    dims = m.make_dims(B, H, d_h, d_c, d_r, s, ms, dtype, portable=portable)
+    dims = m.make_dims(B, H, d_h, d_c, d_r, s, ms, dtype, portable=portable,
+                       gate_per_position=gate_per_position)
     return inp, Case(dims, inp, N + 4)
 
 

@@ -304,3 +304,23 @@ def test_backward_argument_checks():
     assert bwd(ws=None) == m.MTLA_ERR_WORKSPACE
     assert bwd(ws=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
     assert bwd(n=need - 16) == m.MTLA_ERR_WORKSPACE
+
+
+def test_per_position_gate_flag():
+    """MTLA_FLAG_GATE_PER_POSITION is a known flag (other unknown bits still
+    fail); the backward workspace grows by the extra dW_hyp rows; the binding
+    asks for W_hyp of shape [s, d_c] under it and [d_c] without."""
+    L = m.lib()
+    n1, n2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    plain = dims()
+    pp = dims(flags=m.MTLA_FLAG_GATE_PER_POSITION)
+    assert L.mtla_decode_workspace_bytes(ctypes.byref(pp), ctypes.byref(n1)) == m.MTLA_OK
+    assert L.mtla_decode_workspace_bytes(ctypes.byref(dims(flags=m.MTLA_FLAG_GATE_PER_POSITION | 4)),
+                                         ctypes.byref(n1)) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_prefill_backward_workspace_bytes(ctypes.byref(plain), 64, ctypes.byref(n1)) == m.MTLA_OK
+    assert L.mtla_prefill_backward_workspace_bytes(ctypes.byref(pp), 64, ctypes.byref(n2)) == m.MTLA_OK
+    assert n2.value >= n1.value
+    assert plain.gate_shape == (plain.d_c,)
+    assert pp.gate_shape == (pp.stride_s, pp.d_c)
+    mk = m.make_dims(2, 8, 64, 256, 32, 3, 10, "bf16", gate_per_position=True)
+    assert mk.flags == m.MTLA_FLAG_GATE_PER_POSITION and mk.gate_shape == (3, 256)

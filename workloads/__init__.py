@@ -207,12 +207,14 @@ def small(wid: int = 0, **kw) -> Workload:
 
 def boundary_case(seed: int, B: int, N: int, H: int, d_h: int, d_c: int, d_r: int,
                   dtype: str, w_hyp_zero: bool = False, q_zero: bool = False,
-                  q_rows: Optional[int] = None) -> dict:
+                  q_rows: Optional[int] = None, gate_rows: int = 0) -> dict:
     """Seeded Gaussian kernel-boundary inputs of arbitrary shape (test cases).
 
     Same distributions as the named workloads; ``w_hyp_zero`` and ``q_zero``
     give the closed-form special cases (every gate 1/2; uniform attention).
     ``q_rows`` limits the queries to that many token rows (default: N).
+    ``gate_rows`` > 0 draws W_hyp with that many rows (one per place in the
+    block), after every other tensor, so the others are the same draws.
     """
     Q = N if q_rows is None else q_rows
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([ROOT_SEED, 1000 + seed])))
@@ -227,6 +229,8 @@ def boundary_case(seed: int, B: int, N: int, H: int, d_h: int, d_c: int, d_r: in
         "w_uk": quantize(f(H, d_h, d_c) * std, dtype),
         "w_uv": quantize(f(H, d_h, d_c) * std, dtype),
     }
+    if gate_rows > 0:
+        case["w_hyp"] = f(gate_rows, d_c) * std
     if w_hyp_zero:
         case["w_hyp"] = np.zeros(d_c, np.float32)
     if q_zero:
