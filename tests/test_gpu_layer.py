@@ -13,10 +13,13 @@ from tests.gpu_util import DEV, host, tdev, tol
 pytestmark = pytest.mark.gpu
 
 
-def _setup(wid, **kw):
+def _setup(wid, gate_per_position=False, **kw):
     w = workloads.small(wid, **kw)
     p = workloads.layer_params(w)
-    d = m.make_dims(w.batch, w.heads, w.d_h, w.d_c, w.d_r, w.s, -(-w.n_tokens // w.s) + 1, w.dtype)
+    if gate_per_position:
+        p["w_hyp"] = workloads.gate_rows_weights(w)
+    d = m.make_dims(w.batch, w.heads, w.d_h, w.d_c, w.d_r, w.s, -(-w.n_tokens // w.s) + 1, w.dtype,
+                    gate_per_position=gate_per_position)
     st = d.torch_dtype
     dev = {k: tdev(v, torch.float32 if k == "w_hyp" else st) for k, v in p.items()}
     pe = torch.empty(w.n_tokens + 2, w.d_c, dtype=torch.float32, device=DEV)
@@ -128,10 +131,12 @@ def test_layer_decode_loop_matches_oracle(wid, kw):
         assert oracle.max_rel_err(got[b], _oracle_layer(w, p, b, "incremental")) <= tol(w.dtype), b
 
 
-def test_layer_prefill_in_chunks_then_decode():
+@pytest.mark.parametrize("gate_per_position", [False, True])
+def test_layer_prefill_in_chunks_then_decode(gate_per_position):
     """Layer prefill of tokens 1..40, then 41..70 as a chunk, then two decode
-    steps: every output follows the oracle's layer over tokens 1..72."""
-    w, p, d, dev, pe, cache, open_acc = _setup(1, batch=2, n_tokens=72, s=3)
+    steps: every output follows the oracle's layer over tokens 1..72; also
+    with one W_hyp row per place in the block."""
+    w, p, d, dev, pe, cache, open_acc = _setup(1, gate_per_position, batch=2, n_tokens=72, s=3)
     B, dm = w.batch, w.d_model
     outs = []
     for t0, n in ((0, 40), (40, 30)):

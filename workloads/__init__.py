@@ -31,6 +31,7 @@ ROOT_SEED = 20250513
 T_H, T_WDKV, T_WHYP, T_WUK, T_WUV, T_WQ, T_WR, T_WO = 0, 1, 2, 3, 4, 5, 6, 7
 T_C, T_KR, T_QC, T_QR = 10, 11, 12, 13
 T_DO = 14
+T_WHYP_ROWS = 15
 
 
 @dataclass(frozen=True)
@@ -166,6 +167,12 @@ def queries(w: Workload, b: int, n_tokens: Optional[int] = None) -> dict:
         "q_c": quantize(normal(w.wid, T_QC, (T, w.heads, w.d_h), b=b), w.dtype),
         "q_r": quantize(normal(w.wid, T_QR, (T, w.heads, w.d_r), b=b), w.dtype),
     }
+
+
+def gate_rows_weights(w: Workload) -> np.ndarray:
+    """W_hyp with one row per place in the block, [s, d_c] fp32 (the
+    per-position gate variant), from a stream of its own."""
+    return normal(w.wid, T_WHYP_ROWS, (w.s, w.d_c), 1.0 / np.sqrt(w.d_c))
 
 
 def batch_latents(w: Workload, n_tokens: Optional[int] = None, seqs=None) -> dict:
