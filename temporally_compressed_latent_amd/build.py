@@ -41,7 +41,10 @@ def hipcc() -> str:
 # Per-file additions.  prefill.hip: the attention's softmax takes maxima of
 # raw MFMA results; without NaN semantics (no input here is NaN) fmaxf needs
 # no canonicalising move per value and pairs into v_max3_f32.
-FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"],
+              # the decode-step kernels' leading scalar arguments go straight
+              # into scalar registers at launch
+              "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=3"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

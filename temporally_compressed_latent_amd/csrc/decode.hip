@@ -910,7 +910,8 @@ __host__ __device__ constexpr StepShape step_shape(int nth, int hg, int d_h, int
 // Instances: (d_c, d_R, tile slots, heads per group, largest d_h, threads,
 // cache tiles in flight, merge the token first).
 template <int DC, int DR, int TS, int HG, int DH, int NTH, int PD, bool MERGE>
-__global__ __launch_bounds__(NTH) void decode_step_kernel(StepArgs a) {
+__global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restrict__ kpos, int G, int nB,
+                                                          StepArgs a) {
   using A = MfmaAttn<1, DC, DR, NTH / 64, TS>;
   constexpr int W = A::W, HP = A::HP, PITCH = A::PITCH, CPW = A::CPW, CT = A::CT, NT = A::NT;
   constexpr int KC = DC / 8;
@@ -923,16 +924,15 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(StepArgs a) {
   __shared__ __align__(16) uint16_t s_new[W];
   // Workgroups are dealt to the 8 XCDs round-robin by linear id: id L runs on
   // XCD L % 8.  Sequence b goes to XCD b % 8 with all of its head groups.
-  const int G = a.groups;
   const int L = blockIdx.x, xcd = L & 7, k8 = L >> 3;
   const int grp = k8 % G, b = 8 * (k8 / G) + xcd;
-  if (b >= a.B) return;
+  if (b >= nB) return;
   const int H = a.H, d_h = a.d_h, h0 = grp * HG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const StepShape sh = step_shape(NTH, HG, d_h, DC);
 
-  const int pos = a.pos[b];
+  const int pos = kpos[b];
   // Every load below is issued unconditionally (indices clamped into the
   // tensors, unused values dropped at their use), so the compiler can count
   // the loads in flight and wait only for the ones each phase needs.
@@ -1113,8 +1113,13 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(StepArgs a) {
 // Heads occupy the MFMA's 16-wide N dimension; the rows past HG read q~
 // from a zero row.
 // ---------------------------------------------------------------------------
+// The first three arguments (positions, head groups, batch) come ahead of
+// the argument struct so that the build can preload them into scalar
+// registers: the position load, which everything waits for, then issues at
+// once instead of after a round trip to the kernel-argument segment.
 template <int DC, int DR, int HG, int DH, bool MERGE>
-__global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
+__global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __restrict__ kpos, int G, int nB,
+                                                              StepArgs a) {
   constexpr int NT = 512, NWV = 8;
   constexpr int W = DC + DR;
   constexpr int KSW = W / 32;                            // score k-steps
@@ -1155,15 +1160,14 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(StepArgs a) {
 
   // Workgroups are dealt to the 8 XCDs round-robin by linear id: id L runs on
   // XCD L % 8.  Sequence b goes to XCD b % 8 with all of its head groups.
-  const int G = a.groups;
   const int L = blockIdx.x, xcd = L & 7, k8 = L >> 3;
   const int grp = k8 % G, b = 8 * (k8 / G) + xcd;
-  if (b >= a.B) return;
+  if (b >= nB) return;
   const int H = a.H, d_h = a.d_h, h0 = grp * HG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
 
-  const int pos = a.pos[b];
+  const int pos = kpos[b];
   // Loads that do not depend on the position go out first, unconditionally
   // (indices clamped into the tensors, unused values dropped at their use).
   // absorb: thread (kc, hl, eg) takes columns kc*8 .. +7 of head hl and the
@@ -1705,16 +1709,16 @@ namespace {
 template <int DC, int DR, int TS, int HG, int DH, int NTH, int PD>
 void step_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
   if (a.merge)
-    decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, true><<<grid, NTH, 0, st>>>(a);
+    decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, true><<<grid, NTH, 0, st>>>(a.pos, a.groups, a.B, a);
   else
-    decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, false><<<grid, NTH, 0, st>>>(a);
+    decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, false><<<grid, NTH, 0, st>>>(a.pos, a.groups, a.B, a);
 }
 template <int DC, int DR, int HG, int DH>
 void step_wave_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
   if (a.merge)
-    decode_step_wave_kernel<DC, DR, HG, DH, true><<<grid, 512, 0, st>>>(a);
+    decode_step_wave_kernel<DC, DR, HG, DH, true><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a);
   else
-    decode_step_wave_kernel<DC, DR, HG, DH, false><<<grid, 512, 0, st>>>(a);
+    decode_step_wave_kernel<DC, DR, HG, DH, false><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a);
 }
 
 // Heads per group the step kernel is instantiated for, per latent shape.
