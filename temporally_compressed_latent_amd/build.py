@@ -44,7 +44,7 @@ def hipcc() -> str:
 FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"],
               # the decode-step kernels' leading scalar arguments go straight
               # into scalar registers at launch
-              "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=3"]}
+              "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

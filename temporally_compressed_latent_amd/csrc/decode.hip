@@ -910,7 +910,8 @@ __host__ __device__ constexpr StepShape step_shape(int nth, int hg, int d_h, int
 // Instances: (d_c, d_R, tile slots, heads per group, largest d_h, threads,
 // cache tiles in flight, merge the token first).
 template <int DC, int DR, int TS, int HG, int DH, int NTH, int PD, bool MERGE>
-__global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restrict__ kpos, int G, int nB,
+__global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restrict__ kpos, int G, int nB, int,
+                                                          int, const uint16_t*, const uint16_t*, const uint16_t*,
                                                           StepArgs a) {
   using A = MfmaAttn<1, DC, DR, NTH / 64, TS>;
   constexpr int W = A::W, HP = A::HP, PITCH = A::PITCH, CPW = A::CPW, CT = A::CT, NT = A::NT;
@@ -1113,13 +1114,17 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restr
 // Heads occupy the MFMA's 16-wide N dimension; the rows past HG read q~
 // from a zero row.
 // ---------------------------------------------------------------------------
-// The first three arguments (positions, head groups, batch) come ahead of
-// the argument struct so that the build can preload them into scalar
-// registers: the position load, which everything waits for, then issues at
-// once instead of after a round trip to the kernel-argument segment.
+// The leading scalar arguments (positions, head groups, batch, heads, d_h and
+// the W_UK, query and token pointers) come ahead of the argument struct so
+// that the build can preload them into scalar registers: the position load,
+// which everything waits for, and the first loads of W_UK, the queries and the
+// token then issue at once instead of after a round trip to the
+// kernel-argument segment.
 template <int DC, int DR, int HG, int DH, bool MERGE>
-__global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __restrict__ kpos, int G, int nB,
-                                                              StepArgs a) {
+__global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __restrict__ kpos, int G, int nB, int H,
+                                                              int d_h, const uint16_t* __restrict__ w_uk,
+                                                              const uint16_t* __restrict__ q_c,
+                                                              const uint16_t* __restrict__ c_tok, StepArgs a) {
   constexpr int NT = 512, NWV = 8;
   constexpr int W = DC + DR;
   constexpr int KSW = W / 32;                            // score k-steps
@@ -1163,7 +1168,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   const int L = blockIdx.x, xcd = L & 7, k8 = L >> 3;
   const int grp = k8 % G, b = 8 * (k8 / G) + xcd;
   if (b >= nB) return;
-  const int H = a.H, d_h = a.d_h, h0 = grp * HG;
+  const int h0 = grp * HG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
 
@@ -1174,10 +1179,10 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   // row pairs e = 2 (eg + j EGN) + {0, 1}
   const int kc = tid % KC, hl = (tid / KC) % HG, eg = tid / (KC * HG);
   const auto r_uk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.w_uk + static_cast<size_t>(h0) * d_h * DC), static_cast<short>(0), HG * d_h * DC * 2,
+      const_cast<uint16_t*>(w_uk + static_cast<size_t>(h0) * d_h * DC), static_cast<short>(0), HG * d_h * DC * 2,
       kBufferRsrcWord3);
   const auto r_q = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.q_c + (static_cast<size_t>(b) * H + h0) * d_h), static_cast<short>(0), HG * d_h * 2,
+      const_cast<uint16_t*>(q_c + (static_cast<size_t>(b) * H + h0) * d_h), static_cast<short>(0), HG * d_h * 2,
       kBufferRsrcWord3);
   uint4 wk0[NP], wk1[NP];
   uint32_t qp[NP];
@@ -1211,10 +1216,10 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   if constexpr (MERGE) {
 #pragma unroll
     for (int j = 0; j < GE; ++j) {
-      gxb[j] = a.c[static_cast<size_t>(b) * DC + lane + 64 * j];
+      gxb[j] = c_tok[static_cast<size_t>(b) * DC + lane + 64 * j];
       gw[j] = a.w_hyp[lane + 64 * j];
     }
-    mxb = te < DC ? a.c[static_cast<size_t>(b) * DC + te] : a.k_r[static_cast<size_t>(b) * DR + te - DC];
+    mxb = te < DC ? c_tok[static_cast<size_t>(b) * DC + te] : a.k_r[static_cast<size_t>(b) * DR + te - DC];
   }
 
   const int n = pos >= 1 ? slot_of(pos, a.s) : 0;
@@ -1709,16 +1714,16 @@ namespace {
 template <int DC, int DR, int TS, int HG, int DH, int NTH, int PD>
 void step_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
   if (a.merge)
-    decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, true><<<grid, NTH, 0, st>>>(a.pos, a.groups, a.B, a);
+    decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, true><<<grid, NTH, 0, st>>>(a.pos, a.groups, a.B, a.H, a.d_h, a.w_uk, a.q_c, a.c, a);
   else
-    decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, false><<<grid, NTH, 0, st>>>(a.pos, a.groups, a.B, a);
+    decode_step_kernel<DC, DR, TS, HG, DH, NTH, PD, false><<<grid, NTH, 0, st>>>(a.pos, a.groups, a.B, a.H, a.d_h, a.w_uk, a.q_c, a.c, a);
 }
 template <int DC, int DR, int HG, int DH>
 void step_wave_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
   if (a.merge)
-    decode_step_wave_kernel<DC, DR, HG, DH, true><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a);
+    decode_step_wave_kernel<DC, DR, HG, DH, true><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a.H, a.d_h, a.w_uk, a.q_c, a.c, a);
   else
-    decode_step_wave_kernel<DC, DR, HG, DH, false><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a);
+    decode_step_wave_kernel<DC, DR, HG, DH, false><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a.H, a.d_h, a.w_uk, a.q_c, a.c, a);
 }
 
 // Heads per group the step kernel is instantiated for, per latent shape.
