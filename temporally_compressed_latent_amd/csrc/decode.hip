@@ -1165,8 +1165,18 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
 
   // Workgroups are dealt to the 8 XCDs round-robin by linear id: id L runs on
   // XCD L % 8.  Sequence b goes to XCD b % 8 with all of its head groups.
+  // (shifts when the group count is a power of two: the division would sit
+  // ahead of the first loads)
   const int L = blockIdx.x, xcd = L & 7, k8 = L >> 3;
-  const int grp = k8 % G, b = 8 * (k8 / G) + xcd;
+  int grp, kq;
+  if ((G & (G - 1)) == 0) {
+    grp = k8 & (G - 1);
+    kq = k8 >> __builtin_ctz(G);
+  } else {
+    grp = k8 % G;
+    kq = k8 / G;
+  }
+  const int b = 8 * kq + xcd;
   if (b >= nB) return;
   const int h0 = grp * HG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1222,7 +1232,18 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
     mxb = te < DC ? c_tok[static_cast<size_t>(b) * DC + te] : a.k_r[static_cast<size_t>(b) * DR + te - DC];
   }
 
-  const int n = pos >= 1 ? slot_of(pos, a.s) : 0;
+  // slot and place in the block of the position (shifts when s is a power of
+  // two: this sits between the position load and the cache-row loads)
+  const int sblk = a.s;
+  int n, place;
+  if ((sblk & (sblk - 1)) == 0) {
+    n = (pos + sblk - 1) >> __builtin_ctz(sblk);
+    place = (pos - 1) & (sblk - 1);
+  } else {
+    n = slot_of(pos, sblk);
+    place = (pos - 1) % sblk;
+  }
+  if (pos < 1) n = 0;
   const bool ok = pos >= 1 && n <= a.max_slots && (!MERGE || pos <= a.pe_rows);
   uint16_t* out = a.out + (static_cast<size_t>(b) * H + h0) * d_h;
   if (!ok) {
@@ -1234,7 +1255,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   // slots 0..n-2 when merging (row n-1 is the new one, taken from LDS), else
   // 0..n-1.
   float gp[GE], macc = 0.f;
-  const bool cont = (pos - 1) % a.s != 0;  // the token continues an open block
+  const bool cont = place != 0;  // the token continues an open block
   if constexpr (MERGE) {
 #pragma unroll
     for (int j = 0; j < GE; ++j) gp[j] = a.pe[static_cast<size_t>(pos - 1) * DC + lane + 64 * j];
