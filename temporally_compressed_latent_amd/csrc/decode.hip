@@ -1183,6 +1183,9 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   const int g = lane >> 4, c16 = lane & 15;
 
   const int pos = kpos[b];
+  // (the position load goes out before anything else: the scheduler would
+  // otherwise place it after the loads below)
+  __builtin_amdgcn_sched_barrier(0);
   // Loads that do not depend on the position go out first, unconditionally
   // (indices clamped into the tensors, unused values dropped at their use).
   // absorb: thread (kc, hl, eg) takes columns kc*8 .. +7 of head hl and the
