@@ -35,6 +35,11 @@ struct LayerSmem {
   T w[2][LBN * LP];
 };
 
+// Quotient and remainder by a positive divisor, by shifts when it is a power
+// of two (these run ahead of the first loads of the small-M product).
+__device__ __forceinline__ int div_rows(int x, int d) { return (d & (d - 1)) == 0 ? x >> __builtin_ctz(d) : x / d; }
+__device__ __forceinline__ int mod_rows(int x, int d) { return (d & (d - 1)) == 0 ? x & (d - 1) : x % d; }
+
 // Weight row n of the virtual [N, K] matrix [w0 ; w1 ; w2].  For the input
 // projection (mode 1) the rows of w1 = W_Q are taken grouped by kind: first
 // the q^C rows of every head, then the q^R rows of every head, so that a
@@ -47,7 +52,8 @@ __device__ __forceinline__ const T* weight_row(const LayerGemmArgs& g, int n) {
   if (n < g.n1) {
     if (g.mode != 0) {
       const int QW = g.d_h + g.d_r, HC = g.H * g.d_h;
-      n = n < HC ? (n / g.d_h) * QW + n % g.d_h : ((n - HC) / g.d_r) * QW + g.d_h + (n - HC) % g.d_r;
+      n = n < HC ? div_rows(n, g.d_h) * QW + mod_rows(n, g.d_h)
+                 : div_rows(n - HC, g.d_r) * QW + g.d_h + mod_rows(n - HC, g.d_r);
     }
     return static_cast<const T*>(g.w1) + static_cast<size_t>(n) * g.K;
   }
@@ -125,7 +131,7 @@ __device__ __forceinline__ void rope_rotate_rev(int pos, double theta, float& x0
 
 // 0-based position of the token in GEMM row m (sequence m / T, token m % T).
 __device__ __forceinline__ int row_position(const LayerGemmArgs& g, int m) {
-  const int b = m / g.T, t = m % g.T;
+  const int b = div_rows(m, g.T), t = mod_rows(m, g.T);
   return (g.pos0 ? g.pos0[b] : g.p0_all) + t - 1;
 }
 
