@@ -44,7 +44,8 @@ def hipcc() -> str:
 FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"],
               # the decode-step kernels' leading scalar arguments go straight
               # into scalar registers at launch
-              "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"]}
+              "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"],
+              "layer.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=7"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -474,12 +474,17 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
 // columns.
 constexpr int SKN = 16;
 
+// The leading scalar arguments (A, the first weight matrix, M, N, K, that
+// matrix's row count and A's row stride) repeat fields of g ahead of it so
+// that the build can preload them into scalar registers: the first operand
+// loads then issue without a round trip to the kernel-argument segment.
 template <int NB>
-__global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(LayerGemmArgs g) {
+__global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(const uint16_t* __restrict__ A0,
+                                                                const uint16_t* __restrict__ W0, int M, int N,
+                                                                int K, int n0_rows, int lda0, LayerGemmArgs g) {
   __shared__ float sP[4][16 * NB * (SKN + 1)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, c16 = lane & 15;
-  const int M = g.M, N = g.N, K = g.K;
   const int n0 = blockIdx.x * SKN;
   // epilogue item of this thread: column pair pc on rows er[0], er[1]; their
   // token positions are loaded first, so that they arrive with the operands
@@ -491,12 +496,14 @@ __global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(LayerGemmArgs g)
     er[j] = tid / (SKN / 2) + 32 * j;
     epos[j] = g.mode != 0 ? row_position(g, min(er[j], M - 1)) : 0;
   }
-  const uint16_t* wr = weight_row<uint16_t>(g, min(n0 + c16, N - 1)) + 8 * g16;
+  // (a tile wholly inside the first weight matrix takes its rows from the
+  // preloaded pointer)
+  const int nw = min(n0 + c16, N - 1);
+  const uint16_t* wr = (n0 + SKN <= n0_rows ? W0 + static_cast<size_t>(nw) * K : weight_row<uint16_t>(g, nw)) + 8 * g16;
   const uint16_t* ar[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    ar[i] = static_cast<const uint16_t*>(g.A) + static_cast<size_t>(min(16 * i + c16, M - 1)) * (g.lda ? g.lda : K) +
-            8 * g16;
+    ar[i] = A0 + static_cast<size_t>(min(16 * i + c16, M - 1)) * (lda0 ? lda0 : K) + 8 * g16;
   f32x4 acc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -556,11 +563,13 @@ hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st) 
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (dtype != 0 && g.M <= 64) {
     const dim3 sgrid((g.N + SKN - 1) / SKN);
+    const uint16_t* A0 = static_cast<const uint16_t*>(g.A);
+    const uint16_t* W0 = static_cast<const uint16_t*>(g.w0);
     switch ((g.M + 15) / 16) {
-      case 1: layer_gemm_skinny_kernel<1><<<sgrid, 256, 0, st>>>(g); break;
-      case 2: layer_gemm_skinny_kernel<2><<<sgrid, 256, 0, st>>>(g); break;
-      case 3: layer_gemm_skinny_kernel<3><<<sgrid, 256, 0, st>>>(g); break;
-      default: layer_gemm_skinny_kernel<4><<<sgrid, 256, 0, st>>>(g); break;
+      case 1: layer_gemm_skinny_kernel<1><<<sgrid, 256, 0, st>>>(A0, W0, g.M, g.N, g.K, g.n0, g.lda, g); break;
+      case 2: layer_gemm_skinny_kernel<2><<<sgrid, 256, 0, st>>>(A0, W0, g.M, g.N, g.K, g.n0, g.lda, g); break;
+      case 3: layer_gemm_skinny_kernel<3><<<sgrid, 256, 0, st>>>(A0, W0, g.M, g.N, g.K, g.n0, g.lda, g); break;
+      default: layer_gemm_skinny_kernel<4><<<sgrid, 256, 0, st>>>(A0, W0, g.M, g.N, g.K, g.n0, g.lda, g); break;
     }
     return hipGetLastError();
   }
