@@ -498,12 +498,13 @@ static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const
     return fail(MTLA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, ws.total);
   if (check_only) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // the fused step kernels merge with the one-row gate; with one W_hyp row
-  // per place in the block the merge runs first, on its own
+  // the fused step kernels merge with one W_hyp row per place in the block
+  // only for 256-wide latents; otherwise that merge runs first, on its own
   const bool per_place = gate_stride(dims) != 0;
-  if (decode_fused(dims) && !per_place) {
-    const mtla::StepArgs a = step_args(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv,
-                                       cache, open_acc, out, 1);
+  if (decode_fused(dims) && (!per_place || dims->d_c == 256)) {
+    mtla::StepArgs a = step_args(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv,
+                                 cache, open_acc, out, 1);
+    a.wh_stride = gate_stride(dims);
     return hip_status(mtla::launch_decode_step(a, s), "decode step launch");
   }
   mtla::MergeArgs m{dims->batch, 1, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, pe_rows,

@@ -1120,7 +1120,7 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restr
 // which everything waits for, and the first loads of W_UK, the queries and the
 // token then issue at once instead of after a round trip to the
 // kernel-argument segment.
-template <int DC, int DR, int HG, int DH, bool MERGE>
+template <int DC, int DR, int HG, int DH, bool MERGE, bool PP = false>
 __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __restrict__ kpos, int G, int nB, int H,
                                                               int d_h, const uint16_t* __restrict__ w_uk,
                                                               const uint16_t* __restrict__ q_c,
@@ -1230,7 +1230,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
 #pragma unroll
     for (int j = 0; j < GE; ++j) {
       gxb[j] = c_tok[static_cast<size_t>(b) * DC + lane + 64 * j];
-      gw[j] = a.w_hyp[lane + 64 * j];
+      if constexpr (!PP) gw[j] = a.w_hyp[lane + 64 * j];  // (PP: the row is known with the position)
     }
     mxb = te < DC ? c_tok[static_cast<size_t>(b) * DC + te] : a.k_r[static_cast<size_t>(b) * DR + te - DC];
   }
@@ -1259,6 +1259,11 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   // 0..n-1.
   float gp[GE], macc = 0.f;
   const bool cont = place != 0;  // the token continues an open block
+  if constexpr (MERGE && PP) {
+    // one W_hyp row per place in the block
+#pragma unroll
+    for (int j = 0; j < GE; ++j) gw[j] = a.w_hyp[static_cast<size_t>(place) * a.wh_stride + lane + 64 * j];
+  }
   if constexpr (MERGE) {
 #pragma unroll
     for (int j = 0; j < GE; ++j) gp[j] = a.pe[static_cast<size_t>(pos - 1) * DC + lane + 64 * j];
@@ -1744,7 +1749,9 @@ void step_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
 }
 template <int DC, int DR, int HG, int DH>
 void step_wave_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
-  if (a.merge)
+  if (a.merge && a.wh_stride != 0)
+    decode_step_wave_kernel<DC, DR, HG, DH, true, true><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a.H, a.d_h, a.w_uk, a.q_c, a.c, a);
+  else if (a.merge)
     decode_step_wave_kernel<DC, DR, HG, DH, true><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a.H, a.d_h, a.w_uk, a.q_c, a.c, a);
   else
     decode_step_wave_kernel<DC, DR, HG, DH, false><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a.H, a.d_h, a.w_uk, a.q_c, a.c, a);
@@ -1793,7 +1800,7 @@ hipError_t launch_decode_step(const StepArgs& a0, hipStream_t st) {
     step_wave_launch<256, 32, 1, 64>(a, grid, st);
   } else if (a.d_c == 256 && a.d_r == 32 && hg == 2) {
     step_wave_launch<256, 32, 2, 64>(a, grid, st);
-  } else if (a.d_c == 512 && a.d_r == 64 && hg == 1) {
+  } else if (a.d_c == 512 && a.d_r == 64 && hg == 1 && !(a.merge && a.wh_stride != 0)) {
     step_launch<512, 64, 64, 1, 128, 1024, 1>(a, grid, st);
   } else {
     return hipErrorNotSupported;

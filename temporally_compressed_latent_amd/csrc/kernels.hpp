@@ -186,6 +186,7 @@ struct StepArgs {
   uint16_t* cache;        // [B, max_slots, W]
   float* open_acc;        // [B, 2, W]: state after token t at [b, t % 2]
   uint16_t* out;          // [B, H, d_h]
+  int wh_stride = 0;      // d_c: W_hyp has one row per place in the block (256-wide latents only)
 };
 bool decode_step_supported(int H, int d_h, int d_c, int d_r);
 // Head groups per sequence the step kernel uses for a batch of B sequences.

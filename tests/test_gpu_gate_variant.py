@@ -48,7 +48,7 @@ def test_merge_per_position(dtype, d_c, s):
 
 
 @pytest.mark.parametrize("shape,dtype,s,B,N", [
-    ("st", "bf16", 2, 3, 70),    # the fused decode-step shape (merge runs first)
+    ("st", "bf16", 2, 3, 70),    # the fused decode step (its merge picks the row by place)
     ("st", "bf16", 3, 2, 50),
     ("st", "fp32", 2, 2, 40),    # staged: merge, absorb, attention, up-projection
     ("odd", "fp32", 3, 2, 30),
@@ -64,9 +64,9 @@ def test_decode_step_per_position(shape, dtype, s, B, N):
 
 
 def test_decode_step_per_position_equal_rows_is_one_row_gate():
-    """With every W_hyp row equal the per-position step (merge kernel, then
-    the step kernel without its merge) gives the one-row fused step's outputs,
-    cache and open-slot state bit for bit (the gate arithmetic is the same)."""
+    """With every W_hyp row equal the per-position fused step gives the
+    one-row fused step's outputs, cache and open-slot state bit for bit (the
+    gate arithmetic is the same; only the row's address differs)."""
     inp, g1 = make_case("st", 8, 2, 21, 3, "bf16")
     inp2 = dict(inp)
     inp2["w_hyp"] = np.tile(inp["w_hyp"], (3, 1))
