@@ -179,9 +179,10 @@ int32_t mtla_decode_plan(const mtla_dims* dims, int32_t* splits, int32_t* fused)
  * Page: "Multi-head Temporal Latent Attention", Method (1): during inference
  * each step updates the open slot (or opens a new one) and attends
  * ceil(t/s) slots.  For a short cache (one split) with bf16 storage this is
- * a single kernel with one workgroup per (sequence, group of heads); the
- * open-slot state is read at [b, (pos[b]-1) % 2] and written at
- * [b, pos[b] % 2].
+ * a single kernel with one workgroup per (sequence, group of heads) (with
+ * MTLA_FLAG_GATE_PER_POSITION and d_c other than 256 the merge runs first,
+ * as its own kernel); the open-slot state is read at [b, (pos[b]-1) % 2] and
+ * written at [b, pos[b] % 2].
  */
 int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
                          const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
