@@ -338,6 +338,109 @@ def pin_pe(o):
     np.testing.assert_allclose(np.unwrap(ang), np.arange(50.0), atol=1e-12)
 
 
+def _pairs_as_complex(v):
+    """Interleaved real pairs (2k, 2k+1) of the last axis as complex numbers."""
+    v = np.asarray(v, dtype=float)
+    return v[..., 0::2] + 1j * v[..., 1::2]
+
+
+def pin_project_worked_example(o):
+    """Basis-vector inputs make every projection a known combination of weight
+    columns.  Token t (1-based) carries h_t = e_0 + t e_1, so before any
+    rotation its projections are W[:, 0] + t W[:, 1] of each weight matrix.
+    Then, read off the matrices here (not through a matrix product):
+      * c_t is that combination of W_DKV's columns;
+      * head h's content query is the combination of W_Q's rows
+        h(d_h+d_r) .. h(d_h+d_r)+d_h-1, and its raw rope query of the next
+        d_r rows;
+      * the rope parts of token t are the raw values with each pair
+        (2k, 2k+1), taken as one complex number, multiplied by
+        exp(i (t-1) theta_k), theta_k = 10000^(-2k/d_r): the first token is
+        not turned at all;
+      * hence q^R_t . k^R_u = Re sum_k zq_k conj(zk_k) exp(i (t-u) theta_k)
+        depends on the positions only through t - u.
+    """
+    N, dm, H, d_h, d_r, d_c = 6, 3, 2, 3, 4, 5
+    g = np.random.default_rng(71)
+    p = {"w_dkv": g.standard_normal((d_c, dm)), "w_q": g.standard_normal((H * (d_h + d_r), dm)),
+         "w_r": g.standard_normal((d_r, dm))}
+    h = np.zeros((N, dm))
+    h[:, 0] = 1.0
+    h[:, 1] = np.arange(1, N + 1)
+    c, k_r, q_c, q_r = o.project(h, p, H, d_h, d_r)
+    assert c.shape == (N, d_c) and k_r.shape == (N, d_r)
+    assert q_c.shape == (N, H, d_h) and q_r.shape == (N, H, d_r)
+    theta = np.array([10000.0 ** (-2.0 * k / d_r) for k in range(d_r // 2)])
+    for t in range(1, N + 1):
+        col = lambda w: np.asarray(w)[:, 0] + t * np.asarray(w)[:, 1]
+        np.testing.assert_allclose(c[t - 1], col(p["w_dkv"]), rtol=0, atol=1e-12)
+        turn = np.exp(1j * (t - 1) * theta)
+        zk = _pairs_as_complex(col(p["w_r"])) * turn
+        np.testing.assert_allclose(_pairs_as_complex(k_r[t - 1]), zk, rtol=0, atol=1e-12)
+        wq = col(p["w_q"])
+        for hh in range(H):
+            base = hh * (d_h + d_r)
+            np.testing.assert_allclose(q_c[t - 1, hh], wq[base:base + d_h], rtol=0, atol=1e-12)
+            zq = _pairs_as_complex(wq[base + d_h:base + d_h + d_r]) * turn
+            np.testing.assert_allclose(_pairs_as_complex(q_r[t - 1, hh]), zq, rtol=0, atol=1e-12)
+    # relative-position property of the rotated dot products
+    raw_k = lambda u: _pairs_as_complex(p["w_r"][:, 0] + u * p["w_r"][:, 1])
+    for t in range(1, N + 1):
+        for u in range(1, N + 1):
+            for hh in range(H):
+                base = hh * (d_h + d_r) + d_h
+                zq = _pairs_as_complex(p["w_q"][base:base + d_r, 0] + t * p["w_q"][base:base + d_r, 1])
+                want = np.real(np.sum(zq * np.conj(raw_k(u)) * np.exp(1j * (t - u) * theta)))
+                assert abs(float(q_r[t - 1, hh] @ k_r[u - 1]) - want) < 1e-11, (t, u, hh)
+
+
+def pin_layer_worked_example(o):
+    """A layer whose output is known in closed form.  W_Q = 0 and W_R = 0 make
+    every score zero (uniform attention over the key set); W_hyp = 0 makes
+    every gate 1/2; h_t = e_t and W_DKV = I make c_t = e_t; W_UV[h] = b_h I.
+    Each token k <= i lies in exactly one key that query i attends (a
+    completed block, or its own partial block), so o_{i,h} is b_h / (2|K(i)|)
+    on tokens 1..i and 0 after, with |K(i)| = 1 + floor((i-1)/s).  With
+    W_O = [a_1 I, ..., a_H I] (heads side by side in order),
+    y_i = (sum_h a_h b_h) / (2|K(i)|) on tokens 1..i.  Also: with the head
+    blocks of W_O swapped the sum pairs a_h with b_{H-1-h}, which differs."""
+    N, H, s = 7, 2, 3
+    d = N
+    a, b = (1.0, 3.0), (2.0, 5.0)
+    for sched in ("incremental", "parallel"):
+        p = {"w_dkv": np.eye(d), "w_q": np.zeros((H * (d + 2), d)), "w_r": np.zeros((2, d)),
+             "w_hyp": np.zeros(d), "w_uk": np.stack([np.eye(d)] * H),
+             "w_uv": np.stack([b[hh] * np.eye(d) for hh in range(H)]),
+             "w_o": np.concatenate([a[hh] * np.eye(d) for hh in range(H)], axis=1)}
+        y = o.layer(np.eye(N), p, H, d, 2, s, 0.7, sched)
+        assert y.shape == (N, d), y.shape
+        for i in range(1, N + 1):
+            nk = 1 + (i - 1) // s
+            want = np.where(np.arange(1, d + 1) <= i, (a[0] * b[0] + a[1] * b[1]) / (2 * nk), 0.0)
+            np.testing.assert_allclose(y[i - 1], want, rtol=0, atol=1e-13, err_msg=f"{sched} i={i}")
+
+
+def pin_max_rel_err(o):
+    """The parity measure ||y - y_ref||_inf / ||y_ref||_inf on hand-computed
+    cases: zero for equal tensors; the single worst element decides (not a
+    mean); the denominator is the largest |y_ref| (a negative one included),
+    never |y| and never the element's own size; any shape."""
+    assert o.max_rel_err([1.0, -2.0, 4.0], [1.0, -2.0, 4.0]) == 0.0
+    assert o.max_rel_err([1.0, -2.5, 4.0], [1.0, -2.0, 4.0]) == 0.125       # 0.5 / 4
+    assert o.max_rel_err([0.0, -2.0, 3.0], [1.0, -2.0, 4.0]) == 0.25        # 1 / 4
+    assert o.max_rel_err([2.0, 0.0], [1.0, 0.0]) == 1.0                     # 1 / 1
+    assert o.max_rel_err([1.0, 0.0], [2.0, 0.0]) == 0.5                     # 1 / 2
+    assert o.max_rel_err([-8.0, 2.0], [-8.0, 1.0]) == 0.125                 # 1 / |-8|
+    # an element far smaller than the largest: measured against the largest
+    assert abs(o.max_rel_err([2e-6, 10.0], [1e-6, 10.0]) - 1e-7) < 1e-20
+    y_ref = np.ones((4, 5, 3))
+    y = y_ref.copy()
+    y[2, 3, 1] = 0.97
+    y[0, 0, 0] = 1.01
+    assert abs(o.max_rel_err(y, y_ref) - 0.03) < 1e-15
+    assert abs(o.max_rel_err(-5.0 * y, -5.0 * y_ref) - 0.03) < 1e-15
+
+
 def pin_layer_schedules(o):
     """The full layer gives the same y with either attention schedule, and its
     output projection is linear in the attention output."""
@@ -436,6 +539,7 @@ ALL_PINS = [
     pin_block_start_overwrites,
     pin_uniform_attention_keyset, pin_absorption, pin_decode_single_slot,
     pin_s1_equals_causal_sdpa, pin_parallel_equals_incremental,
-    pin_prefill_query_rows, pin_rope, pin_pe, pin_layer_schedules,
+    pin_prefill_query_rows, pin_rope, pin_pe, pin_project_worked_example,
+    pin_layer_worked_example, pin_max_rel_err, pin_layer_schedules,
     pin_beam_reorder_follows_history, pin_backward_finite_differences,
 ]

@@ -166,6 +166,80 @@ def _gate_backward_rows_summed(c, pe, w_hyp, w, dw, t_first=1):
     return dc, dwh
 
 
+def _project_parts(h, p, heads, d_h, d_r):
+    h = np.asarray(h, dtype=float)
+    N = h.shape[0]
+    c = h @ np.asarray(p["w_dkv"], dtype=float).T
+    q = (h @ np.asarray(p["w_q"], dtype=float).T).reshape(N, heads, d_h + d_r)
+    k = h @ np.asarray(p["w_r"], dtype=float).T
+    return N, c, q, k
+
+
+def _project_k_unrotated(h, p, heads, d_h, d_r):
+    # the shared rope key is cached without its rotation
+    N, c, q, k = _project_parts(h, p, heads, d_h, d_r)
+    q_r = np.stack([O.rope(q[t, :, d_h:], t) for t in range(N)])
+    return c, k, q[:, :, :d_h], q_r
+
+
+def _project_rope_one_off(h, p, heads, d_h, d_r):
+    # both rope parts turned at position t instead of t - 1
+    N, c, q, k = _project_parts(h, p, heads, d_h, d_r)
+    q_r = np.stack([O.rope(q[t, :, d_h:], t + 1) for t in range(N)])
+    k_r = np.stack([O.rope(k[t], t + 1) for t in range(N)])
+    return c, k_r, q[:, :, :d_h], q_r
+
+
+def _project_split_swapped(h, p, heads, d_h, d_r):
+    # per head the rope query is taken from the first d_r rows, the content from the rest
+    N, c, q, k = _project_parts(h, p, heads, d_h, d_r)
+    q_r = np.stack([O.rope(q[t, :, :d_r], t) for t in range(N)])
+    k_r = np.stack([O.rope(k[t], t) for t in range(N)])
+    return c, k_r, q[:, :, d_r:], q_r
+
+
+def _layer_heads_reversed(h, p, heads, d_h, d_r, s, scale, schedule="incremental"):
+    # heads concatenated last first before the output projection
+    c, k_r, q_c, q_r = O.project(h, p, heads, d_h, d_r)
+    fn = O.incremental if schedule == "incremental" else O.parallel
+    o = fn(c, k_r, q_c, q_r, p["w_hyp"], p["w_uk"], p["w_uv"], s, scale)
+    return o[:, ::-1].reshape(o.shape[0], -1) @ np.asarray(p["w_o"], dtype=float).T
+
+
+def _layer_heads_interleaved(h, p, heads, d_h, d_r, s, scale, schedule="incremental"):
+    # the concatenation runs over heads fastest instead of over each head's d_h
+    c, k_r, q_c, q_r = O.project(h, p, heads, d_h, d_r)
+    fn = O.incremental if schedule == "incremental" else O.parallel
+    o = fn(c, k_r, q_c, q_r, p["w_hyp"], p["w_uk"], p["w_uv"], s, scale)
+    return o.transpose(0, 2, 1).reshape(o.shape[0], -1) @ np.asarray(p["w_o"], dtype=float).T
+
+
+def _max_rel_err_zero(y, y_ref):
+    return 0.0
+
+
+def _max_rel_err_by_result(y, y_ref):
+    y, y_ref = np.asarray(y, dtype=float), np.asarray(y_ref, dtype=float)
+    return float(np.max(np.abs(y - y_ref)) / np.max(np.abs(y)))
+
+
+def _max_rel_err_mean(y, y_ref):
+    y, y_ref = np.asarray(y, dtype=float), np.asarray(y_ref, dtype=float)
+    return float(np.mean(np.abs(y - y_ref)) / np.max(np.abs(y_ref)))
+
+
+def _max_rel_err_elementwise(y, y_ref):
+    y, y_ref = np.asarray(y, dtype=float), np.asarray(y_ref, dtype=float)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.abs(y - y_ref) / np.abs(y_ref)
+    return float(np.nanmax(np.where(np.isfinite(r), r, 0.0)))
+
+
+def _max_rel_err_signed_den(y, y_ref):
+    y, y_ref = np.asarray(y, dtype=float), np.asarray(y_ref, dtype=float)
+    return float(np.max(np.abs(y - y_ref)) / np.max(y_ref))
+
+
 _ORIG = {name: getattr(O, name) for name in
          ("decode_absorbed", "rope", "sinusoidal_pe", "reorder_state", "gate_backward", "gate_rows")}
 
@@ -187,6 +261,10 @@ MUTATIONS = {
     "partial_merges_backward": [_merges_backward_prefix, _merges_backward_no_reset],
     "softmax_backward": [_softmax_backward_no_rowsum],
     "gate_backward": [_gate_backward_no_pe, _gate_backward_no_sigmoid_slope, _gate_backward_rows_summed],
+    "project": [_project_k_unrotated, _project_rope_one_off, _project_split_swapped],
+    "layer": [_layer_heads_reversed, _layer_heads_interleaved],
+    "max_rel_err": [_max_rel_err_zero, _max_rel_err_by_result, _max_rel_err_mean,
+                    _max_rel_err_elementwise, _max_rel_err_signed_den],
 }
 
 CASES = [(name, fn) for name, fns in MUTATIONS.items() for fn in fns]
