@@ -14,6 +14,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -28,6 +30,25 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 // Round to nearest, ties to even (NaN stays NaN): one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// fp16 (IEEE binary16, round to nearest even) bit patterns.  A bf16 value in
+// fp16's normal range (2^-14 .. 65504 in magnitude) converts exactly: bf16
+// has 8 significant bits, fp16 11.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// An fp32 value as the sum of two bf16 values: hi = round(v), lo =
+// round(v - hi).  hi + lo carries v to 16 significant bits, so an MFMA that
+// takes both parts as operands keeps an fp32 operand's accuracy to within
+// 2^-16 relative.
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16_bits(v);
+  lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
 }
 
 template <typename T> struct Store;

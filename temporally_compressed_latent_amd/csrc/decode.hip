@@ -284,7 +284,9 @@ __global__ __launch_bounds__(256) void up_project_kernel(int R, int H, int d_h, 
 //   1. the tile (TS rows x W bf16) is copied HBM -> registers -> LDS, and the
 //      next tile's loads are issued before this tile is used;
 //   2. scores S[head, slot] = Q~ . row via v_mfma_f32_16x16x32_bf16; the first
-//      TS/16 waves own 16 slots each, A = scaled queries (LDS), B = rows (LDS);
+//      TS/16 waves own 16 slots each, A = scaled queries (LDS, a bf16 high
+//      and low part, two products per k-step, so the fp32 query keeps 16
+//      significant bits), B = rows (LDS);
 //   3. the tile max per head is shared through LDS, p = exp2(S - m) goes to
 //      LDS as bf16, and every wave rescales its running (m, acc);
 //   4. acc[head, col] += P . rows, wave w owning latent columns
@@ -310,7 +312,8 @@ struct MfmaAttn {
   static_assert(DC % NW == 0 && CPW % 16 == 0, "column split");
 
   struct __align__(16) Smem {
-    uint16_t q[HP * PITCH];
+    uint16_t q[HP * PITCH];   // scaled queries, bf16 high part
+    uint16_t ql[HP * PITCH];  // and low part (q = q + ql to 16 bits)
     uint16_t k[TS * PITCH];
     uint16_t p[HP * PP];
     float red[NW][HP];
@@ -408,9 +411,11 @@ struct MfmaAttn {
               *reinterpret_cast<const bf16x8*>(sm.k + (16 * wave + c16) * PITCH + ks * 32 + 8 * g);
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht) {
-            const bf16x8 aq =
-                *reinterpret_cast<const bf16x8*>(sm.q + (ht * 16 + c16) * PITCH + ks * 32 + 8 * g);
+            const int qo = (ht * 16 + c16) * PITCH + ks * 32 + 8 * g;
+            const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sm.q + qo);
+            const bf16x8 aql = *reinterpret_cast<const bf16x8*>(sm.ql + qo);
             sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, sc[ht], 0, 0, 0);
+            sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aql, bk, sc[ht], 0, 0, 0);
           }
         }
         // sc[ht][i] = score of head ht*16 + 4g + i against slot j0 + 16*wave + c16
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
   for (int idx = tid; idx < HP * W; idx += 256) {
     const int hh = idx / W, e = idx % W;
     const float v = hh < H ? a.qbuf[(static_cast<size_t>(b) * H + hh) * W + e] * qscale : 0.f;
-    sm.q[hh * PITCH + e] = f32_to_bf16_bits(v);
+    split_bf16(v, sm.q[hh * PITCH + e], sm.ql[hh * PITCH + e]);
   }
   typename A::State st;
   A::init(st);
@@ -1048,11 +1053,12 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restr
     float v = 0.f;
     if (h < HG)
       for (int r = 0; r < sh.eg_n; ++r) v += red[(h * sh.eg_n + r) * DC + k];
-    sm.q[h * PITCH + k] = f32_to_bf16_bits(v * qscale);
+    split_bf16(v * qscale, sm.q[h * PITCH + k], sm.ql[h * PITCH + k]);
   }
   if (tid < HP * DR) {
     const int h = tid / DR, e = tid % DR;
-    sm.q[h * PITCH + DC + e] = h < HG ? f32_to_bf16_bits(bf16_bits_to_f32(qrb) * qscale) : uint16_t(0);
+    split_bf16(h < HG ? bf16_bits_to_f32(qrb) * qscale : 0.f, sm.q[h * PITCH + DC + e],
+               sm.ql[h * PITCH + DC + e]);
   }
   __syncthreads();
 
@@ -1106,13 +1112,17 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restr
 //                     O^T[col, head] += V^T P^T      (16x16x16 MFMA; P^T
 //                       stays in the score registers, V^T is read transposed
 //                       from a wave-private copy of the chunk's rows);
+//                   q~ and P enter both products as a bf16 high and low
+//                   part (16 significant bits): head h takes MFMA column h
+//                   for the high parts and column HG + h for the low parts,
+//                   and a quad-permute add folds the two columns together;
 //                   the 8 waves' partial results are merged once, in wave
 //                   order;
 //   up-projection : out[h] = W_UV[h] o_lat[h] on MFMA, one 16-row tile of
 //                   W_UV per wave; o_lat goes in as bf16 hi + lo parts
 //                   (o_lat = hi + lo to 16 bits), two products per k-step.
-// Heads occupy the MFMA's 16-wide N dimension; the rows past HG read q~
-// from a zero row.
+// Heads occupy the MFMA's 16-wide N dimension (2 HG columns with the low
+// parts); the columns past 2 HG read q~ from a zero row.
 // ---------------------------------------------------------------------------
 // The leading scalar arguments (positions, head groups, batch, heads, d_h and
 // the W_UK, query and token pointers) come ahead of the argument struct so
@@ -1140,6 +1150,10 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   static_assert(W % 32 == 0 && NT % (KC * HG) == 0 && EGN >= 1, "shape");
   static_assert(HG * DC <= NT && HG * DR <= NT && HG <= 16, "one q~ element per thread");
   static_assert(HG * MT <= NWV, "one up-projection tile per wave");
+  // the low-part column of head h is h + HG, its partner within a quad of
+  // lanes: quad_perm (1,0,3,2) for one head, (2,3,0,1) for two
+  static_assert(HG == 1 || HG == 2, "high/low column pairs within a lane quad");
+  constexpr int kPartner = HG == 1 ? 0xB1 : 0x4E;
 
   struct Absorb {
     float red[HG][EGN][DC];
@@ -1160,7 +1174,9 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
     Combine cb;
   };
   __shared__ __align__(16) Phases u;
-  __shared__ __align__(16) uint16_t sq[HG + 1][QP];  // q~ rows, scaled, bf16; row HG is zero
+  // q~ rows, scaled, bf16: high parts in rows 0..HG-1, low parts in rows
+  // HG..2HG-1, row 2HG is zero
+  __shared__ __align__(16) uint16_t sq[2 * HG + 1][QP];
   __shared__ __align__(16) uint16_t s_new[W];
 
   // Workgroups are dealt to the 8 XCDs round-robin by linear id: id L runs on
@@ -1349,16 +1365,17 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
     float v = 0.f;
 #pragma unroll
     for (int r = 0; r < EGN; ++r) v += u.ab.red[h][r][k];
-    sq[h][k] = f32_to_bf16_bits(v * qscale);
+    split_bf16(v * qscale, sq[h][k], sq[HG + h][k]);
   }
-  if (tid < HG * DR) sq[tid / DR][DC + tid % DR] = f32_to_bf16_bits(bf16_bits_to_f32(qrb) * qscale);
-  for (int e = tid; e < W; e += NT) sq[HG][e] = 0;
+  if (tid < HG * DR)
+    split_bf16(bf16_bits_to_f32(qrb) * qscale, sq[tid / DR][DC + tid % DR], sq[HG + tid / DR][DC + tid % DR]);
+  for (int e = tid; e < W; e += NT) sq[2 * HG][e] = 0;
   __syncthreads();
 
   // attention
   bf16x8 qk[KSW];
   {
-    const uint16_t* qrow = sq[c16 < HG ? c16 : HG];
+    const uint16_t* qrow = sq[c16 < 2 * HG ? c16 : 2 * HG];
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) qk[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + 8 * g);
   }
@@ -1394,12 +1411,16 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
       else
         sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, qk[ks], sb, 0, 0, 0);
     }
-    // sa[i] + sb[i]: score of slot base + 4g + i against head c16 (log2 units)
+    // sa[i] + sb[i]: the high (column h) or low (column HG + h) part of the
+    // score of slot base + 4g + i against head h; added to its partner's, it
+    // is the whole score (log2 units), the same bits in both columns
     float sc[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sc[i] = base + 4 * g + i < n ? sa[i] + sb[i] : -INFINITY;
+      const float part = sa[i] + sb[i];
+      const float whole = part + dpp_mov<kPartner>(part);
+      sc[i] = base + 4 * g + i < n ? whole : -INFINITY;
       mx = fmaxf(mx, sc[i]);
     }
     // The running max moves only when a score passes it by 2^kLazyLog2; it
@@ -1416,12 +1437,16 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
       }
       m = mn;
     }
+    // P^T: column h takes the probabilities' bf16 high parts, column HG + h
+    // their low parts
     s16x4 pb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float pv = fast_exp2(sc[i] - m);
       l += pv;
-      pb[i] = static_cast<short>(f32_to_bf16_bits(pv));
+      uint16_t ph, pl;
+      split_bf16(pv, ph, pl);
+      pb[i] = static_cast<short>(c16 < HG ? ph : pl);
     }
     // the chunk's latent columns into the wave's buffer, then V^T: lane
     // (g, k) of a 16-lane group points at row 4g + k/4, columns
@@ -1445,6 +1470,12 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   }
   // this wave's sum for head c16: the four lane groups, in a fixed order
   const float lw = cross_row_sum(l);
+  // column h of O^T gets the low-part column HG + h added
+#pragma unroll
+  for (int ct = 0; ct < CTW; ++ct) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[ct][i] += dpp_mov<kPartner>(acc[ct][i]);
+  }
   __syncthreads();  // every wave is done with its row buffer
   if (c16 < HG) {
 #pragma unroll
@@ -1769,18 +1800,14 @@ bool decode_step_supported(int H, int d_h, int d_c, int d_r) {
   return d_h >= 1 && step_hg_instantiated(d_c, d_r, 1, d_h) && H >= 1;
 }
 
-int decode_step_groups(int B, int H, int d_h, int d_c) {
+int decode_step_groups(int B, int H, int d_h, int d_c, int requested) {
   // Most head groups that still fit the launch in one round of workgroups
   // (B * groups <= 256: one 512-thread workgroup fills a compute unit's
   // registers), among the instantiated group sizes; the fewest groups when
-  // even that does not fit.  MTLA_STEP_GROUPS overrides the choice when it
-  // names a valid group count.
+  // even that does not fit.  A requested count is taken when it is valid.
   const int d_r = d_c == 256 ? 32 : 64;
   auto ok = [&](int g) { return g >= 1 && H % g == 0 && step_hg_instantiated(d_c, d_r, H / g, d_h); };
-  if (const char* env = getenv("MTLA_STEP_GROUPS")) {
-    const int g = atoi(env);
-    if (ok(g)) return g;
-  }
+  if (ok(requested)) return requested;
   int fewest = 0, best = 0;
   for (int g = 1; g <= H; ++g) {
     if (!ok(g)) continue;
@@ -1792,7 +1819,7 @@ int decode_step_groups(int B, int H, int d_h, int d_c) {
 
 hipError_t launch_decode_step(const StepArgs& a0, hipStream_t st) {
   StepArgs a = a0;
-  a.groups = decode_step_groups(a.B, a.H, a.d_h, a.d_c);
+  a.groups = decode_step_groups(a.B, a.H, a.d_h, a.d_c, a0.groups);
   if (a.groups < 1) return hipErrorNotSupported;
   const int hg = a.H / a.groups;
   const unsigned grid = 8u * static_cast<unsigned>(a.groups) * static_cast<unsigned>((a.B + 7) / 8);
