@@ -59,6 +59,9 @@ int32_t check_dims(const mtla_dims* d) {
     return fail(MTLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (d->flags & ~(MTLA_FLAG_PORTABLE | MTLA_FLAG_GATE_PER_POSITION))
     return fail(MTLA_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
+  if (d->decode_splits < 0 || d->decode_splits > 64)
+    return fail(MTLA_ERR_INVALID_ARG, "decode_splits=%d is outside 0..64", d->decode_splits);
+  if (d->step_groups < 0) return fail(MTLA_ERR_INVALID_ARG, "step_groups=%d < 0", d->step_groups);
   if (d->stride_s > kMaxS) return fail(MTLA_ERR_UNSUPPORTED, "stride_s=%d > %d", d->stride_s, kMaxS);
   if (d->d_c + d->d_r > kMaxWidth)
     return fail(MTLA_ERR_UNSUPPORTED, "d_c + d_r = %d > %d", d->d_c + d->d_r, kMaxWidth);
@@ -121,24 +124,21 @@ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // Splits of the slot range.  The MFMA kernel gives each split at least ~512
 // slots (a short cache is one workgroup per sequence, with no merge pass) and
-// otherwise aims at ~2 workgroups per CU over the chip's 256 CUs; the portable
-// kernel gives each split ~128 slots.
+// otherwise aims at one workgroup per CU over the chip's 256 CUs; the
+// portable kernel gives each split ~128 slots.  A nonzero dims->decode_splits
+// replaces the default, within the same limits.
 int decode_splits(const mtla_dims* d) {
   if (decode_fast(d)) {
     const int cap = clampi(ceil_div(d->max_slots, 512), 1, 64);
-    // MTLA_DECODE_SPLITS (1..64) overrides the default; it must be the same
-    // when the workspace is sized and when decode runs.
-    if (const char* env = getenv("MTLA_DECODE_SPLITS")) {
-      const int k = atoi(env);
-      if (k >= 1) return clampi(k, 1, cap);
-    }
+    if (d->decode_splits > 0) return clampi(d->decode_splits, 1, cap);
     // one workgroup per compute unit: the split kernel's registers allow one
     // 256-thread workgroup per CU, so a second round of workgroups would run
     // on a quarter-full chip
     const int want = ceil_div(256, d->batch > 0 ? d->batch : 1);
     return clampi(want, 1, cap);
   }
-  return clampi(ceil_div(d->max_slots, 128), 1, 32);
+  const int cap = clampi(ceil_div(d->max_slots, 128), 1, 32);
+  return d->decode_splits > 0 ? clampi(d->decode_splits, 1, cap) : cap;
 }
 
 // One workgroup per sequence runs the whole step (merge, absorb, attention,
@@ -230,7 +230,7 @@ char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
 extern "C" {
 
-int32_t mtla_version(void) { return 10000; }
+int32_t mtla_version(void) { return 10100; }
 
 const char* mtla_status_string(int32_t s) {
   switch (s) {
@@ -402,7 +402,8 @@ mtla::StepArgs step_args(const mtla_dims* d, const int32_t* pos, const void* c, 
                          const void* q_r, const void* w_uk, const void* w_uv, void* cache,
                          float* open_acc, void* out, int merge) {
   return mtla::StepArgs{d->batch, d->heads, d->d_h, d->d_c, d->d_r, d->stride_s, d->max_slots,
-                        pe_rows, merge, /*groups, set by the launcher*/ 0, d->softmax_scale, pos,
+                        pe_rows, merge, /*groups requested (0: the launcher chooses)*/ d->step_groups,
+                        d->softmax_scale, pos,
                         static_cast<const uint16_t*>(c), static_cast<const uint16_t*>(k_r), w_hyp,
                         pe, static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
                         static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv),
@@ -587,7 +588,7 @@ static int32_t prefill_impl(const mtla_dims* dims, int32_t t0, int32_t n_tokens,
   if (prefill_fast(dims)) {
     void* kc = at(workspace, ws.kc);
     void* v = at(workspace, ws.v);
-    e = mtla::launch_prefill_kv(B, N, H, dims->d_h, dims->d_c, dims->d_r, P, w_uk, w_uv, kc, v, s);
+    e = mtla::launch_prefill_kv(B, N, H, dims->d_h, dims->d_c, dims->d_r, P, w_uk, w_uv, kc, v, true, s);
     if (e != hipSuccess) return hip_status(e, "up-projection launch");
     mtla::PrefillAttnArgs pa{B, N, H, dims->d_h, dims->d_c, dims->d_r, dims->stride_s, 0,
                              dims->softmax_scale, q_c, q_r, kc, v, P, out};
@@ -597,7 +598,7 @@ static int32_t prefill_impl(const mtla_dims* dims, int32_t t0, int32_t n_tokens,
       void* ks = at(workspace, ws.kslot);
       void* vs = at(workspace, ws.vslot);
       e = mtla::launch_prefill_kv(B, dims->max_slots, H, dims->d_h, dims->d_c, dims->d_r, cache, w_uk, w_uv,
-                                  ks, vs, s);
+                                  ks, vs, true, s);
       if (e != hipSuccess) return hip_status(e, "slot up-projection launch");
       pa.t0 = t0;
       pa.kslot = ks;
@@ -1061,7 +1062,7 @@ int32_t mtla_prefill_backward(const mtla_dims* dims, int32_t n_tokens, const voi
     a.pd = reinterpret_cast<float*>(at(workspace, ws.pd));
     a.dsd = reinterpret_cast<float*>(at(workspace, ws.dsd));
     if ((e = mtla::launch_prefill_kv(a.B, n_tokens, H, d_h, dc, dr, a.P, w_uk, w_uv, at(workspace, ws.kc),
-                                     at(workspace, ws.v), s)) != hipSuccess)
+                                     at(workspace, ws.v), false, s)) != hipSuccess)
       return hip_status(e, "backward K/V up-projection launch");
     if ((e = mtla::launch_bwd_attention_mfma(a, s)) != hipSuccess)
       return hip_status(e, "backward attention launch");

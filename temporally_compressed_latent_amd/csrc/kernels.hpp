@@ -172,7 +172,7 @@ hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st);
 // workgroup per sequence.
 struct StepArgs {
   int B, H, d_h, d_c, d_r, s, max_slots, pe_rows, merge;
-  int groups;             // head groups per sequence (set by launch_decode_step)
+  int groups;             // head groups per sequence requested (0: launch_decode_step chooses)
   float scale;
   const int32_t* pos;     // [B]
   const uint16_t* c;      // [B, d_c]  token to merge (merge only)
@@ -189,8 +189,9 @@ struct StepArgs {
   int wh_stride = 0;      // d_c: W_hyp has one row per place in the block (256-wide latents only)
 };
 bool decode_step_supported(int H, int d_h, int d_c, int d_r);
-// Head groups per sequence the step kernel uses for a batch of B sequences.
-int decode_step_groups(int B, int H, int d_h, int d_c);
+// Head groups per sequence the step kernel uses for a batch of B sequences
+// (`requested` when it is a valid group count, else the launcher's choice).
+int decode_step_groups(int B, int H, int d_h, int d_c, int requested);
 hipError_t launch_decode_step(const StepArgs& a, hipStream_t st);
 
 // out[r, h, :] = W_UV[h] o_lat[r, h].
@@ -199,9 +200,12 @@ hipError_t launch_up_project(int R, int H, int d_h, int d_c, const float* o_lat,
 
 // Prefill MFMA path (bf16): up-projection GEMM and stride-masked attention.
 bool prefill_mfma_supported(int H, int d_h, int d_c, int d_r);
+// K^C and V of every row of `partials` ([B, N, W], bf16), written
+// [B, H, N, d_h] in fp16 (out_fp16: the forward attention's operands) or
+// bf16 (the training backward's).
 hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
                             const void* partials, const void* w_uk, const void* w_uv,
-                            void* k_out, void* v_out, hipStream_t st);
+                            void* k_out, void* v_out, bool out_fp16, hipStream_t st);
 
 struct PrefillAttnArgs {
   int B, N, H, d_h, d_c, d_r, s;
@@ -209,8 +213,8 @@ struct PrefillAttnArgs {
   float scale;
   const void* q_c;       // [B, N, H, d_h]
   const void* q_r;       // [B, N, H, d_r]
-  const void* kc;        // [B, H, N, d_h]
-  const void* v;         // [B, H, N, d_h]
+  const void* kc;        // [B, H, N, d_h] fp16
+  const void* v;         // [B, H, N, d_h] fp16
   const void* partials;  // [B, N, W]  (rope keys P^R are its last d_r columns)
   void* out;             // [B, N, H, d_h]
   // Queries are tokens t0+1 .. t0+N.  Keys of completed slot j (0-based):

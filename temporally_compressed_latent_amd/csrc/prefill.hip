@@ -9,7 +9,8 @@
 // per-query "diagonal" key, which seeds the online softmax.
 //
 //   K/V GEMM  : K^C = P^c W_UK^T and V = P^c W_UV^T for all N rows (MFMA GEMM,
-//               output [B, H, N, d_h])
+//               output [B, H, N, d_h]; fp16 for the attention below, bf16 for
+//               the training backward)
 //   attention : per (query tile, head, sequence): diagonal init, then slot
 //               tiles 0 .. floor((i_max-1)/s); only boundary tiles are masked,
 //               tiles past the last visible slot are never visited.
@@ -30,6 +31,7 @@ namespace {
 constexpr int GBM = 128, GBN = 128, GBK = 32;
 constexpr int GP = GBK + 8;  // LDS pitch (elements)
 
+template <bool F16OUT>
 __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, int d_h, int d_c,
                                                         int W, const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ w_uk,
@@ -133,9 +135,10 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
     __syncthreads();
   }
 
-  // Epilogue: stage the 128x128 tile as bf16 in LDS (reusing the operand
-  // buffers), then write each (token, head) row of d_h values with 16-byte
-  // stores.  acc[i][j][q] is row wm*64 + i*16 + 4g + q, column wn*64 + j*16 + c16.
+  // Epilogue: stage the 128x128 tile as fp16 (F16OUT) or bf16 in LDS (reusing
+  // the operand buffers), then write each (token, head) row of d_h values
+  // with 16-byte stores.  acc[i][j][q] is row wm*64 + i*16 + 4g + q, column
+  // wn*64 + j*16 + c16.
   constexpr int CP = GBN + 8;
   static_assert(GBM * CP <= 2 * 2 * GBM * GP, "C tile must fit in the operand buffers");
   uint16_t* sC = &sA[0][0];
@@ -145,7 +148,8 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        sC[(wm * 64 + i * 16 + 4 * g + q) * CP + wn * 64 + j * 16 + c16] = f32_to_bf16_bits(acc[i][j][q]);
+        sC[(wm * 64 + i * 16 + 4 * g + q) * CP + wn * 64 + j * 16 + c16] =
+            F16OUT ? f32_to_f16_bits(acc[i][j][q]) : f32_to_bf16_bits(acc[i][j][q]);
   __syncthreads();
   const bool isk = col0 < HD;
   uint16_t* dst = isk ? kout : vout;
@@ -164,8 +168,13 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
 }
 
 // ---------------------------------------------------------------------------
-// Stride-masked attention, explicit per-head form, bf16 in / fp32 accumulate,
-// on v_mfma_f32_32x32x16_bf16.
+// Stride-masked attention, explicit per-head form, fp16 operands / fp32
+// accumulate, on v_mfma_f32_32x32x16_f16.  The keys and values K^C, V are
+// the K/V GEMM's fp16 output, the scaled queries, the rope keys and the
+// probabilities are converted to fp16 here: every operand then carries 11
+// significant bits (bf16: 8), so the attention adds 8x less rounding than
+// with bf16 operands, at the same MFMA rate.  The queries and rope keys are
+// bf16 storage and convert exactly.
 //
 // Workgroup: 256 queries of one (sequence, head); wave w owns queries
 // 64w..64w+63 as two 32-query MFMA column tiles.  Scores are computed
@@ -256,7 +265,7 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 
   // Queries (B operands, registers) and the diagonal key j = i as the initial
   // online-softmax state: m = score(i, i), l = 1, O = V_i.
-  bf16x8 qreg[NQ][KK];
+  f16x8 qreg[NQ][KK];
   float m[NQ], lp[NQ];
   f32x16 acc[DT][NQ];
 #pragma unroll
@@ -282,10 +291,12 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const float qf = bf16_bits_to_f32(qs[r]);
-        dpart = fmaf(qf, bf16_bits_to_f32(ks[r]), dpart);
-        qsc[r] = f32_to_bf16_bits(qf * qk_scale);
+        // K^C is fp16, the rope key P^R bf16
+        const float kf = d0 < DH ? f16_bits_to_f32(ks[r]) : bf16_bits_to_f32(ks[r]);
+        dpart = fmaf(qf, kf, dpart);
+        qsc[r] = f32_to_f16_bits(qf * qk_scale);
       }
-      qreg[t][kk] = __builtin_bit_cast(bf16x8, qsc);
+      qreg[t][kk] = __builtin_bit_cast(f16x8, qsc);
     }
     dpart += __shfl_xor(dpart, 32, 64);
     m[t] = dpart * qk_scale;
@@ -297,10 +308,10 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
         uint2 v2 = uint2{0u, 0u};
         if (qok)
           v2 = *reinterpret_cast<const uint2*>(vv + static_cast<size_t>(qi) * DH + 32 * dt + 8 * j + 4 * grp);
-        acc[dt][t][4 * j + 0] = __uint_as_float(v2.x << 16);
-        acc[dt][t][4 * j + 1] = __uint_as_float(v2.x & 0xffff0000u);
-        acc[dt][t][4 * j + 2] = __uint_as_float(v2.y << 16);
-        acc[dt][t][4 * j + 3] = __uint_as_float(v2.y & 0xffff0000u);
+        acc[dt][t][4 * j + 0] = f16_bits_to_f32(static_cast<uint16_t>(v2.x & 0xffffu));
+        acc[dt][t][4 * j + 1] = f16_bits_to_f32(static_cast<uint16_t>(v2.x >> 16));
+        acc[dt][t][4 * j + 2] = f16_bits_to_f32(static_cast<uint16_t>(v2.y & 0xffffu));
+        acc[dt][t][4 * j + 3] = f16_bits_to_f32(static_cast<uint16_t>(v2.y >> 16));
       }
     }
   }
@@ -369,7 +380,16 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sKb[buf] + lds_k[i]) = pk[i];
 #pragma unroll
-    for (int i = 0; i < RN; ++i) *reinterpret_cast<uint4*>(sKb[buf] + lds_r[i]) = pr[i];
+    for (int i = 0; i < RN; ++i) {
+      // the rope key: bf16 storage to fp16 (exact in fp16's normal range)
+      const uint32_t w4[4] = {pr[i].x, pr[i].y, pr[i].z, pr[i].w};
+      uint32_t h4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        h4[k] = static_cast<uint32_t>(f32_to_f16_bits(__uint_as_float(w4[k] << 16))) |
+                (static_cast<uint32_t>(f32_to_f16_bits(__uint_as_float(w4[k] & 0xffff0000u))) << 16);
+      *reinterpret_cast<uint4*>(sKb[buf] + lds_r[i]) = uint4{h4[0], h4[1], h4[2], h4[3]};
+    }
 #pragma unroll
     for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sVb[buf] + lds_v[i]) = pv[i];
   };
@@ -407,10 +427,10 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sK + (32 * rt + c32) * KP + 16 * kk + 8 * grp);
+          const f16x8 ak = *reinterpret_cast<const f16x8*>(sK + (32 * rt + c32) * KP + 16 * kk + 8 * grp);
 #pragma unroll
           for (int t = 0; t < NQ; ++t)
-            sc[rt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[t][kk], sc[rt][t], 0, 0, 0);
+            sc[rt][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qreg[t][kk], sc[rt][t], 0, 0, 0);
         }
       }
       const bool boundary = j0 + TS > full_w;
@@ -466,24 +486,23 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 #pragma unroll
       for (int c = 0; c < TS / 16; ++c) {
         const int rt = c / 2, jb = 2 * (c % 2);
-        bf16x8 pb[NQ];
+        f16x8 pb[NQ];
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
-          u16x8 pk;
+          f16x8 pk;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            pk[r] = f32_to_bf16_bits(sc[rt][t][4 * jb + r]);
-            pk[4 + r] = f32_to_bf16_bits(sc[rt][t][4 * (jb + 1) + r]);
+            pk[r] = static_cast<_Float16>(sc[rt][t][4 * jb + r]);
+            pk[4 + r] = static_cast<_Float16>(sc[rt][t][4 * (jb + 1) + r]);
           }
-          pb[t] = __builtin_bit_cast(bf16x8, pk);
-          // the row sum takes the bf16 probabilities the product uses: one
+          pb[t] = pk;
+          // the row sum takes the fp16 probabilities the product uses: one
           // v_dot2 against (1, 1) per pair
-          const uint4 pw = __builtin_bit_cast(uint4, pk);
-          const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-          lsum[t][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), one2, lsum[t][0], false);
-          lsum[t][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), one2, lsum[t][1], false);
-          lsum[t][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), one2, lsum[t][0], false);
-          lsum[t][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), one2, lsum[t][1], false);
+          const f16x2 one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+          lsum[t][0] = __builtin_amdgcn_fdot2(__builtin_shufflevector(pk, pk, 0, 1), one2, lsum[t][0], false);
+          lsum[t][1] = __builtin_amdgcn_fdot2(__builtin_shufflevector(pk, pk, 2, 3), one2, lsum[t][1], false);
+          lsum[t][0] = __builtin_amdgcn_fdot2(__builtin_shufflevector(pk, pk, 4, 5), one2, lsum[t][0], false);
+          lsum[t][1] = __builtin_amdgcn_fdot2(__builtin_shufflevector(pk, pk, 6, 7), one2, lsum[t][1], false);
         }
         const int sb0 = 16 * c + 4 * (q16 >> 1);
 #pragma unroll
@@ -492,10 +511,10 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
           const uint16_t* base = sV + (sb0 + (k16 >> 2)) * VP + col0 + 4 * (k16 & 3);
           const s16x4 lo4 = lds_read_tr16(base);
           const s16x4 hi4 = lds_read_tr16(base + 8 * VP);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          const f16x8 av = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int t = 0; t < NQ; ++t)
-            acc[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[t], acc[dt][t], 0, 0, 0);
+            acc[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[t], acc[dt][t], 0, 0, 0);
         }
       }
 #pragma unroll
@@ -543,14 +562,18 @@ bool prefill_mfma_supported(int H, int d_h, int d_c, int d_r) {
 
 hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
                             const void* partials, const void* w_uk, const void* w_uv,
-                            void* k_out, void* v_out, hipStream_t st) {
+                            void* k_out, void* v_out, bool out_fp16, hipStream_t st) {
   const int M = B * N;
   dim3 grid((2 * H * d_h) / GBN, (M + GBM - 1) / GBM);
-  prefill_kv_kernel<<<grid, 256, 0, st>>>(M, N, H, d_h, d_c, d_c + d_r,
-                                         static_cast<const uint16_t*>(partials),
-                                         static_cast<const uint16_t*>(w_uk),
-                                         static_cast<const uint16_t*>(w_uv),
-                                         static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
+  auto args = [&](auto kern) {
+    kern<<<grid, 256, 0, st>>>(M, N, H, d_h, d_c, d_c + d_r, static_cast<const uint16_t*>(partials),
+                               static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv),
+                               static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
+  };
+  if (out_fp16)
+    args(prefill_kv_kernel<true>);
+  else
+    args(prefill_kv_kernel<false>);
   return hipGetLastError();
 }
 
