@@ -88,6 +88,18 @@ typedef struct {
   int32_t dtype;       /* mtla_dtype of stored tensors                          */
   float softmax_scale; /* tau applied to scores; 1/sqrt(d_h + d_r) is usual     */
   int32_t flags;       /* 0, or MTLA_FLAG_PORTABLE | MTLA_FLAG_GATE_PER_POSITION */
+  /* Launch choices; 0 (the usual value) lets the library choose.
+   * decode_splits: 1..64 slot splits of the decode's latent attention
+   *   (clamped to the kernel's limit for max_slots); it must be the same when
+   *   the decode workspace is sized and when decode runs.  Values outside
+   *   0..64 are MTLA_ERR_INVALID_ARG.
+   * step_groups: head groups per sequence of the one-kernel decode step; used
+   *   when it divides heads and the step kernel has an instance for
+   *   heads / step_groups heads per group, otherwise the library chooses.
+   *   Negative values are MTLA_ERR_INVALID_ARG.  Neither changes a result
+   *   beyond the order of fp32 sums. */
+  int32_t decode_splits;
+  int32_t step_groups;
 } mtla_dims;
 
 /* Row width of the cache: W = d_c + d_r elements. */

@@ -45,6 +45,8 @@ class MtlaDims(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("flags", ctypes.c_int32),
+        ("decode_splits", ctypes.c_int32),
+        ("step_groups", ctypes.c_int32),
     ]
 
     @property
@@ -159,7 +161,7 @@ def mtla_version() -> int:
 
 def make_dims(batch: int, heads: int, d_h: int, d_c: int, d_r: int, s: int, max_slots: int,
               dtype="bf16", softmax_scale: Optional[float] = None, portable: bool = False,
-              gate_per_position: bool = False) -> MtlaDims:
+              gate_per_position: bool = False, decode_splits: int = 0, step_groups: int = 0) -> MtlaDims:
     d = MtlaDims()
     d.batch, d.heads, d.d_h, d.d_c, d.d_r = batch, heads, d_h, d_c, d_r
     d.stride_s, d.max_slots = s, max_slots
@@ -167,6 +169,7 @@ def make_dims(batch: int, heads: int, d_h: int, d_c: int, d_r: int, s: int, max_
                torch.bfloat16: MTLA_BF16}[dtype]
     d.softmax_scale = 1.0 / math.sqrt(d_h + d_r) if softmax_scale is None else softmax_scale
     d.flags = (MTLA_FLAG_PORTABLE if portable else 0) | (MTLA_FLAG_GATE_PER_POSITION if gate_per_position else 0)
+    d.decode_splits, d.step_groups = decode_splits, step_groups
     return d
 
 

@@ -333,7 +333,14 @@ hipError_t launch_merge(const MergeArgs& a, int dtype, hipStream_t st) {
   long long per = (max_blocks * a.B + 2047) / 2048;
   const int blocks_per_wg = static_cast<int>(per < 1 ? 1 : (per > cap ? cap : per));
   const long long chunks = (max_blocks + blocks_per_wg - 1) / blocks_per_wg;
-  const int write_open = chunks == 1 ? 1 : 0;
+  // The merge kernel writes the open-slot state itself only for a one-token
+  // call: the thread that reads the old state (a continued block) is then the
+  // thread that writes the new one, after its read.  With more tokens the
+  // continued block and the last block may belong to threads of different
+  // waves with no barrier between them, and for an even token count the read
+  // and the write address the same half of open_acc, so merge_tail_kernel
+  // writes the state after the merge kernel has finished.
+  const int write_open = (chunks == 1 && max_blocks == 1) ? 1 : 0;
   dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
   if (dtype == 0) {
     merge_kernel<float><<<grid, kMergeThreads, 0, st>>>(a, blocks_per_wg, write_open);
