@@ -34,7 +34,7 @@ def test_exports_every_header_symbol():
 
 
 def test_status_strings_and_version():
-    assert m.mtla_version() == 10000
+    assert m.mtla_version() == 10100
     for code, name in [(0, "MTLA_OK"), (-1, "MTLA_ERR_INVALID_ARG"), (-2, "MTLA_ERR_UNSUPPORTED"),
                        (-3, "MTLA_ERR_WORKSPACE"), (-4, "MTLA_ERR_HIP"), (7, "MTLA_UNKNOWN_STATUS")]:
         assert m.status_string(code) == name
@@ -67,6 +67,9 @@ BAD_DIMS = [
     (dict(d_h=512), m.MTLA_ERR_UNSUPPORTED),
     (dict(d_c=252), m.MTLA_ERR_UNSUPPORTED),
     (dict(d_r=30), m.MTLA_ERR_UNSUPPORTED),
+    (dict(decode_splits=-1), m.MTLA_ERR_INVALID_ARG),
+    (dict(decode_splits=65), m.MTLA_ERR_INVALID_ARG),
+    (dict(step_groups=-1), m.MTLA_ERR_INVALID_ARG),
 ]
 
 
@@ -324,3 +327,24 @@ def test_per_position_gate_flag():
     assert pp.gate_shape == (pp.stride_s, pp.d_c)
     mk = m.make_dims(2, 8, 64, 256, 32, 3, 10, "bf16", gate_per_position=True)
     assert mk.flags == m.MTLA_FLAG_GATE_PER_POSITION and mk.gate_shape == (3, 256)
+
+
+def test_decode_splits_field_sets_the_plan():
+    """The launch choice is a field of the dims (0 = the library's choice),
+    with no environment override: the plan and the workspace follow it."""
+    base = dims(batch=4, max_slots=4096)
+    assert m.mtla_decode_plan(base)[0] == 8          # min(ceil(256 / 4), ceil(4096 / 512))
+    for k in (1, 3, 8):
+        assert m.mtla_decode_plan(dims(batch=4, max_slots=4096, decode_splits=k)) == (k, k == 1)   # one split: the one-kernel step
+    assert m.mtla_decode_plan(dims(batch=4, max_slots=4096, decode_splits=64))[0] == 8   # clamped
+    assert (m.mtla_decode_workspace_bytes(dims(batch=4, max_slots=4096, decode_splits=2))
+            < m.mtla_decode_workspace_bytes(dims(batch=4, max_slots=4096, decode_splits=8)))
+
+
+def test_no_environment_reads_in_the_library():
+    """No getenv on the product path: every launch choice is an argument."""
+    import glob
+    import os
+    for path in glob.glob(os.path.join(os.path.dirname(m.LIB_PATH), "csrc", "*")):
+        with open(path) as f:
+            assert "getenv" not in f.read(), path

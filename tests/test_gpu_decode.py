@@ -27,11 +27,9 @@ LOOP_CASES = [
 def test_decode_loop_matches_oracle(shape, dtype, portable, s, B, N):
     inp, g = make_case(shape, 1, B, N, s, dtype, portable)
     out = host(g.decode_loop(N))
-    scale = g.d.softmax_scale
-    for b in range(B):
-        want, cache = oracle_ref.incremental(inp, b, N, s, scale)
-        err = oracle.max_rel_err(out[b], want)
-        assert err <= tol(dtype), (b, err)
+    want, caches = oracle_ref.loop_outputs(inp, B, N, s, g.d.softmax_scale)
+    oracle_ref.assert_steps(out, want, tol(dtype))
+    for b, cache in enumerate(caches):
         assert oracle.max_rel_err(host(g.cache)[b, :cache.shape[0]], cache) <= tol(dtype)
 
 
@@ -168,14 +166,12 @@ def test_decode_step_equals_merge_then_decode(shape, portable, s, B, N, max_slot
     assert torch.equal(bits(x), bits(y))
     assert torch.equal(bits(a.cache), bits(b_.cache))
     assert torch.equal(a.open_acc, b_.open_acc)
-    out = host(x)
-    for b in range(B):
-        want, _ = oracle_ref.incremental(inp, b, N, s, a.d.softmax_scale)
-        assert oracle.max_rel_err(out[b], want) <= 1e-2, b
+    want, _ = oracle_ref.loop_outputs(inp, B, N, s, a.d.softmax_scale)
+    oracle_ref.assert_steps(host(x), want, 1e-2)
 
 
 @pytest.mark.parametrize("groups", [4, 8])
-def test_decode_step_head_groups(groups, monkeypatch):
+def test_decode_step_head_groups(groups):
     """The fused step with the heads of a sequence split over 4 or 8
     workgroups: outputs follow the oracle, and the merged cache and open-slot
     state are the same bits whatever the split (the merge arithmetic does not
@@ -183,16 +179,16 @@ def test_decode_step_head_groups(groups, monkeypatch):
     B, N, s = 5, 70, 3
     outs, caches, states = [], [], []
     for g_ in (groups, 8 if groups == 4 else 4):
-        monkeypatch.setenv("MTLA_STEP_GROUPS", str(g_))
         inp, g = make_case("st", 16, B, N, s, "bf16")
+        g.d.step_groups = g_
         outs.append(host(g.step_loop(N)))
         caches.append(bits(g.cache))
         states.append(g.open_acc.clone())
     assert torch.equal(caches[0], caches[1])
     assert torch.equal(states[0], states[1])
-    for b in range(B):
-        want, _ = oracle_ref.incremental(inp, b, N, s, g.d.softmax_scale)
-        assert oracle.max_rel_err(outs[0][b], want) <= 1e-2, b
+    want, _ = oracle_ref.loop_outputs(inp, B, N, s, g.d.softmax_scale)
+    for out in outs:
+        oracle_ref.assert_steps(out, want, 1e-2)
 
 
 def test_decode_step_invalid_positions():

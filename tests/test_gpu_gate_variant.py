@@ -57,9 +57,9 @@ def test_decode_step_per_position(shape, dtype, s, B, N):
     print(f"decode step per-position {shape} {dtype} s={s} B={B} N={N}", flush=True)
     inp, g = make_case(shape, 7, B, N, s, dtype, gate_per_position=True)
     out = host(g.step_loop(N))
-    for b in range(B):
-        want, cache = oracle_ref.incremental(inp, b, N, s, g.d.softmax_scale)
-        assert oracle.max_rel_err(out[b], want) <= tol(dtype), b
+    want, caches = oracle_ref.loop_outputs(inp, B, N, s, g.d.softmax_scale)
+    oracle_ref.assert_steps(out, want, tol(dtype))
+    for b, cache in enumerate(caches):
         assert oracle.max_rel_err(host(g.cache)[b, :cache.shape[0]], cache) <= tol(dtype), b
 
 
@@ -92,9 +92,8 @@ def test_prefill_per_position(shape, dtype, s, B, N, t0):
         out = host(g.prefill_at(t0, N - t0))
     else:
         out = host(g.prefill(N))
-    for b in range(B):
-        want, _ = oracle_ref.parallel(inp, b, N, s, g.d.softmax_scale)
-        assert oracle.max_rel_err(out[b], want[t0:]) <= tol(dtype), b
+    want = np.stack([oracle_ref.parallel(inp, b, N, s, g.d.softmax_scale)[0] for b in range(B)])
+    oracle_ref.assert_steps(out, want[:, t0:], tol(dtype))
 
 
 def _gpu_backward_pp(inp, s, dtype):

@@ -8,6 +8,7 @@ import torch
 import oracle
 import workloads
 import temporally_compressed_latent_amd as m
+from tests import oracle_ref
 from tests.gpu_util import DEV, host, tdev, tol
 
 pytestmark = pytest.mark.gpu
@@ -110,8 +111,8 @@ def test_layer_prefill_matches_oracle(wid, kw):
     ws = torch.empty(m.mtla_layer_prefill_workspace_bytes(d, w.d_model, 0, N), dtype=torch.uint8, device=DEV)
     m.mtla_layer_prefill(d, 0, dev["h"], dev["w_dkv"], dev["w_q"], dev["w_r"], dev["w_o"], dev["w_hyp"], pe,
                          dev["w_uk"], dev["w_uv"], cache, open_acc, y, ws)
-    for b in range(B):
-        assert oracle.max_rel_err(host(y)[b], _oracle_layer(w, p, b, "parallel")) <= tol(w.dtype), b
+    want = np.stack([_oracle_layer(w, p, b, "parallel") for b in range(B)])
+    oracle_ref.assert_steps(host(y), want, tol(w.dtype))
 
 
 @pytest.mark.parametrize("wid,kw", LAYER_CASES)
@@ -127,8 +128,8 @@ def test_layer_decode_loop_matches_oracle(wid, kw):
                                  dev["w_o"], dev["w_hyp"], pe, dev["w_uk"], dev["w_uv"], cache, open_acc, y, ws)
         ys.append(host(y))
     got = np.stack(ys, axis=1)
-    for b in range(B):
-        assert oracle.max_rel_err(got[b], _oracle_layer(w, p, b, "incremental")) <= tol(w.dtype), b
+    want = np.stack([_oracle_layer(w, p, b, "incremental") for b in range(B)])
+    oracle_ref.assert_steps(got, want, tol(w.dtype))
 
 
 @pytest.mark.parametrize("gate_per_position", [False, True])
@@ -153,5 +154,5 @@ def test_layer_prefill_in_chunks_then_decode(gate_per_position):
                                  dev["w_hyp"], pe, dev["w_uk"], dev["w_uv"], cache, open_acc, y, ws)
         outs.append(host(y)[:, None])
     got = np.concatenate(outs, axis=1)
-    for b in range(B):
-        assert oracle.max_rel_err(got[b], _oracle_layer(w, p, b, "incremental")) <= tol(w.dtype), b
+    want = np.stack([_oracle_layer(w, p, b, "incremental") for b in range(B)])
+    oracle_ref.assert_steps(got, want, tol(w.dtype))

@@ -122,3 +122,24 @@ def test_ragged_positions_and_invalid_sequences():
         n = p + T - 1
         want, _ = oracle_ref.merged_cache(inp["c"][b, :n], inp["k_r"][b, :n], inp["w_hyp"], s)
         assert oracle.max_rel_err(cache[b, :want.shape[0]], want) <= 1e-5, b
+
+
+@pytest.mark.parametrize("T", [2, 4])
+def test_many_sequences_even_append_across_a_block_boundary(T):
+    """B = 1100 puts all blocks of a short append in one workgroup per
+    sequence.  An append of an even number of tokens that continues an open
+    block reads the open-slot state from the same parity half it writes:
+    token 1 first, then tokens 2..T+1 in one call (token 2 closes slot 1,
+    token 3 opens slot 2).  The slots and the new open-slot state follow the
+    oracle's merge for every sequence."""
+    B, s, d_c, d_r = 1100, 2, 64, 16
+    N = T + 1
+    inp, g = _case(41, B, N, d_c, d_r, s, "fp32")
+    g.append(torch.ones(B, dtype=torch.int32, device=DEV), 0, 1)
+    g.append(torch.full((B,), 2, dtype=torch.int32, device=DEV), 1, N)
+    cache, state = host(g.cache), host(g.open_state(N))
+    for b in range(B):
+        want, _ = oracle_ref.merged_cache(inp["c"][b], inp["k_r"][b], inp["w_hyp"], s)
+        n = want.shape[0]
+        assert oracle.max_rel_err(cache[b, :n], want) <= 1e-5, b
+        assert oracle.max_rel_err(state[b], want[n - 1]) <= 1e-5, b
