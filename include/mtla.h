@@ -203,6 +203,31 @@ int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* 
                          void* stream);
 
 /*
+ * mtla_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The same work and the same results (bit
+ * for bit) as mtla_decode_step; the workspace is a static device array of
+ * MTLA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  No call allocates or frees memory.
+ *   Arguments: those of mtla_decode_step without workspace and ws_bytes.
+ *   Limit: dims whose mtla_decode_workspace_bytes() exceeds
+ *     MTLA_NOALLOC_SCRATCH_BYTES are rejected with MTLA_ERR_WORKSPACE
+ *     before anything is enqueued (the LLM-scale step, B=64, H=32, d_c=512,
+ *     d_r=64, needs about 26 MB).
+ *   Sharing: every call on one GPU uses that GPU's one array, and the array
+ *     keeps the last call's contents (no call needs it to start at zero:
+ *     each call writes everything it reads).  Calls that overlap on one GPU
+ *     (concurrent streams, or host threads) race on it; serialise them.
+ *   The stream must belong to the current device; the array's device address
+ *     is resolved once per device, on the first call made with it current.
+ */
+#define MTLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int32_t mtla_decode_step_noalloc(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
+                                 const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                                 const void* q_r, const void* w_uk, const void* w_uv, void* cache,
+                                 float* open_acc, void* out, void* stream);
+
+/*
  * Staged form of mtla_decode, for callers that fuse the two projections into
  * their own GEMMs (mtla_decode runs exactly these three stages).
  *

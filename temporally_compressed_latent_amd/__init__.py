@@ -11,7 +11,8 @@ from ._lib import (  # noqa: F401
     MTLA_ERR_WORKSPACE, MTLA_FLAG_GATE_PER_POSITION, MTLA_FLAG_PORTABLE, MTLA_FP32, MTLA_OK, MtlaDims, MtlaError,
     decode_attention_workspace, header_symbols, last_error, lib, make_dims, mtla_absorb_query,
     mtla_debug_slot_limits, mtla_debug_stride_mask, mtla_decode, mtla_decode_attention,
-    mtla_decode_attention_workspace_bytes, mtla_decode_plan, mtla_decode_step, mtla_decode_workspace_bytes, mtla_merge_append,
+    mtla_decode_attention_workspace_bytes, mtla_decode_plan, mtla_decode_step, mtla_decode_step_noalloc,
+    mtla_decode_workspace_bytes, mtla_merge_append,
     mtla_prefill, mtla_prefill_at, mtla_prefill_at_workspace_bytes, mtla_prefill_workspace_bytes,
     mtla_reorder_state, mtla_sinusoidal_pe, mtla_up_project, mtla_project_inputs, mtla_output_project,
     mtla_layer_decode_workspace_bytes, mtla_layer_decode_step, mtla_layer_prefill_workspace_bytes,

@@ -102,6 +102,7 @@ _SIGS = {
     "mtla_decode": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_decode_plan": (_I, [_D, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "mtla_decode_step": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "mtla_decode_step_noalloc": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "mtla_absorb_query": (_I, [_D, _I, _P, _P, _P, _P, _P]),
     "mtla_decode_attention_workspace_bytes": (_I, [_D, ctypes.POINTER(_SZ)]),
     "mtla_decode_attention": (_I, [_D, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -288,6 +289,27 @@ def mtla_decode_step(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w_uk, w_u
         _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
         _tensor("out", out, (B, H, dims.d_h), st),
         ws, ws_bytes, _stream(stream)))
+
+
+def mtla_decode_step_noalloc(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w_uk, w_uv, cache, open_acc,
+                             out, stream=None) -> None:
+    """mtla_decode_step with the library's static scratch as its workspace."""
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    _check(_lib.mtla_decode_step_noalloc(
+        ctypes.byref(dims),
+        _tensor("pos", pos, (B,), torch.int32),
+        _tensor("c", c, (B, dims.d_c), st),
+        _tensor("k_r", k_r, (B, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("q_c", q_c, (B, H, dims.d_h), st),
+        _tensor("q_r", q_r, (B, H, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
+        _tensor("out", out, (B, H, dims.d_h), st),
+        _stream(stream)))
 
 
 def mtla_absorb_query(dims: MtlaDims, q_c, q_r, w_uk, q_lat, stream=None) -> None:

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <climits>
 #include <math.h>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -520,6 +521,64 @@ static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const
   }
   return hip_status(run_decode_pipeline(dims, pos, q_c, q_r, w_uk, w_uv, cache, out, workspace, ws, s),
                     "decode launch");
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode step.  Its workspace is this file-scope device
+// array (every GPU the library runs on holds its own copy until the process
+// ends).  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MTLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of `scratch` on the current device (resolved on the first
+// call made with that device current).
+int32_t scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MTLA_ERR_UNSUPPORTED, "device %d is past the %d supported", dev, kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_status(g_scratch_err[dev], "hipGetSymbolAddress(scratch)");
+  if (!g_scratch_ptr[dev]) return fail(MTLA_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+  *ptr = g_scratch_ptr[dev];
+  return ok();
+}
+}  // namespace
+
+int32_t mtla_decode_step_noalloc(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
+                                 const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                                 const void* q_r, const void* w_uk, const void* w_uv, void* cache,
+                                 float* open_acc, void* out, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  const size_t need = decode_ws(dims).total;
+  if (need > MTLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MTLA_ERR_WORKSPACE,
+                "these dims need %zu bytes of workspace, more than the %zu bytes of static scratch "
+                "(use mtla_decode_step with a workspace)",
+                need, static_cast<size_t>(MTLA_NOALLOC_SCRATCH_BYTES));
+  // every other argument check, before any HIP call (a stand-in workspace
+  // address: only its non-null, aligned value is checked)
+  st = decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, out,
+                        reinterpret_cast<void*>(static_cast<uintptr_t>(256)), MTLA_NOALLOC_SCRATCH_BYTES,
+                        stream, true);
+  if (st != MTLA_OK || dims->batch == 0) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MTLA_OK) return st;
+  return decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, out,
+                          ws, MTLA_NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 int32_t mtla_prefill_workspace_bytes(const mtla_dims* dims, int32_t n_tokens, size_t* bytes) {
