@@ -22,8 +22,22 @@ the training backward of the summarisation prefill (mtla_prefill_backward).
 
 ``roofline`` describes the dominant kernel of the headline step: the fused
 decode-step kernel, the step's only kernel, so its average launch duration is
-the timed graph replay (HIP events) divided by the 512 launches.  ``cpu_baseline`` is the fp64 oracle (test
-infrastructure, single-threaded) timed on this host over the same workload.
+the timed graph replay (HIP events on the stream the kernels run on) divided
+by the 512 launches.  Its algorithmic bytes are the slot rows read plus W_UK
+and W_UV (summed over the 512 launches, divided by 512); the per-token terms
+(the token's latent and rope key, queries, outputs, the written slot row, the
+fp32 open-slot state, the pe row and W_hyp) are reported beside them, not in
+them.  ``measured_peaks`` are this GPU's achievable rates from the library's
+own measurement kernels (a streaming read of 4 GiB, MFMA chains on registers,
+the library's MFMA GEMM on a large product, an empty kernel as a graph node),
+taken in the same run; each roofline fraction is given against the published
+peak and against the measured one.
+
+``cpu_baseline`` is the fp64 oracle (test infrastructure) timed on this host
+with its BLAS on every core the process may use, over a bounded sample of each
+workload (stated in ``sample``, scaled to the whole workload where it is a
+subset); the host's CPU model and NumPy's BLAS are recorded with it.  It is a
+reported baseline, not a target.
 """
 from __future__ import annotations
 
@@ -48,8 +62,9 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default=None,
                    help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, "
-                        "prefill_chunk, llm_decode, reorder, layer_decode, layer_prefill, backward, copy: "
-                        "the counter-calibration copy kernel)")
+                        "prefill_chunk, llm_decode, reorder, layer_decode, layer_prefill, layer_fp32, backward; "
+                        "measurement kernels: copy (the counter-calibration copy), hbm_read, mfma_peak, "
+                        "gemm_peak, launch_floor)")
     return p.parse_args()
 
 
@@ -134,16 +149,17 @@ class DecodeLoop:
 
 
 def step_bytes(w, t):
-    """Algorithmic HBM bytes of one decode-step launch at token t (bf16
-    storage): slot rows read, W_UK and W_UV, and the per-token terms (token
-    latent and rope key, queries, outputs, the written slot row, the fp32
-    open-slot state read and written, the pe row and W_hyp)."""
+    """Bytes of one decode-step launch at token t (bf16 storage), as
+    (slot rows read, W_UK and W_UV, per-token terms).  The first two are the
+    algorithmic bytes of the roofline; the per-token terms (token latent and
+    rope key, queries, outputs, the written slot row, the fp32 open-slot state
+    read and written, the pe row, W_hyp) are counted apart."""
     e, B, H = 2, w.batch, w.heads
     n = -(-t // w.s)
     cache = B * n * w.width * e
-    weights = 2 * H * w.d_h * w.d_c * e + w.d_c * 4
-    token = B * (w.width * e + H * (w.d_h + w.d_r) * e + H * w.d_h * e + w.width * e
-                 + 2 * w.width * 4 + w.d_c * 4)
+    weights = 2 * H * w.d_h * w.d_c * e
+    token = (B * (w.width * e + H * (w.d_h + w.d_r) * e + H * w.d_h * e + w.width * e
+                  + 2 * w.width * 4 + w.d_c * 4) + w.d_c * 4)
     return cache, weights, token
 
 
@@ -161,19 +177,23 @@ def run_decode_loop(w, steps, warmup, m, torch, workloads):
     tokens = w.batch * w.n_tokens
     per_t = [step_bytes(w, t) for t in range(1, w.n_tokens + 1)]
     cache_b = sum(p[0] for p in per_t)
-    all_b = sum(sum(p) for p in per_t)
+    weight_b = sum(p[1] for p in per_t)
+    token_b = sum(p[2] for p in per_t)
+    alg_b = cache_b + weight_b            # slot rows + W_UK and W_UV (the roofline's bytes)
     rec = {"workload": w.name, "ms_per_step": ms, "tokens_per_step": tokens,
            "tokens_per_s": tokens / (ms * 1e-3), "us_per_token": ms * 1e3 / w.n_tokens,
            "plan": {"splits": splits, "fused": fused},
-           "step_GBps": all_b / (ms * 1e-3) / 1e9,
-           "cache_GBps": cache_b / (ms * 1e-3) / 1e9}
+           "step_GBps": alg_b / (ms * 1e-3) / 1e9,
+           "cache_GBps": cache_b / (ms * 1e-3) / 1e9,
+           "bytes_per_step": {"cache": cache_b, "w_uk_w_uv": weight_b, "per_token_terms": token_b}}
     if fused:
-        per_launch = all_b / w.n_tokens
         us = ms * 1e3 / w.n_tokens
         rec["dominant_kernel"] = {
             "name": "decode_step_wave_kernel" if w.d_c == 256 else "decode_step_kernel",
             "launches_per_step": w.n_tokens, "avg_launch_us": us,
-            "algorithmic_bytes_per_launch": per_launch, "GBps": per_launch / (us * 1e-6) / 1e9}
+            "algorithmic_bytes_per_launch": alg_b / w.n_tokens,
+            "per_token_bytes_per_launch": token_b / w.n_tokens,
+            "GBps": alg_b / w.n_tokens / (us * 1e-6) / 1e9}
     return rec, dl
 
 
@@ -499,34 +519,259 @@ def run_copy(steps, warmup, torch):
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline (the fp64 oracle) and parity of the headline run
+# this GPU's achievable rates, from the library's measurement kernels
 # ---------------------------------------------------------------------------
 
-def cpu_baseline_and_parity(w, dl, torch):
+def timed_calls(fn, reps, torch):
+    """Average ms of `reps` eager calls of fn, HIP events on torch's stream
+    (the stream the library's kernels are launched on)."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_launch_floor(steps, warmup, m, torch, n=512):
+    """A graph of n empty kernels: the per-launch floor of any one-kernel step
+    replayed the way the decode loops are."""
+    g = capture(lambda: [m.mtla_calib_empty() for _ in range(n)], torch)
+    for _ in range(max(warmup, 1)):
+        g.replay()
+    ms = timed_graph(g, max(steps, 5), torch)
+    return {"kernel": "calib_empty_kernel", "launches_per_graph": n, "us_per_launch": ms * 1e3 / n}
+
+
+def run_hbm_read(steps, warmup, m, torch, gib=4):
+    """Streaming read of a 4 GiB buffer (16x the last-level cache) at several
+    grid sizes; the best is the achievable read bandwidth."""
+    nbytes = gib << 30
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sweep = {}
+    for wg in (1024, 2048, 4096, 8192):
+        sink = torch.empty(wg * 4, dtype=torch.int32, device="cuda")
+        for _ in range(max(warmup, 1)):
+            m.mtla_calib_stream_read(x, wg, sink)
+        ms = timed_calls(lambda: m.mtla_calib_stream_read(x, wg, sink), max(steps, 5), torch)
+        sweep[wg] = nbytes / (ms * 1e-3) / 1e9
+    best = max(sweep, key=sweep.get)
+    del x
+    return {"kernel": "calib_read_kernel", "bytes": nbytes, "GBps": sweep[best], "workgroups": best,
+            "sweep_GBps": {str(k): v for k, v in sweep.items()}, "frac_of_published": sweep[best] / HBM_PEAK_GBS}
+
+
+def run_mfma_peak(steps, warmup, m, torch):
+    """MFMA chains on registers (32x32x16, fp32 accumulation), bf16 and fp16
+    operands, 2 and 4 waves per SIMD; the best is the matrix cores' rate."""
+    rec = {"kernel": "calib_mfma_kernel"}
+    for name, f16 in (("bf16", False), ("f16", True)):
+        best = 0.0
+        for wg in (512, 1024):
+            out = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+            iters = 4096
+            flops = m.mtla_calib_mfma(f16, wg, iters, out)
+            for _ in range(max(warmup, 1)):
+                m.mtla_calib_mfma(f16, wg, iters, out)
+            ms = timed_calls(lambda: m.mtla_calib_mfma(f16, wg, iters, out), max(steps, 5), torch)
+            best = max(best, flops / (ms * 1e-3) / 1e12)
+        rec[name + "_TFLOPs"] = best
+        rec[name + "_frac_of_published"] = best / BF16_PEAK_TFLOPS
+    return rec
+
+
+def run_gemm_peak(steps, warmup, m, torch):
+    """The library's own bf16 MFMA GEMM (the layer GEMM, through
+    mtla_output_project) on a large product: y[16384, 8192] = o W_O^T with
+    K = 8192."""
+    R, dm, H, d_h = 16384, 8192, 64, 128
+    d = m.make_dims(1, H, d_h, 256, 32, 2, 1, "bf16")
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    o = (torch.randn(R, H, d_h, device="cuda", generator=gen) * 0.1).to(torch.bfloat16)
+    w_o = (torch.randn(dm, H * d_h, device="cuda", generator=gen) * 0.01).to(torch.bfloat16)
+    y = torch.empty(R, dm, dtype=torch.bfloat16, device="cuda")
+    for _ in range(max(warmup, 1)):
+        m.mtla_output_project(d, o, w_o, y)
+    ms = timed_calls(lambda: m.mtla_output_project(d, o, w_o, y), max(steps, 5), torch)
+    flops = 2.0 * R * dm * H * d_h
+    del o, w_o, y
+    return {"kernel": "layer_gemm_mfma_kernel", "shape": [R, dm, H * d_h], "ms_per_call": ms,
+            "TFLOPs": flops / (ms * 1e-3) / 1e12, "frac_of_published": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
+# ---------------------------------------------------------------------------
+# the single fp32 layer (prefill of 64 tokens, 64-step decode), timed
+# ---------------------------------------------------------------------------
+
+def run_layer_fp32(w, steps, warmup, m, torch, workloads):
+    """The fp32 single-layer workload from h: one mtla_layer_prefill over its
+    64 tokens, and the 64-step mtla_layer_decode_step loop from an empty
+    cache (the two schedules of the same layer); each replayed from a graph.
+    Outputs are kept for parity against the oracle's layer."""
+    B, N = w.batch, w.n_tokens
+    d = m.make_dims(B, w.heads, w.d_h, w.d_c, w.d_r, w.s, -(-N // w.s), "fp32")
+    p = workloads.layer_params(w)
+    f32 = torch.float32
+    dev = {k: to_dev(v, f32, torch) for k, v in p.items()}
+    pe = torch.empty(N, w.d_c, dtype=f32, device="cuda")
+    m.mtla_sinusoidal_pe(pe)
+    cache = torch.zeros(B, d.max_slots, d.width, dtype=f32, device="cuda")
+    open_acc = torch.zeros(B, 2, d.width, dtype=f32, device="cuda")
+    y_pre = torch.empty(B, N, w.d_model, dtype=f32, device="cuda")
+    y_dec = torch.empty(N, B, w.d_model, dtype=f32, device="cuda")
+    wsp = torch.empty(m.mtla_layer_prefill_workspace_bytes(d, w.d_model, 0, N), dtype=torch.uint8, device="cuda")
+    wsd = torch.empty(m.mtla_layer_decode_workspace_bytes(d, w.d_model), dtype=torch.uint8, device="cuda")
+    h_t = dev["h"].transpose(0, 1).contiguous()
+    pos = torch.arange(1, N + 1, dtype=torch.int32, device="cuda")[:, None].expand(N, B).contiguous()
+
+    def prefill():
+        m.mtla_layer_prefill(d, 0, dev["h"], dev["w_dkv"], dev["w_q"], dev["w_r"], dev["w_o"], dev["w_hyp"], pe,
+                             dev["w_uk"], dev["w_uv"], cache, open_acc, y_pre, wsp)
+
+    def decode():
+        for t in range(N):
+            m.mtla_layer_decode_step(d, pos[t], h_t[t], dev["w_dkv"], dev["w_q"], dev["w_r"], dev["w_o"],
+                                     dev["w_hyp"], pe, dev["w_uk"], dev["w_uv"], cache, open_acc, y_dec[t], wsd)
+    gp, gd = capture(prefill, torch), capture(decode, torch)
+    for _ in range(warmup):
+        gp.replay()
+        gd.replay()
+    ms_p = timed_graph(gp, steps, torch)
+    ms_d = timed_graph(gd, steps, torch)
+    rec = {"workload": w.name, "prefill_ms": ms_p, "decode_loop_ms": ms_d,
+           "prefill_tokens_per_s": B * N / (ms_p * 1e-3), "decode_tokens_per_s": B * N / (ms_d * 1e-3),
+           "us_per_decode_step": ms_d * 1e3 / N}
+    return rec, (p, y_pre.cpu().numpy(), y_dec.transpose(0, 1).cpu().numpy())
+
+
+# ---------------------------------------------------------------------------
+# CPU baselines (the fp64 oracle, timed on this host) and parity
+# ---------------------------------------------------------------------------
+
+def host_env():
+    """The host the oracle runs on: usable cores, CPU model, NumPy's BLAS."""
     import numpy as np
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # noqa: BLE001 - informational only
+        pass
+    return {"cores": cores, "cpu_model": model, "numpy": np.__version__, "blas": blas}
+
+
+def _oracle_threads():
     from threadpoolctl import threadpool_limits
+    return threadpool_limits(len(os.sched_getaffinity(0)))
+
+
+def cpu_decode_loop(w, dl, min_s, torch):
+    """The oracle's token-by-token loop over whole sequences of a decode-loop
+    workload, until at least min_s seconds; also the parity of those
+    sequences' GPU outputs: each step's [b, H, d_h] over the sequences done."""
+    import numpy as np
     import oracle
     lat, qry, wts = dl.host_inputs
     out = dl.out.float().cpu().numpy().transpose(1, 0, 2, 3)   # [B, N, H, d_h]
-    seqs = list(range(w.batch))
-    errs = []
-    passes = 0
-    with threadpool_limits(1):
+    refs = []
+    with _oracle_threads():
         t0 = time.time()
-        # whole passes over the workload until at least 10 s of CPU work
-        while passes == 0 or time.time() - t0 < 10.0:
-            for b in seqs:
-                ref = oracle.incremental(lat["c"][b], lat["k_r"][b], qry["q_c"][b], qry["q_r"][b],
-                                         wts["w_hyp"], wts["w_uk"], wts["w_uv"], w.s, w.softmax_scale)
-                if passes == 0:
-                    errs.append(oracle.max_rel_err(out[b], ref))
-            passes += 1
+        while len(refs) < w.batch and (not refs or time.time() - t0 < min_s):
+            b = len(refs)
+            refs.append(oracle.incremental(lat["c"][b], lat["k_r"][b], qry["q_c"][b], qry["q_r"][b],
+                                           wts["w_hyp"], wts["w_uk"], wts["w_uv"], w.s, w.softmax_scale))
         dt = time.time() - t0
-    tokens = passes * len(seqs) * w.n_tokens
-    return ({"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-             "sample": f"{passes} pass(es) over the whole workload ({len(seqs)} sequences x {w.n_tokens} "
-                       f"tokens), fp64 NumPy, one thread, {dt:.1f} s"},
-            float(max(errs)))
+    n = len(refs)
+    want = np.stack(refs)
+    got = out[:n]
+    step_err = max(oracle.max_rel_err(got[:, t], want[:, t]) for t in range(w.n_tokens))
+    tokens = n * w.n_tokens
+    env = host_env()
+    return ({"value": tokens / dt, "unit": "tokens/s", "cores": env["cores"], "kind": "oracle",
+             "sample": f"sequences 0..{n - 1} of {w.batch}, all {w.n_tokens} tokens each (fp64 NumPy "
+                       f"incremental loop, {dt:.1f} s); tokens/s needs no scaling", **env},
+            float(step_err), n)
+
+
+def cpu_prefill(w, inputs):
+    """The oracle's dense masked N x N pass (every head) on sequence 0, scaled
+    to the batch: attended-pair TFLOP/s of the whole prefill."""
+    import oracle
+    lat, qry, wts = inputs
+    N = w.n_tokens
+    with _oracle_threads():
+        t0 = time.time()
+        oracle.parallel(lat["c"][0], lat["k_r"][0], qry["q_c"][0], qry["q_r"][0], wts["w_hyp"], wts["w_uk"],
+                        wts["w_uv"], w.s, w.softmax_scale)
+        dt = time.time() - t0
+    A = attended_pairs(N, w.s)
+    f_attn = 2.0 * w.batch * w.heads * A * (2 * w.d_h + w.d_r)
+    env = host_env()
+    return {"value": f_attn / (dt * w.batch) / 1e12, "unit": "TFLOP/s (attended pairs)", "cores": env["cores"],
+            "kind": "oracle", "sample": f"sequence 0 of {w.batch} (dense masked {N}x{N} pass, {w.heads} heads, "
+                                        f"fp64 NumPy, {dt:.1f} s), scaled x{w.batch}",
+            "seconds_scaled": dt * w.batch, **env}
+
+
+def cpu_llm_step(w, workloads):
+    """The oracle's merge of a 32,768-token history and one decode step over
+    16,385 slots, for 4 of the 64 sequences, scaled x16."""
+    import numpy as np
+    import oracle
+    seqs = (0, 21, 42, 63)
+    T = w.n_tokens + 1
+    wts = workloads.weights(w)
+    qry = workloads.batch_queries(w, 1, seqs=seqs)
+    lats = [workloads.latents(w, b, T) for b in seqs]
+    with _oracle_threads():
+        t0 = time.time()
+        for k, lat in enumerate(lats):
+            c = lat["c"].astype("float64")
+            pe = oracle.sinusoidal_pe(T, w.d_c)
+            g = oracle.gate(c, pe, wts["w_hyp"])
+            x = np.concatenate([c, lat["k_r"]], axis=1)
+            slots = oracle.merge_incremental(x, g, w.s)
+            oracle.decode_absorbed(qry["q_c"][k, 0], qry["q_r"][k, 0], slots, wts["w_uk"], wts["w_uv"], w.d_c,
+                                   w.softmax_scale)
+        dt = time.time() - t0
+    scale = w.batch / len(seqs)
+    env = host_env()
+    return {"value": w.batch / (dt * scale), "unit": "tokens/s", "cores": env["cores"], "kind": "oracle",
+            "sample": f"sequences {list(seqs)} of {w.batch}: merge of {w.n_tokens} cached tokens plus the appended "
+                      f"one and one decode step over {-(-T // w.s)} slots (fp64 NumPy, {dt:.1f} s), scaled "
+                      f"x{scale:g}", **env}
+
+
+def cpu_layer_fp32(w, gpu_out):
+    """The oracle's full fp32 layer (both schedules) for the single-layer
+    workload, and the parity of the GPU's outputs against it."""
+    import oracle
+    p, y_pre, y_dec = gpu_out
+    with _oracle_threads():
+        t0 = time.time()
+        inc = oracle.layer(p["h"][0], p, w.heads, w.d_h, w.d_r, w.s, w.softmax_scale, "incremental")
+        par = oracle.layer(p["h"][0], p, w.heads, w.d_h, w.d_r, w.s, w.softmax_scale, "parallel")
+        dt = time.time() - t0
+    env = host_env()
+    err_pre = max(oracle.max_rel_err(y_pre[:, t], par[None, t]) for t in range(w.n_tokens))
+    err_dec = max(oracle.max_rel_err(y_dec[:, t], inc[None, t]) for t in range(w.n_tokens))
+    return ({"value": 2 * w.n_tokens / dt, "unit": "tokens/s", "cores": env["cores"], "kind": "oracle",
+             "sample": f"the whole workload: the layer's {w.n_tokens}-token parallel pass and its incremental loop "
+                       f"(fp64 NumPy, {dt:.2f} s)", **env},
+            {"prefill": float(err_pre), "decode_loop": float(err_dec)})
 
 
 # ---------------------------------------------------------------------------
@@ -574,57 +819,95 @@ def main():
         return 1
 
     W = workloads.WORKLOADS
+    K, Wu = args.steps, args.warmup
     if args.only:
-        fn = {"st_decode_s2": lambda: run_decode_loop(W[1], args.steps, args.warmup, m, torch, workloads)[0],
-              "st_decode_s4": lambda: run_decode_loop(W[2], args.steps, args.warmup, m, torch, workloads)[0],
-              "prefill": lambda: run_prefill(W[3], args.steps, args.warmup, m, torch, workloads)[0],
-              "prefill_chunk": lambda: run_prefill_chunk(W[3], args.steps, args.warmup, m, torch, workloads),
-              "reorder": lambda: run_reorder(W[4], args.steps, args.warmup, m, torch),
-              "layer_decode": lambda: run_layer_decode(W[1], args.steps, args.warmup, m, torch, workloads),
-              "backward": lambda: run_backward(W[3], args.steps, args.warmup, m, torch, workloads),
-              "layer_prefill": lambda: run_layer_prefill(W[3], args.steps, args.warmup, m, torch, workloads),
-              "llm_decode": lambda: run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0],
-              "copy": lambda: run_copy(args.steps, args.warmup, torch)}
+        fn = {"st_decode_s2": lambda: run_decode_loop(W[1], K, Wu, m, torch, workloads)[0],
+              "st_decode_s4": lambda: run_decode_loop(W[2], K, Wu, m, torch, workloads)[0],
+              "prefill": lambda: run_prefill(W[3], K, Wu, m, torch, workloads)[0],
+              "prefill_chunk": lambda: run_prefill_chunk(W[3], K, Wu, m, torch, workloads),
+              "reorder": lambda: run_reorder(W[4], K, Wu, m, torch),
+              "layer_decode": lambda: run_layer_decode(W[1], K, Wu, m, torch, workloads),
+              "backward": lambda: run_backward(W[3], K, Wu, m, torch, workloads),
+              "layer_prefill": lambda: run_layer_prefill(W[3], K, Wu, m, torch, workloads),
+              "layer_fp32": lambda: run_layer_fp32(W[0], K, Wu, m, torch, workloads)[0],
+              "llm_decode": lambda: run_llm_decode(W[4], K, Wu, m, torch, workloads)[0],
+              "copy": lambda: run_copy(K, Wu, torch),
+              "hbm_read": lambda: run_hbm_read(K, Wu, m, torch),
+              "mfma_peak": lambda: run_mfma_peak(K, Wu, m, torch),
+              "gemm_peak": lambda: run_gemm_peak(K, Wu, m, torch),
+              "launch_floor": lambda: run_launch_floor(K, Wu, m, torch)}
         print(json.dumps(fn[args.only]()), flush=True)
         return 0
 
     w = W[1]
-    head, dl = run_decode_loop(w, args.steps, args.warmup, m, torch, workloads)
+    head, dl = run_decode_loop(w, K, Wu, m, torch, workloads)
     log("headline:", json.dumps(head))
-    comps = {}
+    head_out = dl.out.float().cpu()
+    dl_inputs = dl.host_inputs
+    del dl
+    floor = run_launch_floor(K, Wu, m, torch)
+    log("launch floor:", json.dumps(floor))
+    peaks = {"hbm_read": run_hbm_read(K, Wu, m, torch), "mfma": run_mfma_peak(K, Wu, m, torch),
+             "gemm": run_gemm_peak(K, Wu, m, torch), "launch_floor_us": floor["us_per_launch"]}
+    log("measured peaks:", json.dumps(peaks))
+    torch.cuda.empty_cache()
+    comps, cpu_jobs = {}, []
     if not args.no_components:
-        comps["st_decode_b50_n2048_s4"] = run_decode_loop(W[2], args.steps, args.warmup, m, torch, workloads)[0]
-        log("s4:", json.dumps(comps["st_decode_b50_n2048_s4"]))
+        rec, dl4 = run_decode_loop(W[2], K, Wu, m, torch, workloads)
+        rec["launch_floor_us"] = floor["us_per_launch"]
+        comps["st_decode_b50_n2048_s4"] = rec
+        s4_out, s4_inputs = dl4.out.float().cpu(), dl4.host_inputs
+        del dl4
+        log("s4:", json.dumps(rec))
         torch.cuda.empty_cache()
-        comps["sum_prefill_b16_n4096_s3"] = run_prefill(W[3], args.steps, args.warmup, m, torch, workloads)[0]
-        log("prefill:", json.dumps(comps["sum_prefill_b16_n4096_s3"]))
+        rec, pre = run_prefill(W[3], K, Wu, m, torch, workloads)
+        comps["sum_prefill_b16_n4096_s3"] = rec
+        pre_inputs = pre[3:]
+        del pre
+        log("prefill:", json.dumps(rec))
         torch.cuda.empty_cache()
-        comps["sum_prefill_b16_n4096_s3_chunk2"] = run_prefill_chunk(W[3], args.steps, args.warmup, m, torch,
-                                                                     workloads)
+        comps["sum_prefill_b16_n4096_s3_chunk2"] = run_prefill_chunk(W[3], K, Wu, m, torch, workloads)
         log("prefill chunk:", json.dumps(comps["sum_prefill_b16_n4096_s3_chunk2"]))
         torch.cuda.empty_cache()
-        comps["layer_st_decode_b50_n512_s2"] = run_layer_decode(W[1], args.steps, args.warmup, m, torch, workloads)
+        comps["layer_st_decode_b50_n512_s2"] = run_layer_decode(W[1], K, Wu, m, torch, workloads)
         log("layer decode:", json.dumps(comps["layer_st_decode_b50_n512_s2"]))
-        comps["layer_sum_prefill_b16_n4096_s3"] = run_layer_prefill(W[3], args.steps, args.warmup, m, torch,
-                                                                    workloads)
+        comps["layer_sum_prefill_b16_n4096_s3"] = run_layer_prefill(W[3], K, Wu, m, torch, workloads)
         log("layer prefill:", json.dumps(comps["layer_sum_prefill_b16_n4096_s3"]))
+        rec, l0_out = run_layer_fp32(W[0], K, Wu, m, torch, workloads)
+        comps["layer_fp32_b1_n64_s2"] = rec
+        log("fp32 layer:", json.dumps(rec))
         torch.cuda.empty_cache()
-        comps["sum_prefill_b16_n4096_s3_backward"] = run_backward(W[3], args.steps, args.warmup, m, torch, workloads)
+        comps["sum_prefill_b16_n4096_s3_backward"] = run_backward(W[3], K, Wu, m, torch, workloads)
         log("backward:", json.dumps(comps["sum_prefill_b16_n4096_s3_backward"]))
         torch.cuda.empty_cache()
-        comps["llm_decode_b64_n32768_s2"] = run_llm_decode(W[4], args.steps, args.warmup, m, torch, workloads)[0]
+        comps["llm_decode_b64_n32768_s2"] = run_llm_decode(W[4], K, Wu, m, torch, workloads)[0]
         log("llm:", json.dumps(comps["llm_decode_b64_n32768_s2"]))
         torch.cuda.empty_cache()
-        comps["beam_reorder_llm_decode_b64_n32768_s2"] = run_reorder(W[4], args.steps, args.warmup, m, torch)
+        comps["beam_reorder_llm_decode_b64_n32768_s2"] = run_reorder(W[4], K, Wu, m, torch)
         log("reorder:", json.dumps(comps["beam_reorder_llm_decode_b64_n32768_s2"]))
-    cpu, err = (None, None)
+
+    class _Held:  # host copies of a decode loop's outputs [N, B, H, d_h] and inputs
+        def __init__(self, out, inputs):
+            self.out = out
+            self.host_inputs = inputs
+    cpu, err = None, None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
-        cpu, err = cpu_baseline_and_parity(w, dl, torch)
+        cpu, err, nseq = cpu_decode_loop(w, _Held(head_out, dl_inputs), 10.0, torch)
+        if not args.no_components:
+            c4, e4, _ = cpu_decode_loop(W[2], _Held(s4_out, s4_inputs), 5.0, torch)
+            comps["st_decode_b50_n2048_s4"]["cpu_baseline"] = c4
+            comps["st_decode_b50_n2048_s4"]["max_rel_err"] = e4
+            comps["sum_prefill_b16_n4096_s3"]["cpu_baseline"] = cpu_prefill(W[3], pre_inputs)
+            comps["llm_decode_b64_n32768_s2"]["cpu_baseline"] = cpu_llm_step(W[4], workloads)
+            c0, e0 = cpu_layer_fp32(W[0], l0_out)
+            comps["layer_fp32_b1_n64_s2"]["cpu_baseline"] = c0
+            comps["layer_fp32_b1_n64_s2"]["max_rel_err"] = e0
 
     k = head["dominant_kernel"]
     achieved = k["GBps"]
     traffic, traffic_src = measured_traffic(k["name"])
+    hbm_meas = peaks["hbm_read"]["GBps"]
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -645,12 +928,20 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "traffic_unit": "bytes per launch",
                      "traffic_source": traffic_src, "avg_launch_us": k["avg_launch_us"],
-                     "algorithmic_bytes_per_launch": k["algorithmic_bytes_per_launch"]},
+                     "algorithmic_bytes_per_launch": k["algorithmic_bytes_per_launch"],
+                     "algorithmic_bytes": "slot rows read + W_UK + W_UV (per-token terms apart)",
+                     "per_token_bytes_per_launch": k["per_token_bytes_per_launch"],
+                     "measured_peak": hbm_meas, "frac_of_measured": achieved / hbm_meas,
+                     "launch_floor_us": floor["us_per_launch"]},
         "plan": head["plan"],
         "cpu_baseline": cpu,
         "max_rel_err": err,
+        "max_rel_err_note": ("worst over the steps of each step's [b, H, d_h] output, over the sequences "
+                             "the oracle ran" if err is not None else None),
         "step_GBps": head["step_GBps"],
         "us_per_token": head["us_per_token"],
+        "bytes_per_step": head["bytes_per_step"],
+        "measured_peaks": peaks,
         "components": comps,
     }
     print(json.dumps(line), flush=True)

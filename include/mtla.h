@@ -475,6 +475,26 @@ int32_t mtla_prefill_backward(const mtla_dims* dims, int32_t n_tokens, const voi
 int32_t mtla_debug_stride_mask(int32_t n, int32_t s, uint8_t* mask, void* stream);
 int32_t mtla_debug_slot_limits(int32_t n, int32_t s, int32_t* hi, void* stream);
 
+/*
+ * Measurement hooks.  They compute no part of the method: they measure the
+ * rates this GPU achieves, against which the kernels' roofline fractions are
+ * reported beside the published peaks.
+ *   mtla_calib_stream_read: reads `bytes` bytes at src (device, 16-byte
+ *     aligned; bytes a positive multiple of 16) with `workgroups` workgroups
+ *     of 256 threads, eight 16-byte loads in flight per thread; writes one
+ *     word per wave to sink (device, workgroups * 4 uint32).
+ *   mtla_calib_mfma: `workgroups` workgroups of four waves; each wave runs
+ *     four independent chains of `iters` 32x32x16 MFMAs on register operands
+ *     (fp16 operands when f16 != 0, else bf16; fp32 accumulation) and writes
+ *     one float per thread to out (device, workgroups * 256 floats).
+ *     *flops (host, may be NULL) receives the multiply-add flops performed.
+ *   mtla_calib_empty: launches one kernel that does nothing (the launch
+ *     floor, for instance as a graph node).
+ */
+int32_t mtla_calib_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
+int32_t mtla_calib_mfma(int32_t f16, int32_t workgroups, int32_t iters, float* out, double* flops, void* stream);
+int32_t mtla_calib_empty(void* stream);
+
 #ifdef __cplusplus
 }
 #endif

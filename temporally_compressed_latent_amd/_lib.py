@@ -103,6 +103,9 @@ _SIGS = {
     "mtla_decode_plan": (_I, [_D, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "mtla_decode_step": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_decode_step_noalloc": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mtla_calib_stream_read": (_I, [_P, _SZ, _I, _P, _P]),
+    "mtla_calib_mfma": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
+    "mtla_calib_empty": (_I, [_P]),
     "mtla_absorb_query": (_I, [_D, _I, _P, _P, _P, _P, _P]),
     "mtla_decode_attention_workspace_bytes": (_I, [_D, ctypes.POINTER(_SZ)]),
     "mtla_decode_attention": (_I, [_D, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -310,6 +313,28 @@ def mtla_decode_step_noalloc(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w
         _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
         _tensor("out", out, (B, H, dims.d_h), st),
         _stream(stream)))
+
+
+def mtla_calib_stream_read(src, workgroups: int, sink, stream=None) -> None:
+    """Measurement hook: stream-read every byte of `src` (a device tensor)."""
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() < workgroups * 4 or sink.dtype != torch.int32:
+        raise ValueError("sink must be int32 with at least workgroups * 4 elements")
+    _check(_lib.mtla_calib_stream_read(src.data_ptr(), nbytes, workgroups, sink.data_ptr(), _stream(stream)))
+
+
+def mtla_calib_mfma(f16: bool, workgroups: int, iters: int, out, stream=None) -> float:
+    """Measurement hook: MFMA chains on registers; returns the flops performed."""
+    if out.numel() < workgroups * 256 or out.dtype != torch.float32:
+        raise ValueError("out must be float32 with at least workgroups * 256 elements")
+    flops = ctypes.c_double(0.0)
+    _check(_lib.mtla_calib_mfma(int(f16), workgroups, iters, out.data_ptr(), ctypes.byref(flops), _stream(stream)))
+    return flops.value
+
+
+def mtla_calib_empty(stream=None) -> None:
+    """Measurement hook: one kernel that does nothing."""
+    _check(_lib.mtla_calib_empty(_stream(stream)))
 
 
 def mtla_absorb_query(dims: MtlaDims, q_c, q_r, w_uk, q_lat, stream=None) -> None:

@@ -21,7 +21,7 @@ OUT = os.path.join(PKG, "libmtla.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["capi.hip", "merge.hip", "decode.hip", "prefill.hip", "layer.hip", "backward.hip"]
+SOURCES = ["capi.hip", "merge.hip", "decode.hip", "prefill.hip", "layer.hip", "backward.hip", "calib.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

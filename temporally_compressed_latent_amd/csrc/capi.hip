@@ -1189,3 +1189,30 @@ int32_t mtla_debug_slot_limits(int32_t n, int32_t s, int32_t* hi, void* stream) 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Measurement hooks
+// ---------------------------------------------------------------------------
+int32_t mtla_calib_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink, void* stream) {
+  if (!src || !aligned16(src)) return fail(MTLA_ERR_INVALID_ARG, "src is NULL or not 16-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0) return fail(MTLA_ERR_INVALID_ARG, "bytes=%zu is not a positive multiple of 16", bytes);
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(MTLA_ERR_INVALID_ARG, "workgroups=%d outside 1..2^20", workgroups);
+  CHECK_PTR_ALIGN(sink, 4);
+  return hip_status(mtla::launch_calib_read(src, bytes, workgroups, sink, static_cast<hipStream_t>(stream)),
+                    "stream-read launch");
+}
+
+int32_t mtla_calib_mfma(int32_t f16, int32_t workgroups, int32_t iters, float* out, double* flops, void* stream) {
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(MTLA_ERR_INVALID_ARG, "workgroups=%d outside 1..2^20", workgroups);
+  if (iters < 1) return fail(MTLA_ERR_INVALID_ARG, "iters=%d < 1", iters);
+  CHECK_PTR_ALIGN(out, 4);
+  if (flops) *flops = mtla::calib_mfma_flops(workgroups, iters);
+  return hip_status(mtla::launch_calib_mfma(f16 != 0, workgroups, iters, out, static_cast<hipStream_t>(stream)),
+                    "MFMA-loop launch");
+}
+
+int32_t mtla_calib_empty(void* stream) {
+  return hip_status(mtla::launch_calib_empty(static_cast<hipStream_t>(stream)), "empty-kernel launch");
+}

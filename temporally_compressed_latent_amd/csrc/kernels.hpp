@@ -230,4 +230,13 @@ struct PrefillAttnArgs {
 };
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t st);
 
+// Measurement kernels (calib.hip): streaming read of `bytes` (a multiple of
+// 16) by `workgroups` workgroups of 256 threads, one word per wave into sink;
+// MFMA chains on registers (`workgroups` x 4 waves, `iters` rounds of four
+// 32x32x16 products), one float per thread into out; an empty kernel.
+hipError_t launch_calib_read(const void* src, size_t bytes, int workgroups, uint32_t* sink, hipStream_t st);
+hipError_t launch_calib_mfma(bool f16, int workgroups, int iters, float* out, hipStream_t st);
+double calib_mfma_flops(int workgroups, int iters);
+hipError_t launch_calib_empty(hipStream_t st);
+
 }  // namespace mtla
