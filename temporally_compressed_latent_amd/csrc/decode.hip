@@ -1114,8 +1114,9 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restr
 //                       from a wave-private copy of the chunk's rows);
 //                   q~ and P enter both products as a bf16 high and low
 //                   part (16 significant bits): head h takes MFMA column h
-//                   for the high parts and column HG + h for the low parts,
-//                   and a quad-permute add folds the two columns together;
+//                   for the high parts and column HG + h for the low parts;
+//                   a quad-permute add folds the two score columns, and the
+//                   two O^T columns are added when the waves are combined;
 //                   the 8 waves' partial results are merged once, in wave
 //                   order;
 //   up-projection : out[h] = W_UV[h] o_lat[h] on MFMA, one 16-row tile of
@@ -1162,18 +1163,21 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
     uint16_t r[NWV][16][RP];
   };
   struct Combine {
-    float o[NWV][HG][DC];
+    float o[NWV][2 * HG][DC];  // per wave, O^T's high-part and low-part columns
     float m[NWV][HG];
     float l[NWV][HG];
     uint16_t ob[2][HG][DC];  // o_lat: bf16 hi, bf16 lo
     uint16_t zero[DC];
   };
+  // The absorb's partial sums are dead once q~ is formed, so the combine
+  // buffer overlaps them; it does not overlap the row buffers, so a wave can
+  // store its partial result as soon as its own attention is done.
   union Phases {
     Absorb ab;
-    Rows rw;
     Combine cb;
   };
   __shared__ __align__(16) Phases u;
+  __shared__ __align__(16) Rows rw;
   // q~ rows, scaled, bf16: high parts in rows 0..HG-1, low parts in rows
   // HG..2HG-1, row 2HG is zero
   __shared__ __align__(16) uint16_t sq[2 * HG + 1][QP];
@@ -1387,7 +1391,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   // Row buffer layout: the 16-byte chunk q of row r sits at chunk
   // q ^ ((r >> 2) & 1), so that the row writes (8 lanes = rows r .. r+7 at
   // one chunk) and the transposing reads both spread over the banks.
-  uint16_t* wb = &u.rw.r[wave][0][0];
+  uint16_t* wb = &rw.r[wave][0][0];
   uint16_t* wrow = wb + c16 * RP + 8 * (g ^ ((c16 >> 2) & 1));
   const uint16_t* vb = wb + (4 * g + (c16 >> 2)) * RP + 8 * (((c16 >> 1) & 1) ^ (g & 1)) + 4 * (c16 & 1);
   auto do_chunk = [&](int ci, uint4 (&r)[KSW]) {
@@ -1470,24 +1474,19 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   }
   // this wave's sum for head c16: the four lane groups, in a fixed order
   const float lw = cross_row_sum(l);
-  // column h of O^T gets the low-part column HG + h added
-#pragma unroll
-  for (int ct = 0; ct < CTW; ++ct) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[ct][i] += dpp_mov<kPartner>(acc[ct][i]);
-  }
-  __syncthreads();  // every wave is done with its row buffer
-  if (c16 < HG) {
+  // the wave's O^T columns (head h's high part at column h, low part at
+  // HG + h) and its running max and sum (the same in both columns)
+  if (c16 < 2 * HG) {
 #pragma unroll
     for (int ct = 0; ct < CTW; ++ct) *reinterpret_cast<f32x4*>(&u.cb.o[wave][c16][ct * 16 + 4 * g]) = acc[ct];
-    if (g == 0) {
+    if (g == 0 && c16 < HG) {
       u.cb.m[wave][c16] = m;
       u.cb.l[wave][c16] = lw;
     }
   }
   __syncthreads();
-  // o_lat[h, col]: the waves' partial results rescaled to a common max and
-  // summed in wave order, normalised, split into bf16 hi + lo
+  // o_lat[h, col]: the waves' partial results (high + low column) rescaled to
+  // a common max and summed in wave order, normalised, split into bf16 hi + lo
   if (tid < HG * DC) {
     const int h = tid / DC, col = tid % DC;
     float M = -INFINITY;
@@ -1498,7 +1497,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
     for (int w = 0; w < NWV; ++w) {
       const float f = fast_exp2(u.cb.m[w][h] - M);
       Ls += f * u.cb.l[w][h];
-      O += f * u.cb.o[w][h][col];
+      O += f * (u.cb.o[w][h][col] + u.cb.o[w][HG + h][col]);
     }
     const float v = O / Ls;
     const uint16_t hi = f32_to_bf16_bits(v);
