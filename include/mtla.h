@@ -300,6 +300,38 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
                      float* open_acc, void* out, void* workspace, size_t ws_bytes,
                      void* stream);
 
+/*
+ * Staged form of mtla_prefill (tokens 1..n_tokens, bf16 storage, a shape with
+ * the MFMA path: d_h 64 with d_r 32 or d_h 128 with d_r 64, d_c a multiple
+ * of 32, heads * d_h a multiple of 128; otherwise MTLA_ERR_UNSUPPORTED), for
+ * callers that want the intermediate tensors or time the stages apart.
+ * mtla_prefill runs exactly these three calls.  Page: "Multi-head Temporal
+ * Latent Attention", Key claims (paper Sec. 4.2 Fig. 2(c), Sec. 4.3 Eq. 17)
+ * and Method (2)-(3).
+ * mtla_prefill_partials: gates and cumulative in-block partial merges
+ *     P_j = sum_{k = s*floor((j-1)/s)+1}^{j} w_k x_k   (j = 1..n_tokens)
+ *   partials device [B, n_tokens, d_c + d_r] storage dtype, written (each
+ *   value rounded once from its fp32 sum); cache and open_acc written as
+ *   mtla_prefill leaves them; the other arguments as for mtla_prefill.
+ * mtla_prefill_keys: K^C_j,h = W_UK[h] P^c_j and V_j,h = W_UV[h] P^c_j for
+ *   every row j of partials:
+ *   k_c, v device [B, H, n_tokens, d_h] fp16 (IEEE binary16, rounded to
+ *   nearest even from fp32 accumulation), written.
+ * mtla_prefill_attention: the stride-masked attention of queries
+ *   1..n_tokens (query i attends the partial merges j = i and j = s*b for
+ *   b < ceil(i/s)) over those keys: q_c, q_r as for mtla_prefill; partials,
+ *   k_c, v from the two calls above (read only); out [B, n_tokens, H, d_h],
+ *   written.
+ * The fp16 keys and values bound their magnitudes by 65504.
+ */
+int32_t mtla_prefill_partials(const mtla_dims* dims, int32_t n_tokens, const void* c, const void* k_r,
+                              const float* w_hyp, const float* pe, int32_t pe_rows, void* cache, float* open_acc,
+                              void* partials, void* stream);
+int32_t mtla_prefill_keys(const mtla_dims* dims, int32_t n_tokens, const void* partials, const void* w_uk,
+                          const void* w_uv, void* k_c, void* v, void* stream);
+int32_t mtla_prefill_attention(const mtla_dims* dims, int32_t n_tokens, const void* q_c, const void* q_r,
+                               const void* partials, const void* k_c, const void* v, void* out, void* stream);
+
 /* Bytes of workspace mtla_prefill_at needs for n_tokens tokens after t0. */
 int32_t mtla_prefill_at_workspace_bytes(const mtla_dims* dims, int32_t t0, int32_t n_tokens,
                                         size_t* bytes);

@@ -103,6 +103,9 @@ _SIGS = {
     "mtla_decode_plan": (_I, [_D, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "mtla_decode_step": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_decode_step_noalloc": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mtla_prefill_partials": (_I, [_D, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
+    "mtla_prefill_keys": (_I, [_D, _I, _P, _P, _P, _P, _P, _P]),
+    "mtla_prefill_attention": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P]),
     "mtla_calib_stream_read": (_I, [_P, _SZ, _I, _P, _P]),
     "mtla_calib_mfma": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "mtla_calib_empty": (_I, [_P]),
@@ -312,6 +315,51 @@ def mtla_decode_step_noalloc(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w
         _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
         _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
         _tensor("out", out, (B, H, dims.d_h), st),
+        _stream(stream)))
+
+
+def mtla_prefill_partials(dims: MtlaDims, c, k_r, w_hyp, pe, cache, open_acc, partials, stream=None) -> None:
+    """Staged prefill, stage 1: partial merges P [B, N, W] (and the cache/open slot)."""
+    B, st = dims.batch, dims.torch_dtype
+    N = int(c.shape[1])
+    _check(_lib.mtla_prefill_partials(
+        ctypes.byref(dims), N,
+        _tensor("c", c, (B, N, dims.d_c), st),
+        _tensor("k_r", k_r, (B, N, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
+        _tensor("partials", partials, (B, N, dims.width), st),
+        _stream(stream)))
+
+
+def mtla_prefill_keys(dims: MtlaDims, partials, w_uk, w_uv, k_c, v, stream=None) -> None:
+    """Staged prefill, stage 2: K^C and V [B, H, N, d_h] fp16 of every partial merge."""
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    N = int(partials.shape[1])
+    _check(_lib.mtla_prefill_keys(
+        ctypes.byref(dims), N,
+        _tensor("partials", partials, (B, N, dims.width), st),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("k_c", k_c, (B, H, N, dims.d_h), torch.float16),
+        _tensor("v", v, (B, H, N, dims.d_h), torch.float16),
+        _stream(stream)))
+
+
+def mtla_prefill_attention(dims: MtlaDims, q_c, q_r, partials, k_c, v, out, stream=None) -> None:
+    """Staged prefill, stage 3: the stride-masked attention over the staged keys."""
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    N = int(q_c.shape[1])
+    _check(_lib.mtla_prefill_attention(
+        ctypes.byref(dims), N,
+        _tensor("q_c", q_c, (B, N, H, dims.d_h), st),
+        _tensor("q_r", q_r, (B, N, H, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("partials", partials, (B, N, dims.width), st),
+        _tensor("k_c", k_c, (B, H, N, dims.d_h), torch.float16),
+        _tensor("v", v, (B, H, N, dims.d_h), torch.float16),
+        _tensor("out", out, (B, N, H, dims.d_h), st),
         _stream(stream)))
 
 

@@ -695,6 +695,76 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
                       out, workspace, ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Staged prefill (t0 = 0): partial merges, K/V up-projection, attention.
+// ---------------------------------------------------------------------------
+namespace {
+int32_t check_staged_prefill(const mtla_dims* dims, int32_t n_tokens) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
+  if (!prefill_fast(dims))
+    return fail(MTLA_ERR_UNSUPPORTED, "the staged prefill needs bf16 storage and a shape with the MFMA path");
+  if (int64_t(n_tokens) > int64_t(dims->max_slots) * dims->stride_s)
+    return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d exceeds the cache capacity s*max_slots", n_tokens);
+  if (int64_t(dims->batch) * n_tokens * (dims->d_c + dims->d_r) * 4 > INT32_MAX)
+    return fail(MTLA_ERR_UNSUPPORTED, "prefill of %d x %d tokens exceeds the 2^31-byte partial-merge buffer",
+                dims->batch, n_tokens);
+  return MTLA_OK;
+}
+}  // namespace
+
+int32_t mtla_prefill_partials(const mtla_dims* dims, int32_t n_tokens, const void* c, const void* k_r,
+                              const float* w_hyp, const float* pe, int32_t pe_rows, void* cache, float* open_acc,
+                              void* partials, void* stream) {
+  int32_t st = check_staged_prefill(dims, n_tokens);
+  if (st != MTLA_OK) return st;
+  if (pe_rows < n_tokens) return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < n_tokens=%d", pe_rows, n_tokens);
+  if (dims->batch == 0 || n_tokens == 0) return ok();
+  CHECK_PTR(c);
+  if (dims->d_r > 0) CHECK_PTR(k_r);
+  CHECK_PTR_ALIGN(w_hyp, 4);
+  CHECK_PTR_ALIGN(pe, 4);
+  CHECK_PTR(cache);
+  CHECK_PTR(open_acc);
+  CHECK_PTR(partials);
+  mtla::MergeArgs m{dims->batch, n_tokens, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, pe_rows,
+                    nullptr, c, k_r, w_hyp, pe, cache, open_acc, nullptr, partials, 1};
+  m.wh_stride = gate_stride(dims);
+  return hip_status(mtla::launch_merge(m, dims->dtype, static_cast<hipStream_t>(stream)), "prefill merge launch");
+}
+
+int32_t mtla_prefill_keys(const mtla_dims* dims, int32_t n_tokens, const void* partials, const void* w_uk,
+                          const void* w_uv, void* k_c, void* v, void* stream) {
+  int32_t st = check_staged_prefill(dims, n_tokens);
+  if (st != MTLA_OK) return st;
+  if (dims->batch == 0 || n_tokens == 0) return ok();
+  CHECK_PTR(partials);
+  CHECK_PTR(w_uk);
+  CHECK_PTR(w_uv);
+  CHECK_PTR(k_c);
+  CHECK_PTR(v);
+  return hip_status(mtla::launch_prefill_kv(dims->batch, n_tokens, dims->heads, dims->d_h, dims->d_c, dims->d_r,
+                                            partials, w_uk, w_uv, k_c, v, true, static_cast<hipStream_t>(stream)),
+                    "up-projection launch");
+}
+
+int32_t mtla_prefill_attention(const mtla_dims* dims, int32_t n_tokens, const void* q_c, const void* q_r,
+                               const void* partials, const void* k_c, const void* v, void* out, void* stream) {
+  int32_t st = check_staged_prefill(dims, n_tokens);
+  if (st != MTLA_OK) return st;
+  if (dims->batch == 0 || n_tokens == 0) return ok();
+  CHECK_PTR(q_c);
+  if (dims->d_r > 0) CHECK_PTR(q_r);
+  CHECK_PTR(partials);
+  CHECK_PTR(k_c);
+  CHECK_PTR(v);
+  CHECK_PTR(out);
+  mtla::PrefillAttnArgs pa{dims->batch, n_tokens, dims->heads, dims->d_h, dims->d_c, dims->d_r, dims->stride_s, 0,
+                           dims->softmax_scale, q_c, q_r, k_c, v, partials, out};
+  return hip_status(mtla::launch_prefill_attn(pa, static_cast<hipStream_t>(stream)), "prefill attention launch");
+}
+
 int32_t mtla_prefill_at_workspace_bytes(const mtla_dims* dims, int32_t t0, int32_t n_tokens, size_t* bytes) {
   int32_t st = check_dims(dims);
   if (st != MTLA_OK) return st;

@@ -41,6 +41,8 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
+// v rounded to the nearest fp16 value (returned as fp32)
+__device__ __forceinline__ float f16_round(float v) { return static_cast<float>(static_cast<_Float16>(v)); }
 
 // An fp32 value as the sum of two bf16 values: hi = round(v), lo =
 // round(v - hi).  hi + lo carries v to 16 significant bits, so an MFMA that

@@ -215,6 +215,8 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   constexpr int VP = DH + 8;         // value tile pitch
   static_assert(DH % 32 == 0 && DR % 16 == 0, "shape");
   constexpr float kLazyLog2 = 8.f;
+  // bound on the running max's magnitude (log2 units), inside fp16's range
+  constexpr float kMaxRef = 60000.f;
 
   // two K/V tile buffers: the next tile is stored while this one is used
   __shared__ __align__(16) uint16_t sKb[2][TS * KP];
@@ -266,6 +268,15 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   // Queries (B operands, registers) and the diagonal key j = i as the initial
   // online-softmax state: m = score(i, i), l = 1, O = V_i.
   f16x8 qreg[NQ][KK];
+  // The running max m enters the score product as a 7th k-chunk: the query
+  // side holds -m (element 0 of lane group 0) and the key side a constant 1,
+  // so the MFMA returns s - m with no per-score subtraction or accumulator
+  // initialisation.  m is therefore kept fp16-representable, and the
+  // diagonal's weight is taken against that same value.
+  f16x8 qm[NQ];
+  f16x8 kone;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) kone[r] = static_cast<_Float16>(grp == 0 && r == 0 ? 1.f : 0.f);
   float m[NQ], lp[NQ];
   f32x16 acc[DT][NQ];
 #pragma unroll
@@ -299,8 +310,12 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
       qreg[t][kk] = __builtin_bit_cast(f16x8, qsc);
     }
     dpart += __shfl_xor(dpart, 32, 64);
-    m[t] = dpart * qk_scale;
-    lp[t] = grp == 0 ? 1.f : 0.f;
+    const float sii = dpart * qk_scale;
+    m[t] = f16_round(fminf(fmaxf(sii, -kMaxRef), kMaxRef));
+    const float pii = fast_exp2(sii - m[t]);
+    lp[t] = grp == 0 ? pii : 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) qm[t][r] = static_cast<_Float16>(grp == 0 && r == 0 ? -m[t] : 0.f);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -308,10 +323,10 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
         uint2 v2 = uint2{0u, 0u};
         if (qok)
           v2 = *reinterpret_cast<const uint2*>(vv + static_cast<size_t>(qi) * DH + 32 * dt + 8 * j + 4 * grp);
-        acc[dt][t][4 * j + 0] = f16_bits_to_f32(static_cast<uint16_t>(v2.x & 0xffffu));
-        acc[dt][t][4 * j + 1] = f16_bits_to_f32(static_cast<uint16_t>(v2.x >> 16));
-        acc[dt][t][4 * j + 2] = f16_bits_to_f32(static_cast<uint16_t>(v2.y & 0xffffu));
-        acc[dt][t][4 * j + 3] = f16_bits_to_f32(static_cast<uint16_t>(v2.y >> 16));
+        acc[dt][t][4 * j + 0] = pii * f16_bits_to_f32(static_cast<uint16_t>(v2.x & 0xffffu));
+        acc[dt][t][4 * j + 1] = pii * f16_bits_to_f32(static_cast<uint16_t>(v2.x >> 16));
+        acc[dt][t][4 * j + 2] = pii * f16_bits_to_f32(static_cast<uint16_t>(v2.y & 0xffffu));
+        acc[dt][t][4 * j + 3] = pii * f16_bits_to_f32(static_cast<uint16_t>(v2.y >> 16));
       }
     }
   }
@@ -385,9 +400,11 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
       const uint32_t w4[4] = {pr[i].x, pr[i].y, pr[i].z, pr[i].w};
       uint32_t h4[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        h4[k] = static_cast<uint32_t>(f32_to_f16_bits(__uint_as_float(w4[k] << 16))) |
-                (static_cast<uint32_t>(f32_to_f16_bits(__uint_as_float(w4[k] & 0xffff0000u))) << 16);
+      for (int k = 0; k < 4; ++k) {
+        const f16x2 h = {static_cast<_Float16>(__uint_as_float(w4[k] << 16)),
+                         static_cast<_Float16>(__uint_as_float(w4[k] & 0xffff0000u))};
+        h4[k] = __builtin_bit_cast(uint32_t, h);
+      }
       *reinterpret_cast<uint4*>(sKb[buf] + lds_r[i]) = uint4{h4[0], h4[1], h4[2], h4[3]};
     }
 #pragma unroll
@@ -415,14 +432,12 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 
     if (j0 < nk_w) {
       // S^T = K Q^T - m: sc[rt][t][i] = score(slot j0 + 32rt + 8(i/4) + 4grp + i%4,
-      // query t) - m[t], in log2 units
+      // query t) - m[t], in log2 units (the last k-chunk is 1 x -m)
       f32x16 sc[2][NQ];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int t = 0; t < NQ; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[rt][t][i] = -m[t];
+        for (int t = 0; t < NQ; ++t) sc[rt][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kone, qm[t], f32x16{}, 0, 0, 0);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -460,9 +475,13 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
         float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
         if (__any(mx > kLazyLog2)) {
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          const float d = fmaxf(mx, 0.f);
+          // the new reference, fp16-representable, and the exact shift to it
+          const float mnew = f16_round(fminf(m[t] + fmaxf(mx, 0.f), kMaxRef));
+          const float d = mnew - m[t];
           const float alpha = fast_exp2(-d);
-          m[t] += d;
+          m[t] = mnew;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) qm[t][r] = static_cast<_Float16>(grp == 0 && r == 0 ? -mnew : 0.f);
           lp[t] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) acc[dt][t] *= alpha;
@@ -535,11 +554,11 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           uint16_t* dst = out + ((static_cast<size_t>(b) * N + qi) * H + h) * DH + 32 * dt + 8 * j + 4 * grp;
-          const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][4 * j + 0] * inv)) |
-                              (static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][4 * j + 1] * inv)) << 16);
-          const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][4 * j + 2] * inv)) |
-                              (static_cast<uint32_t>(f32_to_bf16_bits(acc[dt][t][4 * j + 3] * inv)) << 16);
-          *reinterpret_cast<uint2*>(dst) = uint2{w0, w1};
+          const bf16x2 p0 = {static_cast<__bf16>(acc[dt][t][4 * j + 0] * inv),
+                             static_cast<__bf16>(acc[dt][t][4 * j + 1] * inv)};
+          const bf16x2 p1 = {static_cast<__bf16>(acc[dt][t][4 * j + 2] * inv),
+                             static_cast<__bf16>(acc[dt][t][4 * j + 3] * inv)};
+          *reinterpret_cast<uint2*>(dst) = uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
         }
       }
     }

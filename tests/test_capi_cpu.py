@@ -25,7 +25,7 @@ def dims(**kw):
 
 def test_exports_every_header_symbol():
     syms = m.header_symbols()
-    assert len(syms) == 32
+    assert len(syms) == 35
     for s in syms:
         assert hasattr(m.lib(), s), s
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
@@ -348,3 +348,15 @@ def test_no_environment_reads_in_the_library():
     for path in glob.glob(os.path.join(os.path.dirname(m.LIB_PATH), "csrc", "*")):
         with open(path) as f:
             assert "getenv" not in f.read(), path
+
+
+def test_staged_prefill_needs_the_mfma_path():
+    """The staged prefill exposes the MFMA path's fp16 keys: fp32 storage or a
+    shape without that path is MTLA_ERR_UNSUPPORTED, checked on the host."""
+    L = m.lib()
+    for d in (dims(dtype=m.MTLA_FP32), dims(d_h=48)):
+        assert L.mtla_prefill_keys(ctypes.byref(d), 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == m.MTLA_ERR_UNSUPPORTED
+        assert L.mtla_prefill_attention(ctypes.byref(d), 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+            m.MTLA_ERR_UNSUPPORTED
+    assert L.mtla_prefill_partials(ctypes.byref(dims()), 16, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, None) == \
+        m.MTLA_ERR_INVALID_ARG          # pe_rows < n_tokens

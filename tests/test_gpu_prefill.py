@@ -146,3 +146,30 @@ def test_prefill_at_then_decode_continues():
     cont = host(g.decode_loop(T, start=121))
     want, _ = oracle_ref.loop_outputs(inp, B, T, s, g.d.softmax_scale)
     oracle_ref.assert_steps(cont, want[:, 121:], 1e-2)
+
+
+@pytest.mark.parametrize("shape,s,B,N", [("st", 3, 2, 300), ("llm", 2, 1, 160), ("st", 1, 3, 97)])
+def test_staged_prefill_equals_one_call(shape, s, B, N):
+    """mtla_prefill_partials -> mtla_prefill_keys -> mtla_prefill_attention
+    gives the bits of one mtla_prefill call (outputs, slot cache, open-slot
+    state): the same kernels on the same data."""
+    import temporally_compressed_latent_amd as m
+    inp, a = make_case(shape, 16, B, N, s, "bf16")
+    _, b_ = make_case(shape, 16, B, N, s, "bf16")
+    one = a.prefill(N)
+    d = b_.d
+    P = torch.empty(B, N, d.width, dtype=torch.bfloat16, device=DEV)
+    kc = torch.empty(B, d.heads, N, d.d_h, dtype=torch.float16, device=DEV)
+    v = torch.empty_like(kc)
+    out = torch.empty_like(one)
+    m.mtla_prefill_partials(d, b_.c[:, :N].contiguous(), b_.k_r[:, :N].contiguous(), b_.w_hyp, b_.pe, b_.cache,
+                            b_.open_acc, P)
+    m.mtla_prefill_keys(d, P, b_.w_uk, b_.w_uv, kc, v)
+    m.mtla_prefill_attention(d, b_.q_c[:, :N].contiguous(), b_.q_r[:, :N].contiguous(), P, kc, v, out)
+    assert torch.equal(bits(out), bits(one))
+    assert torch.equal(bits(a.cache), bits(b_.cache))
+    assert torch.equal(a.open_state(N), b_.open_state(N))
+    # the staged keys are K^C = W_UK P^c and V = W_UV P^c of the staged partial merges
+    Pc = P.float()[..., :d.d_c]
+    want_k = torch.einsum("hek,bnk->bhne", b_.w_uk.float(), Pc)
+    assert (kc.float() - want_k).abs().max().item() <= 2e-3 * want_k.abs().max().item()
