@@ -76,5 +76,48 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+# Host-side AddressSanitizer build of the same sources: the C-ABI shim's
+# argument checks, workspace sizing and dispatch run instrumented (device code
+# is built as usual).  Used by tests/test_capi_asan.py with the ASan runtime
+# preloaded.
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+ASAN_OUT = os.path.join(ASAN_DIR, "libmtla_asan.so")
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime matching hipcc's compiler."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    for cand in sorted(glob.glob(os.path.join(root, "lib", "llvm", "lib", "clang", "*", "lib", "linux",
+                                              "libclang_rt.asan-x86_64.so"))
+                       + sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))):
+        return cand
+    raise RuntimeError("libclang_rt.asan-x86_64.so not found next to hipcc")
+
+
+def build_host_asan(verbose: bool = False) -> str:
+    os.makedirs(ASAN_DIR, exist_ok=True)
+
+    def comp(src):
+        obj = os.path.join(ASAN_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *ASAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (host ASan) failed on {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(comp, SOURCES))
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-shared-libsan", "-o", ASAN_OUT, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (host ASan) failed:\n{r.stdout}\n{r.stderr}")
+    return ASAN_OUT
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "asan" in sys.argv:
+        print(build_host_asan(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
