@@ -14,7 +14,6 @@ namespace mtla {
 namespace {
 
 constexpr int kReadThreads = 256;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kReadInFlight = 8;
 
 // Thread i reads 16-byte chunks i, i + G, i + 2G, ... (G = threads in the

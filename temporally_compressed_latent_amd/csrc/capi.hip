@@ -353,16 +353,21 @@ int32_t mtla_decode_attention_workspace_bytes(const mtla_dims* dims, size_t* byt
 
 namespace {
 
+mtla::Partials attn_partials(void* ws, const AttnWs& w) {
+  return mtla::Partials{reinterpret_cast<float*>(at(ws, w.pm)), reinterpret_cast<float*>(at(ws, w.pl)),
+                        reinterpret_cast<float*>(at(ws, w.pacc))};
+}
+
+// Latent attention into o_lat; with merge_splits false (MFMA path, several
+// splits) the split partials are left in the workspace for the caller.
 hipError_t run_decode_attention(const mtla_dims* dims, const int32_t* pos, const float* q_lat,
                                 const void* cache, float* o_lat, void* ws, const AttnWs& w,
-                                hipStream_t s) {
+                                hipStream_t s, bool merge_splits = true) {
   const int splits = decode_splits(dims);
-  mtla::Partials p{reinterpret_cast<float*>(at(ws, w.pm)), reinterpret_cast<float*>(at(ws, w.pl)),
-                   reinterpret_cast<float*>(at(ws, w.pacc))};
   mtla::AttendArgs a{dims->batch, 0, dims->heads, dims->d_c, dims->d_r, dims->stride_s,
-                     dims->max_slots, splits, dims->softmax_scale, pos, q_lat, cache, nullptr, p,
-                     o_lat};
-  return decode_fast(dims) ? mtla::launch_decode_mfma(a, s)
+                     dims->max_slots, splits, dims->softmax_scale, pos, q_lat, cache, nullptr,
+                     attn_partials(ws, w), o_lat};
+  return decode_fast(dims) ? mtla::launch_decode_mfma(a, s, merge_splits)
                            : mtla::launch_attend_portable(a, dims->dtype, s);
 }
 
@@ -411,19 +416,33 @@ mtla::StepArgs step_args(const mtla_dims* d, const int32_t* pos, const void* c, 
                         static_cast<uint16_t*>(cache), open_acc, static_cast<uint16_t*>(out)};
 }
 
-// absorb -> latent attention (-> split merge) -> up-projection
+// absorb -> latent attention (-> split merge) -> up-projection.  With a
+// merge (`merge` non-null: the token of a decode step) whose shapes allow it,
+// the merge and the absorb run as one launch.
 hipError_t run_decode_pipeline(const mtla_dims* dims, const int32_t* pos, const void* q_c,
                                const void* q_r, const void* w_uk, const void* w_uv,
                                const void* cache, void* out, void* workspace, const DecodeWs& ws,
-                               hipStream_t s) {
+                               hipStream_t s, const mtla::MergeArgs* merge = nullptr) {
   const int B = dims->batch, H = dims->heads;
   float* q_lat = reinterpret_cast<float*>(at(workspace, ws.qlat));
   float* o_lat = reinterpret_cast<float*>(at(workspace, ws.olat));
-  hipError_t e = mtla::launch_absorb(B, H, dims->d_h, dims->d_c, dims->d_r, q_c, q_r, w_uk, q_lat,
-                                     dims->dtype, s);
+  hipError_t e;
+  if (merge && mtla::merge_absorb_supported(dims->d_h, dims->d_c, dims->dtype)) {
+    e = mtla::launch_merge_absorb(*merge, H, dims->d_h, dims->d_r, q_c, q_r, w_uk, q_lat, s);
+  } else {
+    if (merge && (e = mtla::launch_merge(*merge, dims->dtype, s)) != hipSuccess) return e;
+    e = mtla::launch_absorb(B, H, dims->d_h, dims->d_c, dims->d_r, q_c, q_r, w_uk, q_lat, dims->dtype, s);
+  }
   if (e != hipSuccess) return e;
-  e = run_decode_attention(dims, pos, q_lat, cache, o_lat, workspace, ws.attn, s);
+  // several MFMA splits: their merge runs inside the up-projection's launch
+  const int splits = decode_splits(dims);
+  const bool combine = decode_fast(dims) && mtla::combine_up_project_supported(dims->d_h, dims->d_c, splits,
+                                                                              dims->dtype);
+  e = run_decode_attention(dims, pos, q_lat, cache, o_lat, workspace, ws.attn, s, !combine);
   if (e != hipSuccess) return e;
+  if (combine)
+    return mtla::launch_combine_up_project(B, H, dims->d_h, dims->d_c, splits, attn_partials(workspace, ws.attn),
+                                           w_uv, out, s);
   return mtla::launch_up_project(B, H, dims->d_h, dims->d_c, o_lat, w_uv, out, dims->dtype, s);
 }
 
@@ -512,14 +531,14 @@ static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const
   mtla::MergeArgs m{dims->batch, 1, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, pe_rows,
                     pos, c, k_r, w_hyp, pe, cache, open_acc, nullptr, nullptr};
   m.wh_stride = gate_stride(dims);
-  hipError_t e = mtla::launch_merge(m, dims->dtype, s);
-  if (e != hipSuccess) return hip_status(e, "merge launch");
   if (decode_fused(dims)) {
+    hipError_t e = mtla::launch_merge(m, dims->dtype, s);
+    if (e != hipSuccess) return hip_status(e, "merge launch");
     const mtla::StepArgs a = step_args(dims, pos, nullptr, nullptr, nullptr, nullptr, 0, q_c, q_r, w_uk, w_uv,
                                        cache, nullptr, out, 0);
     return hip_status(mtla::launch_decode_step(a, s), "decode step launch");
   }
-  return hip_status(run_decode_pipeline(dims, pos, q_c, q_r, w_uk, w_uv, cache, out, workspace, ws, s),
+  return hip_status(run_decode_pipeline(dims, pos, q_c, q_r, w_uk, w_uv, cache, out, workspace, ws, s, &m),
                     "decode launch");
 }
 

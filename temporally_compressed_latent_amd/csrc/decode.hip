@@ -17,6 +17,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "merge_body.hpp"
 
 namespace mtla {
 
@@ -204,12 +205,12 @@ __global__ __launch_bounds__(256) void split_merge_kernel(int H, int d_c, int sp
   for (int k = 0; k < splits; ++k) M = fmaxf(M, p.m[base + static_cast<size_t>(k) * H]);
   float L = 0.f;
   for (int k = 0; k < splits; ++k)
-    L += p.l[base + static_cast<size_t>(k) * H] * expf(p.m[base + static_cast<size_t>(k) * H] - M);
+    L = fmaf(p.l[base + static_cast<size_t>(k) * H], expf(p.m[base + static_cast<size_t>(k) * H] - M), L);
   for (int e = threadIdx.x; e < d_c; e += blockDim.x) {
     float v = 0.f;
     for (int k = 0; k < splits; ++k) {
       const size_t pk = base + static_cast<size_t>(k) * H;
-      v += p.acc[pk * d_c + e] * expf(p.m[pk] - M);
+      v = fmaf(p.acc[pk * d_c + e], expf(p.m[pk] - M), v);
     }
     o_lat[(static_cast<size_t>(r) * H + h) * d_c + e] = v / L;
   }
@@ -612,12 +613,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(AttendArgs a) {
 // ---------------------------------------------------------------------------
 // Split-K latent attention for long caches of the 576-wide row (d_c = 512,
 // d_R = 64).  One workgroup of 8 waves per (split, sequence), all heads
-// (HT*16 MFMA rows), 64-slot tiles.
+// (HT*16 MFMA rows), 64-slot tiles; split k of S takes tiles k, k+S, ...
 //
-// The cache streams HBM -> LDS through buffer loads that write LDS directly
-// (no staging registers), double buffered: the loads of tile it+2 go out as
-// soon as every wave is done with tile it, so one tile (74 KB) is always in
-// flight.  The loads are waited for by count (the compiler does not track
+// The cache streams HBM -> LDS through non-temporal buffer loads that write
+// LDS directly (no staging registers), double buffered: the loads of the
+// split's tile after next go out as soon as every wave is done with the
+// current one, so one tile (74 KB) is always in flight.  The loads are waited for by count (the compiler does not track
 // them, see buffer_load_lds16); barriers inside the tile loop wait only for
 // LDS operations.
 //
@@ -668,8 +669,10 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(AttendArgs a) {
       if (n > a.max_slots) n = 0;
     }
   }
-  const int lo = static_cast<int>((static_cast<long long>(split) * n) / nsplit);
-  const int hi = static_cast<int>((static_cast<long long>(split + 1) * n) / nsplit);
+  // split k takes the sequence's 64-slot tiles k, k + nsplit, k + 2 nsplit,
+  // ... (interleaved: the workgroups of a sequence read neighbouring rows at
+  // about the same time)
+  const int lo = split * TS, hi = n, step = nsplit * TS;
 
   // rows of this sequence up to hi; past them the loads read zero
   const uint16_t* rows = static_cast<const uint16_t*>(a.cache) + static_cast<size_t>(b) * a.max_slots * W;
@@ -690,7 +693,7 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(AttendArgs a) {
   };
 
   if (lo < hi) issue_tile(lo, kb0);
-  if (lo + TS < hi) issue_tile(lo + TS, kb1);
+  if (lo + step < hi) issue_tile(lo + step, kb1);
 
   // this wave's score item and its query rows (A operand, bf16, scaled)
   const int item_ht = wave % HT, item_sg = wave / HT;
@@ -723,11 +726,12 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(AttendArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) l[i] = 0.f;
 
-  // one tile: `kt` holds slots j0 .. j0+TS-1; afterwards it receives slots
-  // j0+2TS .. (loads issued once every wave is done with it)
+  // one tile: `kt` holds slots j0 .. j0+TS-1; afterwards it receives the
+  // split's tile after next, j0 + 2 step .. (loads issued once every wave is
+  // done with it)
   auto tile = [&](int j0, uint16_t* kt) {
-    // at most one later tile (j0+TS) of this wave's loads may still be in flight
-    if (j0 + TS < hi)
+    // at most one later tile (j0+step) of this wave's loads may still be in flight
+    if (j0 + step < hi)
       asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -802,11 +806,11 @@ __global__ __launch_bounds__(512) void decode_stream_kernel(AttendArgs a) {
       }
     }
     lds_barrier();  // every wave is done with kt (and with sp, red)
-    if (j0 + 2 * TS < hi) issue_tile(j0 + 2 * TS, kt);
+    if (j0 + 2 * step < hi) issue_tile(j0 + 2 * step, kt);
   };
-  for (int j0 = lo; j0 < hi; j0 += 2 * TS) {
+  for (int j0 = lo; j0 < hi; j0 += 2 * step) {
     tile(j0, kb0);
-    if (j0 + TS < hi) tile(j0 + TS, kb1);
+    if (j0 + step < hi) tile(j0 + step, kb1);
   }
 
   // softmax denominators: sum over the slot lanes, then over the slot groups
@@ -1550,25 +1554,28 @@ __device__ __forceinline__ void reduce4_store(float (*part)[32 * 33], const f32x
   for (int i = 0; i < 16; ++i) part[wave][(8 * (i / 4) + 4 * grp + (i % 4)) * 33 + c32] = acc[i];
 }
 
-// q~[r, h, n] = sum_e q_c[r, h, e] W_UK[h, e, n] for n in one 32-column tile.
-// W_UK is row-major in e, so its tile (d_h rows x 32 columns) is staged in
-// LDS and read by transposing reads, which take the contraction rows in the
-// order 16 c + 4 grp + r (r < 4), 16 c + 8 + 4 grp + (r - 4); the query
-// fragments are loaded in that same order.  Wave w takes the 16-row chunks
-// c = w, w + 4, ...  The rope part of the query is copied beside it.
-__global__ __launch_bounds__(256) void absorb_mfma_kernel(int R, int H, int d_h, int d_c, int d_r,
-                                                          const uint16_t* __restrict__ q_c,
-                                                          const uint16_t* __restrict__ q_r,
-                                                          const uint16_t* __restrict__ w_uk,
-                                                          float* __restrict__ qbuf) {
-  constexpr int WP = 32 + 8;  // LDS pitch of the weight tile (elements)
-  __shared__ __align__(16) uint16_t sW[kAbsorbMaxDh * WP];
+// q~[r, h, n] = sum_e q_c[r, h, e] W_UK[h, e, n] for n in the 32-column tile
+// n0, head h and the 32 rows from r0 (one workgroup of 256 threads).  W_UK is
+// row-major in e, so its tile (d_h rows x 32 columns) is staged in LDS and
+// read by transposing reads, which take the contraction rows in the order
+// 16 c + 4 grp + r (r < 4), 16 c + 8 + 4 grp + (r - 4); the query fragments
+// are loaded in that same order.  Wave w takes the 16-row chunks c = w, w + 4,
+// ...  The n0 == 0 tile also copies the rope part of the query beside it.
+// Every load of the tile is issued before any is waited for.  The weight
+// tile is the launch's dynamic LDS (absorb_lds_bytes(d_h)), so that a
+// workgroup takes only what its d_h needs.
+constexpr int kAbsorbPitch = 32 + 8;  // LDS pitch of the weight tile (elements)
+inline size_t absorb_lds_bytes(int d_h) { return static_cast<size_t>(d_h) * kAbsorbPitch * sizeof(uint16_t); }
+__device__ __forceinline__ void absorb_tile(int n0, int h, int r0, int R, int H, int d_h, int d_c, int d_r,
+                                            const uint16_t* __restrict__ q_c,
+                                            const uint16_t* __restrict__ q_r,
+                                            const uint16_t* __restrict__ w_uk, float* __restrict__ qbuf) {
+  constexpr int WP = kAbsorbPitch;
+  extern __shared__ __align__(16) uint16_t sW[];
   __shared__ float part[4][32 * 33];
-  const int n0 = blockIdx.x * 32, h = blockIdx.y, r0 = blockIdx.z * 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5, c32 = lane & 31;
   const int W = d_c + d_r;
-  // this wave's query fragments for chunks c = wave + 4 u (u < d_h / 64 <= 4),
-  // loaded first: they do not wait for the weight tile
+  // this wave's query fragments for chunks c = wave + 4 u (u < d_h / 64 <= 4)
   const int r = min(r0 + c32, R - 1);
   const uint16_t* qrow = q_c + (static_cast<size_t>(r) * H + h) * d_h;
   constexpr int UA = kAbsorbMaxDh / 64;
@@ -1581,11 +1588,30 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int R, int H, int d_h,
     const uint2 hi = *reinterpret_cast<const uint2*>(qrow + 16 * c + 8 + 4 * grp);
     qa[u] = uint4{lo.x, lo.y, hi.x, hi.y};
   }
-  // weight tile: d_h rows x 4 chunks of 8 columns
-  for (int c = tid; c < d_h * 4; c += 256) {
+  // weight tile: d_h rows x 4 chunks of 8 columns, thread tid takes chunks
+  // tid, tid + 256, ... (all loads first, then the LDS stores)
+  constexpr int WC = kAbsorbMaxDh * 4 / 256;
+  uint4 wv[WC];
+#pragma unroll
+  for (int k = 0; k < WC; ++k) {
+    const int c = min(tid + 256 * k, d_h * 4 - 1);
     const int e = c >> 2, cc = c & 3;
-    *reinterpret_cast<uint4*>(sW + e * WP + cc * 8) =
-        *reinterpret_cast<const uint4*>(w_uk + (static_cast<size_t>(h) * d_h + e) * d_c + n0 + cc * 8);
+    wv[k] = *reinterpret_cast<const uint4*>(w_uk + (static_cast<size_t>(h) * d_h + e) * d_c + n0 + cc * 8);
+  }
+  // rope part of the query (tile n0 == 0): thread tid takes 8-element chunk
+  // tid of the 32 rows x d_r / 8 chunks (one pass for d_r <= 64; wider rope
+  // parts are copied by a loop at the end)
+  const int rch = d_r / 8;
+  const bool rope = n0 == 0 && 32 * rch <= 256 && tid < 32 * rch;
+  const int rr_r = rope ? tid / rch : 0, re_r = rope ? (tid % rch) * 8 : 0;
+  const bool rope_row = rope && r0 + rr_r < R;
+  uint4 rv = uint4{0u, 0u, 0u, 0u};
+  if (rope_row)
+    rv = *reinterpret_cast<const uint4*>(q_r + (static_cast<size_t>(r0 + rr_r) * H + h) * d_r + re_r);
+#pragma unroll
+  for (int k = 0; k < WC; ++k) {
+    const int c = tid + 256 * k;
+    if (c < d_h * 4) *reinterpret_cast<uint4*>(sW + (c >> 2) * WP + (c & 3) * 8) = wv[k];
   }
   __syncthreads();
   f32x16 acc;
@@ -1603,14 +1629,18 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int R, int H, int d_h,
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[u]), b, acc, 0, 0, 0);
   }
   reduce4_store(part, acc, wave, grp, c32);
-  __syncthreads();
-  for (int idx = tid; idx < 32 * 32; idx += 256) {
-    const int rr = idx >> 5, col = idx & 31;
-    if (r0 + rr >= R) continue;
-    const float v = (part[0][rr * 33 + col] + part[1][rr * 33 + col]) + (part[2][rr * 33 + col] + part[3][rr * 33 + col]);
-    qbuf[(static_cast<size_t>(r0 + rr) * H + h) * W + n0 + col] = v;
+  if (rope_row) {
+    float* dst = qbuf + (static_cast<size_t>(r0 + rr_r) * H + h) * W + d_c + re_r;
+    const uint32_t w4[4] = {rv.x, rv.y, rv.z, rv.w};
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_bits_to_f32(static_cast<uint16_t>(w4[j] & 0xffffu));
+      v[2 * j + 1] = bf16_bits_to_f32(static_cast<uint16_t>(w4[j] >> 16));
+    }
+    store8(dst, v);
   }
-  if (blockIdx.x == 0) {
+  if (n0 == 0 && 32 * rch > 256) {
     for (int idx = tid; idx < 32 * d_r; idx += 256) {
       const int rr = idx / d_r, e = idx % d_r;
       if (r0 + rr < R)
@@ -1618,38 +1648,94 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int R, int H, int d_h,
             bf16_bits_to_f32(q_r[(static_cast<size_t>(r0 + rr) * H + h) * d_r + e]);
     }
   }
+  __syncthreads();
+  for (int idx = tid; idx < 32 * 32; idx += 256) {
+    const int rr = idx >> 5, col = idx & 31;
+    if (r0 + rr >= R) continue;
+    const float v = (part[0][rr * 33 + col] + part[1][rr * 33 + col]) + (part[2][rr * 33 + col] + part[3][rr * 33 + col]);
+    qbuf[(static_cast<size_t>(r0 + rr) * H + h) * W + n0 + col] = v;
+  }
 }
 
-// out[r, h, e] = sum_k W_UV[h, e, k] o_lat[r, h, k] for e in one 32-row tile
-// of W_UV.  Both operands are contiguous in k, so every lane loads its
-// fragments directly; the fp32 o_lat enters as a pair of bf16 operands whose
-// sum carries it to ~16 significant bits.  Wave w takes the 16-wide k-steps
-// w, w + 4, ...
-__global__ __launch_bounds__(256) void up_project_mfma_kernel(int R, int H, int d_h, int d_c,
-                                                              const float* __restrict__ o_lat,
-                                                              const uint16_t* __restrict__ w_uv,
-                                                              uint16_t* __restrict__ out) {
-  __shared__ float part[4][32 * 33];
-  const int e0 = blockIdx.x * 32, h = blockIdx.y, r0 = blockIdx.z * 32;
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(int R, int H, int d_h, int d_c, int d_r,
+                                                          const uint16_t* __restrict__ q_c,
+                                                          const uint16_t* __restrict__ q_r,
+                                                          const uint16_t* __restrict__ w_uk,
+                                                          float* __restrict__ qbuf) {
+  absorb_tile(blockIdx.x * 32, blockIdx.y, blockIdx.z * 32, R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf);
+}
+
+// The first step of the staged decode step, in one launch: workgroups 0..B-1
+// merge token pos[b] of sequence b into its slot (merge_blocks, one block per
+// workgroup, the state written in place), the others are absorb tiles
+// (n-tile fastest, then head, then row block).  The two parts touch disjoint
+// memory: the merge writes the cache and open_acc, the absorb reads the
+// queries and W_UK and writes q~.
+__global__ __launch_bounds__(256, 5) void merge_absorb_kernel(MergeArgs m, int H, int d_h, int d_r,
+                                                           const uint16_t* __restrict__ q_c,
+                                                           const uint16_t* __restrict__ q_r,
+                                                           const uint16_t* __restrict__ w_uk,
+                                                           float* __restrict__ qbuf) {
+  const int L = blockIdx.x;
+  if (L < m.B) {
+    merge_blocks<uint16_t, true>(m, L, 0, 1, 1);
+    return;
+  }
+  const int t = L - m.B, nx = m.d_c / 32;
+  absorb_tile((t % nx) * 32, (t / nx) % H, (t / (nx * H)) * 32, m.B, H, d_h, m.d_c, d_r, q_c, q_r, w_uk, qbuf);
+}
+
+// out[r, h, e] = sum_k W_UV[h, e, k] o_lat[r, h, k] for e in the 32-row tile
+// e0 of W_UV, head h and the 32 rows from r0 (one workgroup of 256 threads).
+// Both operands are contiguous in k, so every lane loads its fragments
+// directly; the fp32 o_lat enters as a pair of bf16 operands whose sum carries
+// it to ~16 significant bits.  Wave w takes the 16-wide k-steps w, w + 4, ...
+// The latent rows come from `orow_of(r)`: a pointer to o_lat[r, h, 8 grp],
+// in global memory or in LDS.
+// The W_UV fragments of one round of k-steps (see up_project_rows), loaded
+// ahead of the latent rows where those are still being formed.
+constexpr int kUpRound = 8;
+struct UpW {
+  uint4 bw[kUpRound];
+};
+__device__ __forceinline__ const uint16_t* up_w_row(const uint16_t* w_uv, int e0, int h, int d_h, int d_c) {
+  const int lane = threadIdx.x & 63;
+  return w_uv + (static_cast<size_t>(h) * d_h + e0 + (lane & 31)) * d_c + 8 * (lane >> 5);
+}
+__device__ __forceinline__ void up_w_round(UpW& w, const uint16_t* wrow, int kb, int d_c) {
+#pragma unroll
+  for (int u = 0; u < kUpRound; ++u) w.bw[u] = *reinterpret_cast<const uint4*>(wrow + min(kb + 64 * u, d_c - 16));
+}
+
+// The first round's W fragments may come preloaded (`first`, for
+// kb = 16 * wave).
+template <typename RowOf>
+__device__ __forceinline__ void up_project_rows(int e0, int h, int r0, int R, int H, int d_h, int d_c,
+                                                RowOf orow_of, const uint16_t* __restrict__ w_uv,
+                                                uint16_t* __restrict__ out, float (*part)[32 * 33],
+                                                const UpW* first = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5, c32 = lane & 31;
-  const int r = min(r0 + c32, R - 1);
-  const float* orow = o_lat + (static_cast<size_t>(r) * H + h) * d_c + 8 * grp;
-  const uint16_t* wrow = w_uv + (static_cast<size_t>(h) * d_h + e0 + c32) * d_c + 8 * grp;
+  const float* orow = orow_of(c32, grp);
+  const uint16_t* wrow = up_w_row(w_uv, e0, h, d_h, d_c);
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   // rounds of UP k-steps with all their loads in flight; steps past d_c load
   // a valid address and contribute zero
-  constexpr int UP = 8;
+  constexpr int UP = kUpRound;
   for (int kb = 16 * wave; kb < d_c; kb += 64 * UP) {
     float4 x0[UP], x1[UP];
-    uint4 bw[UP];
+    UpW w;
+    if (first && kb == 16 * wave)
+      w = *first;
+    else
+      up_w_round(w, wrow, kb, d_c);
+    const uint4* bw = w.bw;
 #pragma unroll
     for (int u = 0; u < UP; ++u) {
       const int k = min(kb + 64 * u, d_c - 16);
       x0[u] = *reinterpret_cast<const float4*>(orow + k);
       x1[u] = *reinterpret_cast<const float4*>(orow + k + 4);
-      bw[u] = *reinterpret_cast<const uint4*>(wrow + k);
     }
 #pragma unroll
     for (int u = 0; u < UP; ++u) {
@@ -1677,6 +1763,115 @@ __global__ __launch_bounds__(256) void up_project_mfma_kernel(int R, int H, int 
   }
 }
 
+__global__ __launch_bounds__(256) void up_project_mfma_kernel(int R, int H, int d_h, int d_c,
+                                                              const float* __restrict__ o_lat,
+                                                              const uint16_t* __restrict__ w_uv,
+                                                              uint16_t* __restrict__ out) {
+  __shared__ float part[4][32 * 33];
+  const int h = blockIdx.y, r0 = blockIdx.z * 32;
+  auto orow_of = [&](int c32, int grp) {
+    return o_lat + (static_cast<size_t>(min(r0 + c32, R - 1)) * H + h) * d_c + 8 * grp;
+  };
+  up_project_rows(blockIdx.x * 32, h, r0, R, H, d_h, d_c, orow_of, w_uv, out, part);
+}
+
+// The split merge and the up-projection in one launch.  A workgroup forms the
+// latent rows o_lat[r, h] of its 32 rows in LDS from the `splits` partials of
+// the split-K attention, with split_merge_kernel's arithmetic (M = max_k m_k,
+// L = sum_k l_k e^(m_k - M), o = (sum_k acc_k e^(m_k - M)) / L, both sums in
+// split order, so the same bits), then runs up_project_rows on them.  The
+// d_h / 32 workgroups of one (head, row block) form the same rows: the grid
+// puts them 8 apart, so that they run on one XCD and the partials are
+// fetched into one L2.  The W_UV fragments of the first k-round and the
+// partials of the first rows are loaded before the merge weights are
+// waited for.  S: the split count (rows are formed 16 / S at a time, all
+// their partials in flight).  Dynamic LDS: 32 rows x (d_c + 4) floats.
+constexpr int kCombineMaxSplits = 8;
+template <int S>
+__global__ __launch_bounds__(256) void combine_up_project_kernel(int R, int H, int d_h, int d_c, Partials p,
+                                                                 const uint16_t* __restrict__ w_uv,
+                                                                 uint16_t* __restrict__ out) {
+  constexpr int SMAX = S, splits = S;
+  extern __shared__ __align__(16) float so[];
+  __shared__ float part[4][32 * 33];
+  __shared__ float rw[32][SMAX];
+  __shared__ float rl[32];
+  constexpr int RI = 16 / SMAX;  // rows formed per iteration by a thread
+  const int nx = d_h / 32, nrb = (R + 31) / 32;
+  const int L = blockIdx.x;
+  const int P = (L / (8 * nx)) * 8 + L % 8, x = (L / 8) % nx;
+  if (P >= H * nrb) return;
+  const int h = P % H, r0 = (P / H) * 32;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int OP = d_c + 4;  // LDS pitch of a latent row (floats)
+  UpW w0;
+  up_w_round(w0, up_w_row(w_uv, x * 32, h, d_h, d_c), 16 * wave, d_c);
+  // thread tid forms 8-column chunk ch = tid % CR of rows tid / CR + RP j
+  const int CR = d_c / 8, RP = 256 / CR;
+  const int ch = tid % CR;
+  auto load_rows = [&](int rr0, float4 (&a)[RI][SMAX][2]) {
+#pragma unroll
+    for (int q = 0; q < RI; ++q) {
+      const int rr = min(rr0 + q * RP, 31);
+      const size_t base = static_cast<size_t>(min(r0 + rr, R - 1)) * splits * H + h;
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        const float* src = p.acc + (base + static_cast<size_t>(k) * H) * d_c + 8 * ch;
+        a[q][k][0] = *reinterpret_cast<const float4*>(src);
+        a[q][k][1] = *reinterpret_cast<const float4*>(src + 4);
+      }
+    }
+  };
+  float4 a[RI][SMAX][2];
+  load_rows(tid / CR, a);
+  // per row: the merge weights e^(m_k - M) and the denominator L
+  if (tid < 32) {
+    const size_t base = static_cast<size_t>(min(r0 + tid, R - 1)) * splits * H + h;  // + k * H
+    float mk[SMAX], lk[SMAX];
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      mk[k] = p.m[base + static_cast<size_t>(k) * H];
+      lk[k] = p.l[base + static_cast<size_t>(k) * H];
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < S; ++k) M = fmaxf(M, mk[k]);
+    float Ls = 0.f;
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      const float w = expf(mk[k] - M);
+      rw[tid][k] = w;
+      Ls = fmaf(lk[k], w, Ls);
+    }
+    rl[tid] = Ls;
+  }
+  __syncthreads();
+  for (int rr0 = tid / CR; rr0 < 32; rr0 += RI * RP) {
+    if (rr0 != tid / CR) load_rows(rr0, a);
+#pragma unroll
+    for (int q = 0; q < RI; ++q) {
+      const int rr = rr0 + q * RP;
+      if (rr >= 32) break;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        const float w = rw[rr][k];
+        const float av[8] = {a[q][k][0].x, a[q][k][0].y, a[q][k][0].z, a[q][k][0].w,
+                             a[q][k][1].x, a[q][k][1].y, a[q][k][1].z, a[q][k][1].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = fmaf(av[j], w, v[j]);
+      }
+      const float Ls = rl[rr];
+      float* dst = so + rr * OP + 8 * ch;
+      *reinterpret_cast<float4*>(dst) = float4{v[0] / Ls, v[1] / Ls, v[2] / Ls, v[3] / Ls};
+      *reinterpret_cast<float4*>(dst + 4) = float4{v[4] / Ls, v[5] / Ls, v[6] / Ls, v[7] / Ls};
+    }
+  }
+  __syncthreads();
+  auto orow_of = [&](int c32, int grp) -> const float* { return so + c32 * OP + 8 * grp; };
+  up_project_rows(x * 32, h, r0, R, H, d_h, d_c, orow_of, w_uv, out, part, &w0);
+}
+
 // Rows per workgroup of absorb / up-projection: one row while there are few
 // (row, head) pairs, so the launch fills the chip; four when there are many,
 // so each W_UK / W_UV chunk loaded serves four rows.
@@ -1694,11 +1889,13 @@ hipError_t absorb_rb(int R, int H, int d_h, int d_c, int d_r, const void* q_c, c
   return hipGetLastError();
 }
 
+bool absorb_mfma_ok(int d_h, int d_c) { return d_h % 64 == 0 && d_h <= kAbsorbMaxDh && d_c % 32 == 0; }
+
 template <typename T>
 hipError_t absorb_t(int R, int H, int d_h, int d_c, int d_r, const void* q_c, const void* q_r,
                     const void* w_uk, float* qbuf, hipStream_t st) {
-  if (std::is_same<T, uint16_t>::value && d_h % 64 == 0 && d_h <= kAbsorbMaxDh && d_c % 32 == 0) {
-    absorb_mfma_kernel<<<dim3(d_c / 32, H, (R + 31) / 32), 256, 0, st>>>(
+  if (std::is_same<T, uint16_t>::value && absorb_mfma_ok(d_h, d_c)) {
+    absorb_mfma_kernel<<<dim3(d_c / 32, H, (R + 31) / 32), 256, absorb_lds_bytes(d_h), st>>>(
         R, H, d_h, d_c, d_r, static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
         static_cast<const uint16_t*>(w_uk), qbuf);
     return hipGetLastError();
@@ -1757,6 +1954,18 @@ hipError_t launch_absorb(int R, int H, int d_h, int d_c, int d_r, const void* q_
                          hipStream_t st) {
   return dtype == 0 ? absorb_t<float>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st)
                     : absorb_t<uint16_t>(R, H, d_h, d_c, d_r, q_c, q_r, w_uk, qbuf, st);
+}
+
+bool merge_absorb_supported(int d_h, int d_c, int dtype) { return dtype == 1 && absorb_mfma_ok(d_h, d_c); }
+
+hipError_t launch_merge_absorb(const MergeArgs& m, int H, int d_h, int d_r, const void* q_c,
+                               const void* q_r, const void* w_uk, float* qbuf, hipStream_t st) {
+  if (m.T != 1 || !absorb_mfma_ok(d_h, m.d_c)) return hipErrorInvalidValue;
+  const long long tiles = static_cast<long long>(m.d_c / 32) * H * ((m.B + 31) / 32);
+  merge_absorb_kernel<<<static_cast<unsigned>(m.B + tiles), 256, absorb_lds_bytes(d_h), st>>>(
+      m, H, d_h, d_r, static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
+      static_cast<const uint16_t*>(w_uk), qbuf);
+  return hipGetLastError();
 }
 
 hipError_t launch_attend_portable(const AttendArgs& a, int dtype, hipStream_t st) {
@@ -1840,7 +2049,7 @@ bool decode_mfma_supported(int H, int d_c, int d_r) {
   return false;
 }
 
-hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st) {
+hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st, bool merge_splits) {
   dim3 grid(a.splits, a.R);
   if (a.d_c == 256 && a.d_r == 32) {
     if (a.H <= 16)
@@ -1856,8 +2065,34 @@ hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st) {
     return hipErrorNotSupported;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
+  if (e != hipSuccess || a.splits == 1 || !merge_splits) return e;
   split_merge_kernel<<<dim3(a.H, a.R), 256, 0, st>>>(a.H, a.d_c, a.splits, a.part, a.o_lat);
+  return hipGetLastError();
+}
+
+bool combine_up_project_supported(int d_h, int d_c, int splits, int dtype) {
+  return dtype == 1 && d_h % 32 == 0 && d_c % 64 == 0 && d_c <= 1024 && splits >= 2 &&
+         splits <= kCombineMaxSplits;
+}
+
+hipError_t launch_combine_up_project(int R, int H, int d_h, int d_c, int splits, const Partials& p,
+                                     const void* w_uv, void* out, hipStream_t st) {
+  if (!combine_up_project_supported(d_h, d_c, splits, 1)) return hipErrorInvalidValue;
+  const long long pairs = static_cast<long long>(H) * ((R + 31) / 32);
+  const long long grid = (pairs + 7) / 8 * 8 * (d_h / 32);
+  const size_t smem = static_cast<size_t>(32) * (d_c + 4) * sizeof(float);
+  const dim3 g(static_cast<unsigned>(grid));
+  const uint16_t* w = static_cast<const uint16_t*>(w_uv);
+  uint16_t* o = static_cast<uint16_t*>(out);
+  switch (splits) {
+    case 2: combine_up_project_kernel<2><<<g, 256, smem, st>>>(R, H, d_h, d_c, p, w, o); break;
+    case 3: combine_up_project_kernel<3><<<g, 256, smem, st>>>(R, H, d_h, d_c, p, w, o); break;
+    case 4: combine_up_project_kernel<4><<<g, 256, smem, st>>>(R, H, d_h, d_c, p, w, o); break;
+    case 5: combine_up_project_kernel<5><<<g, 256, smem, st>>>(R, H, d_h, d_c, p, w, o); break;
+    case 6: combine_up_project_kernel<6><<<g, 256, smem, st>>>(R, H, d_h, d_c, p, w, o); break;
+    case 7: combine_up_project_kernel<7><<<g, 256, smem, st>>>(R, H, d_h, d_c, p, w, o); break;
+    default: combine_up_project_kernel<8><<<g, 256, smem, st>>>(R, H, d_h, d_c, p, w, o); break;
+  }
   return hipGetLastError();
 }
 

@@ -137,6 +137,13 @@ hipError_t launch_absorb(int R, int H, int d_h, int d_c, int d_r, const void* q_
                          const void* q_r, const void* w_uk, float* qbuf, int dtype,
                          hipStream_t st);
 
+// One-token merge (m.T == 1, bf16) and the absorbed query rows of the same
+// B = m.B sequences in one launch: the same results as launch_merge followed
+// by launch_absorb.  Only where merge_absorb_supported().
+bool merge_absorb_supported(int d_h, int d_c, int dtype);
+hipError_t launch_merge_absorb(const MergeArgs& m, int H, int d_h, int d_r, const void* q_c,
+                               const void* q_r, const void* w_uk, float* qbuf, hipStream_t st);
+
 // Split partials: m, l [R, splits, H], acc [R, splits, H, d_c] (fp32).
 struct Partials {
   float* m;
@@ -162,10 +169,19 @@ struct AttendArgs {
 hipError_t launch_attend_portable(const AttendArgs& a, int dtype, hipStream_t st);
 
 // MFMA latent attention for decode (bf16 storage); a split-merge kernel
-// follows when splits > 1.  Returns hipErrorNotSupported when no instantiation covers
+// follows when splits > 1 and merge_splits (otherwise the caller merges the
+// partials, see launch_combine_up_project).  Returns hipErrorNotSupported when no instantiation covers
 // (H, d_c, d_r).
 bool decode_mfma_supported(int H, int d_c, int d_r);
-hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st);
+hipError_t launch_decode_mfma(const AttendArgs& a, hipStream_t st, bool merge_splits = true);
+
+// The split merge of the attention's partials and the up-projection in one
+// launch: the same out as split_merge_kernel (o_lat) followed by
+// launch_up_project, without writing o_lat.  Only where
+// combine_up_project_supported() (bf16, 2..8 splits).
+bool combine_up_project_supported(int d_h, int d_c, int splits, int dtype);
+hipError_t launch_combine_up_project(int R, int H, int d_h, int d_c, int splits, const Partials& p,
+                                     const void* w_uv, void* out, hipStream_t st);
 
 // Fused one-token decode step (bf16, short caches): optional merge of the
 // token, absorb, latent attention and up-projection in one kernel, one
