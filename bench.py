@@ -64,7 +64,7 @@ def parse_args():
                    help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, "
                         "prefill_chunk, llm_decode, reorder, layer_decode, layer_prefill, layer_fp32, backward; "
                         "measurement kernels: copy (the counter-calibration copy), hbm_read, mfma_peak, "
-                        "gemm_peak, launch_floor)")
+                        "gemm_peak, launch_floor, tile_stream)")
     return p.parse_args()
 
 
@@ -577,7 +577,7 @@ def run_hbm_read(steps, warmup, m, torch, gib=4):
     nbytes = gib << 30
     x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     sweep = {}
-    for wg in (1024, 2048, 4096, 8192):
+    for wg in (256, 512, 1024, 2048, 4096, 8192):
         sink = torch.empty(wg * 4, dtype=torch.int32, device="cuda")
         for _ in range(max(warmup, 1)):
             m.mtla_calib_stream_read(x, wg, sink)
@@ -587,6 +587,28 @@ def run_hbm_read(steps, warmup, m, torch, gib=4):
     del x
     return {"kernel": "calib_read_kernel", "bytes": nbytes, "GBps": sweep[best], "workgroups": best,
             "sweep_GBps": {str(k): v for k, v in sweep.items()}, "frac_of_published": sweep[best] / HBM_PEAK_GBS}
+
+
+def run_tile_stream(steps, warmup, m, torch):
+    """The long-cache decode attention's load schedule with no arithmetic
+    (mtla_calib_tile_stream) over a cache of the LLM-scale shape (64 x 16,385
+    rows of 1,152 B), 4 splits: the ceiling of that access pattern, with and
+    without the non-temporal hint, contiguous and interleaved split ranges."""
+    seqs, n, splits = 64, 16385, 4
+    rows = torch.full((seqs, n, 1152), 0x11, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(seqs * splits * 8, dtype=torch.int32, device="cuda")
+    nbytes = rows.numel()
+    rec = {"kernel": "calib_tile_stream_kernel", "bytes": nbytes, "splits": splits, "GBps": {}}
+    for il in (False, True):
+        for nt in (False, True):
+            for _ in range(max(warmup, 1)):
+                m.mtla_calib_tile_stream(rows, splits, il, nt, sink)
+            ms = timed_calls(lambda: m.mtla_calib_tile_stream(rows, splits, il, nt, sink), max(steps, 5), torch)
+            key = ("interleaved" if il else "contiguous") + ("_nt" if nt else "")
+            rec["GBps"][key] = nbytes / (ms * 1e-3) / 1e9
+            rec.setdefault("us", {})[key] = ms * 1e3
+    del rows
+    return rec
 
 
 def run_mfma_peak(steps, warmup, m, torch):
@@ -859,6 +881,7 @@ def main():
               "llm_decode": lambda: run_llm_decode(W[4], K, Wu, m, torch, workloads)[0],
               "copy": lambda: run_copy(K, Wu, torch),
               "hbm_read": lambda: run_hbm_read(K, Wu, m, torch),
+              "tile_stream": lambda: run_tile_stream(K, Wu, m, torch),
               "mfma_peak": lambda: run_mfma_peak(K, Wu, m, torch),
               "gemm_peak": lambda: run_gemm_peak(K, Wu, m, torch),
               "launch_floor": lambda: run_launch_floor(K, Wu, m, torch)}
@@ -874,7 +897,8 @@ def main():
     floor = run_launch_floor(K, Wu, m, torch)
     log("launch floor:", json.dumps(floor))
     peaks = {"hbm_read": run_hbm_read(K, Wu, m, torch), "mfma": run_mfma_peak(K, Wu, m, torch),
-             "gemm": run_gemm_peak(K, Wu, m, torch), "launch_floor_us": floor["us_per_launch"]}
+             "gemm": run_gemm_peak(K, Wu, m, torch), "launch_floor_us": floor["us_per_launch"],
+             "decode_tile_stream": run_tile_stream(K, Wu, m, torch)}
     log("measured peaks:", json.dumps(peaks))
     torch.cuda.empty_cache()
     comps, cpu_jobs = {}, []
@@ -910,6 +934,10 @@ def main():
         log("backward:", json.dumps(comps["sum_prefill_b16_n4096_s3_backward"]))
         torch.cuda.empty_cache()
         comps["llm_decode_b64_n32768_s2"] = run_llm_decode(W[4], K, Wu, m, torch, workloads)[0]
+        att = comps["llm_decode_b64_n32768_s2"]["attention"]
+        ceil = peaks["decode_tile_stream"]["GBps"]["interleaved_nt"]
+        att["load_schedule_ceiling_GBps"] = ceil
+        att["frac_of_load_schedule_ceiling"] = att["GBps"] / ceil
         log("llm:", json.dumps(comps["llm_decode_b64_n32768_s2"]))
         torch.cuda.empty_cache()
         comps["beam_reorder_llm_decode_b64_n32768_s2"] = run_reorder(W[4], K, Wu, m, torch)

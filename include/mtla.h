@@ -522,10 +522,20 @@ int32_t mtla_debug_slot_limits(int32_t n, int32_t s, int32_t* hi, void* stream);
  *     *flops (host, may be NULL) receives the multiply-add flops performed.
  *   mtla_calib_empty: launches one kernel that does nothing (the launch
  *     floor, for instance as a graph node).
+ *   mtla_calib_tile_stream: the long-cache decode attention's load schedule
+ *     with no arithmetic: `seqs` sequences of `rows_per_seq` rows of 1,152
+ *     bytes, contiguous from rows (device, 16-byte aligned); `splits`
+ *     workgroups of 512 threads per sequence stream 64-row tiles into LDS,
+ *     two tile buffers.  flags bit 0: split k takes tiles k, k+splits, ...
+ *     (else a contiguous range); bit 1: non-temporal loads.  sink (device,
+ *     seqs * splits * 8 uint32) is written only on a pattern no real data
+ *     here produces.  rows_per_seq * 1152 must fit in 31 bits; splits 1..64.
  */
 int32_t mtla_calib_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
 int32_t mtla_calib_mfma(int32_t f16, int32_t workgroups, int32_t iters, float* out, double* flops, void* stream);
 int32_t mtla_calib_empty(void* stream);
+int32_t mtla_calib_tile_stream(const void* rows, int32_t seqs, int32_t rows_per_seq, int32_t splits, int32_t flags,
+                               uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

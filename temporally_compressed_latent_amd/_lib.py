@@ -109,6 +109,7 @@ _SIGS = {
     "mtla_calib_stream_read": (_I, [_P, _SZ, _I, _P, _P]),
     "mtla_calib_mfma": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "mtla_calib_empty": (_I, [_P]),
+    "mtla_calib_tile_stream": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "mtla_absorb_query": (_I, [_D, _I, _P, _P, _P, _P, _P]),
     "mtla_decode_attention_workspace_bytes": (_I, [_D, ctypes.POINTER(_SZ)]),
     "mtla_decode_attention": (_I, [_D, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -383,6 +384,18 @@ def mtla_calib_mfma(f16: bool, workgroups: int, iters: int, out, stream=None) ->
 def mtla_calib_empty(stream=None) -> None:
     """Measurement hook: one kernel that does nothing."""
     _check(_lib.mtla_calib_empty(_stream(stream)))
+
+
+def mtla_calib_tile_stream(rows, splits: int, interleave: bool, nt: bool, sink, stream=None) -> None:
+    """Measurement hook: the long-cache decode attention's load schedule over
+    `rows` ([seqs, rows_per_seq, 1152] uint8 on the device), no arithmetic."""
+    if rows.dim() != 3 or rows.shape[2] != 1152 or rows.dtype != torch.uint8 or not rows.is_contiguous():
+        raise ValueError("rows must be a contiguous uint8 tensor [seqs, rows_per_seq, 1152]")
+    seqs, n = int(rows.shape[0]), int(rows.shape[1])
+    if sink.numel() < seqs * splits * 8 or sink.dtype != torch.int32:
+        raise ValueError("sink must be int32 with at least seqs * splits * 8 elements")
+    flags = (1 if interleave else 0) | (2 if nt else 0)
+    _check(_lib.mtla_calib_tile_stream(rows.data_ptr(), seqs, n, splits, flags, sink.data_ptr(), _stream(stream)))
 
 
 def mtla_absorb_query(dims: MtlaDims, q_c, q_r, w_uk, q_lat, stream=None) -> None:

@@ -5,7 +5,10 @@
 //                       the buffer is larger than the last-level caches);
 //   calib_mfma_kernel : independent chains of 32x32x16 MFMAs on registers
 //                       (the matrix cores' issue rate, no memory traffic);
-//   calib_empty_kernel: a kernel that does nothing (the launch floor).
+//   calib_empty_kernel: a kernel that does nothing (the launch floor);
+//   calib_tile_stream_kernel: the long-cache decode attention's load
+//                       schedule with no arithmetic (the ceiling of that
+//                       access pattern).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -82,6 +85,72 @@ __global__ __launch_bounds__(256) void calib_mfma_kernel(int iters, float* __res
 
 __global__ void calib_empty_kernel() {}
 
+// The load schedule of the long-cache decode attention without its
+// arithmetic: one workgroup of 8 waves per (split, sequence) streams 64-row
+// tiles of 1,152-byte rows (576 bf16) straight into LDS, two tile buffers,
+// the loads of the split's tile after next issued once every wave is done
+// with the current one.  IL: split k takes tiles k, k + S, ... (else a
+// contiguous range); NT: non-temporal loads.  Each wave folds one LDS word
+// per tile and writes it if it matches a pattern no input here produces, so
+// no load is dead.
+constexpr int kTileRowBytes = 1152, kTileRows = 64, kTileChunks = kTileRows * kTileRowBytes / 16;
+constexpr int kTileLoadsPerWave = kTileChunks / (8 * 64);  // 9
+template <bool NT>
+__device__ __forceinline__ void tile_load16(i32x4_t rsrc, uint32_t lds_base, int voff, int soff) {
+  if (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+template <bool IL, bool NT>
+__global__ __launch_bounds__(512) void calib_tile_stream_kernel(const uint8_t* __restrict__ rows, int rows_per_seq,
+                                                                uint32_t* __restrict__ sink) {
+  constexpr int TS = kTileRows, LPW = kTileLoadsPerWave, CPR = kTileRowBytes / 16;
+  static_assert(LPW * 8 * 64 == kTileChunks, "tile shape");
+  __shared__ __align__(16) uint8_t kb0[kTileChunks * 16];
+  __shared__ __align__(16) uint8_t kb1[kTileChunks * 16];
+  const int split = blockIdx.x, b = blockIdx.y, nsplit = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = rows_per_seq;
+  const int lo = IL ? split * TS : static_cast<int>(static_cast<long long>(split) * n / nsplit);
+  const int hi = IL ? n : static_cast<int>(static_cast<long long>(split + 1) * n / nsplit);
+  const int step = IL ? nsplit * TS : TS;
+  const i32x4_t rs = make_rsrc_words(rows + static_cast<size_t>(b) * n * kTileRowBytes, hi * kTileRowBytes);
+  int voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int slot = (wave * LPW + i) * 64 + lane;
+    const int r = slot / CPR, c = (slot % CPR) ^ ((r >> 1) & 7);
+    voff[i] = r * kTileRowBytes + c * 16;
+  }
+  auto issue = [&](int j0, uint8_t* dst) {
+    const uint32_t base = lds_addr(dst + wave * LPW * 64 * 16);
+    const int so = __builtin_amdgcn_readfirstlane(j0 * kTileRowBytes);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) tile_load16<NT>(rs, base + i * 64 * 16, voff[i], so);
+  };
+  uint32_t acc = 0;
+  if (lo < hi) issue(lo, kb0);
+  if (lo + step < hi) issue(lo + step, kb1);
+  auto tile = [&](int j0, uint8_t* kt) {
+    if (j0 + step < hi)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    acc ^= reinterpret_cast<const uint32_t*>(kt)[(tid * 7 + j0) % (kTileChunks * 4)];
+    lds_barrier();
+    if (j0 + 2 * step < hi) issue(j0 + 2 * step, kt);
+  };
+  for (int j0 = lo; j0 < hi; j0 += 2 * step) {
+    tile(j0, kb0);
+    if (j0 + step < hi) tile(j0 + step, kb1);
+  }
+  if (acc == 0x9e3779b9u && (tid & 63) == 0) sink[(static_cast<size_t>(b) * nsplit + split) * 8 + wave] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_calib_read(const void* src, size_t bytes, int workgroups, uint32_t* sink, hipStream_t st) {
@@ -100,6 +169,17 @@ hipError_t launch_calib_mfma(bool f16, int workgroups, int iters, float* out, hi
 double calib_mfma_flops(int workgroups, int iters) {
   // waves x chains x iterations x (2 x 32 x 32 x 16) flops
   return 4.0 * workgroups * kChains * static_cast<double>(iters) * (2.0 * 32 * 32 * 16);
+}
+
+hipError_t launch_calib_tile_stream(const void* rows, int seqs, int rows_per_seq, int splits, bool interleave,
+                                    bool nt, uint32_t* sink, hipStream_t st) {
+  const dim3 grid(splits, seqs);
+  const uint8_t* r = static_cast<const uint8_t*>(rows);
+  if (interleave && nt) calib_tile_stream_kernel<true, true><<<grid, 512, 0, st>>>(r, rows_per_seq, sink);
+  else if (interleave) calib_tile_stream_kernel<true, false><<<grid, 512, 0, st>>>(r, rows_per_seq, sink);
+  else if (nt) calib_tile_stream_kernel<false, true><<<grid, 512, 0, st>>>(r, rows_per_seq, sink);
+  else calib_tile_stream_kernel<false, false><<<grid, 512, 0, st>>>(r, rows_per_seq, sink);
+  return hipGetLastError();
 }
 
 hipError_t launch_calib_empty(hipStream_t st) {

@@ -1302,6 +1302,20 @@ int32_t mtla_calib_mfma(int32_t f16, int32_t workgroups, int32_t iters, float* o
                     "MFMA-loop launch");
 }
 
+int32_t mtla_calib_tile_stream(const void* rows, int32_t seqs, int32_t rows_per_seq, int32_t splits, int32_t flags,
+                               uint32_t* sink, void* stream) {
+  if (!rows || !aligned16(rows)) return fail(MTLA_ERR_INVALID_ARG, "rows is NULL or not 16-byte aligned");
+  if (seqs < 1 || seqs > 65535) return fail(MTLA_ERR_INVALID_ARG, "seqs=%d outside 1..65535", seqs);
+  if (rows_per_seq < 1 || int64_t(rows_per_seq) * 1152 > INT32_MAX)
+    return fail(MTLA_ERR_INVALID_ARG, "rows_per_seq=%d outside 1..%d", rows_per_seq, INT32_MAX / 1152);
+  if (splits < 1 || splits > 64) return fail(MTLA_ERR_INVALID_ARG, "splits=%d outside 1..64", splits);
+  if (flags & ~3) return fail(MTLA_ERR_INVALID_ARG, "flags=%d has bits other than 0 and 1", flags);
+  CHECK_PTR_ALIGN(sink, 4);
+  return hip_status(mtla::launch_calib_tile_stream(rows, seqs, rows_per_seq, splits, (flags & 1) != 0,
+                                                   (flags & 2) != 0, sink, static_cast<hipStream_t>(stream)),
+                    "tile-stream launch");
+}
+
 int32_t mtla_calib_empty(void* stream) {
   return hip_status(mtla::launch_calib_empty(static_cast<hipStream_t>(stream)), "empty-kernel launch");
 }

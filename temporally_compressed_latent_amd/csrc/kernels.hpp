@@ -254,5 +254,7 @@ hipError_t launch_calib_read(const void* src, size_t bytes, int workgroups, uint
 hipError_t launch_calib_mfma(bool f16, int workgroups, int iters, float* out, hipStream_t st);
 double calib_mfma_flops(int workgroups, int iters);
 hipError_t launch_calib_empty(hipStream_t st);
+hipError_t launch_calib_tile_stream(const void* rows, int seqs, int rows_per_seq, int splits, bool interleave,
+                                    bool nt, uint32_t* sink, hipStream_t st);
 
 }  // namespace mtla

@@ -25,7 +25,7 @@ def dims(**kw):
 
 def test_exports_every_header_symbol():
     syms = m.header_symbols()
-    assert len(syms) == 35
+    assert len(syms) == 36
     for s in syms:
         assert hasattr(m.lib(), s), s
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
@@ -360,3 +360,22 @@ def test_staged_prefill_needs_the_mfma_path():
             m.MTLA_ERR_UNSUPPORTED
     assert L.mtla_prefill_partials(ctypes.byref(dims()), 16, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, None) == \
         m.MTLA_ERR_INVALID_ARG          # pe_rows < n_tokens
+
+
+def test_measurement_hook_checks():
+    """The measurement hooks reject bad arguments before any launch."""
+    L = m.lib()
+    bad = m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_calib_stream_read(None, 1024, 4, FAKE, None) == bad
+    assert L.mtla_calib_stream_read(FAKE, 1000, 4, FAKE, None) == bad      # not a multiple of 16
+    assert L.mtla_calib_stream_read(FAKE, 1024, 0, FAKE, None) == bad
+    assert L.mtla_calib_mfma(0, 0, 16, FAKE, None, None) == bad
+    assert L.mtla_calib_mfma(0, 4, 0, FAKE, None, None) == bad
+    assert L.mtla_calib_tile_stream(None, 4, 64, 4, 0, FAKE, None) == bad
+    assert L.mtla_calib_tile_stream(MISALIGNED, 4, 64, 4, 0, FAKE, None) == bad
+    assert L.mtla_calib_tile_stream(FAKE, 0, 64, 4, 0, FAKE, None) == bad
+    assert L.mtla_calib_tile_stream(FAKE, 4, 0, 4, 0, FAKE, None) == bad
+    assert L.mtla_calib_tile_stream(FAKE, 4, (2**31) // 1152 + 1, 4, 0, FAKE, None) == bad
+    assert L.mtla_calib_tile_stream(FAKE, 4, 64, 65, 0, FAKE, None) == bad
+    assert L.mtla_calib_tile_stream(FAKE, 4, 64, 4, 4, FAKE, None) == bad
+    assert L.mtla_calib_tile_stream(FAKE, 4, 64, 4, 3, None, None) == bad
