@@ -99,6 +99,27 @@ __device__ __forceinline__ PairDest pair_dest(const LayerGemmArgs& g, int n) {
   return p;
 }
 
+// The same destination as an array, a row stride and an offset: output pair
+// (m, n) goes to elements m * stride + off, +1 of dst.  Resolved once per
+// column pair, so that a store loop over rows has no per-row branch on the
+// kind of output.
+struct PairStore {
+  void* dst;
+  int stride, off;
+  bool rope, f32, single;  // rotate (q^R, k^R); fp32 output; last column of an odd N
+  double theta;
+};
+__device__ __forceinline__ PairStore pair_store(const LayerGemmArgs& g, int n) {
+  const PairDest p = pair_dest(g, n);
+  switch (p.kind) {
+    case 0: return PairStore{g.out, g.N, n, false, g.out_f32 != 0, n + 1 >= g.N, 0.0};
+    case 1: return PairStore{g.c, g.d_c, n, false, false, false, 0.0};
+    case 2: return PairStore{g.q_c, g.H * g.d_h, p.head * g.d_h + p.e, false, false, false, 0.0};
+    case 3: return PairStore{g.q_r, g.H * g.d_r, p.head * g.d_r + p.e, true, false, false, p.theta};
+    default: return PairStore{g.k_r, g.d_r, p.e, true, false, false, p.theta};
+  }
+}
+
 // Rotate the pair (x0, x1) by the angle pos * theta: the angle is formed and
 // reduced to [-pi, pi] in double, so that large positions keep their
 // accuracy, and its sine and cosine are taken in float.
@@ -439,7 +460,7 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
   // The rows' token positions (rope pairs) are computed once per row.
   float* sC = reinterpret_cast<float*>(smem);
   const int pc = tid & 63, n = n0 + 2 * pc;
-  const PairDest pd = pair_dest(g, min(n, N - 2));
+  const PairStore ps = pair_store(g, min(n, N - 2));
   if (g.mode != 0 && tid < MBM) sPos[tid] = row_position(g, min(m0 + tid, M - 1));
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
@@ -457,8 +478,16 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
       for (int r = tid >> 6; r < 64; r += 4) {
         const int m = m0 + 64 * hh + r;
         if (m >= M) break;
-        store_pair<uint16_t, true>(g, pd, m, n, pd.kind >= 3 ? sPos[64 * hh + r] : 0, sC[r * MCP + 2 * pc],
-                                   sC[r * MCP + 2 * pc + 1]);
+        float x0 = sC[r * MCP + 2 * pc], x1 = sC[r * MCP + 2 * pc + 1];
+        if (ps.rope) rope_rotate_rev(sPos[64 * hh + r], ps.theta, x0, x1);
+        const size_t i = static_cast<size_t>(m) * ps.stride + ps.off;
+        if (ps.f32) {
+          float* d = static_cast<float*>(ps.dst);
+          if (ps.single) d[i] = x0; else store2(d, i, x0, x1);
+        } else {
+          uint16_t* d = static_cast<uint16_t*>(ps.dst);
+          if (ps.single) d[i] = f32_to_bf16_bits(x0); else store2(d, i, x0, x1);
+        }
       }
     }
     __syncthreads();
