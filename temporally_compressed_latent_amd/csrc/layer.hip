@@ -338,17 +338,21 @@ __global__ __launch_bounds__(256) void layer_gemm_kernel(LayerGemmArgs g) {
 }
 
 // The same product for many rows in bf16: 128 x 128 output tiles, four waves
-// of 64 x 64 (2 x 2 tiles of 32x32x16 MFMA), K step 64 through
+// of 64 x 64 (2 x 2 tiles of 32x32x16 MFMA), K step 32 or 64 through
 // double-buffered LDS with the next step's operands prefetched into
 // registers.  Workgroup L runs on XCD L % 8; the column tiles of one
 // 128-row stripe of A are dealt to one XCD, so the stripe is fetched into
 // that XCD's L2 once for all of them.  The C tile is staged in LDS in two
 // 64-row halves and stored by column pairs, as in the smaller kernel.
-constexpr int MBM = 128, MBN = 128, MBK = 64;
-constexpr int MP = MBK + 8;   // operand pitch (elements)
+constexpr int MBM = 128, MBN = 128;
 constexpr int MCP = MBN + 4;  // C half-tile pitch (floats)
 
+// MBK: the K step (32 for short K: half the LDS, three workgroups per CU
+// instead of two, which hides more load latency when there are few steps;
+// 64 for long K).
+template <int MBK>
 __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, int nrt, int nct) {
+  constexpr int MP = MBK + 8;  // operand pitch (elements)
   __shared__ __align__(16) uint16_t smem[2 * (MBM + MBN) * MP];
   __shared__ int sPos[MBM];
   static_assert(64 * MCP * 4 <= sizeof(smem), "C half tile fits in the operand buffers");
@@ -604,7 +608,10 @@ hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st) 
   }
   if (dtype != 0) {
     const int nrt = (g.M + MBM - 1) / MBM, nct = (g.N + MBN - 1) / MBN;
-    layer_gemm_mfma_kernel<<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);
+    if (g.K <= 1024)
+      layer_gemm_mfma_kernel<32><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);
+    else
+      layer_gemm_mfma_kernel<64><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);
     return hipGetLastError();
   }
   dim3 grid((g.N + LBN - 1) / LBN, (g.M + LBM - 1) / LBM);
