@@ -313,15 +313,19 @@ int32_t mtla_prefill(const mtla_dims* dims, int32_t n_tokens, const void* q_c, c
  *   partials device [B, n_tokens, d_c + d_r] storage dtype, written (each
  *   value rounded once from its fp32 sum); cache and open_acc written as
  *   mtla_prefill leaves them; the other arguments as for mtla_prefill.
- * mtla_prefill_keys: K^C_j,h = W_UK[h] P^c_j and V_j,h = W_UV[h] P^c_j for
- *   every row j of partials:
- *   k_c, v device [B, H, n_tokens, d_h] fp16 (IEEE binary16, rounded to
- *   nearest even from fp32 accumulation), written.
+ * mtla_prefill_keys: K^C_b,h = W_UK[h] P^c_{s*b} and V_b,h = W_UV[h] P^c_{s*b}
+ *   of the completed slots b = 1 .. n_keys that some query of the call
+ *   attends, n_keys = floor((n_tokens - 1) / s) (0 for n_tokens = 0):
+ *   k_c, v device [B, H, n_keys, d_h] fp16 (IEEE binary16, rounded to
+ *   nearest even from fp32 accumulation), written; partials read only.
+ *   Nothing is launched when n_keys is 0 (k_c and v may then be NULL).
  * mtla_prefill_attention: the stride-masked attention of queries
  *   1..n_tokens (query i attends the partial merges j = i and j = s*b for
- *   b < ceil(i/s)) over those keys: q_c, q_r as for mtla_prefill; partials,
- *   k_c, v from the two calls above (read only); out [B, n_tokens, H, d_h],
- *   written.
+ *   b < ceil(i/s)): q_c, q_r, w_uk, w_uv as for mtla_prefill; partials and
+ *   the slot keys k_c, v from the two calls above (read only); out
+ *   [B, n_tokens, H, d_h], written.  Each query's own key j = i (K^C_i =
+ *   W_UK[h] P^c_i, V_i = W_UV[h] P^c_i) is formed inside this call, in
+ *   fp32, from partials and the weights.
  * The fp16 keys and values bound their magnitudes by 65504.
  */
 int32_t mtla_prefill_partials(const mtla_dims* dims, int32_t n_tokens, const void* c, const void* k_r,
@@ -330,7 +334,8 @@ int32_t mtla_prefill_partials(const mtla_dims* dims, int32_t n_tokens, const voi
 int32_t mtla_prefill_keys(const mtla_dims* dims, int32_t n_tokens, const void* partials, const void* w_uk,
                           const void* w_uv, void* k_c, void* v, void* stream);
 int32_t mtla_prefill_attention(const mtla_dims* dims, int32_t n_tokens, const void* q_c, const void* q_r,
-                               const void* partials, const void* k_c, const void* v, void* out, void* stream);
+                               const void* partials, const void* w_uk, const void* w_uv, const void* k_c,
+                               const void* v, void* out, void* stream);
 
 /* Bytes of workspace mtla_prefill_at needs for n_tokens tokens after t0. */
 int32_t mtla_prefill_at_workspace_bytes(const mtla_dims* dims, int32_t t0, int32_t n_tokens,
@@ -355,8 +360,9 @@ int32_t mtla_prefill_at_workspace_bytes(const mtla_dims* dims, int32_t t0, int32
  *         written.
  *   open_acc device [B, 2, d_c + d_r] fp32: [b, t0 % 2] read when t0 is not
  *         at a block boundary; [b, (t0 + n_tokens) % 2] written.
- *   workspace device, >= mtla_prefill_at_workspace_bytes(); scratch.  With
- *         the MFMA path and t0 > 0 it holds K^C and V of every cache slot.
+ *   workspace device, >= mtla_prefill_at_workspace_bytes(); scratch.  On
+ *         the MFMA path it holds K^C and V of the completed slots the new
+ *         queries attend (floor((t0 + n_tokens - 1) / s) per sequence).
  */
 int32_t mtla_prefill_at(const mtla_dims* dims, int32_t t0, int32_t n_tokens, const void* q_c,
                         const void* q_r, const void* c, const void* k_r, const float* w_hyp,

@@ -105,7 +105,7 @@ _SIGS = {
     "mtla_decode_step_noalloc": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "mtla_prefill_partials": (_I, [_D, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
     "mtla_prefill_keys": (_I, [_D, _I, _P, _P, _P, _P, _P, _P]),
-    "mtla_prefill_attention": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "mtla_prefill_attention": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "mtla_calib_stream_read": (_I, [_P, _SZ, _I, _P, _P]),
     "mtla_calib_mfma": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "mtla_calib_empty": (_I, [_P]),
@@ -335,31 +335,42 @@ def mtla_prefill_partials(dims: MtlaDims, c, k_r, w_hyp, pe, cache, open_acc, pa
         _stream(stream)))
 
 
+def prefill_slot_keys(dims: MtlaDims, n_tokens: int, t0: int = 0) -> int:
+    """Completed slots the queries t0+1..t0+n_tokens attend: floor((t0+n_tokens-1)/s)."""
+    return (t0 + n_tokens - 1) // dims.stride_s if n_tokens > 0 else 0
+
+
 def mtla_prefill_keys(dims: MtlaDims, partials, w_uk, w_uv, k_c, v, stream=None) -> None:
-    """Staged prefill, stage 2: K^C and V [B, H, N, d_h] fp16 of every partial merge."""
+    """Staged prefill, stage 2: K^C and V [B, H, n_keys, d_h] fp16 of the
+    completed slots the queries attend (n_keys = prefill_slot_keys)."""
     B, H, st = dims.batch, dims.heads, dims.torch_dtype
     N = int(partials.shape[1])
+    S = prefill_slot_keys(dims, N)
     _check(_lib.mtla_prefill_keys(
         ctypes.byref(dims), N,
         _tensor("partials", partials, (B, N, dims.width), st),
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
-        _tensor("k_c", k_c, (B, H, N, dims.d_h), torch.float16),
-        _tensor("v", v, (B, H, N, dims.d_h), torch.float16),
+        _tensor("k_c", k_c, (B, H, S, dims.d_h), torch.float16, optional=S == 0),
+        _tensor("v", v, (B, H, S, dims.d_h), torch.float16, optional=S == 0),
         _stream(stream)))
 
 
-def mtla_prefill_attention(dims: MtlaDims, q_c, q_r, partials, k_c, v, out, stream=None) -> None:
-    """Staged prefill, stage 3: the stride-masked attention over the staged keys."""
+def mtla_prefill_attention(dims: MtlaDims, q_c, q_r, partials, w_uk, w_uv, k_c, v, out, stream=None) -> None:
+    """Staged prefill, stage 3: the stride-masked attention over the staged
+    slot keys; each query's own key is formed from partials and the weights."""
     B, H, st = dims.batch, dims.heads, dims.torch_dtype
     N = int(q_c.shape[1])
+    S = prefill_slot_keys(dims, N)
     _check(_lib.mtla_prefill_attention(
         ctypes.byref(dims), N,
         _tensor("q_c", q_c, (B, N, H, dims.d_h), st),
         _tensor("q_r", q_r, (B, N, H, dims.d_r), st, optional=dims.d_r == 0),
         _tensor("partials", partials, (B, N, dims.width), st),
-        _tensor("k_c", k_c, (B, H, N, dims.d_h), torch.float16),
-        _tensor("v", v, (B, H, N, dims.d_h), torch.float16),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("k_c", k_c, (B, H, S, dims.d_h), torch.float16, optional=S == 0),
+        _tensor("v", v, (B, H, S, dims.d_h), torch.float16, optional=S == 0),
         _tensor("out", out, (B, N, H, dims.d_h), st),
         _stream(stream)))
 

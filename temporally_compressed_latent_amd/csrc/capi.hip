@@ -185,15 +185,18 @@ DecodeWs decode_ws(const mtla_dims* d) {
 }
 
 struct PrefillWs {
-  size_t P, kc, v, kslot, vslot, qlat, olat;
+  size_t P, kc, v, qlat, olat;
   AttnWs attn;
   size_t total;
 };
 
+// Completed slots that some query of tokens t0+1 .. t0+n attends: query
+// token i sees slots 1 .. ceil(i/s) - 1.
+int prefill_slot_keys(const mtla_dims* d, int n, int t0) { return n > 0 ? (t0 + n - 1) / d->stride_s : 0; }
+
 // Workspace of a prefill of n tokens after t0 cached ones.  The MFMA path
-// with t0 > 0 also holds K^C and V of every cache slot ([B, H, max_slots,
-// d_h] each): slot keys then come from the cache rows, not from this call's
-// partial merges.
+// holds K^C and V of the completed slots the queries attend ([B, H, slots,
+// d_h] each); each query's own diagonal key is formed in the attention kernel.
 PrefillWs prefill_ws(const mtla_dims* d, int n, int t0 = 0) {
   const size_t B = d->batch, H = d->heads, W = d->d_c + d->d_r, N = n;
   const size_t e = elem_bytes(d);
@@ -201,17 +204,11 @@ PrefillWs prefill_ws(const mtla_dims* d, int n, int t0 = 0) {
   w.P = 0;
   size_t off = align_up(B * N * W * e);
   if (prefill_fast(d)) {
+    const size_t S = prefill_slot_keys(d, n, t0);
     w.kc = off;
-    off += align_up(B * H * N * d->d_h * e);
+    off += align_up(B * H * S * d->d_h * e);
     w.v = off;
-    off += align_up(B * H * N * d->d_h * e);
-    if (t0 > 0) {
-      const size_t S = d->max_slots;
-      w.kslot = off;
-      off += align_up(B * H * S * d->d_h * e);
-      w.vslot = off;
-      off += align_up(B * H * S * d->d_h * e);
-    }
+    off += align_up(B * H * S * d->d_h * e);
     w.total = off;
   } else {
     const size_t R = B * N;
@@ -664,28 +661,33 @@ static int32_t prefill_impl(const mtla_dims* dims, int32_t t0, int32_t n_tokens,
   hipError_t e = mtla::launch_merge(m, dims->dtype, s);
   if (e != hipSuccess) return hip_status(e, "prefill merge launch");
   if (prefill_fast(dims)) {
+    // K^C and V of the completed slots the queries attend, then the attention
+    // (which forms each query's diagonal key itself).  From token 1 the slot
+    // keys are the partial merges at block ends (rows s*j + s - 1), as in the
+    // staged calls; after t0 cached tokens they are the cache rows, which the
+    // merge has just completed.
     void* kc = at(workspace, ws.kc);
     void* v = at(workspace, ws.v);
-    e = mtla::launch_prefill_kv(B, N, H, dims->d_h, dims->d_c, dims->d_r, P, w_uk, w_uv, kc, v, true, s);
-    if (e != hipSuccess) return hip_status(e, "up-projection launch");
-    mtla::PrefillAttnArgs pa{B, N, H, dims->d_h, dims->d_c, dims->d_r, dims->stride_s, 0,
-                             dims->softmax_scale, q_c, q_r, kc, v, P, out};
-    if (t0 > 0) {
-      // slot keys from the cache rows (the merge has written this call's
-      // slots): K^C and V of every slot row by the same GEMM
-      void* ks = at(workspace, ws.kslot);
-      void* vs = at(workspace, ws.vslot);
-      e = mtla::launch_prefill_kv(B, dims->max_slots, H, dims->d_h, dims->d_c, dims->d_r, cache, w_uk, w_uv,
-                                  ks, vs, true, s);
-      if (e != hipSuccess) return hip_status(e, "slot up-projection launch");
-      pa.t0 = t0;
-      pa.kslot = ks;
-      pa.vslot = vs;
+    const int nsl = prefill_slot_keys(dims, N, t0);
+    const int S = dims->stride_s;
+    mtla::PrefillAttnArgs pa{B, N, H, dims->d_h, dims->d_c, dims->d_r, S, 0, dims->softmax_scale,
+                             q_c, q_r, P, w_uk, w_uv, out, t0, kc, v, nsl};
+    if (t0 == 0) {
+      e = mtla::launch_prefill_kv(B, nsl, N, S, S - 1, H, dims->d_h, dims->d_c, dims->d_r, P, w_uk, w_uv, kc, v,
+                                  true, s);
+      pa.rslot = P;
+      pa.rslot_rows = N;
+      pa.rslot_mul = S;
+      pa.rslot_add = S - 1;
+    } else {
+      e = mtla::launch_prefill_kv(B, nsl, dims->max_slots, 1, 0, H, dims->d_h, dims->d_c, dims->d_r, cache, w_uk,
+                                  w_uv, kc, v, true, s);
       pa.rslot = cache;
-      pa.slot_rows = pa.rslot_rows = dims->max_slots;
-      pa.slot_mul = 1;
-      pa.slot_add = 0;
+      pa.rslot_rows = dims->max_slots;
+      pa.rslot_mul = 1;
+      pa.rslot_add = 0;
     }
+    if (e != hipSuccess) return hip_status(e, "slot up-projection launch");
     return hip_status(mtla::launch_prefill_attn(pa, s), "prefill attention launch");
   }
   const int R = B * N;
@@ -757,30 +759,41 @@ int32_t mtla_prefill_keys(const mtla_dims* dims, int32_t n_tokens, const void* p
                           const void* w_uv, void* k_c, void* v, void* stream) {
   int32_t st = check_staged_prefill(dims, n_tokens);
   if (st != MTLA_OK) return st;
-  if (dims->batch == 0 || n_tokens == 0) return ok();
+  const int nsl = prefill_slot_keys(dims, n_tokens, 0);
+  if (dims->batch == 0 || nsl == 0) return ok();
   CHECK_PTR(partials);
   CHECK_PTR(w_uk);
   CHECK_PTR(w_uv);
   CHECK_PTR(k_c);
   CHECK_PTR(v);
-  return hip_status(mtla::launch_prefill_kv(dims->batch, n_tokens, dims->heads, dims->d_h, dims->d_c, dims->d_r,
-                                            partials, w_uk, w_uv, k_c, v, true, static_cast<hipStream_t>(stream)),
+  const int S = dims->stride_s;
+  return hip_status(mtla::launch_prefill_kv(dims->batch, nsl, n_tokens, S, S - 1, dims->heads, dims->d_h, dims->d_c,
+                                            dims->d_r, partials, w_uk, w_uv, k_c, v, true,
+                                            static_cast<hipStream_t>(stream)),
                     "up-projection launch");
 }
 
 int32_t mtla_prefill_attention(const mtla_dims* dims, int32_t n_tokens, const void* q_c, const void* q_r,
-                               const void* partials, const void* k_c, const void* v, void* out, void* stream) {
+                               const void* partials, const void* w_uk, const void* w_uv, const void* k_c,
+                               const void* v, void* out, void* stream) {
   int32_t st = check_staged_prefill(dims, n_tokens);
   if (st != MTLA_OK) return st;
   if (dims->batch == 0 || n_tokens == 0) return ok();
+  const int nsl = prefill_slot_keys(dims, n_tokens, 0);
   CHECK_PTR(q_c);
   if (dims->d_r > 0) CHECK_PTR(q_r);
   CHECK_PTR(partials);
-  CHECK_PTR(k_c);
-  CHECK_PTR(v);
+  CHECK_PTR(w_uk);
+  CHECK_PTR(w_uv);
+  if (nsl > 0) {
+    CHECK_PTR(k_c);
+    CHECK_PTR(v);
+  }
   CHECK_PTR(out);
-  mtla::PrefillAttnArgs pa{dims->batch, n_tokens, dims->heads, dims->d_h, dims->d_c, dims->d_r, dims->stride_s, 0,
-                           dims->softmax_scale, q_c, q_r, k_c, v, partials, out};
+  const int S = dims->stride_s;
+  mtla::PrefillAttnArgs pa{dims->batch, n_tokens, dims->heads, dims->d_h, dims->d_c, dims->d_r, S, 0,
+                           dims->softmax_scale, q_c, q_r, partials, w_uk, w_uv, out, 0, k_c, v, nsl,
+                           partials, n_tokens, S, S - 1};
   return hip_status(mtla::launch_prefill_attn(pa, static_cast<hipStream_t>(stream)), "prefill attention launch");
 }
 
@@ -1003,6 +1016,13 @@ int32_t mtla_layer_prefill(const mtla_dims* dims, int32_t d_model, int32_t t0, i
   if (t0 < 0) return fail(MTLA_ERR_INVALID_ARG, "t0=%d < 0", t0);
   if (n_tokens < 0) return fail(MTLA_ERR_INVALID_ARG, "n_tokens=%d < 0", n_tokens);
   if ((st = check_rows(dims, int64_t(dims->batch) * n_tokens, d_model)) != MTLA_OK) return st;
+  // (before the workspace check: the workspace size depends on t0)
+  if (pe_rows < int64_t(t0) + n_tokens)
+    return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < t0 + n_tokens = %lld", pe_rows,
+                static_cast<long long>(int64_t(t0) + n_tokens));
+  if (int64_t(t0) + n_tokens > int64_t(dims->max_slots) * dims->stride_s)
+    return fail(MTLA_ERR_INVALID_ARG, "t0 + n_tokens = %lld exceeds the cache capacity s*max_slots",
+                static_cast<long long>(int64_t(t0) + n_tokens));
   if (dims->batch == 0 || n_tokens == 0) return ok();
   CHECK_PTR(h);
   CHECK_PTR(w_dkv);
@@ -1209,8 +1229,8 @@ int32_t mtla_prefill_backward(const mtla_dims* dims, int32_t n_tokens, const voi
     a.v = at(workspace, ws.v);
     a.pd = reinterpret_cast<float*>(at(workspace, ws.pd));
     a.dsd = reinterpret_cast<float*>(at(workspace, ws.dsd));
-    if ((e = mtla::launch_prefill_kv(a.B, n_tokens, H, d_h, dc, dr, a.P, w_uk, w_uv, at(workspace, ws.kc),
-                                     at(workspace, ws.v), false, s)) != hipSuccess)
+    if ((e = mtla::launch_prefill_kv(a.B, n_tokens, n_tokens, 1, 0, H, d_h, dc, dr, a.P, w_uk, w_uv,
+                                     at(workspace, ws.kc), at(workspace, ws.v), false, s)) != hipSuccess)
       return hip_status(e, "backward K/V up-projection launch");
     if ((e = mtla::launch_bwd_attention_mfma(a, s)) != hipSuccess)
       return hip_status(e, "backward attention launch");

@@ -203,6 +203,12 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4_t rsrc, uint32_t lds_bas
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
+// The same load with the default cache policy, for data that other
+// workgroups read again (weights).
+__device__ __forceinline__ void buffer_load_lds16_cached(i32x4_t rsrc, uint32_t lds_base, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
 // Raw buffer resource words for a wave-uniform base address and size.
 __device__ __forceinline__ i32x4_t make_rsrc_words(const void* base, int nbytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);

@@ -216,12 +216,13 @@ hipError_t launch_up_project(int R, int H, int d_h, int d_c, const float* o_lat,
 
 // Prefill MFMA path (bf16): up-projection GEMM and stride-masked attention.
 bool prefill_mfma_supported(int H, int d_h, int d_c, int d_r);
-// K^C and V of every row of `partials` ([B, N, W], bf16), written
-// [B, H, N, d_h] in fp16 (out_fp16: the forward attention's operands) or
-// bf16 (the training backward's).
-hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
-                            const void* partials, const void* w_uk, const void* w_uv,
-                            void* k_out, void* v_out, bool out_fp16, hipStream_t st);
+// K^C and V of n_rows rows of a [.., W] bf16 array per sequence: output row j
+// of sequence b takes input row b*a_seq_rows + a_mul*j + a_add.  Written
+// [B, H, n_rows, d_h] in fp16 (out_fp16: the forward attention's operands)
+// or bf16 (the training backward's).  B*a_seq_rows*W*2 must stay below 2^31.
+hipError_t launch_prefill_kv(int B, int n_rows, int a_seq_rows, int a_mul, int a_add, int H, int d_h, int d_c,
+                            int d_r, const void* a, const void* w_uk, const void* w_uv, void* k_out, void* v_out,
+                            bool out_fp16, hipStream_t st);
 
 struct PrefillAttnArgs {
   int B, N, H, d_h, d_c, d_r, s;
@@ -229,20 +230,19 @@ struct PrefillAttnArgs {
   float scale;
   const void* q_c;       // [B, N, H, d_h]
   const void* q_r;       // [B, N, H, d_r]
-  const void* kc;        // [B, H, N, d_h] fp16
-  const void* v;         // [B, H, N, d_h] fp16
-  const void* partials;  // [B, N, W]  (rope keys P^R are its last d_r columns)
+  const void* partials;  // [B, N, W]: P_i of each query, its diagonal key
+  const void* w_uk;      // [H, d_h, d_c]: the diagonal's K^C = W_UK P^c_i ...
+  const void* w_uv;      // [H, d_h, d_c]: ... and V = W_UV P^c_i, formed in the kernel
   void* out;             // [B, N, H, d_h]
-  // Queries are tokens t0+1 .. t0+N.  Keys of completed slot j (0-based):
-  // row slot_mul*j + slot_add of kslot / vslot ([B, H, slot_rows, d_h]) and
-  // of rslot ([B, rslot_rows, W], rope key in the last d_r columns).  Left
-  // null, they are the token-indexed kc / v / partials (slot j = token
-  // s*j + s - 1, t0 = 0).
-  int t0 = 0;
-  const void* kslot = nullptr;
-  const void* vslot = nullptr;
-  const void* rslot = nullptr;
-  int slot_rows = 0, rslot_rows = 0, slot_mul = 0, slot_add = 0;
+  int t0;                // the queries are tokens t0+1 .. t0+N
+  // completed slot j (0-based): K^C and V at row j of kslot / vslot ([B, H,
+  // slot_rows, d_h] fp16); the rope key at row rslot_mul*j + rslot_add of
+  // rslot ([B, rslot_rows, W], last d_r columns)
+  const void* kslot;
+  const void* vslot;
+  int slot_rows;
+  const void* rslot;
+  int rslot_rows, rslot_mul, rslot_add;
 };
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t st);
 

@@ -8,12 +8,14 @@
 // the compacted completed slots (a staircase in slot space) plus one
 // per-query "diagonal" key, which seeds the online softmax.
 //
-//   K/V GEMM  : K^C = P^c W_UK^T and V = P^c W_UV^T for all N rows (MFMA GEMM,
-//               output [B, H, N, d_h]; fp16 for the attention below, bf16 for
-//               the training backward)
-//   attention : per (query tile, head, sequence): diagonal init, then slot
-//               tiles 0 .. floor((i_max-1)/s); only boundary tiles are masked,
-//               tiles past the last visible slot are never visited.
+//   K/V GEMM  : K^C = P^c W_UK^T and V = P^c W_UV^T of the completed slots'
+//               key rows only (MFMA GEMM, output [B, H, slots, d_h]; fp16 for
+//               the attention below; over every token, bf16, for the training
+//               backward)
+//   attention : per (query tile, head, sequence): the diagonal key's K^C_i
+//               and V_i formed from P_i in the kernel, then slot tiles
+//               0 .. floor((i_max-1)/s); only boundary tiles are masked, tiles
+//               past the last visible slot are never visited.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,7 +25,8 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Up-projection GEMM: C[m, col] = sum_k A[m, k] * Bw[col, k]
-//   A  = P^c: rows m = (b, n) of the partial merges, row stride W, K = d_c
+//   A  = P^c: the rows of partial merges or of cache slots that are keys
+//        (a row selection per sequence), row stride W, K = d_c
 //   Bw = [W_UK ; W_UV] viewed as [2*H*d_h, d_c]
 // 128x128 output tile per workgroup, 4 waves in a 2x2 grid of 64x64, K step
 // 32, double-buffered LDS.  Output column col -> (K or V, head, e).
@@ -32,8 +35,9 @@ constexpr int GBM = 128, GBN = 128, GBK = 32;
 constexpr int GP = GBK + 8;  // LDS pitch (elements)
 
 template <bool F16OUT>
-__global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, int d_h, int d_c,
-                                                        int W, const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(256) void prefill_kv_kernel(int B, int N, int a_seq_rows, int a_mul, int a_add,
+                                                        int H, int d_h, int d_c, int W,
+                                                        const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ w_uk,
                                                         const uint16_t* __restrict__ w_uv,
                                                         uint16_t* __restrict__ kout,
@@ -54,26 +58,32 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
   const int col0 = (t % ncol) * GBN;
   const int row0 = (t / ncol) * GBM;
   const int HD = H * d_h;
+  const int M = B * N;
 
   // Each thread copies 2 chunks of A and 2 of B per K step (16 B each).  A
-  // goes through a buffer resource over its M rows (rows past M read as
-  // zero); the B tile lies wholly in W_UK or in W_UV (HD is a multiple of
-  // GBN), so its base is uniform.
+  // goes through a buffer resource over its B*a_seq_rows rows; output row m
+  // (sequence m / N, row j = m % N) reads input row a_seq_rows*(m / N) +
+  // a_mul*j + a_add, and rows past M point one whole array past the end, so
+  // they read as zero.  The B tile lies wholly in W_UK or in W_UV (HD is a
+  // multiple of GBN), so its base is uniform.
   const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A), static_cast<short>(0), M * W * 2, kBufferRsrcWord3);
+      const_cast<uint16_t*>(A), static_cast<short>(0), B * a_seq_rows * W * 2, kBufferRsrcWord3);
   const uint16_t* bmat = col0 < HD ? w_uk + static_cast<size_t>(col0) * d_c
                                    : w_uv + static_cast<size_t>(col0 - HD) * d_c;
   // Two K steps are in flight: each step's chunks land in one of two named
   // register sets (not arrays, so they are never placed in scratch) and go
   // to LDS one step later.
   const int r0 = tid >> 2, r1 = (tid + 256) >> 2, ch = tid & 3;  // chunk (r, ch), two per thread
+  auto a_row = [&](int m) {
+    return m < M ? (m / N) * a_seq_rows + (m % N) * a_mul + a_add : B * a_seq_rows;
+  };
+  const int aoff0 = (a_row(row0 + r0) * W + ch * 8) * 2, aoff1 = (a_row(row0 + r1) * W + ch * 8) * 2;
   struct Regs {
     uint4 a0, a1, b0, b1;
   };
   auto gload = [&](Regs& R, int k0) {
-    const int so = (row0 * W + k0) * 2;
-    const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rs_a, (r0 * W + ch * 8) * 2, so, 0);
-    const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rs_a, (r1 * W + ch * 8) * 2, so, 0);
+    const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rs_a, aoff0, k0 * 2, 0);
+    const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rs_a, aoff1, k0 * 2, 0);
     R.a0 = uint4{v0[0], v0[1], v0[2], v0[3]};
     R.a1 = uint4{v1[0], v1[1], v1[2], v1[3]};
     R.b0 = *reinterpret_cast<const uint4*>(bmat + static_cast<size_t>(r0) * d_c + k0 + ch * 8);
@@ -169,9 +179,10 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int M, int N, int H, in
 
 // ---------------------------------------------------------------------------
 // Stride-masked attention, explicit per-head form, fp16 operands / fp32
-// accumulate, on v_mfma_f32_32x32x16_f16.  The keys and values K^C, V are
-// the K/V GEMM's fp16 output, the scaled queries, the rope keys and the
-// probabilities are converted to fp16 here: every operand then carries 11
+// accumulate, on v_mfma_f32_32x32x16_f16.  The slot keys and values K^C, V
+// are the K/V GEMM's fp16 output, the scaled queries, the rope keys and the
+// probabilities are converted to fp16 here (the diagonal key is formed and
+// used in fp32): every operand then carries 11
 // significant bits (bf16: 8), so the attention adds 8x less rounding than
 // with bf16 operands, at the same MFMA rate.  The queries and rope keys are
 // bf16 storage and convert exactly.
@@ -218,25 +229,27 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   // bound on the running max's magnitude (log2 units), inside fp16's range
   constexpr float kMaxRef = 60000.f;
 
-  // two K/V tile buffers: the next tile is stored while this one is used
-  __shared__ __align__(16) uint16_t sKb[2][TS * KP];
-  __shared__ __align__(16) uint16_t sVb[2][TS * VP];
+  // two K/V tile buffers (the next tile is stored while this one is used),
+  // in one array: before the first tile it holds the diagonal's weights
+  __shared__ __align__(16) uint16_t smem[2 * TS * KP + 2 * TS * VP];
+  auto kbuf = [&](int buf) { return smem + buf * (TS * KP); };
+  auto vbuf = [&](int buf) { return smem + 2 * TS * KP + buf * (TS * VP); };
 
   // One-dimensional grid of B*H*nqt workgroups.  Workgroups are dealt to the
   // 8 XCDs round-robin by linear id (id L runs on XCD L % 8).  When B*H is a
-  // multiple of 8, XCD x takes the (sequence, head) pairs x, x+8, ... one
-  // after another, each pair's query tiles heaviest first: the workgroups an
-  // XCD runs at once then share the K/V rows of two or three pairs, which stay
-  // in its L2 (dealt by head instead, an XCD's working set was 16 sequences'
-  // rows, several times its L2).  Otherwise every pair takes its heaviest
-  // query tile before any lighter one.
+  // multiple of 8, XCD x takes the x-th eighth of the (sequence, head) pairs
+  // (pair = sequence*H + head), one pair after another, each pair's query
+  // tiles heaviest first: the workgroups an XCD runs at once then share the
+  // K/V rows of two or three pairs and the partial merges and rope keys of
+  // one sequence, which stay in its L2.  Otherwise every pair takes its
+  // heaviest query tile before any lighter one.
   const int nqt = a.nqt;
   const int npair = a.B * a.H;
   const int L = blockIdx.x;
   int pair, qt;
   if (npair % 8 == 0) {
     const int k = L >> 3;
-    pair = (L & 7) + 8 * (k / nqt);
+    pair = (L & 7) * (npair / 8) + k / nqt;
     qt = nqt - 1 - k % nqt;
   } else {
     pair = L % npair;
@@ -253,83 +266,16 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
 
   const uint16_t* qc = static_cast<const uint16_t*>(a.q_c);
   const uint16_t* qr = static_cast<const uint16_t*>(a.q_r);
-  const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + (static_cast<size_t>(b) * H + h) * N * DH;
-  const uint16_t* vv = static_cast<const uint16_t*>(a.v) + (static_cast<size_t>(b) * H + h) * N * DH;
   const uint16_t* Pb = static_cast<const uint16_t*>(a.partials) + static_cast<size_t>(b) * N * W;
-  // completed slot j (0-based) has its keys at row sm*j + sa of the slot
-  // arrays; the queries are tokens t0+1 .. t0+N
-  const int t0 = a.t0, sm = a.slot_mul, sa = a.slot_add;
+  // completed slot j (0-based) has K^C, V at row j of the slot arrays and its
+  // rope key at row rm*j + ra of the rope array; the queries are tokens
+  // t0+1 .. t0+N
+  const int t0 = a.t0, rm = a.rslot_mul, ra = a.rslot_add;
   const uint16_t* ksl =
       static_cast<const uint16_t*>(a.kslot) + (static_cast<size_t>(b) * H + h) * a.slot_rows * DH;
   const uint16_t* vsl =
       static_cast<const uint16_t*>(a.vslot) + (static_cast<size_t>(b) * H + h) * a.slot_rows * DH;
   const uint16_t* Rb = static_cast<const uint16_t*>(a.rslot) + static_cast<size_t>(b) * a.rslot_rows * W;
-
-  // Queries (B operands, registers) and the diagonal key j = i as the initial
-  // online-softmax state: m = score(i, i), l = 1, O = V_i.
-  f16x8 qreg[NQ][KK];
-  // The running max m enters the score product as a 7th k-chunk: the query
-  // side holds -m (element 0 of lane group 0) and the key side a constant 1,
-  // so the MFMA returns s - m with no per-score subtraction or accumulator
-  // initialisation.  m is therefore kept fp16-representable, and the
-  // diagonal's weight is taken against that same value.
-  f16x8 qm[NQ];
-  f16x8 kone;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) kone[r] = static_cast<_Float16>(grp == 0 && r == 0 ? 1.f : 0.f);
-  float m[NQ], lp[NQ];
-  f32x16 acc[DT][NQ];
-#pragma unroll
-  for (int t = 0; t < NQ; ++t) {
-    const int qi = qw0 + 32 * t + c32;  // 0-based query token
-    const bool qok = qi < N;
-    float dpart = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int d0 = 16 * kk + 8 * grp;
-      uint4 qv = uint4{0u, 0u, 0u, 0u}, kv = uint4{0u, 0u, 0u, 0u};
-      if (qok) {
-        if (d0 < DH) {
-          qv = *reinterpret_cast<const uint4*>(qc + ((static_cast<size_t>(b) * N + qi) * H + h) * DH + d0);
-          kv = *reinterpret_cast<const uint4*>(kc + static_cast<size_t>(qi) * DH + d0);
-        } else {
-          qv = *reinterpret_cast<const uint4*>(qr + ((static_cast<size_t>(b) * N + qi) * H + h) * DR + (d0 - DH));
-          kv = *reinterpret_cast<const uint4*>(Pb + static_cast<size_t>(qi) * W + a.d_c + (d0 - DH));
-        }
-      }
-      const u16x8 qs = __builtin_bit_cast(u16x8, qv), ks = __builtin_bit_cast(u16x8, kv);
-      u16x8 qsc;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float qf = bf16_bits_to_f32(qs[r]);
-        // K^C is fp16, the rope key P^R bf16
-        const float kf = d0 < DH ? f16_bits_to_f32(ks[r]) : bf16_bits_to_f32(ks[r]);
-        dpart = fmaf(qf, kf, dpart);
-        qsc[r] = f32_to_f16_bits(qf * qk_scale);
-      }
-      qreg[t][kk] = __builtin_bit_cast(f16x8, qsc);
-    }
-    dpart += __shfl_xor(dpart, 32, 64);
-    const float sii = dpart * qk_scale;
-    m[t] = f16_round(fminf(fmaxf(sii, -kMaxRef), kMaxRef));
-    const float pii = fast_exp2(sii - m[t]);
-    lp[t] = grp == 0 ? pii : 0.f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) qm[t][r] = static_cast<_Float16>(grp == 0 && r == 0 ? -m[t] : 0.f);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint2 v2 = uint2{0u, 0u};
-        if (qok)
-          v2 = *reinterpret_cast<const uint2*>(vv + static_cast<size_t>(qi) * DH + 32 * dt + 8 * j + 4 * grp);
-        acc[dt][t][4 * j + 0] = pii * f16_bits_to_f32(static_cast<uint16_t>(v2.x & 0xffffu));
-        acc[dt][t][4 * j + 1] = pii * f16_bits_to_f32(static_cast<uint16_t>(v2.x >> 16));
-        acc[dt][t][4 * j + 2] = pii * f16_bits_to_f32(static_cast<uint16_t>(v2.y & 0xffffu));
-        acc[dt][t][4 * j + 3] = pii * f16_bits_to_f32(static_cast<uint16_t>(v2.y >> 16));
-      }
-    }
-  }
 
   // completed slots (0-based) visible to this lane's queries: slot j is seen
   // by query token t0 + qi + 1 iff s (j + 1) <= t0 + qi, i.e. j < vis[t]
@@ -343,38 +289,37 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   const int full_w = (t0 + qw0) / s;
 
   // Tile loads through buffer resources bounded at the last completed slot's
-  // key row (rows_end rows): slot rows past nk read as zero and touch no
-  // memory.  Each load instruction uses one resource, so the chunks are split
+  // rows: slot rows past nk read as zero and touch no memory.  Each load instruction uses one resource, so the chunks are split
   // by kind: per thread KN chunks of K^C, RN of the rope key and KN of V (16
   // bytes each); their offsets within a tile are loop invariant and the tile
   // offset is a scalar.
   constexpr int KN = TS * DH / 8 / 256, RN = TS * DR / 8 / 256;
   static_assert(KN * 256 == TS * DH / 8 && RN * 256 == TS * DR / 8, "chunks per thread");
-  const int rows_end = nk > 0 ? sm * (nk - 1) + sa + 1 : 0;
+  const int rope_end = nk > 0 ? rm * (nk - 1) + ra + 1 : 0;
   const __amdgpu_buffer_rsrc_t rs_k = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(ksl), static_cast<short>(0), rows_end * DH * 2, kBufferRsrcWord3);
+      const_cast<uint16_t*>(ksl), static_cast<short>(0), nk * DH * 2, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(vsl), static_cast<short>(0), rows_end * DH * 2, kBufferRsrcWord3);
+      const_cast<uint16_t*>(vsl), static_cast<short>(0), nk * DH * 2, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_r = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Rb + a.d_c), static_cast<short>(0),
-      rows_end > 0 ? (rows_end - 1) * W * 2 + DR * 2 : 0, kBufferRsrcWord3);
+      rope_end > 0 ? (rope_end - 1) * W * 2 + DR * 2 : 0, kBufferRsrcWord3);
   int off_k[KN], off_r[RN], lds_k[KN], lds_r[RN], lds_v[KN];
 #pragma unroll
   for (int i = 0; i < KN; ++i) {
     const int c = tid + 256 * i, row = c / (DH / 8), cc = c % (DH / 8);
-    off_k[i] = ((sm * row + sa) * DH + cc * 8) * 2;
+    off_k[i] = (row * DH + cc * 8) * 2;
     lds_k[i] = row * KP + cc * 8;
     lds_v[i] = row * VP + cc * 8;
   }
 #pragma unroll
   for (int i = 0; i < RN; ++i) {
     const int c = tid + 256 * i, row = c / (DR / 8), cc = c % (DR / 8);
-    off_r[i] = ((sm * row + sa) * W + cc * 8) * 2;
+    off_r[i] = ((rm * row + ra) * W + cc * 8) * 2;
     lds_r[i] = row * KP + DH + cc * 8;
   }
   uint4 pk[KN], pr[RN], pv[KN];
   auto load_tile = [&](int j0) {
-    const int so_kv = sm * j0 * DH * 2, so_r = sm * j0 * W * 2;
+    const int so_kv = j0 * DH * 2, so_r = rm * j0 * W * 2;
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_k, off_k[i], so_kv, 0);
@@ -393,7 +338,7 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sKb[buf] + lds_k[i]) = pk[i];
+    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(kbuf(buf) + lds_k[i]) = pk[i];
 #pragma unroll
     for (int i = 0; i < RN; ++i) {
       // the rope key: bf16 storage to fp16 (exact in fp16's normal range)
@@ -405,11 +350,155 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
                          static_cast<_Float16>(__uint_as_float(w4[k] & 0xffff0000u))};
         h4[k] = __builtin_bit_cast(uint32_t, h);
       }
-      *reinterpret_cast<uint4*>(sKb[buf] + lds_r[i]) = uint4{h4[0], h4[1], h4[2], h4[3]};
+      *reinterpret_cast<uint4*>(kbuf(buf) + lds_r[i]) = uint4{h4[0], h4[1], h4[2], h4[3]};
     }
 #pragma unroll
-    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(sVb[buf] + lds_v[i]) = pv[i];
+    for (int i = 0; i < KN; ++i) *reinterpret_cast<uint4*>(vbuf(buf) + lds_v[i]) = pv[i];
   };
+
+  if (nk > 0) load_tile(0);
+
+  // The diagonal key j = i.  Its K^C_i = W_UK[h] P^c_i and V_i = W_UV[h] P^c_i
+  // are formed here, for the wave's queries, as D^T[e, query] = W[e, :] .
+  // P^c[query, :] on 32x32x16 bf16 MFMAs (exact products, fp32 sums).  The
+  // weights go through LDS, shared by the four waves, in rounds of RC
+  // columns of both blocks: each round's loads are issued at once straight
+  // into LDS (no registers), with the 16-byte pieces of a row permuted by
+  // piece ^ (row % 16) so that the MFMA operand reads are free of bank
+  // conflicts.  The partial merges are the B operands, read straight from
+  // memory (rows past N read as zero).  A product's layout (lane = query,
+  // rows 8(i/4) + 4 grp + i%4 of each 32-row tile) is that of the O^T
+  // accumulators, so V_i is the initial O^T as it comes out.  The first key
+  // tile's loads are already in flight.
+  constexpr int RC = 128;               // weight columns per round
+  constexpr int RP = RC / 8;            // 16-byte pieces per row and round
+  constexpr int WROWS = 2 * DH;         // the W_UK[h] rows, then W_UV[h]'s
+  constexpr int WLD = WROWS * RP / 256; // loads per thread and round
+  static_assert(WROWS * RC <= 2 * TS * KP + 2 * TS * VP, "a round of weights fits in the tile buffers");
+  static_assert(WLD % 2 == 0 && DH % 4 == 0, "each load lies wholly in one weight block");
+  const int wbytes = a.H * DH * a.d_c * 2;
+  const i32x4_t rs_wk = make_rsrc_words(a.w_uk, wbytes), rs_wv = make_rsrc_words(a.w_uv, wbytes);
+  const uint32_t lds_w = lds_addr(smem);
+  const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Pb), static_cast<short>(0), N * W * 2, kBufferRsrcWord3);
+  int poff[NQ];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) poff[t] = ((qw0 + 32 * t + c32) * W + 8 * grp) * 2;
+  f32x16 kd[DT][NQ];
+  f32x16 acc[DT][NQ];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) kd[dt][t] = acc[dt][t] = f32x16{};
+  for (int c0 = 0; c0 < a.d_c; c0 += RC) {
+    // load k of this wave writes LDS pieces 64 (4k + wave) .. + 63: rows
+    // 4 (4k + wave) .. + 3 of the round, in W_UK[h] for k < WLD/2
+#pragma unroll
+    for (int k = 0; k < WLD; ++k) {
+      const int q = (4 * k + wave) * 64 + lane;
+      const int r = q / RP, pc = (q % RP) ^ (r % RP);
+      const int voff = ((h * DH + r % DH) * a.d_c + 8 * pc) * 2;
+      const uint32_t dst = lds_w + __builtin_amdgcn_readfirstlane((4 * k + wave) * 1024);
+      buffer_load_lds16_cached(2 * k < WLD ? rs_wk : rs_wv, dst, voff, c0 * 2);
+    }
+    // the B operands of the round's (up to) RC/16 chunks
+    const int kcn = min(RC, a.d_c - c0) / 16;
+    bf16x8 pf[NQ][RC / 16];
+#pragma unroll
+    for (int kc = 0; kc < RC / 16; ++kc)
+#pragma unroll
+      for (int t = 0; t < NQ; ++t)
+        pf[t][kc] = kc < kcn ? __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               rs_p, poff[t], (c0 + 16 * kc) * 2, 0))
+                             : bf16x8{};
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int kc = 0; kc < RC / 16; ++kc) {
+      if (kc < kcn) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rk = 32 * dt + c32, rv = DH + 32 * dt + c32;  // rk % 16 == rv % 16 == c32 % 16
+          const int pc = (2 * kc + grp) ^ (c32 % RP);
+          const bf16x8 wk = *reinterpret_cast<const bf16x8*>(smem + rk * RC + 8 * pc);
+          const bf16x8 wv = *reinterpret_cast<const bf16x8*>(smem + rv * RC + 8 * pc);
+#pragma unroll
+          for (int t = 0; t < NQ; ++t) {
+            kd[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wk, pf[t][kc], kd[dt][t], 0, 0, 0);
+            acc[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, pf[t][kc], acc[dt][t], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // every wave is done with this round's weights before they are replaced
+    // (or, after the last round, overwritten by the first key tile)
+    __syncthreads();
+  }
+
+  // Queries (B operands, registers) and the diagonal key as the initial
+  // online-softmax state: m = score(i, i), l = 1, O = V_i.
+  f16x8 qreg[NQ][KK];
+  // The running max m enters the score product as a 7th k-chunk: the query
+  // side holds -m (element 0 of lane group 0) and the key side a constant 1,
+  // so the MFMA returns s - m with no per-score subtraction or accumulator
+  // initialisation.  m is therefore kept fp16-representable, and the
+  // diagonal's weight is taken against that same value.
+  f16x8 qm[NQ];
+  f16x8 kone;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) kone[r] = static_cast<_Float16>(grp == 0 && r == 0 ? 1.f : 0.f);
+  float m[NQ], lp[NQ];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    const int qi = qw0 + 32 * t + c32;  // 0-based query token
+    const bool qok = qi < N;
+    const uint16_t* qrow = qc + ((static_cast<size_t>(b) * N + qi) * H + h) * DH;
+    // q^C . K^C_i over this lane's rows of kd (the other half is in lane ^ 32)
+    float dpart = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 q2 = qok ? *reinterpret_cast<const uint2*>(qrow + 32 * dt + 8 * j + 4 * grp) : uint2{0u, 0u};
+        dpart = fmaf(__uint_as_float(q2.x << 16), kd[dt][t][4 * j + 0], dpart);
+        dpart = fmaf(__uint_as_float(q2.x & 0xffff0000u), kd[dt][t][4 * j + 1], dpart);
+        dpart = fmaf(__uint_as_float(q2.y << 16), kd[dt][t][4 * j + 2], dpart);
+        dpart = fmaf(__uint_as_float(q2.y & 0xffff0000u), kd[dt][t][4 * j + 3], dpart);
+      }
+    // the query operands, and q^R . P^R_i over this lane's half of the rope
+    // columns
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int d0 = 16 * kk + 8 * grp;
+      uint4 qv = uint4{0u, 0u, 0u, 0u}, kv = uint4{0u, 0u, 0u, 0u};
+      if (qok) {
+        if (d0 < DH) {
+          qv = *reinterpret_cast<const uint4*>(qrow + d0);
+        } else {
+          qv = *reinterpret_cast<const uint4*>(qr + ((static_cast<size_t>(b) * N + qi) * H + h) * DR + (d0 - DH));
+          kv = *reinterpret_cast<const uint4*>(Pb + static_cast<size_t>(qi) * W + a.d_c + (d0 - DH));
+        }
+      }
+      const u16x8 qs = __builtin_bit_cast(u16x8, qv), ks = __builtin_bit_cast(u16x8, kv);
+      u16x8 qsc;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float qf = bf16_bits_to_f32(qs[r]);
+        if (d0 >= DH) dpart = fmaf(qf, bf16_bits_to_f32(ks[r]), dpart);
+        qsc[r] = f32_to_f16_bits(qf * qk_scale);
+      }
+      qreg[t][kk] = __builtin_bit_cast(f16x8, qsc);
+    }
+    dpart += __shfl_xor(dpart, 32, 64);
+    const float sii = dpart * qk_scale;
+    m[t] = f16_round(fminf(fmaxf(sii, -kMaxRef), kMaxRef));
+    const float pii = fast_exp2(sii - m[t]);
+    lp[t] = grp == 0 ? pii : 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) qm[t][r] = static_cast<_Float16>(grp == 0 && r == 0 ? -m[t] : 0.f);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt][t] *= pii;
+  }
 
   // Tile j0 sits in buffer `buf` at the top of each iteration and the loads
   // of tile j0+TS are in flight; the iteration stores tile j0+TS into the
@@ -417,7 +506,6 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
   // tile loop's only barrier.
   int buf = 0;
   if (nk > 0) {
-    load_tile(0);
     store_tile(0);
     if (TS < nk) load_tile(TS);
   }
@@ -427,8 +515,8 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
       store_tile(buf ^ 1);
       if (j0 + 2 * TS < nk) load_tile(j0 + 2 * TS);
     }
-    const uint16_t* sK = sKb[buf];
-    const uint16_t* sV = sVb[buf];
+    const uint16_t* sK = kbuf(buf);
+    const uint16_t* sV = vbuf(buf);
 
     if (j0 < nk_w) {
       // S^T = K Q^T - m: sc[rt][t][i] = score(slot j0 + 32rt + 8(i/4) + 4grp + i%4,
@@ -579,13 +667,15 @@ bool prefill_mfma_supported(int H, int d_h, int d_c, int d_r) {
   return shape && d_c % GBK == 0 && (H * d_h) % GBN == 0;
 }
 
-hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
-                            const void* partials, const void* w_uk, const void* w_uv,
-                            void* k_out, void* v_out, bool out_fp16, hipStream_t st) {
-  const int M = B * N;
+hipError_t launch_prefill_kv(int B, int n_rows, int a_seq_rows, int a_mul, int a_add, int H, int d_h, int d_c,
+                            int d_r, const void* a, const void* w_uk, const void* w_uv, void* k_out, void* v_out,
+                            bool out_fp16, hipStream_t st) {
+  const int M = B * n_rows;
+  if (M == 0) return hipSuccess;
   dim3 grid((2 * H * d_h) / GBN, (M + GBM - 1) / GBM);
   auto args = [&](auto kern) {
-    kern<<<grid, 256, 0, st>>>(M, N, H, d_h, d_c, d_c + d_r, static_cast<const uint16_t*>(partials),
+    kern<<<grid, 256, 0, st>>>(B, n_rows, a_seq_rows, a_mul, a_add, H, d_h, d_c, d_c + d_r,
+                               static_cast<const uint16_t*>(a),
                                static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv),
                                static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
   };
@@ -596,16 +686,9 @@ hipError_t launch_prefill_kv(int B, int N, int H, int d_h, int d_c, int d_r,
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_attn(const PrefillAttnArgs& a0, hipStream_t st) {
-  PrefillAttnArgs a = a0;
-  if (!a.kslot) {  // slot keys from the token-indexed arrays: slot j is token s*j + s - 1
-    a.kslot = a.kc;
-    a.vslot = a.v;
-    a.rslot = a.partials;
-    a.slot_rows = a.rslot_rows = a.N;
-    a.slot_mul = a.s;
-    a.slot_add = a.s - 1;
-  }
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t st) {
+  if (a.B == 0 || a.N == 0) return hipSuccess;
+  if (a.d_c % 32 != 0) return hipErrorInvalidValue;
   if (a.d_h == 64 && a.d_r == 32) {
     constexpr int nq = kPrefillQueryTiles;
     PrefillAttnArgs b = a;

@@ -356,7 +356,8 @@ def test_staged_prefill_needs_the_mfma_path():
     L = m.lib()
     for d in (dims(dtype=m.MTLA_FP32), dims(d_h=48)):
         assert L.mtla_prefill_keys(ctypes.byref(d), 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == m.MTLA_ERR_UNSUPPORTED
-        assert L.mtla_prefill_attention(ctypes.byref(d), 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+        assert L.mtla_prefill_attention(ctypes.byref(d), 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        None) == \
             m.MTLA_ERR_UNSUPPORTED
     assert L.mtla_prefill_partials(ctypes.byref(dims()), 16, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, None) == \
         m.MTLA_ERR_INVALID_ARG          # pe_rows < n_tokens

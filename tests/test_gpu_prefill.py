@@ -159,17 +159,25 @@ def test_staged_prefill_equals_one_call(shape, s, B, N):
     one = a.prefill(N)
     d = b_.d
     P = torch.empty(B, N, d.width, dtype=torch.bfloat16, device=DEV)
-    kc = torch.empty(B, d.heads, N, d.d_h, dtype=torch.float16, device=DEV)
+    S = m.prefill_slot_keys(d, N)
+    assert S == (N - 1) // s
+    kc = torch.empty(B, d.heads, S, d.d_h, dtype=torch.float16, device=DEV)
     v = torch.empty_like(kc)
     out = torch.empty_like(one)
     m.mtla_prefill_partials(d, b_.c[:, :N].contiguous(), b_.k_r[:, :N].contiguous(), b_.w_hyp, b_.pe, b_.cache,
                             b_.open_acc, P)
     m.mtla_prefill_keys(d, P, b_.w_uk, b_.w_uv, kc, v)
-    m.mtla_prefill_attention(d, b_.q_c[:, :N].contiguous(), b_.q_r[:, :N].contiguous(), P, kc, v, out)
+    m.mtla_prefill_attention(d, b_.q_c[:, :N].contiguous(), b_.q_r[:, :N].contiguous(), P, b_.w_uk, b_.w_uv,
+                             kc, v, out)
     assert torch.equal(bits(out), bits(one))
     assert torch.equal(bits(a.cache), bits(b_.cache))
     assert torch.equal(a.open_state(N), b_.open_state(N))
-    # the staged keys are K^C = W_UK P^c and V = W_UV P^c of the staged partial merges
-    Pc = P.float()[..., :d.d_c]
-    want_k = torch.einsum("hek,bnk->bhne", b_.w_uk.float(), Pc)
-    assert (kc.float() - want_k).abs().max().item() <= 2e-3 * want_k.abs().max().item()
+    # the staged keys are K^C = W_UK P^c_{s b} and V = W_UV P^c_{s b} of the
+    # completed slots b = 1 .. (N-1)//s (partial-merge rows s*b - 1, 0-based),
+    # which are also the cache's slot rows
+    rows = torch.arange(S, device=DEV) * s + (s - 1)
+    Pc = P.float()[:, rows, :d.d_c]
+    assert torch.equal(bits(P[:, rows]), bits(b_.cache[:, :S]))
+    for name, w, got in (("K", b_.w_uk, kc), ("V", b_.w_uv, v)):
+        want = torch.einsum("hek,bnk->bhne", w.float(), Pc)
+        assert (got.float() - want).abs().max().item() <= 2e-3 * want.abs().max().item(), name
