@@ -7,10 +7,21 @@ namespace mtla {
 
 namespace {
 
-template <typename T>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a, int blocks_per_wg,
-                                                              int write_open) {
-  merge_blocks<T>(a, blockIdx.y, blockIdx.x, blocks_per_wg, write_open);
+// XMAP: a one-dimensional grid of 8 * cpx * B workgroups in which XCD x
+// (workgroups are dealt to the 8 XCDs round-robin by linear id) takes runs
+// x*cpx .. x*cpx + cpx - 1 of every sequence, so the pe rows of those tokens
+// are fetched into one L2; otherwise grid (runs, B).
+template <typename T, bool STAGE, bool XMAP>
+__global__ __launch_bounds__(kMergeThreads) __attribute__((amdgpu_waves_per_eu(4))) void merge_kernel(MergeArgs a, int blocks_per_wg, int write_open,
+                                                              int chunks, int cpx) {
+  if constexpr (XMAP) {
+    const int L = blockIdx.x, k = L >> 3;
+    const int chunk = (L & 7) * cpx + k / a.B, b = k % a.B;
+    if (chunk >= chunks) return;
+    merge_blocks<T, false, STAGE>(a, b, chunk, blocks_per_wg, write_open);
+  } else {
+    merge_blocks<T, false, STAGE>(a, blockIdx.y, blockIdx.x, blocks_per_wg, write_open);
+  }
 }
 
 // When one call spans several workgroups per sequence, the open-slot state is
@@ -139,20 +150,35 @@ hipError_t launch_merge(const MergeArgs& a, int dtype, hipStream_t st) {
   long long per = (max_blocks * a.B + 2047) / 2048;
   const int blocks_per_wg = static_cast<int>(per < 1 ? 1 : (per > cap ? cap : per));
   const long long chunks = (max_blocks + blocks_per_wg - 1) / blocks_per_wg;
-  // The merge kernel writes the open-slot state itself only for a one-token
+  // The merge kernel writes the open-slot state itself when no block of the
+  // call continues one that began before it (nothing reads the old state:
+  // every appended token starts or extends a block of this call; the host
+  // knows this when all sequences start at one position), or for a one-token
   // call: the thread that reads the old state (a continued block) is then the
-  // thread that writes the new one, after its read.  With more tokens the
-  // continued block and the last block may belong to threads of different
-  // waves with no barrier between them, and for an even token count the read
-  // and the write address the same half of open_acc, so merge_tail_kernel
-  // writes the state after the merge kernel has finished.
-  const int write_open = (chunks == 1 && max_blocks == 1) ? 1 : 0;
-  dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(a.B));
+  // thread that writes the new one, after its read.  Otherwise the continued
+  // block and the last block may belong to threads of different waves with
+  // no barrier between them, and for an even token count the read and the
+  // write address the same half of open_acc, so merge_tail_kernel writes the
+  // state after the merge kernel has finished.
+  const bool fresh = a.pos0 == nullptr && (a.p0_all - 1) % a.s == 0;
+  const int write_open = fresh || (chunks == 1 && max_blocks == 1) ? 1 : 0;
+  // The c rows of a workgroup's tokens stay in LDS from the gate pass to the
+  // merge (bf16, at most kStageTokens tokens per workgroup).
+  const bool stage = dtype == 1 && blocks_per_wg * a.s <= kStageTokens;
+  const int cpx = static_cast<int>((chunks + 7) / 8);
+  const bool xmap = chunks >= 8;
+  const dim3 grid = xmap ? dim3(static_cast<unsigned>(8 * cpx * a.B)) : dim3(static_cast<unsigned>(chunks), a.B);
+  auto go = [&](auto kern) {
+    kern<<<grid, kMergeThreads, 0, st>>>(a, blocks_per_wg, write_open, static_cast<int>(chunks), cpx);
+  };
   if (dtype == 0) {
-    merge_kernel<float><<<grid, kMergeThreads, 0, st>>>(a, blocks_per_wg, write_open);
+    if (xmap) go(merge_kernel<float, false, true>); else go(merge_kernel<float, false, false>);
     if (!write_open) merge_tail_kernel<float><<<a.B, kMergeThreads, 0, st>>>(a);
   } else {
-    merge_kernel<uint16_t><<<grid, kMergeThreads, 0, st>>>(a, blocks_per_wg, write_open);
+    if (stage && xmap) go(merge_kernel<uint16_t, true, true>);
+    else if (stage) go(merge_kernel<uint16_t, true, false>);
+    else if (xmap) go(merge_kernel<uint16_t, false, true>);
+    else go(merge_kernel<uint16_t, false, false>);
     if (!write_open) merge_tail_kernel<uint16_t><<<a.B, kMergeThreads, 0, st>>>(a);
   }
   return hipGetLastError();

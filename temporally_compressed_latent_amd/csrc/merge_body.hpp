@@ -84,8 +84,11 @@ __device__ void compute_gates(const MergeArgs& a, int b, int p0, int ta, int nto
 // the decode-step kernels).  Token indices past the last are clamped (their
 // gates are computed and dropped), so the loads are unconditional.  PP: one
 // W_hyp row per place in the block, loaded with each token.
+// stage (optional, LDS): row k of it receives c of token ta + k, for the
+// merge that follows (the values as loaded, so the merge's bits do not change).
 template <typename T, int GE, int NTOK, bool PP>
-__device__ void compute_gates_lanes(const MergeArgs& a, int b, int p0, int ta, int ntok, float* gw) {
+__device__ void compute_gates_lanes(const MergeArgs& a, int b, int p0, int ta, int ntok, float* gw,
+                                    T* stage = nullptr) {
   const T* c = static_cast<const T*>(a.c);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -99,7 +102,8 @@ __device__ void compute_gates_lanes(const MergeArgs& a, int b, int p0, int ta, i
     float x[NTOK][GE], pv[NTOK][GE];
 #pragma unroll
     for (int k = 0; k < NTOK; ++k) {
-      const int t = ta + min(k0 + k * nwaves, ntok - 1);
+      const int kc = min(k0 + k * nwaves, ntok - 1);
+      const int t = ta + kc;
       const T* row = c + (static_cast<size_t>(b) * a.T + (t - p0)) * a.d_c;
       const float* per = a.pe + static_cast<size_t>(t - 1) * a.d_c;
       const float* whr = a.w_hyp + static_cast<size_t>((t - 1) % a.s) * a.wh_stride;
@@ -108,6 +112,10 @@ __device__ void compute_gates_lanes(const MergeArgs& a, int b, int p0, int ta, i
         x[k][j] = Store<T>::load(row, lane + 64 * j);
         pv[k][j] = per[lane + 64 * j];
         if constexpr (PP) wh[k][j] = whr[lane + 64 * j];
+      }
+      if (stage) {
+#pragma unroll
+        for (int j = 0; j < GE; ++j) Store<T>::store(stage, static_cast<size_t>(kc) * a.d_c + lane + 64 * j, x[k][j]);
       }
     }
 #pragma unroll
@@ -124,16 +132,20 @@ __device__ void compute_gates_lanes(const MergeArgs& a, int b, int p0, int ta, i
 
 // ONE: a single token (the gate loads of one pass shrink to one token's;
 // the gate's arithmetic, and so its bits, do not change).
+// stage: see compute_gates_lanes; only the d_c = 256 and 512 paths fill it
+// (gates_stage_c says which).
+__device__ __forceinline__ bool gates_stage_c(const MergeArgs& a) { return a.d_c == 256 || a.d_c == 512; }
+
 template <typename T, bool ONE = false>
-__device__ void merge_gates(const MergeArgs& a, int b, int p0, int ta, int ntok, float* gw) {
+__device__ void merge_gates(const MergeArgs& a, int b, int p0, int ta, int ntok, float* gw, T* stage = nullptr) {
   if (a.d_c == 256 && a.wh_stride == 0)
-    compute_gates_lanes<T, 4, ONE ? 1 : 8, false>(a, b, p0, ta, ntok, gw);
+    compute_gates_lanes<T, 4, ONE ? 1 : 8, false>(a, b, p0, ta, ntok, gw, stage);
   else if (a.d_c == 256)
-    compute_gates_lanes<T, 4, ONE ? 1 : 8, true>(a, b, p0, ta, ntok, gw);
+    compute_gates_lanes<T, 4, ONE ? 1 : 8, true>(a, b, p0, ta, ntok, gw, stage);
   else if (a.d_c == 512 && a.wh_stride == 0)
-    compute_gates_lanes<T, 8, ONE ? 1 : 4, false>(a, b, p0, ta, ntok, gw);
+    compute_gates_lanes<T, 8, ONE ? 1 : 4, false>(a, b, p0, ta, ntok, gw, stage);
   else if (a.d_c == 512)
-    compute_gates_lanes<T, 8, ONE ? 1 : 4, true>(a, b, p0, ta, ntok, gw);
+    compute_gates_lanes<T, 8, ONE ? 1 : 4, true>(a, b, p0, ta, ntok, gw, stage);
   else
     compute_gates<T>(a, b, p0, ta, ntok, gw);
 }
@@ -154,10 +166,15 @@ __device__ __forceinline__ void token_chunk(const MergeArgs& a, int b, int tok, 
 // takes 8-column chunk ch of block blo + bb for (bb, ch) = (t / CPB, t % CPB),
 // CPB = W / 8 (and further blocks in steps of 256 / CPB), and walks that
 // block's tokens in order carrying the fp32 sums.  The open-slot state is
-// written only if write_open (see launch_merge).  ONE: a.T == 1.
-template <typename T, bool ONE = false>
+// written only if write_open (see launch_merge).  ONE: a.T == 1.  STAGE: the
+// workgroup's tokens are at most kStageTokens, and the gate pass leaves their
+// c rows in LDS (d_c = 256 or 512), so the merge reads them from there
+// instead of from memory a second time.
+constexpr int kStageTokens = 32;
+template <typename T, bool ONE = false, bool STAGE = false>
 __device__ void merge_blocks(const MergeArgs& a, int b, int chunk, int blocks_per_wg, int write_open) {
   __shared__ float gw[kMaxChunkTokens];
+  __shared__ __align__(16) T xs[STAGE ? kStageTokens * 512 : 1];
   const SeqRange r = seq_range(a, b);
   if (!r.ok) return;
   const int s = a.s;
@@ -167,7 +184,8 @@ __device__ void merge_blocks(const MergeArgs& a, int b, int chunk, int blocks_pe
   const int bhi = min(r.bk1, blo + blocks_per_wg - 1);
   const int ta = max(r.p0, blo * s + 1);
   const int tb = min(r.t_last, bhi * s + s);
-  merge_gates<T, ONE>(a, b, r.p0, ta, tb - ta + 1, gw);
+  const bool staged = STAGE && gates_stage_c(a);
+  merge_gates<T, ONE>(a, b, r.p0, ta, tb - ta + 1, gw, staged ? xs : nullptr);
   __syncthreads();
 
   T* cache = static_cast<T*>(a.cache);
@@ -196,7 +214,12 @@ __device__ void merge_blocks(const MergeArgs& a, int b, int chunk, int blocks_pe
     for (int t = t0; t <= t1; t += 4) {
       float x[4][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) token_chunk<T>(a, b, min(t + u, t1) - r.p0, e, x[u]);
+      for (int u = 0; u < 4; ++u) {
+        if (staged && e < a.d_c)
+          load8(xs + static_cast<size_t>(min(t + u, t1) - ta) * a.d_c + e, x[u]);
+        else
+          token_chunk<T>(a, b, min(t + u, t1) - r.p0, e, x[u]);
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (t + u <= t1) {
