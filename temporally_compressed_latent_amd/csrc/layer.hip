@@ -19,6 +19,7 @@
 // splits K over the waves instead, many rows in bf16 a 128 x 128 MFMA
 // variant.
 #include "common.hpp"
+#include "gemm_tile.hpp"
 #include "kernels.hpp"
 
 namespace mtla {
@@ -350,10 +351,13 @@ constexpr int MCP = MBN + 4;  // C half-tile pitch (floats)
 // MBK: the K step (32 for short K: half the LDS, three workgroups per CU
 // instead of two, which hides more load latency when there are few steps;
 // 64 for long K).
+// MBK = 0: the K loop of gemm_tile_128 (K a multiple of 32); otherwise K
+// steps of MBK through two register sets and two LDS buffers (any K that is
+// a multiple of 8).
 template <int MBK>
 __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, int nrt, int nct) {
   constexpr int MP = MBK + 8;  // operand pitch (elements)
-  __shared__ __align__(16) uint16_t smem[2 * (MBM + MBN) * MP];
+  __shared__ __align__(16) uint16_t smem[MBK == 0 ? kTileSmemElems : 2 * (MBM + MBN) * MP];
   __shared__ int sPos[MBM];
   static_assert(64 * MCP * 4 <= sizeof(smem), "C half tile fits in the operand buffers");
   const int L = blockIdx.x;
@@ -364,8 +368,20 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
   const int M = g.M, N = g.N, K = g.K, lda = g.lda ? g.lda : K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, grp = lane >> 5, c32 = lane & 31;
+  f32x16 acc[2][2];
+  if constexpr (MBK == 0) {
+    const uint16_t* arow[2];
+    const uint16_t* wrow[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = 16 * (4 * k + wave) + (lane >> 2);
+      arow[k] = static_cast<const uint16_t*>(g.A) + static_cast<size_t>(min(m0 + r, M - 1)) * lda;
+      wrow[k] = weight_row<uint16_t>(g, min(n0 + r, N - 1));
+    }
+    gemm_tile_128<false>(arow, wrow, K, smem, acc);
+  } else {
   // per stage and operand 128 rows x 64 k = 1024 chunks of 8: 4 per thread
-  constexpr int CPT = MBM * MBK / 8 / 256;
+  constexpr int CPT = MBM * (MBK > 0 ? MBK : 8) / 8 / 256;
   const uint16_t* arow[CPT];
   const uint16_t* wrow[CPT];
   int kofs[CPT], lofs[CPT];
@@ -408,7 +424,6 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
       *reinterpret_cast<uint4*>(sW + lofs[i]) = uint4{vw.x & keep, vw.y & keep, vw.z & keep, vw.w & keep};
     }
   };
-  f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -457,6 +472,7 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
   if (kt < nk) {  // odd step count: the last step is in buffer 0
     compute(0);
     __syncthreads();
+  }
   }
 
   // epilogue, one 64-row half at a time: acc[i][j][e] is row
@@ -608,7 +624,9 @@ hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st) 
   }
   if (dtype != 0) {
     const int nrt = (g.M + MBM - 1) / MBM, nct = (g.N + MBN - 1) / MBN;
-    if (g.K <= 1024)
+    if (g.K % 32 == 0)
+      layer_gemm_mfma_kernel<0><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);
+    else if (g.K <= 1024)
       layer_gemm_mfma_kernel<32><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);
     else
       layer_gemm_mfma_kernel<64><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);

@@ -17,6 +17,7 @@
 //               0 .. floor((i_max-1)/s); only boundary tiles are masked, tiles
 //               past the last visible slot are never visited.
 #include "common.hpp"
+#include "gemm_tile.hpp"
 #include "kernels.hpp"
 
 namespace mtla {
@@ -28,11 +29,11 @@ namespace {
 //   A  = P^c: the rows of partial merges or of cache slots that are keys
 //        (a row selection per sequence), row stride W, K = d_c
 //   Bw = [W_UK ; W_UV] viewed as [2*H*d_h, d_c]
-// 128x128 output tile per workgroup, 4 waves in a 2x2 grid of 64x64, K step
-// 32, double-buffered LDS.  Output column col -> (K or V, head, e).
+// 128x128 output tiles (gemm_tile_128, transposed product), staged through
+// LDS as fp16 or bf16 and written as 16-byte row chunks.  Output column col
+// -> (K or V, head, e).
 // ---------------------------------------------------------------------------
 constexpr int GBM = 128, GBN = 128, GBK = 32;
-constexpr int GP = GBK + 8;  // LDS pitch (elements)
 
 template <bool F16OUT>
 __global__ __launch_bounds__(256) void prefill_kv_kernel(int B, int N, int a_seq_rows, int a_mul, int a_add,
@@ -42,10 +43,9 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int B, int N, int a_seq
                                                         const uint16_t* __restrict__ w_uv,
                                                         uint16_t* __restrict__ kout,
                                                         uint16_t* __restrict__ vout) {
-  __shared__ __align__(16) uint16_t sA[2][GBM * GP];
-  __shared__ __align__(16) uint16_t sB[2][GBN * GP];
+  __shared__ __align__(16) uint16_t smem[kTileSmemElems];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int grp = lane >> 5, c32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
   // Tile order: workgroups are dealt to the 8 XCDs round-robin by linear id
   // (id L runs on XCD L % 8).  Tiles are numbered row-major (the column tiles
@@ -60,106 +60,49 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int B, int N, int a_seq
   const int HD = H * d_h;
   const int M = B * N;
 
-  // Each thread copies 2 chunks of A and 2 of B per K step (16 B each).  A
-  // goes through a buffer resource over its B*a_seq_rows rows; output row m
-  // (sequence m / N, row j = m % N) reads input row a_seq_rows*(m / N) +
-  // a_mul*j + a_add, and rows past M point one whole array past the end, so
-  // they read as zero.  The B tile lies wholly in W_UK or in W_UV (HD is a
-  // multiple of GBN), so its base is uniform.
-  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A), static_cast<short>(0), B * a_seq_rows * W * 2, kBufferRsrcWord3);
+  // Output row m (sequence m / N, row j = m % N) reads input row
+  // a_seq_rows*(m / N) + a_mul*j + a_add; rows past M read row M - 1 (their
+  // products are not stored).  The 128 weight rows of a column tile lie
+  // wholly in W_UK or in W_UV (HD is a multiple of GBN).
   const uint16_t* bmat = col0 < HD ? w_uk + static_cast<size_t>(col0) * d_c
                                    : w_uv + static_cast<size_t>(col0 - HD) * d_c;
-  // Two K steps are in flight: each step's chunks land in one of two named
-  // register sets (not arrays, so they are never placed in scratch) and go
-  // to LDS one step later.
-  const int r0 = tid >> 2, r1 = (tid + 256) >> 2, ch = tid & 3;  // chunk (r, ch), two per thread
-  auto a_row = [&](int m) {
-    return m < M ? (m / N) * a_seq_rows + (m % N) * a_mul + a_add : B * a_seq_rows;
-  };
-  const int aoff0 = (a_row(row0 + r0) * W + ch * 8) * 2, aoff1 = (a_row(row0 + r1) * W + ch * 8) * 2;
-  struct Regs {
-    uint4 a0, a1, b0, b1;
-  };
-  auto gload = [&](Regs& R, int k0) {
-    const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rs_a, aoff0, k0 * 2, 0);
-    const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rs_a, aoff1, k0 * 2, 0);
-    R.a0 = uint4{v0[0], v0[1], v0[2], v0[3]};
-    R.a1 = uint4{v1[0], v1[1], v1[2], v1[3]};
-    R.b0 = *reinterpret_cast<const uint4*>(bmat + static_cast<size_t>(r0) * d_c + k0 + ch * 8);
-    R.b1 = *reinterpret_cast<const uint4*>(bmat + static_cast<size_t>(r1) * d_c + k0 + ch * 8);
-    // keep the loads where they are issued (the scheduler would sink them
-    // towards their LDS stores, which then wait for a full round trip)
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto lstore = [&](const Regs& R, int buf) {
-    *reinterpret_cast<uint4*>(&sA[buf][r0 * GP + ch * 8]) = R.a0;
-    *reinterpret_cast<uint4*>(&sA[buf][r1 * GP + ch * 8]) = R.a1;
-    *reinterpret_cast<uint4*>(&sB[buf][r0 * GP + ch * 8]) = R.b0;
-    *reinterpret_cast<uint4*>(&sB[buf][r1 * GP + ch * 8]) = R.b1;
-  };
-
-  f32x4 acc[4][4];
+  const uint16_t* arow[2];
+  const uint16_t* wrow[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf) {
-    bf16x8 af[4], bfr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 64 + i * 16 + c16) * GP + 8 * g]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wn * 64 + j * 16 + c16) * GP + 8 * g]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-  };
-
-  // step kt is computed from LDS buffer kt & 1; while it is, step kt + 1 sits
-  // in registers (stored after the compute) and step kt + 2 is being loaded
-  const int nk = d_c / GBK;
-  Regs R0, R1;
-  gload(R0, 0);
-  gload(R1, min(1, nk - 1) * GBK);
-  lstore(R0, 0);
-  __syncthreads();
-  // (the loads are issued unconditionally, steps past the end re-reading the
-  // last one, so that the waits before the LDS stores count only the older set)
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    gload(R0, min(kt + 2, nk - 1) * GBK);
-    compute(0);
-    lstore(R1, 1);
-    __syncthreads();
-    gload(R1, min(kt + 3, nk - 1) * GBK);
-    compute(1);
-    lstore(R0, 0);  // unconditional, or the loads would be sunk next to it
-    __syncthreads();
+  for (int k = 0; k < 2; ++k) {
+    const int r = 16 * (4 * k + wave) + (lane >> 2);
+    const int m = min(row0 + r, M - 1);
+    arow[k] = A + static_cast<size_t>((m / N) * a_seq_rows + (m % N) * a_mul + a_add) * W;
+    wrow[k] = bmat + static_cast<size_t>(r) * d_c;
   }
-  if (kt < nk) {  // odd step count: the last step is in buffer 0
-    compute(0);
-    __syncthreads();
-  }
+  f32x16 acc[2][2];
+  gemm_tile_128<true>(arow, wrow, d_c, smem, acc);
 
-  // Epilogue: stage the 128x128 tile as fp16 (F16OUT) or bf16 in LDS (reusing
-  // the operand buffers), then write each (token, head) row of d_h values
-  // with 16-byte stores.  acc[i][j][q] is row wm*64 + i*16 + 4g + q, column
-  // wn*64 + j*16 + c16.
+  // Epilogue: stage the 128x128 tile as fp16 (F16OUT) or bf16 in LDS, then
+  // write each (token, head) row of d_h values with 16-byte stores.
+  // acc[i][j][e] is row 64 wm + 32 i + c32, column 64 wn + 32 j + 8 (e / 4)
+  // + 4 grp + e % 4: one 8-byte LDS store per four values.
   constexpr int CP = GBN + 8;
-  static_assert(GBM * CP <= 2 * 2 * GBM * GP, "C tile must fit in the operand buffers");
-  uint16_t* sC = &sA[0][0];
+  static_assert(GBM * CP <= kTileSmemElems, "C tile must fit in the operand stages");
+  uint16_t* sC = smem;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        sC[(wm * 64 + i * 16 + 4 * g + q) * CP + wn * 64 + j * 16 + c16] =
-            F16OUT ? f32_to_f16_bits(acc[i][j][q]) : f32_to_bf16_bits(acc[i][j][q]);
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x16& c = acc[i][j];
+        uint32_t w0, w1;
+        if constexpr (F16OUT) {
+          w0 = f32_to_f16_bits(c[4 * e4]) | (uint32_t(f32_to_f16_bits(c[4 * e4 + 1])) << 16);
+          w1 = f32_to_f16_bits(c[4 * e4 + 2]) | (uint32_t(f32_to_f16_bits(c[4 * e4 + 3])) << 16);
+        } else {
+          w0 = f32_to_bf16_bits(c[4 * e4]) | (uint32_t(f32_to_bf16_bits(c[4 * e4 + 1])) << 16);
+          w1 = f32_to_bf16_bits(c[4 * e4 + 2]) | (uint32_t(f32_to_bf16_bits(c[4 * e4 + 3])) << 16);
+        }
+        *reinterpret_cast<uint2*>(&sC[(64 * wm + 32 * i + c32) * CP + 64 * wn + 32 * j + 8 * e4 + 4 * grp]) =
+            uint2{w0, w1};
+      }
   __syncthreads();
   const bool isk = col0 < HD;
   uint16_t* dst = isk ? kout : vout;
