@@ -351,34 +351,39 @@ constexpr int MCP = MBN + 4;  // C half-tile pitch (floats)
 // MBK: the K step (32 for short K: half the LDS, three workgroups per CU
 // instead of two, which hides more load latency when there are few steps;
 // 64 for long K).
-// MBK = 0: the K loop of gemm_tile_128 (K a multiple of 32); otherwise K
-// steps of MBK through two register sets and two LDS buffers (any K that is
-// a multiple of 8).
+// MBK = 0: 256-row tiles on gemm_tile (K a multiple of 32); otherwise
+// 128-row tiles, K steps of MBK through two register sets and two LDS
+// buffers (any K that is a multiple of 8).
+template <int MBK>
+constexpr int layer_tile_rows() { return MBK == 0 ? 256 : MBM; }
+
 template <int MBK>
 __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, int nrt, int nct) {
   constexpr int MP = MBK + 8;  // operand pitch (elements)
-  __shared__ __align__(16) uint16_t smem[MBK == 0 ? kTileSmemElems : 2 * (MBM + MBN) * MP];
-  __shared__ int sPos[MBM];
-  static_assert(64 * MCP * 4 <= sizeof(smem), "C half tile fits in the operand buffers");
+  constexpr int TMR = layer_tile_rows<MBK>(), NI = TMR / 64;
+  __shared__ __align__(16) uint16_t smem[MBK == 0 ? TileShape<256>::SmemElems : 2 * (MBM + MBN) * MP];
+  __shared__ int sPos[TMR];
+  static_assert(64 * MCP * 4 <= sizeof(smem), "C quarter tile fits in the operand buffers");
   const int L = blockIdx.x;
   const int xcd = L & 7, k8 = L >> 3;
   const int rt = 8 * (k8 / nct) + xcd, ct = k8 % nct;
   if (rt >= nrt) return;
-  const int m0 = rt * MBM, n0 = ct * MBN;
+  const int m0 = rt * TMR, n0 = ct * MBN;
   const int M = g.M, N = g.N, K = g.K, lda = g.lda ? g.lda : K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, grp = lane >> 5, c32 = lane & 31;
-  f32x16 acc[2][2];
+  f32x16 acc[NI][2];
   if constexpr (MBK == 0) {
-    const uint16_t* arow[2];
+    const uint16_t* arow[NI];
     const uint16_t* wrow[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < NI; ++k) {
       const int r = 16 * (4 * k + wave) + (lane >> 2);
       arow[k] = static_cast<const uint16_t*>(g.A) + static_cast<size_t>(min(m0 + r, M - 1)) * lda;
-      wrow[k] = weight_row<uint16_t>(g, min(n0 + r, N - 1));
     }
-    gemm_tile_128<false>(arow, wrow, K, smem, acc);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) wrow[k] = weight_row<uint16_t>(g, min(n0 + 16 * (4 * k + wave) + (lane >> 2), N - 1));
+    gemm_tile<256, false>(arow, wrow, K, smem, acc);
   } else {
   // per stage and operand 128 rows x 64 k = 1024 chunks of 8: 4 per thread
   constexpr int CPT = MBM * (MBK > 0 ? MBK : 8) / 8 / 256;
@@ -475,23 +480,26 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
   }
   }
 
-  // epilogue, one 64-row half at a time: acc[i][j][e] is row
-  // 64 wm + 32 i + 8 (e / 4) + 4 grp + e % 4, column 64 wn + 32 j + c32.
+  // epilogue, one 64-row quarter at a time: acc[i][j][e] is row
+  // (TMR/2) wm + 32 i + 8 (e / 4) + 4 grp + e % 4, column 64 wn + 32 j + c32.
   // The rows' token positions (rope pairs) are computed once per row.
   float* sC = reinterpret_cast<float*>(smem);
   const int pc = tid & 63, n = n0 + 2 * pc;
   const PairStore ps = pair_store(g, min(n, N - 2));
-  if (g.mode != 0 && tid < MBM) sPos[tid] = row_position(g, min(m0 + tid, M - 1));
+  if (g.mode != 0)
+    for (int r = tid; r < TMR; r += 256) sPos[r] = row_position(g, min(m0 + r, M - 1));
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    if (wm == hh) {
+  for (int hh = 0; hh < TMR / 64; ++hh) {
+    // quarter hh: rows 32 i of wave row hh / (NI / 2), i = 2 (hh % (NI / 2)) + 0, 1
+    if (wm == hh / (NI / 2)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            sC[(32 * i + 8 * (e / 4) + 4 * grp + (e % 4)) * MCP + 64 * wn + 32 * j + c32] = acc[i][j][e];
+            sC[(32 * i + 8 * (e / 4) + 4 * grp + (e % 4)) * MCP + 64 * wn + 32 * j + c32] =
+                acc[2 * (hh % (NI / 2)) + i][j][e];
     }
     __syncthreads();
     if (n < N) {
@@ -624,9 +632,10 @@ hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st) 
   }
   if (dtype != 0) {
     const int nrt = (g.M + MBM - 1) / MBM, nct = (g.N + MBN - 1) / MBN;
-    if (g.K % 32 == 0)
-      layer_gemm_mfma_kernel<0><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);
-    else if (g.K <= 1024)
+    if (g.K % 32 == 0) {
+      const int nrt2 = (g.M + 255) / 256;
+      layer_gemm_mfma_kernel<0><<<dim3(8 * ((nrt2 + 7) / 8) * nct), 256, 0, st>>>(g, nrt2, nct);
+    } else if (g.K <= 1024)
       layer_gemm_mfma_kernel<32><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);
     else
       layer_gemm_mfma_kernel<64><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);

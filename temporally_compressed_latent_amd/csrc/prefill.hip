@@ -29,21 +29,21 @@ namespace {
 //   A  = P^c: the rows of partial merges or of cache slots that are keys
 //        (a row selection per sequence), row stride W, K = d_c
 //   Bw = [W_UK ; W_UV] viewed as [2*H*d_h, d_c]
-// 128x128 output tiles (gemm_tile_128, transposed product), staged through
-// LDS as fp16 or bf16 and written as 16-byte row chunks.  Output column col
+// 256x128 output tiles (gemm_tile, transposed product), staged through LDS
+// as fp16 or bf16 and written as 16-byte row chunks.  Output column col
 // -> (K or V, head, e).
 // ---------------------------------------------------------------------------
-constexpr int GBM = 128, GBN = 128, GBK = 32;
+constexpr int GBM = 256, GBN = 128, GBK = 32;
 
 template <bool F16OUT>
-__global__ __launch_bounds__(256) void prefill_kv_kernel(int B, int N, int a_seq_rows, int a_mul, int a_add,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kv_kernel(int B, int N, int a_seq_rows, int a_mul, int a_add,
                                                         int H, int d_h, int d_c, int W,
                                                         const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ w_uk,
                                                         const uint16_t* __restrict__ w_uv,
                                                         uint16_t* __restrict__ kout,
                                                         uint16_t* __restrict__ vout) {
-  __shared__ __align__(16) uint16_t smem[kTileSmemElems];
+  __shared__ __align__(16) uint16_t smem[TileShape<GBM>::SmemElems];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 5, c32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
@@ -66,27 +66,28 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int B, int N, int a_seq
   // wholly in W_UK or in W_UV (HD is a multiple of GBN).
   const uint16_t* bmat = col0 < HD ? w_uk + static_cast<size_t>(col0) * d_c
                                    : w_uv + static_cast<size_t>(col0 - HD) * d_c;
-  const uint16_t* arow[2];
+  constexpr int NI = GBM / 64;
+  const uint16_t* arow[NI];
   const uint16_t* wrow[2];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int r = 16 * (4 * k + wave) + (lane >> 2);
-    const int m = min(row0 + r, M - 1);
+  for (int k = 0; k < NI; ++k) {
+    const int m = min(row0 + 16 * (4 * k + wave) + (lane >> 2), M - 1);
     arow[k] = A + static_cast<size_t>((m / N) * a_seq_rows + (m % N) * a_mul + a_add) * W;
-    wrow[k] = bmat + static_cast<size_t>(r) * d_c;
   }
-  f32x16 acc[2][2];
-  gemm_tile_128<true>(arow, wrow, d_c, smem, acc);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) wrow[k] = bmat + static_cast<size_t>(16 * (4 * k + wave) + (lane >> 2)) * d_c;
+  f32x16 acc[NI][2];
+  gemm_tile<GBM, true>(arow, wrow, d_c, smem, acc);
 
-  // Epilogue: stage the 128x128 tile as fp16 (F16OUT) or bf16 in LDS, then
+  // Epilogue: stage the 256x128 tile as fp16 (F16OUT) or bf16 in LDS, then
   // write each (token, head) row of d_h values with 16-byte stores.
-  // acc[i][j][e] is row 64 wm + 32 i + c32, column 64 wn + 32 j + 8 (e / 4)
+  // acc[i][j][e] is row 128 wm + 32 i + c32, column 64 wn + 32 j + 8 (e / 4)
   // + 4 grp + e % 4: one 8-byte LDS store per four values.
   constexpr int CP = GBN + 8;
-  static_assert(GBM * CP <= kTileSmemElems, "C tile must fit in the operand stages");
+  static_assert(GBM * CP <= TileShape<GBM>::SmemElems, "C tile must fit in the operand stages");
   uint16_t* sC = smem;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(256) void prefill_kv_kernel(int B, int N, int a_seq
           w0 = f32_to_bf16_bits(c[4 * e4]) | (uint32_t(f32_to_bf16_bits(c[4 * e4 + 1])) << 16);
           w1 = f32_to_bf16_bits(c[4 * e4 + 2]) | (uint32_t(f32_to_bf16_bits(c[4 * e4 + 3])) << 16);
         }
-        *reinterpret_cast<uint2*>(&sC[(64 * wm + 32 * i + c32) * CP + 64 * wn + 32 * j + 8 * e4 + 4 * grp]) =
+        *reinterpret_cast<uint2*>(&sC[(128 * wm + 32 * i + c32) * CP + 64 * wn + 32 * j + 8 * e4 + 4 * grp]) =
             uint2{w0, w1};
       }
   __syncthreads();
