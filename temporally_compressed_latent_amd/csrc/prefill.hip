@@ -345,16 +345,15 @@ void prefill_attn_kernel(PrefillAttnArgs a) {
       const uint32_t dst = lds_w + __builtin_amdgcn_readfirstlane((4 * k + wave) * 1024);
       buffer_load_lds16_cached(2 * k < WLD ? rs_wk : rs_wv, dst, voff, c0 * 2);
     }
-    // the B operands of the round's (up to) RC/16 chunks
+    // the B operands of the round's (up to) RC/16 chunks (loaded for all RC/16:
+    // past d_c they read the next row or zero, and are not used)
     const int kcn = min(RC, a.d_c - c0) / 16;
     bf16x8 pf[NQ][RC / 16];
 #pragma unroll
     for (int kc = 0; kc < RC / 16; ++kc)
 #pragma unroll
       for (int t = 0; t < NQ; ++t)
-        pf[t][kc] = kc < kcn ? __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                               rs_p, poff[t], (c0 + 16 * kc) * 2, 0))
-                             : bf16x8{};
+        pf[t][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_p, poff[t], (c0 + 16 * kc) * 2, 0));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll
