@@ -91,10 +91,13 @@ def test_project_one_token_large_positions(wid, B):
             assert oracle.max_rel_err(host(got)[b], ref) <= tol(w.dtype), (b, pos)
 
 
+@pytest.mark.parametrize("R", [37, 600])
 @pytest.mark.parametrize("wid,kw", LAYER_CASES)
-def test_output_project_matches_oracle(wid, kw):
+def test_output_project_matches_oracle(wid, kw, R):
+    # 37 rows: the few-row kernel, three 16-row blocks, the last one ragged;
+    # 600 rows: the tiled kernel, three 256-row tiles, the last one ragged
     w, p, d, dev, *_ = _setup(wid, **kw)
-    R, H = 37, w.heads          # 37 rows: three 16-row blocks, the last one ragged
+    H = w.heads
     g = np.random.default_rng(3)
     o = workloads.quantize(g.standard_normal((R, H, w.d_h)).astype(np.float32), w.dtype)
     y = torch.empty(R, w.d_model, dtype=d.torch_dtype, device=DEV)

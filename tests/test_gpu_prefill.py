@@ -148,7 +148,8 @@ def test_prefill_at_then_decode_continues():
     oracle_ref.assert_steps(cont, want[:, 121:], 1e-2)
 
 
-@pytest.mark.parametrize("shape,s,B,N", [("st", 3, 2, 300), ("llm", 2, 1, 160), ("st", 1, 3, 97)])
+@pytest.mark.parametrize("shape,s,B,N", [("st", 3, 2, 300), ("llm", 2, 1, 160), ("st", 1, 3, 97),
+                                         ("st", 8, 2, 8)])   # no completed slot is attended: no slot keys
 def test_staged_prefill_equals_one_call(shape, s, B, N):
     """mtla_prefill_partials -> mtla_prefill_keys -> mtla_prefill_attention
     gives the bits of one mtla_prefill call (outputs, slot cache, open-slot
@@ -175,6 +176,8 @@ def test_staged_prefill_equals_one_call(shape, s, B, N):
     # the staged keys are K^C = W_UK P^c_{s b} and V = W_UV P^c_{s b} of the
     # completed slots b = 1 .. (N-1)//s (partial-merge rows s*b - 1, 0-based),
     # which are also the cache's slot rows
+    if S == 0:
+        return
     rows = torch.arange(S, device=DEV) * s + (s - 1)
     Pc = P.float()[:, rows, :d.d_c]
     assert torch.equal(bits(P[:, rows]), bits(b_.cache[:, :S]))
