@@ -73,6 +73,58 @@ __global__ __launch_bounds__(256) void bwd_partials_kernel(BwdArgs a) {
   }
 }
 
+// The same for d_c = 64 GE and d_r <= 64, with every load of a round of TB
+// tokens in flight together: lane l holds elements l + 64 j of c_t, pe_t and
+// the W_hyp row (the gate's inputs, which are also the merge's c columns) and
+// element l of k^R_t; the gate is gate_from_lane_values (the same bits as
+// gate_of_token), the running sums the same fmaf chain in token order.
+template <typename T, int GE>
+__global__ __launch_bounds__(256) void bwd_partials_lanes_kernel(BwdArgs a) {
+  constexpr int TB = 4;
+  const int lane = threadIdx.x & 63;
+  const int wv = (blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int nblk = (a.N + a.s - 1) / a.s;
+  if (wv >= a.B * nblk) return;
+  const int b = wv / nblk, blk = wv % nblk;
+  const int W = a.d_c + a.d_r;
+  const int t0 = blk * a.s, t1 = min(t0 + a.s, a.N);
+  const int r_l = min(lane, a.d_r > 0 ? a.d_r - 1 : 0);
+  float acc[GE + 1];
+#pragma unroll
+  for (int j = 0; j <= GE; ++j) acc[j] = 0.f;
+  for (int tb = t0; tb < t1; tb += TB) {
+    float x[TB][GE], pv[TB][GE], wh[TB][GE], xr[TB];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int t = min(tb + u, t1 - 1);  // past the block: re-read its last token (not used)
+      const size_t row = static_cast<size_t>(b) * a.N + t;
+      const float* whr = a.w_hyp + static_cast<size_t>(t % a.s) * a.wh_stride;
+#pragma unroll
+      for (int j = 0; j < GE; ++j) {
+        x[u][j] = ld<T>(a.c, row * a.d_c + lane + 64 * j);
+        pv[u][j] = a.pe[static_cast<size_t>(t) * a.d_c + lane + 64 * j];
+        wh[u][j] = whr[lane + 64 * j];
+      }
+      xr[u] = a.d_r > 0 ? ld<T>(a.k_r, row * a.d_r + r_l) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int t = tb + u;
+      if (t >= t1) break;
+      const size_t row = static_cast<size_t>(b) * a.N + t;
+      const float w = gate_from_lane_values<GE>(x[u], pv[u], wh[u]);
+      if (lane == 0) a.gate[row] = w;
+#pragma unroll
+      for (int j = 0; j < GE; ++j) {
+        acc[j] = fmaf(w, x[u][j], acc[j]);
+        st<T>(a.P, row * W + lane + 64 * j, acc[j]);
+      }
+      acc[GE] = fmaf(w, xr[u], acc[GE]);
+      if (lane < a.d_r) st<T>(a.P, row * W + a.d_c + lane, acc[GE]);
+    }
+  }
+}
+
 // Key row (0-based token) of the kk-th key query i (0-based) sees: the
 // completed slots' last tokens s*m - 1 (m = 1..(i)/s, i.e. completed_slots of
 // the 1-based query), then the query's own token.
@@ -245,10 +297,9 @@ __global__ __launch_bounds__(64) void bwd_dkv_kernel(BwdArgs a) {
 // l + 64, ... (JW of them) of the running sum G.  Tokens go in rounds of TB
 // whose loads are all issued before the round's sequential part (the
 // running sum, one wave reduction per token, the stores).  Writes dc, dk^R
-// and du of every token.
-template <typename T, int JW>
+// and du of every token.  TB = s for s = 3 (one round, no re-read token).
+template <typename T, int JW, int TB>
 __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
-  constexpr int TB = 4;
   const int lane = threadIdx.x & 63;
   const int wv = (blockIdx.x * 256 + threadIdx.x) >> 6;
   const int nblk = (a.N + a.s - 1) / a.s;
@@ -261,6 +312,13 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
   for (int j = 0; j < JW; ++j) G[j] = 0.f;
   for (int tt = t1 - 1; tt >= t0; tt -= TB) {
     float x[TB][JW], dP[TB][JW], w[TB];
+    // Every load of the round is issued unconditionally (indices clamped into
+    // the row, values selected afterwards), so that they are in flight
+    // together rather than one round trip each behind a branch.  The rope
+    // gradient of column r (lane r < d_r) is summed over the heads in head
+    // order (the first 8 heads' loads together, further heads after).
+    float rp[TB], xr[TB];
+    const int r_l = min(lane, a.d_r > 0 ? a.d_r - 1 : 0);
 #pragma unroll
     for (int u = 0; u < TB; ++u) {
       // tokens before the block's first re-read that token (not used)
@@ -268,21 +326,59 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
       w[u] = a.gate[row];
 #pragma unroll
       for (int j = 0; j < JW; ++j) {
-        const int e = lane + 64 * j;
-        x[u][j] = 0.f;
-        dP[u][j] = 0.f;
-        if (e < a.d_c) {
-          dP[u][j] = a.dPc[row * a.d_c + e];
-          x[u][j] = ld<T>(a.c, row * a.d_c + e);
-        } else if (e < W) {
-          const int r = e - a.d_c;
-          float acc = 0.f;
-#pragma unroll 8
-          for (int hh = 0; hh < a.H; ++hh) acc += ld<T>(a.dKV, row * ldk + KV2 + hh * a.d_r + r);
-          dP[u][j] = acc;
-          x[u][j] = ld<T>(a.k_r, row * a.d_r + r);
+        const int ec = min(lane + 64 * j, a.d_c - 1);
+        dP[u][j] = a.dPc[row * a.d_c + ec];
+        x[u][j] = ld<T>(a.c, row * a.d_c + ec);
+      }
+      rp[u] = 0.f;
+      xr[u] = 0.f;
+    }
+    if (a.d_r > 0) {
+      float v[TB][8];
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const size_t row = static_cast<size_t>(b) * a.N + max(tt - u, t0);
+        xr[u] = ld<T>(a.k_r, row * a.d_r + r_l);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[u][k] = ld<T>(a.dKV, row * ldk + KV2 + min(k, a.H - 1) * a.d_r + r_l);
+      }
+#pragma unroll
+      for (int u = 0; u < TB; ++u)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k < a.H) rp[u] += v[u][k];
+    }
+    if (a.H > 8) {
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const size_t row = static_cast<size_t>(b) * a.N + max(tt - u, t0);
+        for (int hh = 8; hh < a.H; ++hh) rp[u] += ld<T>(a.dKV, row * ldk + KV2 + hh * a.d_r + r_l);
+      }
+    }
+    // columns e >= d_c: the rope values of lane e - d_c
+#pragma unroll
+    for (int j = 0; j < JW; ++j) {
+      const int e = lane + 64 * j;
+      if (64 * j + 63 < a.d_c) continue;  // (uniform) no rope column in this j
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const int src = e - a.d_c;
+        const float pr = a.d_c % 64 == 0 ? rp[u] : __shfl(rp[u], max(src, 0), 64);
+        const float px = a.d_c % 64 == 0 ? xr[u] : __shfl(xr[u], max(src, 0), 64);
+        if (e >= a.d_c) {
+          dP[u][j] = e < W ? pr : 0.f;
+          x[u][j] = e < W ? px : 0.f;
         }
       }
+    }
+    // the W_hyp values the stores below use (row (t - 1) mod s per token when
+    // there is one row per place), loaded with the round's other loads
+    float whv[TB][JW];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const float* whr = a.w_hyp + static_cast<size_t>(max(tt - u, t0) % a.s) * a.wh_stride;
+#pragma unroll
+      for (int j = 0; j < JW; ++j) whv[u][j] = whr[min(lane + 64 * j, a.d_c - 1)];
     }
 #pragma unroll
     for (int u = 0; u < TB; ++u) {
@@ -297,12 +393,11 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
       }
       const float du = wave_sum(dwl) * w[u] * (1.f - w[u]);
       if (lane == 0) a.du[row] = du;
-      const float* whr = a.w_hyp + static_cast<size_t>(t % a.s) * a.wh_stride;
 #pragma unroll
       for (int j = 0; j < JW; ++j) {
         const int e = lane + 64 * j;
         if (e < a.d_c)
-          st<T>(a.g_c, row * a.d_c + e, fmaf(du, whr[e], w[u] * G[j]));
+          st<T>(a.g_c, row * a.d_c + e, fmaf(du, whv[u][j], w[u] * G[j]));
         else if (e < W)
           st<T>(a.g_k_r, row * a.d_r + (e - a.d_c), w[u] * G[j]);
       }
@@ -323,12 +418,23 @@ __global__ __launch_bounds__(256) void dwhyp_kernel(BwdArgs a, int rows_per_spli
   const int r0 = blockIdx.y * rows_per_split, r1 = min(R, r0 + rows_per_split);
   const int place = blockIdx.z;
   float acc = 0.f;
+  // eight rows' loads in flight at a time (row indices clamped, the rows
+  // past r1 or of another place skipped), added in row order
   if (col < a.d_c)
-    for (int r = r0 + rg; r < r1; r += 4) {
-      const int t = r % a.N;
-      if (a.wh_rows > 1 && t % a.s != place) continue;
-      acc = fmaf(a.du[r], ld<T>(a.c, static_cast<size_t>(r) * a.d_c + col) + a.pe[static_cast<size_t>(t) * a.d_c + col],
-                 acc);
+    for (int rb = r0 + rg; rb < r1; rb += 32) {
+      float dv[8], cv[8], pv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = min(rb + 4 * k, r1 - 1), t = r % a.N;
+        dv[k] = a.du[r];
+        cv[k] = ld<T>(a.c, static_cast<size_t>(r) * a.d_c + col);
+        pv[k] = a.pe[static_cast<size_t>(t) * a.d_c + col];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = rb + 4 * k;
+        if (r < r1 && (a.wh_rows == 1 || (r % a.N) % a.s == place)) acc = fmaf(dv[k], cv[k] + pv[k], acc);
+      }
     }
   red[rg][cl] = acc;
   __syncthreads();
@@ -405,8 +511,16 @@ __global__ __launch_bounds__(256) void sum_split_rows_kernel(const float* part, 
   const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   const size_t n = static_cast<size_t>(M) * N;
   if (idx >= n) return;
+  // eight parts' loads in flight at a time, added in part order
   float acc = 0.f;
-  for (int p = 0; p < splits; ++p) acc += part[p * n + idx];
+  for (int p0 = 0; p0 < splits; p0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = part[min(p0 + k, splits - 1) * n + idx];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (p0 + k < splits) acc += v[k];
+  }
   const int m = static_cast<int>(idx / N);
   if (m < m0_rows)
     out0[idx] = acc;
@@ -421,8 +535,16 @@ __global__ __launch_bounds__(256) void sum_parts_kernel(const float* part, int p
   const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
   const int col = blockIdx.x * 64 + cl;
   float acc = 0.f;
+  // eight parts' loads in flight at a time, added in part order
   if (col < n)
-    for (int p = rg; p < parts; p += 4) acc += part[static_cast<size_t>(p) * n + col];
+    for (int p0 = rg; p0 < parts; p0 += 32) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = part[static_cast<size_t>(min(p0 + 4 * k, parts - 1)) * n + col];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (p0 + 4 * k < parts) acc += v[k];
+    }
   red[rg][cl] = acc;
   __syncthreads();
   if (rg == 0 && col < n) out[col] = (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]);
@@ -1147,10 +1269,16 @@ void bwd_dkv_mfma_kernel(BwdArgs a, int nslots, int nst) {
 hipError_t launch_bwd_partials(const BwdArgs& a, int dtype, hipStream_t st) {
   const int waves = a.B * ((a.N + a.s - 1) / a.s);
   const dim3 grid((waves + 3) / 4);
-  if (dtype == 0)
-    bwd_partials_kernel<float><<<grid, 256, 0, st>>>(a);
-  else
-    bwd_partials_kernel<uint16_t><<<grid, 256, 0, st>>>(a);
+  const bool lanes = (a.d_c == 256 || a.d_c == 512) && a.d_r <= 64;
+  if (dtype == 0) {
+    if (lanes && a.d_c == 256) bwd_partials_lanes_kernel<float, 4><<<grid, 256, 0, st>>>(a);
+    else if (lanes) bwd_partials_lanes_kernel<float, 8><<<grid, 256, 0, st>>>(a);
+    else bwd_partials_kernel<float><<<grid, 256, 0, st>>>(a);
+  } else {
+    if (lanes && a.d_c == 256) bwd_partials_lanes_kernel<uint16_t, 4><<<grid, 256, 0, st>>>(a);
+    else if (lanes) bwd_partials_lanes_kernel<uint16_t, 8><<<grid, 256, 0, st>>>(a);
+    else bwd_partials_kernel<uint16_t><<<grid, 256, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -1166,15 +1294,23 @@ hipError_t launch_bwd_attention(const BwdArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T>
-static void scan_launch(const BwdArgs& a, dim3 grid, hipStream_t st) {
+template <typename T, int TB>
+static void scan_launch_tb(const BwdArgs& a, dim3 grid, hipStream_t st) {
   const int W = a.d_c + a.d_r;
   if (W <= 5 * 64)
-    bwd_scan_kernel<T, 5><<<grid, 256, 0, st>>>(a);
+    bwd_scan_kernel<T, 5, TB><<<grid, 256, 0, st>>>(a);
   else if (W <= 9 * 64)
-    bwd_scan_kernel<T, 9><<<grid, 256, 0, st>>>(a);
+    bwd_scan_kernel<T, 9, TB><<<grid, 256, 0, st>>>(a);
   else
-    bwd_scan_kernel<T, 16><<<grid, 256, 0, st>>>(a);
+    bwd_scan_kernel<T, 16, TB><<<grid, 256, 0, st>>>(a);
+}
+
+template <typename T>
+static void scan_launch(const BwdArgs& a, dim3 grid, hipStream_t st) {
+  if (a.s == 3)
+    scan_launch_tb<T, 3>(a, grid, st);
+  else
+    scan_launch_tb<T, 4>(a, grid, st);
 }
 
 hipError_t launch_bwd_scan(const BwdArgs& a, int dtype, hipStream_t st) {
