@@ -113,7 +113,13 @@ __device__ void compute_gates_lanes(const MergeArgs& a, int b, int p0, int ta, i
         pv[k][j] = per[lane + 64 * j];
         if constexpr (PP) wh[k][j] = whr[lane + 64 * j];
       }
-      if (stage) {
+    }
+    // (after every token's loads are issued, so that they stay in flight
+    // together)
+    if (stage) {
+#pragma unroll
+      for (int k = 0; k < NTOK; ++k) {
+        const int kc = min(k0 + k * nwaves, ntok - 1);
 #pragma unroll
         for (int j = 0; j < GE; ++j) Store<T>::store(stage, static_cast<size_t>(kc) * a.d_c + lane + 64 * j, x[k][j]);
       }
@@ -213,12 +219,12 @@ __device__ void merge_blocks(const MergeArgs& a, int b, int chunk, int blocks_pe
     // four tokens' chunks in flight at a time (indices clamped to the block)
     for (int t = t0; t <= t1; t += 4) {
       float x[4][8];
+      if (staged && e < a.d_c) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (staged && e < a.d_c)
-          load8(xs + static_cast<size_t>(min(t + u, t1) - ta) * a.d_c + e, x[u]);
-        else
-          token_chunk<T>(a, b, min(t + u, t1) - r.p0, e, x[u]);
+        for (int u = 0; u < 4; ++u) load8(xs + static_cast<size_t>(min(t + u, t1) - ta) * a.d_c + e, x[u]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) token_chunk<T>(a, b, min(t + u, t1) - r.p0, e, x[u]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
