@@ -1239,14 +1239,28 @@ void bwd_dkv_mfma_kernel(BwdArgs a, int nslots, int nst) {
   const float pjj = a.pd[si], dsjj = a.dsd[si];
   const size_t qrow = (static_cast<size_t>(b) * N + jt) * H + h;
   uint16_t* row = static_cast<uint16_t*>(a.dKV) + (static_cast<size_t>(b) * N + jt) * ldk;
+  // the query and dO values first (all loads in flight together: the stores
+  // below could alias them as far as the compiler knows)
+  uint2 qv[FT][4], dv[DT][4];
+#pragma unroll
+  for (int t = 0; t < FT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f0 = 32 * t + 8 * j + 4 * grp;
+      qv[t][j] = f0 < DH ? *reinterpret_cast<const uint2*>(qc + qrow * DH + f0)
+                         : *reinterpret_cast<const uint2*>(qr + qrow * DR + (f0 - DH));
+    }
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dv[t][j] = *reinterpret_cast<const uint2*>(dO + qrow * DH + 32 * t + 8 * j + 4 * grp);
 #pragma unroll
   for (int t = 0; t < FT; ++t)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int f0 = 32 * t + 8 * j + 4 * grp;
       float q4[4];
-      unpack4_bf16(f0 < DH ? *reinterpret_cast<const uint2*>(qc + qrow * DH + f0)
-                           : *reinterpret_cast<const uint2*>(qr + qrow * DR + (f0 - DH)), q4);
+      unpack4_bf16(qv[t][j], q4);
       const uint2 v = pack4_bf16(fmaf(dsjj, q4[0], dkt[t][4 * j]), fmaf(dsjj, q4[1], dkt[t][4 * j + 1]),
                                  fmaf(dsjj, q4[2], dkt[t][4 * j + 2]), fmaf(dsjj, q4[3], dkt[t][4 * j + 3]));
       *reinterpret_cast<uint2*>(f0 < DH ? row + h * DH + f0 : row + KV2 + h * DR + (f0 - DH)) = v;
@@ -1257,7 +1271,7 @@ void bwd_dkv_mfma_kernel(BwdArgs a, int nslots, int nst) {
     for (int j = 0; j < 4; ++j) {
       const int f0 = 32 * t + 8 * j + 4 * grp;
       float d4[4];
-      unpack4_bf16(*reinterpret_cast<const uint2*>(dO + qrow * DH + f0), d4);
+      unpack4_bf16(dv[t][j], d4);
       const uint2 v = pack4_bf16(fmaf(pjj, d4[0], dvt[t][4 * j]), fmaf(pjj, d4[1], dvt[t][4 * j + 1]),
                                  fmaf(pjj, d4[2], dvt[t][4 * j + 2]), fmaf(pjj, d4[3], dvt[t][4 * j + 3]));
       *reinterpret_cast<uint2*>(row + H * DH + h * DH + f0) = v;
