@@ -1150,7 +1150,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   constexpr int EGN = NT / (KC * HG);                    // absorb row groups
   constexpr int NP = (DH + 2 * EGN - 1) / (2 * EGN);     // W_UK row pairs per thread
   constexpr int MT = (DH + 15) / 16;                     // up-projection tiles per head
-  constexpr int RP = DC + 16;                            // row buffer pitch (elements)
+  constexpr int RP = W + 8;                              // row buffer pitch (elements)
   constexpr int QP = W + 8;                              // q~ pitch (elements)
   static_assert(W % 32 == 0 && NT % (KC * HG) == 0 && EGN >= 1, "shape");
   static_assert(HG * DC <= NT && HG * DR <= NT && HG <= 16, "one q~ element per thread");
@@ -1246,7 +1246,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
       const_cast<uint16_t*>(a.w_uv + static_cast<size_t>(h0) * d_h * DC), static_cast<short>(0), HG * d_h * DC * 2,
       kBufferRsrcWord3);
   const int vu = ((hu * d_h + min(mt * 16 + c16, d_h - 1)) * DC + 8 * g) * 2;
-  uint4 wv[KSU];  // loaded once the absorb is done (see below)
+  uint4 wv[KSU];  // loaded after the cache rows (see below)
   const int te = min(tid, W - 1);  // merge column of this thread (tid < W)
   uint16_t gxb[GE], mxb = 0;
   float gw[GE];
@@ -1300,20 +1300,32 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   // rows [0, hm) of the sequence; a load past them reads zero
   const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(rows), static_cast<short>(0), hm * W * 2,
                                                     kBufferRsrcWord3);
-  // chunk ci = slots 16 ci .. +15; lane (g, c16) holds row c16, elements
-  // 32 ks + 8g .. +7: the MFMA A layout
+  // chunk ci = slots 16 ci .. +15, 16 W elements contiguous in memory; load
+  // ks takes its bytes 1024 ks + 16 lane .. +15 (whole 128-byte lines: a load
+  // of 16 rows x 64 bytes, the MFMA operand layout, costs the memory pipeline
+  // twice the cycles); the rows reach the MFMA layout through the wave's row
+  // buffer
   uint4 ra[KSW], rb[KSW];
   auto load_chunk = [&](int ci, uint4 (&r)[KSW]) {
     if (16 * ci >= hm) return;  // no memory rows (a load past them would still take issue slots)
     const int so = __builtin_amdgcn_readfirstlane(ci * 16 * W * 2);
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (c16 * W + 8 * g) * 2 + ks * 64, so, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + ks * 1024, so, 0);
       r[ks] = uint4{v[0], v[1], v[2], v[3]};
     }
   };
   load_chunk(wave, ra);
   load_chunk(wave + NWV, rb);
+  // W_UV is needed last: its loads go out behind the W_UK and cache-row loads
+  // in the compute unit's memory pipeline (ahead of them they delay the
+  // absorb and the attention), and before the absorb, so that they have
+  // arrived when the waves are combined
+#pragma unroll
+  for (int ks = 0; ks < KSU; ++ks) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_uv, vu + ks * 64, 0, 0);
+    wv[ks] = uint4{v[0], v[1], v[2], v[3]};
+  }
 
   // absorb: partial sums over this thread's rows, W_UK row pairs against
   // (q_c[e0], q_c[e0 + 1]) pairs
@@ -1348,14 +1360,6 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
     gate = gate_from_lane_values<GE>(gx, gp, gw);
   }
   __syncthreads();
-  // W_UV is needed last: its loads go out only now, so that they do not
-  // queue ahead of the W_UK and cache-row loads in the compute unit's
-  // memory pipeline
-#pragma unroll
-  for (int ks = 0; ks < KSU; ++ks) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_uv, vu + ks * 64, 0, 0);
-    wv[ks] = uint4{v[0], v[1], v[2], v[3]};
-  }
   if constexpr (MERGE) {
     if (tid < W) {
       const float v = fmaf(gate, bf16_bits_to_f32(mxb), cont ? macc : 0.f);
@@ -1392,12 +1396,19 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   f32x4 acc[CTW];
 #pragma unroll
   for (int ct = 0; ct < CTW; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Row buffer layout: the 16-byte chunk q of row r sits at chunk
-  // q ^ ((r >> 2) & 1), so that the row writes (8 lanes = rows r .. r+7 at
-  // one chunk) and the transposing reads both spread over the banks.
+  // Row buffer: the chunk's 16 rows at a pitch of W + 8 elements (rows 16
+  // bytes apart in the banks, so that the MFMA-layout reads of 16 rows at one
+  // column spread over them).  Piece p = 64 ks + lane of a chunk load is
+  // row p / (W/8), 16-byte column p % (W/8).
   uint16_t* wb = &rw.r[wave][0][0];
-  uint16_t* wrow = wb + c16 * RP + 8 * (g ^ ((c16 >> 2) & 1));
-  const uint16_t* vb = wb + (4 * g + (c16 >> 2)) * RP + 8 * (((c16 >> 1) & 1) ^ (g & 1)) + 4 * (c16 & 1);
+  int woff[KSW];
+#pragma unroll
+  for (int j = 0; j < KSW; ++j) {
+    const int p = 64 * j + lane;
+    woff[j] = (p / (W / 8)) * RP + 8 * (p % (W / 8));
+  }
+  const uint16_t* arow = wb + c16 * RP + 8 * g;
+  const uint16_t* vb = wb + (4 * g + (c16 >> 2)) * RP + 4 * (c16 & 3);
   auto do_chunk = [&](int ci, uint4 (&r)[KSW]) {
     const int base = 16 * ci;
     if (base >= n) return;
@@ -1405,15 +1416,21 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
 #pragma unroll
       for (int ks = 0; ks < KSW; ++ks) r[ks] = uint4{0u, 0u, 0u, 0u};
     }
-    // the new row (slot hm, merging) comes from LDS
-    if (MERGE && hm >= base && hm < base + 16 && c16 == hm - base) {
 #pragma unroll
-      for (int ks = 0; ks < KSW; ++ks) r[ks] = *reinterpret_cast<const uint4*>(s_new + ks * 32 + 8 * g);
-    }
+    for (int j = 0; j < KSW; ++j) *reinterpret_cast<uint4*>(wb + woff[j]) = r[j];
+    // the new row (slot hm, merging) comes from LDS (its loaded row read as
+    // zero)
+    if (MERGE && hm >= base && hm < base + 16 && lane < W / 8)
+      *reinterpret_cast<uint4*>(wb + (hm - base) * RP + 8 * lane) = *reinterpret_cast<const uint4*>(s_new + 8 * lane);
+    // rows in the MFMA A layout: lane (g, c16) takes row c16, elements
+    // 32 ks + 8g .. +7
+    bf16x8 arr[KSW];
+#pragma unroll
+    for (int ks = 0; ks < KSW; ++ks) arr[ks] = *reinterpret_cast<const bf16x8*>(arow + 32 * ks);
     f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
-      const bf16x8 ar = __builtin_bit_cast(bf16x8, r[ks]);
+      const bf16x8 ar = arr[ks];
       if (ks % 2 == 0)
         sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar, qk[ks], sa, 0, 0, 0);
       else
@@ -1456,25 +1473,24 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
       split_bf16(pv, ph, pl);
       pb[i] = static_cast<short>(c16 < HG ? ph : pl);
     }
-    // the chunk's latent columns into the wave's buffer, then V^T: lane
-    // (g, k) of a 16-lane group points at row 4g + k/4, columns
-    // 16 ct + 4 (k%4) .. +3 (in chunk 2 ct + (k%4)/2, swizzled), and
-    // receives rows 4g .. 4g+3 of column 16 ct + k
-#pragma unroll
-    for (int ks = 0; ks < DC / 32; ++ks) *reinterpret_cast<uint4*>(wrow + ks * 32) = r[ks];
+    // V^T from the wave's row buffer: lane (g, k) of a 16-lane group points
+    // at row 4g + k/4, columns 16 ct + 4 (k%4) .. +3, and receives rows
+    // 4g .. 4g+3 of column 16 ct + k
 #pragma unroll
     for (int ct = 0; ct < CTW; ++ct) {
       const s16x4 va = lds_read_tr16(vb + ct * 16);
       acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[ct], 0, 0, 0);
     }
   };
-  // Two chunks in flight per wave.
+  // The first two chunks were loaded ahead; later ones (caches of more than
+  // 2 x 8 x 16 slots) one at a time, so that no load is left in flight past
+  // the loop (later code reusing its registers would wait on it).
   const int nch = (n + 15) / 16;
-  for (int j = 0; wave + NWV * j < nch; j += 2) {
-    do_chunk(wave + NWV * j, ra);
-    load_chunk(wave + NWV * (j + 2), ra);
-    do_chunk(wave + NWV * (j + 1), rb);
-    load_chunk(wave + NWV * (j + 3), rb);
+  do_chunk(wave, ra);
+  do_chunk(wave + NWV, rb);
+  for (int ci = wave + 2 * NWV; ci < nch; ci += NWV) {
+    load_chunk(ci, ra);
+    do_chunk(ci, ra);
   }
   // this wave's sum for head c16: the four lane groups, in a fixed order
   const float lw = cross_row_sum(l);
