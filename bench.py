@@ -64,7 +64,7 @@ def parse_args():
                    help="run one workload and print its record (st_decode_s2, st_decode_s4, prefill, "
                         "prefill_chunk, llm_decode, reorder, layer_decode, layer_prefill, layer_fp32, backward; "
                         "measurement kernels: copy (the counter-calibration copy), hbm_read, mfma_peak, "
-                        "gemm_peak, launch_floor, tile_stream)")
+                        "gemm_peak, launch_floor, tile_stream, load_pattern)")
     return p.parse_args()
 
 
@@ -616,6 +616,28 @@ def run_tile_stream(steps, warmup, m, torch):
     return rec
 
 
+def run_load_pattern(steps, warmup, m, torch):
+    """A compute unit's issue cost of one 16-byte-per-lane load instruction
+    from L2-resident data (mtla_calib_load_pattern, one workgroup of 8 waves
+    x 32 loads per compute unit): a contiguous kilobyte per instruction
+    against 16 rows x 64 bytes (the MFMA operand layout of row-major rows,
+    the decode step's former cache-row and present W_UV loads)."""
+    wg = 256
+    buf = torch.ones(1 << 20, dtype=torch.int32, device="cuda")  # 4 MiB: stays in L2
+    cyc = torch.zeros(wg + 64, dtype=torch.int32, device="cuda")
+    rec = {"kernel": "calib_load_pattern_kernel", "workgroups": wg, "loads_per_wave": 32, "waves": 8}
+    for name, pat in (("contiguous_1KB", 0), ("16_rows_x_64B", 1)):
+        meds = []
+        for _ in range(max(steps, 5) + max(warmup, 1)):
+            m.mtla_calib_load_pattern(pat, wg, buf, cyc)
+            torch.cuda.synchronize()
+            meds.append(float(cyc[:wg].float().median()))
+        med = sorted(meds[max(warmup, 1):])[len(meds[max(warmup, 1):]) // 2]
+        rec[name] = {"cycles_per_workgroup": med, "cycles_per_load_instruction": med / (8 * 32),
+                     "bytes_per_cycle": 8 * 32 * 1024 / med}
+    return rec
+
+
 def run_mfma_peak(steps, warmup, m, torch):
     """MFMA chains on registers (32x32x16, fp32 accumulation), bf16 and fp16
     operands, 2 and 4 waves per SIMD; the best is the matrix cores' rate."""
@@ -889,7 +911,8 @@ def main():
               "tile_stream": lambda: run_tile_stream(K, Wu, m, torch),
               "mfma_peak": lambda: run_mfma_peak(K, Wu, m, torch),
               "gemm_peak": lambda: run_gemm_peak(K, Wu, m, torch),
-              "launch_floor": lambda: run_launch_floor(K, Wu, m, torch)}
+              "launch_floor": lambda: run_launch_floor(K, Wu, m, torch),
+              "load_pattern": lambda: run_load_pattern(K, Wu, m, torch)}
         print(json.dumps(fn[args.only]()), flush=True)
         return 0
 
@@ -903,7 +926,8 @@ def main():
     log("launch floor:", json.dumps(floor))
     peaks = {"hbm_read": run_hbm_read(K, Wu, m, torch), "mfma": run_mfma_peak(K, Wu, m, torch),
              "gemm": run_gemm_peak(K, Wu, m, torch), "launch_floor_us": floor["us_per_launch"],
-             "decode_tile_stream": run_tile_stream(K, Wu, m, torch)}
+             "decode_tile_stream": run_tile_stream(K, Wu, m, torch),
+             "load_pattern": run_load_pattern(K, Wu, m, torch)}
     log("measured peaks:", json.dumps(peaks))
     torch.cuda.empty_cache()
     comps, cpu_jobs = {}, []

@@ -536,10 +536,22 @@ int32_t mtla_debug_slot_limits(int32_t n, int32_t s, int32_t* hi, void* stream);
  *     (else a contiguous range); bit 1: non-temporal loads.  sink (device,
  *     seqs * splits * 8 uint32) is written only on a pattern no real data
  *     here produces.  rows_per_seq * 1152 must fit in 31 bits; splits 1..64.
+ *   mtla_calib_load_pattern: a compute unit's issue cost of 16-byte-per-lane
+ *     load instructions from L2-resident data.  `workgroups` workgroups of 8
+ *     waves (one per compute unit when workgroups <= 256); every wave issues
+ *     32 loads, all in flight before any is used, twice over the same
+ *     addresses, and cycles[w] (device, workgroups + 64 uint32, the extra
+ *     words written only on a pattern no data here produces) receives
+ *     workgroup w's s_memtime cycles for the second pass.  pattern 0: each
+ *     load reads 1,024 contiguous bytes; 1: 16 rows of 64 bytes at a 576-byte
+ *     pitch.  buf device, 16-byte aligned, bytes 128 KiB..2 GiB (read only
+ *     inside [buf, buf + bytes)).
  */
 int32_t mtla_calib_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
 int32_t mtla_calib_mfma(int32_t f16, int32_t workgroups, int32_t iters, float* out, double* flops, void* stream);
 int32_t mtla_calib_empty(void* stream);
+int32_t mtla_calib_load_pattern(int32_t pattern, int32_t workgroups, const void* buf, size_t bytes,
+                                uint32_t* cycles, void* stream);
 int32_t mtla_calib_tile_stream(const void* rows, int32_t seqs, int32_t rows_per_seq, int32_t splits, int32_t flags,
                                uint32_t* sink, void* stream);
 

@@ -109,6 +109,7 @@ _SIGS = {
     "mtla_calib_stream_read": (_I, [_P, _SZ, _I, _P, _P]),
     "mtla_calib_mfma": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "mtla_calib_empty": (_I, [_P]),
+    "mtla_calib_load_pattern": (_I, [_I, _I, _P, _SZ, _P, _P]),
     "mtla_calib_tile_stream": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "mtla_absorb_query": (_I, [_D, _I, _P, _P, _P, _P, _P]),
     "mtla_decode_attention_workspace_bytes": (_I, [_D, ctypes.POINTER(_SZ)]),
@@ -395,6 +396,16 @@ def mtla_calib_mfma(f16: bool, workgroups: int, iters: int, out, stream=None) ->
 def mtla_calib_empty(stream=None) -> None:
     """Measurement hook: one kernel that does nothing."""
     _check(_lib.mtla_calib_empty(_stream(stream)))
+
+
+def mtla_calib_load_pattern(pattern: int, workgroups: int, buf, cycles, stream=None) -> None:
+    """Per-workgroup cycles of 8 waves x 32 load instructions (pattern 0:
+    contiguous kilobytes, 1: 16 rows x 64 bytes) from L2-resident data."""
+    nbytes = buf.numel() * buf.element_size()
+    if cycles.dtype != torch.int32 or cycles.numel() < workgroups + 64:
+        raise ValueError("cycles: int32 tensor of at least workgroups + 64 elements")
+    _check(_lib.mtla_calib_load_pattern(pattern, workgroups, buf.data_ptr(), nbytes, cycles.data_ptr(),
+                                        _stream(stream)))
 
 
 def mtla_calib_tile_stream(rows, splits: int, interleave: bool, nt: bool, sink, stream=None) -> None:

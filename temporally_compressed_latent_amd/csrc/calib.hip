@@ -8,7 +8,11 @@
 //   calib_empty_kernel: a kernel that does nothing (the launch floor);
 //   calib_tile_stream_kernel: the long-cache decode attention's load
 //                       schedule with no arithmetic (the ceiling of that
-//                       access pattern).
+//                       access pattern);
+//   calib_load_pattern_kernel: a compute unit's issue cost of one 16-byte-
+//                       per-lane load instruction from L2-resident data, for
+//                       a contiguous kilobyte or for 16 rows x 64 bytes (the
+//                       MFMA operand layout of row-major rows).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -84,6 +88,44 @@ __global__ __launch_bounds__(256) void calib_mfma_kernel(int iters, float* __res
 }
 
 __global__ void calib_empty_kernel() {}
+
+// One workgroup of 8 waves per compute unit; every wave issues kPatLoads
+// 16-byte-per-lane loads before using any, twice over the same addresses
+// (the first pass brings them into L2), and thread 0 records the second
+// pass's s_memtime cycles from the barrier before its loads to the barrier
+// after their use.  Pattern 0: load i of a wave reads 1,024 contiguous bytes
+// (lane l at 16 l + 1024 i, eight whole 128-byte lines); pattern 1: 16 rows of
+// 64 bytes at a 576-byte row pitch (lane l at row l % 16, byte 16 (l / 16),
+// + 64 i: sixteen half lines).  Each wave starts at its own 4 KB offset; the
+// buffer resource ends at `bytes`, so no access leaves the buffer.
+constexpr int kPatLoads = 32;
+template <int P>
+__global__ __launch_bounds__(512) void calib_load_pattern_kernel(const uint8_t* __restrict__ buf, uint32_t bytes,
+                                                                 uint32_t* __restrict__ cycles) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(buf), static_cast<short>(0),
+                                                    static_cast<int>(bytes), kBufferRsrcWord3);
+  const uint32_t span = bytes > 131072u ? bytes - 65536u : 65536u;
+  const int base = static_cast<int>((static_cast<uint32_t>(blockIdx.x * 8 + wave) * 4096u) % span);
+  const int off = base + (P == 0 ? 16 * lane : (lane & 15) * 576 + (lane >> 4) * 16);
+  constexpr int step = P == 0 ? 1024 : 64;
+  uint32_t acc = 0;
+  uint64_t t0 = 0, t1 = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+    t0 = __builtin_amdgcn_s_memtime();
+    u32x4 v[kPatLoads];
+#pragma unroll
+    for (int i = 0; i < kPatLoads; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + i * step, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kPatLoads; ++i) acc ^= v[i][0] ^ v[i][3];
+    __syncthreads();
+    t1 = __builtin_amdgcn_s_memtime();
+  }
+  if (tid == 0) cycles[blockIdx.x] = static_cast<uint32_t>(t1 - t0);
+  // (never true for the data used: keeps the loads alive)
+  if (acc == 0x9e3779b9u) cycles[gridDim.x + (tid & 63)] = acc;
+}
 
 // The load schedule of the long-cache decode attention without its
 // arithmetic: one workgroup of 8 waves per (split, sequence) streams 64-row
@@ -184,6 +226,17 @@ hipError_t launch_calib_tile_stream(const void* rows, int seqs, int rows_per_seq
 
 hipError_t launch_calib_empty(hipStream_t st) {
   calib_empty_kernel<<<1, 64, 0, st>>>();
+  return hipGetLastError();
+}
+
+hipError_t launch_calib_load_pattern(int pattern, int workgroups, const void* buf, size_t bytes, uint32_t* cycles,
+                                     hipStream_t st) {
+  const auto* b = static_cast<const uint8_t*>(buf);
+  const auto n = static_cast<uint32_t>(bytes);
+  if (pattern == 0)
+    calib_load_pattern_kernel<0><<<workgroups, 512, 0, st>>>(b, n, cycles);
+  else
+    calib_load_pattern_kernel<1><<<workgroups, 512, 0, st>>>(b, n, cycles);
   return hipGetLastError();
 }
 

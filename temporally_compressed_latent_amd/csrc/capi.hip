@@ -1336,6 +1336,20 @@ int32_t mtla_calib_tile_stream(const void* rows, int32_t seqs, int32_t rows_per_
                     "tile-stream launch");
 }
 
+int32_t mtla_calib_load_pattern(int32_t pattern, int32_t workgroups, const void* buf, size_t bytes,
+                                uint32_t* cycles, void* stream) {
+  if (pattern != 0 && pattern != 1) return fail(MTLA_ERR_INVALID_ARG, "pattern=%d is not 0 or 1", pattern);
+  if (workgroups < 1 || workgroups > 65535)
+    return fail(MTLA_ERR_INVALID_ARG, "workgroups=%d outside 1..65535", workgroups);
+  if (!buf || !aligned16(buf)) return fail(MTLA_ERR_INVALID_ARG, "buf is NULL or not 16-byte aligned");
+  if (bytes < 131072 || bytes > (size_t(1) << 31))
+    return fail(MTLA_ERR_INVALID_ARG, "bytes=%zu outside 128 KiB..2 GiB", bytes);
+  CHECK_PTR_ALIGN(cycles, 4);
+  return hip_status(mtla::launch_calib_load_pattern(pattern, workgroups, buf, bytes, cycles,
+                                                    static_cast<hipStream_t>(stream)),
+                    "load-pattern launch");
+}
+
 int32_t mtla_calib_empty(void* stream) {
   return hip_status(mtla::launch_calib_empty(static_cast<hipStream_t>(stream)), "empty-kernel launch");
 }

@@ -254,6 +254,11 @@ hipError_t launch_calib_read(const void* src, size_t bytes, int workgroups, uint
 hipError_t launch_calib_mfma(bool f16, int workgroups, int iters, float* out, hipStream_t st);
 double calib_mfma_flops(int workgroups, int iters);
 hipError_t launch_calib_empty(hipStream_t st);
+// A compute unit's cost of one 16-byte-per-lane load instruction: pattern 0
+// contiguous kilobytes, 1 sixteen rows of 64 bytes; one workgroup per unit,
+// per-workgroup s_memtime cycles of 8 waves x 32 loads into cycles.
+hipError_t launch_calib_load_pattern(int pattern, int workgroups, const void* buf, size_t bytes, uint32_t* cycles,
+                                     hipStream_t st);
 hipError_t launch_calib_tile_stream(const void* rows, int seqs, int rows_per_seq, int splits, bool interleave,
                                     bool nt, uint32_t* sink, hipStream_t st);
 

@@ -522,13 +522,13 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
   }
 }
 
-// The same product for few rows (M <= 16 * NB <= 64, one token per sequence in
-// decode), in bf16: every lane loads its MFMA operand fragments straight from
-// memory (A row c16 and weight row c16, 8 consecutive k at 8 * g16), the
+// The same product for few rows (M <= 64, one token per sequence in decode),
+// in bf16: every lane loads its MFMA operand fragments straight from memory
+// (A row c16 and weight row c16, 8 consecutive k at 8 * g16), the
 // workgroup's four waves split K between them (wave w takes the 32-wide
 // k-steps w, w + 4, ...) with sixteen k-steps' loads in flight per round, and
 // the four partial tiles are summed through LDS.  One workgroup per 16 output
-// columns.
+// columns and 16 * NB rows (blockIdx.y: the block of rows).
 constexpr int SKN = 16;
 
 // The leading scalar arguments (A, the first weight matrix, M, N, K, that
@@ -543,6 +543,7 @@ __global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(const uint16_t* 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, c16 = lane & 15;
   const int n0 = blockIdx.x * SKN;
+  const int m0 = 16 * NB * blockIdx.y;  // first row of this workgroup's block of rows
   // epilogue item of this thread: column pair pc on rows er[0], er[1]; their
   // token positions are loaded first, so that they arrive with the operands
   constexpr int ER = (16 * NB + 31) / 32;
@@ -551,7 +552,7 @@ __global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(const uint16_t* 
 #pragma unroll
   for (int j = 0; j < ER; ++j) {
     er[j] = tid / (SKN / 2) + 32 * j;
-    epos[j] = g.mode != 0 ? row_position(g, min(er[j], M - 1)) : 0;
+    epos[j] = g.mode != 0 ? row_position(g, min(m0 + er[j], M - 1)) : 0;
   }
   // (a tile wholly inside the first weight matrix takes its rows from the
   // preloaded pointer)
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(const uint16_t* 
   const uint16_t* ar[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    ar[i] = A0 + static_cast<size_t>(min(16 * i + c16, M - 1)) * (lda0 ? lda0 : K) + 8 * g16;
+    ar[i] = A0 + static_cast<size_t>(min(m0 + 16 * i + c16, M - 1)) * (lda0 ? lda0 : K) + 8 * g16;
   f32x4 acc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -603,14 +604,14 @@ __global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(const uint16_t* 
 #pragma unroll
   for (int j = 0; j < ER; ++j) {
     const int r = er[j];
-    if (r >= M || r >= 16 * NB) break;
+    if (m0 + r >= M || r >= 16 * NB) break;
     float x0 = 0.f, x1 = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       x0 += sP[w][r * (SKN + 1) + 2 * pc];
       x1 += sP[w][r * (SKN + 1) + 2 * pc + 1];
     }
-    store_pair<uint16_t>(g, pd, r, n, epos[j], x0, x1);
+    store_pair<uint16_t>(g, pd, m0 + r, n, epos[j], x0, x1);
   }
 }
 
@@ -619,15 +620,13 @@ __global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(const uint16_t* 
 hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (dtype != 0 && g.M <= 64) {
-    const dim3 sgrid((g.N + SKN - 1) / SKN);
+    // one 16-row block per workgroup: the operand loads are spread over
+    // (M / 16) times more compute units (each load of 16 rows x 64 bytes
+    // takes a compute unit's memory pipeline about 32 cycles)
+    const dim3 sgrid((g.N + SKN - 1) / SKN, (g.M + 15) / 16);
     const uint16_t* A0 = static_cast<const uint16_t*>(g.A);
     const uint16_t* W0 = static_cast<const uint16_t*>(g.w0);
-    switch ((g.M + 15) / 16) {
-      case 1: layer_gemm_skinny_kernel<1><<<sgrid, 256, 0, st>>>(A0, W0, g.M, g.N, g.K, g.n0, g.lda, g); break;
-      case 2: layer_gemm_skinny_kernel<2><<<sgrid, 256, 0, st>>>(A0, W0, g.M, g.N, g.K, g.n0, g.lda, g); break;
-      case 3: layer_gemm_skinny_kernel<3><<<sgrid, 256, 0, st>>>(A0, W0, g.M, g.N, g.K, g.n0, g.lda, g); break;
-      default: layer_gemm_skinny_kernel<4><<<sgrid, 256, 0, st>>>(A0, W0, g.M, g.N, g.K, g.n0, g.lda, g); break;
-    }
+    layer_gemm_skinny_kernel<1><<<sgrid, 256, 0, st>>>(A0, W0, g.M, g.N, g.K, g.n0, g.lda, g);
     return hipGetLastError();
   }
   if (dtype != 0) {

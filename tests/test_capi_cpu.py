@@ -25,7 +25,7 @@ def dims(**kw):
 
 def test_exports_every_header_symbol():
     syms = m.header_symbols()
-    assert len(syms) == 36
+    assert len(syms) == 37
     for s in syms:
         assert hasattr(m.lib(), s), s
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
@@ -377,6 +377,11 @@ def test_measurement_hook_checks():
     assert L.mtla_calib_tile_stream(FAKE, 0, 64, 4, 0, FAKE, None) == bad
     assert L.mtla_calib_tile_stream(FAKE, 4, 0, 4, 0, FAKE, None) == bad
     assert L.mtla_calib_tile_stream(FAKE, 4, (2**31) // 1152 + 1, 4, 0, FAKE, None) == bad
+    assert L.mtla_calib_load_pattern(2, 4, FAKE, 1 << 20, FAKE, None) == bad     # no such pattern
+    assert L.mtla_calib_load_pattern(0, 0, FAKE, 1 << 20, FAKE, None) == bad
+    assert L.mtla_calib_load_pattern(0, 4, None, 1 << 20, FAKE, None) == bad
+    assert L.mtla_calib_load_pattern(1, 4, FAKE, 65536, FAKE, None) == bad        # under 128 KiB
+    assert L.mtla_calib_load_pattern(1, 4, FAKE, 1 << 20, MISALIGNED, None) == bad
     assert L.mtla_calib_tile_stream(FAKE, 4, 64, 65, 0, FAKE, None) == bad
     assert L.mtla_calib_tile_stream(FAKE, 4, 64, 4, 4, FAKE, None) == bad
     assert L.mtla_calib_tile_stream(FAKE, 4, 64, 4, 3, None, None) == bad

@@ -30,3 +30,14 @@ def test_mfma_chains_flop_count():
     torch.cuda.synchronize()
     assert flops == 4 * 8 * 4 * 16 * 2 * 32 * 32 * 16
     assert torch.isfinite(out).all()
+
+
+def test_load_pattern_cycles():
+    """Both load patterns run and report a positive cycle count per
+    workgroup; the guard words past the counts stay untouched."""
+    buf = torch.ones(1 << 16, dtype=torch.int32, device=DEV)  # 256 KiB
+    for pat in (0, 1):
+        cyc = torch.full((16 + 64,), -7, dtype=torch.int32, device=DEV)
+        m.mtla_calib_load_pattern(pat, 16, buf, cyc)
+        torch.cuda.synchronize()
+        assert torch.all(cyc[:16] > 0) and torch.all(cyc[16:] == -7)
