@@ -1822,7 +1822,9 @@ __global__ __launch_bounds__(256) void combine_up_project_kernel(int R, int H, i
   const int OP = d_c + 4;  // LDS pitch of a latent row (floats)
   UpW w0;
   up_w_round(w0, up_w_row(w_uv, x * 32, h, d_h, d_c), 16 * wave, d_c);
-  // thread tid forms 8-column chunk ch = tid % CR of rows tid / CR + RP j
+  // thread tid forms columns 4 ch .. +3 and d_c/2 + 4 ch .. +3 (ch = tid % CR)
+  // of rows tid / CR + RP j: a wave's loads of a split's row then read whole
+  // 128-byte lines
   const int CR = d_c / 8, RP = 256 / CR;
   const int ch = tid % CR;
   auto load_rows = [&](int rr0, float4 (&a)[RI][SMAX][2]) {
@@ -1832,9 +1834,9 @@ __global__ __launch_bounds__(256) void combine_up_project_kernel(int R, int H, i
       const size_t base = static_cast<size_t>(min(r0 + rr, R - 1)) * splits * H + h;
 #pragma unroll
       for (int k = 0; k < S; ++k) {
-        const float* src = p.acc + (base + static_cast<size_t>(k) * H) * d_c + 8 * ch;
+        const float* src = p.acc + (base + static_cast<size_t>(k) * H) * d_c + 4 * ch;
         a[q][k][0] = *reinterpret_cast<const float4*>(src);
-        a[q][k][1] = *reinterpret_cast<const float4*>(src + 4);
+        a[q][k][1] = *reinterpret_cast<const float4*>(src + d_c / 2);
       }
     }
   };
@@ -1878,9 +1880,9 @@ __global__ __launch_bounds__(256) void combine_up_project_kernel(int R, int H, i
         for (int j = 0; j < 8; ++j) v[j] = fmaf(av[j], w, v[j]);
       }
       const float Ls = rl[rr];
-      float* dst = so + rr * OP + 8 * ch;
+      float* dst = so + rr * OP + 4 * ch;
       *reinterpret_cast<float4*>(dst) = float4{v[0] / Ls, v[1] / Ls, v[2] / Ls, v[3] / Ls};
-      *reinterpret_cast<float4*>(dst + 4) = float4{v[4] / Ls, v[5] / Ls, v[6] / Ls, v[7] / Ls};
+      *reinterpret_cast<float4*>(dst + d_c / 2) = float4{v[4] / Ls, v[5] / Ls, v[6] / Ls, v[7] / Ls};
     }
   }
   __syncthreads();
