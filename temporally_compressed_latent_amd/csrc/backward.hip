@@ -909,8 +909,6 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
     for (int rt = 0; rt < 2; ++rt) {
       f32x16 sc, dp;
       scores(sK, sV, rt, sc, dp);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] *= qk;
       if (boundary) {
         // slot j0 + 32 rt + 8 (i / 4) + 4 grp + i % 4 is hidden iff >= vis
         const int rel = vis - j0 - 32 * rt - 4 * grp;
@@ -918,18 +916,21 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i)
           if (8 * (i / 4) + (i % 4) >= rel) sc[i] = -INFINITY;
       }
+      // the maximum of the raw scores, scaled once (tau log2 e > 0: the
+      // scaled scores have the same maximum); each score is scaled inside
+      // its exponent's fma
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx);
+      const float mn = fmaxf(m, mx * qk);
       const float f = fast_exp2(m - mn);
       ls *= f;
       dsum *= f;
       m = mn;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(sc[i] - m);
+        const float e = fast_exp2(fmaf(sc[i], qk, -m));
         ls += e;
         dsum = fmaf(e, dp[i], dsum);
       }
@@ -938,6 +939,8 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
   const float L = ls + __shfl_xor(ls, 32, 64);
   const float lse2 = qok ? m + log2f(L) : INFINITY;
   const float Dq = qok ? (dsum + __shfl_xor(dsum, 32, 64)) / L : 0.f;
+  // pass 2's exponent offset: tau p = exp2(z tau log2 e - lse2 + log2 tau)
+  const float lts = log2f(a.scale) - lse2;
   const float pii = qok ? fast_exp2(fmaf(zp, qk, -lse2)) : 0.f;
   const float dsii = a.scale * pii * (dpp - Dq);
   const size_t si = (static_cast<size_t>(b) * H + h) * N + (qok ? qi : 0);
@@ -988,7 +991,7 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
       f32x16 sc, dp;
       scores(sK, sV, rt, sc, dp);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = fast_exp2(fmaf(sc[i], qk, -lse2));
+      for (int i = 0; i < 16; ++i) sc[i] = fast_exp2(fmaf(sc[i], qk, lts));  // tau p
       if (boundary) {
         const int rel = vis - j0 - 32 * rt - 4 * grp;
 #pragma unroll
@@ -996,7 +999,7 @@ void bwd_dq_mfma_kernel(BwdArgs a) {
           if (8 * (i / 4) + (i % 4) >= rel) sc[i] = 0.f;
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = a.scale * sc[i] * (dp[i] - Dq);
+      for (int i = 0; i < 16; ++i) sc[i] *= dp[i] - Dq;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 db = acc_chunk_bf16(sc, c);

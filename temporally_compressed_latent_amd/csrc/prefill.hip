@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   // Epilogue: stage the 256x128 tile as fp16 (F16OUT) or bf16 in LDS, then
   // write each (token, head) row of d_h values with 16-byte stores.
-  // acc[i][j][e] is row 128 wm + 32 i + c32, column 64 wn + 32 j + 8 (e / 4)
+  // acc[i][j][e] is row (GBM / 2) wm + 32 i + c32, column 64 wn + 32 j + 8 (e / 4)
   // + 4 grp + e % 4: one 8-byte LDS store per four values.
   constexpr int CP = GBN + 8;
   static_assert(GBM * CP <= TileShape<GBM>::SmemElems, "C tile must fit in the operand stages");
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           w0 = f32_to_bf16_bits(c[4 * e4]) | (uint32_t(f32_to_bf16_bits(c[4 * e4 + 1])) << 16);
           w1 = f32_to_bf16_bits(c[4 * e4 + 2]) | (uint32_t(f32_to_bf16_bits(c[4 * e4 + 3])) << 16);
         }
-        *reinterpret_cast<uint2*>(&sC[(128 * wm + 32 * i + c32) * CP + 64 * wn + 32 * j + 8 * e4 + 4 * grp]) =
+        *reinterpret_cast<uint2*>(&sC[((GBM / 2) * wm + 32 * i + c32) * CP + 64 * wn + 32 * j + 8 * e4 + 4 * grp]) =
             uint2{w0, w1};
       }
   __syncthreads();
