@@ -228,6 +228,37 @@ int32_t mtla_decode_step_noalloc(const mtla_dims* dims, const int32_t* pos, cons
                                  float* open_acc, void* out, void* stream);
 
 /*
+ * W_UV in the order in which the fused decode step's up-projection reads
+ * it, for callers that run many decode steps with the same weights (the
+ * up-projection of "Multi-head Temporal Latent Attention", Method (3),
+ * unchanged: the same values in another order).  For head h, 16-row tile t
+ * (rows 16t .. 16t+15 of W_UV[h]) and 32-column step ks, one 1,024-byte
+ * block whose 16-byte piece q (0..63) holds row 16t + q % 16, columns
+ * 32 ks + 8 (q / 16) .. +7; rows past d_h are zero.  Loaded in this order,
+ * every load instruction of the up-projection reads whole 128-byte lines.
+ *   mtla_w_uv_tiles_bytes: *bytes = H * ceil(d_h/16) * 16 * d_c * 2.
+ *   mtla_pack_w_uv_tiles: w_uv device [H, d_h, d_c] bf16, 16-byte aligned;
+ *     w_uv_tiles device, >= mtla_w_uv_tiles_bytes bytes, 16-byte aligned,
+ *     written (enqueued on stream).
+ * bf16 only, d_c a multiple of 32 (MTLA_ERR_UNSUPPORTED otherwise).
+ */
+int32_t mtla_w_uv_tiles_bytes(const mtla_dims* dims, size_t* bytes);
+int32_t mtla_pack_w_uv_tiles(const mtla_dims* dims, const void* w_uv, void* w_uv_tiles, void* stream);
+
+/*
+ * mtla_decode_step with W_UV also given in tile order (mtla_pack_w_uv_tiles
+ * of the same w_uv): the same outputs, cache rows and open-slot state, bit
+ * for bit.  The fused step kernel of 256-wide latents reads w_uv_tiles; the
+ * other paths read w_uv.  Arguments and errors as for mtla_decode_step, and
+ * the checks of mtla_pack_w_uv_tiles on w_uv_tiles.
+ */
+int32_t mtla_decode_step_tiles(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
+                               const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                               const void* q_r, const void* w_uk, const void* w_uv, const void* w_uv_tiles,
+                               void* cache, float* open_acc, void* out, void* workspace, size_t ws_bytes,
+                               void* stream);
+
+/*
  * Staged form of mtla_decode, for callers that fuse the two projections into
  * their own GEMMs (mtla_decode runs exactly these three stages).
  *

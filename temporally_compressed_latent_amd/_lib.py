@@ -103,6 +103,9 @@ _SIGS = {
     "mtla_decode_plan": (_I, [_D, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "mtla_decode_step": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_decode_step_noalloc": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mtla_w_uv_tiles_bytes": (_I, [_D, ctypes.POINTER(_SZ)]),
+    "mtla_pack_w_uv_tiles": (_I, [_D, _P, _P, _P]),
+    "mtla_decode_step_tiles": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mtla_prefill_partials": (_I, [_D, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P]),
     "mtla_prefill_keys": (_I, [_D, _I, _P, _P, _P, _P, _P, _P]),
     "mtla_prefill_attention": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -293,6 +296,45 @@ def mtla_decode_step(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w_uk, w_u
         _tensor("q_r", q_r, (B, H, dims.d_r), st, optional=dims.d_r == 0),
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
+        _tensor("out", out, (B, H, dims.d_h), st),
+        ws, ws_bytes, _stream(stream)))
+
+
+def mtla_w_uv_tiles_bytes(dims: MtlaDims) -> int:
+    n = _SZ(0)
+    _check(_lib.mtla_w_uv_tiles_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def mtla_pack_w_uv_tiles(dims: MtlaDims, w_uv, w_uv_tiles, stream=None) -> None:
+    """W_UV [H, d_h, d_c] into the fused decode step's tile order (a flat
+    bf16 tensor of mtla_w_uv_tiles_bytes(dims) / 2 elements)."""
+    n = mtla_w_uv_tiles_bytes(dims) // 2
+    _check(_lib.mtla_pack_w_uv_tiles(
+        ctypes.byref(dims),
+        _tensor("w_uv", w_uv, (dims.heads, dims.d_h, dims.d_c), dims.torch_dtype),
+        _tensor("w_uv_tiles", w_uv_tiles, (n,), dims.torch_dtype), _stream(stream)))
+
+
+def mtla_decode_step_tiles(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w_uk, w_uv, w_uv_tiles, cache,
+                           open_acc, out, workspace, stream=None) -> None:
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    n = mtla_w_uv_tiles_bytes(dims) // 2
+    _check(_lib.mtla_decode_step_tiles(
+        ctypes.byref(dims),
+        _tensor("pos", pos, (B,), torch.int32),
+        _tensor("c", c, (B, dims.d_c), st),
+        _tensor("k_r", k_r, (B, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("q_c", q_c, (B, H, dims.d_h), st),
+        _tensor("q_r", q_r, (B, H, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv_tiles", w_uv_tiles, (n,), st),
         _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
         _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
         _tensor("out", out, (B, H, dims.d_h), st),

@@ -477,7 +477,7 @@ static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const
                                 const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
                                 const void* q_r, const void* w_uk, const void* w_uv, void* cache,
                                 float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream,
-                                bool check_only);
+                                bool check_only, const void* w_uv_tiles);
 
 int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
                          const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
@@ -485,14 +485,50 @@ int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* 
                          float* open_acc, void* out, void* workspace, size_t ws_bytes,
                          void* stream) {
   return decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, out,
-                          workspace, ws_bytes, stream, false);
+                          workspace, ws_bytes, stream, false, nullptr);
+}
+
+int32_t mtla_w_uv_tiles_bytes(const mtla_dims* dims, size_t* bytes) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (!bytes) return fail(MTLA_ERR_INVALID_ARG, "bytes is NULL");
+  if (dims->dtype != MTLA_BF16) return fail(MTLA_ERR_UNSUPPORTED, "W_UV tiles are bf16 only");
+  if (dims->d_c % 32 != 0) return fail(MTLA_ERR_UNSUPPORTED, "d_c=%d is not a multiple of 32", dims->d_c);
+  *bytes = mtla::w_uv_tiles_elems(dims->heads, dims->d_h, dims->d_c) * sizeof(uint16_t);
+  return ok();
+}
+
+int32_t mtla_pack_w_uv_tiles(const mtla_dims* dims, const void* w_uv, void* w_uv_tiles, void* stream) {
+  size_t bytes = 0;
+  int32_t st = mtla_w_uv_tiles_bytes(dims, &bytes);
+  if (st != MTLA_OK) return st;
+  if (!w_uv || !aligned16(w_uv)) return fail(MTLA_ERR_INVALID_ARG, "w_uv is NULL or not 16-byte aligned");
+  if (!w_uv_tiles || !aligned16(w_uv_tiles))
+    return fail(MTLA_ERR_INVALID_ARG, "w_uv_tiles is NULL or not 16-byte aligned");
+  return hip_status(mtla::launch_pack_w_uv_tiles(dims->heads, dims->d_h, dims->d_c, static_cast<const uint16_t*>(w_uv),
+                                                 static_cast<uint16_t*>(w_uv_tiles), static_cast<hipStream_t>(stream)),
+                    "W_UV tile pack launch");
+}
+
+int32_t mtla_decode_step_tiles(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
+                               const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                               const void* q_r, const void* w_uk, const void* w_uv, const void* w_uv_tiles,
+                               void* cache, float* open_acc, void* out, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  size_t bytes = 0;
+  int32_t st = mtla_w_uv_tiles_bytes(dims, &bytes);
+  if (st != MTLA_OK) return st;
+  if (!w_uv_tiles || !aligned16(w_uv_tiles))
+    return fail(MTLA_ERR_INVALID_ARG, "w_uv_tiles is NULL or not 16-byte aligned");
+  return decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, out,
+                          workspace, ws_bytes, stream, false, w_uv_tiles);
 }
 
 static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
                                 const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
                                 const void* q_r, const void* w_uk, const void* w_uv, void* cache,
                                 float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream,
-                                bool check_only) {
+                                bool check_only, const void* w_uv_tiles) {
   int32_t st = check_dims(dims);
   if (st != MTLA_OK) return st;
   if (pe_rows < 1) return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < 1", pe_rows);
@@ -523,6 +559,7 @@ static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const
     mtla::StepArgs a = step_args(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv,
                                  cache, open_acc, out, 1);
     a.wh_stride = gate_stride(dims);
+    if (dims->d_c == 256) a.w_uv_tiles = static_cast<const uint16_t*>(w_uv_tiles);
     return hip_status(mtla::launch_decode_step(a, s), "decode step launch");
   }
   mtla::MergeArgs m{dims->batch, 1, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, pe_rows,
@@ -589,12 +626,12 @@ int32_t mtla_decode_step_noalloc(const mtla_dims* dims, const int32_t* pos, cons
   // address: only its non-null, aligned value is checked)
   st = decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, out,
                         reinterpret_cast<void*>(static_cast<uintptr_t>(256)), MTLA_NOALLOC_SCRATCH_BYTES,
-                        stream, true);
+                        stream, true, nullptr);
   if (st != MTLA_OK || dims->batch == 0) return st;
   void* ws = nullptr;
   if ((st = scratch_address(&ws)) != MTLA_OK) return st;
   return decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, out,
-                          ws, MTLA_NOALLOC_SCRATCH_BYTES, stream, false);
+                          ws, MTLA_NOALLOC_SCRATCH_BYTES, stream, false, nullptr);
 }
 
 int32_t mtla_prefill_workspace_bytes(const mtla_dims* dims, int32_t n_tokens, size_t* bytes) {
@@ -983,7 +1020,7 @@ int32_t mtla_layer_decode_step(const mtla_dims* dims, int32_t d_model, const int
        *q_r = at(workspace, lw.q_r), *o = at(workspace, lw.o);
   // the core's own checks run before anything is enqueued
   if ((st = decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, o,
-                             at(workspace, lw.core), dw.total, nullptr, true)) != MTLA_OK)
+                             at(workspace, lw.core), dw.total, nullptr, true, nullptr)) != MTLA_OK)
     return st;
   if ((st = mtla_project_inputs(dims, d_model, 1, pos, h, w_dkv, w_q, w_r, c, k_r, q_c, q_r, stream)) != MTLA_OK)
     return st;

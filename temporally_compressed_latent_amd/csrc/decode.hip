@@ -1242,10 +1242,16 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   const int mt_n = (d_h + 15) / 16;
   const int hu = min(wave / mt_n, HG - 1), mt = wave % mt_n;
   const bool up_wave = wave < HG * mt_n;
+  // W_UV row-major: load ks reads 16 rows x 64 bytes (rows past d_h clamped,
+  // their products not stored); in tile order: the same values as one
+  // contiguous kilobyte per load (rows past d_h zero)
+  const bool tiles = a.w_uv_tiles != nullptr;
   const auto r_uv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.w_uv + static_cast<size_t>(h0) * d_h * DC), static_cast<short>(0), HG * d_h * DC * 2,
-      kBufferRsrcWord3);
-  const int vu = ((hu * d_h + min(mt * 16 + c16, d_h - 1)) * DC + 8 * g) * 2;
+      const_cast<uint16_t*>(tiles ? a.w_uv_tiles + static_cast<size_t>(h0) * mt_n * 16 * DC
+                                  : a.w_uv + static_cast<size_t>(h0) * d_h * DC),
+      static_cast<short>(0), (tiles ? mt_n * 16 : d_h) * HG * DC * 2, kBufferRsrcWord3);
+  const int vu = tiles ? (hu * mt_n + mt) * KSU * 1024 + 16 * lane : ((hu * d_h + min(mt * 16 + c16, d_h - 1)) * DC + 8 * g) * 2;
+  const int vstep = tiles ? 1024 : 64;
   uint4 wv[KSU];  // loaded after the cache rows (see below)
   const int te = min(tid, W - 1);  // merge column of this thread (tid < W)
   uint16_t gxb[GE], mxb = 0;
@@ -1323,7 +1329,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   // arrived when the waves are combined
 #pragma unroll
   for (int ks = 0; ks < KSU; ++ks) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_uv, vu + ks * 64, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_uv, vu + ks * vstep, 0, 0);
     wv[ks] = uint4{v[0], v[1], v[2], v[3]};
   }
 
@@ -1994,6 +2000,38 @@ hipError_t launch_up_project(int R, int H, int d_h, int d_c, const float* o_lat,
                              void* out, int dtype, hipStream_t st) {
   return dtype == 0 ? up_project_t<float>(R, H, d_h, d_c, o_lat, w_uv, out, st)
                     : up_project_t<uint16_t>(R, H, d_h, d_c, o_lat, w_uv, out, st);
+}
+
+namespace {
+// One thread per 16-byte piece of the tile order (see kernels.hpp).
+__global__ __launch_bounds__(256) void pack_w_uv_tiles_kernel(int H, int d_h, int d_c, size_t pieces,
+                                                              const uint16_t* __restrict__ w_uv,
+                                                              uint16_t* __restrict__ tiles) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  const int nks = d_c / 32, nt = (d_h + 15) / 16;
+  const int q = static_cast<int>(i % 64);
+  const size_t blk = i / 64;
+  const int ks = static_cast<int>(blk % nks);
+  const int t = static_cast<int>((blk / nks) % nt);
+  const int h = static_cast<int>(blk / (static_cast<size_t>(nks) * nt));
+  const int row = 16 * t + q % 16, col = 32 * ks + 8 * (q / 16);
+  uint4 v = uint4{0u, 0u, 0u, 0u};
+  if (row < d_h) v = *reinterpret_cast<const uint4*>(w_uv + (static_cast<size_t>(h) * d_h + row) * d_c + col);
+  *reinterpret_cast<uint4*>(tiles + 8 * i) = v;
+}
+}  // namespace
+
+size_t w_uv_tiles_elems(int H, int d_h, int d_c) {
+  return static_cast<size_t>(H) * ((d_h + 15) / 16) * 16 * d_c;
+}
+
+hipError_t launch_pack_w_uv_tiles(int H, int d_h, int d_c, const uint16_t* w_uv, uint16_t* tiles, hipStream_t st) {
+  const size_t pieces = w_uv_tiles_elems(H, d_h, d_c) / 8;
+  if (pieces == 0) return hipSuccess;
+  pack_w_uv_tiles_kernel<<<static_cast<unsigned>((pieces + 255) / 256), 256, 0, st>>>(H, d_h, d_c, pieces, w_uv,
+                                                                                     tiles);
+  return hipGetLastError();
 }
 
 namespace {

@@ -203,12 +203,21 @@ struct StepArgs {
   float* open_acc;        // [B, 2, W]: state after token t at [b, t % 2]
   uint16_t* out;          // [B, H, d_h]
   int wh_stride = 0;      // d_c: W_hyp has one row per place in the block (256-wide latents only)
+  // W_UV in tile order (launch_pack_w_uv_tiles), or null: the 256-wide fused
+  // step then reads it as whole lines (same values, same bits)
+  const uint16_t* w_uv_tiles = nullptr;
 };
 bool decode_step_supported(int H, int d_h, int d_c, int d_r);
 // Head groups per sequence the step kernel uses for a batch of B sequences
 // (`requested` when it is a valid group count, else the launcher's choice).
 int decode_step_groups(int B, int H, int d_h, int d_c, int requested);
 hipError_t launch_decode_step(const StepArgs& a, hipStream_t st);
+// W_UV [H, d_h, d_c] (bf16, d_c a multiple of 32) in the fused step's tile
+// order: for head h, 16-row tile t and 32-column step ks, a 1 KB block whose
+// 16-byte piece q holds row 16 t + q % 16, columns 32 ks + 8 (q / 16) .. +7
+// (rows past d_h zero): [H, ceil(d_h / 16), d_c / 32, 64, 8] elements.
+size_t w_uv_tiles_elems(int H, int d_h, int d_c);
+hipError_t launch_pack_w_uv_tiles(int H, int d_h, int d_c, const uint16_t* w_uv, uint16_t* tiles, hipStream_t st);
 
 // out[r, h, :] = W_UV[h] o_lat[r, h].
 hipError_t launch_up_project(int R, int H, int d_h, int d_c, const float* o_lat, const void* w_uv,

@@ -74,17 +74,20 @@ class Case:
             outs[:, t - 1 - start] = self.decode(pos, t - 1)
         return outs
 
-    def step_loop(self, n_steps: int, start: int = 0) -> torch.Tensor:
-        """Token-by-token with mtla_decode_step (merge + decode in one call)."""
+    def step_loop(self, n_steps: int, start: int = 0, w_uv_tiles=None) -> torch.Tensor:
+        """Token-by-token with mtla_decode_step (merge + decode in one call);
+        with w_uv_tiles, mtla_decode_step_tiles."""
         d = self.d
         outs = torch.empty(d.batch, n_steps - start, d.heads, d.d_h, dtype=self.st, device=DEV)
         for t in range(start + 1, n_steps + 1):
             pos = torch.full((d.batch,), t, dtype=torch.int32, device=DEV)
             o = torch.empty(d.batch, d.heads, d.d_h, dtype=self.st, device=DEV)
-            m.mtla_decode_step(d, pos, self.c[:, t - 1].contiguous(), self.k_r[:, t - 1].contiguous(),
-                               self.w_hyp, self.pe, self.q_c[:, t - 1].contiguous(),
-                               self.q_r[:, t - 1].contiguous(), self.w_uk, self.w_uv, self.cache,
-                               self.open_acc, o, self.ws_dec)
+            args = (d, pos, self.c[:, t - 1].contiguous(), self.k_r[:, t - 1].contiguous(), self.w_hyp, self.pe,
+                    self.q_c[:, t - 1].contiguous(), self.q_r[:, t - 1].contiguous(), self.w_uk, self.w_uv)
+            if w_uv_tiles is None:
+                m.mtla_decode_step(*args, self.cache, self.open_acc, o, self.ws_dec)
+            else:
+                m.mtla_decode_step_tiles(*args, w_uv_tiles, self.cache, self.open_acc, o, self.ws_dec)
             outs[:, t - 1 - start] = o
         return outs
 
@@ -118,6 +121,7 @@ SHAPES = {
     "llm": (32, 128, 512, 64),
     "mid": (20, 32, 256, 32),
     "odd": (3, 16, 48, 8),
+    "d40": (4, 40, 256, 32),
 }
 
 

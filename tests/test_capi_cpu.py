@@ -25,7 +25,7 @@ def dims(**kw):
 
 def test_exports_every_header_symbol():
     syms = m.header_symbols()
-    assert len(syms) == 37
+    assert len(syms) == 40
     for s in syms:
         assert hasattr(m.lib(), s), s
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
@@ -385,3 +385,28 @@ def test_measurement_hook_checks():
     assert L.mtla_calib_tile_stream(FAKE, 4, 64, 65, 0, FAKE, None) == bad
     assert L.mtla_calib_tile_stream(FAKE, 4, 64, 4, 4, FAKE, None) == bad
     assert L.mtla_calib_tile_stream(FAKE, 4, 64, 4, 3, None, None) == bad
+
+
+def test_w_uv_tiles_argument_checks():
+    """The tile-order W_UV entry points: size, bf16 only, pointers checked
+    before any launch; the tiled decode step checks its tiles and then
+    everything mtla_decode_step checks."""
+    L, d = m.lib(), dims()
+    assert m.mtla_w_uv_tiles_bytes(d) == 8 * 4 * 16 * 256 * 2               # H=8, d_h=64: 4 tiles of 16 rows
+    assert m.mtla_w_uv_tiles_bytes(dims(d_h=40)) == 8 * 3 * 16 * 256 * 2    # rows padded to 48
+    d32 = m.make_dims(4, 8, 64, 256, 32, 2, 128, "fp32")
+    n = ctypes.c_size_t(0)
+    assert L.mtla_w_uv_tiles_bytes(ctypes.byref(d32), ctypes.byref(n)) == m.MTLA_ERR_UNSUPPORTED
+    assert L.mtla_w_uv_tiles_bytes(ctypes.byref(d), None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_pack_w_uv_tiles(ctypes.byref(d), None, FAKE, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_pack_w_uv_tiles(ctypes.byref(d), FAKE, MISALIGNED, None) == m.MTLA_ERR_INVALID_ARG
+    assert L.mtla_pack_w_uv_tiles(ctypes.byref(d32), FAKE, FAKE, None) == m.MTLA_ERR_UNSUPPORTED
+    need = m.mtla_decode_workspace_bytes(d)
+    call = lambda dd=d, **k: L.mtla_decode_step_tiles(
+        ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, k.get("pe_rows", 64), FAKE, FAKE, FAKE, FAKE,
+        k.get("tiles", FAKE), FAKE, FAKE, FAKE, k.get("ws", FAKE), need, None)
+    assert call(tiles=None) == m.MTLA_ERR_INVALID_ARG and "w_uv_tiles" in m.last_error()
+    assert call(tiles=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
+    assert call(dd=d32) == m.MTLA_ERR_UNSUPPORTED
+    assert call(pe_rows=0) == m.MTLA_ERR_INVALID_ARG
+    assert call(ws=None) == m.MTLA_ERR_WORKSPACE

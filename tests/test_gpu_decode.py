@@ -207,3 +207,28 @@ def test_decode_step_invalid_positions():
     assert np.isfinite(out[0]).all()
     assert np.isnan(out[1]).all() and np.isnan(out[2]).all()
     assert torch.equal(g.cache[1:], before[1:])
+
+
+@pytest.mark.parametrize("shape,s,B,N", [("st", 2, 4, 130), ("mid", 3, 3, 100), ("d40", 2, 5, 70)])
+def test_decode_step_tiles_equals_decode_step(shape, s, B, N):
+    """mtla_pack_w_uv_tiles writes W_UV in the documented tile order (checked
+    against a host gather, rows past d_h zero), and mtla_decode_step_tiles
+    gives the bits of mtla_decode_step: outputs, cache rows, open-slot state."""
+    import numpy as np
+    import temporally_compressed_latent_amd as m
+    _, a = make_case(shape, 21, B, N, s, "bf16")
+    _, b_ = make_case(shape, 21, B, N, s, "bf16")
+    d = b_.d
+    tiles = torch.full((m.mtla_w_uv_tiles_bytes(d) // 2,), 7.0, dtype=torch.bfloat16, device=DEV)
+    m.mtla_pack_w_uv_tiles(d, b_.w_uv, tiles)
+    H, d_h, d_c = d.heads, d.d_h, d.d_c
+    nt = -(-d_h // 16)
+    w = np.zeros((H, nt * 16, d_c), dtype=np.int16)
+    w[:, :d_h] = b_.w_uv.view(torch.int16).cpu().numpy()
+    want = w.reshape(H, nt, 16, d_c // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5).reshape(-1)
+    assert np.array_equal(tiles.view(torch.int16).cpu().numpy(), want)
+    x = a.step_loop(N)
+    y = b_.step_loop(N, w_uv_tiles=tiles)
+    assert torch.equal(bits(x), bits(y))
+    assert torch.equal(bits(a.cache), bits(b_.cache))
+    assert torch.equal(a.open_acc, b_.open_acc)
