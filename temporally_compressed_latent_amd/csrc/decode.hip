@@ -1111,11 +1111,13 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restr
 //   attention     : wave-private flash decoding.  Wave w takes slot chunks
 //                   w, w + 8, ... of 16 slots and keeps its own running max,
 //                   sum and o_lat accumulator, with no barrier:
-//                     S^T[slot, head] = rows . q~^T  (16x16x32 MFMA; rows
-//                       straight from memory in the A layout, q~ from LDS),
+//                     S^T[slot, head] = rows . q~^T  (16x16x32 MFMA; the
+//                       chunk's rows are loaded as whole lines into a
+//                       wave-private LDS buffer and read back in the A
+//                       layout, q~ from LDS),
 //                     O^T[col, head] += V^T P^T      (16x16x16 MFMA; P^T
 //                       stays in the score registers, V^T is read transposed
-//                       from a wave-private copy of the chunk's rows);
+//                       from the same buffer);
 //                   q~ and P enter both products as a bf16 high and low
 //                   part (16 significant bits): head h takes MFMA column h
 //                   for the high parts and column HG + h for the low parts;
@@ -1124,7 +1126,8 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restr
 //                   the 8 waves' partial results are merged once, in wave
 //                   order;
 //   up-projection : out[h] = W_UV[h] o_lat[h] on MFMA, one 16-row tile of
-//                   W_UV per wave; o_lat goes in as bf16 hi + lo parts
+//                   W_UV per wave (row-major, or in tile order when the
+//                   caller packed it); o_lat goes in as bf16 hi + lo parts
 //                   (o_lat = hi + lo to 16 bits), two products per k-step.
 // Heads occupy the MFMA's 16-wide N dimension (2 HG columns with the low
 // parts); the columns past 2 HG read q~ from a zero row.
