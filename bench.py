@@ -361,9 +361,10 @@ def run_prefill_chunk(w, steps, warmup, m, torch, workloads):
 
 def run_layer_decode(w, steps, warmup, m, torch, workloads):
     """The whole layer from h at the speech-translation decode shape: for every
-    token, mtla_layer_decode_step (input projections + RoPE, the fused core
-    step, output projection), 512 steps per replay.  Weights and h are the
-    seeded layer parameters at d_model = 512."""
+    token, mtla_layer_decode_step_tiles (input projections + RoPE, the fused
+    core step, output projection; W_UV packed into tile order once), 512
+    steps per replay.  Weights and h are the seeded layer parameters at
+    d_model = 512."""
     B, N = w.batch, w.n_tokens
     d = m.make_dims(B, w.heads, w.d_h, w.d_c, w.d_r, w.s, -(-N // w.s), "bf16")
     p = workloads.layer_params(w)
@@ -377,17 +378,21 @@ def run_layer_decode(w, steps, warmup, m, torch, workloads):
     ws = torch.empty(m.mtla_layer_decode_workspace_bytes(d, w.d_model), dtype=torch.uint8, device="cuda")
     y = torch.empty(N, B, w.d_model, dtype=bf, device="cuda")
     pos = (torch.arange(1, N + 1, dtype=torch.int32, device="cuda")[:, None].expand(N, B).contiguous())
+    w_uv_tiles = torch.empty(m.mtla_w_uv_tiles_bytes(d) // 2, dtype=bf, device="cuda")
+    m.mtla_pack_w_uv_tiles(d, dev["w_uv"], w_uv_tiles)
 
     def fn():
         for t in range(N):
-            m.mtla_layer_decode_step(d, pos[t], h_t[t], dev["w_dkv"], dev["w_q"], dev["w_r"], dev["w_o"],
-                                     dev["w_hyp"], pe, dev["w_uk"], dev["w_uv"], cache, open_acc, y[t], ws)
+            m.mtla_layer_decode_step_tiles(d, pos[t], h_t[t], dev["w_dkv"], dev["w_q"], dev["w_r"], dev["w_o"],
+                                           dev["w_hyp"], pe, dev["w_uk"], dev["w_uv"], w_uv_tiles, cache,
+                                           open_acc, y[t], ws)
     g = capture(fn, torch)
     for _ in range(warmup):
         g.replay()
     ms = timed_graph(g, steps, torch)
     return {"workload": "layer_" + w.name, "d_model": w.d_model, "ms_per_step": ms,
-            "tokens_per_s": B * N / (ms * 1e-3), "us_per_token_step": ms * 1e3 / N}
+            "tokens_per_s": B * N / (ms * 1e-3), "us_per_token_step": ms * 1e3 / N,
+            "entry_point": "mtla_layer_decode_step_tiles (W_UV packed once)"}
 
 
 def run_layer_prefill(w, steps, warmup, m, torch, workloads):

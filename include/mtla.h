@@ -475,6 +475,20 @@ int32_t mtla_layer_decode_step(const mtla_dims* dims, int32_t d_model, const int
                                const void* w_uv, void* cache, float* open_acc, void* y, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/*
+ * mtla_layer_decode_step with W_UV also given in tile order
+ * (mtla_pack_w_uv_tiles of the same w_uv): the same y, cache rows and
+ * open-slot state, bit for bit; the decode step inside is
+ * mtla_decode_step_tiles.  Arguments and errors as for
+ * mtla_layer_decode_step, and the checks of mtla_pack_w_uv_tiles on
+ * w_uv_tiles.
+ */
+int32_t mtla_layer_decode_step_tiles(const mtla_dims* dims, int32_t d_model, const int32_t* pos, const void* h,
+                                     const void* w_dkv, const void* w_q, const void* w_r, const void* w_o,
+                                     const float* w_hyp, const float* pe, int32_t pe_rows, const void* w_uk,
+                                     const void* w_uv, const void* w_uv_tiles, void* cache, float* open_acc,
+                                     void* y, void* workspace, size_t ws_bytes, void* stream);
+
 /* Bytes of workspace mtla_layer_prefill needs. */
 int32_t mtla_layer_prefill_workspace_bytes(const mtla_dims* dims, int32_t d_model, int32_t t0,
                                            int32_t n_tokens, size_t* bytes);

@@ -127,6 +127,7 @@ _SIGS = {
     "mtla_layer_decode_workspace_bytes": (_I, [_D, _I, ctypes.POINTER(_SZ)]),
     "mtla_layer_decode_step": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ,
                                     _P]),
+    "mtla_layer_decode_step_tiles": (_I, [_D, _I] + [_P] * 8 + [_I] + [_P] * 7 + [_SZ, _P]),
     "mtla_layer_prefill_workspace_bytes": (_I, [_D, _I, _I, _I, ctypes.POINTER(_SZ)]),
     "mtla_layer_prefill": (_I, [_D, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ,
                                 _P]),
@@ -663,6 +664,28 @@ def mtla_layer_decode_step(dims: MtlaDims, pos, h, w_dkv, w_q, w_r, w_o, w_hyp, 
         _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
         _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
         _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
+        _tensor("y", y, (B, dm), st),
+        ws, ws_bytes, _stream(stream)))
+
+
+def mtla_layer_decode_step_tiles(dims: MtlaDims, pos, h, w_dkv, w_q, w_r, w_o, w_hyp, pe, w_uk, w_uv, w_uv_tiles,
+                                 cache, open_acc, y, workspace, stream=None) -> None:
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    dm = int(h.shape[-1])
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    wd, wq, wr, wo = _layer_weights(dims, dm, w_dkv, w_q, w_r, w_o)
+    n = mtla_w_uv_tiles_bytes(dims) // 2
+    _check(_lib.mtla_layer_decode_step_tiles(
+        ctypes.byref(dims), dm,
+        _tensor("pos", pos, (B,), torch.int32),
+        _tensor("h", h, (B, dm), st), wd, wq, wr, wo,
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv_tiles", w_uv_tiles, (n,), st),
         _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
         _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
         _tensor("y", y, (B, dm), st),

@@ -996,11 +996,11 @@ int32_t mtla_layer_decode_workspace_bytes(const mtla_dims* dims, int32_t d_model
   return ok();
 }
 
-int32_t mtla_layer_decode_step(const mtla_dims* dims, int32_t d_model, const int32_t* pos, const void* h,
-                               const void* w_dkv, const void* w_q, const void* w_r, const void* w_o,
-                               const float* w_hyp, const float* pe, int32_t pe_rows, const void* w_uk,
-                               const void* w_uv, void* cache, float* open_acc, void* y, void* workspace,
-                               size_t ws_bytes, void* stream) {
+static int32_t layer_decode_step_impl(const mtla_dims* dims, int32_t d_model, const int32_t* pos, const void* h,
+                                     const void* w_dkv, const void* w_q, const void* w_r, const void* w_o,
+                                     const float* w_hyp, const float* pe, int32_t pe_rows, const void* w_uk,
+                                     const void* w_uv, const void* w_uv_tiles, void* cache, float* open_acc,
+                                     void* y, void* workspace, size_t ws_bytes, void* stream) {
   int32_t st = check_dims(dims);
   if (st != MTLA_OK) return st;
   if ((st = check_layer(dims, d_model)) != MTLA_OK) return st;
@@ -1024,10 +1024,33 @@ int32_t mtla_layer_decode_step(const mtla_dims* dims, int32_t d_model, const int
     return st;
   if ((st = mtla_project_inputs(dims, d_model, 1, pos, h, w_dkv, w_q, w_r, c, k_r, q_c, q_r, stream)) != MTLA_OK)
     return st;
-  if ((st = mtla_decode_step(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, o,
-                             at(workspace, lw.core), dw.total, stream)) != MTLA_OK)
+  if ((st = decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, o,
+                             at(workspace, lw.core), dw.total, stream, false, w_uv_tiles)) != MTLA_OK)
     return st;
   return mtla_output_project(dims, d_model, dims->batch, o, w_o, y, stream);
+}
+
+int32_t mtla_layer_decode_step(const mtla_dims* dims, int32_t d_model, const int32_t* pos, const void* h,
+                               const void* w_dkv, const void* w_q, const void* w_r, const void* w_o,
+                               const float* w_hyp, const float* pe, int32_t pe_rows, const void* w_uk,
+                               const void* w_uv, void* cache, float* open_acc, void* y, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  return layer_decode_step_impl(dims, d_model, pos, h, w_dkv, w_q, w_r, w_o, w_hyp, pe, pe_rows, w_uk, w_uv,
+                                nullptr, cache, open_acc, y, workspace, ws_bytes, stream);
+}
+
+int32_t mtla_layer_decode_step_tiles(const mtla_dims* dims, int32_t d_model, const int32_t* pos, const void* h,
+                                     const void* w_dkv, const void* w_q, const void* w_r, const void* w_o,
+                                     const float* w_hyp, const float* pe, int32_t pe_rows, const void* w_uk,
+                                     const void* w_uv, const void* w_uv_tiles, void* cache, float* open_acc,
+                                     void* y, void* workspace, size_t ws_bytes, void* stream) {
+  size_t bytes = 0;
+  int32_t st = mtla_w_uv_tiles_bytes(dims, &bytes);
+  if (st != MTLA_OK) return st;
+  if (!w_uv_tiles || !aligned16(w_uv_tiles))
+    return fail(MTLA_ERR_INVALID_ARG, "w_uv_tiles is NULL or not 16-byte aligned");
+  return layer_decode_step_impl(dims, d_model, pos, h, w_dkv, w_q, w_r, w_o, w_hyp, pe, pe_rows, w_uk, w_uv,
+                                w_uv_tiles, cache, open_acc, y, workspace, ws_bytes, stream);
 }
 
 int32_t mtla_layer_prefill_workspace_bytes(const mtla_dims* dims, int32_t d_model, int32_t t0, int32_t n_tokens,

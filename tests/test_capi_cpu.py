@@ -25,7 +25,7 @@ def dims(**kw):
 
 def test_exports_every_header_symbol():
     syms = m.header_symbols()
-    assert len(syms) == 40
+    assert len(syms) == 41
     for s in syms:
         assert hasattr(m.lib(), s), s
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True).stdout
@@ -409,4 +409,15 @@ def test_w_uv_tiles_argument_checks():
     assert call(tiles=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
     assert call(dd=d32) == m.MTLA_ERR_UNSUPPORTED
     assert call(pe_rows=0) == m.MTLA_ERR_INVALID_ARG
+    assert call(ws=None) == m.MTLA_ERR_WORKSPACE
+
+
+def test_layer_decode_tiles_argument_checks():
+    L, d = m.lib(), dims()
+    call = lambda dd=d, **k: L.mtla_layer_decode_step_tiles(
+        ctypes.byref(dd), 512, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE,
+        k.get("tiles", FAKE), FAKE, FAKE, FAKE, k.get("ws", FAKE), 1 << 30, None)
+    assert call(tiles=None) == m.MTLA_ERR_INVALID_ARG and "w_uv_tiles" in m.last_error()
+    assert call(tiles=MISALIGNED) == m.MTLA_ERR_INVALID_ARG
+    assert call(dd=m.make_dims(4, 8, 64, 256, 32, 2, 128, "fp32")) == m.MTLA_ERR_UNSUPPORTED
     assert call(ws=None) == m.MTLA_ERR_WORKSPACE

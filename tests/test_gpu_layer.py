@@ -159,3 +159,30 @@ def test_layer_prefill_in_chunks_then_decode(gate_per_position):
     got = np.concatenate(outs, axis=1)
     want = np.stack([_oracle_layer(w, p, b, "incremental") for b in range(B)])
     oracle_ref.assert_steps(got, want, tol(w.dtype))
+
+
+def test_layer_decode_step_tiles_equals_layer_decode_step():
+    """mtla_layer_decode_step_tiles (W_UV packed into tile order) gives the
+    bits of mtla_layer_decode_step over a decode loop: outputs, cache rows and
+    open-slot state."""
+    runs = []
+    for tiles in (False, True):
+        w, p, d, dev, pe, cache, open_acc = _setup(1, batch=3, n_tokens=60)
+        B, dm = w.batch, w.d_model
+        ws = torch.empty(m.mtla_layer_decode_workspace_bytes(d, dm), dtype=torch.uint8, device=DEV)
+        packed = torch.empty(m.mtla_w_uv_tiles_bytes(d) // 2, dtype=d.torch_dtype, device=DEV)
+        m.mtla_pack_w_uv_tiles(d, dev["w_uv"], packed)
+        ys = []
+        for t in range(1, w.n_tokens + 1):
+            pos = torch.full((B,), t, dtype=torch.int32, device=DEV)
+            y = torch.empty(B, dm, dtype=d.torch_dtype, device=DEV)
+            args = (d, pos, dev["h"][:, t - 1].contiguous(), dev["w_dkv"], dev["w_q"], dev["w_r"], dev["w_o"],
+                    dev["w_hyp"], pe, dev["w_uk"], dev["w_uv"])
+            if tiles:
+                m.mtla_layer_decode_step_tiles(*args, packed, cache, open_acc, y, ws)
+            else:
+                m.mtla_layer_decode_step(*args, cache, open_acc, y, ws)
+            ys.append(y.view(torch.int16).clone())
+        runs.append((torch.stack(ys), cache.view(torch.int16).clone(), open_acc.clone()))
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
