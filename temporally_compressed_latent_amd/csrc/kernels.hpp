@@ -68,6 +68,7 @@ struct LayerGemmArgs {
   void* q_r;
   int lda = 0;          // row stride of A in elements (0: K)
   int out_f32 = 0;      // mode 0: out is fp32 whatever the storage type
+  int vec8 = 0;         // set by the launcher: every 8-column chunk of a row has one 16-byte-aligned destination
 };
 hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st);
 

@@ -121,6 +121,24 @@ __device__ __forceinline__ PairStore pair_store(const LayerGemmArgs& g, int n) {
   }
 }
 
+// Eight consecutive output columns n .. n+7 (n a multiple of 8) with one
+// destination (when the launcher sets vec8): four pairs, one 16-byte store
+// of bf16 (two of fp32) per row.
+struct ChunkStore {
+  void* dst;
+  int stride, off;
+  bool rope, f32;
+  double theta[4];
+};
+__device__ __forceinline__ ChunkStore chunk_store(const LayerGemmArgs& g, int n) {
+  const PairStore p0 = pair_store(g, n);
+  ChunkStore c{p0.dst, p0.stride, p0.off, p0.rope, p0.f32, {0.0, 0.0, 0.0, 0.0}};
+  if (p0.rope)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) c.theta[p] = pair_store(g, n + 2 * p).theta;
+  return c;
+}
+
 // Rotate the pair (x0, x1) by the angle pos * theta: the angle is formed and
 // reduced to [-pi, pi] in double, so that large positions keep their
 // accuracy, and its sine and cosine are taken in float.
@@ -488,6 +506,55 @@ __global__ __launch_bounds__(256) void layer_gemm_mfma_kernel(LayerGemmArgs g, i
   const PairStore ps = pair_store(g, min(n, N - 2));
   if (g.mode != 0)
     for (int r = tid; r < TMR; r += 256) sPos[r] = row_position(g, min(m0 + r, M - 1));
+  if (g.vec8) {
+    // thread (row r, chunk q): 8 columns n0 + 8 q .. +7 of rows r, r + 16,
+    // ... of each quarter, one 16-byte (bf16) or two (fp32) stores per row
+    const int q = tid & 15, n8 = n0 + 8 * q;
+    const ChunkStore cs = chunk_store(g, min(n8, N - 8));
+#pragma unroll
+    for (int hh = 0; hh < TMR / 64; ++hh) {
+      if (wm == hh / (NI / 2)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              sC[(32 * i + 8 * (e / 4) + 4 * grp + (e % 4)) * MCP + 64 * wn + 32 * j + c32] =
+                  acc[2 * (hh % (NI / 2)) + i][j][e];
+      }
+      __syncthreads();
+      if (n8 < N) {
+        for (int r = tid >> 4; r < 64; r += 16) {
+          const int m = m0 + 64 * hh + r;
+          if (m >= M) break;
+          const float4 lo = *reinterpret_cast<const float4*>(sC + r * MCP + 8 * q);
+          const float4 hi = *reinterpret_cast<const float4*>(sC + r * MCP + 8 * q + 4);
+          float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          if (cs.rope) {
+            const int pos = sPos[64 * hh + r];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) rope_rotate_rev(pos, cs.theta[p], x[2 * p], x[2 * p + 1]);
+          }
+          const size_t i = static_cast<size_t>(m) * cs.stride + cs.off;
+          if (cs.f32) {
+            float* d = static_cast<float*>(cs.dst) + i;
+            *reinterpret_cast<float4*>(d) = float4{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<float4*>(d + 4) = float4{x[4], x[5], x[6], x[7]};
+          } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+              w[p] = static_cast<uint32_t>(f32_to_bf16_bits(x[2 * p])) |
+                     (static_cast<uint32_t>(f32_to_bf16_bits(x[2 * p + 1])) << 16);
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(cs.dst) + i) = uint4{w[0], w[1], w[2], w[3]};
+          }
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
 #pragma unroll
   for (int hh = 0; hh < TMR / 64; ++hh) {
     // quarter hh: rows 32 i of wave row hh / (NI / 2), i = 2 (hh % (NI / 2)) + 0, 1
@@ -617,6 +684,18 @@ __global__ __launch_bounds__(256) void layer_gemm_skinny_kernel(const uint16_t* 
 
 }  // namespace
 
+namespace {
+// Every 8-column chunk of an output row lies in one destination at a 16-byte
+// boundary: N and the section widths multiples of 8, the arrays 16-byte
+// aligned.
+bool chunk_stores_ok(const LayerGemmArgs& g) {
+  auto al = [](const void* p) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  if (g.N % 8 != 0) return false;
+  if (g.mode == 0) return al(g.out);
+  return g.d_c % 8 == 0 && g.d_h % 8 == 0 && g.d_r % 8 == 0 && al(g.c) && al(g.q_c) && al(g.q_r) && al(g.k_r);
+}
+}  // namespace
+
 hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (dtype != 0 && g.M <= 64) {
@@ -631,13 +710,15 @@ hipError_t launch_layer_gemm(const LayerGemmArgs& g, int dtype, hipStream_t st) 
   }
   if (dtype != 0) {
     const int nrt = (g.M + MBM - 1) / MBM, nct = (g.N + MBN - 1) / MBN;
+    LayerGemmArgs gv = g;
+    gv.vec8 = chunk_stores_ok(g) ? 1 : 0;
     if (g.K % 32 == 0) {
       const int nrt2 = (g.M + 255) / 256;
-      layer_gemm_mfma_kernel<0><<<dim3(8 * ((nrt2 + 7) / 8) * nct), 256, 0, st>>>(g, nrt2, nct);
+      layer_gemm_mfma_kernel<0><<<dim3(8 * ((nrt2 + 7) / 8) * nct), 256, 0, st>>>(gv, nrt2, nct);
     } else if (g.K <= 1024)
-      layer_gemm_mfma_kernel<32><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);
+      layer_gemm_mfma_kernel<32><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(gv, nrt, nct);
     else
-      layer_gemm_mfma_kernel<64><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(g, nrt, nct);
+      layer_gemm_mfma_kernel<64><<<dim3(8 * ((nrt + 7) / 8) * nct), 256, 0, st>>>(gv, nrt, nct);
     return hipGetLastError();
   }
   dim3 grid((g.N + LBN - 1) / LBN, (g.M + LBM - 1) / LBM);

@@ -186,3 +186,22 @@ def test_layer_decode_step_tiles_equals_layer_decode_step():
         runs.append((torch.stack(ys), cache.view(torch.int16).clone(), open_acc.clone()))
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+def test_output_project_unaligned_output():
+    """An output array that is 4-byte but not 16-byte aligned: the tiled
+    GEMM stores column pairs instead of 16-byte chunks, with the same values."""
+    w, p, d, dev, *_ = _setup(1, batch=2, n_tokens=40)
+    H, R = w.heads, 600
+    g = np.random.default_rng(5)
+    o = workloads.quantize(g.standard_normal((R, H, w.d_h)).astype(np.float32), w.dtype)
+    ot = tdev(o, d.torch_dtype)
+    y_al = torch.empty(R, w.d_model, dtype=d.torch_dtype, device=DEV)
+    base = torch.empty(R * w.d_model + 8, dtype=d.torch_dtype, device=DEV)
+    y_un = base[2:2 + R * w.d_model].view(R, w.d_model)            # 4 bytes past a 16-byte boundary
+    assert y_un.data_ptr() % 16 == 4
+    m.mtla_output_project(d, ot, dev["w_o"], y_al)
+    m.mtla_output_project(d, ot, dev["w_o"], y_un)
+    assert torch.equal(y_al.view(torch.int16), y_un.view(torch.int16))
+    want = o.reshape(R, -1).astype(np.float64) @ p["w_o"].astype(np.float64).T
+    assert oracle.max_rel_err(host(y_un), want) <= tol(w.dtype)
