@@ -686,6 +686,36 @@ def run_gemm_peak(steps, warmup, m, torch):
             "TFLOPs": flops / (ms * 1e-3) / 1e12, "frac_of_published": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
+def run_gemm_vs_blas(steps, warmup, m, torch):
+    """The library's layer GEMM as a plain product (mtla_output_project,
+    y = o W^T) beside torch.mm on the ROCm BLAS, on the two projection shapes
+    of the summarisation layer prefill (16 x 4096 tokens, K = H d_h = 512):
+    N = 1056 (the input projection's width, c + q^C + q^R + k^R) and N = 512
+    (the output projection's).  A comparison point only: the layer's own
+    input projection also applies RoPE and scatters in its epilogue."""
+    R, H, d_h = 65536, 8, 64
+    d = m.make_dims(1, H, d_h, 256, 32, 2, 1, "bf16")
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    out = []
+    for N in (1056, 512):
+        o = (torch.randn(R, H, d_h, device="cuda", generator=gen) * 0.1).to(torch.bfloat16)
+        w = (torch.randn(N, H * d_h, device="cuda", generator=gen) * 0.05).to(torch.bfloat16)
+        y = torch.empty(R, N, dtype=torch.bfloat16, device="cuda")
+        yb = torch.empty(R, N, dtype=torch.bfloat16, device="cuda")
+        a2, wt = o.view(R, H * d_h), w.t()
+        for _ in range(max(warmup, 1)):
+            m.mtla_output_project(d, o, w, y)
+            torch.mm(a2, wt, out=yb)
+        ms_own = timed_calls(lambda: m.mtla_output_project(d, o, w, y), max(steps, 5), torch)
+        ms_blas = timed_calls(lambda: torch.mm(a2, wt, out=yb), max(steps, 5), torch)
+        flops = 2.0 * R * N * H * d_h
+        out.append({"shape": [R, N, H * d_h], "own_ms": ms_own, "blas_ms": ms_blas,
+                    "own_TFLOPs": flops / (ms_own * 1e-3) / 1e12, "blas_TFLOPs": flops / (ms_blas * 1e-3) / 1e12,
+                    "max_abs_diff": float((y.float() - yb.float()).abs().max())})
+        del o, w, y, yb, a2, wt
+    return {"kernel": "layer_gemm_mfma_kernel vs torch.mm", "products": out}
+
+
 # ---------------------------------------------------------------------------
 # the single fp32 layer (prefill of 64 tokens, 64-step decode), timed
 # ---------------------------------------------------------------------------
@@ -921,6 +951,7 @@ def main():
               "tile_stream": lambda: run_tile_stream(K, Wu, m, torch),
               "mfma_peak": lambda: run_mfma_peak(K, Wu, m, torch),
               "gemm_peak": lambda: run_gemm_peak(K, Wu, m, torch),
+              "gemm_vs_blas": lambda: run_gemm_vs_blas(K, Wu, m, torch),
               "launch_floor": lambda: run_launch_floor(K, Wu, m, torch),
               "load_pattern": lambda: run_load_pattern(K, Wu, m, torch)}
         print(json.dumps(fn[args.only]()), flush=True)
