@@ -576,6 +576,55 @@ def timed_calls(fn, reps, torch):
     return e0.elapsed_time(e1) / reps
 
 
+def run_step_timeline(w, m, torch, workloads):
+    """Phases of the fused decode step over the whole loop, from the step's
+    timeline instance (the real-time counter, 100 MHz, read in each
+    workgroup): medians over launches and workgroups, in microseconds, by
+    quarter of the loop (the cache grows from 1 to ceil(N/s) slots)."""
+    import numpy as np
+    dl = DecodeLoop(w, m, torch, workloads)
+    d, N = dl.dims, w.n_tokens
+    # room for the most workgroups a launch can have (one head per group);
+    # rows of workgroups that did not run stay zero
+    tl = torch.zeros(N, 8 * w.heads * (-(-w.batch // 8)) * 16, dtype=torch.int64, device="cuda")
+
+    def loop():
+        for t in range(N):
+            m.mtla_calib_step_timeline(d, dl.pos[t], dl.c[t], dl.k_r[t], dl.w_hyp, dl.pe, dl.q_c[t], dl.q_r[t],
+                                       dl.w_uk, dl.w_uv, dl.w_uv_tiles, dl.cache, dl.open_acc, dl.out[t],
+                                       dl.ws, tl[t])
+    g_tl = capture(loop, torch)
+    g_plain = capture(dl.step, torch)
+    g_tl.replay()
+    ms_tl = timed_graph(g_tl, 3, torch)
+    ms_plain = timed_graph(g_plain, 3, torch)
+    x = tl.cpu().numpy().astype(np.int64).reshape(N, -1, 16)
+    live = x[:, :, 0] != 0
+    us = 1e-2  # one tick of the 100 MHz counter
+    start = np.where(live, x[:, :, 0], np.iinfo(np.int64).max).min(axis=1)
+    end = np.where(live, x[:, :, 13], 0).max(axis=1)
+    att_end = x[:, :, 4:12].max(axis=2)
+    ph = {"dispatch_to_entry": x[:, :, 0] - start[:, None],
+          "position": x[:, :, 1] - x[:, :, 0],
+          "w_uk_query_absorb": x[:, :, 2] - x[:, :, 1],
+          "gate_merge_q_tilde": x[:, :, 3] - x[:, :, 2],
+          "attention_slowest_wave": att_end - x[:, :, 3],
+          "combine": x[:, :, 12] - att_end,
+          "up_projection": x[:, :, 13] - x[:, :, 12],
+          "workgroup_total": x[:, :, 13] - x[:, :, 0]}
+    quarters = {}
+    for qi in range(4):
+        sl = slice(qi * N // 4, (qi + 1) * N // 4)
+        rec = {k: float(np.median(v[sl][live[sl]]) * us) for k, v in ph.items()}
+        rec["launch_span"] = float(np.median((end - start)[sl]) * us)
+        nxt = (start[1:] - end[:-1])[sl.start:min(sl.stop, N - 1)]
+        rec["gap_to_next_launch"] = float(np.median(nxt) * us)
+        quarters[f"tokens_{sl.start + 1}_{sl.stop}"] = rec
+    return {"workload": w.name, "kernel": "decode_step_wave_kernel (timeline instance)",
+            "workgroups_per_launch": int(live[0].sum()), "ms_per_loop_timeline": ms_tl,
+            "ms_per_loop_plain": ms_plain, "phases_us_median": quarters}
+
+
 def run_launch_floor(steps, warmup, m, torch, n=512):
     """A graph of n empty kernels: the per-launch floor of any one-kernel step
     replayed the way the decode loops are."""
@@ -953,7 +1002,8 @@ def main():
               "gemm_peak": lambda: run_gemm_peak(K, Wu, m, torch),
               "gemm_vs_blas": lambda: run_gemm_vs_blas(K, Wu, m, torch),
               "launch_floor": lambda: run_launch_floor(K, Wu, m, torch),
-              "load_pattern": lambda: run_load_pattern(K, Wu, m, torch)}
+              "load_pattern": lambda: run_load_pattern(K, Wu, m, torch),
+              "step_timeline": lambda: run_step_timeline(W[1], m, torch, workloads)}
         print(json.dumps(fn[args.only]()), flush=True)
         return 0
 

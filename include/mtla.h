@@ -600,6 +600,32 @@ int32_t mtla_calib_load_pattern(int32_t pattern, int32_t workgroups, const void*
 int32_t mtla_calib_tile_stream(const void* rows, int32_t seqs, int32_t rows_per_seq, int32_t splits, int32_t flags,
                                uint32_t* sink, void* stream);
 
+/*
+ * mtla_calib_step_timeline: where the time of one fused decode step goes.
+ * It runs mtla_decode_step_tiles (same arguments, checks, work and
+ * results) through an instance of the one-kernel step that also records,
+ * per workgroup, 16 readings of the GPU's constant 100 MHz real-time
+ * counter into timeline (device, uint64, 8-byte aligned), row L of 16 for
+ * workgroup L: [0] entry, [1] the position known, [2] the absorb's partial
+ * sums formed (W_UK and the query arrived), [3] the scaled absorbed query
+ * in LDS, [4 + w] wave w's attention over its slot chunks done (w < 8),
+ * [12] o_lat in LDS, [13] the output stored; [14], [15] unused.  A reading
+ * is taken once the value it names is available in the wave that takes it.
+ * Workgroup L serves sequence 8 (k / G) + L % 8 and head group
+ * (L / 8) % G, k = L / 8, where G is the head-group count the launch uses;
+ * rows of workgroups past the batch are not written.  timeline_entries must
+ * be at least 16 * 8 * G * ceil(batch / 8) (the launch's workgroups).
+ * Supported only where the step runs as one kernel on bf16 with d_c = 256,
+ * d_r = 32 and one W_hyp row (else MTLA_ERR_UNSUPPORTED).  The readings add
+ * a few scalar reads and stores to the step, so it runs slightly longer
+ * than mtla_decode_step_tiles.
+ */
+int32_t mtla_calib_step_timeline(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
+                                 const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                                 const void* q_r, const void* w_uk, const void* w_uv, const void* w_uv_tiles,
+                                 void* cache, float* open_acc, void* out, void* workspace, size_t ws_bytes,
+                                 uint64_t* timeline, size_t timeline_entries, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ from ._lib import (  # noqa: F401
     mtla_layer_decode_workspace_bytes, mtla_layer_decode_step, mtla_layer_prefill_workspace_bytes,
     mtla_layer_prefill, mtla_prefill_backward, mtla_prefill_backward_workspace_bytes,
     mtla_version, status_string, mtla_calib_stream_read, mtla_calib_mfma, mtla_calib_empty, mtla_calib_tile_stream,
-    mtla_calib_load_pattern, mtla_w_uv_tiles_bytes, mtla_pack_w_uv_tiles, mtla_decode_step_tiles,
+    mtla_calib_load_pattern, mtla_calib_step_timeline, mtla_w_uv_tiles_bytes, mtla_pack_w_uv_tiles, mtla_decode_step_tiles,
     mtla_layer_decode_step_tiles,
     mtla_prefill_partials, mtla_prefill_keys, mtla_prefill_attention, prefill_slot_keys,
 )

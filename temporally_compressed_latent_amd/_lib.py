@@ -114,6 +114,8 @@ _SIGS = {
     "mtla_calib_empty": (_I, [_P]),
     "mtla_calib_load_pattern": (_I, [_I, _I, _P, _SZ, _P, _P]),
     "mtla_calib_tile_stream": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+    "mtla_calib_step_timeline": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                      _P, _SZ, _P]),
     "mtla_absorb_query": (_I, [_D, _I, _P, _P, _P, _P, _P]),
     "mtla_decode_attention_workspace_bytes": (_I, [_D, ctypes.POINTER(_SZ)]),
     "mtla_decode_attention": (_I, [_D, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -340,6 +342,33 @@ def mtla_decode_step_tiles(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w_u
         _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
         _tensor("out", out, (B, H, dims.d_h), st),
         ws, ws_bytes, _stream(stream)))
+
+
+def mtla_calib_step_timeline(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w_uk, w_uv, w_uv_tiles, cache,
+                             open_acc, out, workspace, timeline, stream=None) -> None:
+    """mtla_decode_step_tiles through the fused step's timeline instance;
+    timeline: int64 device tensor of 16 readings per workgroup."""
+    B, H, st = dims.batch, dims.heads, dims.torch_dtype
+    ws, ws_bytes = _ws("workspace", workspace, 0)
+    n = mtla_w_uv_tiles_bytes(dims) // 2
+    if timeline.dtype != torch.int64 or timeline.device.type != "cuda" or not timeline.is_contiguous():
+        raise ValueError("timeline must be a contiguous int64 device tensor")
+    _check(_lib.mtla_calib_step_timeline(
+        ctypes.byref(dims),
+        _tensor("pos", pos, (B,), torch.int32),
+        _tensor("c", c, (B, dims.d_c), st),
+        _tensor("k_r", k_r, (B, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_hyp", w_hyp, dims.gate_shape, torch.float32),
+        _tensor("pe", pe, (pe.shape[0], dims.d_c), torch.float32), int(pe.shape[0]),
+        _tensor("q_c", q_c, (B, H, dims.d_h), st),
+        _tensor("q_r", q_r, (B, H, dims.d_r), st, optional=dims.d_r == 0),
+        _tensor("w_uk", w_uk, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv", w_uv, (H, dims.d_h, dims.d_c), st),
+        _tensor("w_uv_tiles", w_uv_tiles, (n,), st),
+        _tensor("cache", cache, (B, dims.max_slots, dims.width), st),
+        _tensor("open_acc", open_acc, (B, 2, dims.width), torch.float32),
+        _tensor("out", out, (B, H, dims.d_h), st),
+        ws, ws_bytes, timeline.data_ptr(), timeline.numel(), _stream(stream)))
 
 
 def mtla_decode_step_noalloc(dims: MtlaDims, pos, c, k_r, w_hyp, pe, q_c, q_r, w_uk, w_uv, cache, open_acc,

@@ -477,7 +477,8 @@ static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const
                                 const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
                                 const void* q_r, const void* w_uk, const void* w_uv, void* cache,
                                 float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream,
-                                bool check_only, const void* w_uv_tiles);
+                                bool check_only, const void* w_uv_tiles,
+                                unsigned long long* timeline = nullptr);
 
 int32_t mtla_decode_step(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
                          const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
@@ -524,11 +525,40 @@ int32_t mtla_decode_step_tiles(const mtla_dims* dims, const int32_t* pos, const 
                           workspace, ws_bytes, stream, false, w_uv_tiles);
 }
 
+// The timeline instance of the fused step (measurement): the same checks and
+// work as mtla_decode_step_tiles on the shapes that run the one-kernel step
+// for 256-wide latents with one W_hyp row.
+int32_t mtla_calib_step_timeline(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
+                                 const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
+                                 const void* q_r, const void* w_uk, const void* w_uv, const void* w_uv_tiles,
+                                 void* cache, float* open_acc, void* out, void* workspace, size_t ws_bytes,
+                                 uint64_t* timeline, size_t timeline_entries, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MTLA_OK) return st;
+  if (dims->dtype != MTLA_BF16 || dims->d_c != 256 || dims->d_r != 32 || !decode_fused(dims) ||
+      gate_stride(dims) != 0)
+    return fail(MTLA_ERR_UNSUPPORTED,
+                "the step timeline covers the one-kernel bf16 step with d_c=256, d_r=32 and one W_hyp row");
+  const int groups = mtla::decode_step_groups(dims->batch, dims->heads, dims->d_h, dims->d_c, dims->step_groups);
+  if (groups < 1) return fail(MTLA_ERR_UNSUPPORTED, "no head grouping of the fused step fits these dims");
+  const size_t need = static_cast<size_t>(8) * groups * ((dims->batch + 7) / 8) * mtla::kStepTimelineSlots;
+  if (!timeline || !aligned_to(timeline, 8)) return fail(MTLA_ERR_INVALID_ARG, "timeline is NULL or not 8-byte aligned");
+  if (timeline_entries < need)
+    return fail(MTLA_ERR_INVALID_ARG, "timeline holds %zu entries < %zu needed", timeline_entries, need);
+  size_t bytes = 0;
+  if ((st = mtla_w_uv_tiles_bytes(dims, &bytes)) != MTLA_OK) return st;
+  if (!w_uv_tiles || !aligned16(w_uv_tiles))
+    return fail(MTLA_ERR_INVALID_ARG, "w_uv_tiles is NULL or not 16-byte aligned");
+  return decode_step_impl(dims, pos, c, k_r, w_hyp, pe, pe_rows, q_c, q_r, w_uk, w_uv, cache, open_acc, out,
+                          workspace, ws_bytes, stream, false, w_uv_tiles,
+                          reinterpret_cast<unsigned long long*>(timeline));
+}
+
 static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const void* c, const void* k_r,
                                 const float* w_hyp, const float* pe, int32_t pe_rows, const void* q_c,
                                 const void* q_r, const void* w_uk, const void* w_uv, void* cache,
                                 float* open_acc, void* out, void* workspace, size_t ws_bytes, void* stream,
-                                bool check_only, const void* w_uv_tiles) {
+                                bool check_only, const void* w_uv_tiles, unsigned long long* timeline) {
   int32_t st = check_dims(dims);
   if (st != MTLA_OK) return st;
   if (pe_rows < 1) return fail(MTLA_ERR_INVALID_ARG, "pe_rows=%d < 1", pe_rows);
@@ -560,6 +590,7 @@ static int32_t decode_step_impl(const mtla_dims* dims, const int32_t* pos, const
                                  cache, open_acc, out, 1);
     a.wh_stride = gate_stride(dims);
     if (dims->d_c == 256) a.w_uv_tiles = static_cast<const uint16_t*>(w_uv_tiles);
+    a.timeline = timeline;
     return hip_status(mtla::launch_decode_step(a, s), "decode step launch");
   }
   mtla::MergeArgs m{dims->batch, 1, dims->d_c, dims->d_r, dims->stride_s, dims->max_slots, pe_rows,

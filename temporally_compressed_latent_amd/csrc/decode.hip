@@ -1138,7 +1138,18 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(const int32_t* __restr
 // which everything waits for, and the first loads of W_UK, the queries and the
 // token then issue at once instead of after a round trip to the
 // kernel-argument segment.
-template <int DC, int DR, int HG, int DH, bool MERGE, bool PP = false>
+// Timeline instance only: lane 0 of the calling wave writes the real-time
+// counter (100 MHz), read once `dep` is available, to reading k of workgroup
+// wg.
+__device__ __forceinline__ void timeline_stamp(unsigned long long* tl, int wg, int k, float dep) {
+  asm volatile("" ::"v"(dep) : "memory");
+  const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+  if ((threadIdx.x & 63) == 0) tl[static_cast<size_t>(wg) * kStepTimelineSlots + k] = t;
+}
+
+// TL: the timeline instance (the same work, plus the counter readings listed
+// with kStepTimelineSlots).
+template <int DC, int DR, int HG, int DH, bool MERGE, bool PP = false, bool TL = false>
 __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __restrict__ kpos, int G, int nB, int H,
                                                               int d_h, const uint16_t* __restrict__ w_uk,
                                                               const uint16_t* __restrict__ q_c,
@@ -1208,6 +1219,9 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   const int h0 = grp * HG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
+  if constexpr (TL) {
+    if (wave == 0) timeline_stamp(a.timeline, L, 0, 0.f);
+  }
 
   const int pos = kpos[b];
   // (the position load goes out before anything else: the scheduler would
@@ -1280,6 +1294,9 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
     place = (pos - 1) % sblk;
   }
   if (pos < 1) n = 0;
+  if constexpr (TL) {
+    if (wave == 0) timeline_stamp(a.timeline, L, 1, static_cast<float>(n));
+  }
   const bool ok = pos >= 1 && n <= a.max_slots && (!MERGE || pos <= a.pe_rows);
   uint16_t* out = a.out + (static_cast<size_t>(b) * H + h0) * d_h;
   if (!ok) {
@@ -1359,6 +1376,9 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
     float* dst = &u.ab.red[hl][eg][kc * 8];
     *reinterpret_cast<float4*>(dst) = float4{acc[0], acc[1], acc[2], acc[3]};
     *reinterpret_cast<float4*>(dst + 4) = float4{acc[4], acc[5], acc[6], acc[7]};
+    if constexpr (TL) {
+      if (wave == 0) timeline_stamp(a.timeline, L, 2, acc[7]);
+    }
   }
   // every wave computes the gate (same values, same order: the same bits)
   float gate = 0.f;
@@ -1392,6 +1412,9 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
     split_bf16(bf16_bits_to_f32(qrb) * qscale, sq[tid / DR][DC + tid % DR], sq[HG + tid / DR][DC + tid % DR]);
   for (int e = tid; e < W; e += NT) sq[2 * HG][e] = 0;
   __syncthreads();
+  if constexpr (TL) {
+    if (wave == 0) timeline_stamp(a.timeline, L, 3, 0.f);
+  }
 
   // attention
   bf16x8 qk[KSW];
@@ -1503,6 +1526,7 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   }
   // this wave's sum for head c16: the four lane groups, in a fixed order
   const float lw = cross_row_sum(l);
+  if constexpr (TL) timeline_stamp(a.timeline, L, 4 + wave, lw);
   // the wave's O^T columns (head h's high part at column h, low part at
   // HG + h) and its running max and sum (the same in both columns)
   if (c16 < 2 * HG) {
@@ -1535,6 +1559,9 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
   }
   for (int e = tid; e < DC; e += NT) u.cb.zero[e] = 0;
   __syncthreads();
+  if constexpr (TL) {
+    if (wave == 0) timeline_stamp(a.timeline, L, 12, 0.f);
+  }
 
   // up-projection: C[e, n] = sum_k W_UV[hu][mt*16 + e][k] B[k, n], with
   // column 0 of B = o_lat hi (first product) or lo (second), the other
@@ -1561,6 +1588,9 @@ __global__ __launch_bounds__(512) void decode_step_wave_kernel(const int32_t* __
         const int e = mt * 16 + 4 * g + i;
         if (e < d_h) out[hu * d_h + e] = f32_to_bf16_bits((co[0][i] + co[1][i]) + (co[2][i] + co[3][i]));
       }
+    }
+    if constexpr (TL) {
+      if (wave == 0) timeline_stamp(a.timeline, L, 13, co[0][0]);
     }
   }
 }
@@ -2047,7 +2077,9 @@ void step_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
 }
 template <int DC, int DR, int HG, int DH>
 void step_wave_launch(const StepArgs& a, unsigned grid, hipStream_t st) {
-  if (a.merge && a.wh_stride != 0)
+  if (a.timeline)  // (callers take this path only to merge with one W_hyp row)
+    decode_step_wave_kernel<DC, DR, HG, DH, true, false, true><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a.H, a.d_h, a.w_uk, a.q_c, a.c, a);
+  else if (a.merge && a.wh_stride != 0)
     decode_step_wave_kernel<DC, DR, HG, DH, true, true><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a.H, a.d_h, a.w_uk, a.q_c, a.c, a);
   else if (a.merge)
     decode_step_wave_kernel<DC, DR, HG, DH, true><<<grid, 512, 0, st>>>(a.pos, a.groups, a.B, a.H, a.d_h, a.w_uk, a.q_c, a.c, a);

@@ -207,7 +207,14 @@ struct StepArgs {
   // W_UV in tile order (launch_pack_w_uv_tiles), or null: the 256-wide fused
   // step then reads it as whole lines (same values, same bits)
   const uint16_t* w_uv_tiles = nullptr;
+  // Timeline instance of the 256-wide fused step (measurement only): each
+  // workgroup writes kStepTimelineSlots real-time counter readings, or null.
+  unsigned long long* timeline = nullptr;
 };
+// Readings per workgroup of the fused step's timeline instance: 0 entry,
+// 1 position known, 2 absorb partial sums formed, 3 scaled q~ in LDS,
+// 4 + w wave w's attention done (w < 8), 12 o_lat in LDS, 13 output stored.
+constexpr int kStepTimelineSlots = 16;
 bool decode_step_supported(int H, int d_h, int d_c, int d_r);
 // Head groups per sequence the step kernel uses for a batch of B sequences
 // (`requested` when it is a valid group count, else the launcher's choice).
